@@ -1,0 +1,291 @@
+"""Seeded synthetic inputs for the hybrid conv/IIR/attention verify path.
+
+This module only draws random numbers and arranges them into arrays.  It
+holds none of the method's arithmetic (no FIR, no IIR step, no softmax, no
+attention, no acceptance rule), so that the fp64 oracle and the HIP path can
+both be fed from it without sharing any computation.
+
+Workloads follow the five operating points of the EvSpark digest (Synopsis
+and Perspective: 7B-scale layers, 51k-262k context, batching, multiple
+candidates, sustained generation) as fixed synthetic shapes:
+
+* ``c1``  tiny fp32 layer: d=64, 3/7 FIR taps, 16 poles, 1 head x 64, L=256, gamma=6
+* ``c2``  d=4096, bf16, 3/128 taps, 16 poles, 32 heads x 128, L=8192, gamma=12, sampling
+* ``c3``  c2's layer at L=262144, gamma=12 (``c3``) or gamma=6 (``c3g6``), greedy
+* ``c4``  4 sequences x 4 candidates, ragged L in {16384, 32768, 51200, 65536}
+* ``c5``  d=8192, 64 heads x 128, L=131072, gamma=12, 256 sustained rounds
+
+Distributions (variance readings): FIR taps N(0, 1/taps); poles U(0.5, 0.99);
+input and readout gains N(0, 1/16); activations and KV N(0, 1); logits N(0, 2).
+bf16 values are produced by round-to-nearest-even from fp32 and are handed to
+both sides as raw 16-bit patterns (``numpy.uint16``).
+
+Random streams are independent torch CPU generators keyed by
+``(config id, stream id, round)``; the large KV prefixes can instead be drawn
+on a GPU with torch's device generator (``kv_prefix(..., device="cuda")``),
+the host side then receives a copy of the very same bits.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+F32 = "f32"
+BF16 = "bf16"
+
+# fixed stream ids (part of every seed)
+_S_WSHORT, _S_WOUTER, _S_LAMBDA, _S_BETA, _S_C = 1, 2, 3, 4, 5
+_S_EX, _S_EQ, _S_EK, _S_EV = 10, 11, 12, 13
+_S_SWIN, _S_OWIN, _S_IIR = 20, 21, 22
+_S_KPRE, _S_VPRE = 30, 31
+_S_TOK, _S_ZT, _S_ZD, _S_GUMBEL, _S_U, _S_GEOM = 40, 41, 42, 43, 44, 45
+_S_NEEDLE = 50
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    cfg_id: int
+    d: int
+    taps_short: int
+    taps_outer: int
+    poles: int
+    heads: int
+    head_dim: int
+    kv_lens: tuple          # committed prefix length per sequence
+    gamma: int
+    nc: int = 1             # candidate blocks per sequence
+    vocab: int = 512
+    act: str = BF16
+    mode: str = "sample"    # "greedy" or "sample"
+    temperature: float = 1.0
+    rounds: int = 1
+
+    @property
+    def nb(self) -> int:
+        return len(self.kv_lens)
+
+    @property
+    def P(self) -> int:
+        return self.gamma + 1
+
+    @property
+    def max_kv_len(self) -> int:
+        return max(self.kv_lens)
+
+    def kv_cap(self, extra_rounds: Optional[int] = None) -> int:
+        r = self.rounds if extra_rounds is None else extra_rounds
+        need = self.max_kv_len + (r + 1) * self.P
+        return (need + 31) // 32 * 32
+
+
+CONFIGS: Dict[str, Config] = {
+    "c1": Config("c1", 1, d=64, taps_short=3, taps_outer=7, poles=16, heads=1, head_dim=64,
+                 kv_lens=(256,), gamma=6, act=F32, mode="sample"),
+    "c2": Config("c2", 2, d=4096, taps_short=3, taps_outer=128, poles=16, heads=32, head_dim=128,
+                 kv_lens=(8192,), gamma=12, act=BF16, mode="sample"),
+    "c3": Config("c3", 3, d=4096, taps_short=3, taps_outer=128, poles=16, heads=32, head_dim=128,
+                 kv_lens=(262144,), gamma=12, act=BF16, mode="greedy"),
+    "c3g6": Config("c3g6", 6, d=4096, taps_short=3, taps_outer=128, poles=16, heads=32, head_dim=128,
+                   kv_lens=(262144,), gamma=6, act=BF16, mode="greedy"),
+    "c4": Config("c4", 4, d=4096, taps_short=3, taps_outer=128, poles=16, heads=32, head_dim=128,
+                 kv_lens=(16384, 32768, 51200, 65536), gamma=12, nc=4, act=BF16, mode="sample"),
+    "c5": Config("c5", 5, d=8192, taps_short=3, taps_outer=128, poles=16, heads=64, head_dim=128,
+                 kv_lens=(131072,), gamma=12, act=BF16, mode="greedy", rounds=256),
+}
+
+
+def scaled(cfg: Config, **kw) -> Config:
+    """A copy of ``cfg`` with some fields replaced (smaller parity variants)."""
+    return dataclasses.replace(cfg, **kw)
+
+
+# ---------------------------------------------------------------- generators
+
+def _gen(cfg: Config, stream: int, rnd: int = 0, seed: int = 0) -> torch.Generator:
+    g = torch.Generator()
+    g.manual_seed(((seed * 1000 + cfg.cfg_id) * 100 + stream) * 100003 + rnd)
+    return g
+
+
+def bf16_bits(a: torch.Tensor) -> np.ndarray:
+    """fp32 tensor -> bf16 bit patterns (round to nearest even) as uint16."""
+    return a.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact widening)."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _act(cfg: Config, t: torch.Tensor) -> np.ndarray:
+    t = t.to(torch.float32)
+    return bf16_bits(t) if cfg.act == BF16 else t.numpy().astype(np.float32)
+
+
+def _normal(cfg, stream, shape, std=1.0, rnd=0, seed=0) -> torch.Tensor:
+    return torch.randn(shape, generator=_gen(cfg, stream, rnd, seed), dtype=torch.float32) * std
+
+
+# ---------------------------------------------------------------- layer
+
+def make_layer(cfg: Config, seed: int = 0) -> Dict[str, np.ndarray]:
+    d, N = cfg.d, cfg.poles
+    lam = torch.rand((d, N), generator=_gen(cfg, _S_LAMBDA, 0, seed), dtype=torch.float64)
+    lam = (0.5 + 0.49 * lam).to(torch.float32)
+    return {
+        "w_short": _normal(cfg, _S_WSHORT, (cfg.taps_short, d), 1.0 / math.sqrt(cfg.taps_short), seed=seed).numpy(),
+        "w_outer": _normal(cfg, _S_WOUTER, (cfg.taps_outer, d), 1.0 / math.sqrt(cfg.taps_outer), seed=seed).numpy(),
+        "lam": lam.numpy(),
+        "beta": _normal(cfg, _S_BETA, (d, N), 0.25, seed=seed).numpy(),
+        "c": _normal(cfg, _S_C, (d, N), 0.25, seed=seed).numpy(),
+    }
+
+
+def make_tables(cfg: Config, seed: int = 0) -> Dict[str, np.ndarray]:
+    """Token-keyed input tables: block inputs are rows of these tables."""
+    V, d, H, Dh = cfg.vocab, cfg.d, cfg.heads, cfg.head_dim
+    return {
+        "E_x": _act(cfg, _normal(cfg, _S_EX, (V, d), seed=seed)),
+        "E_q": _act(cfg, _normal(cfg, _S_EQ, (V, H, Dh), seed=seed)),
+        "E_k": _act(cfg, _normal(cfg, _S_EK, (V, H, Dh), seed=seed)),
+        "E_v": _act(cfg, _normal(cfg, _S_EV, (V, H, Dh), seed=seed)),
+    }
+
+
+def make_state_small(cfg: Config, seed: int = 0) -> Dict[str, np.ndarray]:
+    """Committed FIR windows and IIR state (the KV prefix is drawn separately)."""
+    nb, d, N = cfg.nb, cfg.d, cfg.poles
+    return {
+        "short_win": _act(cfg, _normal(cfg, _S_SWIN, (nb, cfg.taps_short - 1, d), seed=seed)),
+        "outer_win": _normal(cfg, _S_OWIN, (nb, cfg.taps_outer - 1, d), seed=seed).numpy(),
+        "iir": _normal(cfg, _S_IIR, (nb, d, N), 0.5, seed=seed).numpy(),
+    }
+
+
+def kv_prefix(cfg: Config, b: int, which: str, seed: int = 0, device: str = "cpu",
+              length: Optional[int] = None) -> torch.Tensor:
+    """Committed KV prefix of sequence ``b``: [H][L][Dh] ~ N(0,1) in act dtype.
+
+    Returns a torch tensor (bf16 or fp32) on ``device``.  On a GPU the values
+    come from torch's device generator; on the CPU from torch's CPU generator.
+    """
+    L = cfg.kv_lens[b] if length is None else length
+    stream = _S_KPRE if which == "k" else _S_VPRE
+    s = ((seed * 1000 + cfg.cfg_id) * 100 + stream) * 100003 + 7 * b + 1
+    g = torch.Generator(device=device)
+    g.manual_seed(s)
+    out_dtype = torch.bfloat16 if cfg.act == BF16 else torch.float32
+    out = torch.empty((cfg.heads, L, cfg.head_dim), dtype=out_dtype, device=device)
+    for h in range(cfg.heads):  # one head at a time bounds the fp32 temporary
+        out[h] = torch.randn((L, cfg.head_dim), generator=g, device=device, dtype=torch.float32).to(out_dtype)
+    return out
+
+
+def needle_positions(cfg: Config, b: int, count: int = 4, seed: int = 0) -> np.ndarray:
+    """Prefix rows where a key is replaced by a scaled copy of a block query."""
+    L = cfg.kv_lens[b]
+    g = _gen(cfg, _S_NEEDLE, b, seed)
+    return torch.randint(0, max(L, 1), (count,), generator=g).numpy()
+
+
+# ---------------------------------------------------------------- tokens, logits, uniforms
+
+def gather_block(cfg: Config, tables: Dict[str, np.ndarray], tokens: np.ndarray) -> Dict[str, np.ndarray]:
+    """Block inputs from token ids ``tokens`` [nb][nc][P]: x, q, k, v rows of the tables."""
+    return {
+        "x": tables["E_x"][tokens],   # [nb][nc][P][d]
+        "q": tables["E_q"][tokens],   # [nb][nc][P][H][Dh]
+        "k": tables["E_k"][tokens],
+        "v": tables["E_v"][tokens],
+    }
+
+
+def anchors(cfg: Config, rnd: int = 0, seed: int = 0) -> np.ndarray:
+    return torch.randint(0, cfg.vocab, (cfg.nb,), generator=_gen(cfg, _S_TOK, rnd, seed)).numpy().astype(np.int32)
+
+
+def logits(cfg: Config, stream: str, rows: int, rnd: int = 0, seed: int = 0) -> np.ndarray:
+    """[nb][nc][rows][V] fp32 logits ~ N(0, 2)."""
+    sid = _S_ZT if stream == "target" else _S_ZD
+    return _normal(cfg, sid, (cfg.nb, cfg.nc, rows, cfg.vocab), math.sqrt(2.0), rnd, seed).numpy()
+
+
+def uniforms(cfg: Config, rnd: int = 0, seed: int = 0) -> np.ndarray:
+    """[nb][nc][P] fp64 uniforms in [0, 1): r_1..r_gamma then r*."""
+    g = _gen(cfg, _S_U, rnd, seed)
+    return torch.rand((cfg.nb, cfg.nc, cfg.P), generator=g, dtype=torch.float64).numpy()
+
+
+def gumbel_drafts(cfg: Config, draft_logits: np.ndarray, rnd: int = 0, seed: int = 0) -> np.ndarray:
+    """Draft tokens sampled from softmax(draft_logits / T) by the Gumbel-max trick.
+
+    ``argmax(z / T + G)`` with G i.i.d. standard Gumbel is an exact sample of the
+    categorical distribution softmax(z / T); no probabilities are formed here.
+    """
+    g = _gen(cfg, _S_GUMBEL, rnd, seed)
+    u = torch.rand(draft_logits.shape, generator=g, dtype=torch.float64).numpy()
+    u = np.clip(u, 1e-300, 1.0 - 1e-16)
+    gum = -np.log(-np.log(u))
+    return np.argmax(draft_logits.astype(np.float64) / cfg.temperature + gum, axis=-1).astype(np.int32)
+
+
+def geometric_agreement(cfg: Config, rnd: int = 0, seed: int = 0, p_continue: float = 0.7,
+                        forced_len: Optional[Sequence[int]] = None):
+    """Greedy workload: drafts agree with the target argmax for a Geometric(0.7) prefix.
+
+    Returns (drafts [nb][nc][gamma] int32, target_logits [nb][nc][P][V] fp32, lengths).
+    Agreement is planted, not measured: row m-1 of the target logits gets a
+    logit of +100 at draft t_m for m <= Lg (N(0,2) logits never come near it),
+    and row Lg gets -100 at draft t_{Lg+1}, so that draft cannot be the argmax.
+    """
+    nb, nc, gam, V = cfg.nb, cfg.nc, cfg.gamma, cfg.vocab
+    g = _gen(cfg, _S_GEOM, rnd, seed)
+    drafts = torch.randint(0, V, (nb, nc, gam), generator=g).numpy().astype(np.int32)
+    zt = logits(cfg, "target", cfg.P, rnd, seed)
+    lens = np.zeros((nb, nc), dtype=np.int32)
+    u = torch.rand((nb, nc, gam), generator=g, dtype=torch.float64).numpy()
+    for b in range(nb):
+        for c in range(nc):
+            if forced_len is not None:
+                n = int(forced_len[b * nc + c])
+            else:
+                n = 0
+                while n < gam and u[b, c, n] < p_continue:
+                    n += 1
+            lens[b, c] = n
+            for m in range(1, n + 1):
+                zt[b, c, m - 1, drafts[b, c, m - 1]] = 100.0
+            if n < gam:
+                zt[b, c, n, drafts[b, c, n]] = -100.0
+    return drafts, zt, lens
+
+
+def block_tokens(anchor: np.ndarray, drafts: np.ndarray) -> np.ndarray:
+    """[nb] anchors and [nb][nc][gamma] drafts -> [nb][nc][P] block tokens."""
+    nb, nc, gam = drafts.shape
+    t = np.empty((nb, nc, gam + 1), dtype=np.int32)
+    t[:, :, 0] = anchor[:, None]
+    t[:, :, 1:] = drafts
+    return t
+
+
+def round_inputs(cfg: Config, anchor: np.ndarray, rnd: int = 0, seed: int = 0,
+                 forced_len: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """Everything one verify/accept round needs besides layer, state and tables."""
+    if cfg.mode == "greedy":
+        drafts, zt, lens = geometric_agreement(cfg, rnd, seed, forced_len=forced_len)
+        zd = None
+        u = None
+    else:
+        zt = logits(cfg, "target", cfg.P, rnd, seed)
+        zd = logits(cfg, "draft", cfg.gamma, rnd, seed)
+        drafts = gumbel_drafts(cfg, zd, rnd, seed)
+        u = uniforms(cfg, rnd, seed)
+        lens = None
+    return {"drafts": drafts, "target_logits": zt, "draft_logits": zd, "uniforms": u,
+            "tokens": block_tokens(anchor, drafts), "planted_len": lens}

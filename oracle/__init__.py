@@ -1,0 +1,41 @@
+"""fp64 CPU oracle for replay-free block verification of a hybrid conv/IIR/attention layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this package: only the tests, the ``smoke()`` check of the entry
+module and the CPU-baseline leg of the benchmark use it.  It shares no code
+with the HIP library or its Python binding.
+
+What it computes follows the EvSpark digest ("EvSpark: Lossless Speculative
+Decoding for Hybrid DNA Foundation Models"): one initial-state block forward
+over the anchor and gamma drafts (Interpretation), lossless acceptance with a
+sampled correction as the next anchor (Figure 1(c)), and slicing of the three
+state classes -- FIR windows, modal IIR state, KV cache -- to the accepted
+index without replay (Figure 1(d)).  The acceptance rules follow the ReaDy
+summary (section 3.1 for greedy verification, section D.2 for the
+speculative-sampling rule).
+
+Everything is plain numpy in float64.  bf16 inputs arrive as uint16 bit
+patterns and are widened exactly.
+
+Pinning (see tests/test_oracle_*.py):
+  * FIR: brute-force full convolution from zero state, delta taps.
+  * IIR: closed form y = h * g with the materialised impulse response,
+    lfilter for one pole, lambda = 0 and beta = 0 special cases.
+  * attention: explicit full softmax matrix per query and torch's
+    scaled_dot_product_attention in fp64, plus invariants.
+  * greedy / rejection acceptance: brute force for forced k, the exact
+    first-token distribution identity, a Monte-Carlo chi-square test.
+  * slicing: the Figure 1(d) worked example; block+slice equals sequential steps.
+  * multi-candidate selection (largest accepted count, lowest index on ties):
+    parity unpinned -- the pages give no rule for choosing among candidates.
+"""
+from .layer import (depthwise_fir, modal_iir, block_attention, verify_block,
+                    as_f64, Layer, SeqState)
+from .acceptance import greedy_accept, rejection_accept, accept_candidates
+from .slicing import slice_state, sequential_steps
+
+__all__ = [
+    "depthwise_fir", "modal_iir", "block_attention", "verify_block", "as_f64",
+    "Layer", "SeqState", "greedy_accept", "rejection_accept", "accept_candidates",
+    "slice_state", "sequential_steps",
+]

@@ -1,0 +1,60 @@
+"""The seeded input generator: determinism, shapes, distributions, planted agreement (CPU)."""
+import numpy as np
+import pytest
+
+import oracle
+from hybrid_conv_iir_amd import synth
+
+
+def test_seeded_and_deterministic():
+    cfg = synth.CONFIGS["c1"]
+    a, b = synth.make_layer(cfg), synth.make_layer(cfg)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+    assert not np.array_equal(synth.make_layer(cfg, seed=1)["w_outer"], a["w_outer"])
+
+
+def test_layer_distributions():
+    cfg = synth.CONFIGS["c2"]
+    p = synth.make_layer(cfg)
+    assert p["w_outer"].shape == (128, 4096) and p["lam"].shape == (4096, 16)
+    assert 0.5 <= p["lam"].min() and p["lam"].max() <= 0.99
+    assert abs(p["beta"].var() - 1 / 16) < 0.003
+    assert abs(p["w_outer"].var() - 1 / 128) < 0.0005
+
+
+def test_bf16_rounding_is_nearest_even():
+    import torch
+    vals = torch.tensor([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5], dtype=torch.float32)
+    bits = synth.bf16_bits(vals)
+    np.testing.assert_array_equal(oracle.as_f64(bits), [1.0, 1.0, 1.0 + 2 ** -6, -2.5])
+
+
+def test_geometric_agreement_planted_length_is_the_greedy_k():
+    cfg = synth.CONFIGS["c3"]
+    lens = []
+    for rnd in range(40):
+        drafts, zt, ln = synth.geometric_agreement(cfg, rnd)
+        k, _, _ = oracle.greedy_accept(zt[0, 0], drafts[0, 0])
+        assert k == ln[0, 0]
+        lens.append(k)
+    assert 0 < np.mean(lens) < cfg.gamma
+
+
+def test_gumbel_drafts_follow_draft_distribution():
+    cfg = synth.scaled(synth.CONFIGS["c1"], vocab=4)
+    z = np.array([[[[0.0, 1.0, -1.0, 0.5]]]], dtype=np.float32)
+    counts = np.zeros(4)
+    for rnd in range(4000):
+        counts[synth.gumbel_drafts(cfg, z, rnd)[0, 0, 0]] += 1
+    p = np.exp(z[0, 0, 0] - z.max())
+    p /= p.sum()
+    assert np.max(np.abs(counts / counts.sum() - p)) < 0.03
+
+
+def test_kv_prefix_cpu_shape_and_moments():
+    cfg = synth.scaled(synth.CONFIGS["c2"], kv_lens=(1000,), heads=2)
+    k = synth.kv_prefix(cfg, 0, "k")
+    assert tuple(k.shape) == (2, 1000, 128)
+    kk = k.float().numpy()
+    assert abs(kk.mean()) < 0.02 and abs(kk.std() - 1) < 0.02
