@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark of the replay-free verify hot path on one MI355X.
+
+A step is one pass of the whole path over one block: verify (short FIR,
+outer FIR, modal IIR scan, split-K causal block attention over the KV
+prefix), accept, and slice.  Default workload: the long-context layer --
+d = 4096, 3/128 FIR taps, 16 poles, 32 heads x 128, a 262144-token bf16 KV
+prefix, gamma = 12 (13 block positions), greedy acceptance with drafts
+agreeing for a Geometric(0.7) prefix.  Inputs are resident in HBM before the
+timed region starts.
+
+Prints ONE JSON line (metric, value = verified block-positions per second,
+roofline of the prefix-attention kernel, CPU oracle baseline, ...).
+
+    python bench.py [--steps K] [--warmup W] [--config c3|c3g6|c2|c4|c5]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+WORKLOAD_NAMES = {
+    "c3": "long-context verify: d=4096, FIR 3/128 taps, 16 poles, 32x128 heads, 262144-token bf16 KV prefix, gamma=12, greedy",
+    "c3g6": "long-context verify: d=4096, FIR 3/128 taps, 16 poles, 32x128 heads, 262144-token bf16 KV prefix, gamma=6, greedy",
+    "c2": "mid-size verify: d=4096, FIR 3/128 taps, 16 poles, 32x128 heads, 8192-token bf16 KV prefix, gamma=12, sampling T=1",
+    "c4": "batched multi-candidate verify: 4 sequences x 4 candidates, KV prefixes 16384/32768/51200/65536, gamma=12, sampling",
+    "c5": "wide layer: d=8192, FIR 3/128 taps, 16 poles, 64x128 heads, 131072-token bf16 KV prefix, gamma=12, greedy",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefix_traffic.json")
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so.7")      # the runtime torch already loaded
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def _events(hip, n):
+    evs = (ctypes.c_void_p * n)()
+    for i in range(n):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs[i] = e
+    return evs
+
+
+def _ms(hip, a, b) -> float:
+    out = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+    return float(out.value)
+
+
+def verify_alg_bytes(cfg, kv_lens) -> int:
+    """Bytes the verify must move: KV prefix once per sequence, block tensors, conv/IIR state and weights."""
+    act = 2 if cfg.act == "bf16" else 4
+    nq = cfg.nb * cfg.nc * cfg.P
+    H, Dh, d, N = cfg.heads, cfg.head_dim, cfg.d, cfg.poles
+    kv = sum(2 * H * L * Dh * act for L in kv_lens)
+    attn_io = 4 * nq * H * Dh * act                                   # q, block k, block v in; o out
+    conv = (nq * d * act                                              # x
+            + cfg.nb * ((cfg.taps_short - 1) * d * act + (cfg.taps_outer - 1) * d * 4 + d * N * 4)  # windows, IIR
+            + (cfg.taps_short + cfg.taps_outer) * d * 4 + 3 * d * N * 4                              # weights
+            + nq * d * 4 + nq * d * N * 4 + nq * d * act)            # f, s, y out
+    return kv + attn_io + conv
+
+
+def prefix_alg_bytes(cfg, kv_lens) -> int:
+    """Per-unit 512 B (one key of one head: Dh bf16 K + Dh bf16 V) x keys x heads, plus the queries."""
+    act = 2 if cfg.act == "bf16" else 4
+    return sum(2 * cfg.heads * L * cfg.head_dim * act for L in kv_lens) + cfg.nb * cfg.nc * cfg.P * cfg.heads * cfg.head_dim * act
+
+
+def _kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("attention.hip", "hci_internal.h"):
+        with open(os.path.join(ROOT, "hybrid_conv_iir_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(cfg_name):
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != _kernel_sha() or t.get("config") != cfg_name:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, case_np, heads):
+    """The fp64 oracle as it stands, timed on this host on a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    layer = oracle.Layer.from_dict(case_np["params"])
+    small, bn, ri = case_np["small"], case_np["blk"], case_np["ri"]
+    b, c = 0, 0
+    x, q, k, v = bn["x"][b, c], bn["q"][b, c][:, heads], bn["k"][b, c][:, heads], bn["v"][b, c][:, heads]
+    st = oracle.SeqState(small["short_win"][b], small["outer_win"][b], small["iir"][b],
+                         [case_np["kpre"]], [case_np["vpre"]])
+    t0 = time.perf_counter()
+    f = oracle.depthwise_fir(x, st.short_win, layer.w_short)
+    g = oracle.depthwise_fir(f, st.outer_win, layer.w_outer)
+    s, y = oracle.modal_iir(g, st.iir, layer.lam, layer.beta, layer.c)
+    t1 = time.perf_counter()
+    oracle.block_attention(q, k, v, st.k_blocks, st.v_blocks)
+    t2 = time.perf_counter()
+    if cfg.mode == "greedy":
+        kk, _, _ = oracle.greedy_accept(ri["target_logits"][b, c], ri["drafts"][b, c])
+    else:
+        kk, _, _ = oracle.rejection_accept(ri["target_logits"][b, c], ri["draft_logits"][b, c], ri["drafts"][b, c],
+                                           ri["uniforms"][b, c], cfg.temperature)
+    t3 = time.perf_counter()
+    oracle.slice_state(st, x, {"f": f, "s": s}, k, v, kk)
+    t4 = time.perf_counter()
+    scale = cfg.heads / len(heads)
+    blocks = cfg.nb * cfg.nc          # the sample is one (sequence, candidate) block
+    est = ((t1 - t0) + (t2 - t1) * scale + (t3 - t2) + (t4 - t3)) * blocks
+    measured = t4 - t0
+    return {
+        "value": round(cfg.nb * cfg.nc * cfg.P / est, 3),
+        "unit": "verified block-positions/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle, one verify->accept->slice of one block with attention over {len(heads)} of "
+                   f"{cfg.heads} heads (timed {measured:.1f} s; attention time scaled x{scale:g} to all heads"
+                   f"{', x%d blocks' % blocks if blocks > 1 else ''})"),
+        "seconds_per_step_est": round(est, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(multi-GPU sharding is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from hybrid_conv_iir_amd import device as dv
+    from hybrid_conv_iir_amd import hci, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    hip = _hip()
+    cfg = synth.CONFIGS[args.config]
+    W, K = args.warmup, args.steps
+    P = cfg.P
+    kv_cap = (cfg.max_kv_len + (W + K + 2) * P + 31) // 32 * 32
+
+    # ---------------------------------------------------------------- inputs (resident before timing)
+    params = synth.make_layer(cfg)
+    small = synth.make_state_small(cfg)
+    tables = synth.make_tables(cfg)
+    anchor = synth.anchors(cfg)
+    ri = synth.round_inputs(cfg, anchor)
+    bn = synth.gather_block(cfg, tables, ri["tokens"])
+    lay = dv.DeviceLayer(cfg, params)
+    st = dv.DeviceState(lay, cfg.nb, kv_cap)
+    st.load_small(small)
+    heads = list(range(min(args.cpu_heads, cfg.heads)))
+    kpre_host = vpre_host = None
+    for b in range(cfg.nb):
+        kp = synth.kv_prefix(cfg, b, "k", device="cuda")
+        vp = synth.kv_prefix(cfg, b, "v", device="cuda")
+        st.write_prefix(b, kp, vp)
+        if b == 0:
+            kpre_host, vpre_host = dv.to_host(kp[heads]), dv.to_host(vp[heads])
+        del kp, vp
+    st.kv_len.copy_(torch.tensor(cfg.kv_lens, dtype=torch.int32))
+    blk = dv.DeviceBlock(lay, cfg.nb, cfg.nc, cfg.gamma)
+    blk.set_inputs(bn["x"], bn["q"], bn["k"], bn["v"])
+    acc = dv.DeviceAccept(cfg.nb, cfg.nc, cfg.gamma, cfg.vocab)
+    acc.set_inputs(ri["target_logits"], ri["drafts"], ri["draft_logits"], ri["uniforms"])
+    mode = hci.GREEDY if cfg.mode == "greedy" else hci.SAMPLE
+    bound = cfg.max_kv_len
+    blk.ensure_workspace(bound + (W + K + 1) * P)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    # ---------------------------------------------------------------- HBM read ceiling (probe)
+    sink = torch.empty(hci.probe_sink_words(), dtype=torch.float32, device="cuda")
+    pe = _events(hip, 2)
+    hci.probe_read(st.k_cache, sink)
+    probe_ms = []
+    for _ in range(5):
+        hip.hipEventRecord(pe[0], sp)
+        hci.probe_read(st.k_cache, sink)
+        hip.hipEventRecord(pe[1], sp)
+        hip.hipEventSynchronize(pe[1])
+        probe_ms.append(_ms(hip, pe[0], pe[1]))
+    probe_gbs = st.k_cache.numel() * 2 / (min(probe_ms) * 1e-3) / 1e9
+
+    # ---------------------------------------------------------------- warm-up
+    def step(evs=None):
+        nonlocal bound
+        if evs is None:
+            dv.verify(lay, st, blk, bound)
+        else:
+            hci.verify_block_timed(lay.c, st.c, blk.c, blk.nb, blk.nc, blk.gamma, bound, blk.ws, evs)
+        dv.accept(acc, mode, cfg.temperature)
+        if evs is not None:
+            hip.hipEventRecord(evs[4], sp)
+        dv.slice_state(lay, st, blk, acc, bound)
+        if evs is not None:
+            hip.hipEventRecord(evs[5], sp)
+        bound += P
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    len_before = dv.to_host(st.kv_len).astype(np.int64)
+
+    # ---------------------------------------------------------------- timed region
+    evsets = [_events(hip, 6) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evsets[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    len_after = dv.to_host(st.kv_len).astype(np.int64)
+
+    ms_step = (t1 - t0) * 1e3 / K
+    conv_ms = [_ms(hip, e[0], e[1]) for e in evsets]
+    prefix_ms = [_ms(hip, e[1], e[2]) for e in evsets]
+    combine_ms = [_ms(hip, e[2], e[3]) for e in evsets]
+    verify_ms = [_ms(hip, e[0], e[3]) for e in evsets]
+    accept_ms = [_ms(hip, e[3], e[4]) for e in evsets]
+    slice_ms = [_ms(hip, e[4], e[5]) for e in evsets]
+    step_dev_ms = [_ms(hip, e[0], e[5]) for e in evsets]
+
+    # mean committed length over the timed steps (the prefix grows by k+1 per step)
+    mean_lens = [int(a) + (int(b) - int(a)) * (K - 1) / (2.0 * K) for a, b in zip(len_before, len_after)]
+    alg_verify = verify_alg_bytes(cfg, mean_lens)
+    alg_prefix = prefix_alg_bytes(cfg, mean_lens)
+    avg_prefix_s = float(np.mean(prefix_ms)) * 1e-3
+    achieved = alg_prefix / avg_prefix_s / 1e9
+    positions = cfg.nb * cfg.nc * P
+    value = positions / (ms_step * 1e-3)
+
+    out = {
+        "metric": "verified block-positions/sec per layer",
+        "value": round(value, 2),
+        "unit": "block-positions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.act == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations and KV, N(0,2) logits; no trained weights)",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "config_id": cfg.name, "nb": cfg.nb, "nc": cfg.nc,
+                   "gamma": cfg.gamma, "kv_len": list(cfg.kv_lens), "d": cfg.d, "heads": cfg.heads,
+                   "head_dim": cfg.head_dim, "parallelism": "single GPU"},
+        "verify_ms": round(float(np.median(verify_ms)), 4),
+        "verify_hbm_GBs": round(alg_verify / (float(np.median(verify_ms)) * 1e-3) / 1e9, 1),
+        "verify_pct_of_8TBs": round(100.0 * alg_verify / (float(np.median(verify_ms)) * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "verify_positions_per_s": round(positions / (float(np.median(verify_ms)) * 1e-3), 1),
+        "breakdown_ms_median": {"conv_iir": round(float(np.median(conv_ms)), 4),
+                                "attn_prefix": round(float(np.median(prefix_ms)), 4),
+                                "attn_combine": round(float(np.median(combine_ms)), 4),
+                                "accept": round(float(np.median(accept_ms)), 4),
+                                "slice": round(float(np.median(slice_ms)), 4),
+                                "step_device": round(float(np.median(step_dev_ms)), 4)},
+        "slice_ms": round(float(np.median(slice_ms)), 4),
+        "hbm_probe_read_GBs": round(probe_gbs, 1),
+        "roofline": {"kernel": "k_attn_prefix_bf16" if cfg.act == "bf16" else "k_attn_prefix_f32",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": _traffic(args.config),
+                     "alg_bytes_per_launch": int(alg_prefix),
+                     "avg_launch_ms": round(avg_prefix_s * 1e3, 4)},
+        "accepted_per_step": [int(x) for x in ((len_after - len_before) // K)],
+    }
+    if not args.no_cpu_baseline:
+        case_np = {"params": params, "small": small, "blk": bn, "ri": ri, "kpre": kpre_host, "vpre": vpre_host}
+        out["cpu_baseline"] = cpu_baseline(cfg, case_np, heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

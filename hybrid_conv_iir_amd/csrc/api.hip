@@ -1,0 +1,196 @@
+// Host side of the C ABI: argument validation, launch planning, launches.
+// Every check runs before the first launch, so a rejected call enqueues
+// nothing; no call allocates, frees, synchronises or keeps a pointer.
+#include "hci_internal.h"
+
+#include <atomic>
+
+namespace hci {
+
+static std::atomic<int> g_cu_cache[64];
+
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < 64) {
+        const int c = g_cu_cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev >= 0 && dev < 64) g_cu_cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static int check_layer(const hci_layer* L) {
+    if (!L) return HCI_EINVAL;
+    if (L->d < 1 || L->taps_short < 1 || L->taps_outer < 1 || L->poles < 1 || L->heads < 1 || L->head_dim < 1)
+        return HCI_EINVAL;
+    if (L->act_dtype != HCI_F32 && L->act_dtype != HCI_BF16) return HCI_EINVAL;
+    if (L->poles > 64 || L->heads > 65535) return HCI_EUNSUPPORTED;
+    if (L->act_dtype == HCI_BF16 && L->head_dim != 64 && L->head_dim != 128) return HCI_EUNSUPPORTED;
+    if (L->act_dtype == HCI_F32 && (L->head_dim % 32 != 0 || L->head_dim > 128)) return HCI_EUNSUPPORTED;
+    if (!L->w_short || !L->w_outer || !L->lambda || !L->beta || !L->c) return HCI_EINVAL;
+    return HCI_OK;
+}
+
+static int check_state(const hci_layer* L, const hci_state* S, int nb, long long need_rows) {
+    if (!S) return HCI_EINVAL;
+    if (S->kv_cap < kTile || S->kv_cap % kTile != 0) return HCI_EINVAL;
+    if (!S->k_cache || !S->v_cache || !S->kv_len || !S->iir) return HCI_EINVAL;
+    if (L->taps_short > 1 && !S->short_win) return HCI_EINVAL;
+    if (L->taps_outer > 1 && !S->outer_win) return HCI_EINVAL;
+    if (!aligned(S->k_cache, 16) || !aligned(S->v_cache, 16)) return HCI_EINVAL;
+    if (nb < 1 || nb > 65535) return HCI_EINVAL;
+    if (need_rows > S->kv_cap) return HCI_ECAPACITY;
+    return HCI_OK;
+}
+
+static int check_block(const hci_block* blk) {
+    if (!blk || !blk->x || !blk->q || !blk->k || !blk->v || !blk->f || !blk->s || !blk->y || !blk->o)
+        return HCI_EINVAL;
+    if (!aligned(blk->q, 16)) return HCI_EINVAL;
+    return HCI_OK;
+}
+
+}  // namespace hci
+
+using namespace hci;
+
+extern "C" {
+
+const char* hci_status_string(int status) {
+    switch (status) {
+        case HCI_OK: return "HCI_OK";
+        case HCI_EINVAL: return "HCI_EINVAL: invalid argument";
+        case HCI_ECAPACITY: return "HCI_ECAPACITY: KV cache capacity exceeded";
+        case HCI_EUNSUPPORTED: return "HCI_EUNSUPPORTED: shape or dtype not supported";
+        case HCI_EDEVICE: return "HCI_EDEVICE: HIP launch error";
+        case HCI_EWORKSPACE: return "HCI_EWORKSPACE: workspace missing or too small";
+        default: return "HCI: unknown status";
+    }
+}
+
+int hci_version(void) { return 100; }
+
+size_t hci_verify_workspace_bytes(const hci_layer* L, int nb, int nc, int gamma, int max_kv_len) {
+    if (check_layer(L) != HCI_OK || nb < 1 || nc < 1 || gamma < 0 || max_kv_len < 0) return 0;
+    return plan_attention(L, nb, nc, gamma, max_kv_len, device_cu_count()).bytes;
+}
+
+static int verify_impl(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                       int nb, int nc, int gamma, int max_kv_len,
+                       void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
+    int rc = check_layer(L);
+    if (rc) return rc;
+    if (nc < 1 || gamma < 0 || max_kv_len < 0) return HCI_EINVAL;
+    const int P = gamma + 1;
+    if (P > 64 || (long long)nc * P > 64) return HCI_EUNSUPPORTED;
+    rc = check_state(L, S, nb, (long long)max_kv_len + gamma + 1);
+    if (rc) return rc;
+    rc = check_block(blk);
+    if (rc) return rc;
+    const AttnPlan plan = plan_attention(L, nb, nc, gamma, max_kv_len, device_cu_count());
+    if (plan.bytes > 0 && (!ws || ws_bytes < plan.bytes || !aligned(ws, 256))) return HCI_EWORKSPACE;
+
+    auto mark = [&](int i) { return (ev && ev[i]) ? hipEventRecord(ev[i], stream) : hipSuccess; };
+    if (mark(0) != hipSuccess) return HCI_EDEVICE;
+    if (launch_conv_iir(L, S, blk, nb, nc, P, stream) != hipSuccess) return HCI_EDEVICE;
+    if (mark(1) != hipSuccess) return HCI_EDEVICE;
+    if (launch_attention(L, S, blk, nb, nc, P, plan, ws, stream, ev ? &ev[2] : nullptr) != hipSuccess)
+        return HCI_EDEVICE;
+    if (mark(3) != hipSuccess) return HCI_EDEVICE;
+    return HCI_OK;
+}
+
+int hci_verify_block(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                     int nb, int nc, int gamma, int max_kv_len,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+    return verify_impl(L, S, blk, nb, nc, gamma, max_kv_len, ws, ws_bytes, stream, nullptr);
+}
+
+int hci_verify_block_timed(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                           int nb, int nc, int gamma, int max_kv_len,
+                           void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+    if (!events) return HCI_EINVAL;
+    return verify_impl(L, S, blk, nb, nc, gamma, max_kv_len, ws, ws_bytes, stream, events);
+}
+
+int hci_accept(int mode, int nb, int nc, int gamma, int vocab, float temperature,
+               const float* target_logits, const float* draft_logits,
+               const int32_t* draft_tokens, const double* uniforms,
+               int32_t* n_accepted, int32_t* next_token, int32_t* best_cand,
+               double* margin, hipStream_t stream) {
+    if (mode != HCI_GREEDY && mode != HCI_SAMPLE) return HCI_EINVAL;
+    if (nb < 1 || nb > 2147483647 || nc < 1 || nc > 64 || gamma < 0 || vocab < 1) return HCI_EINVAL;
+    if (vocab > 65536) return HCI_EUNSUPPORTED;
+    if (!target_logits || !n_accepted || !next_token) return HCI_EINVAL;
+    if (gamma > 0 && !draft_tokens) return HCI_EINVAL;
+    if (mode == HCI_SAMPLE) {
+        if (!(temperature > 0.f) || temperature == INFINITY) return HCI_EINVAL;
+        if (!uniforms || (gamma > 0 && !draft_logits)) return HCI_EINVAL;
+    }
+    if (launch_accept(mode, nb, nc, gamma, vocab, temperature, target_logits, draft_logits, draft_tokens,
+                      uniforms, n_accepted, next_token, best_cand, margin, stream) != hipSuccess)
+        return HCI_EDEVICE;
+    return HCI_OK;
+}
+
+int hci_slice_state(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                    int nb, int nc, int gamma, int max_kv_len,
+                    const int32_t* n_accepted, const int32_t* best_cand, hipStream_t stream) {
+    int rc = check_layer(L);
+    if (rc) return rc;
+    if (nc < 1 || gamma < 0 || max_kv_len < 0 || !n_accepted) return HCI_EINVAL;
+    if (nc > 1 && !best_cand) return HCI_EINVAL;
+    if (gamma + 1 > 64 || (long long)nc * (gamma + 1) > 64) return HCI_EUNSUPPORTED;
+    rc = check_state(L, S, nb, (long long)max_kv_len + gamma + 1);
+    if (rc) return rc;
+    if (!blk || !blk->x || !blk->k || !blk->v || !blk->f || !blk->s) return HCI_EINVAL;
+    if (launch_slice(L, S, blk, nb, nc, gamma + 1, n_accepted, best_cand, stream) != hipSuccess)
+        return HCI_EDEVICE;
+    return HCI_OK;
+}
+
+size_t hci_kv_cache_elems(const hci_layer* L, int nb, int kv_cap) {
+    if (check_layer(L) != HCI_OK || nb < 1 || kv_cap < kTile || kv_cap % kTile) return 0;
+    return (size_t)nb * L->heads * (size_t)kv_cap * L->head_dim;
+}
+
+static int kv_access(const hci_layer* L, const hci_state* S, int nb, int b, int row0, int nrows,
+                     const void* a, const void* c, bool write, hipStream_t stream, void* oa, void* oc) {
+    int rc = check_layer(L);
+    if (rc) return rc;
+    if (!S || !S->k_cache || !S->v_cache || S->kv_cap < kTile || S->kv_cap % kTile) return HCI_EINVAL;
+    if (nb < 1 || b < 0 || b >= nb || row0 < 0 || nrows < 0) return HCI_EINVAL;
+    if ((long long)row0 + nrows > S->kv_cap) return HCI_ECAPACITY;
+    if (write ? (!a || !c) : (!oa || !oc)) return HCI_EINVAL;
+    if (launch_kv_copy(L, S, b, row0, nrows, a, c, oa, oc, write, stream) != hipSuccess) return HCI_EDEVICE;
+    return HCI_OK;
+}
+
+int hci_kv_write(const hci_layer* L, const hci_state* S, int nb, int b, int row0, int nrows,
+                 const void* k_rows, const void* v_rows, hipStream_t stream) {
+    return kv_access(L, S, nb, b, row0, nrows, k_rows, v_rows, true, stream, nullptr, nullptr);
+}
+
+int hci_kv_read(const hci_layer* L, const hci_state* S, int nb, int b, int row0, int nrows,
+                void* k_rows, void* v_rows, hipStream_t stream) {
+    return kv_access(L, S, nb, b, row0, nrows, nullptr, nullptr, false, stream, k_rows, v_rows);
+}
+
+int hci_probe_sink_words(void) { return probe_blocks(); }
+
+int hci_probe_read(const void* src, size_t bytes, float* sink, hipStream_t stream) {
+    if (!src || !sink || bytes % 16 || !aligned(src, 16)) return HCI_EINVAL;
+    return launch_probe_read(src, bytes, sink, stream) == hipSuccess ? HCI_OK : HCI_EDEVICE;
+}
+
+int hci_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+    if (!src || !dst || bytes % 16 || !aligned(src, 16) || !aligned(dst, 16)) return HCI_EINVAL;
+    return launch_probe_copy(dst, src, bytes, stream) == hipSuccess ? HCI_OK : HCI_EDEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Internal helpers shared by the libhci kernels and host code (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "hci.h"
+
+namespace hci {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = HCI_KV_TILE;   // keys per KV tile
+
+// ------------------------------------------------------------------ bf16
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <int ACT> struct Act;
+template <> struct Act<HCI_F32> {
+    typedef float T;
+    __device__ static __forceinline__ float load(const T* p, size_t i) { return p[i]; }
+    __device__ static __forceinline__ void store(T* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Act<HCI_BF16> {
+    typedef uint16_t T;
+    __device__ static __forceinline__ float load(const T* p, size_t i) { return bf2f(p[i]); }
+    __device__ static __forceinline__ void store(T* p, size_t i, float v) { p[i] = f2bf(v); }
+};
+
+// ------------------------------------------------------------- KV layout
+//
+// A cache holds, per (sequence, head), kv_cap/32 tiles of 32 keys x Dh.
+// Inside a tile the element order is the register order of the attention
+// kernel's matrix-core operands, so that every wave-wide 16-byte load reads
+// one contiguous kilobyte:
+//   K: [u<2][j<Dh/32][g<4][m<16][e<8]  holds K[16u+m][32j+8g+e]
+//   V: [t<Dh/16][g<4][m<16][i<8]       holds V[kmap(g,i)][16t+m]
+// with kmap(g,i) = 4g+i for i<4 and 16+4g+(i-4) for i>=4: the keys a lane
+// holds after the score product (4 per 16-key half) are the keys it must
+// supply to the value product.
+
+__host__ __device__ __forceinline__ size_t k_tile_offset(int w, int dd, int Dh) {
+    const int u = w >> 4, m = w & 15;
+    const int j = dd >> 5, g = (dd >> 3) & 3, e = dd & 7;
+    return ((((size_t)(u * (Dh >> 5) + j) * 4 + g) * 16 + m) * 8 + e);
+}
+
+__host__ __device__ __forceinline__ size_t v_tile_offset(int w, int dd, int Dh) {
+    (void)Dh;
+    const int half = w >> 4, r = w & 15;
+    const int g = r >> 2, i = (r & 3) + 4 * half;
+    const int t = dd >> 4, m = dd & 15;
+    return ((((size_t)t * 4 + g) * 16 + m) * 8 + i);
+}
+
+// element offset of (row, dd) inside one (sequence, head) cache slab
+__host__ __device__ __forceinline__ size_t k_elem(int row, int dd, int Dh) {
+    return (size_t)(row >> 5) * kTile * Dh + k_tile_offset(row & 31, dd, Dh);
+}
+__host__ __device__ __forceinline__ size_t v_elem(int row, int dd, int Dh) {
+    return (size_t)(row >> 5) * kTile * Dh + v_tile_offset(row & 31, dd, Dh);
+}
+
+// ----------------------------------------------------------- launch API
+
+// Split-K plan for the attention prefix: the same function sizes the
+// workspace and launches the kernels, so both always agree.
+struct AttnPlan {
+    int nq;            // queries per sequence = nc * P
+    int chunk_tiles;   // tiles per split-K chunk
+    int n_chunks;      // chunks per (sequence, head), from max_kv_len
+    size_t part_o_elems, part_ml_elems;
+    size_t bytes;      // workspace bytes (256-aligned sections)
+};
+AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_kv_len, int num_cus);
+int device_cu_count();
+
+hipError_t launch_conv_iir(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                           int nb, int nc, int P, hipStream_t st);
+// after_prefix (may be null): an event recorded right after the prefix kernel
+hipError_t launch_attention(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                            int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st,
+                            hipEvent_t* after_prefix);
+hipError_t launch_accept(int mode, int nb, int nc, int gamma, int V, float temperature,
+                         const float* zt, const float* zd, const int32_t* drafts, const double* u,
+                         int32_t* n_acc, int32_t* next, int32_t* best, double* margin, hipStream_t st);
+hipError_t launch_slice(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                        int nb, int nc, int P, const int32_t* n_acc, const int32_t* best, hipStream_t st);
+hipError_t launch_kv_copy(const hci_layer* L, const hci_state* S, int b, int row0, int nrows,
+                          const void* k_rows, const void* v_rows, void* k_out, void* v_out,
+                          bool write, hipStream_t st);
+hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t st);
+hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
+int probe_blocks();
+
+}  // namespace hci

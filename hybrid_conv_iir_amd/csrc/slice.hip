@@ -1,0 +1,186 @@
+// State slicing to the accepted index (EvSpark digest, Figure 1(d) and
+// Interpretation): the three state classes are restored by selecting values
+// the block forward already produced -- no target computation is replayed.
+//
+// k_slice reads k and the winning candidate c* on the device, so no host
+// synchronisation sits between acceptance and slicing.  Workgroup roles
+// (blockIdx.y):
+//   0  FIR windows: 64 channels per workgroup; the new window rows are first
+//      gathered into LDS, then written back (the update is in place)
+//   1  IIR state <- s_k of c*
+//   2  KV rows kv_len .. kv_len+k <- block k/v rows 0..k of c* (tiled layout)
+// k_slice_len then advances kv_len; it runs after every role of k_slice has
+// read the old length (stream order).
+#include "hci_internal.h"
+
+namespace hci {
+
+constexpr int kSliceCG = 64;         // channels per window workgroup
+constexpr int kSliceWinMax = 128;    // window rows staged in LDS per pass
+
+__device__ __forceinline__ void winner(const int32_t* n_acc, const int32_t* best, int b, int nc,
+                                       int gamma, int& cstar, int& k) {
+    int c = (best != nullptr && nc > 1) ? best[b] : 0;
+    c = c < 0 ? 0 : (c >= nc ? nc - 1 : c);
+    int kk = n_acc[(size_t)b * nc + c];
+    kk = kk < 0 ? 0 : (kk > gamma ? gamma : kk);
+    cstar = c;
+    k = kk;
+}
+
+template <int ACT>
+__device__ void window_update(typename Act<ACT>::T* win, const typename Act<ACT>::T* blk_rows,
+                              int W, int d, int k, int ch0, float (*stage)[kSliceCG])
+{
+    // new[r] = concat(old[0..W), rows[0..k])[k+1+r] for r < W.  Rows are
+    // processed in ascending chunks; chunk [r0, r0+128) reads old rows at or
+    // above r0+k+1, which no earlier chunk has overwritten.
+    const int tid = threadIdx.x, cl = tid & (kSliceCG - 1), part = tid >> 6;
+    const int ch = ch0 + cl;
+    for (int r0 = 0; r0 < W; r0 += kSliceWinMax) {
+        const int r1 = min(W, r0 + kSliceWinMax);
+        for (int r = r0 + part; r < r1; r += 4) {
+            const int m = k + 1 + r;
+            float v = 0.f;
+            if (ch < d) v = (m < W) ? Act<ACT>::load(win, (size_t)m * d + ch)
+                                    : Act<ACT>::load(blk_rows, (size_t)(m - W) * d + ch);
+            stage[r - r0][cl] = v;
+        }
+        __syncthreads();
+        for (int r = r0 + part; r < r1; r += 4)
+            if (ch < d) Act<ACT>::store(win, (size_t)r * d + ch, stage[r - r0][cl]);
+        __syncthreads();
+    }
+}
+
+template <int ACT>
+__global__ __launch_bounds__(256) void k_slice(
+    typename Act<ACT>::T* __restrict__ short_win, float* __restrict__ outer_win,
+    float* __restrict__ iir, typename Act<ACT>::T* __restrict__ kc, typename Act<ACT>::T* __restrict__ vc,
+    const int32_t* __restrict__ kv_len, const typename Act<ACT>::T* __restrict__ x,
+    const float* __restrict__ f, const float* __restrict__ s,
+    const typename Act<ACT>::T* __restrict__ kb, const typename Act<ACT>::T* __restrict__ vb,
+    const int32_t* __restrict__ n_acc, const int32_t* __restrict__ best,
+    int d, int Ts, int To, int N, int H, int DH, int kv_cap, int nc, int gamma)
+{
+    __shared__ float stage[kSliceWinMax][kSliceCG];
+    const int b = blockIdx.z, role = blockIdx.y;
+    const int P = gamma + 1;
+    int cstar, k;
+    winner(n_acc, best, b, nc, gamma, cstar, k);
+    const size_t blk = (size_t)b * nc + cstar;
+
+    if (role == 0) {
+        const int ch0 = blockIdx.x * kSliceCG;
+        if (ch0 >= d) return;
+        if (Ts > 1)
+            window_update<ACT>(short_win + (size_t)b * (Ts - 1) * d, x + blk * P * d, Ts - 1, d, k, ch0, stage);
+        if (To > 1)
+            window_update<HCI_F32>(outer_win + (size_t)b * (To - 1) * d, f + blk * P * d, To - 1, d, k, ch0, stage);
+    } else if (role == 1) {
+        const size_t n = (size_t)d * N;
+        const float* src = s + (blk * P + k) * n;
+        float* dst = iir + (size_t)b * n;
+        for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
+            dst[e] = src[e];
+    } else {
+        int L = kv_len[b];
+        L = L < 0 ? 0 : L;
+        const size_t per_row = (size_t)H * DH;
+        const size_t n = (size_t)(k + 1) * per_row;
+        const size_t slab = (size_t)kv_cap * DH;
+        for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+            const int i = (int)(e / per_row);
+            const int h = (int)((e / DH) % H);
+            const int dd = (int)(e % DH);
+            const int row = L + i;
+            if (row >= kv_cap) continue;
+            const size_t src = ((blk * P + i) * H + h) * DH + dd;
+            const size_t base = ((size_t)b * H + h) * slab;
+            kc[base + k_elem(row, dd, DH)] = kb[src];
+            vc[base + v_elem(row, dd, DH)] = vb[src];
+        }
+    }
+}
+
+__global__ void k_slice_len(int32_t* __restrict__ kv_len, const int32_t* __restrict__ n_acc,
+                            const int32_t* __restrict__ best, int nb, int nc, int gamma, int kv_cap)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nb) return;
+    int cstar, k;
+    winner(n_acc, best, b, nc, gamma, cstar, k);
+    int L = kv_len[b] + k + 1;
+    kv_len[b] = L > kv_cap ? kv_cap : L;
+}
+
+hipError_t launch_slice(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                        int nb, int nc, int P, const int32_t* n_acc, const int32_t* best, hipStream_t st)
+{
+    const int gamma = P - 1;
+    const int win_blocks = (L->d + kSliceCG - 1) / kSliceCG;
+    dim3 grid(win_blocks < 64 ? 64 : win_blocks, 3, nb), block(256);
+    if (L->act_dtype == HCI_BF16) {
+        hipLaunchKernelGGL(k_slice<HCI_BF16>, grid, block, 0, st,
+            (uint16_t*)S->short_win, S->outer_win, S->iir, (uint16_t*)S->k_cache, (uint16_t*)S->v_cache,
+            S->kv_len, (const uint16_t*)blk->x, blk->f, blk->s, (const uint16_t*)blk->k,
+            (const uint16_t*)blk->v, n_acc, best, L->d, L->taps_short, L->taps_outer, L->poles,
+            L->heads, L->head_dim, S->kv_cap, nc, gamma);
+    } else {
+        hipLaunchKernelGGL(k_slice<HCI_F32>, grid, block, 0, st,
+            (float*)S->short_win, S->outer_win, S->iir, (float*)S->k_cache, (float*)S->v_cache,
+            S->kv_len, (const float*)blk->x, blk->f, blk->s, (const float*)blk->k,
+            (const float*)blk->v, n_acc, best, L->d, L->taps_short, L->taps_outer, L->poles,
+            L->heads, L->head_dim, S->kv_cap, nc, gamma);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_slice_len, dim3((nb + 63) / 64), dim3(64), 0, st,
+                       S->kv_len, n_acc, best, nb, nc, gamma, S->kv_cap);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- KV rows
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_kv_copy(T* __restrict__ kc, T* __restrict__ vc,
+                                                 const T* __restrict__ ksrc, const T* __restrict__ vsrc,
+                                                 T* __restrict__ kdst, T* __restrict__ vdst,
+                                                 int b, int row0, int nrows, int H, int DH, int kv_cap, int write)
+{
+    const size_t n = (size_t)H * nrows * DH;
+    const size_t slab = (size_t)kv_cap * DH;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+        const int h = (int)(e / ((size_t)nrows * DH));
+        const int r = (int)((e / DH) % nrows);
+        const int dd = (int)(e % DH);
+        const size_t base = ((size_t)b * H + h) * slab;
+        const size_t ko = base + k_elem(row0 + r, dd, DH), vo = base + v_elem(row0 + r, dd, DH);
+        if (write) { kc[ko] = ksrc[e]; vc[vo] = vsrc[e]; }
+        else { kdst[e] = kc[ko]; vdst[e] = vc[vo]; }
+    }
+}
+
+hipError_t launch_kv_copy(const hci_layer* L, const hci_state* S, int b, int row0, int nrows,
+                          const void* k_rows, const void* v_rows, void* k_out, void* v_out,
+                          bool write, hipStream_t st)
+{
+    const size_t n = (size_t)L->heads * nrows * L->head_dim;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks == 0) return hipSuccess;
+    if (L->act_dtype == HCI_BF16) {
+        hipLaunchKernelGGL(k_kv_copy<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st,
+                           (uint16_t*)S->k_cache, (uint16_t*)S->v_cache, (const uint16_t*)k_rows,
+                           (const uint16_t*)v_rows, (uint16_t*)k_out, (uint16_t*)v_out, b, row0, nrows,
+                           L->heads, L->head_dim, S->kv_cap, write ? 1 : 0);
+    } else {
+        hipLaunchKernelGGL(k_kv_copy<float>, dim3((unsigned)blocks), dim3(256), 0, st,
+                           (float*)S->k_cache, (float*)S->v_cache, (const float*)k_rows,
+                           (const float*)v_rows, (float*)k_out, (float*)v_out, b, row0, nrows,
+                           L->heads, L->head_dim, S->kv_cap, write ? 1 : 0);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hci

@@ -1,0 +1,214 @@
+"""Python binding of libhci (ctypes): argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, checks
+their dtype / shape / contiguity against the C ABI (include/hci.h), and
+passes raw pointers and the current HIP stream.  All arithmetic happens in
+the HIP kernels; if the library is missing this module raises on import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhci.so")
+
+OK, EINVAL, ECAPACITY, EUNSUPPORTED, EDEVICE, EWORKSPACE = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+GREEDY, SAMPLE = 0, 1
+KV_TILE = 32
+
+
+class HciError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {_lib.hci_status_string(status).decode()} ({status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libhci.so not built at {LIB_PATH}; run `python -m hybrid_conv_iir_amd.build`")
+    return ctypes.CDLL(LIB_PATH)
+
+
+_lib = _load()
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("d", _i), ("taps_short", _i), ("taps_outer", _i), ("poles", _i), ("heads", _i),
+                ("head_dim", _i), ("act_dtype", _i), ("w_short", _p), ("w_outer", _p), ("lambda_", _p),
+                ("beta", _p), ("c", _p)]
+
+
+class State(ctypes.Structure):
+    _fields_ = [("kv_cap", _i), ("short_win", _p), ("outer_win", _p), ("iir", _p), ("k_cache", _p),
+                ("v_cache", _p), ("kv_len", _p)]
+
+
+class Block(ctypes.Structure):
+    _fields_ = [("x", _p), ("q", _p), ("k", _p), ("v", _p), ("f", _p), ("s", _p), ("y", _p), ("o", _p)]
+
+
+EXPORTS = {
+    "hci_status_string": (ctypes.c_char_p, [_i]),
+    "hci_version": (_i, []),
+    "hci_verify_workspace_bytes": (_sz, [ctypes.POINTER(Layer), _i, _i, _i, _i]),
+    "hci_verify_block": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), ctypes.POINTER(Block),
+                              _i, _i, _i, _i, _p, _sz, _p]),
+    "hci_verify_block_timed": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), ctypes.POINTER(Block),
+                                    _i, _i, _i, _i, _p, _sz, _p, _p]),
+    "hci_accept": (_i, [_i, _i, _i, _i, _i, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "hci_slice_state": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), ctypes.POINTER(Block),
+                             _i, _i, _i, _i, _p, _p, _p]),
+    "hci_kv_cache_elems": (_sz, [ctypes.POINTER(Layer), _i, _i]),
+    "hci_kv_write": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), _i, _i, _i, _i, _p, _p, _p]),
+    "hci_kv_read": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), _i, _i, _i, _i, _p, _p, _p]),
+    "hci_probe_read": (_i, [_p, _sz, _p, _p]),
+    "hci_probe_sink_words": (_i, []),
+    "hci_probe_copy": (_i, [_p, _p, _sz, _p]),
+}
+for _name, (_res, _args) in EXPORTS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != OK:
+        raise HciError(rc, where)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "") -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def act_torch_dtype(act: int) -> torch.dtype:
+    return torch.bfloat16 if act == BF16 else torch.float32
+
+
+# ------------------------------------------------------------------ structs
+
+def make_layer(d, taps_short, taps_outer, poles, heads, head_dim, act, w_short, w_outer, lam, beta, c) -> Layer:
+    f32 = torch.float32
+    return Layer(d, taps_short, taps_outer, poles, heads, head_dim, act,
+                 _ptr(w_short, f32, "w_short"), _ptr(w_outer, f32, "w_outer"), _ptr(lam, f32, "lambda"),
+                 _ptr(beta, f32, "beta"), _ptr(c, f32, "c"))
+
+
+def make_state(act, kv_cap, short_win, outer_win, iir, k_cache, v_cache, kv_len) -> State:
+    at = act_torch_dtype(act)
+    return State(kv_cap, _ptr(short_win, at, "short_win"), _ptr(outer_win, torch.float32, "outer_win"),
+                 _ptr(iir, torch.float32, "iir"), _ptr(k_cache, at, "k_cache"), _ptr(v_cache, at, "v_cache"),
+                 _ptr(kv_len, torch.int32, "kv_len"))
+
+
+def make_block(act, x, q, k, v, f, s, y, o) -> Block:
+    at = act_torch_dtype(act)
+    return Block(_ptr(x, at, "x"), _ptr(q, at, "q"), _ptr(k, at, "k"), _ptr(v, at, "v"),
+                 _ptr(f, torch.float32, "f"), _ptr(s, torch.float32, "s"), _ptr(y, at, "y"), _ptr(o, at, "o"))
+
+
+# ------------------------------------------------------------------ calls
+
+def version() -> int:
+    return _lib.hci_version()
+
+
+def status_string(status: int) -> str:
+    return _lib.hci_status_string(status).decode()
+
+
+def verify_workspace_bytes(layer: Layer, nb: int, nc: int, gamma: int, max_kv_len: int) -> int:
+    return _lib.hci_verify_workspace_bytes(ctypes.byref(layer), nb, nc, gamma, max_kv_len)
+
+
+def verify_block(layer: Layer, state: State, block: Block, nb: int, nc: int, gamma: int, max_kv_len: int,
+                 ws: Optional[torch.Tensor], stream=None) -> None:
+    wsp = _ptr(ws, None, "ws") if ws is not None else None
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(_lib.hci_verify_block(ctypes.byref(layer), ctypes.byref(state), ctypes.byref(block), nb, nc, gamma,
+                                 max_kv_len, wsp, nbytes, _stream(stream)), "hci_verify_block")
+
+
+def verify_block_timed(layer: Layer, state: State, block: Block, nb: int, nc: int, gamma: int, max_kv_len: int,
+                       ws: Optional[torch.Tensor], events, stream=None) -> None:
+    """events: a ctypes array of 4 hipEvent_t handles created by the caller."""
+    wsp = _ptr(ws, None, "ws") if ws is not None else None
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(_lib.hci_verify_block_timed(ctypes.byref(layer), ctypes.byref(state), ctypes.byref(block), nb, nc, gamma,
+                                       max_kv_len, wsp, nbytes, _stream(stream), ctypes.cast(events, _p)),
+           "hci_verify_block_timed")
+
+
+def accept(mode: int, nb: int, nc: int, gamma: int, vocab: int, temperature: float,
+           target_logits, draft_logits, draft_tokens, uniforms,
+           n_accepted, next_token, best_cand=None, margin=None, stream=None) -> None:
+    _check(_lib.hci_accept(mode, nb, nc, gamma, vocab, float(temperature),
+                           _ptr(target_logits, torch.float32, "target_logits"),
+                           _ptr(draft_logits, torch.float32, "draft_logits"),
+                           _ptr(draft_tokens, torch.int32, "draft_tokens"),
+                           _ptr(uniforms, torch.float64, "uniforms"),
+                           _ptr(n_accepted, torch.int32, "n_accepted"), _ptr(next_token, torch.int32, "next_token"),
+                           _ptr(best_cand, torch.int32, "best_cand"), _ptr(margin, torch.float64, "margin"),
+                           _stream(stream)), "hci_accept")
+
+
+def slice_state(layer: Layer, state: State, block: Block, nb: int, nc: int, gamma: int, max_kv_len: int,
+                n_accepted, best_cand=None, stream=None) -> None:
+    _check(_lib.hci_slice_state(ctypes.byref(layer), ctypes.byref(state), ctypes.byref(block), nb, nc, gamma,
+                                max_kv_len, _ptr(n_accepted, torch.int32, "n_accepted"),
+                                _ptr(best_cand, torch.int32, "best_cand"), _stream(stream)), "hci_slice_state")
+
+
+def kv_cache_elems(layer: Layer, nb: int, kv_cap: int) -> int:
+    return _lib.hci_kv_cache_elems(ctypes.byref(layer), nb, kv_cap)
+
+
+def kv_write(layer: Layer, state: State, nb: int, b: int, row0: int, k_rows, v_rows, stream=None) -> None:
+    nrows = k_rows.shape[1]
+    _check(_lib.hci_kv_write(ctypes.byref(layer), ctypes.byref(state), nb, b, row0, nrows,
+                             _ptr(k_rows, None, "k_rows"), _ptr(v_rows, None, "v_rows"), _stream(stream)),
+           "hci_kv_write")
+
+
+def kv_read(layer: Layer, state: State, nb: int, b: int, row0: int, k_rows, v_rows, stream=None) -> None:
+    nrows = k_rows.shape[1]
+    _check(_lib.hci_kv_read(ctypes.byref(layer), ctypes.byref(state), nb, b, row0, nrows,
+                            _ptr(k_rows, None, "k_rows"), _ptr(v_rows, None, "v_rows"), _stream(stream)),
+           "hci_kv_read")
+
+
+def probe_sink_words() -> int:
+    return _lib.hci_probe_sink_words()
+
+
+def probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    _check(_lib.hci_probe_read(_ptr(src, None, "src"), src.numel() * src.element_size(),
+                               _ptr(sink, torch.float32, "sink"), _stream(stream)), "hci_probe_read")
+
+
+def probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    _check(_lib.hci_probe_copy(_ptr(dst, None, "dst"), _ptr(src, None, "src"), src.numel() * src.element_size(),
+                               _stream(stream)), "hci_probe_copy")

@@ -1,0 +1,247 @@
+/*
+ * hci.h -- C ABI of libhci: replay-free block verification for one hybrid
+ * convolutional-recurrent-attention layer on AMD MI355X (gfx950).
+ *
+ * The method is the one summarised in "EvSpark: Lossless Speculative Decoding
+ * for Hybrid DNA Foundation Models" (ai4snews digest): the target verifies the
+ * old anchor and gamma drafts in ONE initial-state block forward
+ * (Interpretation; Figure 1(c)), decides losslessly how many drafts to keep
+ * (Figure 1(c): a sampled correction becomes the next anchor), and then
+ * restores all three state classes -- finite FIR windows, modal IIR state,
+ * attention KV cache -- by selecting retained intermediate values instead of
+ * replaying the accepted tokens (Figure 1(d); Interpretation).  The acceptance
+ * rules are the greedy rule of the ReaDy summary section 3.1 and the
+ * speculative-sampling rule of its section D.2.
+ *
+ * General conventions (all calls):
+ *  - Every pointer is a DEVICE pointer unless said otherwise, owned by the
+ *    caller, and must stay valid until the work enqueued on `stream` has run.
+ *    The library never allocates, frees or keeps a pointer after returning.
+ *  - Every call is asynchronous on `stream` and never synchronises the host.
+ *  - Return value: HCI_OK (0) or a negative HCI_E* code.  All argument checks
+ *    run on the host before anything is enqueued, so a failed call enqueues
+ *    nothing.  HCI_EDEVICE reports a launch error from the HIP runtime.
+ *  - Sizes: nb sequences, nc candidate blocks per sequence, gamma drafts,
+ *    P = gamma + 1 block positions (position 0 is the anchor), d channels,
+ *    Ts / To short / outer FIR taps, N poles per channel, H heads of Dh,
+ *    V vocabulary entries.  "act" is the activation dtype of the layer
+ *    (HCI_F32 or HCI_BF16); bf16 values are raw 16-bit patterns.
+ *  - Arrays are dense, row-major in the order their dimensions are listed.
+ */
+#ifndef HCI_H
+#define HCI_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+#define HCI_OK            0
+#define HCI_EINVAL       -1  /* null/misaligned pointer, bad dimension, bad mode */
+#define HCI_ECAPACITY    -2  /* max_kv_len + gamma + 1 > kv_cap */
+#define HCI_EUNSUPPORTED -3  /* dtype or shape this build has no kernel for */
+#define HCI_EDEVICE      -4  /* HIP runtime reported an error at launch */
+#define HCI_EWORKSPACE   -5  /* workspace missing or smaller than required */
+
+#define HCI_F32  0
+#define HCI_BF16 1
+
+#define HCI_GREEDY 0
+#define HCI_SAMPLE 1
+
+/* Rows of the KV cache are grouped in tiles of this many keys. */
+#define HCI_KV_TILE 32
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* hci_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int hci_version(void);
+
+/* -------------------------------------------------------------- structures */
+
+/* Fixed per-layer parameters.  All weight arrays are fp32 on the device.
+ *   w_short [Ts][d]   short depthwise FIR taps, w_short[j] multiplies lag j
+ *   w_outer [To][d]   outer depthwise FIR taps, same convention
+ *   lambda, beta, c [d][N]   modal IIR poles, input gains and readout gains:
+ *       s_i = lambda * s_{i-1} + beta * g_i,   y_i = sum_n c * s_i
+ * Limits: d >= 1, Ts >= 1, To >= 1, 1 <= N <= 64, 1 <= H <= 65535,
+ *         Dh in {64, 128} (bf16) or Dh in {32, 64, 96, 128} (f32). */
+typedef struct hci_layer {
+    int d, taps_short, taps_outer, poles, heads, head_dim;
+    int act_dtype;                 /* HCI_F32 or HCI_BF16 */
+    const float* w_short;
+    const float* w_outer;
+    const float* lambda;
+    const float* beta;
+    const float* c;
+} hci_layer;
+
+/* Committed (per-sequence) state: the three state classes of the EvSpark
+ * digest (Interpretation: finite convolution windows, modal IIR states,
+ * attention caches).
+ *   short_win [nb][Ts-1][d] act   last Ts-1 short-FIR inputs, oldest first
+ *   outer_win [nb][To-1][d] fp32  last To-1 outer-FIR inputs (the u of
+ *                                 Figure 1(d)), oldest first
+ *   iir       [nb][d][N]    fp32  modal IIR state
+ *   k_cache, v_cache              [nb][H][kv_cap/32][32*Dh] act, TILED layout:
+ *                                 rows are grouped in tiles of 32 keys whose
+ *                                 element order matches the matrix-core
+ *                                 operand layout of the attention kernel.
+ *                                 Read and write logical rows only through
+ *                                 hci_kv_write / hci_kv_read.
+ *   kv_len    [nb] int32          readable prefix length of each sequence
+ *   kv_cap                        rows per (sequence, head); multiple of 32. */
+typedef struct hci_state {
+    int kv_cap;
+    void* short_win;
+    float* outer_win;
+    float* iir;
+    void* k_cache;
+    void* v_cache;
+    int32_t* kv_len;
+} hci_state;
+
+/* One verify round's block: inputs, retained intermediates, outputs.
+ *   x [nb][nc][P][d] act            conv-path inputs of the block positions
+ *   q, k, v [nb][nc][P][H][Dh] act  attention inputs of the block positions
+ *   f [nb][nc][P][d] fp32           OUT of verify: short-FIR outputs
+ *                                   (= outer-FIR inputs), read by slice
+ *   s [nb][nc][P][d][N] fp32        OUT of verify: IIR state after each
+ *                                   position (s_0..s_gamma), read by slice
+ *   y [nb][nc][P][d] act            OUT of verify: IIR readout
+ *   o [nb][nc][P][H][Dh] act        OUT of verify: attention output
+ * x, k and v must stay unchanged between hci_verify_block and
+ * hci_slice_state: slicing copies the accepted rows from them. */
+typedef struct hci_block {
+    const void* x;
+    const void* q;
+    const void* k;
+    const void* v;
+    float* f;
+    float* s;
+    void* y;
+    void* o;
+} hci_block;
+
+/* ------------------------------------------------------------------ verify */
+
+/* Bytes of workspace hci_verify_block needs for these sizes on the current
+ * device (split-K attention partials).  Returns 0 for invalid arguments. */
+size_t hci_verify_workspace_bytes(const hci_layer* L, int nb, int nc, int gamma, int max_kv_len);
+
+/* One initial-state block forward over P = gamma + 1 positions for every
+ * (sequence, candidate) -- EvSpark digest, Interpretation ("one initial-state
+ * block forward") and Figure 1(c).  For each block position i:
+ *   f_i = sum_j w_short[j] * xbar[i-j]   (xbar = short_win then x_0..x_i)
+ *   g_i = sum_j w_outer[j] * fbar[i-j]   (fbar = outer_win then f_0..f_i)
+ *   s_i = lambda * s_{i-1} + beta * g_i,  s_{-1} = iir;  y_i = sum_n c * s_i
+ *   o_i[h] = softmax(q_i[h] . keys / sqrt(Dh)) . values over the sequence's
+ *            kv_len committed rows followed by block rows 0..i (causal).
+ * The candidates of a sequence share its committed state; the committed
+ * prefix is read once per sequence for all nc*P queries.
+ * Committed state is only read: a round abandoned after verify can be
+ * verified again from the same state.
+ *   max_kv_len  host-side upper bound on every kv_len[b] (sizes the grid);
+ *               must satisfy max_kv_len + gamma + 1 <= kv_cap.
+ *   ws, ws_bytes  device workspace of at least
+ *               hci_verify_workspace_bytes(...) bytes, 256-byte aligned.
+ * Limits: gamma >= 0; nc * P <= 64. */
+int hci_verify_block(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                     int nb, int nc, int gamma, int max_kv_len,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* hci_verify_block that also records events[0..3] on `stream`: before the
+ * conv/IIR kernel, before the prefix-attention kernel, after it, and after
+ * the combine kernel, so the caller can time each part with
+ * hipEventElapsedTime.  events must point at 4 events created by the caller
+ * (entries may be NULL to skip one).  Errors as hci_verify_block. */
+int hci_verify_block_timed(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                           int nb, int nc, int gamma, int max_kv_len,
+                           void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
+
+/* ------------------------------------------------------------------ accept */
+
+/* Lossless acceptance for every candidate block, and the best candidate.
+ * Row i of target_logits (i = 0..gamma) is the target's prediction for the
+ * token after block position i; draft_tokens[..][m-1] is draft t_m.
+ *   mode HCI_GREEDY (ReaDy summary, section 3.1): accept the longest prefix
+ *     of drafts equal to the target argmax (ties -> lowest id); next token =
+ *     argmax of row k (a correction if k < gamma, the bonus if k == gamma).
+ *   mode HCI_SAMPLE (ReaDy summary, section D.2; EvSpark Figure 1(c)):
+ *     p_m = softmax(target row m / T), q_m = softmax(draft row m-1 / T), both
+ *     in fp64; draft t_m is kept iff r_m * q_m(t_m) < p_{m-1}(t_m), checked
+ *     left to right, stopping at the first rejection; after a rejection at
+ *     m = k+1 the correction is drawn from max(0, p_k - q_{k+1}), after full
+ *     acceptance the bonus from p_gamma; a draw takes the smallest token id
+ *     whose running sum exceeds r* x (total running sum), else the last
+ *     token with positive weight.
+ *   Inputs: target_logits [nb][nc][P][V] fp32; draft_logits [nb][nc][gamma][V]
+ *     fp32 (the distribution each draft was actually sampled from; NULL in
+ *     greedy mode); draft_tokens [nb][nc][gamma] int32 (an id outside [0, V)
+ *     counts as a mismatch / rejection); uniforms [nb][nc][P] fp64 in [0, 1):
+ *     r_1..r_gamma then r* (NULL in greedy mode).
+ *   Outputs: n_accepted [nb][nc] int32 = k; next_token [nb][nc] int32;
+ *     best_cand [nb] int32 = candidate with the largest k (lowest index on
+ *     ties); margin [nb][nc] fp64 = smallest relative distance of any
+ *     decision from its threshold (greedy: smallest top-1 logit gap of the
+ *     rows read); may be NULL.
+ * Limits: 1 <= V <= 65536; temperature > 0 in sample mode; nc <= 64. */
+int hci_accept(int mode, int nb, int nc, int gamma, int vocab, float temperature,
+               const float* target_logits, const float* draft_logits,
+               const int32_t* draft_tokens, const double* uniforms,
+               int32_t* n_accepted, int32_t* next_token, int32_t* best_cand,
+               double* margin, hipStream_t stream);
+
+/* ------------------------------------------------------------------- slice */
+
+/* Commit block positions 0..k of the winning candidate c* = best_cand[b]
+ * (k = n_accepted[b][c*]) -- EvSpark digest, Figure 1(d) and Interpretation
+ * (state slicing, no replay):
+ *   kv rows kv_len..kv_len+k  <- block k/v rows 0..k of c*;  kv_len += k+1
+ *   short_win <- last Ts-1 rows of [short_win ; x_0..x_k]
+ *   outer_win <- last To-1 rows of [outer_win ; f_0..f_k]
+ *   iir       <- s_k
+ * k and c* are read on the device (no host synchronisation).  best_cand may
+ * be NULL when nc == 1.  max_kv_len is the same host bound as for verify.
+ * Rows that would land at or beyond kv_cap are never written. */
+int hci_slice_state(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                    int nb, int nc, int gamma, int max_kv_len,
+                    const int32_t* n_accepted, const int32_t* best_cand,
+                    hipStream_t stream);
+
+/* -------------------------------------------------------------- KV access */
+
+/* Elements (not bytes) of ONE of k_cache / v_cache for nb sequences. */
+size_t hci_kv_cache_elems(const hci_layer* L, int nb, int kv_cap);
+
+/* Write logical rows [row0, row0+nrows) of sequence b (0 <= b < nb) into the
+ * tiled caches.  k_rows, v_rows: [H][nrows][Dh] act.  Does not touch kv_len.
+ * HCI_ECAPACITY if row0 + nrows > kv_cap. */
+int hci_kv_write(const hci_layer* L, const hci_state* S, int nb, int b, int row0, int nrows,
+                 const void* k_rows, const void* v_rows, hipStream_t stream);
+
+/* Read logical rows [row0, row0+nrows) of sequence b: [H][nrows][Dh] act. */
+int hci_kv_read(const hci_layer* L, const hci_state* S, int nb, int b, int row0, int nrows,
+                void* k_rows, void* v_rows, hipStream_t stream);
+
+/* ------------------------------------------------------------------ probes */
+
+/* Stream `bytes` (multiple of 16) from src; one word per workgroup is written
+ * to sink[0..blocks) so the reads cannot be elided.  sink must hold
+ * hci_probe_sink_words() floats.  Measures the practical HBM read ceiling. */
+int hci_probe_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
+int hci_probe_sink_words(void);
+
+/* Plain device copy of `bytes` (multiple of 16): the known-size kernel that
+ * hardware byte counters are calibrated against. */
+int hci_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HCI_H */
