@@ -30,8 +30,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // ------------------------------------------------------------ bf16 prefix
 
+constexpr int kPrefixWaves = 4;      // waves per workgroup; their partials merge in LDS
+
 template <int DH, int NQT>
-__global__ __launch_bounds__(64) void k_attn_prefix_bf16(
+constexpr size_t prefix_merge_floats() {
+    // per merged wave: O^T accumulators (16*NQT queries x DH), running max, normaliser
+    return (size_t)NQT * 16 * DH + 2 * NQT * 16;
+}
+
+template <int DH, int NQT>
+__global__ __launch_bounds__(64 * kPrefixWaves) void k_attn_prefix_bf16(
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ kv_len, const uint16_t* __restrict__ q,
     float* __restrict__ part_o, float* __restrict__ part_ml,
@@ -40,16 +48,21 @@ __global__ __launch_bounds__(64) void k_attn_prefix_bf16(
     constexpr int J = DH / 32;          // k-steps of the score product
     constexpr int DT = DH / 16;         // 16-wide output tiles of the value product
     constexpr int KV4 = 4 * DH;         // uint4 per tile (32 keys x DH bf16)
+    constexpr size_t MF = prefix_merge_floats<DH, NQT>();
+    extern __shared__ float merge[];    // [kPrefixWaves-1][MF]
 
     const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     int L = kv_len[b];
     L = L < 0 ? 0 : (L > kv_cap ? kv_cap : L);
     const int tiles = (L + kTile - 1) / kTile;
     const int t0 = chunk * chunk_tiles;
-    if (t0 >= tiles) return;
+    if (t0 >= tiles) return;                           // whole workgroup
     const int t1 = min(t0 + chunk_tiles, tiles);
+    const int wave = threadIdx.x >> 6;
+    const int per = (t1 - t0 + kPrefixWaves - 1) / kPrefixWaves;
+    const int w0 = min(t0 + wave * per, t1), w1 = min(w0 + per, t1);   // wave 0 is never empty
 
-    const int lane = threadIdx.x, g = lane >> 4, n = lane & 15;
+    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
 
     // queries as B operands: lane (g, n) holds Q[16nt+n][32j+8g .. 32j+8g+7]
     bf16x8 qreg[NQT][J];
@@ -79,14 +92,16 @@ __global__ __launch_bounds__(64) void k_attn_prefix_bf16(
     const uint4* vp = (const uint4*)vc + slab;
 
     uint4 kr[2 * J], vr[DT];
+    if (w0 < w1) {
 #pragma unroll
-    for (int i = 0; i < 2 * J; ++i) kr[i] = kp[(size_t)t0 * KV4 + i * 64 + lane];
+        for (int i = 0; i < 2 * J; ++i) kr[i] = kp[(size_t)w0 * KV4 + i * 64 + lane];
 #pragma unroll
-    for (int t = 0; t < DT; ++t) vr[t] = vp[(size_t)t0 * KV4 + t * 64 + lane];
+        for (int t = 0; t < DT; ++t) vr[t] = vp[(size_t)w0 * KV4 + t * 64 + lane];
+    }
 
-    for (int T = t0; T < t1; ++T) {
+    for (int T = w0; T < w1; ++T) {
         uint4 kn[2 * J], vn[DT];
-        const bool more = T + 1 < t1;
+        const bool more = T + 1 < w1;
         if (more) {
             const size_t base = (size_t)(T + 1) * KV4;
 #pragma unroll
@@ -163,23 +178,62 @@ __global__ __launch_bounds__(64) void k_attn_prefix_bf16(
         }
     }
 
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+        lrun[nt] += __shfl_xor(lrun[nt], 16);
+        lrun[nt] += __shfl_xor(lrun[nt], 32);
+    }
+
+    // merge the four waves' partial softmax states in LDS (fixed order: wave 0, 1, 2, 3)
+    if (wave > 0) {
+        float* mw = merge + (size_t)(wave - 1) * MF;
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) {
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+                *(float4*)(mw + (((size_t)nt * DT + t) * 64 + lane) * 4) =
+                    make_float4(oacc[t][nt][0], oacc[t][nt][1], oacc[t][nt][2], oacc[t][nt][3]);
+            if (g == 0) {
+                mw[(size_t)NQT * 16 * DH + nt * 16 + n] = mrun[nt];
+                mw[(size_t)NQT * 16 * DH + NQT * 16 + nt * 16 + n] = lrun[nt];
+            }
+        }
+    }
+    __syncthreads();
+    if (wave > 0) return;
+
     // partial softmax state of this chunk: part_o [nb][H][n_chunks][nq][DH] (unnormalised),
     // part_ml [..][nq][2] = (running max in log2 units, normaliser)
     const size_t pbase = (((size_t)b * H + h) * n_chunks + chunk) * nq;
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
-        float l = lrun[nt];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        const int qi = 16 * nt + n;
-        if (qi < nq) {
+        float M = mrun[nt];
 #pragma unroll
-            for (int t = 0; t < DT; ++t) {
-                float4 o4 = make_float4(oacc[t][nt][0], oacc[t][nt][1], oacc[t][nt][2], oacc[t][nt][3]);
-                *(float4*)(part_o + (pbase + qi) * DH + 16 * t + 4 * g) = o4;
-            }
-            if (g == 0) *(float2*)(part_ml + (pbase + qi) * 2) = make_float2(mrun[nt], l);
+        for (int w = 1; w < kPrefixWaves; ++w) M = fmaxf(M, merge[(w - 1) * MF + (size_t)NQT * 16 * DH + nt * 16 + n]);
+        float sc[kPrefixWaves];
+        sc[0] = exp2f(mrun[nt] - M);
+        float l = sc[0] * lrun[nt];
+#pragma unroll
+        for (int w = 1; w < kPrefixWaves; ++w) {
+            const float* mw = merge + (size_t)(w - 1) * MF;
+            sc[w] = exp2f(mw[(size_t)NQT * 16 * DH + nt * 16 + n] - M);
+            l = fmaf(sc[w], mw[(size_t)NQT * 16 * DH + NQT * 16 + nt * 16 + n], l);
         }
+        const int qi = 16 * nt + n;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            f32x4 acc = oacc[t][nt] * sc[0];
+#pragma unroll
+            for (int w = 1; w < kPrefixWaves; ++w) {
+                const float4 o = *(const float4*)(merge + (size_t)(w - 1) * MF + (((size_t)nt * DT + t) * 64 + lane) * 4);
+                acc[0] = fmaf(sc[w], o.x, acc[0]);
+                acc[1] = fmaf(sc[w], o.y, acc[1]);
+                acc[2] = fmaf(sc[w], o.z, acc[2]);
+                acc[3] = fmaf(sc[w], o.w, acc[3]);
+            }
+            if (qi < nq) *(float4*)(part_o + (pbase + qi) * DH + 16 * t + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+        if (qi < nq && g == 0) *(float2*)(part_ml + (pbase + qi) * 2) = make_float2(M, l);
     }
 }
 
@@ -293,72 +347,118 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
 
 // ----------------------------------------------------------------- combine
 //
-// One workgroup of DH threads per (query, head, sequence): the causal part
-// over the block's own keys 0..i is computed here in fp32, then the prefix
-// partials and the block part are merged in a fixed order (chunk 0, 1, ...,
-// then the block), so the result does not depend on scheduling.
+// One workgroup of 256 threads per (query, head, sequence).  First the
+// causal part over the block's own keys 0..i is computed in fp32 (one
+// partial softmax state), then the prefix partials are merged with it:
+//   M = max(m_tail, m_c), w_c = 2^(m_c - M),
+//   o = (sum_c w_c O_c + 2^(m_tail - M) O_tail) / (sum_c w_c l_c + 2^(m_tail - M) l_tail)
+// Chunk weights are formed once per chunk in LDS; thread groups accumulate
+// interleaved chunks and are merged in a fixed order, so the result does not
+// depend on scheduling.
+
+constexpr int kCombT = 256;
+constexpr int kMaxChunks = 4096;     // the split-K plan never exceeds this
 
 template <int ACT>
-__global__ __launch_bounds__(256) void k_attn_combine(
+__global__ __launch_bounds__(kCombT) void k_attn_combine(
     const typename Act<ACT>::T* __restrict__ q, const typename Act<ACT>::T* __restrict__ kb,
     const typename Act<ACT>::T* __restrict__ vb, const int32_t* __restrict__ kv_len,
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     typename Act<ACT>::T* __restrict__ o,
     int H, int DH, int P, int nq, int kv_cap, int chunk_tiles, int n_chunks, float scale_log2)
 {
-    __shared__ float red[8][64];
+    __shared__ float wts[kMaxChunks];
+    __shared__ float red[kCombT / 64][64];
     __shared__ float sc[64];
+    __shared__ float acc_s[kCombT];
 
     const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int c = qi / P, i = qi % P;
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    const int wave = tid >> 6, ln = tid & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
+    const int nw = kCombT / 64;
 
-    // block keys 0..i of this candidate: scores by a two-level fixed-order reduction
+    // ---- block part: scores of keys 0..i (two-level fixed-order reduction)
     const size_t rowq = (((size_t)b * nq + qi) * H + h) * DH;
+    const size_t rowb = ((size_t)b * nq + (size_t)c * P) * H;   // + j*H + h for block row j
     const float qd = tid < DH ? Act<ACT>::load(q, rowq + tid) : 0.f;
     for (int j = 0; j <= i; ++j) {
-        const size_t rowk = (((size_t)b * nq + (size_t)c * P + j) * H + h) * DH;
-        float v = tid < DH ? qd * Act<ACT>::load(kb, rowk + tid) : 0.f;
+        float v = tid < DH ? qd * Act<ACT>::load(kb, (rowb + (size_t)j * H + h) * DH + tid) : 0.f;
         for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-        if (ln == 0) red[wave][j & 63] = v;
-        __syncthreads();
-        if (tid == 0) {
-            float s = 0.f;
-            for (int w = 0; w < (nthr >> 6); ++w) s += red[w][j & 63];
-            sc[j] = s * scale_log2;
-        }
-        __syncthreads();
+        if (ln == 0) red[wave][j] = v;
     }
+    __syncthreads();
+    if (tid <= i) {
+        float s = 0.f;
+        for (int w = 0; w < nw; ++w) s += red[w][tid];
+        sc[tid] = s * scale_log2;
+    }
+    __syncthreads();
     float mt = -INFINITY;
     for (int j = 0; j <= i; ++j) mt = fmaxf(mt, sc[j]);
-    float lt = 0.f, ot = 0.f;
-    for (int j = 0; j <= i; ++j) {
-        const float p = exp2f(sc[j] - mt);
-        lt += p;
-        if (tid < DH) ot = fmaf(p, Act<ACT>::load(vb, (((size_t)b * nq + (size_t)c * P + j) * H + h) * DH + tid), ot);
-    }
 
+    // ---- prefix partials: running max over chunks
     int L = kv_len[b];
     L = L < 0 ? 0 : (L > kv_cap ? kv_cap : L);
     const int tiles = (L + kTile - 1) / kTile;
     int nch = (tiles + chunk_tiles - 1) / chunk_tiles;
     nch = nch > n_chunks ? n_chunks : nch;
-
     const size_t pb = ((size_t)b * H + h) * n_chunks;
+    float mloc = -INFINITY;
+    for (int ck = tid; ck < nch; ck += kCombT) mloc = fmaxf(mloc, part_ml[((pb + ck) * nq + qi) * 2]);
+    for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+    if (ln == 0) red[wave][0] = mloc;
+    __syncthreads();
     float M = mt;
-    for (int ck = 0; ck < nch; ++ck) M = fmaxf(M, part_ml[((pb + ck) * nq + qi) * 2]);
-    float l = 0.f, acc = 0.f;
-    for (int ck = 0; ck < nch; ++ck) {
-        const size_t r = (pb + ck) * nq + qi;
-        const float w = exp2f(part_ml[r * 2] - M);
-        l = fmaf(w, part_ml[r * 2 + 1], l);
-        if (tid < DH) acc = fmaf(w, part_o[r * DH + tid], acc);
+    for (int w = 0; w < nw; ++w) M = fmaxf(M, red[w][0]);
+    __syncthreads();
+
+    // ---- chunk weights and the normaliser
+    float lloc = 0.f;
+    for (int ck = tid; ck < nch; ck += kCombT) {
+        const float2 ml = *(const float2*)(part_ml + ((pb + ck) * nq + qi) * 2);
+        const float w = exp2f(ml.x - M);
+        wts[ck] = w;
+        lloc = fmaf(w, ml.y, lloc);
     }
-    const float wt = exp2f(mt - M);
-    l = fmaf(wt, lt, l);
-    acc = fmaf(wt, ot, acc);
-    if (tid < DH) Act<ACT>::store(o, rowq + tid, acc / l);
+    for (int off = 32; off >= 1; off >>= 1) lloc += __shfl_xor(lloc, off);
+    if (ln == 0) red[wave][1] = lloc;
+    __syncthreads();
+    float l = 0.f;
+    for (int w = 0; w < nw; ++w) l += red[w][1];
+
+    // ---- weighted sum of the chunk outputs: thread (group, d) takes chunks group, group+ng, ...
+    const int ng = kCombT / DH;
+    const int grp = tid / DH, dd = tid % DH;
+    float acc = 0.f;
+    if (grp < ng) {
+        int ck = grp;
+        for (; ck + 3 * ng < nch; ck += 4 * ng) {
+            const float o0 = part_o[((pb + ck) * nq + qi) * DH + dd];
+            const float o1 = part_o[((pb + ck + ng) * nq + qi) * DH + dd];
+            const float o2 = part_o[((pb + ck + 2 * ng) * nq + qi) * DH + dd];
+            const float o3 = part_o[((pb + ck + 3 * ng) * nq + qi) * DH + dd];
+            acc = fmaf(wts[ck], o0, acc);
+            acc = fmaf(wts[ck + ng], o1, acc);
+            acc = fmaf(wts[ck + 2 * ng], o2, acc);
+            acc = fmaf(wts[ck + 3 * ng], o3, acc);
+        }
+        for (; ck < nch; ck += ng) acc = fmaf(wts[ck], part_o[((pb + ck) * nq + qi) * DH + dd], acc);
+    }
+    acc_s[tid] = acc;
+    __syncthreads();
+
+    if (tid < DH) {
+        float tot = 0.f;
+        for (int g2 = 0; g2 < ng; ++g2) tot += acc_s[g2 * DH + tid];
+        // block part: weights 2^(s_j - M) directly in the merged frame
+        float lt = 0.f, ot = 0.f;
+        for (int j = 0; j <= i; ++j) {
+            const float p = exp2f(sc[j] - M);
+            lt += p;
+            ot = fmaf(p, Act<ACT>::load(vb, (rowb + (size_t)j * H + h) * DH + tid), ot);
+        }
+        Act<ACT>::store(o, rowq + tid, (tot + ot) / (l + lt));
+    }
 }
 
 // -------------------------------------------------------------------- host
@@ -369,13 +469,16 @@ AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_k
     const int P = gamma + 1;
     p.nq = nc * P;
     const int tiles = (max_kv_len + kTile - 1) / kTile;
-    // Aim for about 16 waves per CU over the whole grid so that every CU keeps
-    // several waves (and their prefetched tiles) in flight, with chunks of at
-    // least 8 tiles so that partials stay a small fraction of the traffic.
+    // Aim for about 16 waves (4 workgroups of 4 waves) per CU over the whole
+    // grid so that every CU keeps several waves and their prefetched tiles in
+    // flight, with at least 8 tiles per wave so that partials stay a small
+    // fraction of the traffic.
     const long long total_tiles = (long long)tiles * nb * L->heads;
-    const long long target_waves = (long long)num_cus * 16;
-    long long ct = (total_tiles + target_waves - 1) / (target_waves > 0 ? target_waves : 1);
-    if (ct < 8) ct = 8;
+    const long long target_wgs = (long long)num_cus * 4;
+    long long ct = (total_tiles + target_wgs - 1) / (target_wgs > 0 ? target_wgs : 1);
+    if (ct < 8 * kPrefixWaves) ct = 8 * kPrefixWaves;
+    const long long min_ct = (tiles + kMaxChunks - 1) / kMaxChunks;   // combine holds <= kMaxChunks weights
+    if (ct < min_ct) ct = min_ct;
     if (ct > tiles && tiles > 0) ct = tiles;
     if (ct < 1) ct = 1;
     p.chunk_tiles = (int)ct;
@@ -401,10 +504,18 @@ hipError_t launch_attention(const hci_layer* L, const hci_state* S, const hci_bl
         if (L->act_dtype == HCI_BF16) {
             const int nqt = (nq + 15) / 16;
 #define HCI_PREFIX(DHV, NQTV)                                                                      \
-    hipLaunchKernelGGL((k_attn_prefix_bf16<DHV, NQTV>), grid, block, 0, st,                          \
-                       (const uint16_t*)S->k_cache, (const uint16_t*)S->v_cache, S->kv_len,          \
-                       (const uint16_t*)blk->q, part_o, part_ml, H, S->kv_cap, nq, plan.chunk_tiles, \
-                       plan.n_chunks, scale_log2)
+    do {                                                                                           \
+        const size_t lds = (kPrefixWaves - 1) * prefix_merge_floats<DHV, NQTV>() * sizeof(float);  \
+        if (lds > 65536) {                                                                         \
+            hipError_t ea = hipFuncSetAttribute((const void*)k_attn_prefix_bf16<DHV, NQTV>,        \
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+            if (ea != hipSuccess) return ea;                                                       \
+        }                                                                                          \
+        hipLaunchKernelGGL((k_attn_prefix_bf16<DHV, NQTV>), grid, dim3(64 * kPrefixWaves), lds, st, \
+                           (const uint16_t*)S->k_cache, (const uint16_t*)S->v_cache, S->kv_len,    \
+                           (const uint16_t*)blk->q, part_o, part_ml, H, S->kv_cap, nq,             \
+                           plan.chunk_tiles, plan.n_chunks, scale_log2);                           \
+    } while (0)
             if (DH == 128) {
                 switch (nqt) {
                     case 1: HCI_PREFIX(128, 1); break;
@@ -435,7 +546,7 @@ hipError_t launch_attention(const hci_layer* L, const hci_state* S, const hci_bl
         if (e != hipSuccess) return e;
     }
 
-    dim3 cgrid(nq, H, nb), cblock(DH < 64 ? 64 : DH);
+    dim3 cgrid(nq, H, nb), cblock(kCombT);
     if (L->act_dtype == HCI_BF16) {
         hipLaunchKernelGGL(k_attn_combine<HCI_BF16>, cgrid, cblock, 0, st,
                            (const uint16_t*)blk->q, (const uint16_t*)blk->k, (const uint16_t*)blk->v,

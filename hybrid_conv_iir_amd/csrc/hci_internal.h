@@ -86,6 +86,10 @@ struct AttnPlan {
 AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_kv_len, int num_cus);
 int device_cu_count();
 
+// dynamic LDS bytes of the conv/IIR kernel (must not exceed kMaxLds)
+size_t conv_iir_lds_bytes(int To, int P);
+constexpr size_t kMaxLds = 160 * 1024;
+
 hipError_t launch_conv_iir(const hci_layer* L, const hci_state* S, const hci_block* blk,
                            int nb, int nc, int P, hipStream_t st);
 // after_prefix (may be null): an event recorded right after the prefix kernel

@@ -150,7 +150,8 @@ size_t hci_verify_workspace_bytes(const hci_layer* L, int nb, int nc, int gamma,
  *               must satisfy max_kv_len + gamma + 1 <= kv_cap.
  *   ws, ws_bytes  device workspace of at least
  *               hci_verify_workspace_bytes(...) bytes, 256-byte aligned.
- * Limits: gamma >= 0; nc * P <= 64. */
+ * Limits: gamma >= 0; nc * P <= 64; To + P <= 320 (LDS staging of the
+ * outer window and taps). */
 int hci_verify_block(const hci_layer* L, const hci_state* S, const hci_block* blk,
                      int nb, int nc, int gamma, int max_kv_len,
                      void* ws, size_t ws_bytes, hipStream_t stream);
