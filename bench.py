@@ -36,7 +36,7 @@ WORKLOAD_NAMES = {
     "c4": "batched multi-candidate verify: 4 sequences x 4 candidates, KV prefixes 16384/32768/51200/65536, gamma=12, sampling",
     "c5": "wide layer: d=8192, FIR 3/128 taps, 16 poles, 64x128 heads, 131072-token bf16 KV prefix, gamma=12, greedy",
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefix_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_stream_c3_traffic.json")
 
 
 def _hip():
@@ -78,15 +78,18 @@ def verify_alg_bytes(cfg, kv_lens) -> int:
     return kv + attn_io + conv
 
 
-def prefix_alg_bytes(cfg, kv_lens) -> int:
-    """Per-unit 512 B (one key of one head: Dh bf16 K + Dh bf16 V) x keys x heads, plus the queries."""
+def stream_alg_bytes(cfg, kv_lens) -> int:
+    """Bytes the streaming kernel must move: the verify's bytes minus the output o the combine writes.
+
+    Dominated by 512 B per (key, head) of the prefix (Dh bf16 K + Dh bf16 V), read once per sequence.
+    """
     act = 2 if cfg.act == "bf16" else 4
-    return sum(2 * cfg.heads * L * cfg.head_dim * act for L in kv_lens) + cfg.nb * cfg.nc * cfg.P * cfg.heads * cfg.head_dim * act
+    return verify_alg_bytes(cfg, kv_lens) - cfg.nb * cfg.nc * cfg.P * cfg.heads * cfg.head_dim * act
 
 
 def _kernel_sha() -> str:
     h = hashlib.sha256()
-    for f in ("attention.hip", "hci_internal.h"):
+    for f in ("attention.hip", "conv_iir_body.h", "hci_internal.h"):
         with open(os.path.join(ROOT, "hybrid_conv_iir_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -103,8 +106,12 @@ def _traffic(cfg_name):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, case_np, heads):
-    """The fp64 oracle as it stands, timed on this host on a bounded sample of the workload."""
+def cpu_baseline(cfg, case_np, heads, reps):
+    """The fp64 oracle as it stands, timed on this host on a bounded sample of the workload.
+
+    The sample is one (sequence, candidate) block's verify -> accept -> slice with attention over
+    `heads`, repeated `reps` times; time is scaled to all heads and all blocks of the workload.
+    """
     import numpy as np
     import oracle
     try:
@@ -118,33 +125,40 @@ def cpu_baseline(cfg, case_np, heads):
     x, q, k, v = bn["x"][b, c], bn["q"][b, c][:, heads], bn["k"][b, c][:, heads], bn["v"][b, c][:, heads]
     st = oracle.SeqState(small["short_win"][b], small["outer_win"][b], small["iir"][b],
                          [case_np["kpre"]], [case_np["vpre"]])
-    t0 = time.perf_counter()
-    f = oracle.depthwise_fir(x, st.short_win, layer.w_short)
-    g = oracle.depthwise_fir(f, st.outer_win, layer.w_outer)
-    s, y = oracle.modal_iir(g, st.iir, layer.lam, layer.beta, layer.c)
-    t1 = time.perf_counter()
-    oracle.block_attention(q, k, v, st.k_blocks, st.v_blocks)
-    t2 = time.perf_counter()
-    if cfg.mode == "greedy":
-        kk, _, _ = oracle.greedy_accept(ri["target_logits"][b, c], ri["drafts"][b, c])
-    else:
-        kk, _, _ = oracle.rejection_accept(ri["target_logits"][b, c], ri["draft_logits"][b, c], ri["drafts"][b, c],
-                                           ri["uniforms"][b, c], cfg.temperature)
-    t3 = time.perf_counter()
-    oracle.slice_state(st, x, {"f": f, "s": s}, k, v, kk)
-    t4 = time.perf_counter()
+    t_conv = t_attn = t_acc = t_slice = 0.0
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        f = oracle.depthwise_fir(x, st.short_win, layer.w_short)
+        g = oracle.depthwise_fir(f, st.outer_win, layer.w_outer)
+        s, y = oracle.modal_iir(g, st.iir, layer.lam, layer.beta, layer.c)
+        t1 = time.perf_counter()
+        oracle.block_attention(q, k, v, st.k_blocks, st.v_blocks)
+        t2 = time.perf_counter()
+        if cfg.mode == "greedy":
+            kk, _, _ = oracle.greedy_accept(ri["target_logits"][b, c], ri["drafts"][b, c])
+        else:
+            kk, _, _ = oracle.rejection_accept(ri["target_logits"][b, c], ri["draft_logits"][b, c],
+                                               ri["drafts"][b, c], ri["uniforms"][b, c], cfg.temperature)
+        t3 = time.perf_counter()
+        oracle.slice_state(st, x, {"f": f, "s": s}, k, v, kk)
+        t4 = time.perf_counter()
+        t_conv += t1 - t0
+        t_attn += t2 - t1
+        t_acc += t3 - t2
+        t_slice += t4 - t3
     scale = cfg.heads / len(heads)
     blocks = cfg.nb * cfg.nc          # the sample is one (sequence, candidate) block
-    est = ((t1 - t0) + (t2 - t1) * scale + (t3 - t2) + (t4 - t3)) * blocks
-    measured = t4 - t0
+    measured = t_conv + t_attn + t_acc + t_slice
+    est = (t_conv + t_attn * scale + t_acc + t_slice) / reps * blocks
     return {
         "value": round(cfg.nb * cfg.nc * cfg.P / est, 3),
         "unit": "verified block-positions/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle, one verify->accept->slice of one block with attention over {len(heads)} of "
-                   f"{cfg.heads} heads (timed {measured:.1f} s; attention time scaled x{scale:g} to all heads"
-                   f"{', x%d blocks' % blocks if blocks > 1 else ''})"),
+        "sample": (f"fp64 numpy oracle, verify->accept->slice of one block with attention over {len(heads)} of "
+                   f"{cfg.heads} heads, {reps} repetitions (timed {measured:.1f} s"
+                   f"{'; attention time scaled x%g to all heads' % scale if scale != 1 else ''}"
+                   f"{'; x%d blocks' % blocks if blocks > 1 else ''})"),
         "seconds_per_step_est": round(est, 3),
     }
 
@@ -155,8 +169,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the CPU-oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-oracle sample (0 = all)")
+    ap.add_argument("--cpu-reps", type=int, default=3, help="repetitions of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run the known-size copy kernel once on this many MiB (byte-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -186,13 +203,13 @@ def main():
     lay = dv.DeviceLayer(cfg, params)
     st = dv.DeviceState(lay, cfg.nb, kv_cap)
     st.load_small(small)
-    heads = list(range(min(args.cpu_heads, cfg.heads)))
+    heads = list(range(cfg.heads if args.cpu_heads <= 0 else min(args.cpu_heads, cfg.heads)))
     kpre_host = vpre_host = None
     for b in range(cfg.nb):
         kp = synth.kv_prefix(cfg, b, "k", device="cuda")
         vp = synth.kv_prefix(cfg, b, "v", device="cuda")
         st.write_prefix(b, kp, vp)
-        if b == 0:
+        if b == 0 and not args.no_cpu_baseline:
             kpre_host, vpre_host = dv.to_host(kp[heads]), dv.to_host(vp[heads])
         del kp, vp
     st.kv_len.copy_(torch.tensor(cfg.kv_lens, dtype=torch.int32))
@@ -219,6 +236,14 @@ def main():
         probe_ms.append(_ms(hip, pe[0], pe[1]))
     probe_gbs = st.k_cache.numel() * 2 / (min(probe_ms) * 1e-3) / 1e9
 
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        csrc = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        cdst = torch.empty_like(csrc)
+        hci.probe_copy(cdst, csrc)
+        torch.cuda.synchronize()
+        del csrc, cdst
+
     # ---------------------------------------------------------------- warm-up
     def step(evs=None):
         nonlocal bound
@@ -228,10 +253,10 @@ def main():
             hci.verify_block_timed(lay.c, st.c, blk.c, blk.nb, blk.nc, blk.gamma, bound, blk.ws, evs)
         dv.accept(acc, mode, cfg.temperature)
         if evs is not None:
-            hip.hipEventRecord(evs[4], sp)
+            hip.hipEventRecord(evs[3], sp)
         dv.slice_state(lay, st, blk, acc, bound)
         if evs is not None:
-            hip.hipEventRecord(evs[5], sp)
+            hip.hipEventRecord(evs[4], sp)
         bound += P
 
     for _ in range(W):
@@ -240,7 +265,7 @@ def main():
     len_before = dv.to_host(st.kv_len).astype(np.int64)
 
     # ---------------------------------------------------------------- timed region
-    evsets = [_events(hip, 6) for _ in range(K)]
+    evsets = [_events(hip, 5) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -250,20 +275,19 @@ def main():
     len_after = dv.to_host(st.kv_len).astype(np.int64)
 
     ms_step = (t1 - t0) * 1e3 / K
-    conv_ms = [_ms(hip, e[0], e[1]) for e in evsets]
-    prefix_ms = [_ms(hip, e[1], e[2]) for e in evsets]
-    combine_ms = [_ms(hip, e[2], e[3]) for e in evsets]
-    verify_ms = [_ms(hip, e[0], e[3]) for e in evsets]
-    accept_ms = [_ms(hip, e[3], e[4]) for e in evsets]
-    slice_ms = [_ms(hip, e[4], e[5]) for e in evsets]
-    step_dev_ms = [_ms(hip, e[0], e[5]) for e in evsets]
+    stream_ms = [_ms(hip, e[0], e[1]) for e in evsets]
+    combine_ms = [_ms(hip, e[1], e[2]) for e in evsets]
+    verify_ms = [_ms(hip, e[0], e[2]) for e in evsets]
+    accept_ms = [_ms(hip, e[2], e[3]) for e in evsets]
+    slice_ms = [_ms(hip, e[3], e[4]) for e in evsets]
+    step_dev_ms = [_ms(hip, e[0], e[4]) for e in evsets]
 
     # mean committed length over the timed steps (the prefix grows by k+1 per step)
     mean_lens = [int(a) + (int(b) - int(a)) * (K - 1) / (2.0 * K) for a, b in zip(len_before, len_after)]
     alg_verify = verify_alg_bytes(cfg, mean_lens)
-    alg_prefix = prefix_alg_bytes(cfg, mean_lens)
-    avg_prefix_s = float(np.mean(prefix_ms)) * 1e-3
-    achieved = alg_prefix / avg_prefix_s / 1e9
+    alg_stream = stream_alg_bytes(cfg, mean_lens)
+    avg_stream_s = float(np.mean(stream_ms)) * 1e-3
+    achieved = alg_stream / avg_stream_s / 1e9
     positions = cfg.nb * cfg.nc * P
     value = positions / (ms_step * 1e-3)
 
@@ -287,24 +311,23 @@ def main():
         "verify_hbm_GBs": round(alg_verify / (float(np.median(verify_ms)) * 1e-3) / 1e9, 1),
         "verify_pct_of_8TBs": round(100.0 * alg_verify / (float(np.median(verify_ms)) * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "verify_positions_per_s": round(positions / (float(np.median(verify_ms)) * 1e-3), 1),
-        "breakdown_ms_median": {"conv_iir": round(float(np.median(conv_ms)), 4),
-                                "attn_prefix": round(float(np.median(prefix_ms)), 4),
+        "breakdown_ms_median": {"verify_stream": round(float(np.median(stream_ms)), 4),
                                 "attn_combine": round(float(np.median(combine_ms)), 4),
                                 "accept": round(float(np.median(accept_ms)), 4),
                                 "slice": round(float(np.median(slice_ms)), 4),
                                 "step_device": round(float(np.median(step_dev_ms)), 4)},
         "slice_ms": round(float(np.median(slice_ms)), 4),
         "hbm_probe_read_GBs": round(probe_gbs, 1),
-        "roofline": {"kernel": "k_attn_prefix_bf16" if cfg.act == "bf16" else "k_attn_prefix_f32",
+        "roofline": {"kernel": "k_verify_stream" if cfg.act == "bf16" else "conv+tail+prefix (fp32 kernels)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": _traffic(args.config),
-                     "alg_bytes_per_launch": int(alg_prefix),
-                     "avg_launch_ms": round(avg_prefix_s * 1e3, 4)},
+                     "alg_bytes_per_launch": int(alg_stream),
+                     "avg_launch_ms": round(avg_stream_s * 1e3, 4)},
         "accepted_per_step": [int(x) for x in ((len_after - len_before) // K)],
     }
     if not args.no_cpu_baseline:
         case_np = {"params": params, "small": small, "blk": bn, "ri": ri, "kpre": kpre_host, "vpre": vpre_host}
-        out["cpu_baseline"] = cpu_baseline(cfg, case_np, heads)
+        out["cpu_baseline"] = cpu_baseline(cfg, case_np, heads, max(1, args.cpu_reps))
     print(json.dumps(out), flush=True)
 
 

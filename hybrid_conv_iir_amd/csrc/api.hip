@@ -92,17 +92,12 @@ static int verify_impl(const hci_layer* L, const hci_state* S, const hci_block* 
     if (rc) return rc;
     rc = check_block(blk);
     if (rc) return rc;
-    if (conv_iir_lds_bytes(L->taps_outer, P) > kMaxLds) return HCI_EUNSUPPORTED;
+    if (conv_iir_lds_bytes(L->taps_outer, P) > kMaxLds || stream_lds_bytes(L, nc, P) > kMaxLds)
+        return HCI_EUNSUPPORTED;
     const AttnPlan plan = plan_attention(L, nb, nc, gamma, max_kv_len, device_cu_count());
     if (plan.bytes > 0 && (!ws || ws_bytes < plan.bytes || !aligned(ws, 256))) return HCI_EWORKSPACE;
 
-    auto mark = [&](int i) { return (ev && ev[i]) ? hipEventRecord(ev[i], stream) : hipSuccess; };
-    if (mark(0) != hipSuccess) return HCI_EDEVICE;
-    if (launch_conv_iir(L, S, blk, nb, nc, P, stream) != hipSuccess) return HCI_EDEVICE;
-    if (mark(1) != hipSuccess) return HCI_EDEVICE;
-    if (launch_attention(L, S, blk, nb, nc, P, plan, ws, stream, ev ? &ev[2] : nullptr) != hipSuccess)
-        return HCI_EDEVICE;
-    if (mark(3) != hipSuccess) return HCI_EDEVICE;
+    if (launch_verify(L, S, blk, nb, nc, P, plan, ws, stream, ev) != hipSuccess) return HCI_EDEVICE;
     return HCI_OK;
 }
 

@@ -1,31 +1,45 @@
-// Attention half of the block forward: the block queries attend to the
-// committed KV prefix (split-K over the prefix, one partial softmax state per
-// chunk) and causally to the block's own keys; a combine kernel merges the
-// partials in a fixed order.  EvSpark digest, Interpretation: the verify is
-// one block forward from the committed state, so all nc*P queries of a
-// sequence share a single read of its prefix; the prefix read is the part of
-// the verify that grows with context (ReaDy summary, section 5: token-wise KV
-// traffic grows with the number of attended tokens).
+// Attention half of the block forward, plus the fused streaming kernel.
 //
-// Prefix kernel (bf16): one wave per (chunk, head, sequence).  Per 32-key
-// tile the wave issues 2*Dh/32 + Dh/16 sixteen-byte loads per lane, each a
-// contiguous kilobyte thanks to the tiled cache layout, prefetching the next
-// tile while the current one is consumed.  Scores S^T = K Q^T and the value
-// product O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16 with the keys in
-// the M dimension and up to 16*NQT queries in N; the online softmax (max,
-// rescale, exp2) runs in fp32 registers with a 4-lane exchange per query.
-#include "hci_internal.h"
+// The block queries attend to the committed KV prefix and, causally, to the
+// block's own keys.  EvSpark digest, Interpretation: the verify is one block
+// forward from the committed state, so all nc*P queries of a sequence share
+// a single read of its prefix; that read is the part of the verify that grows
+// with context (ReaDy summary, section 5: token-wise KV traffic grows with the
+// number of attended tokens).  The prefix is split into chunks (split-K); each
+// chunk leaves a partial softmax state (running max in log2 units, normaliser,
+// unnormalised output), the block part leaves one more, and a combine kernel
+// merges them in a fixed order.
+//
+// bf16 layers run ONE streaming kernel with three workgroup roles, dispatched
+// in this order so the short ones overlap the long KV stream:
+//   conv   the conv/IIR scan of 16 channels (conv_iir_body.h)
+//   tail   the causal block part of one (sequence, candidate, head)
+//   prefix one chunk of one (sequence, head): four waves, each streaming a
+//          contiguous run of 32-key tiles with non-temporal 16-byte loads
+//          (a contiguous kilobyte per wave-wide load, thanks to the tiled
+//          cache layout) and one tile prefetched into registers; scores
+//          S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with the
+//          keys in M and up to 16*NQT queries in N; online softmax in fp32
+//          registers; the four waves' states merge in LDS before one partial
+//          is written.
+// fp32 layers (small shapes) use separate conv, tail, prefix (vector ALU)
+// and combine kernels.
+#include "conv_iir_body.h"
 
 #include <math.h>
 
 namespace hci {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kRoleT = 256;            // threads per workgroup of every streaming role
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x8 ones_bf16x8() {
+    return as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));   // eight bf16 1.0
 }
 
 // ------------------------------------------------------------ bf16 prefix
@@ -33,27 +47,121 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 constexpr int kPrefixWaves = 4;      // waves per workgroup; their partials merge in LDS
 
 template <int DH, int NQT>
-constexpr size_t prefix_merge_floats() {
+__host__ __device__ constexpr size_t prefix_merge_floats() {
     // per merged wave: O^T accumulators (16*NQT queries x DH), running max, normaliser
     return (size_t)NQT * 16 * DH + 2 * NQT * 16;
 }
 
+// Per-wave register state of the prefix kernel: queries (B operands), the
+// O^T accumulators, running max (log2 units) and lane-partial normaliser.
 template <int DH, int NQT>
-__global__ __launch_bounds__(64 * kPrefixWaves) void k_attn_prefix_bf16(
-    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ kv_len, const uint16_t* __restrict__ q,
-    float* __restrict__ part_o, float* __restrict__ part_ml,
-    int H, int kv_cap, int nq, int chunk_tiles, int n_chunks, float scale_log2)
+struct PrefixAcc {
+    bf16x8 q[NQT][DH / 32];
+    f32x4 o[DH / 16][NQT];
+    float m[NQT], l[NQT];
+};
+
+template <int DH>
+struct KvTile {
+    uint4 k[2 * (DH / 32)];   // two 16-key halves x DH/32 k-steps
+    uint4 v[DH / 16];         // DH/16 value-product tiles
+};
+
+template <int DH>
+__device__ __forceinline__ void load_tile(KvTile<DH>& t, const uint4* kp, const uint4* vp, int T, int lane) {
+    constexpr int KV4 = 4 * DH;
+    const size_t base = (size_t)T * KV4;
+#pragma unroll
+    for (int i = 0; i < 2 * (DH / 32); ++i) t.k[i] = load_nt(kp + base + i * 64 + lane);
+#pragma unroll
+    for (int i = 0; i < DH / 16; ++i) t.v[i] = load_nt(vp + base + i * 64 + lane);
+}
+
+// One 32-key tile: S^T = K Q^T on the matrix cores, online softmax in fp32,
+// O^T += V^T P^T on the matrix cores.  Keys >= L (the ragged end) are masked.
+template <int DH, int NQT>
+__device__ __forceinline__ void consume_tile(PrefixAcc<DH, NQT>& a, KvTile<DH>& t, int T, int L, int g,
+                                             float scale_log2) {
+    constexpr int J = DH / 32, DT = DH / 16;
+    const int kbase = T * kTile;
+    const bool tail = kbase + kTile > L;
+    if (tail) {
+        // zero value rows past the prefix so that 0 * (stale bits) cannot poison the sums
+#pragma unroll
+        for (int i = 0; i < DT; ++i) {
+            uint32_t w[4] = {t.v[i].x, t.v[i].y, t.v[i].z, t.v[i].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int key = kbase + 16 * (e >> 2) + 4 * g + (e & 3);
+                if (key >= L) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            }
+            t.v[i] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+        float s[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[u * J + j]), a.q[nt][j], acc, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = acc[r] * scale_log2;
+                if (tail && kbase + 16 * u + 4 * g + r >= L) v = -INFINITY;
+                s[u][r] = v;
+            }
+        }
+        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(a.m[nt], mx);
+        const float alpha = __builtin_amdgcn_exp2f(a.m[nt] - mnew);
+        a.m[nt] = mnew;
+        f32x2 pf[4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            pf[2 * u] = f32x2{__builtin_amdgcn_exp2f(s[u][0] - mnew), __builtin_amdgcn_exp2f(s[u][1] - mnew)};
+            pf[2 * u + 1] = f32x2{__builtin_amdgcn_exp2f(s[u][2] - mnew), __builtin_amdgcn_exp2f(s[u][3] - mnew)};
+        }
+        const bf16x8 pb = __builtin_shufflevector(
+            __builtin_shufflevector(__builtin_convertvector(pf[0], bf16x2), __builtin_convertvector(pf[1], bf16x2), 0, 1, 2, 3),
+            __builtin_shufflevector(__builtin_convertvector(pf[2], bf16x2), __builtin_convertvector(pf[3], bf16x2), 0, 1, 2, 3),
+            0, 1, 2, 3, 4, 5, 6, 7);                            // round to nearest even
+        // the running max only grows now and then: skip the rescale when no lane of the wave needs it
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+            for (int i = 0; i < DT; ++i) a.o[i][nt] *= alpha;
+            a.l[nt] *= alpha;
+        }
+#pragma unroll
+        for (int i = 0; i < DT; ++i)
+            a.o[i][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.v[i]), pb, a.o[i][nt], 0, 0, 0);
+        // normaliser = the same product against a row of ones: it sums exactly the bf16
+        // weights the value product used, and every lane of query n receives it
+        const f32x4 lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_bf16x8(), pb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        a.l[nt] += lsum[0];
+    }
+}
+
+
+// One prefix workgroup: chunk `chunk` of head h of sequence b, all nq queries.
+// Partials: part_o [nb][H][slots][nq][DH], part_ml [..][2], slot = chunk.
+template <int DH, int NQT>
+__device__ __forceinline__ void prefix_block(
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int L,
+    const uint16_t* __restrict__ q, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int H, int kv_cap, int nq, int chunk_tiles, int slots, float scale_log2,
+    int chunk, int h, int b, float* merge)
 {
     constexpr int J = DH / 32;          // k-steps of the score product
     constexpr int DT = DH / 16;         // 16-wide output tiles of the value product
     constexpr int KV4 = 4 * DH;         // uint4 per tile (32 keys x DH bf16)
     constexpr size_t MF = prefix_merge_floats<DH, NQT>();
-    extern __shared__ float merge[];    // [kPrefixWaves-1][MF]
 
-    const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    int L = kv_len[b];
-    L = L < 0 ? 0 : (L > kv_cap ? kv_cap : L);
     const int tiles = (L + kTile - 1) / kTile;
     const int t0 = chunk * chunk_tiles;
     if (t0 >= tiles) return;                           // whole workgroup
@@ -61,11 +169,10 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void k_attn_prefix_bf16(
     const int wave = threadIdx.x >> 6;
     const int per = (t1 - t0 + kPrefixWaves - 1) / kPrefixWaves;
     const int w0 = min(t0 + wave * per, t1), w1 = min(w0 + per, t1);   // wave 0 is never empty
-
     const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
 
+    PrefixAcc<DH, NQT> a;
     // queries as B operands: lane (g, n) holds Q[16nt+n][32j+8g .. 32j+8g+7]
-    bf16x8 qreg[NQT][J];
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
         const int qi = 16 * nt + n;
@@ -73,115 +180,24 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void k_attn_prefix_bf16(
         for (int j = 0; j < J; ++j) {
             uint4 v = make_uint4(0, 0, 0, 0);
             if (qi < nq) v = *(const uint4*)(q + (((size_t)b * nq + qi) * H + h) * DH + 32 * j + 8 * g);
-            qreg[nt][j] = as_bf16x8(v);
+            a.q[nt][j] = as_bf16x8(v);
         }
-    }
-
-    f32x4 oacc[DT][NQT];
-    float mrun[NQT], lrun[NQT];
+        a.m[nt] = -INFINITY;
+        a.l[nt] = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) {
-        mrun[nt] = -INFINITY;
-        lrun[nt] = 0.f;
-#pragma unroll
-        for (int t = 0; t < DT; ++t) oacc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < DT; ++t) a.o[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     const size_t slab = ((size_t)b * H + h) * (size_t)(kv_cap / kTile) * KV4;
     const uint4* kp = (const uint4*)kc + slab;
     const uint4* vp = (const uint4*)vc + slab;
-
-    uint4 kr[2 * J], vr[DT];
-    if (w0 < w1) {
-#pragma unroll
-        for (int i = 0; i < 2 * J; ++i) kr[i] = kp[(size_t)w0 * KV4 + i * 64 + lane];
-#pragma unroll
-        for (int t = 0; t < DT; ++t) vr[t] = vp[(size_t)w0 * KV4 + t * 64 + lane];
-    }
-
+    KvTile<DH> cur, nxt;
+    if (w0 < w1) load_tile<DH>(cur, kp, vp, w0, lane);
     for (int T = w0; T < w1; ++T) {
-        uint4 kn[2 * J], vn[DT];
         const bool more = T + 1 < w1;
-        if (more) {
-            const size_t base = (size_t)(T + 1) * KV4;
-#pragma unroll
-            for (int i = 0; i < 2 * J; ++i) kn[i] = kp[base + i * 64 + lane];
-#pragma unroll
-            for (int t = 0; t < DT; ++t) vn[t] = vp[base + t * 64 + lane];
-        }
-
-        const int kbase = T * kTile;
-        const bool tail = kbase + kTile > L;
-        if (tail) {
-            // zero value rows past the prefix so that 0 * (stale bits) cannot poison the sums
-#pragma unroll
-            for (int t = 0; t < DT; ++t) {
-                uint32_t w[4] = {vr[t].x, vr[t].y, vr[t].z, vr[t].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int key = kbase + 16 * (e >> 2) + 4 * g + (e & 3);
-                    if (key >= L) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-                }
-                vr[t] = make_uint4(w[0], w[1], w[2], w[3]);
-            }
-        }
-
-#pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) {
-            float s[2][4];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int j = 0; j < J; ++j)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[u * J + j]), qreg[nt][j], acc, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = acc[r] * scale_log2;
-                    if (tail && kbase + 16 * u + 4 * g + r >= L) v = -INFINITY;
-                    s[u][r] = v;
-                }
-            }
-            float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                             fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(mrun[nt], mx);
-            const float alpha = exp2f(mrun[nt] - mnew);
-            mrun[nt] = mnew;
-            uint32_t pk[4];
-            float psum = 0.f;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const float p0 = exp2f(s[u][0] - mnew), p1 = exp2f(s[u][1] - mnew);
-                const float p2 = exp2f(s[u][2] - mnew), p3 = exp2f(s[u][3] - mnew);
-                pk[2 * u] = pack_bf16x2(p0, p1);
-                pk[2 * u + 1] = pack_bf16x2(p2, p3);
-                // the normaliser sums the same bf16-rounded weights the value product uses
-                psum += (bf2f(pk[2 * u] & 0xffff) + bf2f(pk[2 * u] >> 16)) +
-                        (bf2f(pk[2 * u + 1] & 0xffff) + bf2f(pk[2 * u + 1] >> 16));
-            }
-            lrun[nt] = fmaf(lrun[nt], alpha, psum);
-            const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-#pragma unroll
-            for (int t = 0; t < DT; ++t) {
-                oacc[t][nt] *= alpha;
-                oacc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[t]), pb, oacc[t][nt], 0, 0, 0);
-            }
-        }
-
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < 2 * J; ++i) kr[i] = kn[i];
-#pragma unroll
-            for (int t = 0; t < DT; ++t) vr[t] = vn[t];
-        }
-    }
-
-#pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) {
-        lrun[nt] += __shfl_xor(lrun[nt], 16);
-        lrun[nt] += __shfl_xor(lrun[nt], 32);
+        if (more) load_tile<DH>(nxt, kp, vp, T + 1, lane);
+        consume_tile<DH, NQT>(a, cur, T, L, g, scale_log2);
+        if (more) cur = nxt;
     }
 
     // merge the four waves' partial softmax states in LDS (fixed order: wave 0, 1, 2, 3)
@@ -192,37 +208,35 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void k_attn_prefix_bf16(
 #pragma unroll
             for (int t = 0; t < DT; ++t)
                 *(float4*)(mw + (((size_t)nt * DT + t) * 64 + lane) * 4) =
-                    make_float4(oacc[t][nt][0], oacc[t][nt][1], oacc[t][nt][2], oacc[t][nt][3]);
+                    make_float4(a.o[t][nt][0], a.o[t][nt][1], a.o[t][nt][2], a.o[t][nt][3]);
             if (g == 0) {
-                mw[(size_t)NQT * 16 * DH + nt * 16 + n] = mrun[nt];
-                mw[(size_t)NQT * 16 * DH + NQT * 16 + nt * 16 + n] = lrun[nt];
+                mw[(size_t)NQT * 16 * DH + nt * 16 + n] = a.m[nt];
+                mw[(size_t)NQT * 16 * DH + NQT * 16 + nt * 16 + n] = a.l[nt];
             }
         }
     }
     __syncthreads();
     if (wave > 0) return;
 
-    // partial softmax state of this chunk: part_o [nb][H][n_chunks][nq][DH] (unnormalised),
-    // part_ml [..][nq][2] = (running max in log2 units, normaliser)
-    const size_t pbase = (((size_t)b * H + h) * n_chunks + chunk) * nq;
+    const size_t pbase = (((size_t)b * H + h) * slots + chunk) * nq;
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
-        float M = mrun[nt];
+        float M = a.m[nt];
 #pragma unroll
         for (int w = 1; w < kPrefixWaves; ++w) M = fmaxf(M, merge[(w - 1) * MF + (size_t)NQT * 16 * DH + nt * 16 + n]);
         float sc[kPrefixWaves];
-        sc[0] = exp2f(mrun[nt] - M);
-        float l = sc[0] * lrun[nt];
+        sc[0] = __builtin_amdgcn_exp2f(a.m[nt] - M);
+        float l = sc[0] * a.l[nt];
 #pragma unroll
         for (int w = 1; w < kPrefixWaves; ++w) {
             const float* mw = merge + (size_t)(w - 1) * MF;
-            sc[w] = exp2f(mw[(size_t)NQT * 16 * DH + nt * 16 + n] - M);
+            sc[w] = __builtin_amdgcn_exp2f(mw[(size_t)NQT * 16 * DH + nt * 16 + n] - M);
             l = fmaf(sc[w], mw[(size_t)NQT * 16 * DH + NQT * 16 + nt * 16 + n], l);
         }
         const int qi = 16 * nt + n;
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-            f32x4 acc = oacc[t][nt] * sc[0];
+            f32x4 acc = a.o[t][nt] * sc[0];
 #pragma unroll
             for (int w = 1; w < kPrefixWaves; ++w) {
                 const float4 o = *(const float4*)(merge + (size_t)(w - 1) * MF + (((size_t)nt * DT + t) * 64 + lane) * 4);
@@ -235,6 +249,137 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void k_attn_prefix_bf16(
         }
         if (qi < nq && g == 0) *(float2*)(part_ml + (pbase + qi) * 2) = make_float2(M, l);
     }
+}
+
+// ------------------------------------------------------------- block part
+//
+// One workgroup per (sequence, candidate, head): the P block queries attend
+// causally to the block's own keys (query i sees keys 0..i), in fp32.  The
+// result is one more partial softmax state, in slot `tail_slot`.
+
+constexpr int kMaxP = 64;
+
+// LDS floats of the block part: scores [P][P+1], row max and sum, and the
+// q and k rows of the block staged as raw activations
+__host__ __device__ constexpr size_t tail_lds_floats(int P, int DH, int act_bytes) {
+    return (size_t)P * (P + 1) + 2 * P + ((size_t)2 * P * DH * act_bytes + 3) / 4;
+}
+
+template <int ACT>
+__device__ __forceinline__ void tail_block(
+    const typename Act<ACT>::T* __restrict__ q, const typename Act<ACT>::T* __restrict__ kb,
+    const typename Act<ACT>::T* __restrict__ vb, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int H, int DH, int P, int nq, int slots, int tail_slot, float scale_log2, int c, int h, int b, float* lds)
+{
+    typedef typename Act<ACT>::T T;
+    float* S = lds;                                   // [P][P + 1] scores, then weights
+    float* mrow = S + P * (P + 1);                    // [P]
+    float* lrow = mrow + P;                           // [P]
+    T* qs = (T*)(lrow + P);                           // [P][DH]
+    T* ks = qs + (size_t)P * DH;                      // [P][DH]
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const size_t row0 = (size_t)b * nq + (size_t)c * P;          // block row of position 0
+    for (int e = tid; e < P * DH; e += nthr) {
+        const int i = e / DH, dd = e % DH;
+        const size_t o = ((row0 + i) * H + h) * DH + dd;
+        qs[e] = q[o];
+        ks[e] = kb[o];
+    }
+    __syncthreads();
+    // scores s_ij = q_i . k_j * scale (log2 units), j <= i
+    const int npairs = P * (P + 1) / 2;
+    for (int p = tid; p < npairs; p += nthr) {
+        int i = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+        while ((i + 1) * (i + 2) / 2 <= p) ++i;
+        while (i * (i + 1) / 2 > p) --i;
+        const int j = p - i * (i + 1) / 2;
+        float acc = 0.f;
+        for (int dd = 0; dd < DH; ++dd) acc = fmaf(Act<ACT>::load(qs, (size_t)i * DH + dd), Act<ACT>::load(ks, (size_t)j * DH + dd), acc);
+        S[i * (P + 1) + j] = acc * scale_log2;
+    }
+    __syncthreads();
+    if (tid < P) {
+        const int i = tid;
+        float m = -INFINITY;
+        for (int j = 0; j <= i; ++j) m = fmaxf(m, S[i * (P + 1) + j]);
+        float l = 0.f;
+        for (int j = 0; j <= i; ++j) {
+            const float w = __builtin_amdgcn_exp2f(S[i * (P + 1) + j] - m);
+            S[i * (P + 1) + j] = w;
+            l += w;
+        }
+        mrow[i] = m;
+        lrow[i] = l;
+    }
+    __syncthreads();
+    const size_t pbase = (((size_t)b * H + h) * slots + tail_slot) * nq + (size_t)c * P;
+    for (int e = tid; e < P * DH; e += nthr) {
+        const int i = e / DH, dd = e % DH;
+        float acc = 0.f;
+        for (int j = 0; j <= i; ++j)
+            acc = fmaf(S[i * (P + 1) + j], Act<ACT>::load(vb, ((row0 + j) * H + h) * DH + dd), acc);
+        part_o[(pbase + i) * DH + dd] = acc;
+    }
+    for (int i = tid; i < P; i += nthr) *(float2*)(part_ml + (pbase + i) * 2) = make_float2(mrow[i], lrow[i]);
+}
+
+// ------------------------------------------------------ fused bf16 kernel
+
+struct StreamArgs {
+    // conv / IIR
+    const float *w_short, *w_outer, *lam, *beta, *cc;
+    const uint16_t* short_win; const float* outer_win; const float* iir; const uint16_t* x;
+    float* f_out; float* s_out; uint16_t* y_out;
+    int d, Ts, To, N;
+    // attention
+    const uint16_t *kc, *vc, *q, *kb, *vb; const int32_t* kv_len;
+    float *part_o, *part_ml;
+    int H, kv_cap, nq, chunk_tiles, n_chunks, slots, P, nc;
+    float scale_log2;
+    // role layout: prefix workgroups first, then conv, then the block part
+    int prefix_blocks, prefix_x, n_conv, n_tail;
+};
+
+template <int DH, int NQT>
+__global__ __launch_bounds__(kRoleT) void k_verify_stream(StreamArgs A)
+{
+    extern __shared__ float lds[];
+    const int id = blockIdx.x;
+    if (id < A.prefix_blocks) {
+        const int chunk = id % A.prefix_x, h = (id / A.prefix_x) % A.H, b = id / (A.prefix_x * A.H);
+        if (chunk >= A.n_chunks) return;
+        int L = A.kv_len[b];
+        L = L < 0 ? 0 : (L > A.kv_cap ? A.kv_cap : L);
+        prefix_block<DH, NQT>(A.kc, A.vc, L, A.q, A.part_o, A.part_ml, A.H, A.kv_cap, A.nq, A.chunk_tiles, A.slots,
+                              A.scale_log2, chunk, h, b, lds);
+        return;
+    }
+    // the short roles come last: they fill the slots the KV stream frees as it drains
+    const int r = id - A.prefix_blocks;
+    if (r < A.n_conv) {
+        const int groups = (A.d + kCG - 1) / kCG;
+        const int cgi = r % groups, c = (r / groups) % A.nc, b = r / (groups * A.nc);
+        conv_iir_block<HCI_BF16>(A.w_short, A.w_outer, A.lam, A.beta, A.cc, A.short_win, A.outer_win, A.iir, A.x,
+                                 A.f_out, A.s_out, A.y_out, A.d, A.Ts, A.To, A.N, A.nc, A.P, cgi, c, b, lds);
+        return;
+    }
+    const int t = r - A.n_conv;
+    const int h = t % A.H, c = (t / A.H) % A.nc, b = t / (A.H * A.nc);
+    tail_block<HCI_BF16>(A.q, A.kb, A.vb, A.part_o, A.part_ml, A.H, DH, A.P, A.nq, A.slots, A.n_chunks,
+                         A.scale_log2, c, h, b, lds);
+}
+
+// -------------------------------------------------- stand-alone fp32 parts
+
+template <int ACT>
+__global__ __launch_bounds__(kRoleT) void k_attn_tail(
+    const typename Act<ACT>::T* __restrict__ q, const typename Act<ACT>::T* __restrict__ kb,
+    const typename Act<ACT>::T* __restrict__ vb, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int H, int DH, int P, int nq, int slots, int tail_slot, float scale_log2)
+{
+    extern __shared__ float lds[];
+    tail_block<ACT>(q, kb, vb, part_o, part_ml, H, DH, P, nq, slots, tail_slot, scale_log2,
+                    blockIdx.y, blockIdx.x, blockIdx.z, lds);
 }
 
 // ------------------------------------------------------------- f32 prefix
@@ -251,7 +396,7 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
     const float* __restrict__ kc, const float* __restrict__ vc,
     const int32_t* __restrict__ kv_len, const float* __restrict__ q,
     float* __restrict__ part_o, float* __restrict__ part_ml,
-    int H, int DH, int kv_cap, int nq, int chunk_tiles, int n_chunks, float scale_log2)
+    int H, int DH, int kv_cap, int nq, int chunk_tiles, int slots, float scale_log2)
 {
     __shared__ float ks[kTile][kF32Dh + 1];
     __shared__ float vs[kTile][kF32Dh + 1];
@@ -328,7 +473,7 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
             }
         }
     }
-    const size_t pbase = (((size_t)b * H + h) * n_chunks + chunk) * nq;
+    const size_t pbase = (((size_t)b * H + h) * slots + chunk) * nq;
 #pragma unroll
     for (int qi = 0; qi < kF32Nq; ++qi) {
         if (qi < nq) {
@@ -347,77 +492,52 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
 
 // ----------------------------------------------------------------- combine
 //
-// One workgroup of 256 threads per (query, head, sequence).  First the
-// causal part over the block's own keys 0..i is computed in fp32 (one
-// partial softmax state), then the prefix partials are merged with it:
-//   M = max(m_tail, m_c), w_c = 2^(m_c - M),
-//   o = (sum_c w_c O_c + 2^(m_tail - M) O_tail) / (sum_c w_c l_c + 2^(m_tail - M) l_tail)
-// Chunk weights are formed once per chunk in LDS; thread groups accumulate
-// interleaved chunks and are merged in a fixed order, so the result does not
-// depend on scheduling.
+// One workgroup of 256 threads per (query, head, sequence) merges the chunk
+// partials (slots 0..nch-1, nch from kv_len) and the block part (slot
+// n_chunks):  M = max m_s, w_s = 2^(m_s - M),
+//   o = sum_s w_s O_s / sum_s w_s l_s,
+// with the chunks taken in a fixed interleave and the group sums merged in a
+// fixed order, so the result does not depend on scheduling.
 
 constexpr int kCombT = 256;
 constexpr int kMaxChunks = 4096;     // the split-K plan never exceeds this
 
 template <int ACT>
 __global__ __launch_bounds__(kCombT) void k_attn_combine(
-    const typename Act<ACT>::T* __restrict__ q, const typename Act<ACT>::T* __restrict__ kb,
-    const typename Act<ACT>::T* __restrict__ vb, const int32_t* __restrict__ kv_len,
-    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ kv_len, const float* __restrict__ part_o, const float* __restrict__ part_ml,
     typename Act<ACT>::T* __restrict__ o,
-    int H, int DH, int P, int nq, int kv_cap, int chunk_tiles, int n_chunks, float scale_log2)
+    int H, int DH, int nq, int kv_cap, int chunk_tiles, int n_chunks, int slots, float scale_log2)
 {
-    __shared__ float wts[kMaxChunks];
-    __shared__ float red[kCombT / 64][64];
-    __shared__ float sc[64];
+    __shared__ float wts[kMaxChunks + 1];
+    __shared__ float red[kCombT / 64][2];
     __shared__ float acc_s[kCombT];
 
     const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int c = qi / P, i = qi % P;
     const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
     const int nw = kCombT / 64;
 
-    // ---- block part: scores of keys 0..i (two-level fixed-order reduction)
-    const size_t rowq = (((size_t)b * nq + qi) * H + h) * DH;
-    const size_t rowb = ((size_t)b * nq + (size_t)c * P) * H;   // + j*H + h for block row j
-    const float qd = tid < DH ? Act<ACT>::load(q, rowq + tid) : 0.f;
-    for (int j = 0; j <= i; ++j) {
-        float v = tid < DH ? qd * Act<ACT>::load(kb, (rowb + (size_t)j * H + h) * DH + tid) : 0.f;
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-        if (ln == 0) red[wave][j] = v;
-    }
-    __syncthreads();
-    if (tid <= i) {
-        float s = 0.f;
-        for (int w = 0; w < nw; ++w) s += red[w][tid];
-        sc[tid] = s * scale_log2;
-    }
-    __syncthreads();
-    float mt = -INFINITY;
-    for (int j = 0; j <= i; ++j) mt = fmaxf(mt, sc[j]);
-
-    // ---- prefix partials: running max over chunks
     int L = kv_len[b];
     L = L < 0 ? 0 : (L > kv_cap ? kv_cap : L);
     const int tiles = (L + kTile - 1) / kTile;
     int nch = (tiles + chunk_tiles - 1) / chunk_tiles;
     nch = nch > n_chunks ? n_chunks : nch;
-    const size_t pb = ((size_t)b * H + h) * n_chunks;
+    const size_t pb = ((size_t)b * H + h) * slots;
+    auto slot_of = [&](int s) { return s < nch ? s : n_chunks; };    // s == nch is the block part
+    const int ns = nch + 1;
+
     float mloc = -INFINITY;
-    for (int ck = tid; ck < nch; ck += kCombT) mloc = fmaxf(mloc, part_ml[((pb + ck) * nq + qi) * 2]);
+    for (int s = tid; s < ns; s += kCombT) mloc = fmaxf(mloc, part_ml[((pb + slot_of(s)) * nq + qi) * 2]);
     for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
     if (ln == 0) red[wave][0] = mloc;
     __syncthreads();
-    float M = mt;
-    for (int w = 0; w < nw; ++w) M = fmaxf(M, red[w][0]);
-    __syncthreads();
+    float M = red[0][0];
+    for (int w = 1; w < nw; ++w) M = fmaxf(M, red[w][0]);
 
-    // ---- chunk weights and the normaliser
     float lloc = 0.f;
-    for (int ck = tid; ck < nch; ck += kCombT) {
-        const float2 ml = *(const float2*)(part_ml + ((pb + ck) * nq + qi) * 2);
+    for (int s = tid; s < ns; s += kCombT) {
+        const float2 ml = *(const float2*)(part_ml + ((pb + slot_of(s)) * nq + qi) * 2);
         const float w = exp2f(ml.x - M);
-        wts[ck] = w;
+        wts[s] = w;
         lloc = fmaf(w, ml.y, lloc);
     }
     for (int off = 32; off >= 1; off >>= 1) lloc += __shfl_xor(lloc, off);
@@ -426,38 +546,30 @@ __global__ __launch_bounds__(kCombT) void k_attn_combine(
     float l = 0.f;
     for (int w = 0; w < nw; ++w) l += red[w][1];
 
-    // ---- weighted sum of the chunk outputs: thread (group, d) takes chunks group, group+ng, ...
+    // thread (group, d) accumulates slots group, group+ng, ...
     const int ng = kCombT / DH;
     const int grp = tid / DH, dd = tid % DH;
     float acc = 0.f;
     if (grp < ng) {
-        int ck = grp;
-        for (; ck + 3 * ng < nch; ck += 4 * ng) {
-            const float o0 = part_o[((pb + ck) * nq + qi) * DH + dd];
-            const float o1 = part_o[((pb + ck + ng) * nq + qi) * DH + dd];
-            const float o2 = part_o[((pb + ck + 2 * ng) * nq + qi) * DH + dd];
-            const float o3 = part_o[((pb + ck + 3 * ng) * nq + qi) * DH + dd];
-            acc = fmaf(wts[ck], o0, acc);
-            acc = fmaf(wts[ck + ng], o1, acc);
-            acc = fmaf(wts[ck + 2 * ng], o2, acc);
-            acc = fmaf(wts[ck + 3 * ng], o3, acc);
+        int s = grp;
+        for (; s + 3 * ng < ns; s += 4 * ng) {
+            const float o0 = part_o[((pb + slot_of(s)) * nq + qi) * DH + dd];
+            const float o1 = part_o[((pb + slot_of(s + ng)) * nq + qi) * DH + dd];
+            const float o2 = part_o[((pb + slot_of(s + 2 * ng)) * nq + qi) * DH + dd];
+            const float o3 = part_o[((pb + slot_of(s + 3 * ng)) * nq + qi) * DH + dd];
+            acc = fmaf(wts[s], o0, acc);
+            acc = fmaf(wts[s + ng], o1, acc);
+            acc = fmaf(wts[s + 2 * ng], o2, acc);
+            acc = fmaf(wts[s + 3 * ng], o3, acc);
         }
-        for (; ck < nch; ck += ng) acc = fmaf(wts[ck], part_o[((pb + ck) * nq + qi) * DH + dd], acc);
+        for (; s < ns; s += ng) acc = fmaf(wts[s], part_o[((pb + slot_of(s)) * nq + qi) * DH + dd], acc);
     }
     acc_s[tid] = acc;
     __syncthreads();
-
     if (tid < DH) {
         float tot = 0.f;
         for (int g2 = 0; g2 < ng; ++g2) tot += acc_s[g2 * DH + tid];
-        // block part: weights 2^(s_j - M) directly in the merged frame
-        float lt = 0.f, ot = 0.f;
-        for (int j = 0; j <= i; ++j) {
-            const float p = exp2f(sc[j] - M);
-            lt += p;
-            ot = fmaf(p, Act<ACT>::load(vb, (rowb + (size_t)j * H + h) * DH + tid), ot);
-        }
-        Act<ACT>::store(o, rowq + tid, (tot + ot) / (l + lt));
+        Act<ACT>::store(o, (((size_t)b * nq + qi) * H + h) * DH + tid, tot / l);
     }
 }
 
@@ -483,82 +595,137 @@ AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_k
     if (ct < 1) ct = 1;
     p.chunk_tiles = (int)ct;
     p.n_chunks = tiles > 0 ? (int)((tiles + ct - 1) / ct) : 0;
-    p.part_o_elems = (size_t)nb * L->heads * p.n_chunks * p.nq * L->head_dim;
-    p.part_ml_elems = (size_t)nb * L->heads * p.n_chunks * p.nq * 2;
+    p.slots = p.n_chunks + 1;                       // + the block part
+    p.part_o_elems = (size_t)nb * L->heads * p.slots * p.nq * L->head_dim;
+    p.part_ml_elems = (size_t)nb * L->heads * p.slots * p.nq * 2;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     p.bytes = up(p.part_o_elems * 4) + up(p.part_ml_elems * 4);
     return p;
 }
 
-hipError_t launch_attention(const hci_layer* L, const hci_state* S, const hci_block* blk,
-                            int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st,
-                            hipEvent_t* after_prefix)
+size_t stream_lds_bytes(const hci_layer* L, int nc, int P) {
+    const int nqt = (nc * P + 15) / 16;
+    const size_t pre = (kPrefixWaves - 1) * (size_t)nqt * (16 * L->head_dim + 32);
+    const int act_bytes = L->act_dtype == HCI_BF16 ? 2 : 4;
+    size_t f = conv_iir_lds_floats(L->taps_outer, P);
+    const size_t t = tail_lds_floats(P, L->head_dim, act_bytes);
+    f = f > t ? f : t;
+    f = f > pre ? f : pre;
+    return f * sizeof(float);
+}
+
+template <int DH, int NQT>
+static hipError_t launch_stream(const StreamArgs& A, int blocks, size_t lds, hipStream_t st) {
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)k_verify_stream<DH, NQT>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_verify_stream<DH, NQT>), dim3(blocks), dim3(kRoleT), lds, st, A);
+    return hipGetLastError();
+}
+
+hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                         int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st, hipEvent_t* ev)
 {
     const int H = L->heads, DH = L->head_dim, nq = plan.nq;
     const float scale_log2 = kLog2e / sqrtf((float)DH);
     float* part_o = (float*)ws;
     float* part_ml = (float*)((char*)ws + (plan.part_o_elems * 4 + 255) / 256 * 256);
+    auto mark = [&](int i) { return (ev && ev[i]) ? hipEventRecord(ev[i], st) : hipSuccess; };
+    hipError_t e = mark(0);
+    if (e != hipSuccess) return e;
 
-    if (plan.n_chunks > 0) {
-        dim3 grid(plan.n_chunks, H, nb), block(64);
-        if (L->act_dtype == HCI_BF16) {
-            const int nqt = (nq + 15) / 16;
-#define HCI_PREFIX(DHV, NQTV)                                                                      \
-    do {                                                                                           \
-        const size_t lds = (kPrefixWaves - 1) * prefix_merge_floats<DHV, NQTV>() * sizeof(float);  \
-        if (lds > 65536) {                                                                         \
-            hipError_t ea = hipFuncSetAttribute((const void*)k_attn_prefix_bf16<DHV, NQTV>,        \
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-            if (ea != hipSuccess) return ea;                                                       \
-        }                                                                                          \
-        hipLaunchKernelGGL((k_attn_prefix_bf16<DHV, NQTV>), grid, dim3(64 * kPrefixWaves), lds, st, \
-                           (const uint16_t*)S->k_cache, (const uint16_t*)S->v_cache, S->kv_len,    \
-                           (const uint16_t*)blk->q, part_o, part_ml, H, S->kv_cap, nq,             \
-                           plan.chunk_tiles, plan.n_chunks, scale_log2);                           \
-    } while (0)
+    if (L->act_dtype == HCI_BF16) {
+        StreamArgs A{};
+        A.w_short = L->w_short; A.w_outer = L->w_outer; A.lam = L->lambda; A.beta = L->beta; A.cc = L->c;
+        A.short_win = (const uint16_t*)S->short_win; A.outer_win = S->outer_win; A.iir = S->iir;
+        A.x = (const uint16_t*)blk->x; A.f_out = blk->f; A.s_out = blk->s; A.y_out = (uint16_t*)blk->y;
+        A.d = L->d; A.Ts = L->taps_short; A.To = L->taps_outer; A.N = L->poles;
+        A.kc = (const uint16_t*)S->k_cache; A.vc = (const uint16_t*)S->v_cache; A.q = (const uint16_t*)blk->q;
+        A.kb = (const uint16_t*)blk->k; A.vb = (const uint16_t*)blk->v; A.kv_len = S->kv_len;
+        A.part_o = part_o; A.part_ml = part_ml;
+        A.H = H; A.kv_cap = S->kv_cap; A.nq = nq; A.chunk_tiles = plan.chunk_tiles; A.n_chunks = plan.n_chunks;
+        A.slots = plan.slots; A.P = P; A.nc = nc; A.scale_log2 = scale_log2;
+        A.prefix_x = plan.n_chunks;
+        A.prefix_blocks = plan.n_chunks * H * nb;
+        const int nqt = (nq + 15) / 16;
+        // With one query tile the streaming kernel keeps two workgroups per CU and the
+        // short roles ride along at the end of its grid.  With more query tiles it holds
+        // a whole CU per workgroup, so the short roles run as their own light kernels.
+        const bool fuse = nqt == 1;
+        if (!fuse) {
+            e = launch_conv_iir(L, S, blk, nb, nc, P, st);
+            if (e != hipSuccess) return e;
+            const size_t tail_lds = tail_lds_floats(P, DH, 2) * sizeof(float);
+            if (tail_lds > 65536) {
+                e = hipFuncSetAttribute((const void*)k_attn_tail<HCI_BF16>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        (int)tail_lds);
+                if (e != hipSuccess) return e;
+            }
+            hipLaunchKernelGGL(k_attn_tail<HCI_BF16>, dim3(H, nc, nb), dim3(kRoleT), tail_lds, st,
+                               (const uint16_t*)blk->q, (const uint16_t*)blk->k, (const uint16_t*)blk->v, part_o,
+                               part_ml, H, DH, P, nq, plan.slots, plan.n_chunks, scale_log2);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        A.n_conv = fuse ? ((L->d + kCG - 1) / kCG) * nc * nb : 0;
+        A.n_tail = fuse ? nb * nc * H : 0;
+        const long long blocks = (long long)A.prefix_blocks + A.n_conv + A.n_tail;
+        if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+        const size_t lds = stream_lds_bytes(L, nc, P);
+        if (blocks > 0) {
             if (DH == 128) {
                 switch (nqt) {
-                    case 1: HCI_PREFIX(128, 1); break;
-                    case 2: HCI_PREFIX(128, 2); break;
-                    case 3: HCI_PREFIX(128, 3); break;
-                    default: HCI_PREFIX(128, 4); break;
+                    case 1: e = launch_stream<128, 1>(A, (int)blocks, lds, st); break;
+                    case 2: e = launch_stream<128, 2>(A, (int)blocks, lds, st); break;
+                    case 3: e = launch_stream<128, 3>(A, (int)blocks, lds, st); break;
+                    default: e = launch_stream<128, 4>(A, (int)blocks, lds, st); break;
                 }
             } else {
                 switch (nqt) {
-                    case 1: HCI_PREFIX(64, 1); break;
-                    case 2: HCI_PREFIX(64, 2); break;
-                    case 3: HCI_PREFIX(64, 3); break;
-                    default: HCI_PREFIX(64, 4); break;
+                    case 1: e = launch_stream<64, 1>(A, (int)blocks, lds, st); break;
+                    case 2: e = launch_stream<64, 2>(A, (int)blocks, lds, st); break;
+                    case 3: e = launch_stream<64, 3>(A, (int)blocks, lds, st); break;
+                    default: e = launch_stream<64, 4>(A, (int)blocks, lds, st); break;
                 }
             }
-#undef HCI_PREFIX
-        } else {
-            hipLaunchKernelGGL(k_attn_prefix_f32, grid, block, 0, st,
+            if (e != hipSuccess) return e;
+        }
+    } else {
+        e = launch_conv_iir(L, S, blk, nb, nc, P, st);
+        if (e != hipSuccess) return e;
+        const size_t tail_lds = tail_lds_floats(P, DH, 4) * sizeof(float);
+        if (tail_lds > 65536) {
+            e = hipFuncSetAttribute((const void*)k_attn_tail<HCI_F32>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)tail_lds);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(k_attn_tail<HCI_F32>, dim3(H, nc, nb), dim3(kRoleT), tail_lds, st,
+                           (const float*)blk->q, (const float*)blk->k, (const float*)blk->v, part_o, part_ml,
+                           H, DH, P, nq, plan.slots, plan.n_chunks, scale_log2);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (plan.n_chunks > 0) {
+            hipLaunchKernelGGL(k_attn_prefix_f32, dim3(plan.n_chunks, H, nb), dim3(64), 0, st,
                                (const float*)S->k_cache, (const float*)S->v_cache, S->kv_len,
                                (const float*)blk->q, part_o, part_ml, H, DH, S->kv_cap, nq,
-                               plan.chunk_tiles, plan.n_chunks, scale_log2);
+                               plan.chunk_tiles, plan.slots, scale_log2);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
     }
-    if (after_prefix && *after_prefix) {
-        hipError_t e = hipEventRecord(*after_prefix, st);
-        if (e != hipSuccess) return e;
-    }
+    if ((e = mark(1)) != hipSuccess) return e;
 
     dim3 cgrid(nq, H, nb), cblock(kCombT);
     if (L->act_dtype == HCI_BF16) {
-        hipLaunchKernelGGL(k_attn_combine<HCI_BF16>, cgrid, cblock, 0, st,
-                           (const uint16_t*)blk->q, (const uint16_t*)blk->k, (const uint16_t*)blk->v,
-                           S->kv_len, part_o, part_ml, (uint16_t*)blk->o, H, DH, P, nq, S->kv_cap,
-                           plan.chunk_tiles, plan.n_chunks, scale_log2);
+        hipLaunchKernelGGL(k_attn_combine<HCI_BF16>, cgrid, cblock, 0, st, S->kv_len, part_o, part_ml,
+                           (uint16_t*)blk->o, H, DH, nq, S->kv_cap, plan.chunk_tiles, plan.n_chunks, plan.slots,
+                           scale_log2);
     } else {
-        hipLaunchKernelGGL(k_attn_combine<HCI_F32>, cgrid, cblock, 0, st,
-                           (const float*)blk->q, (const float*)blk->k, (const float*)blk->v,
-                           S->kv_len, part_o, part_ml, (float*)blk->o, H, DH, P, nq, S->kv_cap,
-                           plan.chunk_tiles, plan.n_chunks, scale_log2);
+        hipLaunchKernelGGL(k_attn_combine<HCI_F32>, cgrid, cblock, 0, st, S->kv_len, part_o, part_ml,
+                           (float*)blk->o, H, DH, nq, S->kv_cap, plan.chunk_tiles, plan.n_chunks, plan.slots,
+                           scale_log2);
     }
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return mark(2);
 }
 
 }  // namespace hci

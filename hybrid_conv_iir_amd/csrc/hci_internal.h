@@ -11,6 +11,15 @@ namespace hci {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal: streamed data that is read exactly once
+// (the KV prefix) bypasses cache retention, which lifts the sustained read
+// rate of a full-chip stream by about 15% on gfx950.
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 constexpr int kTile = HCI_KV_TILE;   // keys per KV tile
 
@@ -80,22 +89,25 @@ struct AttnPlan {
     int nq;            // queries per sequence = nc * P
     int chunk_tiles;   // tiles per split-K chunk
     int n_chunks;      // chunks per (sequence, head), from max_kv_len
+    int slots;         // partial slots per (sequence, head): the chunks, then the block part
     size_t part_o_elems, part_ml_elems;
     size_t bytes;      // workspace bytes (256-aligned sections)
 };
 AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_kv_len, int num_cus);
 int device_cu_count();
 
-// dynamic LDS bytes of the conv/IIR kernel (must not exceed kMaxLds)
+// dynamic LDS bytes of the conv/IIR kernel and of the fused streaming
+// kernel (neither may exceed kMaxLds)
 size_t conv_iir_lds_bytes(int To, int P);
+size_t stream_lds_bytes(const hci_layer* L, int nc, int P);
 constexpr size_t kMaxLds = 160 * 1024;
 
 hipError_t launch_conv_iir(const hci_layer* L, const hci_state* S, const hci_block* blk,
                            int nb, int nc, int P, hipStream_t st);
-// after_prefix (may be null): an event recorded right after the prefix kernel
-hipError_t launch_attention(const hci_layer* L, const hci_state* S, const hci_block* blk,
-                            int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st,
-                            hipEvent_t* after_prefix);
+// the whole verify: streaming kernel(s) then the combine; ev (may be null)
+// = 3 events recorded before, after the streaming part, and at the end
+hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                         int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st, hipEvent_t* ev);
 hipError_t launch_accept(int mode, int nb, int nc, int gamma, int V, float temperature,
                          const float* zt, const float* zd, const int32_t* drafts, const double* u,
                          int32_t* n_acc, int32_t* next, int32_t* best, double* margin, hipStream_t st);

@@ -5,7 +5,7 @@
 
 namespace hci {
 
-constexpr int kProbeBlocks = 256 * 8;   // 8 workgroups per CU on a 256-CU part
+constexpr int kProbeBlocks = 256 * 2;   // 8 waves per CU on a 256-CU part (the sweep optimum)
 constexpr int kProbeThreads = 256;
 
 __global__ __launch_bounds__(kProbeThreads) void k_probe_read(const uint4* __restrict__ src, size_t n16,
@@ -15,7 +15,8 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_read(const uint4* __res
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        const uint4 a = load_nt(src + i), b = load_nt(src + i + stride);
+        const uint4 c = load_nt(src + i + 2 * stride), d = load_nt(src + i + 3 * stride);
         acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
     }
     for (; i < n16; i += stride) {

@@ -156,11 +156,13 @@ int hci_verify_block(const hci_layer* L, const hci_state* S, const hci_block* bl
                      int nb, int nc, int gamma, int max_kv_len,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* hci_verify_block that also records events[0..3] on `stream`: before the
- * conv/IIR kernel, before the prefix-attention kernel, after it, and after
- * the combine kernel, so the caller can time each part with
- * hipEventElapsedTime.  events must point at 4 events created by the caller
- * (entries may be NULL to skip one).  Errors as hci_verify_block. */
+/* hci_verify_block that also records events[0..2] on `stream`: before the
+ * first kernel, after the streaming part (the kernel that reads the KV
+ * prefix; for bf16 layers it also runs the conv/IIR scan and the causal
+ * block part), and after the final combine kernel, so the caller can time
+ * the parts with hipEventElapsedTime.  events must point at 3 events created
+ * by the caller (entries may be NULL to skip one).  Errors as
+ * hci_verify_block. */
 int hci_verify_block_timed(const hci_layer* L, const hci_state* S, const hci_block* blk,
                            int nb, int nc, int gamma, int max_kv_len,
                            void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
