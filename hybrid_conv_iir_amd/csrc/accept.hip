@@ -18,12 +18,18 @@ namespace hci {
 constexpr int kAccT = 256;
 constexpr int kAccW = kAccT / 64;
 
+constexpr int kAccRows = 64;     // P <= 64
+
 struct AccScratch {
     double d[kAccW];
     int i[kAccW];
     double d2[kAccW];
     double bcast[4];
     int ibcast[2];
+    int arg[kAccRows];             // greedy: argmax per target row
+    double gap[kAccRows];          // greedy: top-1 gap per target row
+    double pm[kAccRows], ps[kAccRows];   // sampling: target row max / sum
+    double qm[kAccRows], qs[kAccRows];   // sampling: draft row max / sum
 };
 
 __device__ __forceinline__ double block_sum(double v, AccScratch& sh) {
@@ -76,14 +82,27 @@ __device__ __forceinline__ int block_imax(int v, AccScratch& sh) {
     return s;
 }
 
-// (best value, its lowest index, runner-up value) of one fp32 row
-__device__ void row_argmax(const float* z, int V, AccScratch& sh, int& arg, double& gap) {
+constexpr int kLaneBatch = 8;   // row entries each lane loads before using any of them
+
+// argmax / runner-up of one fp32 row by ONE wave (lanes stride the row, fixed butterfly)
+__device__ void wave_row_argmax(const float* z, int V, int lane, int& arg, double& gap) {
     float b1 = -INFINITY, b2 = -INFINITY;
     int i1 = INT_MAX;
-    for (int j = threadIdx.x; j < V; j += kAccT) {      // ascending ids per thread
-        const float v = z[j];
-        if (v > b1) { b2 = b1; b1 = v; i1 = j; }
-        else if (v > b2) b2 = v;
+    for (int j0 = 0; j0 < V; j0 += 64 * kLaneBatch) {
+        float v[kLaneBatch];
+#pragma unroll
+        for (int e = 0; e < kLaneBatch; ++e) {
+            const int j = j0 + e * 64 + lane;
+            v[e] = j < V ? z[j] : -INFINITY;
+        }
+#pragma unroll
+        for (int e = 0; e < kLaneBatch; ++e) {     // ascending ids per lane
+            const int j = j0 + e * 64 + lane;
+            if (j < V) {
+                if (v[e] > b1) { b2 = b1; b1 = v[e]; i1 = j; }
+                else if (v[e] > b2) b2 = v[e];
+            }
+        }
     }
     for (int off = 32; off >= 1; off >>= 1) {
         const float o1 = __shfl_xor(b1, off), o2 = __shfl_xor(b2, off);
@@ -93,33 +112,39 @@ __device__ void row_argmax(const float* z, int V, AccScratch& sh, int& arg, doub
         else { n1 = b1; ni = i1; n2 = fmaxf(b2, o1); }
         b1 = n1; b2 = n2; i1 = ni;
     }
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) {
-        sh.d[threadIdx.x >> 6] = b1;
-        sh.d2[threadIdx.x >> 6] = b2;
-        sh.i[threadIdx.x >> 6] = i1;
-    }
-    __syncthreads();
-    double B1 = sh.d[0], B2 = sh.d2[0];
-    int I1 = sh.i[0];
-    for (int w = 1; w < kAccW; ++w) {
-        const double o1 = sh.d[w], o2 = sh.d2[w];
-        const int oi = sh.i[w];
-        if (o1 > B1 || (o1 == B1 && oi < I1)) { B2 = fmax(B1, o2); B1 = o1; I1 = oi; }
-        else B2 = fmax(B2, o1);
-    }
-    arg = I1;
-    gap = (B2 == -INFINITY) ? INFINITY : B1 - B2;
+    arg = i1;
+    gap = (b2 == -INFINITY) ? INFINITY : (double)b1 - (double)b2;
 }
 
-// softmax(z / T) of one row: returns (max of z/T, sum of exp(z/T - max)) in fp64
-__device__ void row_stats(const float* z, int V, double T, AccScratch& sh, double& mx, double& sum) {
+// softmax(z / T) statistics of one row by ONE wave: (max of z/T, sum of exp(z/T - max)) in fp64
+__device__ void wave_row_stats(const float* z, int V, double T, int lane, double& mx, double& sum) {
     double m = -INFINITY;
-    for (int j = threadIdx.x; j < V; j += kAccT) m = fmax(m, (double)z[j] / T);
-    mx = block_max(m, sh);
+    for (int j0 = 0; j0 < V; j0 += 64 * kLaneBatch) {
+        float v[kLaneBatch];
+#pragma unroll
+        for (int e = 0; e < kLaneBatch; ++e) {
+            const int j = j0 + e * 64 + lane;
+            v[e] = j < V ? z[j] : -INFINITY;
+        }
+#pragma unroll
+        for (int e = 0; e < kLaneBatch; ++e) m = fmax(m, (double)v[e] / T);
+    }
+    for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
     double s = 0.0;
-    for (int j = threadIdx.x; j < V; j += kAccT) s += exp((double)z[j] / T - mx);
-    sum = block_sum(s, sh);
+    for (int j0 = 0; j0 < V; j0 += 64 * kLaneBatch) {
+        float v[kLaneBatch];
+#pragma unroll
+        for (int e = 0; e < kLaneBatch; ++e) {
+            const int j = j0 + e * 64 + lane;
+            v[e] = j < V ? z[j] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < kLaneBatch; ++e)
+            if (j0 + e * 64 + lane < V) s += exp((double)v[e] / T - m);
+    }
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    mx = m;
+    sum = s;
 }
 
 __global__ __launch_bounds__(kAccT) void k_accept(
@@ -140,33 +165,64 @@ __global__ __launch_bounds__(kAccT) void k_accept(
         int k = gamma, nxt = 0;
         double margin = INFINITY;
 
+        const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
         if (mode == HCI_GREEDY) {
-            for (int i = 0; i <= gamma; ++i) {
-                int g; double gap;
-                row_argmax(zt_c + (size_t)i * V, V, sh, g, gap);
-                margin = fmin(margin, gap);
-                if (i == gamma || dr[i] != g) { k = i; nxt = g; break; }
+            // target rows four at a time (one per wave), stopping at the batch holding the first mismatch
+            k = -1;
+            for (int i0 = 0; i0 <= gamma && k < 0; i0 += kAccW) {
+                const int i = i0 + wv;
+                if (i <= gamma) {
+                    int g; double gap;
+                    wave_row_argmax(zt_c + (size_t)i * V, V, lane, g, gap);
+                    if (lane == 0) { sh.arg[i] = g; sh.gap[i] = gap; }
+                }
+                __syncthreads();
+                for (int r = i0; r < i0 + kAccW && r <= gamma; ++r)
+                    if (r == gamma || dr[r] != sh.arg[r]) { k = r; break; }
             }
+            nxt = sh.arg[k];
+            for (int i = 0; i <= k; ++i) margin = fmin(margin, sh.gap[i]);
         } else {
             const float* zd_c = zd + blk * gamma * V;
             const double* u = uni + blk * P;
-            for (int m = 1; m <= gamma; ++m) {
-                const int t = dr[m - 1];
-                if (t < 0 || t >= V) { k = m - 1; break; }
-                double pm, ps, qm, qs;
-                row_stats(zt_c + (size_t)(m - 1) * V, V, T, sh, pm, ps);
-                row_stats(zd_c + (size_t)(m - 1) * V, V, T, sh, qm, qs);
-                const double p_t = exp((double)zt_c[(size_t)(m - 1) * V + t] / T - pm) / ps;
-                const double q_t = exp((double)zd_c[(size_t)(m - 1) * V + t] / T - qm) / qs;
-                const double lhs = u[m - 1] * q_t;
-                margin = fmin(margin, fabs(lhs - p_t) / fmax(p_t, 1e-300));
-                if (!(lhs < p_t)) { k = m - 1; break; }
+            // ratio tests two drafts at a time: waves 0,1 take target rows m-1, waves 2,3 draft rows m-1
+            k = gamma;
+            bool done = false;
+            for (int m0 = 1; m0 <= gamma && !done; m0 += kAccW / 2) {
+                const int m = m0 + (wv & 1);
+                if (m <= gamma) {
+                    double mx, sum;
+                    if (wv < 2) {
+                        wave_row_stats(zt_c + (size_t)(m - 1) * V, V, T, lane, mx, sum);
+                        if (lane == 0) { sh.pm[m - 1] = mx; sh.ps[m - 1] = sum; }
+                    } else {
+                        wave_row_stats(zd_c + (size_t)(m - 1) * V, V, T, lane, mx, sum);
+                        if (lane == 0) { sh.qm[m - 1] = mx; sh.qs[m - 1] = sum; }
+                    }
+                }
+                __syncthreads();
+                for (int mm = m0; mm < m0 + kAccW / 2 && mm <= gamma; ++mm) {
+                    const int t = dr[mm - 1];
+                    if (t < 0 || t >= V) { k = mm - 1; done = true; break; }
+                    const double p_t = exp((double)zt_c[(size_t)(mm - 1) * V + t] / T - sh.pm[mm - 1]) / sh.ps[mm - 1];
+                    const double q_t = exp((double)zd_c[(size_t)(mm - 1) * V + t] / T - sh.qm[mm - 1]) / sh.qs[mm - 1];
+                    const double lhs = u[mm - 1] * q_t;
+                    margin = fmin(margin, fabs(lhs - p_t) / fmax(p_t, 1e-300));
+                    if (!(lhs < p_t)) { k = mm - 1; done = true; break; }
+                }
+            }
+            if (k == gamma) {          // every draft kept: the bonus row p_gamma is still needed
+                if (wv == 0) {
+                    double mx, sum;
+                    wave_row_stats(zt_c + (size_t)gamma * V, V, T, lane, mx, sum);
+                    if (lane == 0) { sh.pm[gamma] = mx; sh.ps[gamma] = sum; }
+                }
+                __syncthreads();
             }
             // weights of the final draw: residual after a rejection, else p_gamma
-            double pm, ps, qm = 0.0, qs = 1.0;
-            row_stats(zt_c + (size_t)k * V, V, T, sh, pm, ps);
+            const double pm = sh.pm[k], ps = sh.ps[k];
             bool resid = k < gamma;
-            if (resid) row_stats(zd_c + (size_t)k * V, V, T, sh, qm, qs);
+            const double qm = resid ? sh.qm[k] : 0.0, qs = resid ? sh.qs[k] : 1.0;
             const float* prow = zt_c + (size_t)k * V;
             const float* qrow = zd_c + (size_t)k * V;
             auto weight = [&](int j) {

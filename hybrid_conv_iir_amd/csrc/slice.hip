@@ -15,7 +15,8 @@
 
 namespace hci {
 
-constexpr int kSliceCG = 64;         // channels per window workgroup
+constexpr int kSliceCG = 16;         // channels per window workgroup
+constexpr int kSliceRows = 256 / kSliceCG;   // window rows handled per pass of the 256 threads
 constexpr int kSliceWinMax = 128;    // window rows staged in LDS per pass
 
 __device__ __forceinline__ void winner(const int32_t* n_acc, const int32_t* best, int b, int nc,
@@ -35,11 +36,11 @@ __device__ void window_update(typename Act<ACT>::T* win, const typename Act<ACT>
     // new[r] = concat(old[0..W), rows[0..k])[k+1+r] for r < W.  Rows are
     // processed in ascending chunks; chunk [r0, r0+128) reads old rows at or
     // above r0+k+1, which no earlier chunk has overwritten.
-    const int tid = threadIdx.x, cl = tid & (kSliceCG - 1), part = tid >> 6;
+    const int tid = threadIdx.x, cl = tid % kSliceCG, part = tid / kSliceCG;
     const int ch = ch0 + cl;
     for (int r0 = 0; r0 < W; r0 += kSliceWinMax) {
         const int r1 = min(W, r0 + kSliceWinMax);
-        for (int r = r0 + part; r < r1; r += 4) {
+        for (int r = r0 + part; r < r1; r += kSliceRows) {
             const int m = k + 1 + r;
             float v = 0.f;
             if (ch < d) v = (m < W) ? Act<ACT>::load(win, (size_t)m * d + ch)
@@ -47,7 +48,7 @@ __device__ void window_update(typename Act<ACT>::T* win, const typename Act<ACT>
             stage[r - r0][cl] = v;
         }
         __syncthreads();
-        for (int r = r0 + part; r < r1; r += 4)
+        for (int r = r0 + part; r < r1; r += kSliceRows)
             if (ch < d) Act<ACT>::store(win, (size_t)r * d + ch, stage[r - r0][cl]);
         __syncthreads();
     }
@@ -119,7 +120,7 @@ hipError_t launch_slice(const hci_layer* L, const hci_state* S, const hci_block*
 {
     const int gamma = P - 1;
     const int win_blocks = (L->d + kSliceCG - 1) / kSliceCG;
-    dim3 grid(win_blocks < 64 ? 64 : win_blocks, 3, nb), block(256);
+    dim3 grid(win_blocks < 256 ? 256 : win_blocks, 3, nb), block(256);
     if (L->act_dtype == HCI_BF16) {
         hipLaunchKernelGGL(k_slice<HCI_BF16>, grid, block, 0, st,
             (uint16_t*)S->short_win, S->outer_win, S->iir, (uint16_t*)S->k_cache, (uint16_t*)S->v_cache,

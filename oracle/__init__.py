@@ -26,6 +26,8 @@ Pinning (see tests/test_oracle_*.py):
   * greedy / rejection acceptance: brute force for forced k, the exact
     first-token distribution identity, a Monte-Carlo chi-square test.
   * slicing: the Figure 1(d) worked example; block+slice equals sequential steps.
+  * prefill: equals the prompt's sequential single-position steps; the long
+    FIR equals the plain FIR; the IIR scan equals the state-keeping scan.
   * multi-candidate selection (largest accepted count, lowest index on ties):
     parity unpinned -- the pages give no rule for choosing among candidates.
 """
@@ -33,9 +35,10 @@ from .layer import (depthwise_fir, modal_iir, block_attention, verify_block,
                     as_f64, Layer, SeqState)
 from .acceptance import greedy_accept, rejection_accept, accept_candidates
 from .slicing import slice_state, sequential_steps
+from .prefill import depthwise_fir_long, iir_scan, prefill_state
 
 __all__ = [
     "depthwise_fir", "modal_iir", "block_attention", "verify_block", "as_f64",
     "Layer", "SeqState", "greedy_accept", "rejection_accept", "accept_candidates",
-    "slice_state", "sequential_steps",
+    "slice_state", "sequential_steps", "depthwise_fir_long", "iir_scan", "prefill_state",
 ]
