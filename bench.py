@@ -163,6 +163,82 @@ def cpu_baseline(cfg, case_np, heads, reps):
     }
 
 
+PEAK_FP32_VECTOR_TFLOPS = 157.3
+
+
+def prefill_alg_flops(cfg, T) -> float:
+    """Per position and channel: a multiply and an add per short and outer FIR tap; per pole two
+    multiplies and an add for the state update and a multiply-add for the readout."""
+    return float(cfg.nb) * T * cfg.d * (2 * cfg.taps_short + 2 * cfg.taps_outer + 5 * cfg.poles)
+
+
+def prefill_alg_bytes(cfg, T, want_y) -> float:
+    act = 2 if cfg.act == "bf16" else 4
+    per = cfg.d * act + 2 * cfg.heads * cfg.head_dim * act * 2 + (cfg.d * act if want_y else 0)   # x, k+v in, cache out, y
+    return float(cfg.nb) * T * per
+
+
+def bench_prefill(args, cfg, hip):
+    """Prompt -> committed state: chunked FIR + IIR scan, carry scan, window commit, KV append."""
+    import numpy as np
+    import torch
+    from hybrid_conv_iir_amd import device as dv
+    from hybrid_conv_iir_amd import hci, synth
+    T, W, K = args.prompt, args.warmup, args.steps
+    cfg = synth.scaled(cfg, kv_lens=(0,) * cfg.nb)
+    lay = dv.DeviceLayer(cfg, synth.make_layer(cfg))
+    st = dv.DeviceState(lay, cfg.nb, (T + 31) // 32 * 32)
+    small = synth.make_state_small(cfg)
+    pr = synth.prompt(cfg, T, device="cuda")
+    at = hci.act_torch_dtype(lay.act)
+    y = torch.empty((cfg.nb, T, cfg.d), dtype=at, device="cuda")
+    ws = torch.empty(hci.prefill_workspace_bytes(lay.c, cfg.nb, T, True), dtype=torch.uint8, device="cuda")
+    sp = torch.cuda.current_stream().cuda_stream
+
+    def one(with_y, evs=None):
+        st.load_small(small)
+        st.kv_len.zero_()
+        if evs is not None:
+            hip.hipEventRecord(evs[0], sp)
+        hci.prefill(lay.c, st.c, cfg.nb, T, 0, pr["x"], pr["k"], pr["v"], y if with_y else None, ws)
+        if evs is not None:
+            hip.hipEventRecord(evs[1], sp)
+
+    res = {}
+    for with_y in (False, True):
+        for _ in range(W):
+            one(with_y)
+        evsets = [_events(hip, 2) for _ in range(K)]
+        for i in range(K):
+            one(with_y, evsets[i])
+        torch.cuda.synchronize()
+        res[with_y] = float(np.median([_ms(hip, e[0], e[1]) for e in evsets]))
+    t_state = res[False] * 1e-3
+    flops = prefill_alg_flops(cfg, T)
+    achieved = flops / t_state / 1e12
+    out = {
+        "metric": "prefill positions/sec per layer (prompt -> committed state)",
+        "value": round(cfg.nb * T / t_state, 1),
+        "unit": "positions/s",
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(res[False], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.act == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) prompt)",
+        "config": {"workload": f"prefill of a {T}-token prompt into the {cfg.name} layer "
+                               f"(d={cfg.d}, FIR {cfg.taps_short}/{cfg.taps_outer} taps, {cfg.poles} poles, "
+                               f"{cfg.heads}x{cfg.head_dim} heads)", "prompt": T, "nb": cfg.nb},
+        "ms_with_outputs_y": round(res[True], 4),
+        "hbm_GBs_state_only": round(prefill_alg_bytes(cfg, T, False) / t_state / 1e9, 1),
+        "roofline": {"kernel": "prefill (k_prefill_local + carry + commit + KV append)", "bound": "alu",
+                     "achieved": round(achieved, 2), "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP32_VECTOR_TFLOPS, 4), "traffic": None,
+                     "alg_flops_per_launch": flops,
+                     "frac_of_unpacked_fp32": round(achieved / (PEAK_FP32_VECTOR_TFLOPS / 2), 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +248,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-oracle sample (0 = all)")
     ap.add_argument("--cpu-reps", type=int, default=3, help="repetitions of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="verify", choices=["verify", "prefill"],
+                    help="verify: the verify->accept->slice step (default); prefill: prompt -> committed state")
+    ap.add_argument("--prompt", type=int, default=262144, help="prompt length for --mode prefill")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run the known-size copy kernel once on this many MiB (byte-counter calibration)")
     args = ap.parse_args()
@@ -189,6 +268,8 @@ def main():
     torch.cuda.set_device(0)
     hip = _hip()
     cfg = synth.CONFIGS[args.config]
+    if args.mode == "prefill":
+        return bench_prefill(args, cfg, hip)
     W, K = args.warmup, args.steps
     P = cfg.P
     kv_cap = (cfg.max_kv_len + (W + K + 2) * P + 31) // 32 * 32

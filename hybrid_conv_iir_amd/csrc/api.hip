@@ -150,6 +150,28 @@ int hci_slice_state(const hci_layer* L, const hci_state* S, const hci_block* blk
     return HCI_OK;
 }
 
+size_t hci_prefill_workspace_bytes(const hci_layer* L, int nb, int T, int want_y) {
+    if (check_layer(L) != HCI_OK || nb < 1 || T < 1) return 0;
+    return plan_prefill(L, nb, T, want_y != 0).bytes;
+}
+
+int hci_prefill(const hci_layer* L, const hci_state* S, int nb, int T, int max_kv_len,
+                const void* x, const void* k, const void* v, void* y,
+                void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_layer(L);
+    if (rc) return rc;
+    if (T < 1 || max_kv_len < 0 || !x || !k || !v) return HCI_EINVAL;
+    if (L->poles > 16) return HCI_EUNSUPPORTED;
+    rc = check_state(L, S, nb, (long long)max_kv_len + T);
+    if (rc) return rc;
+    if (prefill_lds_bytes(L->taps_outer) > kMaxLds) return HCI_EUNSUPPORTED;
+    const PrefillPlan plan = plan_prefill(L, nb, T, y != nullptr);
+    if (plan.nchunks > 65535) return HCI_EUNSUPPORTED;
+    if (!ws || ws_bytes < plan.bytes || !aligned(ws, 256)) return HCI_EWORKSPACE;
+    if (launch_prefill(L, S, nb, T, x, k, v, y, plan, ws, stream) != hipSuccess) return HCI_EDEVICE;
+    return HCI_OK;
+}
+
 size_t hci_kv_cache_elems(const hci_layer* L, int nb, int kv_cap) {
     if (check_layer(L) != HCI_OK || nb < 1 || kv_cap < kTile || kv_cap % kTile) return 0;
     return (size_t)nb * L->heads * (size_t)kv_cap * L->head_dim;

@@ -116,6 +116,21 @@ hipError_t launch_slice(const hci_layer* L, const hci_state* S, const hci_block*
 hipError_t launch_kv_copy(const hci_layer* L, const hci_state* S, int b, int row0, int nrows,
                           const void* k_rows, const void* v_rows, void* k_out, void* v_out,
                           bool write, hipStream_t st);
+hipError_t launch_kv_pack(const hci_layer* L, const hci_state* S, int b, int row0, int nrows, const void* k_rows,
+                          const void* v_rows, size_t row_stride, size_t head_stride, hipStream_t st);
+hipError_t launch_len_add(const hci_state* S, int nb, int add, hipStream_t st);
+
+// prefill of a prompt into the committed state
+struct PrefillPlan {
+    int nchunks;                 // 256-position chunks
+    size_t s_elems, ftail_elems, yloc_elems;
+    size_t bytes;                // workspace bytes (256-aligned sections)
+};
+PrefillPlan plan_prefill(const hci_layer* L, int nb, int T, bool want_y);
+size_t prefill_lds_bytes(int To);
+hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T, const void* x, const void* k,
+                          const void* v, void* y, const PrefillPlan& plan, void* ws, hipStream_t st);
+
 hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t st);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 int probe_blocks();

@@ -162,10 +162,103 @@ __global__ __launch_bounds__(256) void k_kv_copy(T* __restrict__ kc, T* __restri
     }
 }
 
+// Append rows in the tiled layout 16 bytes at a time (8 bf16 or 2 x 4 fp32 elements).
+// Row r of head h comes from src + r * row_stride + h * head_stride; the first
+// row lands at row0, or at kv_len[b] when row0 < 0 (read on the device).
+// One unit = 8 consecutive tile elements: for K one key row's 8 consecutive
+// dims, for V one dim of 8 keys; units whose keys fall partly outside the
+// appended rows write element by element.
+template <typename T>
+__global__ __launch_bounds__(256) void k_kv_pack(T* __restrict__ kc, T* __restrict__ vc, const T* __restrict__ ks,
+                                                 const T* __restrict__ vs, const int32_t* __restrict__ kv_len,
+                                                 int b, int row0, int nrows, int H, int DH, int kv_cap,
+                                                 size_t row_stride, size_t head_stride)
+{
+    const int L0 = row0 >= 0 ? row0 : kv_len[b];
+    if (L0 < 0 || L0 + nrows > kv_cap) return;            // host checks make this unreachable
+    const int tile0 = L0 / kTile, tile1 = (L0 + nrows - 1) / kTile;
+    const int units = 4 * DH;                               // per (head, tile) and per cache
+    const size_t total = (size_t)(tile1 - tile0 + 1) * H * units * 2;
+    const int J = DH / 32;
+    const size_t slab = (size_t)kv_cap * DH;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+        const int q = (int)(e % units);
+        const int is_v = (int)((e / units) % 2);
+        const int h = (int)((e / ((size_t)units * 2)) % H);
+        const int tile = tile0 + (int)(e / ((size_t)units * 2 * H));
+        const int m = q & 15, g = (q >> 4) & 3;
+        T* dst = (is_v ? vc : kc) + ((size_t)b * H + h) * slab + (size_t)tile * kTile * DH + (size_t)q * 8;
+        if (!is_v) {
+            const int j = (q >> 6) % J, u = q / (64 * J);
+            const int row = tile * kTile + 16 * u + m;
+            if (row < L0 || row >= L0 + nrows) continue;
+            const T* src = ks + (size_t)(row - L0) * row_stride + (size_t)h * head_stride + 32 * j + 8 * g;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dst[i] = src[i];
+        } else {
+            const int dd = 16 * (q >> 6) + m;
+            T vals[8];
+            bool full = true;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = tile * kTile + 16 * (i >> 2) + 4 * g + (i & 3);
+                const bool ok = row >= L0 && row < L0 + nrows;
+                full = full && ok;
+                vals[i] = ok ? vs[(size_t)(row - L0) * row_stride + (size_t)h * head_stride + dd] : T(0);
+            }
+            if (full) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dst[i] = vals[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int row = tile * kTile + 16 * (i >> 2) + 4 * g + (i & 3);
+                    if (row >= L0 && row < L0 + nrows) dst[i] = vals[i];
+                }
+            }
+        }
+    }
+}
+
+hipError_t launch_kv_pack(const hci_layer* L, const hci_state* S, int b, int row0, int nrows, const void* k_rows,
+                          const void* v_rows, size_t row_stride, size_t head_stride, hipStream_t st)
+{
+    if (nrows <= 0) return hipSuccess;
+    const size_t tiles = (size_t)(nrows + 2 * kTile - 1) / kTile;   // upper bound on tiles touched
+    size_t blocks = (tiles * L->heads * 4 * L->head_dim * 2 + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (L->act_dtype == HCI_BF16)
+        hipLaunchKernelGGL(k_kv_pack<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st, (uint16_t*)S->k_cache,
+                           (uint16_t*)S->v_cache, (const uint16_t*)k_rows, (const uint16_t*)v_rows, S->kv_len, b, row0,
+                           nrows, L->heads, L->head_dim, S->kv_cap, row_stride, head_stride);
+    else
+        hipLaunchKernelGGL(k_kv_pack<float>, dim3((unsigned)blocks), dim3(256), 0, st, (float*)S->k_cache,
+                           (float*)S->v_cache, (const float*)k_rows, (const float*)v_rows, S->kv_len, b, row0, nrows,
+                           L->heads, L->head_dim, S->kv_cap, row_stride, head_stride);
+    return hipGetLastError();
+}
+
+__global__ void k_len_add(int32_t* __restrict__ kv_len, int nb, int add, int kv_cap)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nb) return;
+    const int L = kv_len[b] + add;
+    kv_len[b] = L > kv_cap ? kv_cap : L;
+}
+
+hipError_t launch_len_add(const hci_state* S, int nb, int add, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_len_add, dim3((nb + 63) / 64), dim3(64), 0, st, S->kv_len, nb, add, S->kv_cap);
+    return hipGetLastError();
+}
+
 hipError_t launch_kv_copy(const hci_layer* L, const hci_state* S, int b, int row0, int nrows,
                           const void* k_rows, const void* v_rows, void* k_out, void* v_out,
                           bool write, hipStream_t st)
 {
+    if (write)   // logical rows [H][nrows][Dh]: row stride Dh, head stride nrows * Dh
+        return launch_kv_pack(L, S, b, row0, nrows, k_rows, v_rows, (size_t)L->head_dim,
+                              (size_t)nrows * L->head_dim, st);
     const size_t n = (size_t)L->heads * nrows * L->head_dim;
     size_t blocks = (n + 255) / 256;
     if (blocks > 65536) blocks = 65536;

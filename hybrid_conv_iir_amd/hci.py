@@ -67,6 +67,8 @@ EXPORTS = {
     "hci_accept": (_i, [_i, _i, _i, _i, _i, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "hci_slice_state": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), ctypes.POINTER(Block),
                              _i, _i, _i, _i, _p, _p, _p]),
+    "hci_prefill_workspace_bytes": (_sz, [ctypes.POINTER(Layer), _i, _i, _i]),
+    "hci_prefill": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p]),
     "hci_kv_cache_elems": (_sz, [ctypes.POINTER(Layer), _i, _i]),
     "hci_kv_write": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), _i, _i, _i, _i, _p, _p, _p]),
     "hci_kv_read": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), _i, _i, _i, _i, _p, _p, _p]),
@@ -180,6 +182,17 @@ def slice_state(layer: Layer, state: State, block: Block, nb: int, nc: int, gamm
     _check(_lib.hci_slice_state(ctypes.byref(layer), ctypes.byref(state), ctypes.byref(block), nb, nc, gamma,
                                 max_kv_len, _ptr(n_accepted, torch.int32, "n_accepted"),
                                 _ptr(best_cand, torch.int32, "best_cand"), _stream(stream)), "hci_slice_state")
+
+
+def prefill_workspace_bytes(layer: Layer, nb: int, T: int, want_y: bool) -> int:
+    return _lib.hci_prefill_workspace_bytes(ctypes.byref(layer), nb, T, 1 if want_y else 0)
+
+
+def prefill(layer: Layer, state: State, nb: int, T: int, max_kv_len: int, x, k, v, y, ws, stream=None) -> None:
+    _check(_lib.hci_prefill(ctypes.byref(layer), ctypes.byref(state), nb, T, max_kv_len,
+                            _ptr(x, None, "x"), _ptr(k, None, "k"), _ptr(v, None, "v"), _ptr(y, None, "y"),
+                            _ptr(ws, None, "ws"), ws.numel() * ws.element_size() if ws is not None else 0,
+                            _stream(stream)), "hci_prefill")
 
 
 def kv_cache_elems(layer: Layer, nb: int, kv_cap: int) -> int:

@@ -44,6 +44,7 @@ _S_SWIN, _S_OWIN, _S_IIR = 20, 21, 22
 _S_KPRE, _S_VPRE = 30, 31
 _S_TOK, _S_ZT, _S_ZD, _S_GUMBEL, _S_U, _S_GEOM = 40, 41, 42, 43, 44, 45
 _S_NEEDLE = 50
+_S_PROMPT = 60
 
 
 @dataclasses.dataclass(frozen=True)
@@ -183,6 +184,24 @@ def kv_prefix(cfg: Config, b: int, which: str, seed: int = 0, device: str = "cpu
     out = torch.empty((cfg.heads, L, cfg.head_dim), dtype=out_dtype, device=device)
     for h in range(cfg.heads):  # one head at a time bounds the fp32 temporary
         out[h] = torch.randn((L, cfg.head_dim), generator=g, device=device, dtype=torch.float32).to(out_dtype)
+    return out
+
+
+def prompt(cfg: Config, T: int, seed: int = 0, device: str = "cpu"):
+    """A prompt of T positions for every sequence: x [nb][T][d], k, v [nb][T][H][Dh] ~ N(0, 1), act dtype.
+
+    Drawn with torch's generator on ``device`` (the host receives copies of the same bits).
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(((seed * 1000 + cfg.cfg_id) * 100 + _S_PROMPT) * 100003 + T)
+    out_dtype = torch.bfloat16 if cfg.act == BF16 else torch.float32
+    shapes = {"x": (cfg.nb, T, cfg.d), "k": (cfg.nb, T, cfg.heads, cfg.head_dim), "v": (cfg.nb, T, cfg.heads, cfg.head_dim)}
+    out = {}
+    for name, shape in shapes.items():
+        t = torch.empty(shape, dtype=out_dtype, device=device)
+        for b in range(cfg.nb):
+            t[b] = torch.randn(shape[1:], generator=g, device=device, dtype=torch.float32).to(out_dtype)
+        out[name] = t
     return out
 
 

@@ -217,6 +217,30 @@ int hci_slice_state(const hci_layer* L, const hci_state* S, const hci_block* blk
                     const int32_t* n_accepted, const int32_t* best_cand,
                     hipStream_t stream);
 
+/* ----------------------------------------------------------------- prefill */
+
+/* Bytes of workspace hci_prefill needs (want_y: whether y is requested). */
+size_t hci_prefill_workspace_bytes(const hci_layer* L, int nb, int T, int want_y);
+
+/* Prefill a prompt of T positions into the committed state -- the step
+ * before the verify hot path.  By the block-forward contract of the EvSpark
+ * digest (Interpretation) this equals T sequential single-position steps
+ * restricted to the state:
+ *   short_win <- last Ts-1 rows of [short_win ; x_0..x_{T-1}]
+ *   outer_win <- last To-1 rows of [outer_win ; f_0..f_{T-1}]
+ *   iir       <- s_{T-1}   (s_t = lambda * s_{t-1} + beta * g_t from iir)
+ *   kv rows kv_len..kv_len+T-1 <- k, v;   kv_len += T
+ * and, if y is not NULL, y_t = sum_n c * s_t for every prompt position.  The
+ * prompt's attention outputs are not computed (they are not state).
+ *   x [nb][T][d] act;  k, v [nb][T][H][Dh] act;  y [nb][T][d] act or NULL.
+ *   max_kv_len  host bound on every kv_len[b]; max_kv_len + T <= kv_cap.
+ *   ws, ws_bytes  workspace of hci_prefill_workspace_bytes(...), 256-aligned.
+ * Limits: N <= 16 poles; T <= 16776960.  The IIR runs as a chunked parallel
+ * scan, so its results equal the sequential recurrence up to fp32 rounding. */
+int hci_prefill(const hci_layer* L, const hci_state* S, int nb, int T, int max_kv_len,
+                const void* x, const void* k, const void* v, void* y,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* -------------------------------------------------------------- KV access */
 
 /* Elements (not bytes) of ONE of k_cache / v_cache for nb sequences. */
