@@ -87,21 +87,29 @@ def stream_alg_bytes(cfg, kv_lens) -> int:
     return verify_alg_bytes(cfg, kv_lens) - cfg.nb * cfg.nc * cfg.P * cfg.heads * cfg.head_dim * act
 
 
-def _kernel_sha() -> str:
+VERIFY_SOURCES = ("attention.hip", "conv_iir_body.h", "hci_internal.h")
+PREFILL_SOURCES = ("prefill.hip", "slice.hip", "hci_internal.h")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_c3_traffic.json")
+
+
+def _kernel_sha(sources=VERIFY_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in ("attention.hip", "conv_iir_body.h", "hci_internal.h"):
+    for f in sources:
         with open(os.path.join(ROOT, "hybrid_conv_iir_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def _traffic(cfg_name):
+def _traffic(cfg_name, path=TRAFFIC_FILE, sources=VERIFY_SOURCES, prompt=None):
+    """Counter-measured HBM bytes per launch, or None once the kernel sources changed since."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha") != _kernel_sha() or t.get("config") != cfg_name:
+    if t.get("kernel_sha") != _kernel_sha(sources) or t.get("config") != cfg_name:
+        return None
+    if prompt is not None and t.get("prompt") != prompt:
         return None
     return t.get("bytes_per_launch")
 
@@ -163,19 +171,21 @@ def cpu_baseline(cfg, case_np, heads, reps):
     }
 
 
-PEAK_FP32_VECTOR_TFLOPS = 157.3
-
 
 def prefill_alg_flops(cfg, T) -> float:
-    """Per position and channel: a multiply and an add per short and outer FIR tap; per pole two
-    multiplies and an add for the state update and a multiply-add for the readout."""
+    """FIR then IIR as written, per position and channel: a multiply and an add per short and outer
+    tap; per pole two multiplies and an add for the state update and a multiply-add for the readout."""
     return float(cfg.nb) * T * cfg.d * (2 * cfg.taps_short + 2 * cfg.taps_outer + 5 * cfg.poles)
 
 
 def prefill_alg_bytes(cfg, T, want_y) -> float:
+    """Prompt x, K/V rows in, K/V rows appended to the cache, outputs y if wanted, and the committed
+    windows and IIR state read and written."""
     act = 2 if cfg.act == "bf16" else 4
-    per = cfg.d * act + 2 * cfg.heads * cfg.head_dim * act * 2 + (cfg.d * act if want_y else 0)   # x, k+v in, cache out, y
-    return float(cfg.nb) * T * per
+    per_pos = cfg.d * act + 4 * cfg.heads * cfg.head_dim * act + (cfg.d * act if want_y else 0)
+    state = 2 * cfg.d * ((cfg.taps_short - 1) * act + (cfg.taps_outer - 1) * 4 + cfg.poles * 4)
+    weights = cfg.d * (cfg.taps_short + cfg.taps_outer + 2 * cfg.poles) * 4
+    return float(cfg.nb) * (T * per_pos + state) + weights
 
 
 def bench_prefill(args, cfg, hip):
@@ -216,6 +226,8 @@ def bench_prefill(args, cfg, hip):
     t_state = res[False] * 1e-3
     flops = prefill_alg_flops(cfg, T)
     achieved = flops / t_state / 1e12
+    alg = prefill_alg_bytes(cfg, T, False)
+    gbs = alg / t_state / 1e9
     out = {
         "metric": "prefill positions/sec per layer (prompt -> committed state)",
         "value": round(cfg.nb * T / t_state, 1),
@@ -225,16 +237,17 @@ def bench_prefill(args, cfg, hip):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.act == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) prompt)",
-        "config": {"workload": f"prefill of a {T}-token prompt into the {cfg.name} layer "
+        "config": {"workload": f"prefill of a {T}-token prompt into one hybrid layer "
                                f"(d={cfg.d}, FIR {cfg.taps_short}/{cfg.taps_outer} taps, {cfg.poles} poles, "
                                f"{cfg.heads}x{cfg.head_dim} heads)", "prompt": T, "nb": cfg.nb},
         "ms_with_outputs_y": round(res[True], 4),
-        "hbm_GBs_state_only": round(prefill_alg_bytes(cfg, T, False) / t_state / 1e9, 1),
-        "roofline": {"kernel": "prefill (k_prefill_local + carry + commit + KV append)", "bound": "alu",
-                     "achieved": round(achieved, 2), "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP32_VECTOR_TFLOPS, 4), "traffic": None,
-                     "alg_flops_per_launch": flops,
-                     "frac_of_unpacked_fp32": round(achieved / (PEAK_FP32_VECTOR_TFLOPS / 2), 4)},
+        "hbm_GBs_with_outputs_y": round(prefill_alg_bytes(cfg, T, True) / (res[True] * 1e-3) / 1e9, 1),
+        "fir_iir_TFLOPs_equivalent": round(achieved, 2),
+        "roofline": {"kernel": "hci_prefill, all launches (scan, state, KV append)", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000.0, 4),
+                     "traffic": _traffic(cfg.name, PREFILL_TRAFFIC_FILE, PREFILL_SOURCES, T),
+                     "alg_bytes_per_launch": alg},
     }
     print(json.dumps(out), flush=True)
 
@@ -268,6 +281,13 @@ def main():
     torch.cuda.set_device(0)
     hip = _hip()
     cfg = synth.CONFIGS[args.config]
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        csrc = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        cdst = torch.empty_like(csrc)
+        hci.probe_copy(cdst, csrc)
+        torch.cuda.synchronize()
+        del csrc, cdst
     if args.mode == "prefill":
         return bench_prefill(args, cfg, hip)
     W, K = args.warmup, args.steps
@@ -316,14 +336,6 @@ def main():
         hip.hipEventSynchronize(pe[1])
         probe_ms.append(_ms(hip, pe[0], pe[1]))
     probe_gbs = st.k_cache.numel() * 2 / (min(probe_ms) * 1e-3) / 1e9
-
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib << 20
-        csrc = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        cdst = torch.empty_like(csrc)
-        hci.probe_copy(cdst, csrc)
-        torch.cuda.synchronize()
-        del csrc, cdst
 
     # ---------------------------------------------------------------- warm-up
     def step(evs=None):

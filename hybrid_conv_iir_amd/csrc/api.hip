@@ -161,11 +161,13 @@ int hci_prefill(const hci_layer* L, const hci_state* S, int nb, int T, int max_k
     int rc = check_layer(L);
     if (rc) return rc;
     if (T < 1 || max_kv_len < 0 || !x || !k || !v) return HCI_EINVAL;
+    if (!aligned(x, 16) || !aligned(k, 16) || !aligned(v, 16) || (y && !aligned(y, 16))) return HCI_EINVAL;
     if (L->poles > 16) return HCI_EUNSUPPORTED;
     rc = check_state(L, S, nb, (long long)max_kv_len + T);
     if (rc) return rc;
-    if (prefill_lds_bytes(L->taps_outer) > kMaxLds) return HCI_EUNSUPPORTED;
     const PrefillPlan plan = plan_prefill(L, nb, T, y != nullptr);
+    if (plan.state_only ? prefill_state_lds_bytes(L) > 65536 : prefill_lds_bytes(L->taps_outer) > kMaxLds)
+        return HCI_EUNSUPPORTED;
     if (plan.nchunks > 65535) return HCI_EUNSUPPORTED;
     if (!ws || ws_bytes < plan.bytes || !aligned(ws, 256)) return HCI_EWORKSPACE;
     if (launch_prefill(L, S, nb, T, x, k, v, y, plan, ws, stream) != hipSuccess) return HCI_EDEVICE;
@@ -185,6 +187,7 @@ static int kv_access(const hci_layer* L, const hci_state* S, int nb, int b, int 
     if (nb < 1 || b < 0 || b >= nb || row0 < 0 || nrows < 0) return HCI_EINVAL;
     if ((long long)row0 + nrows > S->kv_cap) return HCI_ECAPACITY;
     if (write ? (!a || !c) : (!oa || !oc)) return HCI_EINVAL;
+    if (write && (!aligned(a, 16) || !aligned(c, 16))) return HCI_EINVAL;
     if (launch_kv_copy(L, S, b, row0, nrows, a, c, oa, oc, write, stream) != hipSuccess) return HCI_EDEVICE;
     return HCI_OK;
 }

@@ -122,12 +122,16 @@ hipError_t launch_len_add(const hci_state* S, int nb, int add, hipStream_t st);
 
 // prefill of a prompt into the committed state
 struct PrefillPlan {
-    int nchunks;                 // 256-position chunks
+    bool state_only;             // folded FIR/IIR path (no outputs y; T >= To)
+    int sub_len, chunk_len;      // state path: positions per scan thread and per chunk
+    int nchunks;                 // chunks (256 positions on the output path, chunk_len on the state path)
     size_t s_elems, ftail_elems, yloc_elems;
     size_t bytes;                // workspace bytes (256-aligned sections)
 };
 PrefillPlan plan_prefill(const hci_layer* L, int nb, int T, bool want_y);
 size_t prefill_lds_bytes(int To);
+bool prefill_state_path(const hci_layer* L, int T, bool want_y);
+size_t prefill_state_lds_bytes(const hci_layer* L);
 hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T, const void* x, const void* k,
                           const void* v, void* y, const PrefillPlan& plan, void* ws, hipStream_t st);
 

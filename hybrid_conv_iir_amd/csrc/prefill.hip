@@ -23,6 +23,24 @@
 //   k_prefill_commit FIR windows <- the prompt's last inputs
 //   k_kv_pack        K/V rows appended in the tiled cache layout, then
 //   k_len_add        kv_len += T.
+//
+// When only the state is wanted (no per-position outputs y) the outer FIR
+// is folded into the IIR instead.  Both are linear and time-invariant per
+// channel, so the state after the prompt is a fixed linear functional of
+// the short-FIR outputs f, and exchanging the order of the two sums gives,
+// with W = To-1, M = T-W and per (channel, pole),
+//   s_T = lam^T s_0 + beta * ( H V + lam^(T-To) A + B )
+//   V = sum_{m<M} lam^(M-1-m) f_m               one multiply-add per position
+//   H = sum_{j<=W} w_j lam^(W-j)
+//   B = sum_{b<W} f_{T-1-b} P_b,   P_b = sum_{j<=b} w_j lam^(b-j)
+//   A = sum_{1<=a<=W} fbar_{-a} lam^a Q_a,   Q_a = sum_{j>=a} w_j lam^(W-j)
+// (fbar_{-a} the committed outer window).  The per-position work drops from
+// To + 2N multiply-adds to N, which leaves prefill bound by HBM traffic
+// (dominated by the K/V append).  Requires T >= To.
+//   k_prefill_scan   per (64 channels, chunk): short FIR in registers and the
+//                    V scan over the chunk from zero, 8 sub-chunks merged in LDS
+//   k_prefill_state  per (16 channels): chunk carries -> V, one pass over the
+//                    taps for H, B and A, the new IIR state and both windows
 #include "hci_internal.h"
 
 namespace hci {
@@ -36,18 +54,60 @@ constexpr int kPfN = 16;                   // poles held in registers (N <= 16)
 
 __host__ __device__ inline int pf_taps_padded(int To) { return (To + 15) / 16 * 16; }
 
+__device__ __forceinline__ float powi(float x, int e) {      // x^e, e >= 0, by squaring
+    float r = 1.f;
+    while (e > 0) {
+        if (e & 1) r *= x;
+        x *= x;
+        e >>= 1;
+    }
+    return r;
+}
+
+
 size_t prefill_lds_bytes(int To) {
     const int Wp = pf_taps_padded(To) - 1;
     return ((size_t)(Wp + kPfC) * kPfCG + (size_t)pf_taps_padded(To) * kPfCG + (size_t)kPfSub * kPfCG * kPfN) * 4;
 }
 
+constexpr int kScCh = 64;                  // channels per scan workgroup (32 lanes x 2 channels)
+constexpr int kScSub = 8;                  // sub-chunks (threads along time) per scan chunk
+constexpr int kScTs = 4;                   // short taps held in registers on the state path
+constexpr int kScU = 8;                    // positions loaded ahead per step
+constexpr int kScPad = kPfN + 1;           // LDS row pitch of the sub-chunk states
+
+bool prefill_state_path(const hci_layer* L, int T, bool want_y) {
+    return !want_y && T >= L->taps_outer && L->taps_short <= kScTs && L->d % 2 == 0 && L->poles <= kPfN;
+}
+
+size_t prefill_state_lds_bytes(const hci_layer* L) {
+    const size_t rows = 2 * (size_t)(L->taps_outer - 1) + (size_t)(L->taps_short - 1);
+    return rows * kPfCG * 4 + 16;
+}
+
 PrefillPlan plan_prefill(const hci_layer* L, int nb, int T, bool want_y) {
     PrefillPlan p{};
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    if (prefill_state_path(L, T, want_y)) {
+        p.state_only = true;
+        const int M = T - L->taps_outer + 1;
+        const long long ncg = (L->d + kScCh - 1) / kScCh;
+        long long want = (4096 + ncg * nb - 1) / (ncg * nb);
+        want = want < 1 ? 1 : (want > 256 ? 256 : want);
+        long long sub = (M + want * kScSub - 1) / (want * kScSub);
+        sub = (sub + kScU - 1) / kScU * kScU;
+        if (sub < 2 * kScU) sub = 2 * kScU;
+        p.sub_len = (int)sub;
+        p.chunk_len = (int)(sub * kScSub);
+        p.nchunks = (int)((M + p.chunk_len - 1) / p.chunk_len);
+        p.s_elems = (size_t)nb * p.nchunks * L->d * kPfN;
+        p.bytes = up(p.s_elems * 4);
+        return p;
+    }
     p.nchunks = (T + kPfC - 1) / kPfC;
     p.s_elems = (size_t)nb * p.nchunks * L->d * kPfN;
     p.ftail_elems = (size_t)nb * (L->taps_outer - 1 > 0 ? L->taps_outer - 1 : 1) * L->d;
     p.yloc_elems = want_y ? (size_t)nb * T * L->d : 0;
-    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     p.bytes = up(p.s_elems * 4) + up(p.ftail_elems * 4) + up(p.yloc_elems * 4);
     return p;
 }
@@ -160,9 +220,7 @@ __global__ __launch_bounds__(kPfT) void k_prefill_local(
             const int len = max(0, min(kPfS, T - (t0 + sb * kPfS)));
             const float e = se[((size_t)sb * kPfCG + c2) * kPfN + n2];
             se[((size_t)sb * kPfCG + c2) * kPfN + n2] = S;                 // start state of sub-chunk sb
-            float p = 1.f;
-            for (int i = 0; i < len; ++i) p *= l2;
-            S = fmaf(p, S, e);
+            S = fmaf(powi(l2, len), S, e);
         }
         if (ch2 < d) s_loc[(((size_t)b * nchunks + chunk) * d + ch2) * kPfN + n2] = S;   // chunk end (local)
     }
@@ -199,8 +257,7 @@ __global__ __launch_bounds__(256) void k_prefill_carry(
     const int b = (int)(e / ((size_t)kPfN * d));
     if (n >= N) return;
     const float l = lam[(size_t)ch * N + n];
-    float pc = 1.f;
-    for (int i = 0; i < kPfC; ++i) pc *= l;                 // lambda^C for full chunks
+    const float pc = powi(l, kPfC);                          // lambda^C for full chunks
     float S = iir[((size_t)b * d + ch) * N + n];
     float* sp = s_loc + ((size_t)b * nchunks * d + ch) * kPfN + n;
     const size_t stride = (size_t)d * kPfN;
@@ -208,12 +265,7 @@ __global__ __launch_bounds__(256) void k_prefill_carry(
         const float end = sp[k * stride];
         sp[k * stride] = S;                                  // start state of chunk k
         const int len = min(kPfC, T - k * kPfC);
-        float p = pc;
-        if (len < kPfC) {
-            p = 1.f;
-            for (int i = 0; i < len; ++i) p *= l;
-        }
-        S = fmaf(p, S, end);
+        S = fmaf(len < kPfC ? powi(l, len) : pc, S, end);
     }
     iir[((size_t)b * d + ch) * N + n] = S;                   // committed IIR state after the prompt
 }
@@ -235,9 +287,8 @@ __global__ __launch_bounds__(kPfT) void k_prefill_fixup(
         const bool ok = n < N;
         lm[n] = ok ? lam[(size_t)ch * N + n] : 0.f;
         cv[n] = ok ? cc[(size_t)ch * N + n] : 0.f;
-        float v = ok ? s_loc[(((size_t)b * nchunks + chunk) * d + ch) * kPfN + n] : 0.f;
-        for (int i = 0; i < sub * kPfS; ++i) v *= lm[n];    // decay to the sub-chunk start
-        p[n] = v;
+        const float v = ok ? s_loc[(((size_t)b * nchunks + chunk) * d + ch) * kPfN + n] : 0.f;
+        p[n] = v * powi(lm[n], sub * kPfS);                // decay to the sub-chunk start
     }
     for (int i = 0; i < valid; ++i) {
         float acc = 0.f;
@@ -279,6 +330,258 @@ __global__ __launch_bounds__(256) void k_prefill_commit(
     }
 }
 
+// ------------------------------------------------------------ state path
+
+template <int ACT> struct PairLoad;
+template <> struct PairLoad<HCI_BF16> {       // two consecutive bf16 channels
+    __device__ static __forceinline__ void get(const uint16_t* p, float& a, float& b) {
+        const uint32_t w = __builtin_nontemporal_load((const uint32_t*)p);
+        a = __uint_as_float(w << 16);
+        b = __uint_as_float(w & 0xffff0000u);
+    }
+};
+template <> struct PairLoad<HCI_F32> {
+    __device__ static __forceinline__ void get(const float* p, float& a, float& b) {
+        a = __builtin_nontemporal_load(p);
+        b = __builtin_nontemporal_load(p + 1);
+    }
+};
+
+// V over the chunk's positions from a zero start, per (channel, pole).
+// Thread (cp, sub) owns channels ch, ch+1 and sub_len consecutive positions.
+template <int ACT>
+__global__ __launch_bounds__(256) void k_prefill_scan(
+    const float* __restrict__ w_short, const float* __restrict__ lam,
+    const typename Act<ACT>::T* __restrict__ short_win, const typename Act<ACT>::T* __restrict__ x,
+    float* __restrict__ e_out, int d, int Ts, int N, int T, int M, int sub_len, int nchunks)
+{
+    typedef typename Act<ACT>::T AT;
+    __shared__ float es[kScSub * kScCh * kScPad];
+    const int cg = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
+    const int cp = threadIdx.x % (kScCh / 2), sub = threadIdx.x / (kScCh / 2);
+    const int ch = cg * kScCh + 2 * cp;                 // d is even, so ch + 1 < d whenever ch < d
+    const bool live = ch < d;
+    const int chunk_len = kScSub * sub_len;
+    const int t_begin = chunk * chunk_len + sub * sub_len;
+    const int t_end = min(t_begin + sub_len, M);
+    const AT* xb = x + (size_t)b * T * d;
+    const AT* sw = short_win + (size_t)b * (Ts - 1) * d;
+
+    float wa[kScTs], wb[kScTs];
+#pragma unroll
+    for (int j = 0; j < kScTs; ++j) {
+        wa[j] = (live && j < Ts) ? w_short[(size_t)j * d + ch] : 0.f;
+        wb[j] = (live && j < Ts) ? w_short[(size_t)j * d + ch + 1] : 0.f;
+    }
+    float la[kPfN], lb[kPfN], sa[kPfN], sb[kPfN];
+#pragma unroll
+    for (int n = 0; n < kPfN; ++n) {
+        la[n] = (live && n < N) ? lam[(size_t)ch * N + n] : 0.f;
+        lb[n] = (live && n < N) ? lam[(size_t)(ch + 1) * N + n] : 0.f;
+        sa[n] = 0.f;
+        sb[n] = 0.f;
+    }
+    // xa[j] / xb_[j] = xbar[t - 1 - j]: the previous inputs of the running position t
+    float xa[kScTs - 1], xq[kScTs - 1];
+#pragma unroll
+    for (int j = 0; j < kScTs - 1; ++j) {
+        const int tp = t_begin - 1 - j;
+        float va = 0.f, vb = 0.f;
+        if (live && t_begin < t_end) {
+            if (tp >= 0) {
+                va = Act<ACT>::load(xb, (size_t)tp * d + ch);
+                vb = Act<ACT>::load(xb, (size_t)tp * d + ch + 1);
+            } else if (tp >= -(Ts - 1)) {
+                va = Act<ACT>::load(sw, (size_t)(Ts - 1 + tp) * d + ch);
+                vb = Act<ACT>::load(sw, (size_t)(Ts - 1 + tp) * d + ch + 1);
+            }
+        }
+        xa[j] = va;
+        xq[j] = vb;
+    }
+
+    auto step = [&](float ua, float ub) {
+        float fa = wa[0] * ua, fb = wb[0] * ub;
+#pragma unroll
+        for (int j = 1; j < kScTs; ++j) {
+            fa = fmaf(wa[j], xa[j - 1], fa);
+            fb = fmaf(wb[j], xq[j - 1], fb);
+        }
+#pragma unroll
+        for (int j = kScTs - 2; j > 0; --j) {
+            xa[j] = xa[j - 1];
+            xq[j] = xq[j - 1];
+        }
+        xa[0] = ua;
+        xq[0] = ub;
+#pragma unroll
+        for (int n = 0; n < kPfN; ++n) {
+            sa[n] = fmaf(la[n], sa[n], fa);
+            sb[n] = fmaf(lb[n], sb[n], fb);
+        }
+    };
+
+    if (live) {
+        int t = t_begin;
+        for (; t + kScU <= t_end; t += kScU) {
+            float ua[kScU], ub[kScU];
+#pragma unroll
+            for (int u = 0; u < kScU; ++u) PairLoad<ACT>::get(xb + (size_t)(t + u) * d + ch, ua[u], ub[u]);
+#pragma unroll
+            for (int u = 0; u < kScU; ++u) step(ua[u], ub[u]);
+        }
+        for (; t < t_end; ++t) {
+            float ua, ub;
+            PairLoad<ACT>::get(xb + (size_t)t * d + ch, ua, ub);
+            step(ua, ub);
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < kPfN; ++n) {
+        es[(sub * kScCh + 2 * cp) * kScPad + n] = sa[n];
+        es[(sub * kScCh + 2 * cp + 1) * kScPad + n] = sb[n];
+    }
+    __syncthreads();
+    // merge the sub-chunk states in time order: acc <- lam^len(sub) acc + state(sub)
+    for (int e = threadIdx.x; e < kScCh * kPfN; e += blockDim.x) {
+        const int c = e / kPfN, n = e % kPfN, chc = cg * kScCh + c;
+        if (chc >= d) continue;
+        const float l = n < N ? lam[(size_t)chc * N + n] : 0.f;
+        const float l_full = powi(l, sub_len);
+        float acc = 0.f;
+        for (int q = 0; q < kScSub; ++q) {
+            const int len = max(0, min(sub_len, M - (chunk * chunk_len + q * sub_len)));
+            const float p = len == sub_len ? l_full : powi(l, len);
+            acc = fmaf(p, acc, es[(q * kScCh + c) * kScPad + n]);
+        }
+        e_out[(((size_t)b * nchunks + chunk) * d + chc) * kPfN + n] = acc;
+    }
+}
+
+// Carries, the tap pass and the commit, per 16 channels of one sequence.
+template <int ACT>
+__global__ __launch_bounds__(256) void k_prefill_state(
+    const float* __restrict__ w_short, const float* __restrict__ w_outer, const float* __restrict__ lam,
+    const float* __restrict__ beta, typename Act<ACT>::T* __restrict__ short_win, float* __restrict__ outer_win,
+    float* __restrict__ iir, const typename Act<ACT>::T* __restrict__ x, const float* __restrict__ e_in,
+    int d, int Ts, int To, int N, int T, int M, int chunk_len, int nchunks)
+{
+    typedef typename Act<ACT>::T AT;
+    extern __shared__ float lds[];
+    const int W = To - 1, Ws = Ts - 1;
+    float* ft = lds;                       // [W][16]  f at positions T-W .. T-1
+    float* ow = ft + (size_t)W * kPfCG;    // [W][16]  committed outer window, oldest first
+    float* sw = ow + (size_t)W * kPfCG;    // [Ws][16] committed short window, oldest first
+    const int cg = blockIdx.x, b = blockIdx.y, ch0 = cg * kPfCG;
+    const AT* xb = x + (size_t)b * T * d;
+    AT* swg = short_win + (size_t)b * Ws * d;
+    float* owg = outer_win + (size_t)b * W * d;
+
+    for (int e = threadIdx.x; e < Ws * kPfCG; e += blockDim.x) {
+        const int r = e / kPfCG, ch = ch0 + e % kPfCG;
+        sw[e] = ch < d ? Act<ACT>::load(swg, (size_t)r * d + ch) : 0.f;
+    }
+    for (int e = threadIdx.x; e < W * kPfCG; e += blockDim.x) {
+        const int r = e / kPfCG, ch = ch0 + e % kPfCG;
+        ow[e] = ch < d ? owg[(size_t)r * d + ch] : 0.f;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < W * kPfCG; e += blockDim.x) {
+        const int r = e / kPfCG, c = e % kPfCG, ch = ch0 + c;
+        const int t = T - W + r;                     // >= 1 because T >= To
+        float f = 0.f;
+        if (ch < d) {
+            for (int j = 0; j < Ts; ++j) {
+                const int m = t - j;
+                const float xv = m >= 0 ? Act<ACT>::load(xb, (size_t)m * d + ch) : sw[(Ws + m) * kPfCG + c];
+                f = fmaf(w_short[(size_t)j * d + ch], xv, f);
+            }
+        }
+        ft[e] = f;
+    }
+    __syncthreads();
+
+    {
+        const int c = threadIdx.x / kPfN, n = threadIdx.x % kPfN, ch = ch0 + c;
+        if (ch < d && n < N) {
+            const size_t o = (size_t)ch * N + n;
+            const float l = lam[o];
+            const float l_chunk = powi(l, chunk_len);
+            float V = 0.f;
+            const float* ep = e_in + ((size_t)b * nchunks * d + ch) * kPfN + n;
+#pragma unroll 8
+            for (int k = 0; k < nchunks; ++k) {
+                const int len = min(chunk_len, M - k * chunk_len);
+                const float p = len == chunk_len ? l_chunk : powi(l, len);
+                V = fmaf(p, V, ep[(size_t)k * d * kPfN]);
+            }
+            float P = 0.f, B = 0.f, pa = 1.f, R = 0.f, A = 0.f;
+            for (int j = 0; j <= W; ++j) {
+                const float w = w_outer[(size_t)j * d + ch];
+                P = fmaf(P, l, w);                                        // P_j
+                if (j < W) B = fmaf(ft[(W - 1 - j) * kPfCG + c], P, B);   // f_{T-1-j} P_j
+                if (j >= 1) {
+                    pa *= l;                                              // lam^j
+                    R = fmaf(ow[(W - j) * kPfCG + c], pa, R);             // R_j = sum_{a<=j} fbar_{-a} lam^a
+                    A = fmaf(A, l, w * R);                                // Horner: sum_j w_j R_j lam^(W-j)
+                }
+            }
+            const float bt = beta[o];
+            const float l_to = pa * l;                                    // lam^To
+            const float l_rest = powi(l, T - To);
+            float* sp = iir + (size_t)b * d * N + o;
+            *sp = fmaf(l_rest, fmaf(l_to, *sp, bt * A), bt * fmaf(P, V, B));
+        }
+    }
+
+    // windows: every read of the committed windows went to LDS above
+    for (int e = threadIdx.x; e < W * kPfCG; e += blockDim.x) {
+        const int r = e / kPfCG, ch = ch0 + e % kPfCG;
+        if (ch < d) owg[(size_t)r * d + ch] = ft[e];
+    }
+    for (int e = threadIdx.x; e < Ws * kPfCG; e += blockDim.x) {
+        const int r = e / kPfCG, c = e % kPfCG, ch = ch0 + c;
+        if (ch >= d) continue;
+        const int m = T + r;                         // row of [window ; x] that becomes row r
+        const float v = m < Ws ? sw[m * kPfCG + c] : Act<ACT>::load(xb, (size_t)(m - Ws) * d + ch);
+        Act<ACT>::store(swg, (size_t)r * d + ch, v);
+    }
+}
+
+// K/V rows at kv_len .. kv_len+T-1 of every sequence, then the lengths
+static hipError_t append_kv(const hci_layer* L, const hci_state* S, int nb, int T, const void* k, const void* v,
+                            hipStream_t st)
+{
+    const size_t row_stride = (size_t)L->heads * L->head_dim;
+    const size_t esz = L->act_dtype == HCI_BF16 ? 2 : 4;
+    for (int b = 0; b < nb; ++b) {
+        const hipError_t e = launch_kv_pack(L, S, b, -1, T, (const char*)k + (size_t)b * T * row_stride * esz,
+                                            (const char*)v + (size_t)b * T * row_stride * esz, row_stride,
+                                            (size_t)L->head_dim, st);
+        if (e != hipSuccess) return e;
+    }
+    return launch_len_add(S, nb, T, st);
+}
+
+template <int ACT>
+static hipError_t launch_state_path(const hci_layer* L, const hci_state* S, int nb, int T,
+                                    const typename Act<ACT>::T* x, const PrefillPlan& plan, void* ws, hipStream_t st)
+{
+    typedef typename Act<ACT>::T AT;
+    const int d = L->d, M = T - L->taps_outer + 1;
+    float* e = (float*)ws;
+    hipLaunchKernelGGL(k_prefill_scan<ACT>, dim3((d + kScCh - 1) / kScCh, plan.nchunks, nb), dim3(256), 0, st,
+                       L->w_short, L->lambda, (const AT*)S->short_win, x, e, d, L->taps_short, L->poles, T, M,
+                       plan.sub_len, plan.nchunks);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_prefill_state<ACT>, dim3((d + kPfCG - 1) / kPfCG, nb), dim3(256),
+                       prefill_state_lds_bytes(L), st, L->w_short, L->w_outer, L->lambda, L->beta, (AT*)S->short_win,
+                       S->outer_win, S->iir, x, (const float*)e, d, L->taps_short, L->taps_outer, L->poles, T, M,
+                       plan.chunk_len, plan.nchunks);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T, const void* x, const void* k,
                           const void* v, void* y, const PrefillPlan& plan, void* ws, hipStream_t st)
 {
@@ -286,9 +589,16 @@ hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T,
     float* f_tail = (float*)((char*)ws + (plan.s_elems * 4 + 255) / 256 * 256);
     float* y_loc = y ? (float*)((char*)f_tail + (plan.ftail_elems * 4 + 255) / 256 * 256) : nullptr;
     const int d = L->d;
+    hipError_t e;
+    if (plan.state_only) {
+        e = L->act_dtype == HCI_BF16
+                ? launch_state_path<HCI_BF16>(L, S, nb, T, (const uint16_t*)x, plan, ws, st)
+                : launch_state_path<HCI_F32>(L, S, nb, T, (const float*)x, plan, ws, st);
+        if (e != hipSuccess) return e;
+        return append_kv(L, S, nb, T, k, v, st);
+    }
     const size_t lds = prefill_lds_bytes(L->taps_outer);
     dim3 grid((d + kPfCG - 1) / kPfCG, plan.nchunks, nb);
-    hipError_t e;
     if (L->act_dtype == HCI_BF16) {
         if (lds > 65536 && (e = hipFuncSetAttribute((const void*)k_prefill_local<HCI_BF16>,
                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
@@ -326,15 +636,7 @@ hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T,
         hipLaunchKernelGGL(k_prefill_commit<HCI_F32>, cgrid, dim3(256), 0, st, (float*)S->short_win, S->outer_win,
                            (const float*)x, f_tail, d, L->taps_short, L->taps_outer, T);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // K/V rows at kv_len .. kv_len+T-1 of every sequence, then the lengths
-    const size_t row_stride = (size_t)L->heads * L->head_dim;
-    for (int b = 0; b < nb; ++b) {
-        e = launch_kv_pack(L, S, b, -1, T, (const char*)k + (size_t)b * T * row_stride * (L->act_dtype == HCI_BF16 ? 2 : 4),
-                           (const char*)v + (size_t)b * T * row_stride * (L->act_dtype == HCI_BF16 ? 2 : 4),
-                           row_stride, (size_t)L->head_dim, st);
-        if (e != hipSuccess) return e;
-    }
-    return launch_len_add(S, nb, T, st);
+    return append_kv(L, S, nb, T, k, v, st);
 }
 
 }  // namespace hci

@@ -162,59 +162,76 @@ __global__ __launch_bounds__(256) void k_kv_copy(T* __restrict__ kc, T* __restri
     }
 }
 
-// Append rows in the tiled layout 16 bytes at a time (8 bf16 or 2 x 4 fp32 elements).
-// Row r of head h comes from src + r * row_stride + h * head_stride; the first
-// row lands at row0, or at kv_len[b] when row0 < 0 (read on the device).
-// One unit = 8 consecutive tile elements: for K one key row's 8 consecutive
-// dims, for V one dim of 8 keys; units whose keys fall partly outside the
-// appended rows write element by element.
+// Append logical K/V rows to the tiled caches of sequence b: row i of the
+// source (at k_rows + i * row_stride + h * head_stride) becomes cache row
+// row0 + i, or kv_len[b] + i when row0 < 0 (read on the device).  One
+// workgroup per (32-key tile, head): a K unit (8 consecutive dims of one key
+// row) is one 16-byte load and store; V rows are staged in LDS and each V unit
+// gathers one dim column of 8 keys.  Units whose keys fall partly outside the
+// appended rows store element by element.  Sources and caches are 16-byte
+// aligned and the row/head strides are multiples of 8 elements (checked on
+// the host).
+template <typename T>
+struct Unit8 {                  // 8 consecutive elements
+    u32x4 w[sizeof(T) / 2];
+};
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_kv_pack(T* __restrict__ kc, T* __restrict__ vc, const T* __restrict__ ks,
                                                  const T* __restrict__ vs, const int32_t* __restrict__ kv_len,
                                                  int b, int row0, int nrows, int H, int DH, int kv_cap,
                                                  size_t row_stride, size_t head_stride)
 {
+    constexpr int kMaxDh = 128, kPad = 8;
+    __shared__ __align__(16) T vt[kTile * (kMaxDh + kPad)];
     const int L0 = row0 >= 0 ? row0 : kv_len[b];
-    if (L0 < 0 || L0 + nrows > kv_cap) return;            // host checks make this unreachable
-    const int tile0 = L0 / kTile, tile1 = (L0 + nrows - 1) / kTile;
-    const int units = 4 * DH;                               // per (head, tile) and per cache
-    const size_t total = (size_t)(tile1 - tile0 + 1) * H * units * 2;
-    const int J = DH / 32;
-    const size_t slab = (size_t)kv_cap * DH;
-    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
-        const int q = (int)(e % units);
-        const int is_v = (int)((e / units) % 2);
-        const int h = (int)((e / ((size_t)units * 2)) % H);
-        const int tile = tile0 + (int)(e / ((size_t)units * 2 * H));
-        const int m = q & 15, g = (q >> 4) & 3;
-        T* dst = (is_v ? vc : kc) + ((size_t)b * H + h) * slab + (size_t)tile * kTile * DH + (size_t)q * 8;
-        if (!is_v) {
-            const int j = (q >> 6) % J, u = q / (64 * J);
-            const int row = tile * kTile + 16 * u + m;
-            if (row < L0 || row >= L0 + nrows) continue;
-            const T* src = ks + (size_t)(row - L0) * row_stride + (size_t)h * head_stride + 32 * j + 8 * g;
+    if (L0 < 0 || L0 + nrows > kv_cap || DH > kMaxDh) return;     // host checks make this unreachable
+    const int tile = L0 / kTile + (int)blockIdx.x;
+    const int r0 = tile * kTile;
+    if (r0 >= L0 + nrows) return;                                  // the grid covers an upper bound of tiles
+    const int h = blockIdx.y;
+    const int lo = max(L0, r0), hi = min(L0 + nrows, r0 + kTile);
+    const bool full = lo == r0 && hi == r0 + kTile;
+    const int pitch = DH + kPad, upr = DH / 8, J = DH / 32, units = 4 * DH;
+    const size_t base = ((size_t)b * H + h) * (size_t)kv_cap * DH + (size_t)r0 * DH;
+    T* kdst = kc + base;
+    T* vdst = vc + base;
+    const T* ksrc = ks + (size_t)h * head_stride;
+    const T* vsrc = vs + (size_t)h * head_stride;
+    for (int e = threadIdx.x; e < kTile * upr; e += blockDim.x) {
+        const int r = e / upr, u = e % upr, row = r0 + r;
+        if (row < lo || row >= hi) continue;
+        const Unit8<T>* src = (const Unit8<T>*)(vsrc + (size_t)(row - L0) * row_stride + 8 * u);
+        Unit8<T> val;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) dst[i] = src[i];
+        for (int w = 0; w < (int)(sizeof(T) / 2); ++w) val.w[w] = __builtin_nontemporal_load(&src->w[w]);
+        *(Unit8<T>*)(vt + r * pitch + 8 * u) = val;
+    }
+    for (int q = threadIdx.x; q < units; q += blockDim.x) {
+        const int m = q & 15, g = (q >> 4) & 3, j = (q >> 6) % J, u = q / (64 * J);
+        const int row = r0 + 16 * u + m;
+        if (row < lo || row >= hi) continue;
+        const Unit8<T>* src = (const Unit8<T>*)(ksrc + (size_t)(row - L0) * row_stride + 32 * j + 8 * g);
+        Unit8<T> val;
+#pragma unroll
+        for (int w = 0; w < (int)(sizeof(T) / 2); ++w) val.w[w] = __builtin_nontemporal_load(&src->w[w]);
+        *(Unit8<T>*)(kdst + (size_t)q * 8) = val;
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < units; q += blockDim.x) {
+        const int m = q & 15, g = (q >> 4) & 3, dd = 16 * (q >> 6) + m;
+        T vals[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vals[i] = vt[(16 * (i >> 2) + 4 * g + (i & 3)) * pitch + dd];
+        if (full) {
+            Unit8<T> o;
+            __builtin_memcpy(&o, vals, sizeof(o));
+            *(Unit8<T>*)(vdst + (size_t)q * 8) = o;
         } else {
-            const int dd = 16 * (q >> 6) + m;
-            T vals[8];
-            bool full = true;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int row = tile * kTile + 16 * (i >> 2) + 4 * g + (i & 3);
-                const bool ok = row >= L0 && row < L0 + nrows;
-                full = full && ok;
-                vals[i] = ok ? vs[(size_t)(row - L0) * row_stride + (size_t)h * head_stride + dd] : T(0);
-            }
-            if (full) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) dst[i] = vals[i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int row = tile * kTile + 16 * (i >> 2) + 4 * g + (i & 3);
-                    if (row >= L0 && row < L0 + nrows) dst[i] = vals[i];
-                }
+                const int row = r0 + 16 * (i >> 2) + 4 * g + (i & 3);
+                if (row >= lo && row < hi) vdst[(size_t)q * 8 + i] = vals[i];
             }
         }
     }
@@ -224,15 +241,15 @@ hipError_t launch_kv_pack(const hci_layer* L, const hci_state* S, int b, int row
                           const void* v_rows, size_t row_stride, size_t head_stride, hipStream_t st)
 {
     if (nrows <= 0) return hipSuccess;
-    const size_t tiles = (size_t)(nrows + 2 * kTile - 1) / kTile;   // upper bound on tiles touched
-    size_t blocks = (tiles * L->heads * 4 * L->head_dim * 2 + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
+    if (L->head_dim > 128 || L->head_dim % 32 || row_stride % 8 || head_stride % 8) return hipErrorInvalidValue;
+    // tiles touched: at most nrows / 32 + 2 (row0 may be read on the device)
+    const dim3 grid((unsigned)((nrows + 2 * kTile - 1) / kTile), (unsigned)L->heads);
     if (L->act_dtype == HCI_BF16)
-        hipLaunchKernelGGL(k_kv_pack<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st, (uint16_t*)S->k_cache,
+        hipLaunchKernelGGL(k_kv_pack<uint16_t>, grid, dim3(256), 0, st, (uint16_t*)S->k_cache,
                            (uint16_t*)S->v_cache, (const uint16_t*)k_rows, (const uint16_t*)v_rows, S->kv_len, b, row0,
                            nrows, L->heads, L->head_dim, S->kv_cap, row_stride, head_stride);
     else
-        hipLaunchKernelGGL(k_kv_pack<float>, dim3((unsigned)blocks), dim3(256), 0, st, (float*)S->k_cache,
+        hipLaunchKernelGGL(k_kv_pack<float>, grid, dim3(256), 0, st, (float*)S->k_cache,
                            (float*)S->v_cache, (const float*)k_rows, (const float*)v_rows, S->kv_len, b, row0, nrows,
                            L->heads, L->head_dim, S->kv_cap, row_stride, head_stride);
     return hipGetLastError();

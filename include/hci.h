@@ -232,7 +232,8 @@ size_t hci_prefill_workspace_bytes(const hci_layer* L, int nb, int T, int want_y
  *   kv rows kv_len..kv_len+T-1 <- k, v;   kv_len += T
  * and, if y is not NULL, y_t = sum_n c * s_t for every prompt position.  The
  * prompt's attention outputs are not computed (they are not state).
- *   x [nb][T][d] act;  k, v [nb][T][H][Dh] act;  y [nb][T][d] act or NULL.
+ *   x [nb][T][d] act;  k, v [nb][T][H][Dh] act;  y [nb][T][d] act or NULL;
+ *   all four 16-byte aligned (HCI_EINVAL otherwise).
  *   max_kv_len  host bound on every kv_len[b]; max_kv_len + T <= kv_cap.
  *   ws, ws_bytes  workspace of hci_prefill_workspace_bytes(...), 256-aligned.
  * Limits: N <= 16 poles; T <= 16776960.  The IIR runs as a chunked parallel
@@ -247,7 +248,8 @@ int hci_prefill(const hci_layer* L, const hci_state* S, int nb, int T, int max_k
 size_t hci_kv_cache_elems(const hci_layer* L, int nb, int kv_cap);
 
 /* Write logical rows [row0, row0+nrows) of sequence b (0 <= b < nb) into the
- * tiled caches.  k_rows, v_rows: [H][nrows][Dh] act.  Does not touch kv_len.
+ * tiled caches.  k_rows, v_rows: [H][nrows][Dh] act, 16-byte aligned
+ * (HCI_EINVAL otherwise).  Does not touch kv_len.
  * HCI_ECAPACITY if row0 + nrows > kv_cap. */
 int hci_kv_write(const hci_layer* L, const hci_state* S, int nb, int b, int row0, int nrows,
                  const void* k_rows, const void* v_rows, hipStream_t stream);

@@ -43,15 +43,15 @@ def _run_prefill(lay, st, cfg, T, L0, pr, want_y=True):
     return y
 
 
-def _check(cfg, T, L0, chans=None, seed=0):
+def _check(cfg, T, L0, chans=None, seed=0, want_y=True):
     kv_cap = (L0 + T + 31) // 32 * 32 + 32
     params, small, lay, st, pre = _layer_state(cfg, L0, kv_cap, seed)
     pr = synth.prompt(cfg, T, seed, device="cuda")
-    say(f"prefill {cfg.name} d={cfg.d} To={cfg.taps_outer} T={T} L0={L0}")
-    y = _run_prefill(lay, st, cfg, T, L0, pr)
+    say(f"prefill {cfg.name} d={cfg.d} To={cfg.taps_outer} T={T} L0={L0} want_y={want_y}")
+    y = _run_prefill(lay, st, cfg, T, L0, pr, want_y)
     torch.cuda.synchronize()
     snap = st.snapshot()
-    yh = dv.to_host(y)
+    yh = dv.to_host(y) if want_y else None
     chs = slice(None) if chans is None else chans
     for b in range(cfg.nb):
         sub = lambda a: np.asarray(a)[..., chs] if chans is not None else np.asarray(a)
@@ -65,7 +65,8 @@ def _check(cfg, T, L0, chans=None, seed=0):
         np.testing.assert_array_equal(f64(snap["short_win"][b][:, chs]), new.short_win, err_msg=tag)
         assert_f32_close(snap["outer_win"][b][:, chs], new.outer_win, tag + " outer_win")
         assert_f32_close(snap["iir"][b][chs], new.iir, tag + " iir")
-        assert_out_close(cfg, yh[b][:, chs], yo, tag + " y")
+        if want_y:
+            assert_out_close(cfg, yh[b][:, chs], yo, tag + " y")
         assert int(snap["kv_len"][b]) == L0 + T
         kr, vr = st.read_rows(b, L0, T)
         assert torch.equal(kr, pr["k"][b].transpose(0, 1).contiguous()), tag + " k rows"
@@ -75,41 +76,54 @@ def _check(cfg, T, L0, chans=None, seed=0):
             np.testing.assert_array_equal(dv.to_host(k0), pre[b][0])
 
 
-@pytest.mark.parametrize("T", [1, 5, 255, 256, 257, 1000])
-def test_prefill_fp32_tiny_layer(T):
-    _check(synth.CONFIGS["c1"], T, L0=100)
+# want_y=False with T >= To takes the folded state-only path; the others the chunked output path
+@pytest.mark.parametrize("want_y", [True, False])
+@pytest.mark.parametrize("T", [1, 5, 7, 8, 255, 256, 257, 1000])
+def test_prefill_fp32_tiny_layer(T, want_y):
+    _check(synth.CONFIGS["c1"], T, L0=100, want_y=want_y)
 
 
-@pytest.mark.parametrize("T", [1, 13, 300, 4096])
-def test_prefill_bf16_layer(T):
+@pytest.mark.parametrize("want_y", [True, False])
+@pytest.mark.parametrize("T", [1, 13, 128, 129, 300, 4096, 9000])
+def test_prefill_bf16_layer(T, want_y):
     cfg = synth.scaled(synth.CONFIGS["c2"], d=512, heads=4, kv_lens=(0, 0))
-    _check(cfg, T, L0=37)
+    _check(cfg, T, L0=37, want_y=want_y)
 
 
-def test_prefill_short_taps_and_few_poles():
+@pytest.mark.parametrize("want_y", [True, False])
+def test_prefill_short_taps_and_few_poles(want_y):
     cfg = synth.scaled(synth.CONFIGS["c2"], d=48, heads=1, taps_short=1, taps_outer=2, poles=5, kv_lens=(0,))
-    _check(cfg, 700, L0=0)
+    _check(cfg, 700, L0=0, want_y=want_y)
 
 
-def test_prefill_long_prompt_262k_channel_sample():
+@pytest.mark.parametrize("want_y", [True, False])
+def test_prefill_odd_channel_groups(want_y):
+    """d not a multiple of the 64-channel scan group, 4 short taps, outer taps = 1."""
+    cfg = synth.scaled(synth.CONFIGS["c2"], d=96, heads=1, taps_short=4, taps_outer=1, poles=16, kv_lens=(0,))
+    _check(cfg, 3001, L0=5, want_y=want_y)
+
+
+@pytest.mark.parametrize("want_y", [True, False])
+def test_prefill_long_prompt_262k_channel_sample(want_y):
     cfg = synth.scaled(synth.CONFIGS["c3"], kv_lens=(0,))
-    chans = np.array([0, 1, 777, 2048, 4095])
-    _check(cfg, 262144, L0=0, chans=chans)
+    chans = np.array([0, 1, 63, 64, 777, 2048, 4095])
+    _check(cfg, 262144, L0=0, chans=chans, want_y=want_y)
 
 
-def test_prefill_chunks_compose_on_gpu():
+@pytest.mark.parametrize("want_y", [True, False])
+def test_prefill_chunks_compose_on_gpu(want_y):
     cfg = synth.scaled(synth.CONFIGS["c2"], d=256, heads=2, kv_lens=(0,))
     T1, T2 = 1000, 3000
     kv_cap = 4096
     _, _, lay, st_a, _ = _layer_state(cfg, 0, kv_cap)
     _, _, _, st_b, _ = _layer_state(cfg, 0, kv_cap)
     pr = synth.prompt(cfg, T1 + T2, 3, device="cuda")
-    say("prefill composition")
-    y_full = _run_prefill(lay, st_a, cfg, T1 + T2, 0, pr)
+    say(f"prefill composition want_y={want_y}")
+    y_full = _run_prefill(lay, st_a, cfg, T1 + T2, 0, pr, want_y)
     p1 = {n: t[:, :T1].contiguous() for n, t in pr.items()}
     p2 = {n: t[:, T1:].contiguous() for n, t in pr.items()}
-    y1 = _run_prefill(lay, st_b, cfg, T1, 0, p1)
-    y2 = _run_prefill(lay, st_b, cfg, T2, T1, p2)
+    y1 = _run_prefill(lay, st_b, cfg, T1, 0, p1, want_y)
+    y2 = _run_prefill(lay, st_b, cfg, T2, T1, p2, want_y)
     torch.cuda.synchronize()
     a, b = st_a.snapshot(), st_b.snapshot()
     np.testing.assert_array_equal(a["short_win"], b["short_win"])
@@ -119,7 +133,8 @@ def test_prefill_chunks_compose_on_gpu():
     ka, va = st_a.read_rows(0, 0, T1 + T2)      # rows past kv_len are never written: compare the used ones
     kb, vb = st_b.read_rows(0, 0, T1 + T2)
     assert torch.equal(ka, kb) and torch.equal(va, vb)
-    assert_out_close(cfg, dv.to_host(torch.cat([y1, y2], dim=1)), f64(dv.to_host(y_full)), "y")
+    if want_y:
+        assert_out_close(cfg, dv.to_host(torch.cat([y1, y2], dim=1)), f64(dv.to_host(y_full)), "y")
 
 
 def test_prefill_then_verify_round():
