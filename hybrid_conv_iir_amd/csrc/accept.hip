@@ -6,8 +6,11 @@
 // Sampling (ReaDy summary, section D.2; EvSpark digest, Figure 1(c)): the
 // ratio test r * q(t) < p(t) left to right in fp64, correction from the
 // residual max(0, p_k - q_{k+1}) or bonus from p_gamma, drawn by inverse
-// CDF over ascending token ids.  All reductions are fixed-order butterflies
-// and a fixed-order LDS pass, so the result does not depend on scheduling.
+// CDF over ascending token ids.  Recursive sampling over several candidate
+// blocks (multi-draft recursive rejection) keeps the target distribution
+// when the candidates' drafts are independent.  All reductions are
+// fixed-order butterflies and a fixed-order LDS pass, so the result does
+// not depend on scheduling.
 #include "hci_internal.h"
 
 #include <math.h>
@@ -30,6 +33,11 @@ struct AccScratch {
     double gap[kAccRows];          // greedy: top-1 gap per target row
     double pm[kAccRows], ps[kAccRows];   // sampling: target row max / sum
     double qm[kAccRows], qs[kAccRows];   // sampling: draft row max / sum
+    double st[4];                  // recursive: (p max, p sum, q max, q sum) of the current depth
+    double cm[kAccRows];           // recursive: per-candidate margin
+    int na[kAccRows];              // recursive: per-candidate accepted count
+    double zh[kAccRows + 1];       // recursive: residual totals z^(0..r)
+    int zapp[kAccRows];            // recursive: whether rejection i changed the residual
 };
 
 __device__ __forceinline__ double block_sum(double v, AccScratch& sh) {
@@ -147,6 +155,171 @@ __device__ void wave_row_stats(const float* z, int V, double T, int lane, double
     sum = s;
 }
 
+
+// Inverse-CDF draw over token ids with weights weight(j) >= 0: the smallest j whose running sum
+// exceeds r x total (total = the running sum at the last token, formed exactly as the search
+// forms it), else the last token with positive weight.  Every thread owns a contiguous run of
+// ids; the run totals are scanned in a fixed order.  Returns the token and the distance of the
+// nearest running sum from the threshold, relative to the total.
+template <typename F>
+__device__ void draw_token(F weight, int V, double r, AccScratch& sh, int& token, double& margin)
+{
+    const int per = (V + kAccT - 1) / kAccT;
+    const int j0 = min((int)threadIdx.x * per, V), j1 = min(j0 + per, V);
+    double loc = 0.0;
+    for (int j = j0; j < j1; ++j) loc += weight(j);
+    // exclusive scan of the per-thread totals: Hillis-Steele inside a wave, waves in order
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    double incl = loc;
+    for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    __syncthreads();
+    if (lane == 63) sh.d[wv] = incl;
+    __syncthreads();
+    double excl = 0.0;
+    for (int w = 0; w < wv; ++w) excl += sh.d[w];
+    excl += incl - loc;
+    double run = excl;
+    for (int j = j0; j < j1; ++j) run += weight(j);
+    __syncthreads();
+    if (j0 < j1 && j1 == V) sh.bcast[0] = run;
+    __syncthreads();
+    const double total = sh.bcast[0];
+    const double target = r * total;
+    int first = INT_MAX, lastpos = -1;
+    double dmin = INFINITY;
+    run = excl;
+    for (int j = j0; j < j1; ++j) {
+        const double w = weight(j);
+        run += w;
+        if (run > target && first == INT_MAX) first = j;
+        if (w > 0.0) lastpos = j;
+        dmin = fmin(dmin, fabs(run - target));
+    }
+    first = block_imin(first, sh);
+    lastpos = block_imax(lastpos, sh);
+    dmin = block_min(dmin, sh);
+    token = first != INT_MAX ? first : lastpos;
+    margin = dmin / total;
+}
+
+
+// Residual weight of one token after r rejections at the current depth: w^(0) = p,
+// w^(i+1) = max(0, w^(i) - z^(i) q) when rejection i changed the residual (z^(0) = 1,
+// z^(i+1) = the total of w^(i+1)).  The product z q is rounded before the subtraction.
+__device__ __forceinline__ double residual_weight(double p, double q, int r, const AccScratch& sh) {
+    double w = p;
+    for (int i = 0; i < r; ++i)
+        if (sh.zapp[i]) w = fmax(0.0, w - __dmul_rn(sh.zh[i], q));
+    return w;
+}
+
+// Recursive acceptance over the candidates of sequence b (several drafts per depth): at depth k
+// the alive candidates share the accepted prefix and the lowest-index one supplies p and q; they
+// are tried in index order against the running residual; the first kept draft extends the
+// prefix, and if all are rejected the next token is drawn from the residual.  The multi-draft
+// generalisation of the ReaDy summary's section D.2 rule (the pages give no rule for several
+// candidates); with one candidate it is the one-candidate rule bit for bit.
+__device__ void accept_recursive(int b, int nc, int gamma, int V, double T,
+                                 const float* __restrict__ zt, const float* __restrict__ zd,
+                                 const int32_t* __restrict__ drafts, const double* __restrict__ uni,
+                                 int32_t* __restrict__ n_acc, int32_t* __restrict__ next,
+                                 int32_t* __restrict__ best, double* __restrict__ margin_out, AccScratch& sh)
+{
+    const int P = gamma + 1;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    unsigned long long alive = nc == 64 ? ~0ull : ((1ull << nc) - 1ull);
+    if (threadIdx.x < nc) {
+        sh.cm[threadIdx.x] = INFINITY;
+        sh.na[threadIdx.x] = 0;
+    }
+    int k = 0, nrej = 0, rep = 0;
+    const float* prow = nullptr;
+    const float* qrow = nullptr;
+    for (;;) {
+        rep = __ffsll((long long)alive) - 1;
+        const size_t rb = (size_t)b * nc + rep;
+        prow = zt + (rb * P + k) * V;
+        qrow = k < gamma ? zd + (rb * gamma + k) * V : nullptr;
+        nrej = 0;
+        __syncthreads();
+        if (wv == 0 || (wv == 1 && k < gamma)) {
+            double mx, sum;
+            wave_row_stats(wv == 0 ? prow : qrow, V, T, lane, mx, sum);
+            if (lane == 0) {
+                sh.st[2 * wv] = mx;
+                sh.st[2 * wv + 1] = sum;
+            }
+        }
+        if (threadIdx.x == 0) sh.zh[0] = 1.0;
+        __syncthreads();
+        if (k == gamma) break;                       // the alive path kept every draft: bonus from p_gamma
+        const double pm = sh.st[0], ps = sh.st[1], qm = sh.st[2], qs = sh.st[3];
+        int kept = -1;
+        for (int c = 0; c < nc && kept < 0; ++c) {
+            if (!((alive >> c) & 1ull)) continue;
+            const int t = drafts[((size_t)b * nc + c) * gamma + k];
+            if (t >= 0 && t < V) {
+                const double p_t = exp((double)prow[t] / T - pm) / ps;
+                const double q_t = exp((double)qrow[t] / T - qm) / qs;
+                const double lhs = uni[((size_t)b * nc + c) * P + k] * q_t * sh.zh[nrej];
+                const double rhs = residual_weight(p_t, q_t, nrej, sh);
+                if (threadIdx.x == 0) sh.cm[c] = fmin(sh.cm[c], fabs(lhs - rhs) / fmax(rhs, 1e-300));
+                if (lhs < rhs) {
+                    kept = t;
+                    break;
+                }
+            }
+            // rejection: total of max(0, w - z q) over the vocabulary
+            const double z = sh.zh[nrej];
+            double loc = 0.0;
+            for (int j = threadIdx.x; j < V; j += kAccT) {
+                const double q = exp((double)qrow[j] / T - qm) / qs;
+                const double w = residual_weight(exp((double)prow[j] / T - pm) / ps, q, nrej, sh);
+                loc += fmax(0.0, w - __dmul_rn(z, q));
+            }
+            const double tot = block_sum(loc, sh);
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const bool ok = tot > 0.0;            // cannot fail after a rejection; guard only
+                sh.zapp[nrej] = ok ? 1 : 0;
+                sh.zh[nrej + 1] = ok ? tot : z;
+            }
+            __syncthreads();
+            ++nrej;
+        }
+        if (kept < 0) break;
+        for (int c = 0; c < nc; ++c) {
+            if (((alive >> c) & 1ull) && drafts[((size_t)b * nc + c) * gamma + k] != kept) {
+                if (threadIdx.x == 0) sh.na[c] = k;
+                alive &= ~(1ull << c);
+            }
+        }
+        ++k;
+    }
+    const double pm = sh.st[0], ps = sh.st[1], qm = sh.st[2], qs = sh.st[3];
+    const int r = nrej;
+    auto weight = [&](int j) {
+        const double p = exp((double)prow[j] / T - pm) / ps;
+        return r == 0 ? p : residual_weight(p, exp((double)qrow[j] / T - qm) / qs, r, sh);
+    };
+    int tok;
+    double m2;
+    draw_token(weight, V, uni[(size_t)b * nc * P + gamma], sh, tok, m2);
+    __syncthreads();
+    if (threadIdx.x == 0) sh.cm[rep] = fmin(sh.cm[rep], m2);
+    __syncthreads();
+    for (int c = threadIdx.x; c < nc; c += kAccT) {
+        const size_t o = (size_t)b * nc + c;
+        n_acc[o] = ((alive >> c) & 1ull) ? k : sh.na[c];
+        next[o] = tok;
+        if (margin_out) margin_out[o] = sh.cm[c];
+    }
+    if (threadIdx.x == 0 && best) best[b] = rep;
+}
+
 __global__ __launch_bounds__(kAccT) void k_accept(
     int mode, int nc, int gamma, int V, double T,
     const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ drafts,
@@ -157,6 +330,10 @@ __global__ __launch_bounds__(kAccT) void k_accept(
     const int b = blockIdx.x;
     const int P = gamma + 1;
     int best_c = 0, best_k = -1;
+    if (mode == HCI_SAMPLE_RECURSIVE) {
+        accept_recursive(b, nc, gamma, V, T, zt, zd, drafts, uni, n_acc, next, best, margin_out, sh);
+        return;
+    }
 
     for (int c = 0; c < nc; ++c) {
         const size_t blk = (size_t)b * nc + c;
@@ -229,52 +406,18 @@ __global__ __launch_bounds__(kAccT) void k_accept(
                 const double p = exp((double)prow[j] / T - pm) / ps;
                 return resid ? fmax(0.0, p - exp((double)qrow[j] / T - qm) / qs) : p;
             };
-            // each thread owns a contiguous run of token ids
-            const int per = (V + kAccT - 1) / kAccT;
-            const int j0 = min((int)threadIdx.x * per, V), j1 = min(j0 + per, V);
-            double loc = 0.0;
-            for (int j = j0; j < j1; ++j) loc += weight(j);
-            if (resid && !(block_sum(loc, sh) > 0.0)) {   // cannot happen after a rejection; guard only
-                resid = false;
-                loc = 0.0;
+            if (resid) {               // cannot be empty after a rejection; guard only
+                const int per = (V + kAccT - 1) / kAccT;
+                const int j0 = min((int)threadIdx.x * per, V), j1 = min(j0 + per, V);
+                double loc = 0.0;
                 for (int j = j0; j < j1; ++j) loc += weight(j);
+                if (!(block_sum(loc, sh) > 0.0)) resid = false;
             }
-            // exclusive scan of the per-thread totals: Hillis-Steele inside a wave, waves in order
-            const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-            double incl = loc;
-            for (int off = 1; off < 64; off <<= 1) {
-                const double o = __shfl_up(incl, off);
-                if (lane >= off) incl += o;
-            }
-            __syncthreads();
-            if (lane == 63) sh.d[wv] = incl;
-            __syncthreads();
-            double excl = 0.0;
-            for (int w = 0; w < wv; ++w) excl += sh.d[w];
-            excl += incl - loc;
-            // total = the running sum at the last token, exactly as the search below forms it
-            double run = excl;
-            for (int j = j0; j < j1; ++j) run += weight(j);
-            __syncthreads();
-            if (j0 < j1 && j1 == V) sh.bcast[0] = run;
-            __syncthreads();
-            const double total = sh.bcast[0];
-            const double target = u[gamma] * total;
-            int first = INT_MAX, lastpos = -1;
-            double dmin = INFINITY;
-            run = excl;
-            for (int j = j0; j < j1; ++j) {
-                const double w = weight(j);
-                run += w;
-                if (run > target && first == INT_MAX) first = j;
-                if (w > 0.0) lastpos = j;
-                dmin = fmin(dmin, fabs(run - target));
-            }
-            first = block_imin(first, sh);
-            lastpos = block_imax(lastpos, sh);
-            dmin = block_min(dmin, sh);
-            nxt = first != INT_MAX ? first : lastpos;
-            margin = fmin(margin, dmin / total);
+            int tok;
+            double m2;
+            draw_token(weight, V, u[gamma], sh, tok, m2);
+            nxt = tok;
+            margin = fmin(margin, m2);
         }
         if (threadIdx.x == 0) {
             n_acc[blk] = k;

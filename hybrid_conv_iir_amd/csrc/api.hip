@@ -119,12 +119,12 @@ int hci_accept(int mode, int nb, int nc, int gamma, int vocab, float temperature
                const int32_t* draft_tokens, const double* uniforms,
                int32_t* n_accepted, int32_t* next_token, int32_t* best_cand,
                double* margin, hipStream_t stream) {
-    if (mode != HCI_GREEDY && mode != HCI_SAMPLE) return HCI_EINVAL;
+    if (mode != HCI_GREEDY && mode != HCI_SAMPLE && mode != HCI_SAMPLE_RECURSIVE) return HCI_EINVAL;
     if (nb < 1 || nb > 2147483647 || nc < 1 || nc > 64 || gamma < 0 || vocab < 1) return HCI_EINVAL;
     if (vocab > 65536) return HCI_EUNSUPPORTED;
     if (!target_logits || !n_accepted || !next_token) return HCI_EINVAL;
     if (gamma > 0 && !draft_tokens) return HCI_EINVAL;
-    if (mode == HCI_SAMPLE) {
+    if (mode != HCI_GREEDY) {
         if (!(temperature > 0.f) || temperature == INFINITY) return HCI_EINVAL;
         if (!uniforms || (gamma > 0 && !draft_logits)) return HCI_EINVAL;
     }

@@ -154,7 +154,7 @@ def verify(layer: DeviceLayer, state: DeviceState, blk: DeviceBlock, max_kv_len:
 
 
 def accept(acc: DeviceAccept, mode: int, temperature: float = 1.0, stream=None) -> None:
-    sample = mode == hci.SAMPLE
+    sample = mode != hci.GREEDY
     hci.accept(mode, acc.nb, acc.nc, acc.gamma, acc.vocab, temperature, acc.zt,
                acc.zd if sample else None, acc.drafts, acc.u if sample else None,
                acc.n_acc, acc.next, acc.best, acc.margin, stream)

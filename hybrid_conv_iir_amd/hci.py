@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libhci.so")
 
 OK, EINVAL, ECAPACITY, EUNSUPPORTED, EDEVICE, EWORKSPACE = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
-GREEDY, SAMPLE = 0, 1
+GREEDY, SAMPLE, SAMPLE_RECURSIVE = 0, 1, 2
 KV_TILE = 32
 
 

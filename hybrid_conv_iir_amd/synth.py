@@ -253,6 +253,40 @@ def gumbel_drafts(cfg: Config, draft_logits: np.ndarray, rnd: int = 0, seed: int
     return np.argmax(draft_logits.astype(np.float64) / cfg.temperature + gum, axis=-1).astype(np.int32)
 
 
+def prefix_keyed_round(cfg: Config, rnd: int = 0, seed: int = 0, scale: float = math.sqrt(2.0)):
+    """Sampling inputs whose logit rows are a seeded function of (sequence, prefix).
+
+    Candidates of a sequence that share a draft prefix get the same target and
+    draft rows at the next position, and each candidate's drafts are
+    independent Gumbel-max draws from its draft rows -- what several
+    candidate blocks drafted from one anchor look like.  Returns
+    (target_logits [nb][nc][P][V], draft_logits [nb][nc][gamma][V],
+    drafts [nb][nc][gamma], uniforms [nb][nc][P]).
+    """
+    nb, nc, gam, V = cfg.nb, cfg.nc, cfg.gamma, cfg.vocab
+
+    def row(kind, b, prefix):
+        g = np.random.default_rng([cfg.cfg_id, seed, rnd, kind, b, len(prefix)] + [int(t) for t in prefix])
+        return (g.standard_normal(V) * scale).astype(np.float32)
+
+    noise = np.random.default_rng([cfg.cfg_id, seed, rnd, 7]).random((nb, nc, max(gam, 1), V))
+    noise = np.clip(noise, 1e-300, 1.0 - 1e-16)
+    zt = np.empty((nb, nc, gam + 1, V), np.float32)
+    zd = np.empty((nb, nc, gam, V), np.float32)
+    drafts = np.empty((nb, nc, gam), np.int32)
+    for b in range(nb):
+        for c in range(nc):
+            pre = []
+            for i in range(gam):
+                zt[b, c, i] = row(0, b, pre)
+                zd[b, c, i] = row(1, b, pre)
+                gum = -np.log(-np.log(noise[b, c, i]))
+                drafts[b, c, i] = int(np.argmax(zd[b, c, i].astype(np.float64) / cfg.temperature + gum))
+                pre.append(int(drafts[b, c, i]))
+            zt[b, c, gam] = row(0, b, pre)
+    return zt, zd, drafts, uniforms(cfg, rnd, seed)
+
+
 def geometric_agreement(cfg: Config, rnd: int = 0, seed: int = 0, p_continue: float = 0.7,
                         forced_len: Optional[Sequence[int]] = None):
     """Greedy workload: drafts agree with the target argmax for a Geometric(0.7) prefix.
@@ -300,6 +334,9 @@ def round_inputs(cfg: Config, anchor: np.ndarray, rnd: int = 0, seed: int = 0,
         drafts, zt, lens = geometric_agreement(cfg, rnd, seed, forced_len=forced_len)
         zd = None
         u = None
+    elif cfg.mode == "recursive":
+        zt, zd, drafts, u = prefix_keyed_round(cfg, rnd, seed)
+        lens = None
     else:
         zt = logits(cfg, "target", cfg.P, rnd, seed)
         zd = logits(cfg, "draft", cfg.gamma, rnd, seed)

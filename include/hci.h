@@ -52,6 +52,7 @@ extern "C" {
 
 #define HCI_GREEDY 0
 #define HCI_SAMPLE 1
+#define HCI_SAMPLE_RECURSIVE 2
 
 /* Rows of the KV cache are grouped in tiles of this many keys. */
 #define HCI_KV_TILE 32
@@ -183,6 +184,21 @@ int hci_verify_block_timed(const hci_layer* L, const hci_state* S, const hci_blo
  *     acceptance the bonus from p_gamma; a draw takes the smallest token id
  *     whose running sum exceeds r* x (total running sum), else the last
  *     token with positive weight.
+ *   mode HCI_SAMPLE_RECURSIVE (lossless over several candidates; the pages
+ *     report C = 1/2/4 candidate blocks (EvSpark digest, Interpretation) but
+ *     no rule, so this is the published recursive rejection scheme for
+ *     multiple drafts): the candidates of a sequence share the anchor; at
+ *     depth k the alive candidates (drafts t_1..t_k equal to the accepted
+ *     prefix) are tried in index order with the rows p, q of the lowest-index
+ *     alive candidate and the running residual w / z (w = p, z = 1 at the
+ *     start of a depth): draft t is kept iff r * q(t) * z < w(t), a rejection
+ *     sets w <- max(0, w - z q), z <- sum w.  The first kept draft extends
+ *     the prefix (candidates holding it stay alive); if all are rejected the
+ *     next token is drawn from w, after gamma kept drafts from p_gamma; the
+ *     draw uses r* = uniforms[b][0][gamma].  Candidate c's depth-k test uses
+ *     uniforms[b][c][k].  With nc = 1 it equals HCI_SAMPLE bit for bit.  The
+ *     caller supplies equal rows for candidates that share a prefix, and the
+ *     drafts of such candidates are independent draws from q.
  *   Inputs: target_logits [nb][nc][P][V] fp32; draft_logits [nb][nc][gamma][V]
  *     fp32 (the distribution each draft was actually sampled from; NULL in
  *     greedy mode); draft_tokens [nb][nc][gamma] int32 (an id outside [0, V)
@@ -190,10 +206,13 @@ int hci_verify_block_timed(const hci_layer* L, const hci_state* S, const hci_blo
  *     r_1..r_gamma then r* (NULL in greedy mode).
  *   Outputs: n_accepted [nb][nc] int32 = k; next_token [nb][nc] int32;
  *     best_cand [nb] int32 = candidate with the largest k (lowest index on
- *     ties); margin [nb][nc] fp64 = smallest relative distance of any
+ *     ties); in recursive mode n_accepted[b][c] = how many of candidate c's
+ *     leading drafts are in the accepted sequence, next_token[b][c] = the one
+ *     emitted token, best_cand[b] = the lowest-index candidate alive at the
+ *     end (n_accepted[b][best] = k); margin [nb][nc] fp64 = smallest relative distance of any
  *     decision from its threshold (greedy: smallest top-1 logit gap of the
  *     rows read); may be NULL.
- * Limits: 1 <= V <= 65536; temperature > 0 in sample mode; nc <= 64. */
+ * Limits: 1 <= V <= 65536; temperature > 0 in the sampling modes; nc <= 64. */
 int hci_accept(int mode, int nb, int nc, int gamma, int vocab, float temperature,
                const float* target_logits, const float* draft_logits,
                const int32_t* draft_tokens, const double* uniforms,

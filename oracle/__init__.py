@@ -30,15 +30,19 @@ Pinning (see tests/test_oracle_*.py):
     FIR equals the plain FIR; the IIR scan equals the state-keeping scan.
   * multi-candidate selection (largest accepted count, lowest index on ties):
     parity unpinned -- the pages give no rule for choosing among candidates.
+  * recursive multi-candidate acceptance: reduces to the one-candidate rule;
+    exact first-token distribution = target over every draft combination
+    (decision boundaries found by bisection); Monte-Carlo joint law of the
+    first two emitted tokens under a toy prefix-keyed target and drafter.
 """
 from .layer import (depthwise_fir, modal_iir, block_attention, verify_block,
                     as_f64, Layer, SeqState)
-from .acceptance import greedy_accept, rejection_accept, accept_candidates
+from .acceptance import greedy_accept, rejection_accept, recursive_accept, accept_candidates
 from .slicing import slice_state, sequential_steps
 from .prefill import depthwise_fir_long, iir_scan, prefill_state
 
 __all__ = [
     "depthwise_fir", "modal_iir", "block_attention", "verify_block", "as_f64",
-    "Layer", "SeqState", "greedy_accept", "rejection_accept", "accept_candidates",
+    "Layer", "SeqState", "greedy_accept", "rejection_accept", "recursive_accept", "accept_candidates",
     "slice_state", "sequential_steps", "depthwise_fir_long", "iir_scan", "prefill_state",
 ]

@@ -114,6 +114,95 @@ def rejection_accept(target_logits, draft_logits, drafts, u, temperature: float 
     return k, nxt, min(margin, m2)
 
 
+def _residual(w: np.ndarray, z: float, q: np.ndarray):
+    """One rejection: the next residual weights max(0, w - z q) and their total.
+
+    w holds unnormalised weights whose normalised form w / z is the current
+    target distribution; the result keeps the same convention.  If rounding
+    leaves no positive weight (a rejection implies some token has more
+    target than draft mass, so this cannot happen in exact arithmetic) the
+    weights stay as they were.
+    """
+    w2 = np.maximum(0.0, w - z * q)
+    z2 = float(np.sum(w2))
+    if not z2 > 0.0:
+        return w, z
+    return w2, z2
+
+
+def recursive_accept(target_logits, draft_logits, drafts, u, temperature: float = 1.0):
+    """Lossless acceptance over several candidate blocks of one sequence.
+
+    A multi-draft generalisation of the ReaDy summary's section D.2 rule for
+    the C = 1/2/4 candidate blocks of the EvSpark digest (Interpretation);
+    the pages state no rule for several candidates, so this follows the
+    published recursive rejection scheme for multiple drafts (SpecInfer's
+    multi-step speculative sampling).  All candidates share the anchor; at
+    depth k the alive candidates are those whose drafts t_1..t_k equal the
+    accepted prefix, and the lowest-index alive candidate supplies the rows
+    p = softmax(target row k / T) and q = softmax(draft row k / T) (rows of
+    candidates that share a prefix are the same distributions).  Alive
+    candidates are tried in index order: draft t is kept iff
+    r * q(t) < w(t) / z for the current residual w / z (w = p, z = 1 at the
+    start of a depth); a rejection replaces w by max(0, w - z q).  The first
+    kept draft extends the prefix and the candidates holding it stay alive;
+    if every alive candidate is rejected the next token is drawn from the
+    final residual, and after gamma kept drafts the bonus is drawn from
+    p_gamma.  Draws use r* = u[0][gamma] by inverse CDF.  When the drafts of
+    the alive candidates are independent draws from q, every emitted token
+    is distributed as the target's.  With one candidate this is exactly
+    ``rejection_accept``.
+
+    target_logits [nc][P][V]; draft_logits [nc][gamma][V]; drafts [nc][gamma];
+    u [nc][P]: candidate c's depth-k test uses u[c][k].  Returns (n_acc [nc],
+    next, best, margin [nc]): n_acc[c] counts candidate c's leading drafts
+    that are in the accepted sequence, best is the lowest-index candidate
+    alive at the end (n_acc[best] = k), margin[c] is the smallest relative
+    distance of candidate c's tests from their thresholds (the final draw's
+    margin goes to best).
+    """
+    zt = np.asarray(target_logits)
+    zd = np.asarray(draft_logits)
+    dr = np.asarray(drafts)
+    nc, P, V = zt.shape
+    gamma = P - 1
+    margin = np.full(nc, np.inf)
+    n_acc = np.zeros(nc, np.int32)
+    alive = list(range(nc))
+    k = 0
+    while True:
+        rep = alive[0]
+        w = _softmax(zt[rep, k], temperature)
+        if k == gamma:                        # every draft of the alive path kept: bonus from p_gamma
+            break
+        z = 1.0
+        q = _softmax(zd[rep, k], temperature)
+        kept = None
+        for c in alive:
+            t = int(dr[c, k])
+            if 0 <= t < V:
+                lhs = float(u[c, k]) * q[t] * z
+                rhs = w[t]
+                margin[c] = min(margin[c], abs(lhs - rhs) / max(rhs, 1e-300))
+                if lhs < rhs:
+                    kept = t
+                    break
+            w, z = _residual(w, z, q)
+        if kept is None:
+            break
+        for c in alive:
+            if int(dr[c, k]) != kept:
+                n_acc[c] = k
+        alive = [c for c in alive if int(dr[c, k]) == kept]
+        k += 1
+    for c in alive:
+        n_acc[c] = k
+    best = alive[0]
+    nxt, m2 = _inverse_cdf(w, float(u[0, gamma]))
+    margin[best] = min(margin[best], m2)
+    return n_acc, nxt, best, margin
+
+
 def accept_candidates(mode, target_logits, draft_logits, drafts, u, temperature=1.0):
     """Acceptance for every candidate block of every sequence, then the winner.
 
@@ -131,6 +220,10 @@ def accept_candidates(mode, target_logits, draft_logits, drafts, u, temperature=
     marg = np.zeros((nb, nc))
     best = np.zeros(nb, np.int32)
     for b in range(nb):
+        if mode == "recursive":
+            n_acc[b], t, best[b], marg[b] = recursive_accept(zt[b], draft_logits[b], drafts[b], u[b], temperature)
+            nxt[b] = t
+            continue
         for c in range(nc):
             if mode == "greedy":
                 k, t, m = greedy_accept(zt[b, c], drafts[b, c])

@@ -148,7 +148,8 @@ class Case:
         dv.verify(self.lay, self.st, self.blk, self.cfg.max_kv_len)
 
     def run_accept(self):
-        dv.accept(self.acc, hci.GREEDY if self.cfg.mode == "greedy" else hci.SAMPLE, self.cfg.temperature)
+        mode = {"greedy": hci.GREEDY, "sample": hci.SAMPLE, "recursive": hci.SAMPLE_RECURSIVE}[self.cfg.mode]
+        dv.accept(self.acc, mode, self.cfg.temperature)
 
     def run_slice(self):
         dv.slice_state(self.lay, self.st, self.blk, self.acc, self.cfg.max_kv_len)

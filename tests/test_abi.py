@@ -88,7 +88,11 @@ def test_accept_and_slice_validation():
     from hybrid_conv_iir_amd import hci
     lib = hci._lib
     p = 4096
-    assert lib.hci_accept(2, 1, 1, 6, 512, 1.0, p, p, p, p, p, p, p, p, None) == hci.EINVAL
+    assert lib.hci_accept(3, 1, 1, 6, 512, 1.0, p, p, p, p, p, p, p, p, None) == hci.EINVAL
+    assert lib.hci_accept(-1, 1, 1, 6, 512, 1.0, p, p, p, p, p, p, p, p, None) == hci.EINVAL
+    assert lib.hci_accept(hci.SAMPLE_RECURSIVE, 1, 2, 6, 512, -1.0, p, p, p, p, p, p, p, p, None) == hci.EINVAL
+    assert lib.hci_accept(hci.SAMPLE_RECURSIVE, 1, 2, 6, 512, 1.0, p, p, p, None, p, p, p, p, None) == hci.EINVAL
+    assert lib.hci_accept(hci.SAMPLE_RECURSIVE, 1, 65, 6, 512, 1.0, p, p, p, p, p, p, p, p, None) == hci.EINVAL
     assert lib.hci_accept(hci.SAMPLE, 1, 1, 6, 512, 0.0, p, p, p, p, p, p, p, p, None) == hci.EINVAL
     assert lib.hci_accept(hci.SAMPLE, 1, 1, 6, 512, 1.0, p, None, p, p, p, p, p, p, None) == hci.EINVAL
     assert lib.hci_accept(hci.GREEDY, 1, 1, 6, 0, 1.0, p, None, p, None, p, p, p, p, None) == hci.EINVAL

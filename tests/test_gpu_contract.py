@@ -73,8 +73,9 @@ def test_block_plus_slice_equals_sequential_steps(cfgname, L):
         a, bsnap = blk_state.snapshot(), seq_state.snapshot()
         for key in a:
             np.testing.assert_array_equal(a[key], bsnap[key], err_msg=f"k={k} {key}")
-        for cache in ("k_cache", "v_cache"):
-            assert torch.equal(getattr(blk_state, cache), getattr(seq_state, cache)), f"k={k} {cache}"
+        for cache in ("k_cache", "v_cache"):    # bitwise: rows past kv_len hold whatever the allocator left
+            assert torch.equal(getattr(blk_state, cache).view(torch.uint8),
+                               getattr(seq_state, cache).view(torch.uint8)), f"k={k} {cache}"
         np.testing.assert_array_equal(f[: k + 1], outs["f"])
         np.testing.assert_array_equal(s[: k + 1], outs["s"])
         np.testing.assert_array_equal(y[: k + 1], outs["y"])

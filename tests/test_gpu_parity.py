@@ -138,6 +138,17 @@ def test_c4_multi_candidate_ragged_full_size():
     _check_round(Case(synth.CONFIGS["c4"]))
 
 
+def test_c4_recursive_acceptance_full_size():
+    """The 4-candidate workload with lossless recursive acceptance over the candidates."""
+    _check_round(Case(synth.scaled(synth.CONFIGS["c4"], mode="recursive")))
+
+
+def test_recursive_acceptance_shared_prefixes_round():
+    """Small vocabulary: candidates share drafted prefixes, so the kept path can belong to any of them."""
+    cfg = synth.scaled(synth.CONFIGS["c4"], mode="recursive", vocab=4, kv_lens=(333, 31, 1024, 0), cfg_id=41)
+    _check_round(Case(cfg))
+
+
 def test_c4_needles():
     cfg = synth.scaled(synth.CONFIGS["c4"], kv_lens=(100, 2047, 5000, 64))
     _check_round(Case(cfg, needle="self"))
