@@ -252,6 +252,118 @@ def bench_prefill(args, cfg, hip):
     print(json.dumps(out), flush=True)
 
 
+def bench_linear(args, hip):
+    """y = x W for the verified block's rows: every weight byte read once per call (HBM-bound)."""
+    import numpy as np
+    import torch
+    from hybrid_conv_iir_amd import hci, synth
+    M, K, N = (int(v) for v in args.linear_shape.split(","))
+    x = synth.dense((M, K), 1.0, 1, device="cuda")
+    w = synth.dense((K, N), K ** -0.5, 2, device="cuda")
+    wps = []
+    for _ in range(4):          # rotate weights so no call finds the previous one's bytes in the 256 MB MALL
+        wp = torch.empty(hci.linear_packed_elems(K, N), dtype=torch.bfloat16, device="cuda")
+        hci.linear_pack(w, wp)
+        wps.append(wp)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    sp = torch.cuda.current_stream().cuda_stream
+    for i in range(args.warmup):
+        hci.linear(x, wps[i % 4], N, y)
+    evs = [_events(hip, 2) for _ in range(args.steps)]
+    for i in range(args.steps):
+        hip.hipEventRecord(evs[i][0], sp)
+        hci.linear(x, wps[i % 4], N, y)
+        hip.hipEventRecord(evs[i][1], sp)
+    torch.cuda.synchronize()
+    ms = float(np.median([_ms(hip, e[0], e[1]) for e in evs]))
+    alg = 2.0 * (K * N + M * K + M * N)
+    gbs = alg / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "dense projection rows/sec (weights streamed once per call)",
+        "value": round(M / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) rows, N(0,1/K) weights)",
+        "config": {"workload": f"y = x W with x {M}x{K}, W {K}x{N} bf16 (a block of {M} rows through a "
+                               f"{K}->{N} projection)", "M": M, "K": K, "N": N},
+        "roofline": {"kernel": "k_linear", "bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0,
+                     "unit": "GB/s", "frac": round(gbs / 8000.0, 4), "traffic": None, "alg_bytes_per_launch": alg},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def model_alg_bytes(mc) -> float:
+    """Bytes a stack verify must move: every projection weight once, each attention layer's KV prefix
+    once per sequence, the committed windows and IIR states read, and the block tensors written
+    (residual streams, in-projection streams, u / s) -- activations in bf16, retained tensors in fp32."""
+    d, rows, N = mc.d, mc.rows, mc.poles
+    total = 0.0
+    for l, kind in enumerate(mc.kinds):
+        total += 2.0 * (3 * d * d + d * d)                               # W_in, W_out
+        total += rows * d * 2 * 2                                        # a and the new x
+        if kind == "attn":
+            total += sum(2.0 * 2 * L * d for L in mc.kv_lens)            # K and V prefix, bf16
+            total += 3 * rows * d * 2 + rows * d * 2                     # q/k/v, o
+        else:
+            total += 3 * rows * d * 4 + rows * d * 2                     # z (fp32), y
+            total += mc.nb * (mc.taps_short - 1) * 3 * d * 4             # short window
+            if kind == "fir":
+                total += rows * d * 4 + mc.nb * (mc.taps_long[l] - 1) * d * 4 + mc.taps_long[l] * d * 4
+            else:
+                total += rows * d * N * 4 + mc.nb * d * N * 4 + 3 * d * N * 4
+    return total
+
+
+def bench_model(args, hip):
+    """One verify of the block through the whole layer stack (+ the slice), inputs resident."""
+    import numpy as np
+    import torch
+    from hybrid_conv_iir_amd import model as dm
+    from hybrid_conv_iir_amd import synth
+    mc = synth.MODEL_CONFIGS[args.model]
+    params = synth.make_model(mc, 0, device="cuda")
+    dmod = dm.DeviceModel(mc, params)
+    del params
+    st0 = synth.make_model_state(mc, 0, device="cuda")
+    st = dm.DeviceModelState(dmod, (max(mc.kv_lens) + 64 + 31) // 32 * 32)
+    st.load(st0)
+    del st0
+    blk = dm.DeviceModelBlock(dmod, mc.nb, mc.nc, mc.gamma)
+    blk.set_input(synth.model_block_input(mc, 0, 0, device="cuda"))
+    bound = max(mc.kv_lens)
+    n_acc = torch.zeros((mc.nb, mc.nc), dtype=torch.int32, device="cuda")
+    sp = torch.cuda.current_stream().cuda_stream
+    for _ in range(args.warmup):
+        dm.verify(dmod, st, blk, bound)
+    evs = [_events(hip, 3) for _ in range(args.steps)]
+    for i in range(args.steps):
+        hip.hipEventRecord(evs[i][0], sp)
+        dm.verify(dmod, st, blk, bound)
+        hip.hipEventRecord(evs[i][1], sp)
+        dm.slice_state(dmod, st, blk, bound, n_acc)              # commits k = 0 (one row): state changes
+        hip.hipEventRecord(evs[i][2], sp)
+        bound += 1
+    torch.cuda.synchronize()
+    v_ms = float(np.median([_ms(hip, e[0], e[1]) for e in evs]))
+    s_ms = float(np.median([_ms(hip, e[1], e[2]) for e in evs]))
+    alg = model_alg_bytes(mc)
+    gbs = alg / (v_ms * 1e-3) / 1e9
+    out = {
+        "metric": "verified block-positions/sec through the layer stack",
+        "value": round(mc.rows / (v_ms * 1e-3), 1), "unit": "block-positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(v_ms + s_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded weights, state and block rows; no trained weights)",
+        "config": {"workload": f"{len(mc.kinds)}-layer stripe {'/'.join(mc.kinds)} at d={mc.d}, "
+                               f"{mc.heads}x{mc.head_dim} heads, KV prefix {list(mc.kv_lens)}, gamma={mc.gamma}",
+                   "layers": list(mc.kinds), "d": mc.d, "kv_len": list(mc.kv_lens), "gamma": mc.gamma},
+        "verify_ms": round(v_ms, 4), "slice_ms": round(s_ms, 4),
+        "roofline": {"kernel": "hci_model_verify, all launches", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": 8000.0, "unit": "GB/s", "frac": round(gbs / 8000.0, 4), "traffic": None,
+                     "alg_bytes_per_launch": alg},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,8 +373,11 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-oracle sample (0 = all)")
     ap.add_argument("--cpu-reps", type=int, default=3, help="repetitions of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="verify", choices=["verify", "prefill"],
-                    help="verify: the verify->accept->slice step (default); prefill: prompt -> committed state")
+    ap.add_argument("--mode", default="verify", choices=["verify", "prefill", "linear", "model"],
+                    help="verify: the verify->accept->slice step (default); prefill: prompt -> committed state; "
+                         "linear: one dense projection of the verified block")
+    ap.add_argument("--linear-shape", default="13,4096,12288", help="M,K,N for --mode linear")
+    ap.add_argument("--model", default="m4_long", help="layer stack for --mode model")
     ap.add_argument("--prompt", type=int, default=262144, help="prompt length for --mode prefill")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run the known-size copy kernel once on this many MiB (byte-counter calibration)")
@@ -290,6 +405,10 @@ def main():
         del csrc, cdst
     if args.mode == "prefill":
         return bench_prefill(args, cfg, hip)
+    if args.mode == "linear":
+        return bench_linear(args, hip)
+    if args.mode == "model":
+        return bench_model(args, hip)
     W, K = args.warmup, args.steps
     P = cfg.P
     kv_cap = (cfg.max_kv_len + (W + K + 2) * P + 31) // 32 * 32

@@ -202,6 +202,119 @@ int hci_kv_read(const hci_layer* L, const hci_state* S, int nb, int b, int row0,
     return kv_access(L, S, nb, b, row0, nrows, nullptr, nullptr, false, stream, k_rows, v_rows);
 }
 
+static bool linear_shape_ok(int K, int N) {
+    return K >= 32 && N >= 16 && K % 32 == 0 && N % 16 == 0 && N / 16 <= 2147483647 / 16 && K <= (1 << 20) &&
+           N <= (1 << 20);
+}
+
+size_t hci_linear_packed_elems(int K, int N) {
+    return linear_shape_ok(K, N) ? (size_t)K * N : 0;
+}
+
+int hci_linear_pack(int K, int N, const void* w, void* w_packed, hipStream_t stream) {
+    if (!linear_shape_ok(K, N)) return HCI_EUNSUPPORTED;
+    if (!w || !w_packed || !aligned(w_packed, 16)) return HCI_EINVAL;
+    return launch_linear_pack(K, N, w, w_packed, stream) == hipSuccess ? HCI_OK : HCI_EDEVICE;
+}
+
+int hci_linear(int M, int K, int N, const void* x, const void* w_packed, const void* residual, void* y,
+               int out_f32, hipStream_t stream) {
+    if (!linear_shape_ok(K, N)) return HCI_EUNSUPPORTED;
+    if (M < 1 || M > 65535 * 64) return HCI_EINVAL;
+    if (!x || !w_packed || !y || !aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 16)) return HCI_EINVAL;
+    if (residual && !aligned(residual, 16)) return HCI_EINVAL;
+    return launch_linear(M, K, N, 1, x, w_packed, residual, y, out_f32 != 0, stream) == hipSuccess ? HCI_OK
+                                                                                                : HCI_EDEVICE;
+}
+
+int hci_rmsnorm(int M, int K, const void* x, const float* gamma, float eps, void* y, hipStream_t stream) {
+    if (M < 1 || K < 1 || !x || !gamma || !y || !(eps >= 0.f)) return HCI_EINVAL;
+    return launch_rmsnorm(M, K, x, gamma, eps, y, stream) == hipSuccess ? HCI_OK : HCI_EDEVICE;
+}
+
+static int check_model(const hci_model* M) {
+    if (!M || !M->layers || M->n_layers < 1 || M->n_layers > 1024) return HCI_EINVAL;
+    if (M->d < 32 || M->d % 32 || M->heads < 1 || M->head_dim < 1 || M->heads * M->head_dim != M->d)
+        return HCI_EINVAL;
+    if (M->head_dim != 64 && M->head_dim != 128) return HCI_EUNSUPPORTED;
+    if (M->feature_layer < 0 || M->feature_layer >= M->n_layers || M->feature_window < 1) return HCI_EINVAL;
+    if (!(M->eps >= 0.f)) return HCI_EINVAL;
+    for (int l = 0; l < M->n_layers; ++l) {
+        const hci_mixer& x = M->layers[l];
+        if (!x.norm || !x.w_in || !x.w_out || !aligned(x.w_in, 16) || !aligned(x.w_out, 16)) return HCI_EINVAL;
+        if (x.kind == HCI_MIX_ATTN) continue;
+        if (x.kind != HCI_MIX_FIR && x.kind != HCI_MIX_IIR) return HCI_EINVAL;
+        if (x.taps_short < 1 || x.taps_short > 8 || !x.w_short) return HCI_EUNSUPPORTED;
+        if (x.kind == HCI_MIX_FIR && (x.taps_long < 1 || x.taps_long > 256 || !x.w_long)) return HCI_EUNSUPPORTED;
+        if (x.kind == HCI_MIX_IIR && (x.poles < 1 || x.poles > 16 || !x.lambda || !x.beta || !x.c))
+            return HCI_EUNSUPPORTED;
+    }
+    return HCI_OK;
+}
+
+static int check_model_io(const hci_model* M, const hci_model_state* S, const hci_model_block* blk, int nb, int nc,
+                          int gamma, int max_kv_len) {
+    int rc = check_model(M);
+    if (rc) return rc;
+    if (nb < 1 || nb > 65535 || nc < 1 || gamma < 0 || max_kv_len < 0) return HCI_EINVAL;
+    const int P = gamma + 1;
+    if (P > 64 || (long long)nc * P > 64 || (long long)nb * nc * P > 65535) return HCI_EUNSUPPORTED;
+    if (!S || !S->layers || !S->kv_len || !S->feature || !blk || !blk->x || !blk->layers) return HCI_EINVAL;
+    if (!aligned(blk->x, 16)) return HCI_EINVAL;
+    bool attn = false;
+    for (int l = 0; l < M->n_layers; ++l) {
+        const hci_mixer& x = M->layers[l];
+        const hci_layer_state& ls = S->layers[l];
+        const hci_layer_block& lb = blk->layers[l];
+        if (!lb.z || !aligned(lb.z, 16)) return HCI_EINVAL;
+        if (x.kind == HCI_MIX_ATTN) {
+            attn = true;
+            if (!ls.k_cache || !ls.v_cache || !aligned(ls.k_cache, 16) || !aligned(ls.v_cache, 16)) return HCI_EINVAL;
+            continue;
+        }
+        if (x.taps_short > 1 && !ls.short_win) return HCI_EINVAL;
+        if (x.kind == HCI_MIX_FIR && (!lb.u || (x.taps_long > 1 && !ls.long_win))) return HCI_EINVAL;
+        if (x.kind == HCI_MIX_IIR && (!lb.s || !ls.iir)) return HCI_EINVAL;
+    }
+    if (attn) {
+        if (S->kv_cap < kTile || S->kv_cap % kTile) return HCI_EINVAL;
+        if ((long long)max_kv_len + P > S->kv_cap) return HCI_ECAPACITY;
+    }
+    return HCI_OK;
+}
+
+size_t hci_model_workspace_bytes(const hci_model* M, int nb, int nc, int gamma, int max_kv_len) {
+    if (check_model(M) != HCI_OK || nb < 1 || nc < 1 || gamma < 0 || max_kv_len < 0) return 0;
+    return plan_model(M, nb, nc, gamma, max_kv_len, device_cu_count()).bytes;
+}
+
+int hci_model_verify(const hci_model* M, const hci_model_state* S, const hci_model_block* blk,
+                     int nb, int nc, int gamma, int max_kv_len, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_model_io(M, S, blk, nb, nc, gamma, max_kv_len);
+    if (rc) return rc;
+    const int P = gamma + 1;
+    const ModelPlan plan = plan_model(M, nb, nc, gamma, max_kv_len, device_cu_count());
+    if (!ws || ws_bytes < plan.bytes || !aligned(ws, 256)) return HCI_EWORKSPACE;
+    if (plan.has_attn) {
+        const hci_layer L{M->d, 1, 1, 1, M->heads, M->head_dim, HCI_BF16, nullptr, nullptr, nullptr, nullptr, nullptr};
+        if (stream_lds_bytes(&L, nc, P) > kMaxLds) return HCI_EUNSUPPORTED;
+    }
+    if (launch_model_verify(M, S, blk, nb, nc, P, plan, ws, stream) != hipSuccess) return HCI_EDEVICE;
+    return HCI_OK;
+}
+
+int hci_model_slice(const hci_model* M, const hci_model_state* S, const hci_model_block* blk,
+                    int nb, int nc, int gamma, int max_kv_len,
+                    const int32_t* n_accepted, const int32_t* best_cand, hipStream_t stream) {
+    int rc = check_model_io(M, S, blk, nb, nc, gamma, max_kv_len);
+    if (rc) return rc;
+    if (!n_accepted || (nc > 1 && !best_cand)) return HCI_EINVAL;
+    if (launch_model_slice(M, S, blk, nb, nc, gamma + 1, n_accepted, nc > 1 ? best_cand : nullptr, stream) !=
+        hipSuccess)
+        return HCI_EDEVICE;
+    return HCI_OK;
+}
+
 int hci_probe_sink_words(void) { return probe_blocks(); }
 
 int hci_probe_read(const void* src, size_t bytes, float* sink, hipStream_t stream) {

@@ -626,7 +626,8 @@ static hipError_t launch_stream(const StreamArgs& A, int blocks, size_t lds, hip
 }
 
 hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block* blk,
-                         int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st, hipEvent_t* ev)
+                         int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st, hipEvent_t* ev,
+                         bool conv)
 {
     const int H = L->heads, DH = L->head_dim, nq = plan.nq;
     const float scale_log2 = kLog2e / sqrtf((float)DH);
@@ -655,8 +656,7 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
         // a whole CU per workgroup, so the short roles run as their own light kernels.
         const bool fuse = nqt == 1;
         if (!fuse) {
-            e = launch_conv_iir(L, S, blk, nb, nc, P, st);
-            if (e != hipSuccess) return e;
+            if (conv && (e = launch_conv_iir(L, S, blk, nb, nc, P, st)) != hipSuccess) return e;
             const size_t tail_lds = tail_lds_floats(P, DH, 2) * sizeof(float);
             if (tail_lds > 65536) {
                 e = hipFuncSetAttribute((const void*)k_attn_tail<HCI_BF16>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -668,7 +668,7 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
                                part_ml, H, DH, P, nq, plan.slots, plan.n_chunks, scale_log2);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        A.n_conv = fuse ? ((L->d + kCG - 1) / kCG) * nc * nb : 0;
+        A.n_conv = fuse && conv ? ((L->d + kCG - 1) / kCG) * nc * nb : 0;
         A.n_tail = fuse ? nb * nc * H : 0;
         const long long blocks = (long long)A.prefix_blocks + A.n_conv + A.n_tail;
         if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -692,8 +692,7 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
             if (e != hipSuccess) return e;
         }
     } else {
-        e = launch_conv_iir(L, S, blk, nb, nc, P, st);
-        if (e != hipSuccess) return e;
+        if (conv && (e = launch_conv_iir(L, S, blk, nb, nc, P, st)) != hipSuccess) return e;
         const size_t tail_lds = tail_lds_floats(P, DH, 4) * sizeof(float);
         if (tail_lds > 65536) {
             e = hipFuncSetAttribute((const void*)k_attn_tail<HCI_F32>, hipFuncAttributeMaxDynamicSharedMemorySize,

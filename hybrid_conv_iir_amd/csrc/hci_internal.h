@@ -107,7 +107,8 @@ hipError_t launch_conv_iir(const hci_layer* L, const hci_state* S, const hci_blo
 // the whole verify: streaming kernel(s) then the combine; ev (may be null)
 // = 3 events recorded before, after the streaming part, and at the end
 hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block* blk,
-                         int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st, hipEvent_t* ev);
+                         int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st, hipEvent_t* ev,
+                         bool conv = true);
 hipError_t launch_accept(int mode, int nb, int nc, int gamma, int V, float temperature,
                          const float* zt, const float* zd, const int32_t* drafts, const double* u,
                          int32_t* n_acc, int32_t* next, int32_t* best, double* margin, hipStream_t st);
@@ -134,6 +135,32 @@ bool prefill_state_path(const hci_layer* L, int T, bool want_y);
 size_t prefill_state_lds_bytes(const hci_layer* L);
 hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T, const void* x, const void* k,
                           const void* v, void* y, const PrefillPlan& plan, void* ws, hipStream_t st);
+
+// dense projections
+struct LinearPlan {
+    int ct, mt, kw, kspw;        // column strips and 16-row tiles per workgroup, waves splitting K, K steps per wave
+    int grid_x, grid_y;
+    size_t lds;
+};
+LinearPlan plan_linear(int M, int K, int N);
+hipError_t launch_linear(int M, int K, int N, int parts, const void* x, const void* wp, const void* res, void* y,
+                         bool out_f32, hipStream_t st);
+hipError_t launch_linear_pack(int K, int N, const void* w, void* wp, hipStream_t st);
+hipError_t launch_rmsnorm(int M, int K, const void* x, const float* g, float eps, void* y, hipStream_t st);
+
+// full layer stack
+struct ModelPlan {
+    size_t rows;                 // nb * nc * P
+    size_t a_off, y_off, attn_off, bytes;
+    bool has_attn;
+    AttnPlan attn;
+};
+size_t mixer_lds_bytes(int kind, int Tl, int P);
+ModelPlan plan_model(const hci_model* M, int nb, int nc, int gamma, int max_kv_len, int num_cus);
+hipError_t launch_model_verify(const hci_model* M, const hci_model_state* S, const hci_model_block* blk, int nb,
+                               int nc, int P, const ModelPlan& plan, void* ws, hipStream_t st);
+hipError_t launch_model_slice(const hci_model* M, const hci_model_state* S, const hci_model_block* blk, int nb,
+                              int nc, int P, const int32_t* n_acc, const int32_t* best, hipStream_t st);
 
 hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t st);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t st);

@@ -1,0 +1,234 @@
+// Dense projections for the layers around the conv/IIR/attention mixers:
+// y = x W (+ residual) with few rows (the verified block: nb * nc * P rows)
+// and a large weight, so the weight stream from HBM is the cost and every
+// weight byte is read once per call.
+//
+// The weight is packed once in matrix-core operand order: tiles of 32 (K) x
+// 16 (N), the tiles of one 16-column strip stored consecutively, and inside
+// a tile element [g<4][n<16][e<8] holding W[32 kt + 8 g + e][16 nt + n], so
+// the B operand of v_mfma_f32_16x16x32_bf16 is one contiguous 16-byte load
+// per lane (a contiguous kilobyte per wave).  A workgroup owns one column
+// strip and up to 64 rows; its waves split K into contiguous ranges
+// and stream their part of the strip with non-temporal loads, the rows
+// (A operands) come from L2; the wave partials are summed in a fixed order
+// through LDS, so results do not depend on scheduling.
+#include "hci_internal.h"
+
+namespace hci {
+
+constexpr int kLinMT = 4;              // 16-row tiles per workgroup (64 rows)
+
+__device__ __forceinline__ bf16x8 as_bf16x8_u(u32x4 v) {
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
+// One workgroup: CT column strips (16 columns each) x up to 16 * MT rows; its KW waves
+// split K.  Per K step a wave loads CT weight fragments and one row fragment per 16-row tile,
+// so each row fragment read from L2 feeds CT matrix-core products.
+template <int CT, int MT, bool OUT_F32>
+__global__ __launch_bounds__(1024) void k_linear(const uint16_t* __restrict__ x, const u32x4* __restrict__ wp,
+                                                 const uint16_t* __restrict__ res, void* __restrict__ y,
+                                                 int M, int K, int N, int kspw, int parts)
+{
+    extern __shared__ float red[];                 // [KW][CT][mts][64][4]
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, KW = blockDim.x >> 6;
+    const int nt0 = blockIdx.x * CT, row0 = blockIdx.y * 16 * MT;
+    const int NT = N >> 4, KT = K >> 5;
+    const int kt0 = wv * kspw, kt1 = min(KT, kt0 + kspw);
+    const int rl = lane & 15, ko = 8 * (lane >> 4);
+    int mts = (M - row0 + 15) >> 4;
+    mts = mts > MT ? MT : mts;
+    const u32x4* wcol[CT];
+    bool cok[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        cok[c] = nt0 + c < NT;
+        wcol[c] = wp + (size_t)(cok[c] ? nt0 + c : 0) * KT * 64 + lane;
+    }
+    f32x4 acc[CT][MT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* xr[MT];
+    bool ok[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int row = row0 + 16 * mt + rl;
+        ok[mt] = row < M;
+        xr[mt] = x + (size_t)(ok[mt] ? row : 0) * K + ko;
+    }
+    constexpr int U = CT >= 4 ? 2 : 4;
+    int kt = kt0;
+    for (; kt + U <= kt1; kt += U) {
+        u32x4 b[U][CT];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+                b[u][c] = cok[c] ? __builtin_nontemporal_load(wcol[c] + (size_t)(kt + u) * 64) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if (mt < mts) {
+                u32x4 a[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    a[u] = ok[mt] ? *(const u32x4*)(xr[mt] + 32 * (kt + u)) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int c = 0; c < CT; ++c)
+                        acc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_u(a[u]), as_bf16x8_u(b[u][c]),
+                                                                             acc[c][mt], 0, 0, 0);
+            }
+        }
+    }
+    for (; kt < kt1; ++kt) {
+        u32x4 b[CT];
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+            b[c] = cok[c] ? __builtin_nontemporal_load(wcol[c] + (size_t)kt * 64) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if (mt < mts) {
+                const u32x4 a = ok[mt] ? *(const u32x4*)(xr[mt] + 32 * kt) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int c = 0; c < CT; ++c)
+                    acc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_u(a), as_bf16x8_u(b[c]),
+                                                                         acc[c][mt], 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            if (mt < mts)
+                *(f32x4*)(red + ((((size_t)wv * CT + c) * mts + mt) * 64 + lane) * 4) = acc[c][mt];
+    __syncthreads();
+    // element e -> (c, mt, r, g, n): row 16 mt + 4 g + r, column 16 (nt0 + c) + n (columns fastest)
+    const int Np = N / parts;
+    for (int e = threadIdx.x; e < CT * MT * 256; e += blockDim.x) {
+        const int n = e & 15, g = (e >> 4) & 3, r = (e >> 6) & 3, mt = (e >> 8) % MT, c = e / (256 * MT);
+        const int row = row0 + 16 * mt + 4 * g + r;
+        if (mt >= mts || row >= M || nt0 + c >= NT) continue;
+        const int ln = 16 * g + n;
+        float v = 0.f;
+        for (int w = 0; w < KW; ++w) v += red[((((size_t)w * CT + c) * mts + mt) * 64 + ln) * 4 + r];
+        const int col = 16 * (nt0 + c) + n;
+        const int p = col / Np;
+        const size_t o = ((size_t)p * M + row) * Np + (col - p * Np);     // [parts][M][N / parts]
+        if (res) v += bf2f(res[o]);
+        if (OUT_F32) ((float*)y)[o] = v;
+        else ((uint16_t*)y)[o] = f2bf(v);
+    }
+}
+
+// w [K][N] bf16 row-major -> packed tiles
+__global__ void k_linear_pack(const uint16_t* __restrict__ w, uint16_t* __restrict__ wp, int K, int N)
+{
+    const size_t total = (size_t)K * N;
+    const int KT = K >> 5;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+        const int e = (int)(i & 7), n = (int)((i >> 3) & 15), g = (int)((i >> 7) & 3);
+        const size_t tile = i >> 9;
+        const int kt = (int)(tile % KT), nt = (int)(tile / KT);
+        wp[i] = w[(size_t)(32 * kt + 8 * g + e) * N + 16 * nt + n];
+    }
+}
+
+// y = x * g / sqrt(mean(x^2) + eps) per row, rounded to bf16; one workgroup per row
+__global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t* __restrict__ x, const float* __restrict__ gamma,
+                                                 float eps, uint16_t* __restrict__ y, int K)
+{
+    __shared__ float part[4];
+    const uint16_t* xr = x + (size_t)blockIdx.x * K;
+    float s = 0.f;
+    for (int k = threadIdx.x; k < K; k += blockDim.x) {
+        const float v = bf2f(xr[k]);
+        s = fmaf(v, v, s);
+    }
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float inv = 1.0f / sqrtf(tot / (float)K + eps);
+    for (int k = threadIdx.x; k < K; k += blockDim.x)
+        y[(size_t)blockIdx.x * K + k] = f2bf(bf2f(xr[k]) * inv * gamma[k]);
+}
+
+// Launch shape: CT column strips per workgroup and KW waves splitting K, sized so that the
+// grid holds about 4096 waves and the per-wave partials fit in 64 KB of LDS.
+LinearPlan plan_linear(int M, int K, int N) {
+    LinearPlan p{};
+    const int mts = (M + 15) / 16 < kLinMT ? (M + 15) / 16 : kLinMT;
+    p.mt = mts <= 1 ? 1 : (mts <= 2 ? 2 : 4);
+    const int NT = N / 16, KT = K / 32;
+    p.ct = NT >= 768 ? 4 : (NT >= 512 ? 2 : 1);     // keep >= 192 workgroups
+    if (p.mt == 4 && p.ct == 4) p.ct = 2;          // 4 x 4 accumulator tiles would not fit the register budget
+    const long long wgs = (long long)((NT + p.ct - 1) / p.ct) * ((M + 16 * p.mt - 1) / (16 * p.mt));
+    long long kw = (4096 + wgs - 1) / wgs;
+    const int lds_cap = 64 / (p.ct * mts);          // KB of partials per wave: ct * mts
+    if (kw > 16) kw = 16;
+    if (kw > lds_cap) kw = lds_cap;
+    if (kw > KT) kw = KT;
+    if (kw < 1) kw = 1;
+    p.kw = (int)kw;
+    p.kspw = (KT + p.kw - 1) / p.kw;
+    p.lds = (size_t)p.kw * p.ct * mts * 64 * 4 * sizeof(float);
+    p.grid_x = (NT + p.ct - 1) / p.ct;
+    p.grid_y = (M + 16 * p.mt - 1) / (16 * p.mt);
+    return p;
+}
+
+template <int CT, int MT>
+static hipError_t launch_ct(const LinearPlan& p, int M, int K, int N, int parts, const void* x, const void* wp,
+                            const void* res, void* y, bool out_f32, hipStream_t st)
+{
+    const void* fn = out_f32 ? (const void*)k_linear<CT, MT, true> : (const void*)k_linear<CT, MT, false>;
+    if (p.lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid(p.grid_x, p.grid_y), block(64 * p.kw);
+    if (out_f32)
+        hipLaunchKernelGGL((k_linear<CT, MT, true>), grid, block, p.lds, st, (const uint16_t*)x, (const u32x4*)wp,
+                           (const uint16_t*)res, y, M, K, N, p.kspw, parts);
+    else
+        hipLaunchKernelGGL((k_linear<CT, MT, false>), grid, block, p.lds, st, (const uint16_t*)x, (const u32x4*)wp,
+                           (const uint16_t*)res, y, M, K, N, p.kspw, parts);
+    return hipGetLastError();
+}
+
+hipError_t launch_linear(int M, int K, int N, int parts, const void* x, const void* wp, const void* res, void* y,
+                         bool out_f32, hipStream_t st)
+{
+    const LinearPlan p = plan_linear(M, K, N);
+#define HCI_LIN_CASE(CT_, MT_) \
+    if (p.ct == CT_ && p.mt == MT_) return launch_ct<CT_, MT_>(p, M, K, N, parts, x, wp, res, y, out_f32, st);
+    HCI_LIN_CASE(4, 1) HCI_LIN_CASE(4, 2)
+    HCI_LIN_CASE(2, 1) HCI_LIN_CASE(2, 2) HCI_LIN_CASE(2, 4)
+    HCI_LIN_CASE(1, 1) HCI_LIN_CASE(1, 2) HCI_LIN_CASE(1, 4)
+#undef HCI_LIN_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_linear_pack(int K, int N, const void* w, void* wp, hipStream_t st)
+{
+    const size_t total = (size_t)K * N;
+    size_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(k_linear_pack, dim3((unsigned)blocks), dim3(256), 0, st, (const uint16_t*)w, (uint16_t*)wp,
+                       K, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int M, int K, const void* x, const float* g, float eps, void* y, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, st, (const uint16_t*)x, g, eps, (uint16_t*)y, K);
+    return hipGetLastError();
+}
+
+}  // namespace hci

@@ -1,0 +1,338 @@
+// A stack of full hybrid layers verified as one block and sliced layer by
+// layer (the StripedHyena2 target of the EvSpark digest: Hyena layers with
+// explicit or modal long filters interleaved with attention; Figure 1(a),
+// Interpretation; slicing per state class as in Figure 1(d)).
+//
+// Per layer, on the block rows (nb * nc * P of them):
+//   k_rmsnorm        a = bf16(RMSNorm(x) g)
+//   k_linear         z = a W_in as three [rows][d] streams (fp32 for Hyena,
+//                    bf16 q/k/v for attention)
+//   k_hyena_mixer    short FIR of the 3d channels, u = zk * zv, the long
+//                    filter (explicit FIR over the u window, or the modal
+//                    IIR keeping every s_i), y = bf16(zq * h)
+//   (attention)      the verify attention path (KV stream, causal block
+//                    part, fixed-order combine) with the conv role off
+//   k_linear         x' = bf16(x + y W_out)
+// Slicing: k_model_slice_hyena (both windows and the IIR state),
+// k_model_slice_kv (accepted K/V rows into the tiled cache),
+// k_model_slice_feature (the drafter's window of target states), then
+// k_model_slice_len (kv_len += k + 1, after every reader of kv_len).
+#include "hci_internal.h"
+
+namespace hci {
+
+constexpr int kMxCG = 16;                   // channels per mixer workgroup (16 lanes each)
+
+size_t mixer_lds_bytes(int kind, int Tl, int P) {
+    size_t f = 3 * (size_t)P * kMxCG;                                       // zhat [3][P][16]
+    if (kind == HCI_MIX_FIR) f += ((size_t)(Tl - 1) + P) * kMxCG + (size_t)Tl * kMxCG;   // u window + u, taps
+    else f += (size_t)P * kMxCG;                                            // u
+    return f * sizeof(float);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void k_hyena_mixer(
+    const float* __restrict__ z, const float* __restrict__ short_win, const float* __restrict__ long_win,
+    const float* __restrict__ iir, const float* __restrict__ w_short, const float* __restrict__ w_long,
+    const float* __restrict__ lam, const float* __restrict__ beta, const float* __restrict__ cc,
+    uint16_t* __restrict__ y, float* __restrict__ u_out, float* __restrict__ s_out,
+    int d, int Ts, int Tl, int N, int nc, int P)
+{
+    extern __shared__ float lds[];
+    const int cg = blockIdx.x, cand = blockIdx.y, b = blockIdx.z;
+    const int ch0 = cg * kMxCG;
+    const size_t rows = (size_t)gridDim.z * nc * P;
+    const size_t row0 = ((size_t)b * nc + cand) * P;
+    const int Ws = Ts - 1, Wl = Tl - 1;
+    float* zh = lds;                                                        // [3][P][16]
+    float* ub = zh + (size_t)3 * P * kMxCG;                                 // FIR: [Wl + P][16], IIR: [P][16]
+    float* hl = ub + (size_t)(KIND == HCI_MIX_FIR ? Wl + P : P) * kMxCG;   // FIR: [Tl][16]
+    const int tid = threadIdx.x;
+
+    // short FIR of the three streams over [window ; block rows]
+    for (int e = tid; e < 3 * P * kMxCG; e += blockDim.x) {
+        const int c = e % kMxCG, i = (e / kMxCG) % P, sidx = e / (kMxCG * P);
+        const int ch = ch0 + c;
+        float acc = 0.f;
+        if (ch < d) {
+            const int col = sidx * d + ch;
+            for (int j = 0; j < Ts; ++j) {
+                const int m = i - j;
+                const float v = m >= 0 ? z[((size_t)sidx * rows + row0 + m) * d + ch]
+                                       : short_win[((size_t)b * Ws + (Ws + m)) * 3 * d + col];
+                acc = fmaf(w_short[(size_t)j * 3 * d + col], v, acc);
+            }
+        }
+        zh[e] = acc;
+    }
+    if (KIND == HCI_MIX_FIR) {
+        for (int e = tid; e < Wl * kMxCG; e += blockDim.x) {
+            const int ch = ch0 + e % kMxCG, r = e / kMxCG;
+            ub[e] = ch < d ? long_win[((size_t)b * Wl + r) * d + ch] : 0.f;
+        }
+        for (int e = tid; e < Tl * kMxCG; e += blockDim.x) {
+            const int ch = ch0 + e % kMxCG, j = e / kMxCG;
+            hl[e] = ch < d ? w_long[(size_t)j * d + ch] : 0.f;
+        }
+    }
+    __syncthreads();
+    const int uo = KIND == HCI_MIX_FIR ? Wl : 0;
+    for (int e = tid; e < P * kMxCG; e += blockDim.x) {
+        const int c = e % kMxCG, i = e / kMxCG, ch = ch0 + c;
+        const float u = zh[((size_t)P + i) * kMxCG + c] * zh[((size_t)2 * P + i) * kMxCG + c];
+        ub[(uo + i) * kMxCG + c] = u;
+        if (KIND == HCI_MIX_FIR && ch < d) u_out[(row0 + i) * d + ch] = u;
+    }
+    __syncthreads();
+    if (KIND == HCI_MIX_FIR) {
+        for (int e = tid; e < P * kMxCG; e += blockDim.x) {
+            const int c = e % kMxCG, i = e / kMxCG, ch = ch0 + c;
+            if (ch >= d) continue;
+            float h = 0.f;
+            for (int j = 0; j < Tl; ++j) h = fmaf(hl[j * kMxCG + c], ub[(Wl + i - j) * kMxCG + c], h);
+            y[(row0 + i) * d + ch] = f2bf(zh[(size_t)i * kMxCG + c] * h);
+        }
+    } else {
+        // 16 channels x 16 pole lanes; the readout sums the pole lanes by butterfly
+        const int c = tid >> 4, n = tid & 15, ch = ch0 + c;
+        const bool ok = ch < d && n < N;
+        const size_t o = (size_t)ch * N + n;
+        const float l = ok ? lam[o] : 0.f, bt = ok ? beta[o] : 0.f, cv = ok ? cc[o] : 0.f;
+        float s = ok ? iir[(size_t)b * d * N + o] : 0.f;
+        for (int i = 0; i < P; ++i) {
+            s = fmaf(l, s, bt * ub[i * kMxCG + c]);
+            if (ok) s_out[((row0 + i) * d + ch) * N + n] = s;
+            float part = cv * s;
+            part += __shfl_xor(part, 8);
+            part += __shfl_xor(part, 4);
+            part += __shfl_xor(part, 2);
+            part += __shfl_xor(part, 1);
+            if (n == 0 && ch < d) y[(row0 + i) * d + ch] = f2bf(zh[(size_t)i * kMxCG + c] * part);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ slicing
+
+__device__ __forceinline__ int accepted_rows(const int32_t* n_acc, const int32_t* best, int b, int nc, int P,
+                                             int& cand) {
+    int c = best ? best[b] : 0;
+    c = c < 0 ? 0 : (c >= nc ? nc - 1 : c);
+    int k = n_acc[(size_t)b * nc + c];
+    k = k < 0 ? 0 : (k >= P ? P - 1 : k);
+    cand = c;
+    return k + 1;
+}
+
+// new[r] = [old ; rows][nrow + r]: each thread owns one column and walks r upward, so every
+// read of old row nrow + r happens before that row is overwritten
+template <int KIND>
+__global__ __launch_bounds__(256) void k_model_slice_hyena(
+    float* __restrict__ short_win, float* __restrict__ long_win, float* __restrict__ iir,
+    const float* __restrict__ z, const float* __restrict__ u, const float* __restrict__ s,
+    const int32_t* __restrict__ n_acc, const int32_t* __restrict__ best, int d, int Ts, int Tl, int N, int nc,
+    int P)
+{
+    const int b = blockIdx.y;
+    int cand;
+    const int nrow = accepted_rows(n_acc, best, b, nc, P, cand);
+    const size_t rows = (size_t)gridDim.y * nc * P;
+    const size_t row0 = ((size_t)b * nc + cand) * P;
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    const int Ws = Ts - 1, Wl = Tl - 1;
+    if (t < 3 * d && Ws > 0) {
+        const int sidx = t / d, ch = t % d;
+        float* w = short_win + (size_t)b * Ws * 3 * d + t;
+        for (int r = 0; r < Ws; ++r) {
+            const int m = nrow + r;
+            w[(size_t)r * 3 * d] = m < Ws ? w[(size_t)m * 3 * d] : z[((size_t)sidx * rows + row0 + (m - Ws)) * d + ch];
+        }
+    }
+    if (KIND == HCI_MIX_FIR) {
+        if (t < d && Wl > 0) {
+            float* w = long_win + (size_t)b * Wl * d + t;
+            for (int r = 0; r < Wl; ++r) {
+                const int m = nrow + r;
+                w[(size_t)r * d] = m < Wl ? w[(size_t)m * d] : u[(row0 + (m - Wl)) * d + t];
+            }
+        }
+    } else if (t < d * N) {
+        iir[(size_t)b * d * N + t] = s[(row0 + nrow - 1) * d * N + t];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_model_slice_kv(
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const uint16_t* __restrict__ z,
+    const int32_t* __restrict__ kv_len, const int32_t* __restrict__ n_acc, const int32_t* __restrict__ best,
+    int H, int DH, int kv_cap, int nc, int P)
+{
+    const int b = blockIdx.y;
+    int cand;
+    const int nrow = accepted_rows(n_acc, best, b, nc, P, cand);
+    const size_t rows = (size_t)gridDim.y * nc * P;
+    const size_t row0 = ((size_t)b * nc + cand) * P;
+    const int d = H * DH, L0 = kv_len[b];
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;         // (i, h, dd)
+    if (e >= P * d) return;
+    const int i = e / d, hd = e % d, h = hd / DH, dd = hd % DH;
+    const int row = L0 + i;
+    if (i >= nrow || row < 0 || row >= kv_cap) return;
+    const size_t base = ((size_t)b * H + h) * (size_t)kv_cap * DH + (size_t)(row & ~(kTile - 1)) * DH;
+    kc[base + k_tile_offset(row & (kTile - 1), dd, DH)] = z[(rows + row0 + i) * d + hd];
+    vc[base + v_tile_offset(row & (kTile - 1), dd, DH)] = z[(2 * rows + row0 + i) * d + hd];
+}
+
+__global__ __launch_bounds__(256) void k_model_slice_feature(
+    uint16_t* __restrict__ feat, const uint16_t* __restrict__ xf, const int32_t* __restrict__ n_acc,
+    const int32_t* __restrict__ best, int d, int W, int nc, int P)
+{
+    const int b = blockIdx.y;
+    int cand;
+    const int nrow = accepted_rows(n_acc, best, b, nc, P, cand);
+    const size_t row0 = ((size_t)b * nc + cand) * P;
+    const int ch = blockIdx.x * blockDim.x + threadIdx.x;
+    if (ch >= d) return;
+    uint16_t* w = feat + (size_t)b * W * d + ch;
+    for (int r = 0; r < W; ++r) {
+        const int m = nrow + r;
+        w[(size_t)r * d] = m < W ? w[(size_t)m * d] : xf[(row0 + (m - W)) * d + ch];
+    }
+}
+
+__global__ void k_model_slice_len(int32_t* __restrict__ kv_len, const int32_t* __restrict__ n_acc,
+                                  const int32_t* __restrict__ best, int nb, int nc, int P, int kv_cap)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nb) return;
+    int cand;
+    const int L = kv_len[b] + accepted_rows(n_acc, best, b, nc, P, cand);
+    kv_len[b] = L > kv_cap ? kv_cap : L;
+}
+
+// ------------------------------------------------------------------ host
+
+static hci_layer attn_layer_view(const hci_model* M, const float* dummy) {
+    hci_layer L{};
+    L.d = M->d;
+    L.taps_short = 1;
+    L.taps_outer = 1;
+    L.poles = 1;
+    L.heads = M->heads;
+    L.head_dim = M->head_dim;
+    L.act_dtype = HCI_BF16;
+    L.w_short = L.w_outer = L.lambda = L.beta = L.c = dummy;
+    return L;
+}
+
+ModelPlan plan_model(const hci_model* M, int nb, int nc, int gamma, int max_kv_len, int num_cus) {
+    ModelPlan p{};
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t rows = (size_t)nb * nc * (gamma + 1);
+    p.rows = rows;
+    p.a_off = 0;
+    p.y_off = up(rows * M->d * 2);
+    p.attn_off = p.y_off + up(rows * M->d * 2);
+    bool has_attn = false;
+    for (int l = 0; l < M->n_layers; ++l) has_attn = has_attn || M->layers[l].kind == HCI_MIX_ATTN;
+    p.has_attn = has_attn;
+    size_t attn = 0;
+    if (has_attn) {
+        const hci_layer L = attn_layer_view(M, nullptr);
+        p.attn = plan_attention(&L, nb, nc, gamma, max_kv_len, num_cus);
+        attn = p.attn.bytes;
+    }
+    p.bytes = p.attn_off + up(attn);
+    return p;
+}
+
+hipError_t launch_model_verify(const hci_model* M, const hci_model_state* S, const hci_model_block* blk, int nb,
+                               int nc, int P, const ModelPlan& plan, void* ws, hipStream_t st)
+{
+    const int d = M->d;
+    const size_t rows = plan.rows;
+    uint16_t* a = (uint16_t*)((char*)ws + plan.a_off);
+    uint16_t* y = (uint16_t*)((char*)ws + plan.y_off);
+    void* attn_ws = (char*)ws + plan.attn_off;
+    hipError_t e;
+    for (int l = 0; l < M->n_layers; ++l) {
+        const hci_mixer& mx = M->layers[l];
+        const hci_layer_state& ls = S->layers[l];
+        const hci_layer_block& lb = blk->layers[l];
+        const uint16_t* xl = (const uint16_t*)blk->x + (size_t)l * rows * d;
+        uint16_t* xn = (uint16_t*)blk->x + (size_t)(l + 1) * rows * d;
+        if ((e = launch_rmsnorm((int)rows, d, xl, mx.norm, M->eps, a, st)) != hipSuccess) return e;
+        if (mx.kind == HCI_MIX_ATTN) {
+            if ((e = launch_linear((int)rows, d, 3 * d, 3, a, mx.w_in, nullptr, lb.z, false, st)) != hipSuccess)
+                return e;
+            const hci_layer L = attn_layer_view(M, mx.norm);
+            hci_state SA{};
+            SA.kv_cap = S->kv_cap;
+            SA.k_cache = ls.k_cache;
+            SA.v_cache = ls.v_cache;
+            SA.kv_len = S->kv_len;
+            hci_block B{};
+            B.q = lb.z;
+            B.k = (uint16_t*)lb.z + rows * d;
+            B.v = (uint16_t*)lb.z + 2 * rows * d;
+            B.o = y;
+            if ((e = launch_verify(&L, &SA, &B, nb, nc, P, plan.attn, attn_ws, st, nullptr, false)) != hipSuccess)
+                return e;
+        } else {
+            if ((e = launch_linear((int)rows, d, 3 * d, 3, a, mx.w_in, nullptr, lb.z, true, st)) != hipSuccess)
+                return e;
+            const dim3 grid((d + kMxCG - 1) / kMxCG, nc, nb);
+            const size_t lds = mixer_lds_bytes(mx.kind, mx.taps_long, P);
+            if (mx.kind == HCI_MIX_FIR)
+                hipLaunchKernelGGL(k_hyena_mixer<HCI_MIX_FIR>, grid, dim3(256), lds, st, (const float*)lb.z,
+                                   ls.short_win, ls.long_win, ls.iir, mx.w_short, mx.w_long, mx.lambda, mx.beta, mx.c,
+                                   y, lb.u, lb.s, d, mx.taps_short, mx.taps_long, mx.poles, nc, P);
+            else
+                hipLaunchKernelGGL(k_hyena_mixer<HCI_MIX_IIR>, grid, dim3(256), lds, st, (const float*)lb.z,
+                                   ls.short_win, ls.long_win, ls.iir, mx.w_short, mx.w_long, mx.lambda, mx.beta, mx.c,
+                                   y, lb.u, lb.s, d, mx.taps_short, 1, mx.poles, nc, P);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        if ((e = launch_linear((int)rows, d, d, 1, y, mx.w_out, xl, xn, false, st)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_model_slice(const hci_model* M, const hci_model_state* S, const hci_model_block* blk, int nb,
+                              int nc, int P, const int32_t* n_acc, const int32_t* best, hipStream_t st)
+{
+    const int d = M->d;
+    const size_t rows = (size_t)nb * nc * P;
+    for (int l = 0; l < M->n_layers; ++l) {
+        const hci_mixer& mx = M->layers[l];
+        const hci_layer_state& ls = S->layers[l];
+        const hci_layer_block& lb = blk->layers[l];
+        if (mx.kind == HCI_MIX_ATTN) {
+            const dim3 grid((unsigned)((P * (size_t)d + 255) / 256), nb);
+            hipLaunchKernelGGL(k_model_slice_kv, grid, dim3(256), 0, st, (uint16_t*)ls.k_cache, (uint16_t*)ls.v_cache,
+                               (const uint16_t*)lb.z, S->kv_len, n_acc, best, M->heads, M->head_dim, S->kv_cap, nc, P);
+        } else {
+            const int cols = mx.kind == HCI_MIX_FIR ? 3 * d : (3 * d > d * mx.poles ? 3 * d : d * mx.poles);
+            const dim3 grid((cols + 255) / 256, nb);
+            if (mx.kind == HCI_MIX_FIR)
+                hipLaunchKernelGGL(k_model_slice_hyena<HCI_MIX_FIR>, grid, dim3(256), 0, st, ls.short_win, ls.long_win,
+                                   ls.iir, (const float*)lb.z, lb.u, lb.s, n_acc, best, d, mx.taps_short,
+                                   mx.taps_long, mx.poles, nc, P);
+            else
+                hipLaunchKernelGGL(k_model_slice_hyena<HCI_MIX_IIR>, grid, dim3(256), 0, st, ls.short_win, ls.long_win,
+                                   ls.iir, (const float*)lb.z, lb.u, lb.s, n_acc, best, d, mx.taps_short, 1, mx.poles,
+                                   nc, P);
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const uint16_t* xf = (const uint16_t*)blk->x + (size_t)(M->feature_layer + 1) * rows * d;
+    hipLaunchKernelGGL(k_model_slice_feature, dim3((d + 255) / 256, nb), dim3(256), 0, st, (uint16_t*)S->feature, xf,
+                       n_acc, best, d, M->feature_window, nc, P);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_model_slice_len, dim3((nb + 63) / 64), dim3(64), 0, st, S->kv_len, n_acc, best, nb, nc, P,
+                       S->kv_cap);
+    return hipGetLastError();
+}
+
+}  // namespace hci

@@ -56,6 +56,35 @@ class Block(ctypes.Structure):
     _fields_ = [("x", _p), ("q", _p), ("k", _p), ("v", _p), ("f", _p), ("s", _p), ("y", _p), ("o", _p)]
 
 
+MIX_FIR, MIX_IIR, MIX_ATTN = 0, 1, 2
+
+
+class Mixer(ctypes.Structure):
+    _fields_ = [("kind", _i), ("taps_short", _i), ("taps_long", _i), ("poles", _i), ("norm", _p), ("w_in", _p),
+                ("w_out", _p), ("w_short", _p), ("w_long", _p), ("lambda_", _p), ("beta", _p), ("c", _p)]
+
+
+class Model(ctypes.Structure):
+    _fields_ = [("n_layers", _i), ("d", _i), ("heads", _i), ("head_dim", _i), ("feature_layer", _i),
+                ("feature_window", _i), ("eps", ctypes.c_float), ("layers", ctypes.POINTER(Mixer))]
+
+
+class LayerState(ctypes.Structure):
+    _fields_ = [("short_win", _p), ("long_win", _p), ("iir", _p), ("k_cache", _p), ("v_cache", _p)]
+
+
+class ModelState(ctypes.Structure):
+    _fields_ = [("kv_cap", _i), ("kv_len", _p), ("feature", _p), ("layers", ctypes.POINTER(LayerState))]
+
+
+class LayerBlock(ctypes.Structure):
+    _fields_ = [("z", _p), ("u", _p), ("s", _p)]
+
+
+class ModelBlock(ctypes.Structure):
+    _fields_ = [("x", _p), ("layers", ctypes.POINTER(LayerBlock))]
+
+
 EXPORTS = {
     "hci_status_string": (ctypes.c_char_p, [_i]),
     "hci_version": (_i, []),
@@ -69,6 +98,15 @@ EXPORTS = {
                              _i, _i, _i, _i, _p, _p, _p]),
     "hci_prefill_workspace_bytes": (_sz, [ctypes.POINTER(Layer), _i, _i, _i]),
     "hci_prefill": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p]),
+    "hci_linear_packed_elems": (_sz, [_i, _i]),
+    "hci_linear_pack": (_i, [_i, _i, _p, _p, _p]),
+    "hci_linear": (_i, [_i, _i, _i, _p, _p, _p, _p, _i, _p]),
+    "hci_rmsnorm": (_i, [_i, _i, _p, _p, ctypes.c_float, _p, _p]),
+    "hci_model_workspace_bytes": (_sz, [ctypes.POINTER(Model), _i, _i, _i, _i]),
+    "hci_model_verify": (_i, [ctypes.POINTER(Model), ctypes.POINTER(ModelState), ctypes.POINTER(ModelBlock),
+                              _i, _i, _i, _i, _p, _sz, _p]),
+    "hci_model_slice": (_i, [ctypes.POINTER(Model), ctypes.POINTER(ModelState), ctypes.POINTER(ModelBlock),
+                             _i, _i, _i, _i, _p, _p, _p]),
     "hci_kv_cache_elems": (_sz, [ctypes.POINTER(Layer), _i, _i]),
     "hci_kv_write": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), _i, _i, _i, _i, _p, _p, _p]),
     "hci_kv_read": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), _i, _i, _i, _i, _p, _p, _p]),
@@ -193,6 +231,49 @@ def prefill(layer: Layer, state: State, nb: int, T: int, max_kv_len: int, x, k, 
                             _ptr(x, None, "x"), _ptr(k, None, "k"), _ptr(v, None, "v"), _ptr(y, None, "y"),
                             _ptr(ws, None, "ws"), ws.numel() * ws.element_size() if ws is not None else 0,
                             _stream(stream)), "hci_prefill")
+
+
+def linear_packed_elems(K: int, N: int) -> int:
+    return _lib.hci_linear_packed_elems(K, N)
+
+
+def linear_pack(w, w_packed, stream=None) -> None:
+    """w [K][N] bf16 -> w_packed (linear_packed_elems(K, N) bf16 elements)."""
+    K, N = w.shape
+    _check(_lib.hci_linear_pack(K, N, _ptr(w, torch.bfloat16, "w"), _ptr(w_packed, torch.bfloat16, "w_packed"),
+                                _stream(stream)), "hci_linear_pack")
+
+
+def linear(x, w_packed, N: int, y, residual=None, stream=None) -> None:
+    """y [M][N] = x [M][K] w (+ residual); y bf16 or fp32."""
+    M, K = x.shape
+    _check(_lib.hci_linear(M, K, N, _ptr(x, torch.bfloat16, "x"), _ptr(w_packed, torch.bfloat16, "w_packed"),
+                           _ptr(residual, torch.bfloat16, "residual"), _ptr(y, None, "y"),
+                           1 if y.dtype == torch.float32 else 0, _stream(stream)), "hci_linear")
+
+
+def rmsnorm(x, gamma, eps: float, y, stream=None) -> None:
+    M, K = x.shape
+    _check(_lib.hci_rmsnorm(M, K, _ptr(x, torch.bfloat16, "x"), _ptr(gamma, torch.float32, "gamma"), float(eps),
+                            _ptr(y, torch.bfloat16, "y"), _stream(stream)), "hci_rmsnorm")
+
+
+def model_workspace_bytes(model: Model, nb: int, nc: int, gamma: int, max_kv_len: int) -> int:
+    return _lib.hci_model_workspace_bytes(ctypes.byref(model), nb, nc, gamma, max_kv_len)
+
+
+def model_verify(model: Model, state: ModelState, block: ModelBlock, nb: int, nc: int, gamma: int, max_kv_len: int,
+                 ws, stream=None) -> None:
+    _check(_lib.hci_model_verify(ctypes.byref(model), ctypes.byref(state), ctypes.byref(block), nb, nc, gamma,
+                                 max_kv_len, _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
+           "hci_model_verify")
+
+
+def model_slice(model: Model, state: ModelState, block: ModelBlock, nb: int, nc: int, gamma: int, max_kv_len: int,
+                n_accepted, best_cand=None, stream=None) -> None:
+    _check(_lib.hci_model_slice(ctypes.byref(model), ctypes.byref(state), ctypes.byref(block), nb, nc, gamma,
+                                max_kv_len, _ptr(n_accepted, torch.int32, "n_accepted"),
+                                _ptr(best_cand, torch.int32, "best_cand"), _stream(stream)), "hci_model_slice")
 
 
 def kv_cache_elems(layer: Layer, nb: int, kv_cap: int) -> int:

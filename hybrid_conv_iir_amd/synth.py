@@ -29,7 +29,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Dict, List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 import torch
@@ -45,6 +45,7 @@ _S_KPRE, _S_VPRE = 30, 31
 _S_TOK, _S_ZT, _S_ZD, _S_GUMBEL, _S_U, _S_GEOM = 40, 41, 42, 43, 44, 45
 _S_NEEDLE = 50
 _S_PROMPT = 60
+_S_DENSE = 70
 
 
 @dataclasses.dataclass(frozen=True)
@@ -205,6 +206,13 @@ def prompt(cfg: Config, T: int, seed: int = 0, device: str = "cpu"):
     return out
 
 
+def dense(shape, std: float, tag: int, seed: int = 0, device: str = "cpu") -> torch.Tensor:
+    """A seeded N(0, std^2) bf16 tensor (weights, activations of the dense projections)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(((seed * 1000 + tag) * 100 + _S_DENSE) * 100003 + int(np.prod(shape)) % 100003)
+    return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
 def needle_positions(cfg: Config, b: int, count: int = 4, seed: int = 0) -> np.ndarray:
     """Prefix rows where a key is replaced by a scaled copy of a block query."""
     L = cfg.kv_lens[b]
@@ -345,3 +353,121 @@ def round_inputs(cfg: Config, anchor: np.ndarray, rnd: int = 0, seed: int = 0,
         lens = None
     return {"drafts": drafts, "target_logits": zt, "draft_logits": zd, "uniforms": u,
             "tokens": block_tokens(anchor, drafts), "planted_len": lens}
+
+
+# ---------------------------------------------------------------- full layer stacks
+
+@dataclasses.dataclass(frozen=True)
+class ModelConfig:
+    """A striped stack: per layer "fir" (explicit long filter), "iir" (modal) or "attn"."""
+    name: str
+    cfg_id: int
+    d: int
+    heads: int
+    head_dim: int
+    kinds: Tuple[str, ...]
+    taps_short: int
+    taps_long: Tuple[int, ...]          # per layer, used by "fir" layers
+    poles: int
+    feature_layer: int
+    feature_window: int
+    kv_lens: Tuple[int, ...]            # committed length per sequence
+    gamma: int
+    nc: int = 1
+    eps: float = 1e-6
+
+    @property
+    def nb(self) -> int:
+        return len(self.kv_lens)
+
+    @property
+    def P(self) -> int:
+        return self.gamma + 1
+
+    @property
+    def rows(self) -> int:
+        return self.nb * self.nc * self.P
+
+
+_STRIPE = ("fir", "fir", "iir", "attn")          # short-explicit, medium-regularised, long-implicit, attention
+MODEL_CONFIGS: Dict[str, ModelConfig] = {
+    "m4_small": ModelConfig("m4_small", 201, d=256, heads=2, head_dim=128, kinds=_STRIPE, taps_short=3,
+                            taps_long=(7, 128, 0, 0), poles=16, feature_layer=2, feature_window=64,
+                            kv_lens=(300, 37), gamma=6),
+    "m4_long": ModelConfig("m4_long", 202, d=4096, heads=32, head_dim=128, kinds=_STRIPE, taps_short=3,
+                           taps_long=(7, 128, 0, 0), poles=16, feature_layer=2, feature_window=64,
+                           kv_lens=(262144,), gamma=12),
+}
+
+
+def model_scaled(mc: ModelConfig, **kw) -> ModelConfig:
+    return dataclasses.replace(mc, **kw)
+
+
+def _mgen(mc: ModelConfig, tag: int, seed: int, device: str = "cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(((seed * 1000 + mc.cfg_id) * 1000 + tag) * 100003 + 17)
+    return g
+
+
+def make_model(mc: ModelConfig, seed: int = 0, device: str = "cpu") -> list:
+    """Per layer: g [d] fp32 ~ 1 + N(0, 0.1^2); w_in [d][3d], w_out [d][d] bf16 ~ N(0, 1/d);
+    w_short [Ts][3d] ~ N(0, 1/Ts); w_long [Tl][d] ~ N(0, 1/Tl); lam ~ U(0.5, 0.99); beta, c ~ N(0, 1/16)."""
+    d, out = mc.d, []
+    for l, kind in enumerate(mc.kinds):
+        t = 100 * (l + 1)
+        g = lambda k: _mgen(mc, t + k, seed, device)
+        p = {"kind": kind,
+             "g": 1.0 + 0.1 * torch.randn(d, generator=g(0), device=device),
+             "w_in": (torch.randn((d, 3 * d), generator=g(1), device=device) * d ** -0.5).to(torch.bfloat16),
+             "w_out": (torch.randn((d, d), generator=g(2), device=device) * d ** -0.5).to(torch.bfloat16)}
+        if kind != "attn":
+            Ts = mc.taps_short
+            p["w_short"] = torch.randn((Ts, 3 * d), generator=g(3), device=device) * Ts ** -0.5
+        if kind == "fir":
+            Tl = mc.taps_long[l]
+            p["w_long"] = torch.randn((Tl, d), generator=g(4), device=device) * Tl ** -0.5
+        if kind == "iir":
+            N = mc.poles
+            p["lam"] = 0.5 + 0.49 * torch.rand((d, N), generator=g(5), device=device)
+            p["beta"] = 0.25 * torch.randn((d, N), generator=g(6), device=device)
+            p["c"] = 0.25 * torch.randn((d, N), generator=g(7), device=device)
+        out.append(p)
+    return out
+
+
+def make_model_state(mc: ModelConfig, seed: int = 0, device: str = "cpu") -> dict:
+    """Committed state: windows N(0,1), IIR N(0, 1/4), feature window and KV prefixes N(0,1) bf16.
+
+    KV prefixes are [nb][H][L_b][Dh] per attention layer (a list per sequence)."""
+    d, nb = mc.d, mc.nb
+    layers = []
+    for l, kind in enumerate(mc.kinds):
+        t = 100 * (l + 1) + 50
+        g = lambda k: _mgen(mc, t + k, seed, device)
+        if kind == "attn":
+            ks, vs = [], []
+            for b, L in enumerate(mc.kv_lens):
+                ks.append(torch.randn((mc.heads, L, mc.head_dim), generator=g(10 + 2 * b), device=device)
+                          .to(torch.bfloat16))
+                vs.append(torch.randn((mc.heads, L, mc.head_dim), generator=g(11 + 2 * b), device=device)
+                          .to(torch.bfloat16))
+            layers.append({"k": ks, "v": vs})
+            continue
+        st = {"short_win": torch.randn((nb, mc.taps_short - 1, 3 * d), generator=g(0), device=device)}
+        if kind == "fir":
+            st["long_win"] = torch.randn((nb, mc.taps_long[l] - 1, d), generator=g(1), device=device)
+        else:
+            st["iir"] = 0.5 * torch.randn((nb, d, mc.poles), generator=g(2), device=device)
+        layers.append(st)
+    feat = torch.randn((nb, mc.feature_window, d), generator=_mgen(mc, 99, seed, device), device=device)
+    return {"layers": layers, "feature": feat.to(torch.bfloat16)}
+
+
+def model_block_input(mc: ModelConfig, rnd: int = 0, seed: int = 0, device: str = "cpu") -> torch.Tensor:
+    """x rows of the verified block [nb * nc * P][d] bf16 ~ N(0, 1); the candidates of a sequence share
+    row 0 (the anchor)."""
+    g = _mgen(mc, 900 + rnd, seed, device)
+    x = torch.randn((mc.nb, mc.nc, mc.P, mc.d), generator=g, device=device)
+    x[:, :, 0] = x[:, :1, 0]
+    return x.to(torch.bfloat16).reshape(mc.rows, mc.d)

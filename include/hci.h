@@ -261,6 +261,132 @@ int hci_prefill(const hci_layer* L, const hci_state* S, int nb, int T, int max_k
                 const void* x, const void* k, const void* v, void* y,
                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------ dense projections */
+
+/* The projections around the mixers of a full hybrid layer (input / output
+ * projections of the Hyena and attention blocks; StripedHyena2-style layers
+ * as described by the EvSpark digest, Figure 1(a)).  The weight W [K][N]
+ * (y = x W) is packed once, in matrix-core operand order: tiles of 32 (K) x
+ * 16 (N), the K/32 tiles of each 16-column strip consecutive, and inside a
+ * tile element [g<4][n<16][e<8] = W[32 kt + 8 g + e][16 nt + n].
+ * Limits: K % 32 == 0, N % 16 == 0, K, N <= 65536 x 16; bf16 data. */
+size_t hci_linear_packed_elems(int K, int N);          /* 0 if K, N unsupported */
+
+/* w [K][N] bf16 row-major -> w_packed (hci_linear_packed_elems bf16 elements). */
+int hci_linear_pack(int K, int N, const void* w, void* w_packed, hipStream_t stream);
+
+/* y [M][N] = x [M][K] w (+ residual [M][N]), bf16 inputs, fp32 accumulation;
+ * y is bf16 (round to nearest even) or fp32 (out_f32 != 0).  residual may be
+ * NULL (bf16 when given).  x, w_packed, residual and y are 16-byte aligned.
+ * Every weight byte is read once per call; sums over K run in a fixed order. */
+int hci_linear(int M, int K, int N, const void* x, const void* w_packed, const void* residual, void* y,
+               int out_f32, hipStream_t stream);
+
+/* y [M][K] = bf16( x * gamma / sqrt(mean_k(x^2) + eps) ) per row; x, y bf16,
+ * gamma fp32 [K]. */
+int hci_rmsnorm(int M, int K, const void* x, const float* gamma, float eps, void* y, hipStream_t stream);
+
+/* ------------------------------------------------------- full layer stack */
+
+/* A stack of full hybrid layers around the mixers above: the StripedHyena2
+ * target of the EvSpark digest (Synopsis, Figure 1(a)) interleaves Hyena
+ * layers (short-explicit and medium-regularised explicit filters, long
+ * implicit modal filters) with attention, and each state class of Figure
+ * 1(d) then lives in its own layer.  The pages print no layer equations;
+ * the plain reading implemented here, per layer on the residual stream x:
+ *   a = bf16( RMSNorm(x) * g )
+ *   Hyena (HCI_MIX_FIR / HCI_MIX_IIR):
+ *     z = a W_in (fp32), three streams z_q, z_k, z_v of d channels;
+ *     zhat = short depthwise FIR (Ts taps) of each of the 3d channels;
+ *     u = zhat_k * zhat_v;
+ *     h = explicit FIR of Tl taps over u (HCI_MIX_FIR) or the modal IIR
+ *         s_i = lambda s_{i-1} + beta u_i, h_i = sum_n c s_i (HCI_MIX_IIR);
+ *     y = bf16( zhat_q * h )
+ *   attention (HCI_MIX_ATTN): (q, k, v) = bf16( a W_in ), H heads of Dh,
+ *     y = causal block attention over the layer's KV cache (as hci_verify_block)
+ *   x <- bf16( x + y W_out )
+ * The feature buffer (the drafter's window of target states, Figure 1(b);
+ * it commits the same consumed prefix, Figure 1(d)) holds the residual
+ * stream after layer feature_layer for the last feature_window positions.
+ * Limits: d % 32 == 0, d = H * Dh, Dh in {64, 128}, Ts <= 8, Tl <= 256,
+ * N <= 16, nc * P <= 64, nb * nc * P <= 65535. */
+#define HCI_MIX_FIR  0
+#define HCI_MIX_IIR  1
+#define HCI_MIX_ATTN 2
+
+typedef struct hci_mixer {
+    int kind;                      /* HCI_MIX_* */
+    int taps_short, taps_long, poles;
+    const float* norm;             /* [d] RMSNorm gain g */
+    const void* w_in;              /* packed (hci_linear_pack) bf16 [d][3d] */
+    const void* w_out;             /* packed bf16 [d][d] */
+    const float* w_short;          /* [Ts][3d] (Hyena) */
+    const float* w_long;           /* [Tl][d]  (HCI_MIX_FIR) */
+    const float* lambda;           /* [d][N]   (HCI_MIX_IIR) */
+    const float* beta;
+    const float* c;
+} hci_mixer;
+
+typedef struct hci_model {
+    int n_layers, d, heads, head_dim;
+    int feature_layer, feature_window;
+    float eps;                     /* RMSNorm epsilon */
+    const hci_mixer* layers;       /* host array of n_layers */
+} hci_model;
+
+/* Committed state of one layer for nb sequences (all fp32 except the caches):
+ *   short_win [nb][Ts-1][3d]  last Ts-1 rows of z, oldest first (Hyena)
+ *   long_win  [nb][Tl-1][d]   last Tl-1 values of u (HCI_MIX_FIR)
+ *   iir       [nb][d][N]      (HCI_MIX_IIR)
+ *   k_cache, v_cache          tiled bf16 caches as in hci_state (HCI_MIX_ATTN) */
+typedef struct hci_layer_state {
+    float* short_win;
+    float* long_win;
+    float* iir;
+    void* k_cache;
+    void* v_cache;
+} hci_layer_state;
+
+typedef struct hci_model_state {
+    int kv_cap;
+    int32_t* kv_len;               /* [nb], shared by every attention layer */
+    void* feature;                 /* [nb][feature_window][d] bf16, oldest first */
+    const hci_layer_state* layers; /* host array of n_layers */
+} hci_model_state;
+
+/* Block tensors of one verify, retained for the slice (rows = nb * nc * P,
+ * row (b, c, i) at (b * nc + c) * P + i):
+ *   x [n_layers+1][rows][d] bf16: x[0] is the block input (caller-filled),
+ *     x[l+1] the residual stream after layer l (OUT); x[n_layers] is the output
+ *   per layer: z [3][rows][d] (fp32 for Hyena, bf16 for attention), u [rows][d]
+ *     fp32 (HCI_MIX_FIR), s [rows][d][N] fp32 (HCI_MIX_IIR). */
+typedef struct hci_layer_block {
+    void* z;
+    float* u;
+    float* s;
+} hci_layer_block;
+
+typedef struct hci_model_block {
+    void* x;
+    const hci_layer_block* layers; /* host array of n_layers */
+} hci_model_block;
+
+size_t hci_model_workspace_bytes(const hci_model* M, int nb, int nc, int gamma, int max_kv_len);
+
+/* One block forward through every layer from the committed state (state is
+ * only read).  Same block conventions as hci_verify_block. */
+int hci_model_verify(const hci_model* M, const hci_model_state* S, const hci_model_block* blk,
+                     int nb, int nc, int gamma, int max_kv_len, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Commit rows 0..k of candidate c* of every sequence in every layer (EvSpark
+ * digest, Figure 1(d), layer by layer): Hyena windows <- their last rows,
+ * IIR state <- s_k, attention rows appended at kv_len, feature buffer <- its
+ * last rows, then kv_len += k + 1.  k = n_accepted[b][c*], c* = best_cand[b]
+ * (NULL when nc == 1), read on the device. */
+int hci_model_slice(const hci_model* M, const hci_model_state* S, const hci_model_block* blk,
+                    int nb, int nc, int gamma, int max_kv_len,
+                    const int32_t* n_accepted, const int32_t* best_cand, hipStream_t stream);
+
 /* -------------------------------------------------------------- KV access */
 
 /* Elements (not bytes) of ONE of k_cache / v_cache for nb sequences. */

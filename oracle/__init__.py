@@ -28,6 +28,12 @@ Pinning (see tests/test_oracle_*.py):
   * slicing: the Figure 1(d) worked example; block+slice equals sequential steps.
   * prefill: equals the prompt's sequential single-position steps; the long
     FIR equals the plain FIR; the IIR scan equals the state-keeping scan.
+  * linear / rmsnorm: a pure-Python triple loop on small shapes, permutation
+    and identity weights; RMS of the output = 1 with unit gains, scale
+    invariance of the input.
+  * model stack: block forward + slice at k equals k+1 one-row steps for
+    every k (rounding off, fp64), each sublayer equals the pinned single-layer
+    pieces; bf16 rounding equals torch's conversion on fp32-exact values.
   * multi-candidate selection (largest accepted count, lowest index on ties):
     parity unpinned -- the pages give no rule for choosing among candidates.
   * recursive multi-candidate acceptance: reduces to the one-candidate rule;
@@ -40,9 +46,11 @@ from .layer import (depthwise_fir, modal_iir, block_attention, verify_block,
 from .acceptance import greedy_accept, rejection_accept, recursive_accept, accept_candidates
 from .slicing import slice_state, sequential_steps
 from .prefill import depthwise_fir_long, iir_scan, prefill_state
+from .linear import linear, rmsnorm
+from . import model
 
 __all__ = [
     "depthwise_fir", "modal_iir", "block_attention", "verify_block", "as_f64",
     "Layer", "SeqState", "greedy_accept", "rejection_accept", "recursive_accept", "accept_candidates",
-    "slice_state", "sequential_steps", "depthwise_fir_long", "iir_scan", "prefill_state",
+    "slice_state", "sequential_steps", "depthwise_fir_long", "iir_scan", "prefill_state", "linear", "rmsnorm",
 ]
