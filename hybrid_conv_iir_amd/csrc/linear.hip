@@ -139,24 +139,55 @@ __global__ void k_linear_pack(const uint16_t* __restrict__ w, uint16_t* __restri
     }
 }
 
-// y = x * g / sqrt(mean(x^2) + eps) per row, rounded to bf16; one workgroup per row
-__global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t* __restrict__ x, const float* __restrict__ gamma,
-                                                 float eps, uint16_t* __restrict__ y, int K)
+// y = x * g / sqrt(mean(x^2) + eps) per row, rounded to bf16; one workgroup per row.  With
+// K % 8 == 0 every thread holds 8 consecutive values from one 16-byte load and the row is read
+// once; the sum of squares is a fixed butterfly per wave, then the waves in order.
+template <bool VEC>
+__global__ __launch_bounds__(1024) void k_rmsnorm(const uint16_t* __restrict__ x, const float* __restrict__ gamma,
+                                                  float eps, uint16_t* __restrict__ y, int K)
 {
-    __shared__ float part[4];
+    __shared__ float part[16];
     const uint16_t* xr = x + (size_t)blockIdx.x * K;
+    uint16_t* yr = y + (size_t)blockIdx.x * K;
+    const int nw = blockDim.x >> 6;
+    float v[8];
     float s = 0.f;
-    for (int k = threadIdx.x; k < K; k += blockDim.x) {
-        const float v = bf2f(xr[k]);
-        s = fmaf(v, v, s);
+    if (VEC) {
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+        const int k0 = 8 * threadIdx.x;
+        if (k0 < K) {
+            const u32x4 w = *(const u32x4*)(xr + k0);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = __uint_as_float(ws[i] << 16);
+                v[2 * i + 1] = __uint_as_float(ws[i] & 0xffff0000u);
+            }
+        }
+        for (int i = 0; i < 8; ++i) s = fmaf(v[i], v[i], s);
+    } else {
+        for (int k = threadIdx.x; k < K; k += blockDim.x) {
+            const float t = bf2f(xr[k]);
+            s = fmaf(t, t, s);
+        }
     }
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
     __syncthreads();
-    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    float tot = 0.f;
+    for (int w = 0; w < nw; ++w) tot += part[w];
     const float inv = 1.0f / sqrtf(tot / (float)K + eps);
-    for (int k = threadIdx.x; k < K; k += blockDim.x)
-        y[(size_t)blockIdx.x * K + k] = f2bf(bf2f(xr[k]) * inv * gamma[k]);
+    if (VEC) {
+        const int k0 = 8 * threadIdx.x;
+        if (k0 < K) {
+            uint32_t o[4];
+            for (int i = 0; i < 4; ++i)
+                o[i] = (uint32_t)f2bf(v[2 * i] * inv * gamma[k0 + 2 * i]) |
+                       ((uint32_t)f2bf(v[2 * i + 1] * inv * gamma[k0 + 2 * i + 1]) << 16);
+            *(u32x4*)(yr + k0) = u32x4{o[0], o[1], o[2], o[3]};
+        }
+    } else {
+        for (int k = threadIdx.x; k < K; k += blockDim.x) yr[k] = f2bf(bf2f(xr[k]) * inv * gamma[k]);
+    }
 }
 
 // Launch shape: CT column strips per workgroup and KW waves splitting K, sized so that the
@@ -227,7 +258,14 @@ hipError_t launch_linear_pack(int K, int N, const void* w, void* wp, hipStream_t
 
 hipError_t launch_rmsnorm(int M, int K, const void* x, const float* g, float eps, void* y, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, st, (const uint16_t*)x, g, eps, (uint16_t*)y, K);
+    const bool vec = K % 8 == 0 && K <= 8 * 1024 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)y % 16) == 0;
+    if (vec) {
+        const int threads = ((K / 8 + 63) / 64) * 64;
+        hipLaunchKernelGGL(k_rmsnorm<true>, dim3(M), dim3(threads), 0, st, (const uint16_t*)x, g, eps, (uint16_t*)y,
+                           K);
+    } else {
+        hipLaunchKernelGGL(k_rmsnorm<false>, dim3(M), dim3(256), 0, st, (const uint16_t*)x, g, eps, (uint16_t*)y, K);
+    }
     return hipGetLastError();
 }
 

@@ -13,10 +13,10 @@
 //   (attention)      the verify attention path (KV stream, causal block
 //                    part, fixed-order combine) with the conv role off
 //   k_linear         x' = bf16(x + y W_out)
-// Slicing: k_model_slice_hyena (both windows and the IIR state),
-// k_model_slice_kv (accepted K/V rows into the tiled cache),
-// k_model_slice_feature (the drafter's window of target states), then
-// k_model_slice_len (kv_len += k + 1, after every reader of kv_len).
+// Slicing: k_model_slice (one launch for every layer: both windows, the
+// IIR state, accepted K/V rows into the tiled cache, the drafter's window of
+// target states), then k_model_slice_len (kv_len += k + 1, after every
+// reader of kv_len).
 #include "hci_internal.h"
 
 namespace hci {
@@ -124,78 +124,94 @@ __device__ __forceinline__ int accepted_rows(const int32_t* n_acc, const int32_t
     return k + 1;
 }
 
-// new[r] = [old ; rows][nrow + r]: each thread owns one column and walks r upward, so every
-// read of old row nrow + r happens before that row is overwritten
-template <int KIND>
-__global__ __launch_bounds__(256) void k_model_slice_hyena(
-    float* __restrict__ short_win, float* __restrict__ long_win, float* __restrict__ iir,
-    const float* __restrict__ z, const float* __restrict__ u, const float* __restrict__ s,
-    const int32_t* __restrict__ n_acc, const int32_t* __restrict__ best, int d, int Ts, int Tl, int N, int nc,
-    int P)
+// All of a slice's copies in one launch: a table of jobs (windows, IIR states, K/V rows, the
+// feature buffer) for every layer; blockIdx.x walks the jobs' workgroup ranges, blockIdx.y is the
+// sequence.  Windows follow new[r] = [old ; accepted rows][nrow + r]: a workgroup owns 16 columns,
+// stages up to 128 rows of the result in LDS and writes them back; chunks go upward, and chunk
+// [r0, r0 + 128) only reads old rows at or above r0 + nrow, which no earlier chunk has written.
+constexpr int kJobMax = 24;
+constexpr int kWinRows = 128;
+enum { JOB_WIN_F32 = 0, JOB_WIN_BF16 = 1, JOB_COPY_F32 = 2, JOB_KV = 3 };
+
+struct SliceJob {
+    int type, wgs;
+    void* dst;                   // window / state / K cache of sequence 0
+    void* dst2;                  // V cache (JOB_KV)
+    const void* src;             // block rows (row 0 of the block)
+    long long dst_b;             // elements between sequences' windows / states
+    int W, ncols;                // window rows, columns
+    int seg, seg_stride_rows;    // source column t -> segment t / seg at t / seg * seg_stride_rows rows further
+};
+
+struct SliceJobs {
+    SliceJob job[kJobMax];
+    int njobs, nc, P, H, DH, kv_cap;
+    long long rows;              // nb * nc * P
+};
+
+__global__ __launch_bounds__(256) void k_model_slice(SliceJobs J, const int32_t* __restrict__ n_acc,
+                                                     const int32_t* __restrict__ best,
+                                                     const int32_t* __restrict__ kv_len)
 {
+    __shared__ float stage[kWinRows][kMxCG];
     const int b = blockIdx.y;
+    int wg = blockIdx.x, j = 0;
+    while (j < J.njobs && wg >= J.job[j].wgs) wg -= J.job[j++].wgs;
+    if (j >= J.njobs) return;
+    const SliceJob& jb = J.job[j];
     int cand;
-    const int nrow = accepted_rows(n_acc, best, b, nc, P, cand);
-    const size_t rows = (size_t)gridDim.y * nc * P;
-    const size_t row0 = ((size_t)b * nc + cand) * P;
-    const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    const int Ws = Ts - 1, Wl = Tl - 1;
-    if (t < 3 * d && Ws > 0) {
-        const int sidx = t / d, ch = t % d;
-        float* w = short_win + (size_t)b * Ws * 3 * d + t;
-        for (int r = 0; r < Ws; ++r) {
-            const int m = nrow + r;
-            w[(size_t)r * 3 * d] = m < Ws ? w[(size_t)m * 3 * d] : z[((size_t)sidx * rows + row0 + (m - Ws)) * d + ch];
-        }
-    }
-    if (KIND == HCI_MIX_FIR) {
-        if (t < d && Wl > 0) {
-            float* w = long_win + (size_t)b * Wl * d + t;
-            for (int r = 0; r < Wl; ++r) {
+    const int nrow = accepted_rows(n_acc, best, b, J.nc, J.P, cand);
+    const long long row0 = ((long long)b * J.nc + cand) * J.P;
+
+    if (jb.type == JOB_WIN_F32 || jb.type == JOB_WIN_BF16) {
+        const int cl = threadIdx.x % kMxCG, part = threadIdx.x / kMxCG;
+        const int t = wg * kMxCG + cl;
+        const bool live = t < jb.ncols;
+        const long long src_col = live ? (long long)(t / jb.seg) * jb.seg_stride_rows * jb.seg + t % jb.seg : 0;
+        const int sw = jb.seg;       // source row stride (one segment's width)
+        for (int r0 = 0; r0 < jb.W; r0 += kWinRows) {
+            const int r1 = min(jb.W, r0 + kWinRows);
+            for (int r = r0 + part; r < r1; r += 256 / kMxCG) {
                 const int m = nrow + r;
-                w[(size_t)r * d] = m < Wl ? w[(size_t)m * d] : u[(row0 + (m - Wl)) * d + t];
+                float v = 0.f;
+                if (live) {
+                    if (jb.type == JOB_WIN_F32) {
+                        const float* win = (const float*)jb.dst + b * jb.dst_b;
+                        v = m < jb.W ? win[(long long)m * jb.ncols + t]
+                                     : ((const float*)jb.src)[(row0 + m - jb.W) * sw + src_col];
+                    } else {
+                        const uint16_t* win = (const uint16_t*)jb.dst + b * jb.dst_b;
+                        v = bf2f(m < jb.W ? win[(long long)m * jb.ncols + t]
+                                          : ((const uint16_t*)jb.src)[(row0 + m - jb.W) * sw + src_col]);
+                    }
+                }
+                stage[r - r0][cl] = v;
             }
+            __syncthreads();
+            for (int r = r0 + part; r < r1; r += 256 / kMxCG) {
+                if (!live) continue;
+                if (jb.type == JOB_WIN_F32)
+                    ((float*)jb.dst + b * jb.dst_b)[(long long)r * jb.ncols + t] = stage[r - r0][cl];
+                else
+                    ((uint16_t*)jb.dst + b * jb.dst_b)[(long long)r * jb.ncols + t] = f2bf(stage[r - r0][cl]);
+            }
+            __syncthreads();
         }
-    } else if (t < d * N) {
-        iir[(size_t)b * d * N + t] = s[(row0 + nrow - 1) * d * N + t];
-    }
-}
-
-__global__ __launch_bounds__(256) void k_model_slice_kv(
-    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const uint16_t* __restrict__ z,
-    const int32_t* __restrict__ kv_len, const int32_t* __restrict__ n_acc, const int32_t* __restrict__ best,
-    int H, int DH, int kv_cap, int nc, int P)
-{
-    const int b = blockIdx.y;
-    int cand;
-    const int nrow = accepted_rows(n_acc, best, b, nc, P, cand);
-    const size_t rows = (size_t)gridDim.y * nc * P;
-    const size_t row0 = ((size_t)b * nc + cand) * P;
-    const int d = H * DH, L0 = kv_len[b];
-    const int e = blockIdx.x * blockDim.x + threadIdx.x;         // (i, h, dd)
-    if (e >= P * d) return;
-    const int i = e / d, hd = e % d, h = hd / DH, dd = hd % DH;
-    const int row = L0 + i;
-    if (i >= nrow || row < 0 || row >= kv_cap) return;
-    const size_t base = ((size_t)b * H + h) * (size_t)kv_cap * DH + (size_t)(row & ~(kTile - 1)) * DH;
-    kc[base + k_tile_offset(row & (kTile - 1), dd, DH)] = z[(rows + row0 + i) * d + hd];
-    vc[base + v_tile_offset(row & (kTile - 1), dd, DH)] = z[(2 * rows + row0 + i) * d + hd];
-}
-
-__global__ __launch_bounds__(256) void k_model_slice_feature(
-    uint16_t* __restrict__ feat, const uint16_t* __restrict__ xf, const int32_t* __restrict__ n_acc,
-    const int32_t* __restrict__ best, int d, int W, int nc, int P)
-{
-    const int b = blockIdx.y;
-    int cand;
-    const int nrow = accepted_rows(n_acc, best, b, nc, P, cand);
-    const size_t row0 = ((size_t)b * nc + cand) * P;
-    const int ch = blockIdx.x * blockDim.x + threadIdx.x;
-    if (ch >= d) return;
-    uint16_t* w = feat + (size_t)b * W * d + ch;
-    for (int r = 0; r < W; ++r) {
-        const int m = nrow + r;
-        w[(size_t)r * d] = m < W ? w[(size_t)m * d] : xf[(row0 + (m - W)) * d + ch];
+    } else if (jb.type == JOB_COPY_F32) {
+        const int e = wg * 256 + threadIdx.x;
+        if (e < jb.ncols)
+            ((float*)jb.dst + b * jb.dst_b)[e] = ((const float*)jb.src)[(row0 + nrow - 1) * jb.ncols + e];
+    } else {
+        const int d = J.H * J.DH;
+        const int e = wg * 256 + threadIdx.x;                      // (i, h, dd)
+        if (e >= J.P * d) return;
+        const int i = e / d, hd = e % d, h = hd / J.DH, dd = hd % J.DH;
+        const int row = kv_len[b] + i;
+        if (i >= nrow || row < 0 || row >= J.kv_cap) return;
+        const long long base = ((long long)b * J.H + h) * J.kv_cap * J.DH + (long long)(row & ~(kTile - 1)) * J.DH;
+        const uint16_t* z = (const uint16_t*)jb.src;
+        ((uint16_t*)jb.dst)[base + k_tile_offset(row & (kTile - 1), dd, J.DH)] = z[(J.rows + row0 + i) * d + hd];
+        ((uint16_t*)jb.dst2)[base + v_tile_offset(row & (kTile - 1), dd, J.DH)] = z[(2 * J.rows + row0 + i) * d + hd];
     }
 }
 
@@ -301,35 +317,72 @@ hipError_t launch_model_slice(const hci_model* M, const hci_model_state* S, cons
                               int nc, int P, const int32_t* n_acc, const int32_t* best, hipStream_t st)
 {
     const int d = M->d;
-    const size_t rows = (size_t)nb * nc * P;
+    const long long rows = (long long)nb * nc * P;
+    SliceJobs J{};
+    J.nc = nc;
+    J.P = P;
+    J.H = M->heads;
+    J.DH = M->head_dim;
+    J.kv_cap = S->kv_cap;
+    J.rows = rows;
+    auto win = [&](int type, void* dst, long long dst_b, const void* src, int W, int ncols, int seg, int seg_rows) {
+        SliceJob j{};
+        j.type = type;
+        j.wgs = (ncols + kMxCG - 1) / kMxCG;
+        j.dst = dst;
+        j.src = src;
+        j.dst_b = dst_b;
+        j.W = W;
+        j.ncols = ncols;
+        j.seg = seg;
+        j.seg_stride_rows = seg_rows;
+        J.job[J.njobs++] = j;
+    };
+    auto flush = [&]() -> hipError_t {
+        if (J.njobs == 0) return hipSuccess;
+        long long wgs = 0;
+        for (int i = 0; i < J.njobs; ++i) wgs += J.job[i].wgs;
+        hipLaunchKernelGGL(k_model_slice, dim3((unsigned)wgs, nb), dim3(256), 0, st, J, n_acc, best, S->kv_len);
+        J.njobs = 0;
+        return hipGetLastError();
+    };
+    hipError_t e;
     for (int l = 0; l < M->n_layers; ++l) {
+        if (J.njobs + 2 > kJobMax && (e = flush()) != hipSuccess) return e;
         const hci_mixer& mx = M->layers[l];
         const hci_layer_state& ls = S->layers[l];
         const hci_layer_block& lb = blk->layers[l];
         if (mx.kind == HCI_MIX_ATTN) {
-            const dim3 grid((unsigned)((P * (size_t)d + 255) / 256), nb);
-            hipLaunchKernelGGL(k_model_slice_kv, grid, dim3(256), 0, st, (uint16_t*)ls.k_cache, (uint16_t*)ls.v_cache,
-                               (const uint16_t*)lb.z, S->kv_len, n_acc, best, M->heads, M->head_dim, S->kv_cap, nc, P);
-        } else {
-            const int cols = mx.kind == HCI_MIX_FIR ? 3 * d : (3 * d > d * mx.poles ? 3 * d : d * mx.poles);
-            const dim3 grid((cols + 255) / 256, nb);
-            if (mx.kind == HCI_MIX_FIR)
-                hipLaunchKernelGGL(k_model_slice_hyena<HCI_MIX_FIR>, grid, dim3(256), 0, st, ls.short_win, ls.long_win,
-                                   ls.iir, (const float*)lb.z, lb.u, lb.s, n_acc, best, d, mx.taps_short,
-                                   mx.taps_long, mx.poles, nc, P);
-            else
-                hipLaunchKernelGGL(k_model_slice_hyena<HCI_MIX_IIR>, grid, dim3(256), 0, st, ls.short_win, ls.long_win,
-                                   ls.iir, (const float*)lb.z, lb.u, lb.s, n_acc, best, d, mx.taps_short, 1, mx.poles,
-                                   nc, P);
+            SliceJob j{};
+            j.type = JOB_KV;
+            j.wgs = (int)((P * (long long)d + 255) / 256);
+            j.dst = ls.k_cache;
+            j.dst2 = ls.v_cache;
+            j.src = lb.z;
+            J.job[J.njobs++] = j;
+            continue;
         }
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (mx.taps_short > 1)       // window columns [s d, (s+1) d) come from stream s of z
+            win(JOB_WIN_F32, ls.short_win, (long long)(mx.taps_short - 1) * 3 * d, lb.z, mx.taps_short - 1, 3 * d,
+                d, (int)rows);
+        if (mx.kind == HCI_MIX_FIR) {
+            if (mx.taps_long > 1)
+                win(JOB_WIN_F32, ls.long_win, (long long)(mx.taps_long - 1) * d, lb.u, mx.taps_long - 1, d, d, 0);
+        } else {
+            SliceJob j{};
+            j.type = JOB_COPY_F32;
+            j.ncols = d * mx.poles;
+            j.wgs = (j.ncols + 255) / 256;
+            j.dst = ls.iir;
+            j.dst_b = (long long)d * mx.poles;
+            j.src = lb.s;
+            J.job[J.njobs++] = j;
+        }
     }
+    if (J.njobs + 1 > kJobMax && (e = flush()) != hipSuccess) return e;
     const uint16_t* xf = (const uint16_t*)blk->x + (size_t)(M->feature_layer + 1) * rows * d;
-    hipLaunchKernelGGL(k_model_slice_feature, dim3((d + 255) / 256, nb), dim3(256), 0, st, (uint16_t*)S->feature, xf,
-                       n_acc, best, d, M->feature_window, nc, P);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    win(JOB_WIN_BF16, S->feature, (long long)M->feature_window * d, xf, M->feature_window, d, d, 0);
+    if ((e = flush()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_model_slice_len, dim3((nb + 63) / 64), dim3(64), 0, st, S->kv_len, n_acc, best, nb, nc, P,
                        S->kv_cap);
     return hipGetLastError();
