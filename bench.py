@@ -364,6 +364,63 @@ def bench_model(args, hip):
     print(json.dumps(out), flush=True)
 
 
+def bench_draft(args, hip):
+    """Drafting one block: the trunk pass and the serial Markov-biased sampling, eagerly and as a
+    replayed HIP graph (the whole draft is launch-bound: ~20 small launches)."""
+    import numpy as np
+    import torch
+    from hybrid_conv_iir_amd import drafter as ddr
+    from hybrid_conv_iir_amd import synth
+    dc = synth.DRAFTER_CONFIGS["d1k"]
+    nb, gamma = 1, 12
+    dd = ddr.DeviceDrafter(dc, synth.make_drafter(dc, 0, device="cuda"))
+    rd = synth.draft_round(dc, nb, gamma, 0, 0, device="cuda")
+    win, anchor, u = rd["window"], rd["anchor"].cuda(), rd["uniforms"].cuda()
+    out = dd.buffers(nb, gamma)
+
+    def timed(fn, stream):
+        sp = stream.cuda_stream
+        for _ in range(args.warmup):
+            fn()
+        evs = [_events(hip, 2) for _ in range(args.steps)]
+        for i in range(args.steps):
+            hip.hipEventRecord(evs[i][0], sp)
+            fn()
+            hip.hipEventRecord(evs[i][1], sp)
+        torch.cuda.synchronize()
+        return float(np.median([_ms(hip, e[0], e[1]) for e in evs]))
+
+    cur = torch.cuda.current_stream()
+    eager_ms = timed(lambda: dd.draft(win, anchor, u, 1.0, out), cur)
+    s = torch.cuda.Stream()
+    s.wait_stream(cur)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        dd.draft(win, anchor, u, 1.0, out, stream=s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            dd.draft(win, anchor, u, 1.0, out, stream=s)
+    cur.wait_stream(s)
+    graph_ms = timed(graph.replay, cur)
+    d, F, L = dc.d, dc.ffn, dc.layers
+    weights = 2.0 * (dc.d_target * d + L * (3 * d * d + d * d + 2 * d * F) + d * dc.vocab)
+    alg = weights + 2.0 * nb * dc.window * dc.d_target + 4.0 * dc.vocab * dc.vocab
+    gbs = alg / (graph_ms * 1e-3) / 1e9
+    out_json = {
+        "metric": "drafted blocks/sec (trunk + serial sampling, graph replay)",
+        "value": round(nb / (graph_ms * 1e-3), 1), "unit": "blocks/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(graph_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded weights and window; no trained drafter)",
+        "config": {"workload": f"drafter d={d}, {dc.heads}x{dc.head_dim} heads, ffn {F}, {L} layers, "
+                               f"window {dc.window} x {dc.d_target}, vocab {dc.vocab}, gamma={gamma}, nb={nb}"},
+        "eager_ms": round(eager_ms, 4), "graph_ms": round(graph_ms, 4),
+        "roofline": {"kernel": "hci_draft_logits + hci_draft_sample (launch-bound)", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(gbs / 8000.0, 4),
+                     "traffic": None, "alg_bytes_per_launch": alg},
+    }
+    print(json.dumps(out_json), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -373,7 +430,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-oracle sample (0 = all)")
     ap.add_argument("--cpu-reps", type=int, default=3, help="repetitions of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="verify", choices=["verify", "prefill", "linear", "model"],
+    ap.add_argument("--mode", default="verify", choices=["verify", "prefill", "linear", "model", "draft"],
                     help="verify: the verify->accept->slice step (default); prefill: prompt -> committed state; "
                          "linear: one dense projection of the verified block")
     ap.add_argument("--linear-shape", default="13,4096,12288", help="M,K,N for --mode linear")
@@ -409,6 +466,8 @@ def main():
         return bench_linear(args, hip)
     if args.mode == "model":
         return bench_model(args, hip)
+    if args.mode == "draft":
+        return bench_draft(args, hip)
     W, K = args.warmup, args.steps
     P = cfg.P
     kv_cap = (cfg.max_kv_len + (W + K + 2) * P + 31) // 32 * 32

@@ -430,6 +430,57 @@ __global__ __launch_bounds__(kAccT) void k_accept(
     if (threadIdx.x == 0 && best) best[b] = best_c;
 }
 
+// Serial drafting with the previous-token bias (EvSpark digest, Figure 1(b)): draft m draws from
+// softmax(l / T), l = z[m] + B[prev] in fp32, by the same inverse-CDF rule as the acceptance
+// draws; one workgroup per sequence, the gamma draws in order.
+__global__ __launch_bounds__(kAccT) void k_draft_sample(int gamma, int V, double T, const float* __restrict__ z,
+                                                        const float* __restrict__ markov,
+                                                        const int32_t* __restrict__ anchor,
+                                                        const double* __restrict__ uni, int32_t* __restrict__ drafts,
+                                                        float* __restrict__ dl, double* __restrict__ margin_out)
+{
+    __shared__ AccScratch sh;
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int prev = anchor[b];
+    prev = prev < 0 ? 0 : (prev >= V ? V - 1 : prev);
+    for (int m = 0; m < gamma; ++m) {
+        const size_t r = ((size_t)b * gamma + m) * V;
+        float* row = dl + r;
+        for (int j = threadIdx.x; j < V; j += kAccT) row[j] = z[r + j] + markov[(size_t)prev * V + j];
+        __syncthreads();
+        if (wv == 0) {
+            double mx, sum;
+            wave_row_stats(row, V, T, lane, mx, sum);
+            if (lane == 0) {
+                sh.st[0] = mx;
+                sh.st[1] = sum;
+            }
+        }
+        __syncthreads();
+        const double pm = sh.st[0], ps = sh.st[1];
+        auto weight = [&](int j) { return exp((double)row[j] / T - pm) / ps; };
+        int tok;
+        double mg;
+        draw_token(weight, V, uni[(size_t)b * gamma + m], sh, tok, mg);
+        if (threadIdx.x == 0) {
+            drafts[(size_t)b * gamma + m] = tok;
+            if (margin_out) margin_out[(size_t)b * gamma + m] = mg;
+        }
+        prev = tok;
+        __syncthreads();
+    }
+}
+
+hipError_t launch_draft_sample(int nb, int gamma, int V, float temperature, const float* z, const float* markov,
+                               const int32_t* anchor, const double* u, int32_t* drafts, float* dl, double* margin,
+                               hipStream_t st)
+{
+    hipLaunchKernelGGL(k_draft_sample, dim3(nb), dim3(kAccT), 0, st, gamma, V, (double)temperature, z, markov, anchor,
+                       u, drafts, dl, margin);
+    return hipGetLastError();
+}
+
 hipError_t launch_accept(int mode, int nb, int nc, int gamma, int V, float temperature,
                          const float* zt, const float* zd, const int32_t* drafts, const double* u,
                          int32_t* n_acc, int32_t* next, int32_t* best, double* margin, hipStream_t st)

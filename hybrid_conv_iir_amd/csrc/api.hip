@@ -315,6 +315,51 @@ int hci_model_slice(const hci_model* M, const hci_model_state* S, const hci_mode
     return HCI_OK;
 }
 
+static int check_drafter(const hci_drafter* D) {
+    if (!D || !D->layers || D->n_layers < 1 || D->n_layers > 64) return HCI_EINVAL;
+    if (D->d < 32 || D->d % 32 || D->head_dim != 128 || D->heads * D->head_dim != D->d) return HCI_EUNSUPPORTED;
+    if (D->d_target < 32 || D->d_target % 32 || D->ffn < 32 || D->ffn % 32 || D->vocab < 16 || D->vocab % 16)
+        return HCI_EUNSUPPORTED;
+    if (D->window < 1 || D->window > 64 || !(D->eps >= 0.f)) return HCI_EINVAL;
+    if (!D->w_proj || !D->emb || !D->emb_t || !D->mask || !D->g_f) return HCI_EINVAL;
+    if (!aligned(D->w_proj, 16) || !aligned(D->emb_t, 16)) return HCI_EINVAL;
+    for (int l = 0; l < D->n_layers; ++l) {
+        const hci_drafter_layer& L = D->layers[l];
+        if (!L.g1 || !L.g2 || !L.w_qkv || !L.w_o || !L.w_up || !L.w_down) return HCI_EINVAL;
+        if (!aligned(L.w_qkv, 16) || !aligned(L.w_o, 16) || !aligned(L.w_up, 16) || !aligned(L.w_down, 16))
+            return HCI_EINVAL;
+    }
+    return HCI_OK;
+}
+
+size_t hci_draft_workspace_bytes(const hci_drafter* D, int nb, int gamma) {
+    if (check_drafter(D) != HCI_OK || nb < 1 || gamma < 1 || gamma > 32) return 0;
+    return plan_draft(D, nb, gamma).bytes;
+}
+
+int hci_draft_logits(const hci_drafter* D, int nb, int gamma, const void* window, const int32_t* anchor,
+                     float* z, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_drafter(D);
+    if (rc) return rc;
+    if (nb < 1 || nb > 65535 || gamma < 1 || gamma > 32) return HCI_EINVAL;
+    if (!window || !anchor || !z || !aligned(window, 16) || !aligned(z, 16)) return HCI_EINVAL;
+    const DraftPlan p = plan_draft(D, nb, gamma);
+    if (p.attn_lds > kMaxLds) return HCI_EUNSUPPORTED;
+    if (!ws || ws_bytes < p.bytes || !aligned(ws, 256)) return HCI_EWORKSPACE;
+    return launch_draft_logits(D, nb, gamma, window, anchor, z, p, ws, stream) == hipSuccess ? HCI_OK : HCI_EDEVICE;
+}
+
+int hci_draft_sample(int nb, int gamma, int vocab, float temperature, const float* z, const float* markov,
+                     const int32_t* anchor, const double* uniforms, int32_t* drafts, float* draft_logits,
+                     double* margin, hipStream_t stream) {
+    if (nb < 1 || nb > 2147483647 || gamma < 1 || vocab < 1) return HCI_EINVAL;
+    if (vocab > 65536) return HCI_EUNSUPPORTED;
+    if (!(temperature > 0.f) || temperature == INFINITY) return HCI_EINVAL;
+    if (!z || !markov || !anchor || !uniforms || !drafts || !draft_logits) return HCI_EINVAL;
+    return launch_draft_sample(nb, gamma, vocab, temperature, z, markov, anchor, uniforms, drafts, draft_logits,
+                               margin, stream) == hipSuccess ? HCI_OK : HCI_EDEVICE;
+}
+
 int hci_probe_sink_words(void) { return probe_blocks(); }
 
 int hci_probe_read(const void* src, size_t bytes, float* sink, hipStream_t stream) {

@@ -143,8 +143,9 @@ struct LinearPlan {
     size_t lds;
 };
 LinearPlan plan_linear(int M, int K, int N);
+// act: 0 none, 1 SiLU (applied after the residual)
 hipError_t launch_linear(int M, int K, int N, int parts, const void* x, const void* wp, const void* res, void* y,
-                         bool out_f32, hipStream_t st);
+                         bool out_f32, hipStream_t st, int act = 0);
 hipError_t launch_linear_pack(int K, int N, const void* w, void* wp, hipStream_t st);
 hipError_t launch_rmsnorm(int M, int K, const void* x, const float* g, float eps, void* y, hipStream_t st);
 
@@ -161,6 +162,20 @@ hipError_t launch_model_verify(const hci_model* M, const hci_model_state* S, con
                                int nc, int P, const ModelPlan& plan, void* ws, hipStream_t st);
 hipError_t launch_model_slice(const hci_model* M, const hci_model_state* S, const hci_model_block* blk, int nb,
                               int nc, int P, const int32_t* n_acc, const int32_t* best, hipStream_t st);
+
+// drafter trunk and sampling
+struct DraftPlan {
+    size_t rows;                 // nb * (W + gamma)
+    size_t h_off, a_off, qkv_off, o_off, m_off, bytes;
+    size_t attn_lds;
+};
+size_t draft_attn_lds(int W, int gamma, int DH);
+DraftPlan plan_draft(const hci_drafter* D, int nb, int gamma);
+hipError_t launch_draft_logits(const hci_drafter* D, int nb, int gamma, const void* window, const int32_t* anchor,
+                               float* z, const DraftPlan& p, void* ws, hipStream_t st);
+hipError_t launch_draft_sample(int nb, int gamma, int V, float temperature, const float* z, const float* markov,
+                               const int32_t* anchor, const double* u, int32_t* drafts, float* dl, double* margin,
+                               hipStream_t st);
 
 hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t st);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t st);

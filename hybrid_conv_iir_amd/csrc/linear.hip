@@ -30,7 +30,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8_u(u32x4 v) {
 template <int CT, int MT, bool OUT_F32>
 __global__ __launch_bounds__(1024) void k_linear(const uint16_t* __restrict__ x, const u32x4* __restrict__ wp,
                                                  const uint16_t* __restrict__ res, void* __restrict__ y,
-                                                 int M, int K, int N, int kspw, int parts)
+                                                 int M, int K, int N, int kspw, int parts, int act)
 {
     extern __shared__ float red[];                 // [KW][CT][mts][64][4]
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, KW = blockDim.x >> 6;
@@ -121,6 +121,7 @@ __global__ __launch_bounds__(1024) void k_linear(const uint16_t* __restrict__ x,
         const int p = col / Np;
         const size_t o = ((size_t)p * M + row) * Np + (col - p * Np);     // [parts][M][N / parts]
         if (res) v += bf2f(res[o]);
+        if (act == 1) v = v / (1.0f + __expf(-v));                   // SiLU
         if (OUT_F32) ((float*)y)[o] = v;
         else ((uint16_t*)y)[o] = f2bf(v);
     }
@@ -216,7 +217,7 @@ LinearPlan plan_linear(int M, int K, int N) {
 
 template <int CT, int MT>
 static hipError_t launch_ct(const LinearPlan& p, int M, int K, int N, int parts, const void* x, const void* wp,
-                            const void* res, void* y, bool out_f32, hipStream_t st)
+                            const void* res, void* y, bool out_f32, int act, hipStream_t st)
 {
     const void* fn = out_f32 ? (const void*)k_linear<CT, MT, true> : (const void*)k_linear<CT, MT, false>;
     if (p.lds > 65536) {
@@ -226,19 +227,19 @@ static hipError_t launch_ct(const LinearPlan& p, int M, int K, int N, int parts,
     const dim3 grid(p.grid_x, p.grid_y), block(64 * p.kw);
     if (out_f32)
         hipLaunchKernelGGL((k_linear<CT, MT, true>), grid, block, p.lds, st, (const uint16_t*)x, (const u32x4*)wp,
-                           (const uint16_t*)res, y, M, K, N, p.kspw, parts);
+                           (const uint16_t*)res, y, M, K, N, p.kspw, parts, act);
     else
         hipLaunchKernelGGL((k_linear<CT, MT, false>), grid, block, p.lds, st, (const uint16_t*)x, (const u32x4*)wp,
-                           (const uint16_t*)res, y, M, K, N, p.kspw, parts);
+                           (const uint16_t*)res, y, M, K, N, p.kspw, parts, act);
     return hipGetLastError();
 }
 
 hipError_t launch_linear(int M, int K, int N, int parts, const void* x, const void* wp, const void* res, void* y,
-                         bool out_f32, hipStream_t st)
+                         bool out_f32, hipStream_t st, int act)
 {
     const LinearPlan p = plan_linear(M, K, N);
 #define HCI_LIN_CASE(CT_, MT_) \
-    if (p.ct == CT_ && p.mt == MT_) return launch_ct<CT_, MT_>(p, M, K, N, parts, x, wp, res, y, out_f32, st);
+    if (p.ct == CT_ && p.mt == MT_) return launch_ct<CT_, MT_>(p, M, K, N, parts, x, wp, res, y, out_f32, act, st);
     HCI_LIN_CASE(4, 1) HCI_LIN_CASE(4, 2)
     HCI_LIN_CASE(2, 1) HCI_LIN_CASE(2, 2) HCI_LIN_CASE(2, 4)
     HCI_LIN_CASE(1, 1) HCI_LIN_CASE(1, 2) HCI_LIN_CASE(1, 4)

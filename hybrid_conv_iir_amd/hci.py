@@ -85,6 +85,16 @@ class ModelBlock(ctypes.Structure):
     _fields_ = [("x", _p), ("layers", ctypes.POINTER(LayerBlock))]
 
 
+class DrafterLayer(ctypes.Structure):
+    _fields_ = [("g1", _p), ("w_qkv", _p), ("w_o", _p), ("g2", _p), ("w_up", _p), ("w_down", _p)]
+
+
+class Drafter(ctypes.Structure):
+    _fields_ = [("d_target", _i), ("d", _i), ("heads", _i), ("head_dim", _i), ("ffn", _i), ("vocab", _i),
+                ("window", _i), ("n_layers", _i), ("eps", ctypes.c_float), ("w_proj", _p), ("emb", _p),
+                ("emb_t", _p), ("mask", _p), ("g_f", _p), ("layers", ctypes.POINTER(DrafterLayer))]
+
+
 EXPORTS = {
     "hci_status_string": (ctypes.c_char_p, [_i]),
     "hci_version": (_i, []),
@@ -107,6 +117,9 @@ EXPORTS = {
                               _i, _i, _i, _i, _p, _sz, _p]),
     "hci_model_slice": (_i, [ctypes.POINTER(Model), ctypes.POINTER(ModelState), ctypes.POINTER(ModelBlock),
                              _i, _i, _i, _i, _p, _p, _p]),
+    "hci_draft_workspace_bytes": (_sz, [ctypes.POINTER(Drafter), _i, _i]),
+    "hci_draft_logits": (_i, [ctypes.POINTER(Drafter), _i, _i, _p, _p, _p, _p, _sz, _p]),
+    "hci_draft_sample": (_i, [_i, _i, _i, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p]),
     "hci_kv_cache_elems": (_sz, [ctypes.POINTER(Layer), _i, _i]),
     "hci_kv_write": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), _i, _i, _i, _i, _p, _p, _p]),
     "hci_kv_read": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), _i, _i, _i, _i, _p, _p, _p]),
@@ -274,6 +287,25 @@ def model_slice(model: Model, state: ModelState, block: ModelBlock, nb: int, nc:
     _check(_lib.hci_model_slice(ctypes.byref(model), ctypes.byref(state), ctypes.byref(block), nb, nc, gamma,
                                 max_kv_len, _ptr(n_accepted, torch.int32, "n_accepted"),
                                 _ptr(best_cand, torch.int32, "best_cand"), _stream(stream)), "hci_model_slice")
+
+
+def draft_workspace_bytes(drafter: Drafter, nb: int, gamma: int) -> int:
+    return _lib.hci_draft_workspace_bytes(ctypes.byref(drafter), nb, gamma)
+
+
+def draft_logits(drafter: Drafter, nb: int, gamma: int, window, anchor, z, ws, stream=None) -> None:
+    _check(_lib.hci_draft_logits(ctypes.byref(drafter), nb, gamma, _ptr(window, torch.bfloat16, "window"),
+                                 _ptr(anchor, torch.int32, "anchor"), _ptr(z, torch.float32, "z"), _ptr(ws, None, "ws"),
+                                 ws.numel() * ws.element_size(), _stream(stream)), "hci_draft_logits")
+
+
+def draft_sample(nb: int, gamma: int, vocab: int, temperature: float, z, markov, anchor, uniforms, drafts,
+                 draft_logits, margin=None, stream=None) -> None:
+    _check(_lib.hci_draft_sample(nb, gamma, vocab, float(temperature), _ptr(z, torch.float32, "z"),
+                                 _ptr(markov, torch.float32, "markov"), _ptr(anchor, torch.int32, "anchor"),
+                                 _ptr(uniforms, torch.float64, "uniforms"), _ptr(drafts, torch.int32, "drafts"),
+                                 _ptr(draft_logits, torch.float32, "draft_logits"),
+                                 _ptr(margin, torch.float64, "margin"), _stream(stream)), "hci_draft_sample")
 
 
 def kv_cache_elems(layer: Layer, nb: int, kv_cap: int) -> int:

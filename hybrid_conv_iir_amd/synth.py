@@ -471,3 +471,64 @@ def model_block_input(mc: ModelConfig, rnd: int = 0, seed: int = 0, device: str 
     x = torch.randn((mc.nb, mc.nc, mc.P, mc.d), generator=g, device=device)
     x[:, :, 0] = x[:, :1, 0]
     return x.to(torch.bfloat16).reshape(mc.rows, mc.d)
+
+
+# ---------------------------------------------------------------- drafter
+
+@dataclasses.dataclass(frozen=True)
+class DrafterConfig:
+    name: str
+    cfg_id: int
+    d_target: int
+    d: int
+    heads: int
+    ffn: int
+    vocab: int
+    window: int
+    layers: int = 2
+    eps: float = 1e-6
+
+    @property
+    def head_dim(self) -> int:
+        return self.d // self.heads
+
+
+DRAFTER_CONFIGS: Dict[str, DrafterConfig] = {
+    # width 1024 over a W = 64 window of 4096-wide target states, two layers
+    "d1k": DrafterConfig("d1k", 301, d_target=4096, d=1024, heads=8, ffn=4096, vocab=512, window=64),
+    "d_small": DrafterConfig("d_small", 302, d_target=512, d=256, heads=2, ffn=512, vocab=512, window=64),
+}
+
+
+def make_drafter(dc: DrafterConfig, seed: int = 0, device: str = "cpu") -> dict:
+    """Weights: projections bf16 ~ N(0, 1/fan_in); gains fp32 ~ 1 + N(0, 0.1^2); the tied embedding and
+    the mask embedding bf16 ~ N(0, 1); the Markov bias fp32 ~ N(0, 1)."""
+    g = lambda k: _mgen_d(dc, k, seed, device)
+    bf = lambda shape, std, k: (torch.randn(shape, generator=g(k), device=device) * std).to(torch.bfloat16)
+    d, F = dc.d, dc.ffn
+    out = {"w_proj": bf((dc.d_target, d), dc.d_target ** -0.5, 1), "emb": bf((dc.vocab, d), 1.0, 2),
+           "mask": bf((d,), 1.0, 3), "markov": torch.randn((dc.vocab, dc.vocab), generator=g(4), device=device),
+           "g_f": 1.0 + 0.1 * torch.randn(d, generator=g(5), device=device), "layers": []}
+    for l in range(dc.layers):
+        k = 10 * (l + 1)
+        out["layers"].append({"g1": 1.0 + 0.1 * torch.randn(d, generator=g(k), device=device),
+                              "w_qkv": bf((d, 3 * d), d ** -0.5, k + 1), "w_o": bf((d, d), d ** -0.5, k + 2),
+                              "g2": 1.0 + 0.1 * torch.randn(d, generator=g(k + 3), device=device),
+                              "w_up": bf((d, F), d ** -0.5, k + 4), "w_down": bf((F, d), F ** -0.5, k + 5)})
+    return out
+
+
+def _mgen_d(dc: DrafterConfig, tag: int, seed: int, device: str) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(((seed * 1000 + dc.cfg_id) * 1000 + tag) * 100003 + 29)
+    return g
+
+
+def draft_round(dc: DrafterConfig, nb: int, gamma: int, rnd: int = 0, seed: int = 0, device: str = "cpu") -> dict:
+    """A drafting round: window [nb][W][d_target] bf16 ~ N(0, 1), anchors, uniforms [nb][gamma] fp64."""
+    g = _mgen_d(dc, 500 + rnd, seed, device)
+    win = torch.randn((nb, dc.window, dc.d_target), generator=g, device=device).to(torch.bfloat16)
+    gc = _mgen_d(dc, 600 + rnd, seed, "cpu")
+    anchor = torch.randint(0, dc.vocab, (nb,), generator=gc, dtype=torch.int32)
+    u = torch.rand((nb, gamma), generator=gc, dtype=torch.float64)
+    return {"window": win, "anchor": anchor, "uniforms": u}

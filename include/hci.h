@@ -387,6 +387,63 @@ int hci_model_slice(const hci_model* M, const hci_model_state* S, const hci_mode
                     int nb, int nc, int gamma, int max_kv_len,
                     const int32_t* n_accepted, const int32_t* best_cand, hipStream_t stream);
 
+/* ----------------------------------------------------------------- drafter */
+
+/* The drafter of the EvSpark digest (Figure 1(b); Interpretation): a
+ * projected window of W target states (the feature buffer) forms the K/V
+ * prefix of each of two causal attention layers of width d; the anchor's
+ * embedding followed by gamma-1 mask embeddings gives all gamma draft logits
+ * in one trunk pass (input and output embeddings tied); a previous-token
+ * Markov bias then supports serial sampling.  The pages print no equations;
+ * the reading implemented:
+ *   hw = bf16(window W_proj);   block rows h = [E[anchor]; mask x (gamma-1)]
+ *   per layer: a = bf16(RMSNorm(h) g1); (q,k,v) = bf16(a W_qkv) for the block
+ *     rows and (k,v) of bf16(RMSNorm(hw) g1) W_qkv for the window rows; causal
+ *     block attention with the window as prefix -> o (bf16); h = bf16(h + o W_o);
+ *     h = bf16(h + bf16(SiLU(bf16(RMSNorm(h) g2) W_up)) W_down)
+ *   z = bf16(RMSNorm(h) g_f) E^T  (fp32)
+ * Sizes: d % 32 == 0, d = H * 128, d_target % 32 == 0, ffn % 32 == 0,
+ * vocab % 16 == 0, 1 <= window <= 64, 1 <= gamma <= 32. */
+typedef struct hci_drafter_layer {
+    const float* g1;               /* [d] */
+    const void* w_qkv;             /* packed bf16 [d][3d] */
+    const void* w_o;               /* packed bf16 [d][d] */
+    const float* g2;               /* [d] */
+    const void* w_up;              /* packed bf16 [d][ffn] */
+    const void* w_down;            /* packed bf16 [ffn][d] */
+} hci_drafter_layer;
+
+typedef struct hci_drafter {
+    int d_target, d, heads, head_dim, ffn, vocab, window, n_layers;
+    float eps;
+    const void* w_proj;            /* packed bf16 [d_target][d] */
+    const void* emb;               /* [vocab][d] bf16 row-major (input embedding) */
+    const void* emb_t;             /* packed bf16 [d][vocab] (the tied output embedding) */
+    const void* mask;              /* [d] bf16 */
+    const float* g_f;              /* [d] final RMSNorm gain */
+    const hci_drafter_layer* layers;   /* host array of n_layers */
+} hci_drafter;
+
+size_t hci_draft_workspace_bytes(const hci_drafter* D, int nb, int gamma);
+
+/* Trunk pass: z [nb][gamma][vocab] fp32 = the draft logits before the bias.
+ * window [nb][W][d_target] bf16 (e.g. the feature buffer of hci_model_state),
+ * anchor [nb] int32 (ids outside [0, vocab) are clamped). */
+int hci_draft_logits(const hci_drafter* D, int nb, int gamma, const void* window, const int32_t* anchor,
+                     float* z, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Serial sampling with the previous-token bias (prev = anchor, then each
+ * draft): draft m draws from softmax(l / T) with the fp32 logits
+ * l = z[m] + markov[prev][.] (markov [vocab][vocab] fp32), by inverse CDF
+ * with uniforms[b][m] under the acceptance rule's conventions (fp64
+ * probabilities; the smallest id whose running sum exceeds u x total).
+ * Writes drafts [nb][gamma] int32 and draft_logits [nb][gamma][vocab] = l,
+ * the distribution each draft was drawn from (what hci_accept needs as
+ * draft_logits); margin [nb][gamma] fp64 (or NULL) as in hci_accept. */
+int hci_draft_sample(int nb, int gamma, int vocab, float temperature, const float* z, const float* markov,
+                     const int32_t* anchor, const double* uniforms, int32_t* drafts, float* draft_logits,
+                     double* margin, hipStream_t stream);
+
 /* -------------------------------------------------------------- KV access */
 
 /* Elements (not bytes) of ONE of k_cache / v_cache for nb sequences. */

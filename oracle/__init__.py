@@ -34,6 +34,11 @@ Pinning (see tests/test_oracle_*.py):
   * model stack: block forward + slice at k equals k+1 one-row steps for
     every k (rounding off, fp64), each sublayer equals the pinned single-layer
     pieces; bf16 rounding equals torch's conversion on fp32-exact values.
+  * drafter: the sampled draft's law equals softmax((z + B[prev]) / T)
+    exactly, for the first draft and for the second given the first (decision
+    boundaries by bisection); the trunk is causal in the block rows and sees
+    every window row; its pieces are the pinned ones.  Architecture reading:
+    parity unpinned beyond these.
   * multi-candidate selection (largest accepted count, lowest index on ties):
     parity unpinned -- the pages give no rule for choosing among candidates.
   * recursive multi-candidate acceptance: reduces to the one-candidate rule;
@@ -48,6 +53,7 @@ from .slicing import slice_state, sequential_steps
 from .prefill import depthwise_fir_long, iir_scan, prefill_state
 from .linear import linear, rmsnorm
 from . import model
+from . import drafter
 
 __all__ = [
     "depthwise_fir", "modal_iir", "block_attention", "verify_block", "as_f64",
