@@ -432,43 +432,84 @@ __global__ __launch_bounds__(kAccT) void k_accept(
 
 // Serial drafting with the previous-token bias (EvSpark digest, Figure 1(b)): draft m draws from
 // softmax(l / T), l = z[m] + B[prev] in fp32, by the same inverse-CDF rule as the acceptance
-// draws; one workgroup per sequence, the gamma draws in order.
-__global__ __launch_bounds__(kAccT) void k_draft_sample(int gamma, int V, double T, const float* __restrict__ z,
-                                                        const float* __restrict__ markov,
-                                                        const int32_t* __restrict__ anchor,
-                                                        const double* __restrict__ uni, int32_t* __restrict__ drafts,
-                                                        float* __restrict__ dl, double* __restrict__ margin_out)
+// draws.  One wave per sequence and no barrier: each lane holds a contiguous run of ceil(V/64)
+// token ids in registers, the row maximum, the sum and the exclusive scan of the run totals are
+// butterflies / shuffles, and the lane whose run crosses u x total walks it.
+constexpr int kDsMaxPer = 64;              // V <= 4096 on this path
+
+template <int PER>                         // ids per lane, a power of two >= ceil(V / 64)
+__global__ __launch_bounds__(64) void k_draft_sample(int gamma, int V, double T, const float* __restrict__ z,
+                                                     const float* __restrict__ markov,
+                                                     const int32_t* __restrict__ anchor,
+                                                     const double* __restrict__ uni, int32_t* __restrict__ drafts,
+                                                     float* __restrict__ dl, double* __restrict__ margin_out)
 {
-    __shared__ AccScratch sh;
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int b = blockIdx.x, lane = threadIdx.x;
+    const int per = (V + 63) / 64;
+    const int j0 = min(lane * per, V), j1 = min(j0 + per, V), n = j1 - j0;
     int prev = anchor[b];
     prev = prev < 0 ? 0 : (prev >= V ? V - 1 : prev);
     for (int m = 0; m < gamma; ++m) {
         const size_t r = ((size_t)b * gamma + m) * V;
-        float* row = dl + r;
-        for (int j = threadIdx.x; j < V; j += kAccT) row[j] = z[r + j] + markov[(size_t)prev * V + j];
-        __syncthreads();
-        if (wv == 0) {
-            double mx, sum;
-            wave_row_stats(row, V, T, lane, mx, sum);
-            if (lane == 0) {
-                sh.st[0] = mx;
-                sh.st[1] = sum;
+        float l[PER];
+        double mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+            const int j = j0 + t;
+            l[t] = t < n ? z[r + j] + markov[(size_t)prev * V + j] : -INFINITY;
+            if (t < n) {
+                dl[r + j] = l[t];
+                mx = fmax(mx, (double)l[t] / T);
             }
         }
-        __syncthreads();
-        const double pm = sh.st[0], ps = sh.st[1];
-        auto weight = [&](int j) { return exp((double)row[j] / T - pm) / ps; };
-        int tok;
-        double mg;
-        draw_token(weight, V, uni[(size_t)b * gamma + m], sh, tok, mg);
-        if (threadIdx.x == 0) {
+        for (int off = 32; off >= 1; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
+        double e[PER];
+        double loc = 0.0;
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+            e[t] = t < n ? exp((double)l[t] / T - mx) : 0.0;
+            loc += e[t];
+        }
+        double sum = loc;
+        for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+        // probabilities p_j = exp(l_j / T - mx) / sum; running sums over ascending ids
+        double ploc = 0.0;
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+            e[t] = e[t] / sum;
+            ploc += e[t];
+        }
+        double incl = ploc;
+        for (int off = 1; off < 64; off <<= 1) {
+            const double o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        const double total = __shfl(incl, 63);
+        const double excl = incl - ploc;
+        const double target = uni[(size_t)b * gamma + m] * total;
+        int first = INT_MAX, lastpos = -1;
+        double dmin = INFINITY, run = excl;
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+            if (t < n) {
+                const double w = e[t];
+                run += w;
+                if (run > target && first == INT_MAX) first = j0 + t;
+                if (w > 0.0) lastpos = j0 + t;
+                dmin = fmin(dmin, fabs(run - target));
+            }
+        }
+        for (int off = 32; off >= 1; off >>= 1) {
+            first = min(first, __shfl_xor(first, off));
+            lastpos = max(lastpos, __shfl_xor(lastpos, off));
+            dmin = fmin(dmin, __shfl_xor(dmin, off));
+        }
+        const int tok = first != INT_MAX ? first : lastpos;
+        if (lane == 0) {
             drafts[(size_t)b * gamma + m] = tok;
-            if (margin_out) margin_out[(size_t)b * gamma + m] = mg;
+            if (margin_out) margin_out[(size_t)b * gamma + m] = dmin / total;
         }
         prev = tok;
-        __syncthreads();
     }
 }
 
@@ -476,8 +517,17 @@ hipError_t launch_draft_sample(int nb, int gamma, int V, float temperature, cons
                                const int32_t* anchor, const double* u, int32_t* drafts, float* dl, double* margin,
                                hipStream_t st)
 {
-    hipLaunchKernelGGL(k_draft_sample, dim3(nb), dim3(kAccT), 0, st, gamma, V, (double)temperature, z, markov, anchor,
-                       u, drafts, dl, margin);
+    if (V > 64 * kDsMaxPer) return hipErrorInvalidValue;
+    const int per = (V + 63) / 64;
+#define HCI_DS(PER_)                                                                                            \
+    if (per <= PER_) {                                                                                           \
+        hipLaunchKernelGGL(k_draft_sample<PER_>, dim3(nb), dim3(64), 0, st, gamma, V, (double)temperature, z,  \
+                           markov, anchor, u, drafts, dl, margin);                                               \
+        return hipGetLastError();                                                                                \
+    }
+    HCI_DS(1) HCI_DS(2) HCI_DS(4) HCI_DS(8) HCI_DS(16) HCI_DS(32) HCI_DS(64)
+#undef HCI_DS
+    return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

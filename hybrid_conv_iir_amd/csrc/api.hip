@@ -353,7 +353,7 @@ int hci_draft_sample(int nb, int gamma, int vocab, float temperature, const floa
                      const int32_t* anchor, const double* uniforms, int32_t* drafts, float* draft_logits,
                      double* margin, hipStream_t stream) {
     if (nb < 1 || nb > 2147483647 || gamma < 1 || vocab < 1) return HCI_EINVAL;
-    if (vocab > 65536) return HCI_EUNSUPPORTED;
+    if (vocab > 4096) return HCI_EUNSUPPORTED;
     if (!(temperature > 0.f) || temperature == INFINITY) return HCI_EINVAL;
     if (!z || !markov || !anchor || !uniforms || !drafts || !draft_logits) return HCI_EINVAL;
     return launch_draft_sample(nb, gamma, vocab, temperature, z, markov, anchor, uniforms, drafts, draft_logits,

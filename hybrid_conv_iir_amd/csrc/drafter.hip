@@ -8,8 +8,8 @@
 //   k_linear           hw = window W_proj            (into the window rows)
 //   k_draft_embed      block rows = E[anchor], mask, mask, ...
 //   per layer: k_rmsnorm (all rows), k_linear q/k/v (all rows, 3 streams),
-//     k_draft_attn (per sequence and head: scores over the window rows and
-//     the causal block rows in LDS, softmax, weighted values),
+//     k_draft_attn (one wave per query row, head and sequence: scores over
+//     the window rows and the causal block rows, softmax, weighted values),
 //     k_linear o W_o + h, k_rmsnorm, k_linear SiLU(a W_up), k_linear m W_down + h
 //   k_rmsnorm + k_linear  z = hf E^T (fp32)
 #include "hci_internal.h"
@@ -29,68 +29,80 @@ __global__ void k_draft_embed(uint16_t* __restrict__ h, const uint16_t* __restri
 }
 
 size_t draft_attn_lds(int W, int gamma, int DH) {
-    const int nk = W + gamma;
-    return (size_t)2 * nk * DH * 2 + (size_t)gamma * DH * 2 + (size_t)gamma * nk * 4;
+    (void)DH;
+    return (size_t)(W + gamma) * sizeof(float);
 }
 
-// one workgroup per (head, sequence); qkv = [3][rows_all][d] bf16
-__global__ __launch_bounds__(256) void k_draft_attn(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ o,
-                                                    int nb, int W, int gamma, int H, int DH, float scale)
+// one wave per (query row, head, sequence); qkv = [3][rows_all][d] bf16, Dh = 128.  Lanes own
+// keys (lane, lane + 64, ...) for the scores and two value columns each for the output.
+__global__ __launch_bounds__(64) void k_draft_attn(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ o,
+                                                   int nb, int W, int gamma, int H, int DH, float scale)
 {
-    extern __shared__ char smem[];
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int d = H * DH, nk = W + gamma;
+    extern __shared__ float pr[];                         // [W + gamma] probabilities
+    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const int d = H * DH, nk = W + i + 1;                  // the window and block keys 0..i
     const size_t rows = (size_t)nb * (W + gamma);
-    uint16_t* ks = (uint16_t*)smem;                        // [nk][DH]
-    uint16_t* vs = ks + (size_t)nk * DH;                   // [nk][DH]
-    uint16_t* qs = vs + (size_t)nk * DH;                   // [gamma][DH]
-    float* S = (float*)(qs + (size_t)gamma * DH);          // [gamma][nk]
-    const uint16_t* kbase = qkv + rows * d;
-    const uint16_t* vbase = qkv + 2 * rows * d;
-    for (int e = threadIdx.x; e < nk * DH; e += blockDim.x) {
-        const int j = e / DH, dd = e % DH;
+    const uint16_t* qrow = qkv + ((size_t)nb * W + (size_t)b * gamma + i) * d + h * DH;
+    float q[128];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const u32x4 v = *(const u32x4*)(qrow + 8 * c);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            q[8 * c + 2 * t] = __uint_as_float(w[t] << 16);
+            q[8 * c + 2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
+        }
+    }
+    float mloc = -INFINITY;
+    float sc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int j = lane + 64 * u;
+        sc[u] = -INFINITY;
+        if (j < nk) {
+            const size_t row = j < W ? (size_t)b * W + j : (size_t)nb * W + (size_t)b * gamma + (j - W);
+            const uint16_t* krow = qkv + (rows + row) * d + h * DH;
+            float s = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const u32x4 v = *(const u32x4*)(krow + 8 * c);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    s = fmaf(q[8 * c + 2 * t], __uint_as_float(w[t] << 16), s);
+                    s = fmaf(q[8 * c + 2 * t + 1], __uint_as_float(w[t] & 0xffff0000u), s);
+                }
+            }
+            sc[u] = s * scale;
+            mloc = fmaxf(mloc, sc[u]);
+        }
+    }
+    for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int j = lane + 64 * u;
+        const float p = j < nk ? __expf(sc[u] - mloc) : 0.f;
+        sc[u] = p;
+        sum += p;
+    }
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+        if (lane + 64 * u < nk) pr[lane + 64 * u] = sc[u] * inv;
+    __syncthreads();
+    float a0 = 0.f, a1 = 0.f;
+    for (int j = 0; j < nk; ++j) {
         const size_t row = j < W ? (size_t)b * W + j : (size_t)nb * W + (size_t)b * gamma + (j - W);
-        ks[e] = kbase[row * d + h * DH + dd];
-        vs[e] = vbase[row * d + h * DH + dd];
+        const uint32_t v2 = *(const uint32_t*)(qkv + (2 * rows + row) * d + h * DH + 2 * lane);
+        const float p = pr[j];
+        a0 = fmaf(p, __uint_as_float(v2 << 16), a0);
+        a1 = fmaf(p, __uint_as_float(v2 & 0xffff0000u), a1);
     }
-    for (int e = threadIdx.x; e < gamma * DH; e += blockDim.x) {
-        const int i = e / DH, dd = e % DH;
-        qs[e] = qkv[((size_t)nb * W + (size_t)b * gamma + i) * d + h * DH + dd];
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < gamma * nk; e += blockDim.x) {
-        const int i = e / nk, j = e % nk;
-        float s = -INFINITY;
-        if (j < W || j - W <= i) {
-            s = 0.f;
-            for (int dd = 0; dd < DH; ++dd) s = fmaf(bf2f(qs[i * DH + dd]), bf2f(ks[j * DH + dd]), s);
-            s *= scale;
-        }
-        S[e] = s;
-    }
-    __syncthreads();
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    for (int i = wv; i < gamma; i += nw) {
-        float m = -INFINITY;
-        for (int j = lane; j < nk; j += 64) m = fmaxf(m, S[i * nk + j]);
-        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-        float sum = 0.f;
-        for (int j = lane; j < nk; j += 64) {
-            const float p = __expf(S[i * nk + j] - m);
-            S[i * nk + j] = p;
-            sum += p;
-        }
-        for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-        const float inv = 1.0f / sum;
-        for (int j = lane; j < nk; j += 64) S[i * nk + j] *= inv;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < gamma * DH; e += blockDim.x) {
-        const int i = e / DH, dd = e % DH;
-        float acc = 0.f;
-        for (int j = 0; j < nk; ++j) acc = fmaf(S[i * nk + j], bf2f(vs[j * DH + dd]), acc);
-        o[((size_t)b * gamma + i) * d + h * DH + dd] = f2bf(acc);
-    }
+    const uint32_t packed = (uint32_t)f2bf(a0) | ((uint32_t)f2bf(a1) << 16);
+    *(uint32_t*)(o + ((size_t)b * gamma + i) * d + h * DH + 2 * lane) = packed;
 }
 
 DraftPlan plan_draft(const hci_drafter* D, int nb, int gamma) {
@@ -126,17 +138,13 @@ hipError_t launch_draft_logits(const hci_drafter* D, int nb, int gamma, const vo
     hipLaunchKernelGGL(k_draft_embed, dim3((unsigned)brows), dim3(256), 0, st, hb, (const uint16_t*)D->emb,
                        (const uint16_t*)D->mask, anchor, d, gamma, D->vocab);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (p.attn_lds > 65536 && (e = hipFuncSetAttribute((const void*)k_draft_attn,
-                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                        (int)p.attn_lds)) != hipSuccess)
-        return e;
     const float scale = 1.0f / sqrtf((float)D->head_dim);
     for (int l = 0; l < D->n_layers; ++l) {
         const hci_drafter_layer& L = D->layers[l];
         if ((e = launch_rmsnorm((int)rows, d, h, L.g1, D->eps, a, st)) != hipSuccess) return e;
         if ((e = launch_linear((int)rows, d, 3 * d, 3, a, L.w_qkv, nullptr, qkv, false, st)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k_draft_attn, dim3(D->heads, nb), dim3(256), p.attn_lds, st, qkv, o, nb, W, gamma, D->heads,
-                           D->head_dim, scale);
+        hipLaunchKernelGGL(k_draft_attn, dim3(gamma, D->heads, nb), dim3(64), p.attn_lds, st, qkv, o, nb, W, gamma,
+                           D->heads, D->head_dim, scale);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_linear((int)brows, d, d, 1, o, L.w_o, hb, hb, false, st)) != hipSuccess) return e;
         if ((e = launch_rmsnorm((int)brows, d, hb, L.g2, D->eps, ab, st)) != hipSuccess) return e;

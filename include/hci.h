@@ -439,7 +439,8 @@ int hci_draft_logits(const hci_drafter* D, int nb, int gamma, const void* window
  * probabilities; the smallest id whose running sum exceeds u x total).
  * Writes drafts [nb][gamma] int32 and draft_logits [nb][gamma][vocab] = l,
  * the distribution each draft was drawn from (what hci_accept needs as
- * draft_logits); margin [nb][gamma] fp64 (or NULL) as in hci_accept. */
+ * draft_logits); margin [nb][gamma] fp64 (or NULL) as in hci_accept.
+ * Limits: 1 <= vocab <= 4096. */
 int hci_draft_sample(int nb, int gamma, int vocab, float temperature, const float* z, const float* markov,
                      const int32_t* anchor, const double* uniforms, int32_t* drafts, float* draft_logits,
                      double* margin, hipStream_t stream);
