@@ -14,6 +14,8 @@
 // in this order so the short ones overlap the long KV stream:
 //   conv   the conv/IIR scan of 16 channels (conv_iir_body.h)
 //   tail   the causal block part of one (sequence, candidate, head)
+// (with several 16-query tiles the prefix runs as its own kernel,
+// k_attn_prefix_shared, one query tile per wave over LDS-shared KV tiles)
 //   prefix one chunk of one (sequence, head): four waves, each streaming a
 //          contiguous run of 32-key tiles with non-temporal 16-byte loads
 //          (a contiguous kilobyte per wave-wide load, thanks to the tiled
@@ -369,6 +371,104 @@ __global__ __launch_bounds__(kRoleT) void k_verify_stream(StreamArgs A)
                          A.scale_log2, c, h, b, lds);
 }
 
+// ------------------------------------------- several query tiles per prefix
+//
+// With more than 16 queries per sequence (several candidates) every wave of a
+// prefix workgroup owns one 16-query tile and all four walk the same KV
+// tiles: each 32-key tile is read from HBM once per workgroup -- a quarter
+// by each wave, non-temporal, into one of two LDS buffers -- and every wave
+// takes the matrix-core operands from LDS in the order they were stored
+// (a contiguous kilobyte per fragment, no bank conflicts).  A wave keeps the
+// register state of a single query tile, so several workgroups fit a CU.
+// Two tiles' loads are in flight while the current one is consumed (two
+// register sets take turns); one barrier per tile separates the buffers.
+
+template <int DH>
+__global__ __launch_bounds__(kRoleT) void k_attn_prefix_shared(StreamArgs A, int nqt)
+{
+    constexpr int J = DH / 32, DT = DH / 16, KV4 = 4 * DH;
+    constexpr int PER = 2 * KV4 / kRoleT;             // uint4 per thread per tile (K then V)
+    __shared__ uint4 buf[2][2 * KV4];
+    const int id = blockIdx.x;
+    const int chunk = id % A.prefix_x, h = (id / A.prefix_x) % A.H, b = id / (A.prefix_x * A.H);
+    if (chunk >= A.n_chunks) return;
+    int L = A.kv_len[b];
+    L = L < 0 ? 0 : (L > A.kv_cap ? A.kv_cap : L);
+    const int tiles = (L + kTile - 1) / kTile;
+    const int t0 = chunk * A.chunk_tiles;
+    if (t0 >= tiles) return;                           // whole workgroup
+    const int t1 = min(t0 + A.chunk_tiles, tiles);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
+    const bool has_q = wave < nqt;
+
+    PrefixAcc<DH, 1> a;
+    {
+        const int qi = 16 * wave + n;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (has_q && qi < A.nq) v = *(const uint4*)(A.q + (((size_t)b * A.nq + qi) * A.H + h) * DH + 32 * j + 8 * g);
+            a.q[0][j] = as_bf16x8(v);
+        }
+        a.m[0] = -INFINITY;
+        a.l[0] = 0.f;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) a.o[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const size_t slab = ((size_t)b * A.H + h) * (size_t)(A.kv_cap / kTile) * KV4;
+    const uint4* kp = (const uint4*)A.kc + slab;
+    const uint4* vp = (const uint4*)A.vc + slab;
+    // two register sets take turns: while tile T is consumed from LDS, tile T+1 (issued one
+    // iteration earlier) and tile T+2 are in flight, then T+1 goes to the free LDS buffer
+    uint4 ra[PER], rb[PER];
+    auto fetch = [&](uint4* r, int T) {
+        const size_t base = (size_t)T * KV4;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + kRoleT * i;
+            r[i] = e < KV4 ? load_nt(kp + base + e) : load_nt(vp + base + (e - KV4));
+        }
+    };
+    auto stash = [&](const uint4* r, int slot) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) buf[slot][tid + kRoleT * i] = r[i];
+    };
+    auto consume = [&](int T) {
+        if (!has_q) return;
+        const int cur = (T - t0) & 1;
+        KvTile<DH> t;
+#pragma unroll
+        for (int i = 0; i < 2 * J; ++i) t.k[i] = buf[cur][i * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < DT; ++i) t.v[i] = buf[cur][KV4 + i * 64 + lane];
+        consume_tile<DH, 1>(a, t, T, L, g, A.scale_log2);
+    };
+    fetch(ra, t0);
+    stash(ra, 0);
+    if (t0 + 1 < t1) fetch(ra, t0 + 1);
+    __syncthreads();
+    for (int T = t0; T < t1; T += 2) {
+        if (T + 2 < t1) fetch(rb, T + 2);
+        consume(T);
+        if (T + 1 < t1) stash(ra, (T + 1 - t0) & 1);
+        __syncthreads();
+        if (T + 1 >= t1) break;
+        if (T + 3 < t1) fetch(ra, T + 3);
+        consume(T + 1);
+        if (T + 2 < t1) stash(rb, (T + 2 - t0) & 1);
+        __syncthreads();
+    }
+    if (!has_q) return;
+    const int qi = 16 * wave + n;
+    if (qi >= A.nq) return;
+    const size_t pbase = (((size_t)b * A.H + h) * A.slots + chunk) * A.nq;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+        *(float4*)(A.part_o + (pbase + qi) * DH + 16 * t + 4 * g) =
+            make_float4(a.o[t][0][0], a.o[t][0][1], a.o[t][0][2], a.o[t][0][3]);
+    if (g == 0) *(float2*)(A.part_ml + (pbase + qi) * 2) = make_float2(a.m[0], a.l[0]);
+}
+
 // -------------------------------------------------- stand-alone fp32 parts
 
 template <int ACT>
@@ -586,7 +686,9 @@ AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_k
     // flight, with at least 8 tiles per wave so that partials stay a small
     // fraction of the traffic.
     const long long total_tiles = (long long)tiles * nb * L->heads;
-    const long long target_wgs = (long long)num_cus * 4;
+    // several query tiles: a workgroup walks its whole chunk with all four waves, so
+    // twice as many (shorter) chunks keep the same number of tiles in flight
+    const long long target_wgs = (long long)num_cus * ((p.nq + 15) / 16 > 1 ? 8 : 4);
     long long ct = (total_tiles + target_wgs - 1) / (target_wgs > 0 ? target_wgs : 1);
     if (ct < 8 * kPrefixWaves) ct = 8 * kPrefixWaves;
     const long long min_ct = (tiles + kMaxChunks - 1) / kMaxChunks;   // combine holds <= kMaxChunks weights
@@ -673,7 +775,13 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
         const long long blocks = (long long)A.prefix_blocks + A.n_conv + A.n_tail;
         if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
         const size_t lds = stream_lds_bytes(L, nc, P);
-        if (blocks > 0) {
+        if (!fuse && A.prefix_blocks > 0) {
+            if (DH == 128)
+                hipLaunchKernelGGL(k_attn_prefix_shared<128>, dim3(A.prefix_blocks), dim3(kRoleT), 0, st, A, nqt);
+            else
+                hipLaunchKernelGGL(k_attn_prefix_shared<64>, dim3(A.prefix_blocks), dim3(kRoleT), 0, st, A, nqt);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        } else if (blocks > 0) {
             if (DH == 128) {
                 switch (nqt) {
                     case 1: e = launch_stream<128, 1>(A, (int)blocks, lds, st); break;
