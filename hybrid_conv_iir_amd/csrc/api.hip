@@ -95,6 +95,7 @@ static int verify_impl(const hci_layer* L, const hci_state* S, const hci_block* 
     if (conv_iir_lds_bytes(L->taps_outer, P) > kMaxLds || stream_lds_bytes(L, nc, P) > kMaxLds)
         return HCI_EUNSUPPORTED;
     const AttnPlan plan = plan_attention(L, nb, nc, gamma, max_kv_len, device_cu_count());
+    if (plan.items_cap < 0) return HCI_EUNSUPPORTED;
     if (plan.bytes > 0 && (!ws || ws_bytes < plan.bytes || !aligned(ws, 256))) return HCI_EWORKSPACE;
 
     if (launch_verify(L, S, blk, nb, nc, P, plan, ws, stream, ev) != hipSuccess) return HCI_EDEVICE;
@@ -294,6 +295,7 @@ int hci_model_verify(const hci_model* M, const hci_model_state* S, const hci_mod
     if (rc) return rc;
     const int P = gamma + 1;
     const ModelPlan plan = plan_model(M, nb, nc, gamma, max_kv_len, device_cu_count());
+    if (plan.has_attn && plan.attn.items_cap < 0) return HCI_EUNSUPPORTED;
     if (!ws || ws_bytes < plan.bytes || !aligned(ws, 256)) return HCI_EWORKSPACE;
     if (plan.has_attn) {
         const hci_layer L{M->d, 1, 1, 1, M->heads, M->head_dim, HCI_BF16, nullptr, nullptr, nullptr, nullptr, nullptr};

@@ -48,6 +48,60 @@ __device__ __forceinline__ bf16x8 ones_bf16x8() {
 
 constexpr int kPrefixWaves = 4;      // waves per workgroup; their partials merge in LDS
 
+// ------------------------------------------------------------ split-K plan
+//
+// The prefix lengths live on the device, so the split of the committed
+// prefixes into chunks is derived there, from kv_len, by every prefix
+// workgroup and by the combine alike.  Work items (sequence b, head h,
+// chunk c) are numbered consecutively, sequence-major:
+//   item = base_b + h * n_b + c,  n_b = ceil(tiles_b / ct),
+//   base_b = H * (n_0 + ... + n_{b-1}),
+// with ct = max(ct_min, ceil(H * sum_b tiles_b / target)) tiles per chunk.
+// Workgroup ids map one to one onto items and ids past the last item exit at
+// once: real work occupies consecutive ids whatever the lengths, and since the
+// dispatcher deals consecutive ids round-robin to the XCDs, every XCD gets an
+// even share of a ragged batch.  The number of items never exceeds
+// target + nb * H.  Partials: item i at index i; the block part of (b, h) at
+// index tail_base + b * H + h.
+
+// Committed length of sequence b as the attention reads it: kv_len clamped to
+// [0, lim], lim = min(kv_cap, max_kv_len), so that a length above the host's
+// bound can never yield more work items or chunks than the host planned for.
+__device__ __forceinline__ int prefix_len(const int32_t* kv_len, int b, int lim) {
+    const int L = kv_len[b];
+    return L < 0 ? 0 : (L > lim ? lim : L);
+}
+
+__device__ __forceinline__ int prefix_tiles(const int32_t* kv_len, int b, int lim) {
+    return (prefix_len(kv_len, b, lim) + kTile - 1) / kTile;
+}
+
+__device__ __forceinline__ int split_ct(const int32_t* kv_len, int nb, int H, int lim, int ct_min, int target) {
+    long long w = 0;
+    for (int b = 0; b < nb; ++b) w += prefix_tiles(kv_len, b, lim);
+    w *= H;
+    const long long ct = (w + target - 1) / target;
+    return ct > ct_min ? (int)ct : ct_min;
+}
+
+// Locate work item `id`; false past the last item.
+__device__ __forceinline__ bool split_item(const int32_t* kv_len, int nb, int H, int lim, int ct, int id,
+                                           int& b, int& h, int& chunk) {
+    int base = 0;
+    for (int bb = 0; bb < nb; ++bb) {
+        const int n = (prefix_tiles(kv_len, bb, lim) + ct - 1) / ct;
+        if (id < base + n * H) {
+            const int r = id - base;
+            b = bb;
+            h = r / n;
+            chunk = r - h * n;
+            return true;
+        }
+        base += n * H;
+    }
+    return false;
+}
+
 template <int DH, int NQT>
 __host__ __device__ constexpr size_t prefix_merge_floats() {
     // per merged wave: O^T accumulators (16*NQT queries x DH), running max, normaliser
@@ -151,12 +205,12 @@ __device__ __forceinline__ void consume_tile(PrefixAcc<DH, NQT>& a, KvTile<DH>& 
 
 
 // One prefix workgroup: chunk `chunk` of head h of sequence b, all nq queries.
-// Partials: part_o [nb][H][slots][nq][DH], part_ml [..][2], slot = chunk.
+// Partials: part_o [item][nq][DH], part_ml [item][nq][2].
 template <int DH, int NQT>
 __device__ __forceinline__ void prefix_block(
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int L,
     const uint16_t* __restrict__ q, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int H, int kv_cap, int nq, int chunk_tiles, int slots, float scale_log2,
+    int H, int kv_cap, int nq, int chunk_tiles, int item, float scale_log2,
     int chunk, int h, int b, float* merge)
 {
     constexpr int J = DH / 32;          // k-steps of the score product
@@ -220,7 +274,7 @@ __device__ __forceinline__ void prefix_block(
     __syncthreads();
     if (wave > 0) return;
 
-    const size_t pbase = (((size_t)b * H + h) * slots + chunk) * nq;
+    const size_t pbase = (size_t)item * nq;
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
         float M = a.m[nt];
@@ -257,7 +311,7 @@ __device__ __forceinline__ void prefix_block(
 //
 // One workgroup per (sequence, candidate, head): the P block queries attend
 // causally to the block's own keys (query i sees keys 0..i), in fp32.  The
-// result is one more partial softmax state, in slot `tail_slot`.
+// result is one more partial softmax state, at index tail_base + b * H + h.
 
 constexpr int kMaxP = 64;
 
@@ -271,7 +325,7 @@ template <int ACT>
 __device__ __forceinline__ void tail_block(
     const typename Act<ACT>::T* __restrict__ q, const typename Act<ACT>::T* __restrict__ kb,
     const typename Act<ACT>::T* __restrict__ vb, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int H, int DH, int P, int nq, int slots, int tail_slot, float scale_log2, int c, int h, int b, float* lds)
+    int H, int DH, int P, int nq, int tail_base, float scale_log2, int c, int h, int b, float* lds)
 {
     typedef typename Act<ACT>::T T;
     float* S = lds;                                   // [P][P + 1] scores, then weights
@@ -314,7 +368,7 @@ __device__ __forceinline__ void tail_block(
         lrow[i] = l;
     }
     __syncthreads();
-    const size_t pbase = (((size_t)b * H + h) * slots + tail_slot) * nq + (size_t)c * P;
+    const size_t pbase = ((size_t)tail_base + (size_t)b * H + h) * nq + (size_t)c * P;
     for (int e = tid; e < P * DH; e += nthr) {
         const int i = e / DH, dd = e % DH;
         float acc = 0.f;
@@ -336,10 +390,10 @@ struct StreamArgs {
     // attention
     const uint16_t *kc, *vc, *q, *kb, *vb; const int32_t* kv_len;
     float *part_o, *part_ml;
-    int H, kv_cap, nq, chunk_tiles, n_chunks, slots, P, nc;
+    int H, kv_cap, kv_lim, nq, nb, ct_min, target, tail_base, P, nc;
     float scale_log2;
-    // role layout: prefix workgroups first, then conv, then the block part
-    int prefix_blocks, prefix_x, n_conv, n_tail;
+    // role layout: prefix workgroups first (one per possible work item), then conv, then the block part
+    int prefix_blocks, n_conv, n_tail;
 };
 
 template <int DH, int NQT>
@@ -348,11 +402,11 @@ __global__ __launch_bounds__(kRoleT) void k_verify_stream(StreamArgs A)
     extern __shared__ float lds[];
     const int id = blockIdx.x;
     if (id < A.prefix_blocks) {
-        const int chunk = id % A.prefix_x, h = (id / A.prefix_x) % A.H, b = id / (A.prefix_x * A.H);
-        if (chunk >= A.n_chunks) return;
-        int L = A.kv_len[b];
-        L = L < 0 ? 0 : (L > A.kv_cap ? A.kv_cap : L);
-        prefix_block<DH, NQT>(A.kc, A.vc, L, A.q, A.part_o, A.part_ml, A.H, A.kv_cap, A.nq, A.chunk_tiles, A.slots,
+        const int ct = split_ct(A.kv_len, A.nb, A.H, A.kv_lim, A.ct_min, A.target);
+        int b, h, chunk;
+        if (!split_item(A.kv_len, A.nb, A.H, A.kv_lim, ct, id, b, h, chunk)) return;
+        const int L = prefix_len(A.kv_len, b, A.kv_lim);
+        prefix_block<DH, NQT>(A.kc, A.vc, L, A.q, A.part_o, A.part_ml, A.H, A.kv_cap, A.nq, ct, id,
                               A.scale_log2, chunk, h, b, lds);
         return;
     }
@@ -367,7 +421,7 @@ __global__ __launch_bounds__(kRoleT) void k_verify_stream(StreamArgs A)
     }
     const int t = r - A.n_conv;
     const int h = t % A.H, c = (t / A.H) % A.nc, b = t / (A.H * A.nc);
-    tail_block<HCI_BF16>(A.q, A.kb, A.vb, A.part_o, A.part_ml, A.H, DH, A.P, A.nq, A.slots, A.n_chunks,
+    tail_block<HCI_BF16>(A.q, A.kb, A.vb, A.part_o, A.part_ml, A.H, DH, A.P, A.nq, A.tail_base,
                          A.scale_log2, c, h, b, lds);
 }
 
@@ -375,29 +429,67 @@ __global__ __launch_bounds__(kRoleT) void k_verify_stream(StreamArgs A)
 //
 // With more than 16 queries per sequence (several candidates) every wave of a
 // prefix workgroup owns one 16-query tile and all four walk the same KV
-// tiles: each 32-key tile is read from HBM once per workgroup -- a quarter
-// by each wave, non-temporal, into one of two LDS buffers -- and every wave
-// takes the matrix-core operands from LDS in the order they were stored
-// (a contiguous kilobyte per fragment, no bank conflicts).  A wave keeps the
-// register state of a single query tile, so several workgroups fit a CU.
-// Two tiles' loads are in flight while the current one is consumed (two
-// register sets take turns); one barrier per tile separates the buffers.
+// tiles.  Each 32-key tile is read from HBM once per workgroup, straight into
+// LDS by the direct global->LDS loads of gfx950: lane l's 16 bytes land at the
+// wave's LDS base + 16*l, so a wave-wide load copies one contiguous kilobyte
+// of the tiled cache and no registers are spent on staging.  Four LDS stages
+// keep three tiles in flight while the fourth is consumed, and every wave
+// takes its matrix-core operands from LDS in the order they were stored (no
+// bank conflicts).  A wave waits for its own direct loads with an explicit
+// vector-memory count (loads complete in issue order); the barrier that
+// follows publishes the tile to the other waves and also marks the stage
+// read last time as free, so it is refilled as soon as the operands of the
+// current tile are in registers.
+
+constexpr int kStages = 4;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global->LDS load of 16 bytes per lane, non-temporal: lane l's bytes
+// land at lds_base + 16*l (lds_base wave-uniform, in M0).  Written as inline
+// assembly so that the compiler's own wait insertion, which cannot follow a
+// multi-stage LDS pipeline across loop iterations and would drain every load
+// in flight, leaves it alone; the waits are explicit (HCI_WAIT_VM).  M0 is
+// saved and restored, and one wait state separates its write from the load.
+__device__ __forceinline__ void dma16_nt(const uint4* src, const uint4* lds_dst) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_dst);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved) : "v"(src), "s"(base) : "memory");
+}
+
+// s_waitcnt that leaves n vector-memory operations outstanding (vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt at their no-wait maxima)
+#define HCI_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
+
+__device__ __forceinline__ void lds_read_barrier() {
+    // this wave's LDS reads have completed, then the workgroup barrier; the memory
+    // clobber keeps the compiler from moving any load or store across it
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <int DH>
 __global__ __launch_bounds__(kRoleT) void k_attn_prefix_shared(StreamArgs A, int nqt)
 {
-    constexpr int J = DH / 32, DT = DH / 16, KV4 = 4 * DH;
-    constexpr int PER = 2 * KV4 / kRoleT;             // uint4 per thread per tile (K then V)
-    __shared__ uint4 buf[2][2 * KV4];
+    constexpr int KV4 = 4 * DH;                        // uint4 of K (then of V) per tile
+    constexpr int TU = 2 * KV4;                        // uint4 per tile
+    constexpr int PER = TU / kRoleT;                   // direct loads per thread per tile
+    static_assert(TU % kRoleT == 0 && KV4 % 64 == 0, "a tile splits into wave-wide loads");
+    __shared__ uint4 st0[TU], st1[TU], st2[TU], st3[TU];
     const int id = blockIdx.x;
-    const int chunk = id % A.prefix_x, h = (id / A.prefix_x) % A.H, b = id / (A.prefix_x * A.H);
-    if (chunk >= A.n_chunks) return;
-    int L = A.kv_len[b];
-    L = L < 0 ? 0 : (L > A.kv_cap ? A.kv_cap : L);
+    const int ct = split_ct(A.kv_len, A.nb, A.H, A.kv_lim, A.ct_min, A.target);
+    int b, h, chunk;
+    if (!split_item(A.kv_len, A.nb, A.H, A.kv_lim, ct, id, b, h, chunk)) return;   // whole workgroup
+    const int L = prefix_len(A.kv_len, b, A.kv_lim);
     const int tiles = (L + kTile - 1) / kTile;
-    const int t0 = chunk * A.chunk_tiles;
-    if (t0 >= tiles) return;                           // whole workgroup
-    const int t1 = min(t0 + A.chunk_tiles, tiles);
+    const int t0 = chunk * ct;
+    if (t0 >= tiles) return;                           // cannot happen for an item; kept as a guard
+    const int t1 = min(t0 + ct, tiles);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
     const bool has_q = wave < nqt;
 
@@ -405,65 +497,69 @@ __global__ __launch_bounds__(kRoleT) void k_attn_prefix_shared(StreamArgs A, int
     {
         const int qi = 16 * wave + n;
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (has_q && qi < A.nq) v = *(const uint4*)(A.q + (((size_t)b * A.nq + qi) * A.H + h) * DH + 32 * j + 8 * g);
-            a.q[0][j] = as_bf16x8(v);
+        for (int j = 0; j < DH / 32; ++j) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (has_q && qi < A.nq) v = *(const u32x4*)(A.q + (((size_t)b * A.nq + qi) * A.H + h) * DH + 32 * j + 8 * g);
+            // the query loads complete here, before any direct load is issued: the compiler
+            // then has no load of its own pending inside the pipeline below
+            asm volatile("" : "+v"(v));
+            a.q[0][j] = __builtin_bit_cast(bf16x8, v);
         }
         a.m[0] = -INFINITY;
         a.l[0] = 0.f;
 #pragma unroll
-        for (int t = 0; t < DT; ++t) a.o[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < DH / 16; ++t) a.o[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const size_t slab = ((size_t)b * A.H + h) * (size_t)(A.kv_cap / kTile) * KV4;
     const uint4* kp = (const uint4*)A.kc + slab;
     const uint4* vp = (const uint4*)A.vc + slab;
-    // two register sets take turns: while tile T is consumed from LDS, tile T+1 (issued one
-    // iteration earlier) and tile T+2 are in flight, then T+1 goes to the free LDS buffer
-    uint4 ra[PER], rb[PER];
-    auto fetch = [&](uint4* r, int T) {
+
+    auto issue = [&](uint4* dst, int T) {
         const size_t base = (size_t)T * KV4;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int e = tid + kRoleT * i;
-            r[i] = e < KV4 ? load_nt(kp + base + e) : load_nt(vp + base + (e - KV4));
+            const int e = tid + kRoleT * i;            // wave-uniform K/V choice: KV4 is a multiple of 64
+            const uint4* src = e < KV4 ? kp + base + e : vp + base + (e - KV4);
+            dma16_nt(src, dst + (e & ~63));
         }
     };
-    auto stash = [&](const uint4* r, int slot) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) buf[slot][tid + kRoleT * i] = r[i];
-    };
-    auto consume = [&](int T) {
-        if (!has_q) return;
-        const int cur = (T - t0) & 1;
+    auto step = [&](const uint4* cur, uint4* refill, int T) {
+        // loads issued after tile T's: tiles T+1 and T+2, where they exist
+        const int later = min(t1 - 1 - T, kStages - 2);
+        if (later >= 2) HCI_WAIT_VM(2 * PER);
+        else if (later == 1) HCI_WAIT_VM(PER);
+        else HCI_WAIT_VM(0);
+        lds_read_barrier();                            // tile T complete for every wave; tile T-1 read by all
         KvTile<DH> t;
+        if (has_q) {
 #pragma unroll
-        for (int i = 0; i < 2 * J; ++i) t.k[i] = buf[cur][i * 64 + lane];
+            for (int i = 0; i < DH / 16; ++i) t.k[i] = cur[i * 64 + lane];
 #pragma unroll
-        for (int i = 0; i < DT; ++i) t.v[i] = buf[cur][KV4 + i * 64 + lane];
-        consume_tile<DH, 1>(a, t, T, L, g, A.scale_log2);
+            for (int i = 0; i < DH / 16; ++i) t.v[i] = cur[KV4 + i * 64 + lane];
+        }
+        // refill after the operand reads: the compiler then has no direct load to order them against
+        if (T + kStages - 1 < t1) issue(refill, T + kStages - 1);
+        if (has_q) consume_tile<DH, 1>(a, t, T, L, g, A.scale_log2);
     };
-    fetch(ra, t0);
-    stash(ra, 0);
-    if (t0 + 1 < t1) fetch(ra, t0 + 1);
-    __syncthreads();
-    for (int T = t0; T < t1; T += 2) {
-        if (T + 2 < t1) fetch(rb, T + 2);
-        consume(T);
-        if (T + 1 < t1) stash(ra, (T + 1 - t0) & 1);
-        __syncthreads();
+    issue(st0, t0);
+    if (t0 + 1 < t1) issue(st1, t0 + 1);
+    if (t0 + 2 < t1) issue(st2, t0 + 2);
+    for (int T = t0; T < t1; T += kStages) {
+        step(st0, st3, T);
         if (T + 1 >= t1) break;
-        if (T + 3 < t1) fetch(ra, T + 3);
-        consume(T + 1);
-        if (T + 2 < t1) stash(rb, (T + 2 - t0) & 1);
-        __syncthreads();
+        step(st1, st0, T + 1);
+        if (T + 2 >= t1) break;
+        step(st2, st1, T + 2);
+        if (T + 3 >= t1) break;
+        step(st3, st2, T + 3);
     }
+    // the last step waited for every direct load: no LDS write is pending at exit
     if (!has_q) return;
     const int qi = 16 * wave + n;
     if (qi >= A.nq) return;
-    const size_t pbase = (((size_t)b * A.H + h) * A.slots + chunk) * A.nq;
+    const size_t pbase = (size_t)id * A.nq;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+    for (int t = 0; t < DH / 16; ++t)
         *(float4*)(A.part_o + (pbase + qi) * DH + 16 * t + 4 * g) =
             make_float4(a.o[t][0][0], a.o[t][0][1], a.o[t][0][2], a.o[t][0][3]);
     if (g == 0) *(float2*)(A.part_ml + (pbase + qi) * 2) = make_float2(a.m[0], a.l[0]);
@@ -475,16 +571,16 @@ template <int ACT>
 __global__ __launch_bounds__(kRoleT) void k_attn_tail(
     const typename Act<ACT>::T* __restrict__ q, const typename Act<ACT>::T* __restrict__ kb,
     const typename Act<ACT>::T* __restrict__ vb, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int H, int DH, int P, int nq, int slots, int tail_slot, float scale_log2)
+    int H, int DH, int P, int nq, int tail_base, float scale_log2)
 {
     extern __shared__ float lds[];
-    tail_block<ACT>(q, kb, vb, part_o, part_ml, H, DH, P, nq, slots, tail_slot, scale_log2,
+    tail_block<ACT>(q, kb, vb, part_o, part_ml, H, DH, P, nq, tail_base, scale_log2,
                     blockIdx.y, blockIdx.x, blockIdx.z, lds);
 }
 
 // ------------------------------------------------------------- f32 prefix
 //
-// fp32 layers (small shapes): 64 threads per (chunk, head, sequence).  The
+// fp32 layers (small shapes): 64 threads per work item (chunk, head, sequence).  The
 // tile is unpacked into LDS rows; thread tid scores query tid and accumulates
 // output dims tid and tid+64 of every query, all in fp32 on the vector ALUs.
 // Limits: Dh <= 128, nq <= 64.
@@ -496,16 +592,18 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
     const float* __restrict__ kc, const float* __restrict__ vc,
     const int32_t* __restrict__ kv_len, const float* __restrict__ q,
     float* __restrict__ part_o, float* __restrict__ part_ml,
-    int H, int DH, int kv_cap, int nq, int chunk_tiles, int slots, float scale_log2)
+    int nb, int H, int DH, int kv_cap, int kv_lim, int nq, int ct_min, int target, float scale_log2)
 {
     __shared__ float ks[kTile][kF32Dh + 1];
     __shared__ float vs[kTile][kF32Dh + 1];
     __shared__ float ps[kF32Nq][kTile + 1];
     __shared__ float alpha_s[kF32Nq];
 
-    const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    int L = kv_len[b];
-    L = L < 0 ? 0 : (L > kv_cap ? kv_cap : L);
+    const int item = blockIdx.x;
+    const int chunk_tiles = split_ct(kv_len, nb, H, kv_lim, ct_min, target);
+    int b, h, chunk;
+    if (!split_item(kv_len, nb, H, kv_lim, chunk_tiles, item, b, h, chunk)) return;
+    const int L = prefix_len(kv_len, b, kv_lim);
     const int tiles = (L + kTile - 1) / kTile;
     const int t0 = chunk * chunk_tiles;
     if (t0 >= tiles) return;
@@ -573,7 +671,7 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
             }
         }
     }
-    const size_t pbase = (((size_t)b * H + h) * slots + chunk) * nq;
+    const size_t pbase = (size_t)item * nq;
 #pragma unroll
     for (int qi = 0; qi < kF32Nq; ++qi) {
         if (qi < nq) {
@@ -593,8 +691,8 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
 // ----------------------------------------------------------------- combine
 //
 // One workgroup of 256 threads per (query, head, sequence) merges the chunk
-// partials (slots 0..nch-1, nch from kv_len) and the block part (slot
-// n_chunks):  M = max m_s, w_s = 2^(m_s - M),
+// partials (items base_b + h*n_b + 0..n_b-1, derived from kv_len exactly as the
+// prefix kernels derive them) and the block part:  M = max m_s, w_s = 2^(m_s - M),
 //   o = sum_s w_s O_s / sum_s w_s l_s,
 // with the chunks taken in a fixed interleave and the group sums merged in a
 // fixed order, so the result does not depend on scheduling.
@@ -606,7 +704,7 @@ template <int ACT>
 __global__ __launch_bounds__(kCombT) void k_attn_combine(
     const int32_t* __restrict__ kv_len, const float* __restrict__ part_o, const float* __restrict__ part_ml,
     typename Act<ACT>::T* __restrict__ o,
-    int H, int DH, int nq, int kv_cap, int chunk_tiles, int n_chunks, int slots, float scale_log2)
+    int nb, int H, int DH, int nq, int kv_lim, int ct_min, int target, int tail_base)
 {
     __shared__ float wts[kMaxChunks + 1];
     __shared__ float red[kCombT / 64][2];
@@ -616,17 +714,17 @@ __global__ __launch_bounds__(kCombT) void k_attn_combine(
     const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
     const int nw = kCombT / 64;
 
-    int L = kv_len[b];
-    L = L < 0 ? 0 : (L > kv_cap ? kv_cap : L);
-    const int tiles = (L + kTile - 1) / kTile;
-    int nch = (tiles + chunk_tiles - 1) / chunk_tiles;
-    nch = nch > n_chunks ? n_chunks : nch;
-    const size_t pb = ((size_t)b * H + h) * slots;
-    auto slot_of = [&](int s) { return s < nch ? s : n_chunks; };    // s == nch is the block part
+    const int ct = split_ct(kv_len, nb, H, kv_lim, ct_min, target);
+    int base = 0;
+    for (int bb = 0; bb < b; ++bb) base += (prefix_tiles(kv_len, bb, kv_lim) + ct - 1) / ct * H;
+    const int nch = (prefix_tiles(kv_len, b, kv_lim) + ct - 1) / ct;
+    const size_t first = (size_t)base + (size_t)h * nch;
+    const size_t tail = (size_t)tail_base + (size_t)b * H + h;
+    auto slot_of = [&](int s) { return s < nch ? first + s : tail; };    // s == nch is the block part
     const int ns = nch + 1;
 
     float mloc = -INFINITY;
-    for (int s = tid; s < ns; s += kCombT) mloc = fmaxf(mloc, part_ml[((pb + slot_of(s)) * nq + qi) * 2]);
+    for (int s = tid; s < ns; s += kCombT) mloc = fmaxf(mloc, part_ml[(slot_of(s) * nq + qi) * 2]);
     for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
     if (ln == 0) red[wave][0] = mloc;
     __syncthreads();
@@ -635,7 +733,7 @@ __global__ __launch_bounds__(kCombT) void k_attn_combine(
 
     float lloc = 0.f;
     for (int s = tid; s < ns; s += kCombT) {
-        const float2 ml = *(const float2*)(part_ml + ((pb + slot_of(s)) * nq + qi) * 2);
+        const float2 ml = *(const float2*)(part_ml + (slot_of(s) * nq + qi) * 2);
         const float w = exp2f(ml.x - M);
         wts[s] = w;
         lloc = fmaf(w, ml.y, lloc);
@@ -653,16 +751,16 @@ __global__ __launch_bounds__(kCombT) void k_attn_combine(
     if (grp < ng) {
         int s = grp;
         for (; s + 3 * ng < ns; s += 4 * ng) {
-            const float o0 = part_o[((pb + slot_of(s)) * nq + qi) * DH + dd];
-            const float o1 = part_o[((pb + slot_of(s + ng)) * nq + qi) * DH + dd];
-            const float o2 = part_o[((pb + slot_of(s + 2 * ng)) * nq + qi) * DH + dd];
-            const float o3 = part_o[((pb + slot_of(s + 3 * ng)) * nq + qi) * DH + dd];
+            const float o0 = part_o[(slot_of(s) * nq + qi) * DH + dd];
+            const float o1 = part_o[(slot_of(s + ng) * nq + qi) * DH + dd];
+            const float o2 = part_o[(slot_of(s + 2 * ng) * nq + qi) * DH + dd];
+            const float o3 = part_o[(slot_of(s + 3 * ng) * nq + qi) * DH + dd];
             acc = fmaf(wts[s], o0, acc);
             acc = fmaf(wts[s + ng], o1, acc);
             acc = fmaf(wts[s + 2 * ng], o2, acc);
             acc = fmaf(wts[s + 3 * ng], o3, acc);
         }
-        for (; s < ns; s += ng) acc = fmaf(wts[s], part_o[((pb + slot_of(s)) * nq + qi) * DH + dd], acc);
+        for (; s < ns; s += ng) acc = fmaf(wts[s], part_o[(slot_of(s) * nq + qi) * DH + dd], acc);
     }
     acc_s[tid] = acc;
     __syncthreads();
@@ -681,25 +779,34 @@ AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_k
     const int P = gamma + 1;
     p.nq = nc * P;
     const int tiles = (max_kv_len + kTile - 1) / kTile;
-    // Aim for about 16 waves (4 workgroups of 4 waves) per CU over the whole
-    // grid so that every CU keeps several waves and their prefetched tiles in
-    // flight, with at least 8 tiles per wave so that partials stay a small
-    // fraction of the traffic.
-    const long long total_tiles = (long long)tiles * nb * L->heads;
-    // several query tiles: a workgroup walks its whole chunk with all four waves, so
-    // twice as many (shorter) chunks keep the same number of tiles in flight
-    const long long target_wgs = (long long)num_cus * ((p.nq + 15) / 16 > 1 ? 8 : 4);
-    long long ct = (total_tiles + target_wgs - 1) / (target_wgs > 0 ? target_wgs : 1);
-    if (ct < 8 * kPrefixWaves) ct = 8 * kPrefixWaves;
-    const long long min_ct = (tiles + kMaxChunks - 1) / kMaxChunks;   // combine holds <= kMaxChunks weights
-    if (ct < min_ct) ct = min_ct;
-    if (ct > tiles && tiles > 0) ct = tiles;
-    if (ct < 1) ct = 1;
-    p.chunk_tiles = (int)ct;
-    p.n_chunks = tiles > 0 ? (int)((tiles + ct - 1) / ct) : 0;
-    p.slots = p.n_chunks + 1;                       // + the block part
-    p.part_o_elems = (size_t)nb * L->heads * p.slots * p.nq * L->head_dim;
-    p.part_ml_elems = (size_t)nb * L->heads * p.slots * p.nq * 2;
+    // The device splits the real prefixes into about `target` chunks (work
+    // items) over the whole batch.  With one query tile the fused kernel keeps
+    // two 4-wave workgroups per CU: two rounds of them keep every CU streaming
+    // until the end.  With several query tiles a workgroup walks its chunk with
+    // all four waves, so twice as many (shorter) chunks keep the same number of
+    // tiles in flight.  A chunk holds at least 8 tiles per wave, so that
+    // partials stay a small fraction of the traffic, and a sequence never has
+    // more than kMaxChunks chunks (the combine's weight table).
+    const int nqt = (p.nq + 15) / 16;
+    p.target = num_cus * (nqt > 1 ? 8 : 4);
+    if (p.target < 1) p.target = 1;
+    int ct_min = 8 * kPrefixWaves;
+    const int min_ct = (tiles + kMaxChunks - 1) / kMaxChunks;
+    if (ct_min < min_ct) ct_min = min_ct;
+    p.ct_min = ct_min;
+    p.kv_lim = max_kv_len;    // callers check max_kv_len + P <= kv_cap before any launch
+    // items <= H * sum_b (tiles_b / ct + 1) <= target + nb * H, since ct >= H * sum_b tiles_b / target;
+    // no items at all when every prefix is empty
+    const long long nbh = (long long)nb * L->heads;
+    if (p.target + 2 * nbh > (1LL << 30)) {            // beyond any launch: the caller reports it unsupported
+        p.items_cap = -1;
+        return p;
+    }
+    p.items_cap = tiles > 0 ? p.target + (int)nbh : 0;
+    p.tail_base = p.items_cap;
+    const size_t parts = (size_t)p.items_cap + (size_t)nbh;   // + the block part of each (b, h)
+    p.part_o_elems = parts * p.nq * L->head_dim;
+    p.part_ml_elems = parts * p.nq * 2;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     p.bytes = up(p.part_o_elems * 4) + up(p.part_ml_elems * 4);
     return p;
@@ -748,10 +855,9 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
         A.kc = (const uint16_t*)S->k_cache; A.vc = (const uint16_t*)S->v_cache; A.q = (const uint16_t*)blk->q;
         A.kb = (const uint16_t*)blk->k; A.vb = (const uint16_t*)blk->v; A.kv_len = S->kv_len;
         A.part_o = part_o; A.part_ml = part_ml;
-        A.H = H; A.kv_cap = S->kv_cap; A.nq = nq; A.chunk_tiles = plan.chunk_tiles; A.n_chunks = plan.n_chunks;
-        A.slots = plan.slots; A.P = P; A.nc = nc; A.scale_log2 = scale_log2;
-        A.prefix_x = plan.n_chunks;
-        A.prefix_blocks = plan.n_chunks * H * nb;
+        A.H = H; A.kv_cap = S->kv_cap; A.kv_lim = plan.kv_lim; A.nq = nq; A.nb = nb; A.ct_min = plan.ct_min; A.target = plan.target;
+        A.tail_base = plan.tail_base; A.P = P; A.nc = nc; A.scale_log2 = scale_log2;
+        A.prefix_blocks = plan.items_cap;
         const int nqt = (nq + 15) / 16;
         // With one query tile the streaming kernel keeps two workgroups per CU and the
         // short roles ride along at the end of its grid.  With more query tiles it holds
@@ -767,7 +873,7 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
             }
             hipLaunchKernelGGL(k_attn_tail<HCI_BF16>, dim3(H, nc, nb), dim3(kRoleT), tail_lds, st,
                                (const uint16_t*)blk->q, (const uint16_t*)blk->k, (const uint16_t*)blk->v, part_o,
-                               part_ml, H, DH, P, nq, plan.slots, plan.n_chunks, scale_log2);
+                               part_ml, H, DH, P, nq, plan.tail_base, scale_log2);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         A.n_conv = fuse && conv ? ((L->d + kCG - 1) / kCG) * nc * nb : 0;
@@ -809,13 +915,13 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
         }
         hipLaunchKernelGGL(k_attn_tail<HCI_F32>, dim3(H, nc, nb), dim3(kRoleT), tail_lds, st,
                            (const float*)blk->q, (const float*)blk->k, (const float*)blk->v, part_o, part_ml,
-                           H, DH, P, nq, plan.slots, plan.n_chunks, scale_log2);
+                           H, DH, P, nq, plan.tail_base, scale_log2);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (plan.n_chunks > 0) {
-            hipLaunchKernelGGL(k_attn_prefix_f32, dim3(plan.n_chunks, H, nb), dim3(64), 0, st,
+        if (plan.items_cap > 0) {
+            hipLaunchKernelGGL(k_attn_prefix_f32, dim3(plan.items_cap), dim3(64), 0, st,
                                (const float*)S->k_cache, (const float*)S->v_cache, S->kv_len,
-                               (const float*)blk->q, part_o, part_ml, H, DH, S->kv_cap, nq,
-                               plan.chunk_tiles, plan.slots, scale_log2);
+                               (const float*)blk->q, part_o, part_ml, nb, H, DH, S->kv_cap, plan.kv_lim, nq,
+                               plan.ct_min, plan.target, scale_log2);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
@@ -824,12 +930,10 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
     dim3 cgrid(nq, H, nb), cblock(kCombT);
     if (L->act_dtype == HCI_BF16) {
         hipLaunchKernelGGL(k_attn_combine<HCI_BF16>, cgrid, cblock, 0, st, S->kv_len, part_o, part_ml,
-                           (uint16_t*)blk->o, H, DH, nq, S->kv_cap, plan.chunk_tiles, plan.n_chunks, plan.slots,
-                           scale_log2);
+                           (uint16_t*)blk->o, nb, H, DH, nq, plan.kv_lim, plan.ct_min, plan.target, plan.tail_base);
     } else {
         hipLaunchKernelGGL(k_attn_combine<HCI_F32>, cgrid, cblock, 0, st, S->kv_len, part_o, part_ml,
-                           (float*)blk->o, H, DH, nq, S->kv_cap, plan.chunk_tiles, plan.n_chunks, plan.slots,
-                           scale_log2);
+                           (float*)blk->o, nb, H, DH, nq, plan.kv_lim, plan.ct_min, plan.target, plan.tail_base);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return mark(2);

@@ -87,9 +87,11 @@ __host__ __device__ __forceinline__ size_t v_elem(int row, int dd, int Dh) {
 // workspace and launches the kernels, so both always agree.
 struct AttnPlan {
     int nq;            // queries per sequence = nc * P
-    int chunk_tiles;   // tiles per split-K chunk
-    int n_chunks;      // chunks per (sequence, head), from max_kv_len
-    int slots;         // partial slots per (sequence, head): the chunks, then the block part
+    int ct_min;        // smallest split-K chunk (tiles) the device may pick
+    int target;        // work items the device aims for over the whole batch
+    int items_cap;     // bound on the work items (the prefix grid); 0 when max_kv_len is 0
+    int tail_base;     // partial index of the first block part (= items_cap)
+    int kv_lim;        // prefix lengths are read clamped to [0, kv_lim] (= max_kv_len)
     size_t part_o_elems, part_ml_elems;
     size_t bytes;      // workspace bytes (256-aligned sections)
 };
