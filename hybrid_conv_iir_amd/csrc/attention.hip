@@ -396,6 +396,24 @@ struct StreamArgs {
     int prefix_blocks, n_conv, n_tail;
 };
 
+// The short roles of a streaming kernel, workgroup r past the prefix items:
+// first the conv/IIR scan of 16 channels of one sequence (all its
+// candidates), then the causal block part of one (sequence, candidate, head).
+__device__ __forceinline__ void short_role(const StreamArgs& A, int r, int DH, float* lds)
+{
+    if (r < A.n_conv) {
+        const int groups = (A.d + kCG - 1) / kCG;
+        const int cgi = r % groups, b = r / groups;
+        conv_iir_block<HCI_BF16>(A.w_short, A.w_outer, A.lam, A.beta, A.cc, A.short_win, A.outer_win, A.iir, A.x,
+                                 A.f_out, A.s_out, A.y_out, A.d, A.Ts, A.To, A.N, A.nc, A.P, cgi, b, lds);
+        return;
+    }
+    const int t = r - A.n_conv;
+    const int h = t % A.H, c = (t / A.H) % A.nc, b = t / (A.H * A.nc);
+    tail_block<HCI_BF16>(A.q, A.kb, A.vb, A.part_o, A.part_ml, A.H, DH, A.P, A.nq, A.tail_base,
+                         A.scale_log2, c, h, b, lds);
+}
+
 template <int DH, int NQT>
 __global__ __launch_bounds__(kRoleT) void k_verify_stream(StreamArgs A)
 {
@@ -411,18 +429,7 @@ __global__ __launch_bounds__(kRoleT) void k_verify_stream(StreamArgs A)
         return;
     }
     // the short roles come last: they fill the slots the KV stream frees as it drains
-    const int r = id - A.prefix_blocks;
-    if (r < A.n_conv) {
-        const int groups = (A.d + kCG - 1) / kCG;
-        const int cgi = r % groups, c = (r / groups) % A.nc, b = r / (groups * A.nc);
-        conv_iir_block<HCI_BF16>(A.w_short, A.w_outer, A.lam, A.beta, A.cc, A.short_win, A.outer_win, A.iir, A.x,
-                                 A.f_out, A.s_out, A.y_out, A.d, A.Ts, A.To, A.N, A.nc, A.P, cgi, c, b, lds);
-        return;
-    }
-    const int t = r - A.n_conv;
-    const int h = t % A.H, c = (t / A.H) % A.nc, b = t / (A.H * A.nc);
-    tail_block<HCI_BF16>(A.q, A.kb, A.vb, A.part_o, A.part_ml, A.H, DH, A.P, A.nq, A.tail_base,
-                         A.scale_log2, c, h, b, lds);
+    short_role(A, id - A.prefix_blocks, DH, lds);
 }
 
 // ------------------------------------------- several query tiles per prefix
@@ -480,8 +487,15 @@ __global__ __launch_bounds__(kRoleT) void k_attn_prefix_shared(StreamArgs A, int
     constexpr int TU = 2 * KV4;                        // uint4 per tile
     constexpr int PER = TU / kRoleT;                   // direct loads per thread per tile
     static_assert(TU % kRoleT == 0 && KV4 % 64 == 0, "a tile splits into wave-wide loads");
-    __shared__ uint4 st0[TU], st1[TU], st2[TU], st3[TU];
+    __shared__ uint4 stage[kStages][TU];
+    uint4 *st0 = stage[0], *st1 = stage[1], *st2 = stage[2], *st3 = stage[3];
     const int id = blockIdx.x;
+    if (id >= A.prefix_blocks) {
+        // the short roles ride at the end of the grid (the host lets them only when their
+        // LDS fits the stages) and fill the slots the KV stream frees as it drains
+        short_role(A, id - A.prefix_blocks, DH, (float*)&stage[0][0]);
+        return;
+    }
     const int ct = split_ct(A.kv_len, A.nb, A.H, A.kv_lim, A.ct_min, A.target);
     int b, h, chunk;
     if (!split_item(A.kv_len, A.nb, A.H, A.kv_lim, ct, id, b, h, chunk)) return;   // whole workgroup
@@ -813,8 +827,8 @@ AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_k
 }
 
 size_t stream_lds_bytes(const hci_layer* L, int nc, int P) {
-    const int nqt = (nc * P + 15) / 16;
-    const size_t pre = (kPrefixWaves - 1) * (size_t)nqt * (16 * L->head_dim + 32);
+    (void)nc;    // the fused kernel runs with one query tile only
+    const size_t pre = (kPrefixWaves - 1) * (size_t)(16 * L->head_dim + 32);
     const int act_bytes = L->act_dtype == HCI_BF16 ? 2 : 4;
     size_t f = conv_iir_lds_floats(L->taps_outer, P);
     const size_t t = tail_lds_floats(P, L->head_dim, act_bytes);
@@ -823,14 +837,14 @@ size_t stream_lds_bytes(const hci_layer* L, int nc, int P) {
     return f * sizeof(float);
 }
 
-template <int DH, int NQT>
+template <int DH>
 static hipError_t launch_stream(const StreamArgs& A, int blocks, size_t lds, hipStream_t st) {
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_verify_stream<DH, NQT>,
+        hipError_t e = hipFuncSetAttribute((const void*)k_verify_stream<DH, 1>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_verify_stream<DH, NQT>), dim3(blocks), dim3(kRoleT), lds, st, A);
+    hipLaunchKernelGGL((k_verify_stream<DH, 1>), dim3(blocks), dim3(kRoleT), lds, st, A);
     return hipGetLastError();
 }
 
@@ -862,10 +876,15 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
         // With one query tile the streaming kernel keeps two workgroups per CU and the
         // short roles ride along at the end of its grid.  With more query tiles it holds
         // a whole CU per workgroup, so the short roles run as their own light kernels.
+        // With one query tile the streaming kernel keeps two workgroups per CU and the short
+        // roles ride along at the end of its grid.  With several, the shared-prefix kernel
+        // carries them when their LDS fits its stages, else they run as their own kernels first.
         const bool fuse = nqt == 1;
-        if (!fuse) {
+        const size_t stage_bytes = (size_t)kStages * 128 * DH;
+        const size_t tail_lds = tail_lds_floats(P, DH, 2) * sizeof(float);
+        const bool ride = fuse || (conv_iir_lds_bytes(L->taps_outer, P) <= stage_bytes && tail_lds <= stage_bytes);
+        if (!ride) {
             if (conv && (e = launch_conv_iir(L, S, blk, nb, nc, P, st)) != hipSuccess) return e;
-            const size_t tail_lds = tail_lds_floats(P, DH, 2) * sizeof(float);
             if (tail_lds > 65536) {
                 e = hipFuncSetAttribute((const void*)k_attn_tail<HCI_BF16>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                         (int)tail_lds);
@@ -876,32 +895,20 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
                                part_ml, H, DH, P, nq, plan.tail_base, scale_log2);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        A.n_conv = fuse && conv ? ((L->d + kCG - 1) / kCG) * nc * nb : 0;
-        A.n_tail = fuse ? nb * nc * H : 0;
+        A.n_conv = ride && conv ? ((L->d + kCG - 1) / kCG) * nb : 0;
+        A.n_tail = ride ? nb * nc * H : 0;
         const long long blocks = (long long)A.prefix_blocks + A.n_conv + A.n_tail;
         if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-        const size_t lds = stream_lds_bytes(L, nc, P);
-        if (!fuse && A.prefix_blocks > 0) {
-            if (DH == 128)
-                hipLaunchKernelGGL(k_attn_prefix_shared<128>, dim3(A.prefix_blocks), dim3(kRoleT), 0, st, A, nqt);
-            else
-                hipLaunchKernelGGL(k_attn_prefix_shared<64>, dim3(A.prefix_blocks), dim3(kRoleT), 0, st, A, nqt);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        } else if (blocks > 0) {
-            if (DH == 128) {
-                switch (nqt) {
-                    case 1: e = launch_stream<128, 1>(A, (int)blocks, lds, st); break;
-                    case 2: e = launch_stream<128, 2>(A, (int)blocks, lds, st); break;
-                    case 3: e = launch_stream<128, 3>(A, (int)blocks, lds, st); break;
-                    default: e = launch_stream<128, 4>(A, (int)blocks, lds, st); break;
-                }
+        if (blocks > 0) {
+            if (!fuse) {
+                if (DH == 128)
+                    hipLaunchKernelGGL(k_attn_prefix_shared<128>, dim3((int)blocks), dim3(kRoleT), 0, st, A, nqt);
+                else
+                    hipLaunchKernelGGL(k_attn_prefix_shared<64>, dim3((int)blocks), dim3(kRoleT), 0, st, A, nqt);
+                e = hipGetLastError();
             } else {
-                switch (nqt) {
-                    case 1: e = launch_stream<64, 1>(A, (int)blocks, lds, st); break;
-                    case 2: e = launch_stream<64, 2>(A, (int)blocks, lds, st); break;
-                    case 3: e = launch_stream<64, 3>(A, (int)blocks, lds, st); break;
-                    default: e = launch_stream<64, 4>(A, (int)blocks, lds, st); break;
-                }
+                const size_t lds = stream_lds_bytes(L, nc, P);
+                e = DH == 128 ? launch_stream<128>(A, (int)blocks, lds, st) : launch_stream<64>(A, (int)blocks, lds, st);
             }
             if (e != hipSuccess) return e;
         }

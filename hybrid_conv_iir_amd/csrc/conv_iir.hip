@@ -3,10 +3,12 @@
 // state (EvSpark digest, Figure 1(d): the outer-FIR inputs u_i and the IIR
 // states s_i are what slicing later selects from).
 //
-// One workgroup = 16 channels of one (sequence, candidate) block, 256
-// threads, so a 4096-channel layer spreads over 256 workgroups.
+// One workgroup = 16 channels of one sequence, 256 threads, so a
+// 4096-channel layer spreads over 256 workgroups per sequence; the candidate
+// blocks of the sequence share the committed window and taps and run phases
+// 1-3 in turn.
 //  phase 0  the outer window rows and the outer taps of the 16 channels are
-//           staged in LDS
+//           staged in LDS (once)
 //  phase 1  thread (position, channel) computes f_i (short FIR)
 //  phase 2  the same threads compute g_i = sum_j w_outer[j] * fbar[i-j]
 //           from LDS, one fixed-order fma chain per output
@@ -34,13 +36,13 @@ __global__ __launch_bounds__(kConvT) void k_conv_iir(
 {
     extern __shared__ float lds[];
     conv_iir_block<ACT>(w_short, w_outer, lam, beta, cc, short_win, outer_win, iir, x, f_out, s_out, y_out,
-                        d, Ts, To, N, nc, P, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+                        d, Ts, To, N, nc, P, blockIdx.x, blockIdx.y, lds);
 }
 
 hipError_t launch_conv_iir(const hci_layer* L, const hci_state* S, const hci_block* blk,
                            int nb, int nc, int P, hipStream_t st)
 {
-    dim3 grid((L->d + kCG - 1) / kCG, nc, nb), block(kConvT);
+    dim3 grid((L->d + kCG - 1) / kCG, nb), block(kConvT);
     const size_t lds = conv_iir_lds_bytes(L->taps_outer, P);
     if (lds > 65536) {
         // allow the dynamic LDS request beyond the default 64 KiB (gfx950 has 160 KiB per CU)
