@@ -78,13 +78,22 @@ def verify_alg_bytes(cfg, kv_lens) -> int:
     return kv + attn_io + conv
 
 
-def stream_alg_bytes(cfg, kv_lens) -> int:
-    """Bytes the streaming kernel must move: the verify's bytes minus the output o the combine writes.
+def stream_kernel_name(cfg) -> str:
+    """The kernel that streams the KV prefix for this workload (one 16-query tile or several)."""
+    if cfg.act != "bf16":
+        return "k_attn_prefix_f32"
+    return "k_verify_stream" if cfg.nc * cfg.P <= 16 else "k_attn_prefix_shared"
 
-    Dominated by 512 B per (key, head) of the prefix (Dh bf16 K + Dh bf16 V), read once per sequence.
+
+def stream_alg_bytes(cfg, kv_lens) -> int:
+    """Bytes the prefix-streaming kernel must move: the KV prefix once per sequence and the queries.
+
+    512 B per (key, head) of the prefix (Dh bf16 K + Dh bf16 V), read once per sequence for all
+    nc * P queries; the conv/IIR scan, the causal block part and the combine run in the finish kernel.
     """
     act = 2 if cfg.act == "bf16" else 4
-    return verify_alg_bytes(cfg, kv_lens) - cfg.nb * cfg.nc * cfg.P * cfg.heads * cfg.head_dim * act
+    nq = cfg.nb * cfg.nc * cfg.P
+    return sum(2 * cfg.heads * L * cfg.head_dim * act for L in kv_lens) + nq * cfg.heads * cfg.head_dim * act
 
 
 VERIFY_SOURCES = ("attention.hip", "conv_iir_body.h", "hci_internal.h")
@@ -583,13 +592,13 @@ def main():
         "verify_pct_of_8TBs": round(100.0 * alg_verify / (float(np.median(verify_ms)) * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "verify_positions_per_s": round(positions / (float(np.median(verify_ms)) * 1e-3), 1),
         "breakdown_ms_median": {"verify_stream": round(float(np.median(stream_ms)), 4),
-                                "attn_combine": round(float(np.median(combine_ms)), 4),
+                                "verify_finish": round(float(np.median(combine_ms)), 4),
                                 "accept": round(float(np.median(accept_ms)), 4),
                                 "slice": round(float(np.median(slice_ms)), 4),
                                 "step_device": round(float(np.median(step_dev_ms)), 4)},
         "slice_ms": round(float(np.median(slice_ms)), 4),
         "hbm_probe_read_GBs": round(probe_gbs, 1),
-        "roofline": {"kernel": "k_verify_stream" if cfg.act == "bf16" else "conv+tail+prefix (fp32 kernels)",
+        "roofline": {"kernel": stream_kernel_name(cfg),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": _traffic(args.config),
                      "alg_bytes_per_launch": int(alg_stream),

@@ -92,7 +92,7 @@ static int verify_impl(const hci_layer* L, const hci_state* S, const hci_block* 
     if (rc) return rc;
     rc = check_block(blk);
     if (rc) return rc;
-    if (conv_iir_lds_bytes(L->taps_outer, P) > kMaxLds || stream_lds_bytes(L, nc, P) > kMaxLds)
+    if (stream_lds_bytes(L, nc, P) > kMaxLds)
         return HCI_EUNSUPPORTED;
     const AttnPlan plan = plan_attention(L, nb, nc, gamma, max_kv_len, device_cu_count());
     if (plan.items_cap < 0) return HCI_EUNSUPPORTED;

@@ -5,27 +5,39 @@
 // forward from the committed state, so all nc*P queries of a sequence share
 // a single read of its prefix; that read is the part of the verify that grows
 // with context (ReaDy summary, section 5: token-wise KV traffic grows with the
-// number of attended tokens).  The prefix is split into chunks (split-K); each
-// chunk leaves a partial softmax state (running max in log2 units, normaliser,
-// unnormalised output), the block part leaves one more, and a combine kernel
-// merges them in a fixed order.
+// number of attended tokens).  The prefix is cut into work items (split-K);
+// each item leaves a partial softmax state (running max in log2 units,
+// normaliser, unnormalised output), and the combine kernel computes the
+// causal block part and merges everything in a fixed order.
 //
-// bf16 layers run ONE streaming kernel with three workgroup roles, dispatched
-// in this order so the short ones overlap the long KV stream:
-//   conv   the conv/IIR scan of 16 channels (conv_iir_body.h)
-//   tail   the causal block part of one (sequence, candidate, head)
-// (with several 16-query tiles the prefix runs as its own kernel,
-// k_attn_prefix_shared, one query tile per wave over LDS-shared KV tiles)
-//   prefix one chunk of one (sequence, head): four waves, each streaming a
-//          contiguous run of 32-key tiles with non-temporal 16-byte loads
-//          (a contiguous kilobyte per wave-wide load, thanks to the tiled
-//          cache layout) and one tile prefetched into registers; scores
-//          S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with the
-//          keys in M and up to 16*NQT queries in N; online softmax in fp32
-//          registers; the four waves' states merge in LDS before one partial
-//          is written.
-// fp32 layers (small shapes) use separate conv, tail, prefix (vector ALU)
-// and combine kernels.
+// Work distribution.  The streaming kernels run one persistent workgroup per
+// resident slot (two per CU); every workgroup takes jobs from a queue (an
+// atomic ticket counter in the workspace) until it is empty.  The queue holds
+// first the conv/IIR jobs of the layer (conv_iir_body.h), then the prefix
+// items in decreasing size: phase p covers the next half of what is left of
+// every sequence's prefix in chunks of c0 / 2^p tiles, c0 being half of a
+// slot's fair share.  Slots run at different speeds (the older of two
+// workgroups on a CU issues first, and CUs differ), so a static split ends
+// ragged; with the queue the fast slots take more items and the small last
+// items let every slot finish within a few microseconds of the others.  An
+// item always writes the same partial whichever slot runs it, so results do
+// not depend on scheduling.
+//
+// bf16 layers:
+//   k_verify_stream       one 16-query tile (nc*P <= 16): four waves split an
+//                         item into contiguous runs of 32-key tiles, streamed
+//                         with non-temporal 16-byte loads (a contiguous
+//                         kilobyte per wave-wide load, thanks to the tiled
+//                         cache layout), the next tile prefetched into
+//                         registers; S^T = K Q^T and O^T += V^T P^T on
+//                         v_mfma_f32_16x16x32_bf16 with the keys in M; online
+//                         softmax in fp32 registers; the four waves merge in
+//                         LDS before one partial is written.
+//   k_attn_prefix_shared  several query tiles: every wave owns one tile and the
+//                         four walk the same KV tiles, staged once per
+//                         workgroup in LDS by direct global->LDS loads.
+// fp32 layers (small shapes) use a vector-ALU prefix kernel with one item per
+// workgroup.
 #include "conv_iir_body.h"
 
 #include <math.h>
@@ -33,7 +45,14 @@
 namespace hci {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kRoleT = 256;            // threads per workgroup of every streaming role
+constexpr int kRoleT = 256;            // threads per workgroup of every streaming kernel
+// resident streaming workgroups per CU.  The one-tile kernel keeps one, so that no two
+// workgroups on a CU compete for issue (the older one would run up to twice as fast and
+// finish its items late); its four waves keep enough loads in flight.  The several-tile
+// kernel needs two to overlap one workgroup's matrix-core and softmax work with the
+// other's barrier waits.
+constexpr int kSlotsFused = 1;
+constexpr int kSlotsShared = 2;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -44,29 +63,11 @@ __device__ __forceinline__ bf16x8 ones_bf16x8() {
     return as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));   // eight bf16 1.0
 }
 
-// ------------------------------------------------------------ bf16 prefix
-
-constexpr int kPrefixWaves = 4;      // waves per workgroup; their partials merge in LDS
-
-// ------------------------------------------------------------ split-K plan
-//
-// The prefix lengths live on the device, so the split of the committed
-// prefixes into chunks is derived there, from kv_len, by every prefix
-// workgroup and by the combine alike.  Work items (sequence b, head h,
-// chunk c) are numbered consecutively, sequence-major:
-//   item = base_b + h * n_b + c,  n_b = ceil(tiles_b / ct),
-//   base_b = H * (n_0 + ... + n_{b-1}),
-// with ct = max(ct_min, ceil(H * sum_b tiles_b / target)) tiles per chunk.
-// Workgroup ids map one to one onto items and ids past the last item exit at
-// once: real work occupies consecutive ids whatever the lengths, and since the
-// dispatcher deals consecutive ids round-robin to the XCDs, every XCD gets an
-// even share of a ragged batch.  The number of items never exceeds
-// target + nb * H.  Partials: item i at index i; the block part of (b, h) at
-// index tail_base + b * H + h.
+constexpr int kPrefixWaves = 4;      // waves per streaming workgroup
 
 // Committed length of sequence b as the attention reads it: kv_len clamped to
 // [0, lim], lim = min(kv_cap, max_kv_len), so that a length above the host's
-// bound can never yield more work items or chunks than the host planned for.
+// bound can never yield more work than the host planned for.
 __device__ __forceinline__ int prefix_len(const int32_t* kv_len, int b, int lim) {
     const int L = kv_len[b];
     return L < 0 ? 0 : (L > lim ? lim : L);
@@ -76,40 +77,93 @@ __device__ __forceinline__ int prefix_tiles(const int32_t* kv_len, int b, int li
     return (prefix_len(kv_len, b, lim) + kTile - 1) / kTile;
 }
 
-__device__ __forceinline__ int split_ct(const int32_t* kv_len, int nb, int H, int lim, int ct_min, int target) {
-    long long w = 0;
-    for (int b = 0; b < nb; ++b) w += prefix_tiles(kv_len, b, lim);
-    w *= H;
-    const long long ct = (w + target - 1) / target;
-    return ct > ct_min ? (int)ct : ct_min;
+// ------------------------------------------------------------- work list
+//
+// Derived on the device from kv_len, identically by the streaming kernels
+// and the combine.  With W = H * sum_b tiles_b and R resident slots,
+// c0 = max(kChunkMin, ceil(W / 2R)) and np = the number of phases whose chunk
+// c0 >> p stays >= kChunkMin (at most kPhaseMax).  Phase p of a prefix of T
+// tiles covers [T - (T >> p), T - (T >> (p+1))) (the last phase runs to T)
+// in chunks of c0 >> p tiles.  Items are numbered phase-major, then by
+// sequence, head and chunk:
+//   item = base_p + H * sum_{b' < b} n(p, b') + h * n(p, b) + j,
+// n(p, b) = ceil(phase length / chunk).  Item i writes partial i.  Every
+// phase holds at most 2R + 2 nb H items (the last one 4R + nb H), which is
+// the bound the host sizes the workspace with.
+
+constexpr int kChunkMin = 32;        // smallest item (tiles): eight per wave
+constexpr int kPhaseMax = 8;
+
+struct WorkList {
+    int nb, H, lim, c0, np;
+};
+
+__host__ __device__ inline long long worklist_c0(long long total_tiles, int resident) {
+    const long long half = 2LL * (resident > 0 ? resident : 1);
+    long long c0 = (total_tiles + half - 1) / half;
+    if (c0 < kChunkMin) c0 = kChunkMin;
+    if (c0 > (1LL << 28)) c0 = 1LL << 28;
+    return c0;
 }
 
-// Locate work item `id`; false past the last item.
-__device__ __forceinline__ bool split_item(const int32_t* kv_len, int nb, int H, int lim, int ct, int id,
-                                           int& b, int& h, int& chunk) {
-    int base = 0;
-    for (int bb = 0; bb < nb; ++bb) {
-        const int n = (prefix_tiles(kv_len, bb, lim) + ct - 1) / ct;
-        if (id < base + n * H) {
-            const int r = id - base;
-            b = bb;
-            h = r / n;
-            chunk = r - h * n;
-            return true;
+__host__ __device__ inline int worklist_np(long long c0) {
+    int np = 1;
+    while (np < kPhaseMax && (c0 >> np) >= kChunkMin) ++np;
+    return np;
+}
+
+__device__ __forceinline__ WorkList make_worklist(const int32_t* kv_len, int nb, int H, int lim, int resident) {
+    long long tot = 0;
+    for (int b = 0; b < nb; ++b) tot += prefix_tiles(kv_len, b, lim);
+    const long long c0 = worklist_c0(tot * H, resident);
+    return WorkList{nb, H, lim, (int)c0, worklist_np(c0)};
+}
+
+__device__ __forceinline__ int phase_chunk(const WorkList& w, int p) { return w.c0 >> p; }
+
+__device__ __forceinline__ void phase_range(const WorkList& w, int T, int p, int& s, int& e) {
+    s = T - (T >> p);
+    e = p + 1 < w.np ? T - (T >> (p + 1)) : T;
+}
+
+__device__ __forceinline__ int phase_items(const WorkList& w, int T, int p) {
+    int s, e;
+    phase_range(w, T, p, s, e);
+    const int c = phase_chunk(w, p);
+    return (e - s + c - 1) / c;
+}
+
+__device__ __forceinline__ long long work_count(const int32_t* kv_len, const WorkList& w) {
+    long long n = 0;
+    for (int p = 0; p < w.np; ++p)
+        for (int b = 0; b < w.nb; ++b) n += (long long)phase_items(w, prefix_tiles(kv_len, b, w.lim), p) * w.H;
+    return n;
+}
+
+// Locate item `item`: sequence b, head h, tiles [t0, t1); false past the last item.
+__device__ __forceinline__ bool work_item(const int32_t* kv_len, const WorkList& w, long long item,
+                                          int& b, int& h, int& t0, int& t1) {
+    for (int p = 0; p < w.np; ++p) {
+        for (int bb = 0; bb < w.nb; ++bb) {
+            const int T = prefix_tiles(kv_len, bb, w.lim);
+            const int n = phase_items(w, T, p);
+            const long long cnt = (long long)n * w.H;
+            if (item < cnt) {
+                b = bb;
+                h = (int)(item / n);
+                const int j = (int)(item - (long long)h * n);
+                int s, e;
+                phase_range(w, T, p, s, e);
+                t0 = s + j * phase_chunk(w, p);
+                t1 = min(t0 + phase_chunk(w, p), e);
+                return true;
+            }
+            item -= cnt;
         }
-        base += n * H;
     }
     return false;
 }
 
-template <int DH, int NQT>
-__host__ __device__ constexpr size_t prefix_merge_floats() {
-    // per merged wave: O^T accumulators (16*NQT queries x DH), running max, normaliser
-    return (size_t)NQT * 16 * DH + 2 * NQT * 16;
-}
-
-// Per-wave register state of the prefix kernel: queries (B operands), the
-// O^T accumulators, running max (log2 units) and lane-partial normaliser.
 template <int DH, int NQT>
 struct PrefixAcc {
     bf16x8 q[NQT][DH / 32];
@@ -204,232 +258,147 @@ __device__ __forceinline__ void consume_tile(PrefixAcc<DH, NQT>& a, KvTile<DH>& 
 }
 
 
-// One prefix workgroup: chunk `chunk` of head h of sequence b, all nq queries.
-// Partials: part_o [item][nq][DH], part_ml [item][nq][2].
-template <int DH, int NQT>
-__device__ __forceinline__ void prefix_block(
-    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int L,
-    const uint16_t* __restrict__ q, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int H, int kv_cap, int nq, int chunk_tiles, int item, float scale_log2,
-    int chunk, int h, int b, float* merge)
+// ------------------------------------------------ fused kernel (one query tile)
+
+template <int DH>
+__host__ __device__ constexpr size_t prefix_merge_floats() {
+    // per merged wave: O^T accumulators (16 queries x DH), running max, normaliser
+    return (size_t)16 * DH + 2 * 16;
+}
+
+struct StreamArgs {
+    const uint16_t *kc, *vc, *q; const int32_t* kv_len;
+    float *part_o, *part_ml;
+    unsigned* ticket;                  // the job queue's counter (zeroed before the launch)
+    int H, kv_cap, kv_lim, nq, nb, resident;
+    float scale_log2;
+};
+
+// One prefix item of the one-tile kernel: tiles [t0, t1) of head h of sequence
+// b, all nq <= 16 queries, written to partial `slot`.  The four waves take
+// contiguous runs of the item; each streams its run with the next two tiles'
+// loads in flight while the current tile is consumed.  The waves' states
+// merge in LDS in a fixed order.  Every wave returns (no early exit): the
+// caller's barriers stay matched.
+template <int DH>
+__device__ __forceinline__ void prefix_item(const StreamArgs& A, int b, int h, int t0, int t1, long long slot,
+                                            float* merge, unsigned& next)
 {
-    constexpr int J = DH / 32;          // k-steps of the score product
-    constexpr int DT = DH / 16;         // 16-wide output tiles of the value product
-    constexpr int KV4 = 4 * DH;         // uint4 per tile (32 keys x DH bf16)
-    constexpr size_t MF = prefix_merge_floats<DH, NQT>();
-
-    const int tiles = (L + kTile - 1) / kTile;
-    const int t0 = chunk * chunk_tiles;
-    if (t0 >= tiles) return;                           // whole workgroup
-    const int t1 = min(t0 + chunk_tiles, tiles);
-    const int wave = threadIdx.x >> 6;
+    constexpr int J = DH / 32, DT = DH / 16, KV4 = 4 * DH;
+    constexpr size_t MF = prefix_merge_floats<DH>();
+    const int L = prefix_len(A.kv_len, b, A.kv_lim);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
     const int per = (t1 - t0 + kPrefixWaves - 1) / kPrefixWaves;
-    const int w0 = min(t0 + wave * per, t1), w1 = min(w0 + per, t1);   // wave 0 is never empty
-    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+    const int w0 = min(t0 + wave * per, t1), w1 = min(w0 + per, t1);
 
-    PrefixAcc<DH, NQT> a;
-    // queries as B operands: lane (g, n) holds Q[16nt+n][32j+8g .. 32j+8g+7]
+    PrefixAcc<DH, 1> a;
 #pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) {
-        const int qi = 16 * nt + n;
+    for (int j = 0; j < J; ++j) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (n < A.nq) v = *(const uint4*)(A.q + (((size_t)b * A.nq + n) * A.H + h) * DH + 32 * j + 8 * g);
+        a.q[0][j] = as_bf16x8(v);
+    }
+    a.m[0] = -INFINITY;
+    a.l[0] = 0.f;
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (qi < nq) v = *(const uint4*)(q + (((size_t)b * nq + qi) * H + h) * DH + 32 * j + 8 * g);
-            a.q[nt][j] = as_bf16x8(v);
+    for (int t = 0; t < DT; ++t) a.o[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const size_t slab = ((size_t)b * A.H + h) * (size_t)(A.kv_cap / kTile) * KV4;
+    const uint4* kp = (const uint4*)A.kc + slab;
+    const uint4* vp = (const uint4*)A.vc + slab;
+    if (w0 < w1) {
+        // three register buffers, two tiles in flight ahead of the one consumed; the loads
+        // inside the loop are unconditional, so the compiler's waits are exact
+        KvTile<DH> ta, tb, tc;
+        int T = w0;
+        load_tile<DH>(ta, kp, vp, T, lane);
+        if (T + 1 < w1) load_tile<DH>(tb, kp, vp, T + 1, lane);
+        for (; T + 4 < w1; T += 3) {
+            load_tile<DH>(tc, kp, vp, T + 2, lane);
+            consume_tile<DH, 1>(a, ta, T, L, g, A.scale_log2);
+            load_tile<DH>(ta, kp, vp, T + 3, lane);
+            consume_tile<DH, 1>(a, tb, T + 1, L, g, A.scale_log2);
+            load_tile<DH>(tb, kp, vp, T + 4, lane);
+            consume_tile<DH, 1>(a, tc, T + 2, L, g, A.scale_log2);
         }
-        a.m[nt] = -INFINITY;
-        a.l[nt] = 0.f;
-#pragma unroll
-        for (int t = 0; t < DT; ++t) a.o[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // 1..4 tiles left: T (in ta) and T+1 (in tb) are already loaded where they exist
+        const int left = w1 - T;
+        if (left >= 3) load_tile<DH>(tc, kp, vp, T + 2, lane);
+        consume_tile<DH, 1>(a, ta, T, L, g, A.scale_log2);
+        if (left >= 4) load_tile<DH>(ta, kp, vp, T + 3, lane);
+        if (left >= 2) consume_tile<DH, 1>(a, tb, T + 1, L, g, A.scale_log2);
+        if (left >= 3) consume_tile<DH, 1>(a, tc, T + 2, L, g, A.scale_log2);
+        if (left >= 4) consume_tile<DH, 1>(a, ta, T + 3, L, g, A.scale_log2);
     }
 
-    const size_t slab = ((size_t)b * H + h) * (size_t)(kv_cap / kTile) * KV4;
-    const uint4* kp = (const uint4*)kc + slab;
-    const uint4* vp = (const uint4*)vc + slab;
-    KvTile<DH> cur, nxt;
-    if (w0 < w1) load_tile<DH>(cur, kp, vp, w0, lane);
-    for (int T = w0; T < w1; ++T) {
-        const bool more = T + 1 < w1;
-        if (more) load_tile<DH>(nxt, kp, vp, T + 1, lane);
-        consume_tile<DH, NQT>(a, cur, T, L, g, scale_log2);
-        if (more) cur = nxt;
-    }
+    // the next ticket is taken once this item's loads are done: taken earlier, it would
+    // hold the next item back for as long as this one still runs
+    if (threadIdx.x == 0) next = atomicAdd(A.ticket, 1u);
 
-    // merge the four waves' partial softmax states in LDS (fixed order: wave 0, 1, 2, 3)
+    // merge the four waves' states in LDS (fixed order: wave 0, 1, 2, 3); an empty run
+    // contributes m = -inf, l = 0, O = 0
     if (wave > 0) {
         float* mw = merge + (size_t)(wave - 1) * MF;
 #pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) {
-#pragma unroll
-            for (int t = 0; t < DT; ++t)
-                *(float4*)(mw + (((size_t)nt * DT + t) * 64 + lane) * 4) =
-                    make_float4(a.o[t][nt][0], a.o[t][nt][1], a.o[t][nt][2], a.o[t][nt][3]);
-            if (g == 0) {
-                mw[(size_t)NQT * 16 * DH + nt * 16 + n] = a.m[nt];
-                mw[(size_t)NQT * 16 * DH + NQT * 16 + nt * 16 + n] = a.l[nt];
-            }
+        for (int t = 0; t < DT; ++t)
+            *(float4*)(mw + ((size_t)t * 64 + lane) * 4) = make_float4(a.o[t][0][0], a.o[t][0][1], a.o[t][0][2], a.o[t][0][3]);
+        if (g == 0) {
+            mw[16 * DH + n] = a.m[0];
+            mw[16 * DH + 16 + n] = a.l[0];
         }
     }
     __syncthreads();
-    if (wave > 0) return;
-
-    const size_t pbase = (size_t)item * nq;
+    if (wave == 0) {
+        const size_t pbase = (size_t)slot * A.nq;
+        float M = a.m[0];
 #pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) {
-        float M = a.m[nt];
-#pragma unroll
-        for (int w = 1; w < kPrefixWaves; ++w) M = fmaxf(M, merge[(w - 1) * MF + (size_t)NQT * 16 * DH + nt * 16 + n]);
+        for (int w = 1; w < kPrefixWaves; ++w) M = fmaxf(M, merge[(w - 1) * MF + 16 * DH + n]);
         float sc[kPrefixWaves];
-        sc[0] = __builtin_amdgcn_exp2f(a.m[nt] - M);
-        float l = sc[0] * a.l[nt];
+        sc[0] = __builtin_amdgcn_exp2f(a.m[0] - M);
+        float l = sc[0] * a.l[0];
 #pragma unroll
         for (int w = 1; w < kPrefixWaves; ++w) {
             const float* mw = merge + (size_t)(w - 1) * MF;
-            sc[w] = __builtin_amdgcn_exp2f(mw[(size_t)NQT * 16 * DH + nt * 16 + n] - M);
-            l = fmaf(sc[w], mw[(size_t)NQT * 16 * DH + NQT * 16 + nt * 16 + n], l);
+            sc[w] = __builtin_amdgcn_exp2f(mw[16 * DH + n] - M);
+            l = fmaf(sc[w], mw[16 * DH + 16 + n], l);
         }
-        const int qi = 16 * nt + n;
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-            f32x4 acc = a.o[t][nt] * sc[0];
+            f32x4 acc = a.o[t][0] * sc[0];
 #pragma unroll
             for (int w = 1; w < kPrefixWaves; ++w) {
-                const float4 o = *(const float4*)(merge + (size_t)(w - 1) * MF + (((size_t)nt * DT + t) * 64 + lane) * 4);
+                const float4 o = *(const float4*)(merge + (size_t)(w - 1) * MF + ((size_t)t * 64 + lane) * 4);
                 acc[0] = fmaf(sc[w], o.x, acc[0]);
                 acc[1] = fmaf(sc[w], o.y, acc[1]);
                 acc[2] = fmaf(sc[w], o.z, acc[2]);
                 acc[3] = fmaf(sc[w], o.w, acc[3]);
             }
-            if (qi < nq) *(float4*)(part_o + (pbase + qi) * DH + 16 * t + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            if (n < A.nq) *(float4*)(A.part_o + (pbase + n) * DH + 16 * t + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
-        if (qi < nq && g == 0) *(float2*)(part_ml + (pbase + qi) * 2) = make_float2(M, l);
+        if (n < A.nq && g == 0) *(float2*)(A.part_ml + (pbase + n) * 2) = make_float2(M, l);
     }
 }
 
-// ------------------------------------------------------------- block part
-//
-// One workgroup per (sequence, candidate, head): the P block queries attend
-// causally to the block's own keys (query i sees keys 0..i), in fp32.  The
-// result is one more partial softmax state, at index tail_base + b * H + h.
-
-constexpr int kMaxP = 64;
-
-// LDS floats of the block part: scores [P][P+1], row max and sum, and the
-// q and k rows of the block staged as raw activations
-__host__ __device__ constexpr size_t tail_lds_floats(int P, int DH, int act_bytes) {
-    return (size_t)P * (P + 1) + 2 * P + ((size_t)2 * P * DH * act_bytes + 3) / 4;
-}
-
-template <int ACT>
-__device__ __forceinline__ void tail_block(
-    const typename Act<ACT>::T* __restrict__ q, const typename Act<ACT>::T* __restrict__ kb,
-    const typename Act<ACT>::T* __restrict__ vb, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int H, int DH, int P, int nq, int tail_base, float scale_log2, int c, int h, int b, float* lds)
+// Persistent workgroup of the one-tile kernel: prefix items from the queue.
+template <int DH>
+__global__ __launch_bounds__(kRoleT, kSlotsFused) void k_verify_stream(StreamArgs A)
 {
-    typedef typename Act<ACT>::T T;
-    float* S = lds;                                   // [P][P + 1] scores, then weights
-    float* mrow = S + P * (P + 1);                    // [P]
-    float* lrow = mrow + P;                           // [P]
-    T* qs = (T*)(lrow + P);                           // [P][DH]
-    T* ks = qs + (size_t)P * DH;                      // [P][DH]
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    const size_t row0 = (size_t)b * nq + (size_t)c * P;          // block row of position 0
-    for (int e = tid; e < P * DH; e += nthr) {
-        const int i = e / DH, dd = e % DH;
-        const size_t o = ((row0 + i) * H + h) * DH + dd;
-        qs[e] = q[o];
-        ks[e] = kb[o];
-    }
+    __shared__ float merge[(kPrefixWaves - 1) * prefix_merge_floats<DH>()];
+    __shared__ unsigned s_ticket;
+    const WorkList w = make_worklist(A.kv_len, A.nb, A.H, A.kv_lim, A.resident);
+    const long long total = work_count(A.kv_len, w);
+    if (threadIdx.x == 0) s_ticket = atomicAdd(A.ticket, 1u);
     __syncthreads();
-    // scores s_ij = q_i . k_j * scale (log2 units), j <= i
-    const int npairs = P * (P + 1) / 2;
-    for (int p = tid; p < npairs; p += nthr) {
-        int i = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-        while ((i + 1) * (i + 2) / 2 <= p) ++i;
-        while (i * (i + 1) / 2 > p) --i;
-        const int j = p - i * (i + 1) / 2;
-        float acc = 0.f;
-        for (int dd = 0; dd < DH; ++dd) acc = fmaf(Act<ACT>::load(qs, (size_t)i * DH + dd), Act<ACT>::load(ks, (size_t)j * DH + dd), acc);
-        S[i * (P + 1) + j] = acc * scale_log2;
+    for (;;) {
+        const long long t = s_ticket;
+        __syncthreads();                               // every wave has read the ticket
+        if (t >= total) break;
+        unsigned next = 0xffffffffu;                   // past the end unless the item takes a ticket
+        int b = 0, h = 0, t0 = 0, t1 = 0;
+        if (work_item(A.kv_len, w, t, b, h, t0, t1)) prefix_item<DH>(A, b, h, t0, t1, t, merge, next);
+        if (threadIdx.x == 0) s_ticket = next;
+        __syncthreads();
     }
-    __syncthreads();
-    if (tid < P) {
-        const int i = tid;
-        float m = -INFINITY;
-        for (int j = 0; j <= i; ++j) m = fmaxf(m, S[i * (P + 1) + j]);
-        float l = 0.f;
-        for (int j = 0; j <= i; ++j) {
-            const float w = __builtin_amdgcn_exp2f(S[i * (P + 1) + j] - m);
-            S[i * (P + 1) + j] = w;
-            l += w;
-        }
-        mrow[i] = m;
-        lrow[i] = l;
-    }
-    __syncthreads();
-    const size_t pbase = ((size_t)tail_base + (size_t)b * H + h) * nq + (size_t)c * P;
-    for (int e = tid; e < P * DH; e += nthr) {
-        const int i = e / DH, dd = e % DH;
-        float acc = 0.f;
-        for (int j = 0; j <= i; ++j)
-            acc = fmaf(S[i * (P + 1) + j], Act<ACT>::load(vb, ((row0 + j) * H + h) * DH + dd), acc);
-        part_o[(pbase + i) * DH + dd] = acc;
-    }
-    for (int i = tid; i < P; i += nthr) *(float2*)(part_ml + (pbase + i) * 2) = make_float2(mrow[i], lrow[i]);
-}
-
-// ------------------------------------------------------ fused bf16 kernel
-
-struct StreamArgs {
-    // conv / IIR
-    const float *w_short, *w_outer, *lam, *beta, *cc;
-    const uint16_t* short_win; const float* outer_win; const float* iir; const uint16_t* x;
-    float* f_out; float* s_out; uint16_t* y_out;
-    int d, Ts, To, N;
-    // attention
-    const uint16_t *kc, *vc, *q, *kb, *vb; const int32_t* kv_len;
-    float *part_o, *part_ml;
-    int H, kv_cap, kv_lim, nq, nb, ct_min, target, tail_base, P, nc;
-    float scale_log2;
-    // role layout: prefix workgroups first (one per possible work item), then conv, then the block part
-    int prefix_blocks, n_conv, n_tail;
-};
-
-// The short roles of a streaming kernel, workgroup r past the prefix items:
-// first the conv/IIR scan of 16 channels of one sequence (all its
-// candidates), then the causal block part of one (sequence, candidate, head).
-__device__ __forceinline__ void short_role(const StreamArgs& A, int r, int DH, float* lds)
-{
-    if (r < A.n_conv) {
-        const int groups = (A.d + kCG - 1) / kCG;
-        const int cgi = r % groups, b = r / groups;
-        conv_iir_block<HCI_BF16>(A.w_short, A.w_outer, A.lam, A.beta, A.cc, A.short_win, A.outer_win, A.iir, A.x,
-                                 A.f_out, A.s_out, A.y_out, A.d, A.Ts, A.To, A.N, A.nc, A.P, cgi, b, lds);
-        return;
-    }
-    const int t = r - A.n_conv;
-    const int h = t % A.H, c = (t / A.H) % A.nc, b = t / (A.H * A.nc);
-    tail_block<HCI_BF16>(A.q, A.kb, A.vb, A.part_o, A.part_ml, A.H, DH, A.P, A.nq, A.tail_base,
-                         A.scale_log2, c, h, b, lds);
-}
-
-template <int DH, int NQT>
-__global__ __launch_bounds__(kRoleT) void k_verify_stream(StreamArgs A)
-{
-    extern __shared__ float lds[];
-    const int id = blockIdx.x;
-    if (id < A.prefix_blocks) {
-        const int ct = split_ct(A.kv_len, A.nb, A.H, A.kv_lim, A.ct_min, A.target);
-        int b, h, chunk;
-        if (!split_item(A.kv_len, A.nb, A.H, A.kv_lim, ct, id, b, h, chunk)) return;
-        const int L = prefix_len(A.kv_len, b, A.kv_lim);
-        prefix_block<DH, NQT>(A.kc, A.vc, L, A.q, A.part_o, A.part_ml, A.H, A.kv_cap, A.nq, ct, id,
-                              A.scale_log2, chunk, h, b, lds);
-        return;
-    }
-    // the short roles come last: they fill the slots the KV stream frees as it drains
-    short_role(A, id - A.prefix_blocks, DH, lds);
 }
 
 // ------------------------------------------- several query tiles per prefix
@@ -446,9 +415,10 @@ __global__ __launch_bounds__(kRoleT) void k_verify_stream(StreamArgs A)
 // vector-memory count (loads complete in issue order); the barrier that
 // follows publishes the tile to the other waves and also marks the stage
 // read last time as free, so it is refilled as soon as the operands of the
-// current tile are in registers.
+// current tile are in registers.  Nothing else is in flight while the stages
+// fill: the next ticket is taken after an item's last tile.
 
-constexpr int kStages = 4;
+constexpr int kStages = 4;            // LDS stages of the several-tile kernel (16 KB each at Dh = 128; two workgroups per CU)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -488,116 +458,105 @@ __global__ __launch_bounds__(kRoleT) void k_attn_prefix_shared(StreamArgs A, int
     constexpr int PER = TU / kRoleT;                   // direct loads per thread per tile
     static_assert(TU % kRoleT == 0 && KV4 % 64 == 0, "a tile splits into wave-wide loads");
     __shared__ uint4 stage[kStages][TU];
-    uint4 *st0 = stage[0], *st1 = stage[1], *st2 = stage[2], *st3 = stage[3];
-    const int id = blockIdx.x;
-    if (id >= A.prefix_blocks) {
-        // the short roles ride at the end of the grid (the host lets them only when their
-        // LDS fits the stages) and fill the slots the KV stream frees as it drains
-        short_role(A, id - A.prefix_blocks, DH, (float*)&stage[0][0]);
-        return;
-    }
-    const int ct = split_ct(A.kv_len, A.nb, A.H, A.kv_lim, A.ct_min, A.target);
-    int b, h, chunk;
-    if (!split_item(A.kv_len, A.nb, A.H, A.kv_lim, ct, id, b, h, chunk)) return;   // whole workgroup
-    const int L = prefix_len(A.kv_len, b, A.kv_lim);
-    const int tiles = (L + kTile - 1) / kTile;
-    const int t0 = chunk * ct;
-    if (t0 >= tiles) return;                           // cannot happen for an item; kept as a guard
-    const int t1 = min(t0 + ct, tiles);
+    __shared__ unsigned s_ticket;
+    static_assert(kStages >= 3 && kStages <= 8, "the waits cover up to six tiles in flight");
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
     const bool has_q = wave < nqt;
-
-    PrefixAcc<DH, 1> a;
-    {
-        const int qi = 16 * wave + n;
-#pragma unroll
-        for (int j = 0; j < DH / 32; ++j) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (has_q && qi < A.nq) v = *(const u32x4*)(A.q + (((size_t)b * A.nq + qi) * A.H + h) * DH + 32 * j + 8 * g);
-            // the query loads complete here, before any direct load is issued: the compiler
-            // then has no load of its own pending inside the pipeline below
-            asm volatile("" : "+v"(v));
-            a.q[0][j] = __builtin_bit_cast(bf16x8, v);
-        }
-        a.m[0] = -INFINITY;
-        a.l[0] = 0.f;
-#pragma unroll
-        for (int t = 0; t < DH / 16; ++t) a.o[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    const size_t slab = ((size_t)b * A.H + h) * (size_t)(A.kv_cap / kTile) * KV4;
-    const uint4* kp = (const uint4*)A.kc + slab;
-    const uint4* vp = (const uint4*)A.vc + slab;
-
-    auto issue = [&](uint4* dst, int T) {
-        const size_t base = (size_t)T * KV4;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = tid + kRoleT * i;            // wave-uniform K/V choice: KV4 is a multiple of 64
-            const uint4* src = e < KV4 ? kp + base + e : vp + base + (e - KV4);
-            dma16_nt(src, dst + (e & ~63));
-        }
-    };
-    auto step = [&](const uint4* cur, uint4* refill, int T) {
-        // loads issued after tile T's: tiles T+1 and T+2, where they exist
-        const int later = min(t1 - 1 - T, kStages - 2);
-        if (later >= 2) HCI_WAIT_VM(2 * PER);
-        else if (later == 1) HCI_WAIT_VM(PER);
-        else HCI_WAIT_VM(0);
-        lds_read_barrier();                            // tile T complete for every wave; tile T-1 read by all
-        KvTile<DH> t;
-        if (has_q) {
-#pragma unroll
-            for (int i = 0; i < DH / 16; ++i) t.k[i] = cur[i * 64 + lane];
-#pragma unroll
-            for (int i = 0; i < DH / 16; ++i) t.v[i] = cur[KV4 + i * 64 + lane];
-        }
-        // refill after the operand reads: the compiler then has no direct load to order them against
-        if (T + kStages - 1 < t1) issue(refill, T + kStages - 1);
-        if (has_q) consume_tile<DH, 1>(a, t, T, L, g, A.scale_log2);
-    };
-    issue(st0, t0);
-    if (t0 + 1 < t1) issue(st1, t0 + 1);
-    if (t0 + 2 < t1) issue(st2, t0 + 2);
-    for (int T = t0; T < t1; T += kStages) {
-        step(st0, st3, T);
-        if (T + 1 >= t1) break;
-        step(st1, st0, T + 1);
-        if (T + 2 >= t1) break;
-        step(st2, st1, T + 2);
-        if (T + 3 >= t1) break;
-        step(st3, st2, T + 3);
-    }
-    // the last step waited for every direct load: no LDS write is pending at exit
-    if (!has_q) return;
     const int qi = 16 * wave + n;
-    if (qi >= A.nq) return;
-    const size_t pbase = (size_t)id * A.nq;
+    const WorkList w = make_worklist(A.kv_len, A.nb, A.H, A.kv_lim, A.resident);
+    const long long total = work_count(A.kv_len, w);
+    if (tid == 0) s_ticket = atomicAdd(A.ticket, 1u);
+    __syncthreads();
+    for (;;) {
+        const long long t = s_ticket;
+        __syncthreads();                               // every wave has read the ticket
+        if (t >= total) break;
+        int b = 0, h = 0, t0 = 0, t1 = 0;
+        if (work_item(A.kv_len, w, t, b, h, t0, t1)) {
+            const int L = prefix_len(A.kv_len, b, A.kv_lim);
+            PrefixAcc<DH, 1> a;
 #pragma unroll
-    for (int t = 0; t < DH / 16; ++t)
-        *(float4*)(A.part_o + (pbase + qi) * DH + 16 * t + 4 * g) =
-            make_float4(a.o[t][0][0], a.o[t][0][1], a.o[t][0][2], a.o[t][0][3]);
-    if (g == 0) *(float2*)(A.part_ml + (pbase + qi) * 2) = make_float2(a.m[0], a.l[0]);
-}
+            for (int j = 0; j < DH / 32; ++j) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (has_q && qi < A.nq) v = *(const u32x4*)(A.q + (((size_t)b * A.nq + qi) * A.H + h) * DH + 32 * j + 8 * g);
+                // the query loads complete here, before any direct load is issued: the compiler
+                // then has no load of its own pending inside the pipeline below
+                asm volatile("" : "+v"(v));
+                a.q[0][j] = __builtin_bit_cast(bf16x8, v);
+            }
+            a.m[0] = -INFINITY;
+            a.l[0] = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < DH / 16; ++tt) a.o[tt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const size_t slab = ((size_t)b * A.H + h) * (size_t)(A.kv_cap / kTile) * KV4;
+            const uint4* kp = (const uint4*)A.kc + slab;
+            const uint4* vp = (const uint4*)A.vc + slab;
 
-// -------------------------------------------------- stand-alone fp32 parts
-
-template <int ACT>
-__global__ __launch_bounds__(kRoleT) void k_attn_tail(
-    const typename Act<ACT>::T* __restrict__ q, const typename Act<ACT>::T* __restrict__ kb,
-    const typename Act<ACT>::T* __restrict__ vb, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int H, int DH, int P, int nq, int tail_base, float scale_log2)
-{
-    extern __shared__ float lds[];
-    tail_block<ACT>(q, kb, vb, part_o, part_ml, H, DH, P, nq, tail_base, scale_log2,
-                    blockIdx.y, blockIdx.x, blockIdx.z, lds);
+            auto issue = [&](uint4* dst, int T) {
+                const size_t base = (size_t)T * KV4;
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int e = tid + kRoleT * i;    // wave-uniform K/V choice: KV4 is a multiple of 64
+                    const uint4* src = e < KV4 ? kp + base + e : vp + base + (e - KV4);
+                    dma16_nt(src, dst + (e & ~63));
+                }
+            };
+            auto wait_later = [&](int later) {             // leave `later` tiles' loads in flight
+                switch (later) {
+                    case 0: HCI_WAIT_VM(0); break;
+                    case 1: HCI_WAIT_VM(1 * PER); break;
+                    case 2: HCI_WAIT_VM(2 * PER); break;
+                    case 3: HCI_WAIT_VM(3 * PER); break;
+                    case 4: HCI_WAIT_VM(4 * PER); break;
+                    case 5: HCI_WAIT_VM(5 * PER); break;
+                    default: HCI_WAIT_VM(6 * PER); break;
+                }
+            };
+            auto step = [&](const uint4* cur, uint4* refill, int T) {
+                // loads issued after tile T's: tiles T+1 .. T+kStages-2, where they exist
+                wait_later(min(t1 - 1 - T, kStages - 2));
+                lds_read_barrier();                    // tile T complete for every wave; tile T-1 read by all
+                KvTile<DH> tl;
+                if (has_q) {
+#pragma unroll
+                    for (int i = 0; i < DH / 16; ++i) tl.k[i] = cur[i * 64 + lane];
+#pragma unroll
+                    for (int i = 0; i < DH / 16; ++i) tl.v[i] = cur[KV4 + i * 64 + lane];
+                }
+                // refill after the operand reads: the compiler then has no direct load to order them against
+                if (T + kStages - 1 < t1) issue(refill, T + kStages - 1);
+                if (has_q) consume_tile<DH, 1>(a, tl, T, L, g, A.scale_log2);
+            };
+            for (int i = 0; i < kStages - 1; ++i)
+                if (t0 + i < t1) issue(stage[i], t0 + i);
+            int cur = 0;
+            for (int T = t0; T < t1; ++T) {
+                // the stage read one step earlier is free once this step's barrier has passed
+                step(stage[cur], stage[cur == 0 ? kStages - 1 : cur - 1], T);
+                cur = cur + 1 == kStages ? 0 : cur + 1;
+            }
+            // the last step waited for every direct load: no LDS write is pending here
+            if (has_q && qi < A.nq) {
+                const size_t pbase = (size_t)t * A.nq;
+#pragma unroll
+                for (int tt = 0; tt < DH / 16; ++tt)
+                    *(float4*)(A.part_o + (pbase + qi) * DH + 16 * tt + 4 * g) =
+                        make_float4(a.o[tt][0][0], a.o[tt][0][1], a.o[tt][0][2], a.o[tt][0][3]);
+                if (g == 0) *(float2*)(A.part_ml + (pbase + qi) * 2) = make_float2(a.m[0], a.l[0]);
+            }
+        }
+        if (tid == 0) s_ticket = atomicAdd(A.ticket, 1u);
+        __syncthreads();                               // the stages are free and the ticket is published
+    }
 }
 
 // ------------------------------------------------------------- f32 prefix
 //
-// fp32 layers (small shapes): 64 threads per work item (chunk, head, sequence).  The
-// tile is unpacked into LDS rows; thread tid scores query tid and accumulates
-// output dims tid and tid+64 of every query, all in fp32 on the vector ALUs.
-// Limits: Dh <= 128, nq <= 64.
+// fp32 layers (small shapes): 64 threads per work item, one item per
+// workgroup (grid = the host's bound on the items; workgroups past the last
+// item exit at once).  The tile is unpacked into LDS rows; thread tid scores
+// query tid and accumulates output dims tid and tid+64 of every query, all
+// in fp32 on the vector ALUs.  Limits: Dh <= 128, nq <= 64.
 
 constexpr int kF32Dh = 128;
 constexpr int kF32Nq = 64;
@@ -606,22 +565,18 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
     const float* __restrict__ kc, const float* __restrict__ vc,
     const int32_t* __restrict__ kv_len, const float* __restrict__ q,
     float* __restrict__ part_o, float* __restrict__ part_ml,
-    int nb, int H, int DH, int kv_cap, int kv_lim, int nq, int ct_min, int target, float scale_log2)
+    int nb, int H, int DH, int kv_cap, int kv_lim, int nq, int resident, float scale_log2)
 {
     __shared__ float ks[kTile][kF32Dh + 1];
     __shared__ float vs[kTile][kF32Dh + 1];
     __shared__ float ps[kF32Nq][kTile + 1];
     __shared__ float alpha_s[kF32Nq];
 
-    const int item = blockIdx.x;
-    const int chunk_tiles = split_ct(kv_len, nb, H, kv_lim, ct_min, target);
-    int b, h, chunk;
-    if (!split_item(kv_len, nb, H, kv_lim, chunk_tiles, item, b, h, chunk)) return;
+    const long long item = blockIdx.x;
+    const WorkList w = make_worklist(kv_len, nb, H, kv_lim, resident);
+    int b, h, t0, t1;
+    if (!work_item(kv_len, w, item, b, h, t0, t1)) return;
     const int L = prefix_len(kv_len, b, kv_lim);
-    const int tiles = (L + kTile - 1) / kTile;
-    const int t0 = chunk * chunk_tiles;
-    if (t0 >= tiles) return;
-    const int t1 = min(t0 + chunk_tiles, tiles);
     const int tid = threadIdx.x;
 
     float qr[kF32Dh];
@@ -637,32 +592,32 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
     for (int T = t0; T < t1; ++T) {
         __syncthreads();
         for (int e = tid; e < kTile * DH; e += 64) {
-            const int w = e / DH, dd = e % DH;
-            const int key = T * kTile + w;
+            const int wr = e / DH, dd = e % DH;
+            const int key = T * kTile + wr;
             const bool ok = key < L;
-            ks[w][dd] = ok ? kc[slab + k_elem(key, dd, DH)] : 0.f;
-            vs[w][dd] = ok ? vc[slab + v_elem(key, dd, DH)] : 0.f;
+            ks[wr][dd] = ok ? kc[slab + k_elem(key, dd, DH)] : 0.f;
+            vs[wr][dd] = ok ? vc[slab + v_elem(key, dd, DH)] : 0.f;
         }
         __syncthreads();
         if (tid < nq) {
             float sc[kTile];
             float mx = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < kTile; ++w) {
+            for (int wr = 0; wr < kTile; ++wr) {
                 float acc = 0.f;
 #pragma unroll
                 for (int dd = 0; dd < kF32Dh; ++dd)
-                    if (dd < DH) acc = fmaf(qr[dd], ks[w][dd], acc);
-                sc[w] = (T * kTile + w < L) ? acc * scale_log2 : -INFINITY;
-                mx = fmaxf(mx, sc[w]);
+                    if (dd < DH) acc = fmaf(qr[dd], ks[wr][dd], acc);
+                sc[wr] = (T * kTile + wr < L) ? acc * scale_log2 : -INFINITY;
+                mx = fmaxf(mx, sc[wr]);
             }
             const float mnew = fmaxf(mrun, mx);
             const float alpha = exp2f(mrun - mnew);
             float psum = 0.f;
 #pragma unroll
-            for (int w = 0; w < kTile; ++w) {
-                const float p = exp2f(sc[w] - mnew);
-                ps[tid][w] = p;
+            for (int wr = 0; wr < kTile; ++wr) {
+                const float p = exp2f(sc[wr] - mnew);
+                ps[tid][wr] = p;
                 psum += p;
             }
             lrun = fmaf(lrun, alpha, psum);
@@ -678,7 +633,7 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
                     const int dd = tid + 64 * r;
                     if (dd < DH) {
                         float acc = oacc[qi][r] * alpha_s[qi];
-                        for (int w = 0; w < kTile; ++w) acc = fmaf(ps[qi][w], vs[w][dd], acc);
+                        for (int wr = 0; wr < kTile; ++wr) acc = fmaf(ps[qi][wr], vs[wr][dd], acc);
                         oacc[qi][r] = acc;
                     }
                 }
@@ -702,247 +657,356 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
     }
 }
 
-// ----------------------------------------------------------------- combine
+// ------------------------------------------------------------------ finish
 //
-// One workgroup of 256 threads per (query, head, sequence) merges the chunk
-// partials (items base_b + h*n_b + 0..n_b-1, derived from kv_len exactly as the
-// prefix kernels derive them) and the block part:  M = max m_s, w_s = 2^(m_s - M),
-//   o = sum_s w_s O_s / sum_s w_s l_s,
-// with the chunks taken in a fixed interleave and the group sums merged in a
-// fixed order, so the result does not depend on scheduling.
+// The kernel that ends a verify, once the prefix stream is done and HBM is
+// quiet.  Its grid holds two kinds of workgroups:
+//   conv    the conv/IIR scan of 16 channels of one sequence (every
+//           candidate), conv_iir_body.h; it runs here rather than inside the
+//           stream because its chain of dependent loads is short only when
+//           the memory system is not saturated.
+//   combine RG block rows of one (sequence, candidate, head): the four waves
+//           each reduce a fixed subset of the prefix items of (b, h) (item j
+//           of a phase goes to wave j mod 4) into a running softmax state per
+//           row; then each row's causal block part (query i against the
+//           block's own keys 0..i, fp32, from K/V rows staged in LDS) is
+//           computed by one wave, and the five states of a row merge in a
+//           fixed order:
+//             M = max m_s,  o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Lane l holds output dims l and l + 64.  RG (1..16 rows) is chosen by the
+// host so that the grid has a few workgroups per CU.
 
 constexpr int kCombT = 256;
-constexpr int kMaxChunks = 4096;     // the split-K plan never exceeds this
+constexpr int kCombW = kCombT / 64;
 
-template <int ACT>
-__global__ __launch_bounds__(kCombT) void k_attn_combine(
-    const int32_t* __restrict__ kv_len, const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    typename Act<ACT>::T* __restrict__ o,
-    int nb, int H, int DH, int nq, int kv_lim, int ct_min, int target, int tail_base)
+struct FinishArgs {
+    // conv / IIR
+    const float *w_short, *w_outer, *lam, *beta, *cc;
+    const void* short_win; const float* outer_win; const float* iir; const void* x;
+    float* f_out; float* s_out; void* y_out;
+    int d, Ts, To, N, nc, n_conv;
+    // combine
+    const int32_t* kv_len; const float *part_o, *part_ml;
+    const void *q, *kb, *vb; void* o;
+    int nb, H, DH, nq, P, kv_lim, resident, rg_count;
+    float scale_log2;
+};
+
+// dynamic LDS floats of the combine role: the candidate's block K and V rows (raw
+// activations), then per row and state (four waves + the block part) O [Dh] and (m, l)
+__host__ __device__ inline size_t combine_lds_floats(int P, int DH, int act_bytes, int RG) {
+    return ((size_t)2 * P * DH * act_bytes + 3) / 4 + (size_t)(kCombW + 1) * RG * (DH + 2);
+}
+
+template <int ACT, int RG>
+__device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, int h, int b, float* lds)
 {
-    __shared__ float wts[kMaxChunks + 1];
-    __shared__ float red[kCombT / 64][2];
-    __shared__ float acc_s[kCombT];
+    typedef typename Act<ACT>::T T;
+    const T* q = (const T*)A.q;
+    const T* kb = (const T*)A.kb;
+    const T* vb = (const T*)A.vb;
+    const int DH = A.DH, nq = A.nq, H = A.H, P = A.P;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int d0 = lane, d1 = lane + 64;
+    const bool ok0 = d0 < DH, ok1 = d1 < DH;
+    const int i0 = rg * RG, nr = min(RG, P - i0);      // rows i0 .. i0 + nr - 1 of candidate c
+    const int r0 = c * P + i0;                         // their query-row index within the sequence
 
-    const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, ln = tid & 63;
-    const int nw = kCombT / 64;
+    T* ks = (T*)lds;
+    T* vs = ks + (size_t)P * DH;
+    float* st_o = lds + ((size_t)2 * P * DH * sizeof(T) + 3) / 4;   // [state][row][DH]
+    float* st_ml = st_o + (size_t)(kCombW + 1) * RG * DH;           // [state][row][2]
 
-    const int ct = split_ct(kv_len, nb, H, kv_lim, ct_min, target);
-    int base = 0;
-    for (int bb = 0; bb < b; ++bb) base += (prefix_tiles(kv_len, bb, kv_lim) + ct - 1) / ct * H;
-    const int nch = (prefix_tiles(kv_len, b, kv_lim) + ct - 1) / ct;
-    const size_t first = (size_t)base + (size_t)h * nch;
-    const size_t tail = (size_t)tail_base + (size_t)b * H + h;
-    auto slot_of = [&](int s) { return s < nch ? first + s : tail; };    // s == nch is the block part
-    const int ns = nch + 1;
-
-    float mloc = -INFINITY;
-    for (int s = tid; s < ns; s += kCombT) mloc = fmaxf(mloc, part_ml[(slot_of(s) * nq + qi) * 2]);
-    for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
-    if (ln == 0) red[wave][0] = mloc;
-    __syncthreads();
-    float M = red[0][0];
-    for (int w = 1; w < nw; ++w) M = fmaxf(M, red[w][0]);
-
-    float lloc = 0.f;
-    for (int s = tid; s < ns; s += kCombT) {
-        const float2 ml = *(const float2*)(part_ml + (slot_of(s) * nq + qi) * 2);
-        const float w = exp2f(ml.x - M);
-        wts[s] = w;
-        lloc = fmaf(w, ml.y, lloc);
+    // stage the candidate's block K and V rows 0 .. i0 + nr - 1 (one round trip)
+    const size_t krow0 = ((size_t)b * nq + (size_t)c * P) * H + h;
+    for (int e = tid; e < (i0 + nr) * DH; e += kCombT) {
+        const int j = e / DH, dd = e - j * DH;
+        const size_t src = (krow0 + (size_t)j * H) * DH + dd;
+        ks[e] = kb[src];
+        vs[e] = vb[src];
     }
-    for (int off = 32; off >= 1; off >>= 1) lloc += __shfl_xor(lloc, off);
-    if (ln == 0) red[wave][1] = lloc;
-    __syncthreads();
-    float l = 0.f;
-    for (int w = 0; w < nw; ++w) l += red[w][1];
 
-    // thread (group, d) accumulates slots group, group+ng, ...
-    const int ng = kCombT / DH;
-    const int grp = tid / DH, dd = tid % DH;
-    float acc = 0.f;
-    if (grp < ng) {
-        int s = grp;
-        for (; s + 3 * ng < ns; s += 4 * ng) {
-            const float o0 = part_o[(slot_of(s) * nq + qi) * DH + dd];
-            const float o1 = part_o[(slot_of(s + ng) * nq + qi) * DH + dd];
-            const float o2 = part_o[(slot_of(s + 2 * ng) * nq + qi) * DH + dd];
-            const float o3 = part_o[(slot_of(s + 3 * ng) * nq + qi) * DH + dd];
-            acc = fmaf(wts[s], o0, acc);
-            acc = fmaf(wts[s + ng], o1, acc);
-            acc = fmaf(wts[s + 2 * ng], o2, acc);
-            acc = fmaf(wts[s + 3 * ng], o3, acc);
+    // ---- prefix items of (b, h): a running state per row
+    const WorkList w = make_worklist(A.kv_len, A.nb, H, A.kv_lim, A.resident);
+    float M[RG], l[RG], a0[RG], a1[RG];
+#pragma unroll
+    for (int k = 0; k < RG; ++k) { M[k] = -INFINITY; l[k] = 0.f; a0[k] = 0.f; a1[k] = 0.f; }
+    long long base = 0;
+    for (int p = 0; p < w.np; ++p) {
+        long long off = 0, cnt = 0;
+        int nn = 0;
+        for (int bb = 0; bb < A.nb; ++bb) {
+            const int n = phase_items(w, prefix_tiles(A.kv_len, bb, A.kv_lim), p);
+            if (bb < b) off += (long long)n * H;
+            if (bb == b) nn = n;
+            cnt += (long long)n * H;
         }
-        for (; s < ns; s += ng) acc = fmaf(wts[s], part_o[(slot_of(s) * nq + qi) * DH + dd], acc);
+        const long long first = base + off + (long long)h * nn;
+        constexpr int B = RG >= 4 ? 1 : 4 / RG;        // items whose loads are in flight together
+        for (int j0 = wave; j0 < nn; j0 += kCombW * B) {
+            float2 ml[B][RG];
+            float v0[B][RG], v1[B][RG];
+#pragma unroll
+            for (int u = 0; u < B; ++u) {
+                const int j = j0 + u * kCombW;
+#pragma unroll
+                for (int k = 0; k < RG; ++k) {
+                    ml[u][k] = make_float2(-INFINITY, 0.f);
+                    v0[u][k] = v1[u][k] = 0.f;
+                    if (j < nn && k < nr) {
+                        const size_t row = (size_t)(first + j) * nq + r0 + k;
+                        ml[u][k] = *(const float2*)(A.part_ml + row * 2);
+                        if (ok0) v0[u][k] = A.part_o[row * DH + d0];
+                        if (ok1) v1[u][k] = A.part_o[row * DH + d1];
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < B; ++u) {
+                if (j0 + u * kCombW >= nn) break;
+#pragma unroll
+                for (int k = 0; k < RG; ++k) {
+                    if (ml[u][k].x > M[k]) {           // wave-uniform
+                        const float s = __builtin_amdgcn_exp2f(M[k] - ml[u][k].x);
+                        l[k] *= s; a0[k] *= s; a1[k] *= s;
+                        M[k] = ml[u][k].x;
+                    }
+                    const float wgt = __builtin_amdgcn_exp2f(ml[u][k].x - M[k]);
+                    l[k] = fmaf(wgt, ml[u][k].y, l[k]);
+                    a0[k] = fmaf(wgt, v0[u][k], a0[k]);
+                    a1[k] = fmaf(wgt, v1[u][k], a1[k]);
+                }
+            }
+        }
+        base += cnt;
     }
-    acc_s[tid] = acc;
+#pragma unroll
+    for (int k = 0; k < RG; ++k) {
+        float* so = st_o + ((size_t)wave * RG + k) * DH;
+        if (ok0) so[d0] = a0[k];
+        if (ok1) so[d1] = a1[k];
+        if (lane == 0) {
+            st_ml[(wave * RG + k) * 2] = M[k];
+            st_ml[(wave * RG + k) * 2 + 1] = l[k];
+        }
+    }
+    __syncthreads();                                   // block rows staged
+
+    // ---- causal block part: row k of the group by wave k mod 4, keys 0..i of the block
+    for (int k = wave; k < nr; k += kCombW) {
+        const int i = i0 + k;
+        const size_t qrow = ((size_t)b * nq + r0 + k) * H + h;
+        const float q0 = ok0 ? Act<ACT>::load(q, qrow * DH + d0) : 0.f;
+        const float q1 = ok1 ? Act<ACT>::load(q, qrow * DH + d1) : 0.f;
+        float my_s = -INFINITY;                        // lane j keeps score j
+        for (int j = 0; j <= i; ++j) {
+            float part = 0.f;
+            if (ok0) part = fmaf(q0, Act<ACT>::load(ks, (size_t)j * DH + d0), part);
+            if (ok1) part = fmaf(q1, Act<ACT>::load(ks, (size_t)j * DH + d1), part);
+            for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);   // same bits on every lane
+            if (lane == j) my_s = part * A.scale_log2;
+        }
+        float mb = my_s;
+        for (int off = 32; off >= 1; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
+        const float pj = lane <= i ? __builtin_amdgcn_exp2f(my_s - mb) : 0.f;
+        float lb = pj;
+        for (int off = 32; off >= 1; off >>= 1) lb += __shfl_xor(lb, off);
+        float b0 = 0.f, b1 = 0.f;
+        for (int j = 0; j <= i; ++j) {
+            const float pw = __shfl(pj, j);
+            if (ok0) b0 = fmaf(pw, Act<ACT>::load(vs, (size_t)j * DH + d0), b0);
+            if (ok1) b1 = fmaf(pw, Act<ACT>::load(vs, (size_t)j * DH + d1), b1);
+        }
+        float* so = st_o + ((size_t)kCombW * RG + k) * DH;
+        if (ok0) so[d0] = b0;
+        if (ok1) so[d1] = b1;
+        if (lane == 0) {
+            st_ml[(kCombW * RG + k) * 2] = mb;
+            st_ml[(kCombW * RG + k) * 2 + 1] = lb;
+        }
+    }
     __syncthreads();
-    if (tid < DH) {
-        float tot = 0.f;
-        for (int g2 = 0; g2 < ng; ++g2) tot += acc_s[g2 * DH + tid];
-        Act<ACT>::store(o, (((size_t)b * nq + qi) * H + h) * DH + tid, tot / l);
+
+    // ---- fixed-order merge of the four wave states and the block part, per row
+    for (int e = tid; e < nr * DH; e += kCombT) {
+        const int k = e / DH, dd = e - k * DH;
+        float Mt = st_ml[k * 2];
+#pragma unroll
+        for (int s = 1; s <= kCombW; ++s) Mt = fmaxf(Mt, st_ml[(s * RG + k) * 2]);
+        float lt = 0.f, ot = 0.f;
+#pragma unroll
+        for (int s = 0; s <= kCombW; ++s) {
+            const float wgt = __builtin_amdgcn_exp2f(st_ml[(s * RG + k) * 2] - Mt);
+            lt = fmaf(wgt, st_ml[(s * RG + k) * 2 + 1], lt);
+            ot = fmaf(wgt, st_o[((size_t)s * RG + k) * DH + dd], ot);
+        }
+        Act<ACT>::store((T*)A.o, (((size_t)b * nq + r0 + k) * H + h) * DH + dd, ot / lt);
     }
+}
+
+template <int ACT, int RG>
+__global__ __launch_bounds__(kCombT) void k_verify_finish(FinishArgs A)
+{
+    extern __shared__ float lds[];
+    typedef typename Act<ACT>::T T;
+    const int id = blockIdx.x;
+    if (id < A.n_conv) {
+        const int groups = (A.d + kCG - 1) / kCG;
+        conv_iir_block<ACT>(A.w_short, A.w_outer, A.lam, A.beta, A.cc, (const T*)A.short_win, A.outer_win, A.iir,
+                            (const T*)A.x, A.f_out, A.s_out, (T*)A.y_out, A.d, A.Ts, A.To, A.N, A.nc, A.P,
+                            id % groups, id / groups, lds);
+        return;
+    }
+    const int j = id - A.n_conv;            // (rg, c, h, b), row group fastest
+    const int rg = j % A.rg_count;
+    const int t = j / A.rg_count;
+    const int c = t % A.nc, h = (t / A.nc) % A.H, b = t / (A.nc * A.H);
+    combine_job<ACT, RG>(A, c, rg, h, b, lds);
+}
+
+__global__ void k_ticket_reset(unsigned* ticket) {
+    if (threadIdx.x == 0) ticket[0] = 0u;
 }
 
 // -------------------------------------------------------------------- host
 
+// Workspace: the queue's ticket counter (256 bytes), then the partials
+// part_o [items][nq][Dh] and part_ml [items][nq][2].
 AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_kv_len, int num_cus)
 {
     AttnPlan p{};
     const int P = gamma + 1;
     p.nq = nc * P;
-    const int tiles = (max_kv_len + kTile - 1) / kTile;
-    // The device splits the real prefixes into about `target` chunks (work
-    // items) over the whole batch.  With one query tile the fused kernel keeps
-    // two 4-wave workgroups per CU: two rounds of them keep every CU streaming
-    // until the end.  With several query tiles a workgroup walks its chunk with
-    // all four waves, so twice as many (shorter) chunks keep the same number of
-    // tiles in flight.  A chunk holds at least 8 tiles per wave, so that
-    // partials stay a small fraction of the traffic, and a sequence never has
-    // more than kMaxChunks chunks (the combine's weight table).
-    const int nqt = (p.nq + 15) / 16;
-    p.target = num_cus * (nqt > 1 ? 8 : 4);
-    if (p.target < 1) p.target = 1;
-    int ct_min = 8 * kPrefixWaves;
-    const int min_ct = (tiles + kMaxChunks - 1) / kMaxChunks;
-    if (ct_min < min_ct) ct_min = min_ct;
-    p.ct_min = ct_min;
+    p.resident = (num_cus > 0 ? num_cus : 1) * (p.nq > 16 ? kSlotsShared : kSlotsFused);
     p.kv_lim = max_kv_len;    // callers check max_kv_len + P <= kv_cap before any launch
-    // items <= H * sum_b (tiles_b / ct + 1) <= target + nb * H, since ct >= H * sum_b tiles_b / target;
-    // no items at all when every prefix is empty
+    const long long tiles = (max_kv_len + kTile - 1) / kTile;
     const long long nbh = (long long)nb * L->heads;
-    if (p.target + 2 * nbh > (1LL << 30)) {            // beyond any launch: the caller reports it unsupported
+    const int np = worklist_np(worklist_c0(tiles * nbh, p.resident));
+    // every phase holds at most 2R + 2 nb H items, the last at most 4R + nb H
+    const long long cap = tiles > 0 ? (long long)np * (4LL * p.resident + 2 * nbh) : 0;
+    if (cap > (1LL << 30)) {               // beyond any launch: the caller reports it unsupported
         p.items_cap = -1;
         return p;
     }
-    p.items_cap = tiles > 0 ? p.target + (int)nbh : 0;
-    p.tail_base = p.items_cap;
-    const size_t parts = (size_t)p.items_cap + (size_t)nbh;   // + the block part of each (b, h)
-    p.part_o_elems = parts * p.nq * L->head_dim;
-    p.part_ml_elems = parts * p.nq * 2;
+    p.items_cap = (int)cap;
+    p.part_o_elems = (size_t)cap * p.nq * L->head_dim;
+    p.part_ml_elems = (size_t)cap * p.nq * 2;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    p.bytes = up(p.part_o_elems * 4) + up(p.part_ml_elems * 4);
+    p.ticket_bytes = 256;
+    p.bytes = p.ticket_bytes + up(p.part_o_elems * 4) + up(p.part_ml_elems * 4);
     return p;
 }
 
-size_t stream_lds_bytes(const hci_layer* L, int nc, int P) {
-    (void)nc;    // the fused kernel runs with one query tile only
-    const size_t pre = (kPrefixWaves - 1) * (size_t)(16 * L->head_dim + 32);
-    const int act_bytes = L->act_dtype == HCI_BF16 ? 2 : 4;
-    size_t f = conv_iir_lds_floats(L->taps_outer, P);
-    const size_t t = tail_lds_floats(P, L->head_dim, act_bytes);
-    f = f > t ? f : t;
-    f = f > pre ? f : pre;
-    return f * sizeof(float);
+// rows per combine workgroup: the largest power of two (<= 16, <= P rounded up) that still
+// leaves at least eight combine workgroups per CU
+static int combine_rows(int nb, int nc, int H, int P, int num_cus) {
+    const long long blocks = (long long)nb * nc * H;
+    int rg = 1;
+    while (rg < 16 && rg < P && blocks * ((P + 2 * rg - 1) / (2 * rg)) >= 8LL * num_cus) rg *= 2;
+    return rg;
 }
 
-template <int DH>
-static hipError_t launch_stream(const StreamArgs& A, int blocks, size_t lds, hipStream_t st) {
+// dynamic LDS of the finish kernel: the larger of its two roles
+size_t stream_lds_bytes(const hci_layer* L, int nc, int P) {
+    const int act_bytes = L->act_dtype == HCI_BF16 ? 2 : 4;
+    const size_t conv = conv_iir_lds_floats(L->taps_short, L->taps_outer, nc * P);
+    const size_t comb = combine_lds_floats(P, L->head_dim, act_bytes, 16);
+    return (conv > comb ? conv : comb) * sizeof(float);
+}
+
+template <int ACT>
+static hipError_t launch_finish(const FinishArgs& F, int rg, int blocks, size_t lds, hipStream_t st) {
+    const void* fn = nullptr;
+    switch (rg) {
+        case 1: fn = (const void*)k_verify_finish<ACT, 1>; break;
+        case 2: fn = (const void*)k_verify_finish<ACT, 2>; break;
+        case 4: fn = (const void*)k_verify_finish<ACT, 4>; break;
+        case 8: fn = (const void*)k_verify_finish<ACT, 8>; break;
+        default: fn = (const void*)k_verify_finish<ACT, 16>; break;
+    }
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)k_verify_stream<DH, 1>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_verify_stream<DH, 1>), dim3(blocks), dim3(kRoleT), lds, st, A);
+    switch (rg) {
+        case 1: hipLaunchKernelGGL((k_verify_finish<ACT, 1>), dim3(blocks), dim3(kCombT), lds, st, F); break;
+        case 2: hipLaunchKernelGGL((k_verify_finish<ACT, 2>), dim3(blocks), dim3(kCombT), lds, st, F); break;
+        case 4: hipLaunchKernelGGL((k_verify_finish<ACT, 4>), dim3(blocks), dim3(kCombT), lds, st, F); break;
+        case 8: hipLaunchKernelGGL((k_verify_finish<ACT, 8>), dim3(blocks), dim3(kCombT), lds, st, F); break;
+        default: hipLaunchKernelGGL((k_verify_finish<ACT, 16>), dim3(blocks), dim3(kCombT), lds, st, F); break;
+    }
     return hipGetLastError();
 }
 
+// One verify: reset the queue, stream the prefix (bf16: persistent queue kernel; fp32: one
+// workgroup per item), then the finish kernel (conv/IIR scan, causal block part, combine).
 hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block* blk,
                          int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st, hipEvent_t* ev,
                          bool conv)
 {
     const int H = L->heads, DH = L->head_dim, nq = plan.nq;
     const float scale_log2 = kLog2e / sqrtf((float)DH);
-    float* part_o = (float*)ws;
-    float* part_ml = (float*)((char*)ws + (plan.part_o_elems * 4 + 255) / 256 * 256);
+    unsigned* ticket = (unsigned*)ws;
+    float* part_o = (float*)((char*)ws + plan.ticket_bytes);
+    float* part_ml = (float*)((char*)part_o + (plan.part_o_elems * 4 + 255) / 256 * 256);
     auto mark = [&](int i) { return (ev && ev[i]) ? hipEventRecord(ev[i], st) : hipSuccess; };
     hipError_t e = mark(0);
     if (e != hipSuccess) return e;
 
-    if (L->act_dtype == HCI_BF16) {
-        StreamArgs A{};
-        A.w_short = L->w_short; A.w_outer = L->w_outer; A.lam = L->lambda; A.beta = L->beta; A.cc = L->c;
-        A.short_win = (const uint16_t*)S->short_win; A.outer_win = S->outer_win; A.iir = S->iir;
-        A.x = (const uint16_t*)blk->x; A.f_out = blk->f; A.s_out = blk->s; A.y_out = (uint16_t*)blk->y;
-        A.d = L->d; A.Ts = L->taps_short; A.To = L->taps_outer; A.N = L->poles;
-        A.kc = (const uint16_t*)S->k_cache; A.vc = (const uint16_t*)S->v_cache; A.q = (const uint16_t*)blk->q;
-        A.kb = (const uint16_t*)blk->k; A.vb = (const uint16_t*)blk->v; A.kv_len = S->kv_len;
-        A.part_o = part_o; A.part_ml = part_ml;
-        A.H = H; A.kv_cap = S->kv_cap; A.kv_lim = plan.kv_lim; A.nq = nq; A.nb = nb; A.ct_min = plan.ct_min; A.target = plan.target;
-        A.tail_base = plan.tail_base; A.P = P; A.nc = nc; A.scale_log2 = scale_log2;
-        A.prefix_blocks = plan.items_cap;
-        const int nqt = (nq + 15) / 16;
-        // With one query tile the streaming kernel keeps two workgroups per CU and the
-        // short roles ride along at the end of its grid.  With more query tiles it holds
-        // a whole CU per workgroup, so the short roles run as their own light kernels.
-        // With one query tile the streaming kernel keeps two workgroups per CU and the short
-        // roles ride along at the end of its grid.  With several, the shared-prefix kernel
-        // carries them when their LDS fits its stages, else they run as their own kernels first.
-        const bool fuse = nqt == 1;
-        const size_t stage_bytes = (size_t)kStages * 128 * DH;
-        const size_t tail_lds = tail_lds_floats(P, DH, 2) * sizeof(float);
-        const bool ride = fuse || (conv_iir_lds_bytes(L->taps_outer, P) <= stage_bytes && tail_lds <= stage_bytes);
-        if (!ride) {
-            if (conv && (e = launch_conv_iir(L, S, blk, nb, nc, P, st)) != hipSuccess) return e;
-            if (tail_lds > 65536) {
-                e = hipFuncSetAttribute((const void*)k_attn_tail<HCI_BF16>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        (int)tail_lds);
-                if (e != hipSuccess) return e;
-            }
-            hipLaunchKernelGGL(k_attn_tail<HCI_BF16>, dim3(H, nc, nb), dim3(kRoleT), tail_lds, st,
-                               (const uint16_t*)blk->q, (const uint16_t*)blk->k, (const uint16_t*)blk->v, part_o,
-                               part_ml, H, DH, P, nq, plan.tail_base, scale_log2);
+    if (plan.items_cap > 0) {
+        if (L->act_dtype == HCI_BF16) {
+            StreamArgs A{};
+            A.kc = (const uint16_t*)S->k_cache; A.vc = (const uint16_t*)S->v_cache; A.q = (const uint16_t*)blk->q;
+            A.kv_len = S->kv_len; A.part_o = part_o; A.part_ml = part_ml; A.ticket = ticket;
+            A.H = H; A.kv_cap = S->kv_cap; A.kv_lim = plan.kv_lim; A.nq = nq; A.nb = nb; A.resident = plan.resident;
+            A.scale_log2 = scale_log2;
+            const int nqt = (nq + 15) / 16;
+            hipLaunchKernelGGL(k_ticket_reset, dim3(1), dim3(64), 0, st, ticket);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
-        A.n_conv = ride && conv ? ((L->d + kCG - 1) / kCG) * nb : 0;
-        A.n_tail = ride ? nb * nc * H : 0;
-        const long long blocks = (long long)A.prefix_blocks + A.n_conv + A.n_tail;
-        if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-        if (blocks > 0) {
-            if (!fuse) {
+            const int blocks = plan.items_cap < plan.resident ? plan.items_cap : plan.resident;
+            if (nqt > 1) {
                 if (DH == 128)
-                    hipLaunchKernelGGL(k_attn_prefix_shared<128>, dim3((int)blocks), dim3(kRoleT), 0, st, A, nqt);
+                    hipLaunchKernelGGL(k_attn_prefix_shared<128>, dim3(blocks), dim3(kRoleT), 0, st, A, nqt);
                 else
-                    hipLaunchKernelGGL(k_attn_prefix_shared<64>, dim3((int)blocks), dim3(kRoleT), 0, st, A, nqt);
-                e = hipGetLastError();
+                    hipLaunchKernelGGL(k_attn_prefix_shared<64>, dim3(blocks), dim3(kRoleT), 0, st, A, nqt);
             } else {
-                const size_t lds = stream_lds_bytes(L, nc, P);
-                e = DH == 128 ? launch_stream<128>(A, (int)blocks, lds, st) : launch_stream<64>(A, (int)blocks, lds, st);
+                if (DH == 128)
+                    hipLaunchKernelGGL(k_verify_stream<128>, dim3(blocks), dim3(kRoleT), 0, st, A);
+                else
+                    hipLaunchKernelGGL(k_verify_stream<64>, dim3(blocks), dim3(kRoleT), 0, st, A);
             }
-            if (e != hipSuccess) return e;
-        }
-    } else {
-        if (conv && (e = launch_conv_iir(L, S, blk, nb, nc, P, st)) != hipSuccess) return e;
-        const size_t tail_lds = tail_lds_floats(P, DH, 4) * sizeof(float);
-        if (tail_lds > 65536) {
-            e = hipFuncSetAttribute((const void*)k_attn_tail<HCI_F32>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)tail_lds);
-            if (e != hipSuccess) return e;
-        }
-        hipLaunchKernelGGL(k_attn_tail<HCI_F32>, dim3(H, nc, nb), dim3(kRoleT), tail_lds, st,
-                           (const float*)blk->q, (const float*)blk->k, (const float*)blk->v, part_o, part_ml,
-                           H, DH, P, nq, plan.tail_base, scale_log2);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (plan.items_cap > 0) {
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        } else {
             hipLaunchKernelGGL(k_attn_prefix_f32, dim3(plan.items_cap), dim3(64), 0, st,
                                (const float*)S->k_cache, (const float*)S->v_cache, S->kv_len,
                                (const float*)blk->q, part_o, part_ml, nb, H, DH, S->kv_cap, plan.kv_lim, nq,
-                               plan.ct_min, plan.target, scale_log2);
+                               plan.resident, scale_log2);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
     if ((e = mark(1)) != hipSuccess) return e;
 
-    dim3 cgrid(nq, H, nb), cblock(kCombT);
-    if (L->act_dtype == HCI_BF16) {
-        hipLaunchKernelGGL(k_attn_combine<HCI_BF16>, cgrid, cblock, 0, st, S->kv_len, part_o, part_ml,
-                           (uint16_t*)blk->o, nb, H, DH, nq, plan.kv_lim, plan.ct_min, plan.target, plan.tail_base);
-    } else {
-        hipLaunchKernelGGL(k_attn_combine<HCI_F32>, cgrid, cblock, 0, st, S->kv_len, part_o, part_ml,
-                           (float*)blk->o, nb, H, DH, nq, plan.kv_lim, plan.ct_min, plan.target, plan.tail_base);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    FinishArgs F{};
+    F.w_short = L->w_short; F.w_outer = L->w_outer; F.lam = L->lambda; F.beta = L->beta; F.cc = L->c;
+    F.short_win = S->short_win; F.outer_win = S->outer_win; F.iir = S->iir; F.x = blk->x;
+    F.f_out = blk->f; F.s_out = blk->s; F.y_out = blk->y;
+    F.d = L->d; F.Ts = L->taps_short; F.To = L->taps_outer; F.N = L->poles; F.nc = nc;
+    F.n_conv = conv ? ((L->d + kCG - 1) / kCG) * nb : 0;
+    F.kv_len = S->kv_len; F.part_o = part_o; F.part_ml = part_ml;
+    F.q = blk->q; F.kb = blk->k; F.vb = blk->v; F.o = blk->o;
+    F.nb = nb; F.H = H; F.DH = DH; F.nq = nq; F.P = P; F.kv_lim = plan.kv_lim; F.resident = plan.resident;
+    F.scale_log2 = scale_log2;
+    const int rg = combine_rows(nb, nc, H, P, plan.resident / (nq > 16 ? kSlotsShared : kSlotsFused));
+    F.rg_count = (P + rg - 1) / rg;
+    const long long blocks = (long long)F.n_conv + (long long)F.rg_count * nc * H * nb;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    const int act_bytes = L->act_dtype == HCI_BF16 ? 2 : 4;
+    const size_t conv_lds = conv ? conv_iir_lds_floats(L->taps_short, L->taps_outer, nc * P) : 0;
+    const size_t comb_lds = combine_lds_floats(P, DH, act_bytes, rg);
+    const size_t lds = (conv_lds > comb_lds ? conv_lds : comb_lds) * sizeof(float);
+    e = L->act_dtype == HCI_BF16 ? launch_finish<HCI_BF16>(F, rg, (int)blocks, lds, st)
+                                 : launch_finish<HCI_F32>(F, rg, (int)blocks, lds, st);
+    if (e != hipSuccess) return e;
     return mark(2);
 }
 

@@ -1,6 +1,26 @@
-// Conv/recurrent half of the block forward as a workgroup-level device
-// function, shared by the stand-alone conv/IIR kernel and the fused
-// verify kernel.  See conv_iir.hip for the description of the phases.
+// Conv/recurrent half of the block forward: short depthwise FIR -> outer
+// depthwise FIR -> diagonal modal IIR scan that keeps every per-position
+// state (EvSpark digest, Figure 1(d): the outer-FIR inputs u_i and the IIR
+// states s_i are what slicing later selects from).
+//
+// One workgroup = 16 channels of one sequence, 256 threads, every candidate
+// block of the sequence at once (rows r = c * P + i, R = nc * P rows); a
+// 4096-channel layer spreads over 256 workgroups per sequence.
+//  phase 0  one round of loads: the committed short window and the block
+//           inputs x of every row (as fp32), the outer window and the short
+//           and outer taps of the 16 channels go to LDS; the IIR parameters
+//           and the committed IIR state go to registers
+//  phase 1  thread (row slot, channel) computes f_r (short FIR) for rows
+//           r = slot, slot + 16, ...
+//  phase 2  the same threads compute g_r = sum_j w_outer[j] * fbar[i - j]
+//           from LDS, one fixed-order fma chain per output
+//  phase 3  thread (channel, pole lane) runs the IIR recurrence in fp32
+//           registers over the P positions of each candidate in turn and
+//           writes s_i (a contiguous kilobyte per step); the readout y_i is a
+//           fixed-order butterfly over the 16 pole lanes.
+// All per-output arithmetic happens in a fixed order that does not depend
+// on P or on the candidate count, so a block forward and P single-position
+// forwards give identical bits for f, s and y.
 #pragma once
 
 #include "hci_internal.h"
@@ -10,13 +30,13 @@ namespace hci {
 constexpr int kCG = 16;        // channels per workgroup
 constexpr int kConvT = 256;    // threads per workgroup
 
-__host__ __device__ inline size_t conv_iir_lds_floats(int To, int P) {
-    return (size_t)((To - 1 + P) + To + P) * kCG;
+// LDS floats: short window + x rows, outer window + f rows, g rows, outer taps, short taps
+__host__ __device__ inline size_t conv_iir_lds_floats(int Ts, int To, int R) {
+    return (size_t)((Ts - 1 + R) + (To - 1 + R) + R + To + Ts) * kCG;
 }
 
-// one workgroup: channel group cgi (16 channels) of sequence b, for every
-// candidate block c = 0..nc-1 in turn (they share the committed window and
-// the taps, staged once); lds holds conv_iir_lds_floats(To, P) floats
+// one workgroup: channel group cgi (16 channels) of sequence b, all nc candidate blocks
+// (they share the committed windows, state and taps); lds holds conv_iir_lds_floats floats
 template <int ACT>
 __device__ __forceinline__ void conv_iir_block(
     const float* __restrict__ w_short, const float* __restrict__ w_outer,
@@ -26,29 +46,35 @@ __device__ __forceinline__ void conv_iir_block(
     float* __restrict__ f_out, float* __restrict__ s_out, typename Act<ACT>::T* __restrict__ y_out,
     int d, int Ts, int To, int N, int nc, int P, int cgi, int b, float* lds)
 {
-    const int W = To - 1;
-    float* fbar = lds;                          // [W + P][kCG]: row r holds fbar[r - W]
-    float* wl = fbar + (size_t)(W + P) * kCG;   // [To][kCG]
-    float* gl = wl + (size_t)To * kCG;          // [P][kCG]
+    const int W = To - 1, Ws = Ts - 1, R = nc * P;
+    float* xs = lds;                            // [Ws + R][kCG]: short window rows, then x rows
+    float* fb = xs + (size_t)(Ws + R) * kCG;    // [W + R][kCG]: outer window rows, then f rows
+    float* gl = fb + (size_t)(W + R) * kCG;     // [R][kCG]
+    float* wl = gl + (size_t)R * kCG;           // [To][kCG]
+    float* ws = wl + (size_t)To * kCG;          // [Ts][kCG]
 
     const int ch0 = cgi * kCG;
     const int tid = threadIdx.x;
-    const int cl = tid & (kCG - 1), row = tid >> 4;     // 16 rows of 16 channels per pass
+    const int cl = tid & (kCG - 1), row = tid >> 4;     // 16 row slots of 16 channels
     const int ch = ch0 + cl;
     const bool live = ch < d;
-    const typename Act<ACT>::T* sw = short_win + (size_t)b * (Ts - 1) * d;
+    const typename Act<ACT>::T* sw = short_win + (size_t)b * Ws * d;
     const float* ow = outer_win + (size_t)b * W * d;
+    const typename Act<ACT>::T* xb = x + (size_t)b * R * d;
 
-    // phase 0: stage window rows and taps (once for all candidates)
-    for (int r = row; r < W; r += kConvT / kCG) fbar[r * kCG + cl] = live ? ow[(size_t)r * d + ch] : 0.f;
+    // phase 0: every load of the workgroup in one round
+    for (int r = row; r < Ws; r += kConvT / kCG) xs[r * kCG + cl] = live ? Act<ACT>::load(sw, (size_t)r * d + ch) : 0.f;
+    for (int r = row; r < R; r += kConvT / kCG) xs[(Ws + r) * kCG + cl] = live ? Act<ACT>::load(xb, (size_t)r * d + ch) : 0.f;
+    for (int r = row; r < W; r += kConvT / kCG) fb[r * kCG + cl] = live ? ow[(size_t)r * d + ch] : 0.f;
     for (int j = row; j < To; j += kConvT / kCG) wl[j * kCG + cl] = live ? w_outer[(size_t)j * d + ch] : 0.f;
+    for (int j = row; j < Ts; j += kConvT / kCG) ws[j * kCG + cl] = live ? w_short[(size_t)j * d + ch] : 0.f;
 
-    // IIR parameters of thread (channel = tid / 16, lane n = tid % 16): poles n, n+16, ...
+    // IIR parameters and committed state of thread (channel = tid / 16, lane n = tid % 16): poles n, n+16, ...
     const int lane16 = tid & 15;
     const int cg = tid >> 4;
     const int chn = ch0 + cg;
     const bool scan = chn < d;                          // uniform across the 16-lane group
-    float lm[4], bt[4], cv[4];
+    float lm[4], bt[4], cv[4], s0[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int n = lane16 + 16 * r;
@@ -57,66 +83,62 @@ __device__ __forceinline__ void conv_iir_block(
         lm[r] = ok ? lam[o] : 0.f;
         bt[r] = ok ? beta[o] : 0.f;
         cv[r] = ok ? cc[o] : 0.f;
+        s0[r] = ok ? iir[(size_t)b * d * N + o] : 0.f;
     }
+    __syncthreads();
 
-    for (int c = 0; c < nc; ++c) {
-        const size_t blk = (size_t)b * nc + c;
-        const typename Act<ACT>::T* xb = x + blk * P * d;
-
-        // phase 1: short FIR, f_i = sum_{j<Ts} w_short[j] * xbar[i-j]
-        for (int i = row; i < P; i += kConvT / kCG) {
-            float acc = 0.f;
-            if (live) {
-                for (int j = 0; j < Ts; ++j) {
-                    const int m = i - j;
-                    const float xv = (m >= 0) ? Act<ACT>::load(xb, (size_t)m * d + ch)
-                                              : Act<ACT>::load(sw, (size_t)(Ts - 1 + m) * d + ch);
-                    acc = fmaf(w_short[(size_t)j * d + ch], xv, acc);
-                }
-                f_out[(blk * P + i) * d + ch] = acc;
-            }
-            fbar[(W + i) * kCG + cl] = acc;
+    // phase 1: short FIR, f_i = sum_{j<Ts} w_short[j] * xbar[i-j]
+    for (int r = row; r < R; r += kConvT / kCG) {
+        const int c = r / P, i = r - c * P;
+        float acc = 0.f;
+        for (int j = 0; j < Ts; ++j) {
+            const int m = i - j;
+            const float xv = m >= 0 ? xs[(Ws + c * P + m) * kCG + cl] : xs[(Ws + m) * kCG + cl];
+            acc = fmaf(ws[j * kCG + cl], xv, acc);
         }
-        __syncthreads();
+        if (live) f_out[((size_t)b * R + r) * d + ch] = acc;
+        fb[(W + r) * kCG + cl] = acc;
+    }
+    __syncthreads();
 
-        // phase 2: outer FIR, g_i = sum_{j<To} w_outer[j] * fbar[i-j], j ascending
-        for (int i = row; i < P; i += kConvT / kCG) {
-            float acc = 0.f;
-            const float* fp = fbar + (W + i) * kCG + cl;
-            const float* wp = wl + cl;
+    // phase 2: outer FIR, g_i = sum_{j<To} w_outer[j] * fbar[i-j], j ascending
+    for (int r = row; r < R; r += kConvT / kCG) {
+        const int c = r / P, i = r - c * P;
+        const float* fblk = fb + (W + c * P) * kCG + cl;   // candidate c's f rows
+        const float* fwin = fb + W * kCG + cl;             // fwin[-k * kCG] = outer window row W - k
+        float acc = 0.f;
+        int j = 0;
 #pragma unroll 8
-            for (int j = 0; j < To; ++j) acc = fmaf(wp[j * kCG], fp[-j * kCG], acc);
-            gl[i * kCG + cl] = acc;
-        }
-        __syncthreads();
+        for (; j <= i && j < To; ++j) acc = fmaf(wl[j * kCG + cl], fblk[(i - j) * kCG], acc);
+#pragma unroll 8
+        for (; j < To; ++j) acc = fmaf(wl[j * kCG + cl], fwin[(i - j) * kCG], acc);
+        gl[r * kCG + cl] = acc;
+    }
+    __syncthreads();
 
-        // phase 3: IIR scan from the committed state, in registers
-        if (scan) {
-            float s[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int n = lane16 + 16 * r;
-                s[r] = n < N ? iir[(size_t)b * d * N + (size_t)chn * N + n] : 0.f;
-            }
+    // phase 3: IIR scan from the committed state, in registers, one candidate after another
+    if (scan) {
+        for (int c = 0; c < nc; ++c) {
+            float s[4] = {s0[0], s0[1], s0[2], s0[3]};
             for (int i = 0; i < P; ++i) {
-                const float g = gl[i * kCG + cg];
+                const int r = c * P + i;
+                const float g = gl[r * kCG + cg];
                 float part_y = 0.f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int n = lane16 + 16 * r;
-                    s[r] = fmaf(lm[r], s[r], bt[r] * g);
-                    if (n < N) s_out[((blk * P + i) * d + chn) * N + n] = s[r];
-                    part_y = fmaf(cv[r], s[r], part_y);
+                for (int q = 0; q < 4; ++q) {
+                    const int n = lane16 + 16 * q;
+                    s[q] = fmaf(lm[q], s[q], bt[q] * g);
+                    if (n < N) s_out[(((size_t)b * R + r) * d + chn) * N + n] = s[q];
+                    part_y = fmaf(cv[q], s[q], part_y);
                 }
                 // fixed-order butterfly over the 16 pole lanes of this channel
                 part_y += __shfl_xor(part_y, 8, 16);
                 part_y += __shfl_xor(part_y, 4, 16);
                 part_y += __shfl_xor(part_y, 2, 16);
                 part_y += __shfl_xor(part_y, 1, 16);
-                if (lane16 == 0) Act<ACT>::store(y_out, (blk * P + i) * d + chn, part_y);
+                if (lane16 == 0) Act<ACT>::store(y_out, ((size_t)b * R + r) * d + chn, part_y);
             }
         }
-        __syncthreads();                             // f rows and g of this candidate are reused by the next
     }
 }
 

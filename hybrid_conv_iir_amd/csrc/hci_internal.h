@@ -87,26 +87,21 @@ __host__ __device__ __forceinline__ size_t v_elem(int row, int dd, int Dh) {
 // workspace and launches the kernels, so both always agree.
 struct AttnPlan {
     int nq;            // queries per sequence = nc * P
-    int ct_min;        // smallest split-K chunk (tiles) the device may pick
-    int target;        // work items the device aims for over the whole batch
-    int items_cap;     // bound on the work items (the prefix grid); 0 when max_kv_len is 0
-    int tail_base;     // partial index of the first block part (= items_cap)
+    int resident;      // streaming workgroups kept resident (the work list is cut for this many)
+    int items_cap;     // bound on the prefix work items; 0 when max_kv_len is 0, -1 when too many
     int kv_lim;        // prefix lengths are read clamped to [0, kv_lim] (= max_kv_len)
+    size_t ticket_bytes;                 // the job queue's counter (first section of the workspace)
     size_t part_o_elems, part_ml_elems;
     size_t bytes;      // workspace bytes (256-aligned sections)
 };
 AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_kv_len, int num_cus);
 int device_cu_count();
 
-// dynamic LDS bytes of the conv/IIR kernel and of the fused streaming
-// kernel (neither may exceed kMaxLds)
-size_t conv_iir_lds_bytes(int To, int P);
+// dynamic LDS bytes of the verify's finish kernel (conv/IIR scan and combine; at most kMaxLds)
 size_t stream_lds_bytes(const hci_layer* L, int nc, int P);
 constexpr size_t kMaxLds = 160 * 1024;
 
-hipError_t launch_conv_iir(const hci_layer* L, const hci_state* S, const hci_block* blk,
-                           int nb, int nc, int P, hipStream_t st);
-// the whole verify: streaming kernel(s) then the combine; ev (may be null)
+// the whole verify: the prefix stream then the finish kernel; ev (may be null)
 // = 3 events recorded before, after the streaming part, and at the end
 hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block* blk,
                          int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st, hipEvent_t* ev,
