@@ -39,6 +39,11 @@ WORKLOAD_NAMES = {
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_stream_c3_traffic.json")
 
 
+def traffic_file(cfg_name: str) -> str:
+    """Counter summary of the prefix-streaming kernel for one workload (c3: k_verify_stream, c4: the shared one)."""
+    return os.path.join(ROOT, "profiles", f"verify_stream_{cfg_name}_traffic.json")
+
+
 def _hip():
     lib = ctypes.CDLL("libamdhip64.so.7")      # the runtime torch already loaded
     lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -96,7 +101,8 @@ def stream_alg_bytes(cfg, kv_lens) -> int:
     return sum(2 * cfg.heads * L * cfg.head_dim * act for L in kv_lens) + nq * cfg.heads * cfg.head_dim * act
 
 
-VERIFY_SOURCES = ("attention.hip", "conv_iir_body.h", "hci_internal.h")
+VERIFY_SOURCES = ("stream_one.hip", "prefix_tile.h", "worklist.h", "hci_internal.h")
+SHARED_SOURCES = ("stream_shared.hip", "prefix_tile.h", "worklist.h", "hci_internal.h")
 PREFILL_SOURCES = ("prefill.hip", "slice.hip", "hci_internal.h")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_c3_traffic.json")
 
@@ -600,7 +606,9 @@ def main():
         "hbm_probe_read_GBs": round(probe_gbs, 1),
         "roofline": {"kernel": stream_kernel_name(cfg),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": _traffic(args.config),
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": _traffic(args.config, traffic_file(args.config),
+                                         SHARED_SOURCES if cfg.nc * cfg.P > 16 else VERIFY_SOURCES),
                      "alg_bytes_per_launch": int(alg_stream),
                      "avg_launch_ms": round(avg_stream_s * 1e3, 4)},
         "accepted_per_step": [int(x) for x in ((len_after - len_before) // K)],

@@ -6,10 +6,11 @@
 // One workgroup = 16 channels of one sequence, 256 threads, every candidate
 // block of the sequence at once (rows r = c * P + i, R = nc * P rows); a
 // 4096-channel layer spreads over 256 workgroups per sequence.
-//  phase 0  one round of loads: the committed short window and the block
-//           inputs x of every row (as fp32), the outer window and the short
-//           and outer taps of the 16 channels go to LDS; the IIR parameters
-//           and the committed IIR state go to registers
+//  phase 0  one round of loads (every value to registers first, then to
+//           LDS): the committed short window and the block inputs x of every
+//           row (as fp32), the outer window and the short and outer taps of
+//           the 16 channels go to LDS; the IIR parameters and the committed
+//           IIR state stay in registers
 //  phase 1  thread (row slot, channel) computes f_r (short FIR) for rows
 //           r = slot, slot + 16, ...
 //  phase 2  the same threads compute g_r = sum_j w_outer[j] * fbar[i - j]
@@ -62,13 +63,6 @@ __device__ __forceinline__ void conv_iir_block(
     const float* ow = outer_win + (size_t)b * W * d;
     const typename Act<ACT>::T* xb = x + (size_t)b * R * d;
 
-    // phase 0: every load of the workgroup in one round
-    for (int r = row; r < Ws; r += kConvT / kCG) xs[r * kCG + cl] = live ? Act<ACT>::load(sw, (size_t)r * d + ch) : 0.f;
-    for (int r = row; r < R; r += kConvT / kCG) xs[(Ws + r) * kCG + cl] = live ? Act<ACT>::load(xb, (size_t)r * d + ch) : 0.f;
-    for (int r = row; r < W; r += kConvT / kCG) fb[r * kCG + cl] = live ? ow[(size_t)r * d + ch] : 0.f;
-    for (int j = row; j < To; j += kConvT / kCG) wl[j * kCG + cl] = live ? w_outer[(size_t)j * d + ch] : 0.f;
-    for (int j = row; j < Ts; j += kConvT / kCG) ws[j * kCG + cl] = live ? w_short[(size_t)j * d + ch] : 0.f;
-
     // IIR parameters and committed state of thread (channel = tid / 16, lane n = tid % 16): poles n, n+16, ...
     const int lane16 = tid & 15;
     const int cg = tid >> 4;
@@ -85,6 +79,46 @@ __device__ __forceinline__ void conv_iir_block(
         cv[r] = ok ? cc[o] : 0.f;
         s0[r] = ok ? iir[(size_t)b * d * N + o] : 0.f;
     }
+
+    // phase 0: every load of the workgroup in one round: all values go to registers first
+    // (the common sizes: up to 128 window rows and taps, 64 block rows, 16 short taps), then
+    // to LDS; rows beyond those sizes are staged by a plain loop afterwards
+    {
+        constexpr int SW = 8, SX = 4;                   // rows per thread of the register batch
+        float vw[SW], vt[SW], vx[SX], vsw, vst;
+#pragma unroll
+        for (int u = 0; u < SW; ++u) {
+            const int r = row + 16 * u;
+            vw[u] = live && r < W ? ow[(size_t)r * d + ch] : 0.f;
+            vt[u] = live && r < To ? w_outer[(size_t)r * d + ch] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < SX; ++u) {
+            const int r = row + 16 * u;
+            vx[u] = live && r < R ? Act<ACT>::load(xb, (size_t)r * d + ch) : 0.f;
+        }
+        vsw = live && row < Ws ? Act<ACT>::load(sw, (size_t)row * d + ch) : 0.f;
+        vst = live && row < Ts ? w_short[(size_t)row * d + ch] : 0.f;
+#pragma unroll
+        for (int u = 0; u < SW; ++u) {
+            const int r = row + 16 * u;
+            if (r < W) fb[r * kCG + cl] = vw[u];
+            if (r < To) wl[r * kCG + cl] = vt[u];
+        }
+#pragma unroll
+        for (int u = 0; u < SX; ++u) {
+            const int r = row + 16 * u;
+            if (r < R) xs[(Ws + r) * kCG + cl] = vx[u];
+        }
+        if (row < Ws) xs[row * kCG + cl] = vsw;
+        if (row < Ts) ws[row * kCG + cl] = vst;
+        for (int r = row + 16 * SW; r < W; r += kConvT / kCG) fb[r * kCG + cl] = live ? ow[(size_t)r * d + ch] : 0.f;
+        for (int r = row + 16 * SW; r < To; r += kConvT / kCG) wl[r * kCG + cl] = live ? w_outer[(size_t)r * d + ch] : 0.f;
+        for (int r = row + 16 * SX; r < R; r += kConvT / kCG) xs[(Ws + r) * kCG + cl] = live ? Act<ACT>::load(xb, (size_t)r * d + ch) : 0.f;
+        for (int r = row + 16; r < Ws; r += kConvT / kCG) xs[r * kCG + cl] = live ? Act<ACT>::load(sw, (size_t)r * d + ch) : 0.f;
+        for (int r = row + 16; r < Ts; r += kConvT / kCG) ws[r * kCG + cl] = live ? w_short[(size_t)r * d + ch] : 0.f;
+    }
+
     __syncthreads();
 
     // phase 1: short FIR, f_i = sum_{j<Ts} w_short[j] * xbar[i-j]

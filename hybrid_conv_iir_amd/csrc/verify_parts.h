@@ -1,0 +1,36 @@
+// Arguments and launchers of the verify's finish kernel, shared by its
+// translation unit and the verify's host code.
+#pragma once
+
+#include "hci_internal.h"
+
+namespace hci {
+
+constexpr int kCombT = 256;
+constexpr int kCombW = kCombT / 64;
+
+struct FinishArgs {
+    // conv / IIR
+    const float *w_short, *w_outer, *lam, *beta, *cc;
+    const void* short_win; const float* outer_win; const float* iir; const void* x;
+    float* f_out; float* s_out; void* y_out;
+    int d, Ts, To, N, nc, n_conv;
+    // combine
+    const int32_t* kv_len; const float *part_o, *part_ml;
+    const void *q, *kb, *vb; void* o;
+    int nb, H, DH, nq, P, kv_lim, resident, rg_count;
+    float scale_log2;
+};
+
+// dynamic LDS floats of the combine role: the candidate's block K and V rows (raw
+// activations), then per row and state (four waves + the block part) O [Dh] and (m, l)
+__host__ __device__ inline size_t combine_lds_floats(int P, int DH, int act_bytes, int RG) {
+    return ((size_t)2 * P * DH * act_bytes + 3) / 4 + (size_t)(kCombW + 1) * RG * (DH + 2);
+}
+
+// rows per combine workgroup for these sizes (1, 2, 4, 8 or 16)
+int combine_rows(int nb, int nc, int H, int P, int num_cus);
+// the finish kernel: grid = F.n_conv + F.rg_count * nc * H * nb workgroups of kCombT threads
+hipError_t launch_finish(const FinishArgs& F, int act_dtype, int rg, int blocks, size_t lds, hipStream_t st);
+
+}  // namespace hci

@@ -1,0 +1,110 @@
+// The split of the committed KV prefixes into work items, derived on the
+// device from kv_len -- identically by the prefix-streaming kernels, which
+// take the items from a queue, and by the finish kernel, which merges their
+// partials.  Host code sizes the workspace with the bound stated below.
+#pragma once
+
+#include "hci_internal.h"
+
+namespace hci {
+
+// Committed length of sequence b as the attention reads it: kv_len clamped to
+// [0, lim], lim = min(kv_cap, max_kv_len), so that a length above the host's
+// bound can never yield more work than the host planned for.
+__device__ __forceinline__ int prefix_len(const int32_t* kv_len, int b, int lim) {
+    const int L = kv_len[b];
+    return L < 0 ? 0 : (L > lim ? lim : L);
+}
+
+__device__ __forceinline__ int prefix_tiles(const int32_t* kv_len, int b, int lim) {
+    return (prefix_len(kv_len, b, lim) + kTile - 1) / kTile;
+}
+
+// ------------------------------------------------------------- work list
+//
+// Derived on the device from kv_len, identically by the streaming kernels
+// and the combine.  With W = H * sum_b tiles_b and R resident slots,
+// c0 = max(kChunkMin, ceil(W / 2R)) and np = the number of phases whose chunk
+// c0 >> p stays >= kChunkMin (at most kPhaseMax).  Phase p of a prefix of T
+// tiles covers [T - (T >> p), T - (T >> (p+1))) (the last phase runs to T)
+// in chunks of c0 >> p tiles.  Items are numbered phase-major, then by
+// sequence, head and chunk:
+//   item = base_p + H * sum_{b' < b} n(p, b') + h * n(p, b) + j,
+// n(p, b) = ceil(phase length / chunk).  Item i writes partial i.  Every
+// phase holds at most 2R + 2 nb H items (the last one 4R + nb H), which is
+// the bound the host sizes the workspace with.
+
+constexpr int kChunkMin = 32;        // smallest item (tiles): eight per wave
+constexpr int kPhaseMax = 8;
+
+struct WorkList {
+    int nb, H, lim, c0, np;
+};
+
+__host__ __device__ inline long long worklist_c0(long long total_tiles, int resident) {
+    const long long half = 2LL * (resident > 0 ? resident : 1);
+    long long c0 = (total_tiles + half - 1) / half;
+    if (c0 < kChunkMin) c0 = kChunkMin;
+    if (c0 > (1LL << 28)) c0 = 1LL << 28;
+    return c0;
+}
+
+__host__ __device__ inline int worklist_np(long long c0) {
+    int np = 1;
+    while (np < kPhaseMax && (c0 >> np) >= kChunkMin) ++np;
+    return np;
+}
+
+__device__ __forceinline__ WorkList make_worklist(const int32_t* kv_len, int nb, int H, int lim, int resident) {
+    long long tot = 0;
+    for (int b = 0; b < nb; ++b) tot += prefix_tiles(kv_len, b, lim);
+    const long long c0 = worklist_c0(tot * H, resident);
+    return WorkList{nb, H, lim, (int)c0, worklist_np(c0)};
+}
+
+__device__ __forceinline__ int phase_chunk(const WorkList& w, int p) { return w.c0 >> p; }
+
+__device__ __forceinline__ void phase_range(const WorkList& w, int T, int p, int& s, int& e) {
+    s = T - (T >> p);
+    e = p + 1 < w.np ? T - (T >> (p + 1)) : T;
+}
+
+__device__ __forceinline__ int phase_items(const WorkList& w, int T, int p) {
+    int s, e;
+    phase_range(w, T, p, s, e);
+    const int c = phase_chunk(w, p);
+    return (e - s + c - 1) / c;
+}
+
+__device__ __forceinline__ long long work_count(const int32_t* kv_len, const WorkList& w) {
+    long long n = 0;
+    for (int p = 0; p < w.np; ++p)
+        for (int b = 0; b < w.nb; ++b) n += (long long)phase_items(w, prefix_tiles(kv_len, b, w.lim), p) * w.H;
+    return n;
+}
+
+// Locate item `item`: sequence b, head h, tiles [t0, t1); false past the last item.
+__device__ __forceinline__ bool work_item(const int32_t* kv_len, const WorkList& w, long long item,
+                                          int& b, int& h, int& t0, int& t1) {
+    for (int p = 0; p < w.np; ++p) {
+        for (int bb = 0; bb < w.nb; ++bb) {
+            const int T = prefix_tiles(kv_len, bb, w.lim);
+            const int n = phase_items(w, T, p);
+            const long long cnt = (long long)n * w.H;
+            if (item < cnt) {
+                b = bb;
+                h = (int)(item / n);
+                const int j = (int)(item - (long long)h * n);
+                int s, e;
+                phase_range(w, T, p, s, e);
+                t0 = s + j * phase_chunk(w, p);
+                t1 = min(t0 + phase_chunk(w, p), e);
+                return true;
+            }
+            item -= cnt;
+        }
+    }
+    return false;
+}
+
+}  // namespace hci

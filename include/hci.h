@@ -132,7 +132,9 @@ typedef struct hci_block {
 /* ------------------------------------------------------------------ verify */
 
 /* Bytes of workspace hci_verify_block needs for these sizes on the current
- * device (split-K attention partials).  Returns 0 for invalid arguments. */
+ * device: the prefix stream's job-queue counter (256 bytes, reset by the call
+ * itself) and the split-K attention partials.  Returns 0 for invalid
+ * arguments. */
 size_t hci_verify_workspace_bytes(const hci_layer* L, int nb, int nc, int gamma, int max_kv_len);
 
 /* One initial-state block forward over P = gamma + 1 positions for every
@@ -150,18 +152,21 @@ size_t hci_verify_workspace_bytes(const hci_layer* L, int nb, int nc, int gamma,
  *   max_kv_len  host-side upper bound on every kv_len[b] (sizes the grid);
  *               must satisfy max_kv_len + gamma + 1 <= kv_cap.
  *   ws, ws_bytes  device workspace of at least
- *               hci_verify_workspace_bytes(...) bytes, 256-byte aligned.
- * Limits: gamma >= 0; nc * P <= 64; To + P <= 320 (LDS staging of the
- * outer window and taps). */
+ *               hci_verify_workspace_bytes(...) bytes, 256-byte aligned; two
+ *               calls in flight at once must not share a workspace.
+ * q, k and v must be 16-byte aligned.
+ * Limits: gamma >= 0; nc * P <= 64; the conv/IIR scan stages the outer
+ * window, taps and block rows of 16 channels in LDS:
+ * 16 * 4 * (2*To + 2*Ts + 3*nc*P - 2) bytes <= 160 KiB. */
 int hci_verify_block(const hci_layer* L, const hci_state* S, const hci_block* blk,
                      int nb, int nc, int gamma, int max_kv_len,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* hci_verify_block that also records events[0..2] on `stream`: before the
- * first kernel, after the streaming part (the kernel that reads the KV
- * prefix; for bf16 layers it also runs the conv/IIR scan and the causal
- * block part), and after the final combine kernel, so the caller can time
- * the parts with hipEventElapsedTime.  events must point at 3 events created
+ * first kernel, after the streaming part (the queue reset and the kernel that
+ * reads the KV prefix), and after the finish kernel (conv/IIR scan, causal
+ * block part, merge of the partials), so the caller can time the parts with
+ * hipEventElapsedTime.  events must point at 3 events created
  * by the caller (entries may be NULL to skip one).  Errors as
  * hci_verify_block. */
 int hci_verify_block_timed(const hci_layer* L, const hci_state* S, const hci_block* blk,
