@@ -1,5 +1,6 @@
-// Lossless acceptance of verified blocks (one workgroup per sequence, the
-// candidates of a sequence in turn, then the best candidate).
+// Lossless acceptance of verified blocks: one workgroup per (sequence,
+// candidate) block, then the best candidate of each sequence; recursive
+// sampling over several candidates takes one workgroup per sequence.
 //
 // Greedy (ReaDy summary, section 3.1): keep the longest draft prefix equal
 // to the target argmax, the next token is the argmax of row k.
@@ -320,6 +321,20 @@ __device__ void accept_recursive(int b, int nc, int gamma, int V, double T,
     if (threadIdx.x == 0 && best) best[b] = rep;
 }
 
+// Recursive acceptance: one workgroup per sequence (the candidates are tried in turn at every depth).
+__global__ __launch_bounds__(kAccT) void k_accept_recursive(
+    int nc, int gamma, int V, double T,
+    const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ drafts,
+    const double* __restrict__ uni, int32_t* __restrict__ n_acc, int32_t* __restrict__ next,
+    int32_t* __restrict__ best, double* __restrict__ margin_out)
+{
+    __shared__ AccScratch sh;
+    accept_recursive(blockIdx.x, nc, gamma, V, T, zt, zd, drafts, uni, n_acc, next, best, margin_out, sh);
+}
+
+// Greedy and one-candidate sampling: one workgroup per (sequence, candidate) block, blockIdx.x =
+// b * nc + c; the candidates of a sequence are independent, so they run side by side.  With one
+// candidate the best is candidate 0; otherwise k_accept_best picks it.
 __global__ __launch_bounds__(kAccT) void k_accept(
     int mode, int nc, int gamma, int V, double T,
     const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ drafts,
@@ -327,16 +342,10 @@ __global__ __launch_bounds__(kAccT) void k_accept(
     int32_t* __restrict__ best, double* __restrict__ margin_out)
 {
     __shared__ AccScratch sh;
-    const int b = blockIdx.x;
     const int P = gamma + 1;
-    int best_c = 0, best_k = -1;
-    if (mode == HCI_SAMPLE_RECURSIVE) {
-        accept_recursive(b, nc, gamma, V, T, zt, zd, drafts, uni, n_acc, next, best, margin_out, sh);
-        return;
-    }
-
-    for (int c = 0; c < nc; ++c) {
-        const size_t blk = (size_t)b * nc + c;
+    {
+        const size_t blk = blockIdx.x;
+        const size_t b = blk / nc;
         const float* zt_c = zt + blk * P * V;
         const int32_t* dr = drafts + blk * gamma;
         int k = gamma, nxt = 0;
@@ -423,11 +432,23 @@ __global__ __launch_bounds__(kAccT) void k_accept(
             n_acc[blk] = k;
             next[blk] = nxt;
             if (margin_out) margin_out[blk] = margin;
+            if (nc == 1 && best) best[b] = 0;
         }
-        if (k > best_k) { best_k = k; best_c = c; }
-        __syncthreads();
     }
-    if (threadIdx.x == 0 && best) best[b] = best_c;
+}
+
+// best candidate of each sequence: the largest n_accepted, lowest index on ties
+__global__ __launch_bounds__(256) void k_accept_best(int nb, int nc, const int32_t* __restrict__ n_acc,
+                                                     int32_t* __restrict__ best)
+{
+    const size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= (size_t)nb) return;
+    int bc = 0, bk = n_acc[b * nc];
+    for (int c = 1; c < nc; ++c) {
+        const int k = n_acc[b * nc + c];
+        if (k > bk) { bk = k; bc = c; }
+    }
+    best[b] = bc;
 }
 
 // Serial drafting with the previous-token bias (EvSpark digest, Figure 1(b)): draft m draws from
@@ -535,8 +556,16 @@ hipError_t launch_accept(int mode, int nb, int nc, int gamma, int V, float tempe
                          const float* zt, const float* zd, const int32_t* drafts, const double* u,
                          int32_t* n_acc, int32_t* next, int32_t* best, double* margin, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_accept, dim3(nb), dim3(kAccT), 0, st, mode, nc, gamma, V, (double)temperature,
-                       zt, zd, drafts, u, n_acc, next, best, margin);
+    if (mode == HCI_SAMPLE_RECURSIVE) {
+        hipLaunchKernelGGL(k_accept_recursive, dim3(nb), dim3(kAccT), 0, st, nc, gamma, V, (double)temperature,
+                           zt, zd, drafts, u, n_acc, next, best, margin);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(k_accept, dim3((unsigned)((long long)nb * nc)), dim3(kAccT), 0, st, mode, nc, gamma, V,
+                       (double)temperature, zt, zd, drafts, u, n_acc, next, best, margin);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nc == 1 || !best) return e;
+    hipLaunchKernelGGL(k_accept_best, dim3((nb + 255) / 256), dim3(256), 0, st, nb, nc, n_acc, best);
     return hipGetLastError();
 }
 

@@ -122,7 +122,7 @@ int hci_accept(int mode, int nb, int nc, int gamma, int vocab, float temperature
                double* margin, hipStream_t stream) {
     if (mode != HCI_GREEDY && mode != HCI_SAMPLE && mode != HCI_SAMPLE_RECURSIVE) return HCI_EINVAL;
     if (nb < 1 || nb > 2147483647 || nc < 1 || nc > 64 || gamma < 0 || vocab < 1) return HCI_EINVAL;
-    if (vocab > 65536) return HCI_EUNSUPPORTED;
+    if (vocab > 65536 || (long long)nb * nc > 2147483647LL) return HCI_EUNSUPPORTED;
     if (!target_logits || !n_accepted || !next_token) return HCI_EINVAL;
     if (gamma > 0 && !draft_tokens) return HCI_EINVAL;
     if (mode != HCI_GREEDY) {

@@ -15,10 +15,11 @@
 //           r = slot, slot + 16, ...
 //  phase 2  the same threads compute g_r = sum_j w_outer[j] * fbar[i - j]
 //           from LDS, one fixed-order fma chain per output
-//  phase 3  thread (channel, pole lane) runs the IIR recurrence in fp32
-//           registers over the P positions of each candidate in turn and
-//           writes s_i (a contiguous kilobyte per step); the readout y_i is a
-//           fixed-order butterfly over the 16 pole lanes.
+//  phase 3  thread (channel, candidate, group of four poles) runs the IIR
+//           recurrence in fp32 registers over the P positions and writes
+//           s_i (16 bytes per thread, a contiguous kilobyte per channel group);
+//           the readout y_i adds the group's terms, then the groups by a
+//           fixed-order butterfly over ceil(N/4) lanes.
 // All per-output arithmetic happens in a fixed order that does not depend
 // on P or on the candidate count, so a block forward and P single-position
 // forwards give identical bits for f, s and y.
@@ -63,21 +64,22 @@ __device__ __forceinline__ void conv_iir_block(
     const float* ow = outer_win + (size_t)b * W * d;
     const typename Act<ACT>::T* xb = x + (size_t)b * R * d;
 
-    // IIR parameters and committed state of thread (channel = tid / 16, lane n = tid % 16): poles n, n+16, ...
-    const int lane16 = tid & 15;
-    const int cg = tid >> 4;
-    const int chn = ch0 + cg;
-    const bool scan = chn < d;                          // uniform across the 16-lane group
+    // IIR task of this thread: channel ch0 + tch, poles 4 * tg .. 4 * tg + 3 (G = ceil(N / 4) groups
+    // per channel, rounded up to a power of two), candidates tc, tc + per, ... (see phase 3)
+    const int G = N <= 4 ? 1 : N <= 8 ? 2 : N <= 16 ? 4 : N <= 32 ? 8 : 16;
+    const int tg = tid % G, tch = (tid / G) % kCG, tc = tid / (G * kCG);
+    const int chn = ch0 + tch;
+    const bool scan = chn < d;                          // uniform across the G lanes of a task
     float lm[4], bt[4], cv[4], s0[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int n = lane16 + 16 * r;
+    for (int q = 0; q < 4; ++q) {
+        const int n = 4 * tg + q;
         const bool ok = scan && n < N;
         const size_t o = (size_t)chn * N + n;
-        lm[r] = ok ? lam[o] : 0.f;
-        bt[r] = ok ? beta[o] : 0.f;
-        cv[r] = ok ? cc[o] : 0.f;
-        s0[r] = ok ? iir[(size_t)b * d * N + o] : 0.f;
+        lm[q] = ok ? lam[o] : 0.f;
+        bt[q] = ok ? beta[o] : 0.f;
+        cv[q] = ok ? cc[o] : 0.f;
+        s0[q] = ok ? iir[(size_t)b * d * N + o] : 0.f;
     }
 
     // phase 0: every load of the workgroup in one round: all values go to registers first
@@ -150,27 +152,36 @@ __device__ __forceinline__ void conv_iir_block(
     }
     __syncthreads();
 
-    // phase 3: IIR scan from the committed state, in registers, one candidate after another
-    if (scan) {
-        for (int c = 0; c < nc; ++c) {
-            float s[4] = {s0[0], s0[1], s0[2], s0[3]};
+    // phase 3: IIR scan from the committed state, in registers.  A task = (channel, candidate,
+    // group of 4 poles); 256 / (16 G) candidates advance together.  y_i adds the group's four
+    // terms in pole order, then the G groups by a fixed-order butterfly: the order depends on N
+    // only, never on P or the candidates.
+    {
+        const int per = kConvT / (G * kCG);
+        for (int c = tc; c - tc < nc; c += per) {
+            const bool act = scan && c < nc;
+            float st[4] = {s0[0], s0[1], s0[2], s0[3]};
             for (int i = 0; i < P; ++i) {
                 const int r = c * P + i;
-                const float g = gl[r * kCG + cg];
-                float part_y = 0.f;
+                const float g = act ? gl[r * kCG + tch] : 0.f;
+                float py = 0.f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int n = lane16 + 16 * q;
-                    s[q] = fmaf(lm[q], s[q], bt[q] * g);
-                    if (n < N) s_out[(((size_t)b * R + r) * d + chn) * N + n] = s[q];
-                    part_y = fmaf(cv[q], s[q], part_y);
+                    st[q] = fmaf(lm[q], st[q], bt[q] * g);
+                    py = fmaf(cv[q], st[q], py);
                 }
-                // fixed-order butterfly over the 16 pole lanes of this channel
-                part_y += __shfl_xor(part_y, 8, 16);
-                part_y += __shfl_xor(part_y, 4, 16);
-                part_y += __shfl_xor(part_y, 2, 16);
-                part_y += __shfl_xor(part_y, 1, 16);
-                if (lane16 == 0) Act<ACT>::store(y_out, ((size_t)b * R + r) * d + chn, part_y);
+                if (act) {
+                    float* so = s_out + (((size_t)b * R + r) * d + chn) * N + 4 * tg;
+                    if ((N & 3) == 0) {
+                        *(float4*)so = make_float4(st[0], st[1], st[2], st[3]);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (4 * tg + q < N) so[q] = st[q];
+                    }
+                }
+                for (int off = G >> 1; off >= 1; off >>= 1) py += __shfl_xor(py, off, G);
+                if (act && tg == 0) Act<ACT>::store(y_out, ((size_t)b * R + r) * d + chn, py);
             }
         }
     }
