@@ -48,13 +48,33 @@ __device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, 
     float* st_o = lds + ((size_t)2 * P * DH * sizeof(T) + 3) / 4;   // [state][row][DH]
     float* st_ml = st_o + (size_t)(kCombW + 1) * RG * DH;           // [state][row][2]
 
-    // stage the candidate's block K and V rows 0 .. i0 + nr - 1 (one round trip)
-    const size_t krow0 = ((size_t)b * nq + (size_t)c * P) * H + h;
-    for (int e = tid; e < (i0 + nr) * DH; e += kCombT) {
-        const int j = e / DH, dd = e - j * DH;
-        const size_t src = (krow0 + (size_t)j * H) * DH + dd;
-        ks[e] = kb[src];
-        vs[e] = vb[src];
+    // stage the candidate's block K and V rows 0 .. i0 + nr - 1 in 16-byte pieces (a row is
+    // Dh * act bytes, a multiple of 16); the first pieces of every thread are requested together
+    {
+        const int pr = DH * (int)sizeof(T) / 16;       // pieces per row
+        const int half = (i0 + nr) * pr;               // K pieces, then as many V pieces
+        const size_t krow0 = ((size_t)b * nq + (size_t)c * P) * H + h;
+        auto src = [&](int e) -> const uint4* {
+            const bool isv = e >= half;
+            const int e2 = isv ? e - half : e, j = e2 / pr, u = e2 - j * pr;
+            return (const uint4*)((isv ? vb : kb) + (krow0 + (size_t)j * H) * DH) + u;
+        };
+        auto dst = [&](int e) -> uint4* {
+            return e >= half ? (uint4*)vs + (e - half) : (uint4*)ks + e;
+        };
+        constexpr int SB = 4;
+        uint4 v[SB];
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+            const int e = tid + k * kCombT;
+            v[k] = e < 2 * half ? *src(e) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+            const int e = tid + k * kCombT;
+            if (e < 2 * half) *dst(e) = v[k];
+        }
+        for (int e = tid + SB * kCombT; e < 2 * half; e += kCombT) *dst(e) = *src(e);
     }
 
     // ---- prefix items of (b, h): a running state per row
