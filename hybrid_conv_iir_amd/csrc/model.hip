@@ -10,8 +10,9 @@
 //   k_hyena_mixer    short FIR of the 3d channels, u = zk * zv, the long
 //                    filter (explicit FIR over the u window, or the modal
 //                    IIR keeping every s_i), y = bf16(zq * h)
-//   (attention)      the verify attention path (KV stream, causal block
-//                    part, fixed-order combine) with the conv role off
+//   (attention)      the verify attention path (KV prefix stream, then the
+//                    finish kernel's causal block part and fixed-order merge;
+//                    no conv/IIR work)
 //   k_linear         x' = bf16(x + y W_out)
 // Slicing: k_model_slice (one launch for every layer: both windows, the
 // IIR state, accepted K/V rows into the tiled cache, the drafter's window of
