@@ -485,7 +485,7 @@ def main():
         return bench_draft(args, hip)
     W, K = args.warmup, args.steps
     P = cfg.P
-    kv_cap = (cfg.max_kv_len + (W + K + 2) * P + 31) // 32 * 32
+    kv_cap = (cfg.max_kv_len + (W + 2 * K + 2) * P + 31) // 32 * 32
 
     # ---------------------------------------------------------------- inputs (resident before timing)
     params = synth.make_layer(cfg)
@@ -513,7 +513,7 @@ def main():
     acc.set_inputs(ri["target_logits"], ri["drafts"], ri["draft_logits"], ri["uniforms"])
     mode = hci.GREEDY if cfg.mode == "greedy" else hci.SAMPLE
     bound = cfg.max_kv_len
-    blk.ensure_workspace(bound + (W + K + 1) * P)
+    blk.ensure_workspace(bound + (W + 2 * K + 1) * P)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
@@ -538,10 +538,10 @@ def main():
         else:
             hci.verify_block_timed(lay.c, st.c, blk.c, blk.nb, blk.nc, blk.gamma, bound, blk.ws, evs)
         dv.accept(acc, mode, cfg.temperature)
-        if evs is not None:
+        if evs is not None and evs[3]:
             hip.hipEventRecord(evs[3], sp)
         dv.slice_state(lay, st, blk, acc, bound)
-        if evs is not None:
+        if evs is not None and evs[4]:
             hip.hipEventRecord(evs[4], sp)
         bound += P
 
@@ -551,17 +551,30 @@ def main():
     len_before = dv.to_host(st.kv_len).astype(np.int64)
 
     # ---------------------------------------------------------------- timed region
-    evsets = [_events(hip, 5) for _ in range(K)]
+    # Only the two events around the streaming kernel are recorded here (its
+    # average launch time is the roofline's denominator); an event record costs
+    # a few microseconds of device time, so the per-part breakdown comes from a
+    # second, untimed pass below.
+    stream_evs = []
+    for _ in range(K):
+        e = _events(hip, 5)
+        e[2] = e[3] = e[4] = None
+        stream_evs.append(e)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(evsets[i])
+        step(stream_evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     len_after = dv.to_host(st.kv_len).astype(np.int64)
-
     ms_step = (t1 - t0) * 1e3 / K
-    stream_ms = [_ms(hip, e[0], e[1]) for e in evsets]
+    stream_ms = [_ms(hip, e[0], e[1]) for e in stream_evs]
+
+    # ---------------------------------------------------------------- breakdown pass (not timed)
+    evsets = [_events(hip, 5) for _ in range(K)]
+    for i in range(K):
+        step(evsets[i])
+    torch.cuda.synchronize()
     combine_ms = [_ms(hip, e[1], e[2]) for e in evsets]
     verify_ms = [_ms(hip, e[0], e[2]) for e in evsets]
     accept_ms = [_ms(hip, e[2], e[3]) for e in evsets]
@@ -597,7 +610,7 @@ def main():
         "verify_hbm_GBs": round(alg_verify / (float(np.median(verify_ms)) * 1e-3) / 1e9, 1),
         "verify_pct_of_8TBs": round(100.0 * alg_verify / (float(np.median(verify_ms)) * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "verify_positions_per_s": round(positions / (float(np.median(verify_ms)) * 1e-3), 1),
-        "breakdown_ms_median": {"verify_stream": round(float(np.median(stream_ms)), 4),
+        "breakdown_ms_median": {"verify_stream": round(float(np.median([_ms(hip, e[0], e[1]) for e in evsets])), 4),
                                 "verify_finish": round(float(np.median(combine_ms)), 4),
                                 "accept": round(float(np.median(accept_ms)), 4),
                                 "slice": round(float(np.median(slice_ms)), 4),
