@@ -84,10 +84,8 @@ def verify_alg_bytes(cfg, kv_lens) -> int:
 
 
 def stream_kernel_name(cfg) -> str:
-    """The kernel that streams the KV prefix for this workload (one 16-query tile or several)."""
-    if cfg.act != "bf16":
-        return "k_attn_prefix_f32"
-    return "k_verify_stream" if cfg.nc * cfg.P <= 16 else "k_attn_prefix_shared"
+    """The kernel that streams the KV prefix for this workload."""
+    return "k_verify_stream" if cfg.act == "bf16" else "k_attn_prefix_f32"
 
 
 def stream_alg_bytes(cfg, kv_lens) -> int:
@@ -102,7 +100,6 @@ def stream_alg_bytes(cfg, kv_lens) -> int:
 
 
 VERIFY_SOURCES = ("stream_one.hip", "prefix_tile.h", "worklist.h", "hci_internal.h")
-SHARED_SOURCES = ("stream_shared.hip", "prefix_tile.h", "worklist.h", "hci_internal.h")
 PREFILL_SOURCES = ("prefill.hip", "slice.hip", "hci_internal.h")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_c3_traffic.json")
 
@@ -620,8 +617,7 @@ def main():
         "roofline": {"kernel": stream_kernel_name(cfg),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": _traffic(args.config, traffic_file(args.config),
-                                         SHARED_SOURCES if cfg.nc * cfg.P > 16 else VERIFY_SOURCES),
+                     "traffic": _traffic(args.config, traffic_file(args.config)),
                      "alg_bytes_per_launch": int(alg_stream),
                      "avg_launch_ms": round(avg_stream_s * 1e3, 4)},
         "accepted_per_step": [int(x) for x in ((len_after - len_before) // K)],

@@ -11,9 +11,9 @@
 // units, normaliser, unnormalised output), and the finish kernel computes the
 // causal block part and merges everything in a fixed order.
 //
-// Work distribution.  The bf16 streaming kernels (stream_one.hip for one
-// 16-query tile, stream_shared.hip for several) run persistent workgroups that
-// take prefix items from a queue (an atomic ticket counter in the workspace,
+// Work distribution.  The bf16 streaming kernel (stream_one.hip; one to four
+// 16-query tiles per wave) runs one persistent workgroup per CU that takes
+// prefix items from a queue (an atomic ticket counter in the workspace,
 // zeroed by a one-thread kernel before each launch) until it is empty.  Items
 // come in decreasing size: phase p covers the next half of what is left of
 // every sequence's prefix in chunks of c0 / 2^p tiles, c0 being half of a
@@ -152,7 +152,7 @@ AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_k
     AttnPlan p{};
     const int P = gamma + 1;
     p.nq = nc * P;
-    p.resident = (num_cus > 0 ? num_cus : 1) * (p.nq > 16 ? kSlotsShared : kSlotsFused);
+    p.resident = (num_cus > 0 ? num_cus : 1) * kStreamSlots;
     p.kv_lim = max_kv_len;    // callers check max_kv_len + P <= kv_cap before any launch
     const long long tiles = (max_kv_len + kTile - 1) / kTile;
     const long long nbh = (long long)nb * L->heads;
@@ -206,7 +206,7 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
             hipLaunchKernelGGL(k_ticket_reset, dim3(1), dim3(64), 0, st, ticket);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             const int blocks = plan.items_cap < plan.resident ? plan.items_cap : plan.resident;
-            e = nqt > 1 ? launch_stream_shared(A, DH, nqt, blocks, st) : launch_stream_one(A, DH, blocks, st);
+            e = launch_stream_one(A, DH, nqt, blocks, st);
             if (e != hipSuccess) return e;
         } else {
             hipLaunchKernelGGL(k_attn_prefix_f32, dim3(plan.items_cap), dim3(64), 0, st,
@@ -228,7 +228,7 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
     F.q = blk->q; F.kb = blk->k; F.vb = blk->v; F.o = blk->o;
     F.nb = nb; F.H = H; F.DH = DH; F.nq = nq; F.P = P; F.kv_lim = plan.kv_lim; F.resident = plan.resident;
     F.scale_log2 = scale_log2;
-    const int rg = combine_rows(nb, nc, H, P, plan.resident / (nq > 16 ? kSlotsShared : kSlotsFused));
+    const int rg = combine_rows(nb, nc, H, P, plan.resident / kStreamSlots);
     F.rg_count = (P + rg - 1) / rg;
     const long long blocks = (long long)F.n_conv + (long long)F.rg_count * nc * H * nb;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;

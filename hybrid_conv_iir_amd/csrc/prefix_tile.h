@@ -15,13 +15,10 @@ namespace hci {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kRoleT = 256;            // threads per workgroup of every streaming kernel
 constexpr int kPrefixWaves = 4;        // waves per streaming workgroup
-// resident streaming workgroups per CU.  The one-tile kernel keeps one, so that no two
-// workgroups on a CU compete for issue (the older one would run up to twice as fast and
-// finish its items late); its four waves keep enough loads in flight.  The several-tile
-// kernel needs two to overlap one workgroup's matrix-core and softmax work with the
-// other's barrier waits.
-constexpr int kSlotsFused = 1;
-constexpr int kSlotsShared = 2;
+// resident streaming workgroups per CU: one, so that no two workgroups on a CU compete for
+// issue (the older one would run up to twice as fast and finish its items late); its four
+// waves keep enough loads in flight
+constexpr int kStreamSlots = 1;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -39,6 +36,16 @@ struct StreamArgs {
     int H, kv_cap, kv_lim, nq, nb, resident;
     float scale_log2;
 };
+
+// Maximum over lanes l, l^16, l^32 and l^48 (the four 4-key row groups that hold one query
+// column of a 16x16 product), on the vector ALU: two gfx950 lane swaps, each exchanging a
+// value with the partner half (32 lanes apart) or row (16 lanes apart) of the wave.
+__device__ __forceinline__ float max_over_row_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 template <int DH, int NQT>
 struct PrefixAcc {
@@ -102,8 +109,7 @@ __device__ __forceinline__ void consume_tile(PrefixAcc<DH, NQT>& a, KvTile<DH>& 
         }
         float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_over_row_groups(mx);
         const float mnew = fmaxf(a.m[nt], mx);
         const float alpha = __builtin_amdgcn_exp2f(a.m[nt] - mnew);
         a.m[nt] = mnew;
@@ -133,8 +139,7 @@ __device__ __forceinline__ void consume_tile(PrefixAcc<DH, NQT>& a, KvTile<DH>& 
     }
 }
 
-// launchers of the two streaming kernels (grid = blocks persistent workgroups)
-hipError_t launch_stream_one(const StreamArgs& A, int head_dim, int blocks, hipStream_t st);
-hipError_t launch_stream_shared(const StreamArgs& A, int head_dim, int nqt, int blocks, hipStream_t st);
+// launcher of the streaming kernel (grid = blocks persistent workgroups, nqt 16-query tiles)
+hipError_t launch_stream_one(const StreamArgs& A, int head_dim, int nqt, int blocks, hipStream_t st);
 
 }  // namespace hci
