@@ -4,8 +4,13 @@
 // in flight, and merge their softmax states in LDS before one partial per
 // query is written.  Every wave applies all NQT 16-query tiles of the sequence
 // (nc * P <= 16 NQT queries, NQT <= 4) to each KV tile it streams, so a KV
-// tile is read from HBM once, into the registers of one wave, and no LDS
-// staging or per-tile barrier sits in the streaming loop.
+// tile is read from HBM once, by one wave, and no barrier sits in the
+// streaming loop.  With one or two query tiles the tiles in flight sit in
+// registers (three buffers); with three or four the query and accumulator
+// registers leave no room for them, and each wave streams through a private
+// two-slot LDS ring filled by direct global->LDS loads instead: it copies
+// tile T from its slot into registers, refills the slot with tile T+2 and
+// computes tile T, so two tiles stay in flight.
 #include "prefix_tile.h"
 
 namespace hci {
@@ -16,6 +21,15 @@ __host__ __device__ constexpr size_t prefix_merge_floats() {
     return (size_t)16 * DH + 2 * 16;
 }
 
+// LDS pool of the kernel, in uint4: the merge states of every wave and query tile, which
+// with three or four query tiles share the space of the waves' two-slot tile rings
+template <int DH, int NQT>
+__host__ __device__ constexpr size_t stream_pool_uint4() {
+    const size_t merge = (kPrefixWaves * NQT * prefix_merge_floats<DH>() + 3) / 4;
+    const size_t ring = NQT >= 3 ? (size_t)kPrefixWaves * 2 * (8 * DH) : 0;
+    return merge > ring ? merge : ring;
+}
+
 // One prefix item: tiles [t0, t1) of head h of sequence b, all nq <= 16 NQT
 // queries, written to partial `slot`.  The four waves take contiguous runs of
 // the item; each streams its run with the next two tiles' loads in flight
@@ -24,50 +38,92 @@ __host__ __device__ constexpr size_t prefix_merge_floats() {
 // caller's barriers stay matched.
 template <int DH, int NQT>
 __device__ __forceinline__ void prefix_item(const StreamArgs& A, int b, int h, int t0, int t1, long long slot,
-                                            float* merge, unsigned& next)
+                                            uint4* lds_pool, unsigned& next)
 {
+    float* merge = (float*)lds_pool;
     constexpr int J = DH / 32, DT = DH / 16, KV4 = 4 * DH;
     constexpr size_t MF = prefix_merge_floats<DH>();
     const int L = prefix_len(A.kv_len, b, A.kv_lim);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+    // the wave index is uniform across the wave: said so, every run bound and the waits on
+    // them stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
     const int per = (t1 - t0 + kPrefixWaves - 1) / kPrefixWaves;
     const int w0 = min(t0 + wave * per, t1), w1 = min(w0 + per, t1);
 
     PrefixAcc<DH, NQT> a;
+    auto load_q = [&]() {
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) {
+            const int qi = 16 * nt + n;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (qi < A.nq) v = *(const uint4*)(A.q + (((size_t)b * A.nq + qi) * A.H + h) * DH + 32 * j + 8 * g);
+                a.q[nt][j] = as_bf16x8(v);
+            }
+        }
+    };
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
-        const int qi = 16 * nt + n;
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (qi < A.nq) v = *(const uint4*)(A.q + (((size_t)b * A.nq + qi) * A.H + h) * DH + 32 * j + 8 * g);
-            a.q[nt][j] = as_bf16x8(v);
-        }
         a.m[nt] = -INFINITY;
         a.l[nt] = 0.f;
 #pragma unroll
         for (int t = 0; t < DT; ++t) a.o[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    if constexpr (NQT < 3) load_q();
 
     const size_t slab = ((size_t)b * A.H + h) * (size_t)(A.kv_cap / kTile) * KV4;
     const uint4* kp = (const uint4*)A.kc + slab;
     const uint4* vp = (const uint4*)A.vc + slab;
-    if (w0 < w1 && NQT >= 3) {
-        // two register buffers, one tile in flight: with three or four query tiles a KV tile
-        // takes several times longer to consume, and the registers go to the accumulators
-        KvTile<DH> ta, tb;
-        int T = w0;
-        load_tile<DH>(ta, kp, vp, T, lane);
-        for (; T + 2 < w1; T += 2) {
-            load_tile<DH>(tb, kp, vp, T + 1, lane);
-            consume_tile<DH, NQT>(a, ta, T, L, g, A.scale_log2);
-            load_tile<DH>(ta, kp, vp, T + 2, lane);
-            consume_tile<DH, NQT>(a, tb, T + 1, L, g, A.scale_log2);
+    if constexpr (NQT >= 3) {
+        // the wave's ring: two slots of one tile (K then V, as stored) in the LDS pool
+        constexpr int PT = 2 * KV4 / 64;               // direct loads per lane per tile
+        const uint4* ring = lds_pool + (size_t)wave * 2 * (2 * KV4);
+        const uint32_t ring0 = lds_offset(ring);
+        auto issue = [&](int slot, int T) {
+            const uint32_t dst = ring0 + (uint32_t)slot * (uint32_t)(2 * KV4 * sizeof(uint4));
+            const size_t base = (size_t)T * KV4 + lane;
+#pragma unroll
+            for (int i = 0; i < PT; ++i) {
+                const uint4* src = i < PT / 2 ? kp + base + i * 64 : vp + base + (i - PT / 2) * 64;
+                dma16_nt(src, dst + (uint32_t)(i * 64 * sizeof(uint4)));
+            }
+        };
+        // the queries are requested first (any wait the compiler places around them comes
+        // before a direct load is in flight), then the item's first two tiles, so the three
+        // latencies overlap.  One wait for every load follows (a count that never falls short,
+        // whichever query loads the wave skipped; the two tiles arrive together anyway): the
+        // compiler then knows its own loads are complete and never waits for a direct load.
+        load_q();
+        compiler_fence();
+        if (w0 < w1) issue(0, w0);
+        if (w0 + 1 < w1) issue(1, w0 + 1);
+        compiler_fence();
+        HCI_WAIT_VM(0);
+        compiler_fence();
+        KvTile<DH> cur;
+        int slot = 0;
+        for (int T = w0; T < w1; ++T) {
+            // this wave's loads of tile T are done once at most tile T+1's are outstanding
+            if (T > w0) {
+                if (T + 1 < w1) HCI_WAIT_VM(PT); else HCI_WAIT_VM(0);
+            }
+            compiler_fence();
+            const uint4* src = ring + (size_t)slot * (2 * KV4);
+#pragma unroll
+            for (int i = 0; i < DH / 16; ++i) cur.k[i] = src[i * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < DH / 16; ++i) cur.v[i] = src[KV4 + i * 64 + lane];
+            compiler_fence();
+            HCI_WAIT_LGKM0();                          // the slot is read: refill it
+            compiler_fence();
+            if (T + 2 < w1) issue(slot, T + 2);
+            consume_tile<DH, NQT>(a, cur, T, L, g, A.scale_log2);
+            slot ^= 1;
         }
-        // 1 or 2 tiles left: T (in ta) is loaded
-        if (T + 1 < w1) load_tile<DH>(tb, kp, vp, T + 1, lane);
-        consume_tile<DH, NQT>(a, ta, T, L, g, A.scale_log2);
-        if (T + 1 < w1) consume_tile<DH, NQT>(a, tb, T + 1, L, g, A.scale_log2);
+        // every wave is done with its ring before the merge states overwrite the pool
+        __syncthreads();
     } else if (w0 < w1) {
         // three register buffers, two tiles in flight ahead of the one consumed; the loads
         // inside the loop are unconditional, so the compiler's waits are exact
@@ -153,7 +209,7 @@ __device__ __forceinline__ void prefix_item(const StreamArgs& A, int b, int h, i
 template <int DH, int NQT>
 __global__ __launch_bounds__(kRoleT, kStreamSlots) void k_verify_stream(StreamArgs A)
 {
-    __shared__ float merge[kPrefixWaves * NQT * prefix_merge_floats<DH>()];
+    __shared__ uint4 lds_pool[stream_pool_uint4<DH, NQT>()];
     __shared__ unsigned s_ticket;
     const WorkList w = make_worklist(A.kv_len, A.nb, A.H, A.kv_lim, A.resident);
     const long long total = work_count(A.kv_len, w);
@@ -165,7 +221,7 @@ __global__ __launch_bounds__(kRoleT, kStreamSlots) void k_verify_stream(StreamAr
         if (t >= total) break;
         unsigned next = 0xffffffffu;                   // past the end unless the item takes a ticket
         int b = 0, h = 0, t0 = 0, t1 = 0;
-        if (work_item(A.kv_len, w, t, b, h, t0, t1)) prefix_item<DH, NQT>(A, b, h, t0, t1, t, merge, next);
+        if (work_item(A.kv_len, w, t, b, h, t0, t1)) prefix_item<DH, NQT>(A, b, h, t0, t1, t, lds_pool, next);
         if (threadIdx.x == 0) s_ticket = next;
         __syncthreads();
     }

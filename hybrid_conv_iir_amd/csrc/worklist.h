@@ -10,9 +10,13 @@ namespace hci {
 
 // Committed length of sequence b as the attention reads it: kv_len clamped to
 // [0, lim], lim = min(kv_cap, max_kv_len), so that a length above the host's
-// bound can never yield more work than the host planned for.
+// bound can never yield more work than the host planned for.  kv_len does not
+// change while the verify kernels run, so it is read through the constant
+// address space: with a wave-uniform b that is a scalar load served by the
+// scalar cache, not a vector load queued behind the prefix stream (the work
+// list is decoded at every item start).
 __device__ __forceinline__ int prefix_len(const int32_t* kv_len, int b, int lim) {
-    const int L = kv_len[b];
+    const int L = ((const __attribute__((address_space(4))) int32_t*)kv_len)[b];
     return L < 0 ? 0 : (L > lim ? lim : L);
 }
 
