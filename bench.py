@@ -12,7 +12,7 @@ timed region starts.
 Prints ONE JSON line (metric, value = verified block-positions per second,
 roofline of the prefix-attention kernel, CPU oracle baseline, ...).
 
-    python bench.py [--steps K] [--warmup W] [--config c3|c3g6|c2|c4|c5]
+    python bench.py [--steps K] [--warmup W] [--config long262k|long262k_g6|mid8k|multi4x4|wide131k]
 """
 from __future__ import annotations
 
@@ -30,17 +30,17 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 WORKLOAD_NAMES = {
-    "c3": "long-context verify: d=4096, FIR 3/128 taps, 16 poles, 32x128 heads, 262144-token bf16 KV prefix, gamma=12, greedy",
-    "c3g6": "long-context verify: d=4096, FIR 3/128 taps, 16 poles, 32x128 heads, 262144-token bf16 KV prefix, gamma=6, greedy",
-    "c2": "mid-size verify: d=4096, FIR 3/128 taps, 16 poles, 32x128 heads, 8192-token bf16 KV prefix, gamma=12, sampling T=1",
-    "c4": "batched multi-candidate verify: 4 sequences x 4 candidates, KV prefixes 16384/32768/51200/65536, gamma=12, sampling",
-    "c5": "wide layer: d=8192, FIR 3/128 taps, 16 poles, 64x128 heads, 131072-token bf16 KV prefix, gamma=12, greedy",
+    "long262k": "long-context verify: d=4096, FIR 3/128 taps, 16 poles, 32x128 heads, 262144-token bf16 KV prefix, gamma=12, greedy",
+    "long262k_g6": "long-context verify: d=4096, FIR 3/128 taps, 16 poles, 32x128 heads, 262144-token bf16 KV prefix, gamma=6, greedy",
+    "mid8k": "mid-size verify: d=4096, FIR 3/128 taps, 16 poles, 32x128 heads, 8192-token bf16 KV prefix, gamma=12, sampling T=1",
+    "multi4x4": "batched multi-candidate verify: 4 sequences x 4 candidates, KV prefixes 16384/32768/51200/65536, gamma=12, sampling",
+    "wide131k": "wide layer: d=8192, FIR 3/128 taps, 16 poles, 64x128 heads, 131072-token bf16 KV prefix, gamma=12, greedy",
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_stream_c3_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_stream_long262k_traffic.json")
 
 
 def traffic_file(cfg_name: str) -> str:
-    """Counter summary of the prefix-streaming kernel for one workload (c3: k_verify_stream, c4: the shared one)."""
+    """Counter summary of the prefix-streaming kernel for one workload."""
     return os.path.join(ROOT, "profiles", f"verify_stream_{cfg_name}_traffic.json")
 
 
@@ -101,7 +101,7 @@ def stream_alg_bytes(cfg, kv_lens) -> int:
 
 VERIFY_SOURCES = ("stream_one.hip", "prefix_tile.h", "worklist.h", "hci_internal.h")
 PREFILL_SOURCES = ("prefill.hip", "slice.hip", "hci_internal.h")
-PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_c3_traffic.json")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_long262k_traffic.json")
 
 
 def _kernel_sha(sources=VERIFY_SOURCES) -> str:
@@ -438,7 +438,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c3", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--config", default="long262k", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-oracle sample (0 = all)")
     ap.add_argument("--cpu-reps", type=int, default=3, help="repetitions of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")

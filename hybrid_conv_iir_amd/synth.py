@@ -9,11 +9,11 @@ Workloads follow the five operating points of the EvSpark digest (Synopsis
 and Perspective: 7B-scale layers, 51k-262k context, batching, multiple
 candidates, sustained generation) as fixed synthetic shapes:
 
-* ``c1``  tiny fp32 layer: d=64, 3/7 FIR taps, 16 poles, 1 head x 64, L=256, gamma=6
-* ``c2``  d=4096, bf16, 3/128 taps, 16 poles, 32 heads x 128, L=8192, gamma=12, sampling
-* ``c3``  c2's layer at L=262144, gamma=12 (``c3``) or gamma=6 (``c3g6``), greedy
-* ``c4``  4 sequences x 4 candidates, ragged L in {16384, 32768, 51200, 65536}
-* ``c5``  d=8192, 64 heads x 128, L=131072, gamma=12, 256 sustained rounds
+* ``tiny``  fp32 layer: d=64, 3/7 FIR taps, 16 poles, 1 head x 64, L=256, gamma=6
+* ``mid8k``  d=4096, bf16, 3/128 taps, 16 poles, 32 heads x 128, L=8192, gamma=12, sampling
+* ``long262k``  the mid8k layer at L=262144, gamma=12 (``long262k``) or gamma=6 (``long262k_g6``), greedy
+* ``multi4x4``  4 sequences x 4 candidates, ragged L in {16384, 32768, 51200, 65536}
+* ``wide131k``  d=8192, 64 heads x 128, L=131072, gamma=12, 256 sustained rounds
 
 Distributions (variance readings): FIR taps N(0, 1/taps); poles U(0.5, 0.99);
 input and readout gains N(0, 1/16); activations and KV N(0, 1); logits N(0, 2).
@@ -86,17 +86,17 @@ class Config:
 
 
 CONFIGS: Dict[str, Config] = {
-    "c1": Config("c1", 1, d=64, taps_short=3, taps_outer=7, poles=16, heads=1, head_dim=64,
+    "tiny": Config("tiny", 1, d=64, taps_short=3, taps_outer=7, poles=16, heads=1, head_dim=64,
                  kv_lens=(256,), gamma=6, act=F32, mode="sample"),
-    "c2": Config("c2", 2, d=4096, taps_short=3, taps_outer=128, poles=16, heads=32, head_dim=128,
+    "mid8k": Config("mid8k", 2, d=4096, taps_short=3, taps_outer=128, poles=16, heads=32, head_dim=128,
                  kv_lens=(8192,), gamma=12, act=BF16, mode="sample"),
-    "c3": Config("c3", 3, d=4096, taps_short=3, taps_outer=128, poles=16, heads=32, head_dim=128,
+    "long262k": Config("long262k", 3, d=4096, taps_short=3, taps_outer=128, poles=16, heads=32, head_dim=128,
                  kv_lens=(262144,), gamma=12, act=BF16, mode="greedy"),
-    "c3g6": Config("c3g6", 6, d=4096, taps_short=3, taps_outer=128, poles=16, heads=32, head_dim=128,
+    "long262k_g6": Config("long262k_g6", 6, d=4096, taps_short=3, taps_outer=128, poles=16, heads=32, head_dim=128,
                    kv_lens=(262144,), gamma=6, act=BF16, mode="greedy"),
-    "c4": Config("c4", 4, d=4096, taps_short=3, taps_outer=128, poles=16, heads=32, head_dim=128,
+    "multi4x4": Config("multi4x4", 4, d=4096, taps_short=3, taps_outer=128, poles=16, heads=32, head_dim=128,
                  kv_lens=(16384, 32768, 51200, 65536), gamma=12, nc=4, act=BF16, mode="sample"),
-    "c5": Config("c5", 5, d=8192, taps_short=3, taps_outer=128, poles=16, heads=64, head_dim=128,
+    "wide131k": Config("wide131k", 5, d=8192, taps_short=3, taps_outer=128, poles=16, heads=64, head_dim=128,
                  kv_lens=(131072,), gamma=12, act=BF16, mode="greedy", rounds=256),
 }
 

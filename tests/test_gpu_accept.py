@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _inputs(V, gamma, nb, nc, T, mode, seed):
-    cfg = synth.scaled(synth.CONFIGS["c2"], vocab=V, gamma=gamma, kv_lens=(0,) * nb, nc=nc, mode=mode,
+    cfg = synth.scaled(synth.CONFIGS["mid8k"], vocab=V, gamma=gamma, kv_lens=(0,) * nb, nc=nc, mode=mode,
                        temperature=T, cfg_id=100 + seed)
     anchor = synth.anchors(cfg, 0, seed)
     return cfg, synth.round_inputs(cfg, anchor, 0, seed)
@@ -94,7 +94,7 @@ def test_recursive_prefix_keyed_inputs(V, nc, gamma, T):
     nb = 3
     deep = 0
     for seed in range(3):
-        cfg = synth.scaled(synth.CONFIGS["c4"], vocab=V, gamma=gamma, kv_lens=(0,) * nb, nc=nc, mode="sample",
+        cfg = synth.scaled(synth.CONFIGS["multi4x4"], vocab=V, gamma=gamma, kv_lens=(0,) * nb, nc=nc, mode="sample",
                            temperature=T, cfg_id=300 + seed)
         zt, zd, drafts, u = synth.prefix_keyed_round(cfg, 0, seed, scale=3.0 if V < 10 else 1.4)
         say(f"recursive prefix-keyed V={V} nc={nc} gamma={gamma} T={T} seed={seed}")
@@ -124,7 +124,7 @@ def test_recursive_one_candidate_is_sample_mode_bitwise():
 
 
 def test_recursive_invalid_ids_and_full_acceptance():
-    cfg = synth.scaled(synth.CONFIGS["c4"], vocab=64, gamma=6, kv_lens=(0,), nc=3, mode="sample", cfg_id=320)
+    cfg = synth.scaled(synth.CONFIGS["multi4x4"], vocab=64, gamma=6, kv_lens=(0,), nc=3, mode="sample", cfg_id=320)
     zt, zd, drafts, u = synth.prefix_keyed_round(cfg, 0, 1)
     zd = zt[:, :, :cfg.gamma].copy()               # q == p everywhere: candidate 0 keeps every draft
     say("recursive q == p")

@@ -52,7 +52,7 @@ def _sequential(case: Case, st: dv.DeviceState, blk1: dv.DeviceBlock, acc1: dv.D
     return {k: np.stack(v) for k, v in outs.items()}
 
 
-@pytest.mark.parametrize("cfgname,L", [("c1", 256), ("c2", 1000), ("c2", 8192)])
+@pytest.mark.parametrize("cfgname,L", [("tiny", 256), ("mid8k", 1000), ("mid8k", 8192)])
 def test_block_plus_slice_equals_sequential_steps(cfgname, L):
     cfg = synth.scaled(synth.CONFIGS[cfgname], kv_lens=(L,), mode="greedy")
     base = Case(cfg, host_prefix=False)
@@ -85,7 +85,7 @@ def test_block_plus_slice_equals_sequential_steps(cfgname, L):
 
 def test_abandoned_round_can_be_verified_again():
     """Verify never commits: verify, skip slice, verify again -> identical outputs."""
-    case = Case(synth.scaled(synth.CONFIGS["c2"], kv_lens=(3000,)), host_prefix=False)
+    case = Case(synth.scaled(synth.CONFIGS["mid8k"], kv_lens=(3000,)), host_prefix=False)
     say("abandoned round")
     case.run_verify()
     torch.cuda.synchronize()
@@ -100,9 +100,9 @@ ATTN_ROUNDS = {0, 1, 63, 127, 255}
 ATTN_HEADS = [0, 17, 42, 63]
 
 
-def test_c5_sustained_loop_state_equality():
-    cfg = synth.CONFIGS["c5"]
-    say(f"c5 set-up: d={cfg.d} H={cfg.heads} L={cfg.kv_lens[0]}")
+def test_wide131k_sustained_loop_state_equality():
+    cfg = synth.CONFIGS["wide131k"]
+    say(f"wide131k set-up: d={cfg.d} H={cfg.heads} L={cfg.kv_lens[0]}")
     case = Case(cfg, host_prefix=False)
     kp = synth.kv_prefix(cfg, 0, "k", 0, device="cuda")
     vp = synth.kv_prefix(cfg, 0, "v", 0, device="cuda")
@@ -124,7 +124,7 @@ def test_c5_sustained_loop_state_equality():
         case.blk.set_inputs(bn["x"], bn["q"], bn["k"], bn["v"])
         case.acc.set_inputs(ri["target_logits"], ri["drafts"])
         if r % 32 == 0:
-            say(f"c5 round {r} L={L}")
+            say(f"wide131k round {r} L={L}")
         dv.verify(case.lay, case.st, case.blk, L)
         dv.accept(case.acc, hci.GREEDY)
         dv.slice_state(case.lay, case.st, case.blk, case.acc, L)
@@ -151,7 +151,7 @@ def test_c5_sustained_loop_state_equality():
         so, yo = oracle.modal_iir(go, ost.iir, layer.lam, layer.beta, layer.c)
         assert_out_close(cfg, dv.to_host(case.blk.y)[0, 0], yo, f"round {r} y")
         if r in ATTN_ROUNDS:
-            say(f"c5 round {r}: oracle attention on heads {ATTN_HEADS}")
+            say(f"wide131k round {r}: oracle attention on heads {ATTN_HEADS}")
             oo = oracle.block_attention(q[:, ATTN_HEADS], kk[:, ATTN_HEADS], vv[:, ATTN_HEADS],
                                         ost.k_blocks, ost.v_blocks)
             assert_out_close(cfg, dv.to_host(case.blk.o)[0, 0][:, ATTN_HEADS], oo, f"round {r} o")
@@ -163,5 +163,5 @@ def test_c5_sustained_loop_state_equality():
         L += k + 1
         assert int(snap["kv_len"][0]) == L
         anchor = np.array([nxt], np.int32)
-    say(f"c5 done: {len(ks)} rounds, mean k {np.mean(ks):.2f}, hist {np.bincount(ks, minlength=cfg.P)}")
+    say(f"wide131k done: {len(ks)} rounds, mean k {np.mean(ks):.2f}, hist {np.bincount(ks, minlength=cfg.P)}")
     assert len(set(ks)) >= 5

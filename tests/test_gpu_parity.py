@@ -77,85 +77,85 @@ def _check_round(case: Case, heads=None, check_accept=True):
     return n_acc
 
 
-def test_c1_tiny_fp32_sampling():
-    _check_round(Case(synth.CONFIGS["c1"]))
+def test_tiny_tiny_fp32_sampling():
+    _check_round(Case(synth.CONFIGS["tiny"]))
 
 
-def test_c1_tiny_fp32_greedy():
-    _check_round(Case(synth.scaled(synth.CONFIGS["c1"], mode="greedy")))
+def test_tiny_tiny_fp32_greedy():
+    _check_round(Case(synth.scaled(synth.CONFIGS["tiny"], mode="greedy")))
 
 
 @pytest.mark.parametrize("k", [0, 3, 6])
-def test_c1_forced_k_fig1(k):
+def test_tiny_forced_k_fig1(k):
     """Figure 1(c)/(d) shape: gamma = 6 with a planted accepted length."""
-    _check_round(Case(synth.scaled(synth.CONFIGS["c1"], mode="greedy"), forced_len=[k]))
+    _check_round(Case(synth.scaled(synth.CONFIGS["tiny"], mode="greedy"), forced_len=[k]))
 
 
-def test_c1_needles():
-    _check_round(Case(synth.CONFIGS["c1"], needle="self"))
-    _check_round(Case(synth.CONFIGS["c1"], needle="future"))
+def test_tiny_needles():
+    _check_round(Case(synth.CONFIGS["tiny"], needle="self"))
+    _check_round(Case(synth.CONFIGS["tiny"], needle="future"))
 
 
-def test_c2_mid_bf16_sampling():
-    _check_round(Case(synth.CONFIGS["c2"]))
+def test_mid8k_mid_bf16_sampling():
+    _check_round(Case(synth.CONFIGS["mid8k"]))
 
 
 @pytest.mark.parametrize("needle", ["self", "future"])
-def test_c2_needles(needle):
-    _check_round(Case(synth.CONFIGS["c2"], needle=needle))
+def test_mid8k_needles(needle):
+    _check_round(Case(synth.CONFIGS["mid8k"], needle=needle))
 
 
 @pytest.mark.parametrize("L", [0, 1, 31, 33, 1000])
 def test_ragged_and_empty_prefix(L):
-    cfg = synth.scaled(synth.CONFIGS["c2"], kv_lens=(L,), heads=4, d=256)
+    cfg = synth.scaled(synth.CONFIGS["mid8k"], kv_lens=(L,), heads=4, d=256)
     _check_round(Case(cfg, needle="self"))
 
 
 def test_gamma_zero_and_max_block():
-    _check_round(Case(synth.scaled(synth.CONFIGS["c2"], gamma=0, kv_lens=(500,), heads=2, d=128)))
-    _check_round(Case(synth.scaled(synth.CONFIGS["c2"], gamma=63, kv_lens=(777,), heads=2, d=128)))
+    _check_round(Case(synth.scaled(synth.CONFIGS["mid8k"], gamma=0, kv_lens=(500,), heads=2, d=128)))
+    _check_round(Case(synth.scaled(synth.CONFIGS["mid8k"], gamma=63, kv_lens=(777,), heads=2, d=128)))
 
 
 def test_head_dim_64_bf16():
-    _check_round(Case(synth.scaled(synth.CONFIGS["c2"], head_dim=64, heads=4, d=256, kv_lens=(3000,)), needle="self"))
+    _check_round(Case(synth.scaled(synth.CONFIGS["mid8k"], head_dim=64, heads=4, d=256, kv_lens=(3000,)), needle="self"))
 
 
 def test_capacity_edge_exactly_full():
-    cfg = synth.scaled(synth.CONFIGS["c2"], kv_lens=(1011,), heads=2, d=128)   # 1011 + 13 = 1024 = kv_cap
+    cfg = synth.scaled(synth.CONFIGS["mid8k"], kv_lens=(1011,), heads=2, d=128)   # 1011 + 13 = 1024 = kv_cap
     _check_round(Case(cfg, kv_cap=1024))
 
 
-@pytest.mark.parametrize("name", ["c3", "c3g6"])
-def test_c3_long_context_full_size(name):
+@pytest.mark.parametrize("name", ["long262k", "long262k_g6"])
+def test_long262k_long_context_full_size(name):
     _check_round(Case(synth.CONFIGS[name]))
 
 
-def test_c3_needles_full_size():
-    _check_round(Case(synth.CONFIGS["c3"], needle="self"))
+def test_long262k_needles_full_size():
+    _check_round(Case(synth.CONFIGS["long262k"], needle="self"))
 
 
-def test_c4_multi_candidate_ragged_full_size():
-    _check_round(Case(synth.CONFIGS["c4"]))
+def test_multi4x4_multi_candidate_ragged_full_size():
+    _check_round(Case(synth.CONFIGS["multi4x4"]))
 
 
-def test_c4_recursive_acceptance_full_size():
+def test_multi4x4_recursive_acceptance_full_size():
     """The 4-candidate workload with lossless recursive acceptance over the candidates."""
-    _check_round(Case(synth.scaled(synth.CONFIGS["c4"], mode="recursive")))
+    _check_round(Case(synth.scaled(synth.CONFIGS["multi4x4"], mode="recursive")))
 
 
 def test_recursive_acceptance_shared_prefixes_round():
     """Small vocabulary: candidates share drafted prefixes, so the kept path can belong to any of them."""
-    cfg = synth.scaled(synth.CONFIGS["c4"], mode="recursive", vocab=4, kv_lens=(333, 31, 1024, 0), cfg_id=41)
+    cfg = synth.scaled(synth.CONFIGS["multi4x4"], mode="recursive", vocab=4, kv_lens=(333, 31, 1024, 0), cfg_id=41)
     _check_round(Case(cfg))
 
 
-def test_c4_needles():
-    cfg = synth.scaled(synth.CONFIGS["c4"], kv_lens=(100, 2047, 5000, 64))
+def test_multi4x4_needles():
+    cfg = synth.scaled(synth.CONFIGS["multi4x4"], kv_lens=(100, 2047, 5000, 64))
     _check_round(Case(cfg, needle="self"))
 
 
 def test_verify_is_deterministic_and_leaves_state_untouched():
-    case = Case(synth.scaled(synth.CONFIGS["c2"], kv_lens=(4321,)))
+    case = Case(synth.scaled(synth.CONFIGS["mid8k"], kv_lens=(4321,)))
     say("determinism: verify twice")
     before = case.st.snapshot()
     case.run_verify()
@@ -172,7 +172,7 @@ def test_verify_is_deterministic_and_leaves_state_untouched():
 
 
 def test_kv_write_read_roundtrip():
-    cfg = synth.scaled(synth.CONFIGS["c2"], heads=3, kv_lens=(0,))
+    cfg = synth.scaled(synth.CONFIGS["mid8k"], heads=3, kv_lens=(0,))
     lay = dv.DeviceLayer(cfg, synth.make_layer(cfg))
     st = dv.DeviceState(lay, 2, 256)
     say("kv write/read round trip")

@@ -80,39 +80,39 @@ def _check(cfg, T, L0, chans=None, seed=0, want_y=True):
 @pytest.mark.parametrize("want_y", [True, False])
 @pytest.mark.parametrize("T", [1, 5, 7, 8, 255, 256, 257, 1000])
 def test_prefill_fp32_tiny_layer(T, want_y):
-    _check(synth.CONFIGS["c1"], T, L0=100, want_y=want_y)
+    _check(synth.CONFIGS["tiny"], T, L0=100, want_y=want_y)
 
 
 @pytest.mark.parametrize("want_y", [True, False])
 @pytest.mark.parametrize("T", [1, 13, 128, 129, 300, 4096, 9000])
 def test_prefill_bf16_layer(T, want_y):
-    cfg = synth.scaled(synth.CONFIGS["c2"], d=512, heads=4, kv_lens=(0, 0))
+    cfg = synth.scaled(synth.CONFIGS["mid8k"], d=512, heads=4, kv_lens=(0, 0))
     _check(cfg, T, L0=37, want_y=want_y)
 
 
 @pytest.mark.parametrize("want_y", [True, False])
 def test_prefill_short_taps_and_few_poles(want_y):
-    cfg = synth.scaled(synth.CONFIGS["c2"], d=48, heads=1, taps_short=1, taps_outer=2, poles=5, kv_lens=(0,))
+    cfg = synth.scaled(synth.CONFIGS["mid8k"], d=48, heads=1, taps_short=1, taps_outer=2, poles=5, kv_lens=(0,))
     _check(cfg, 700, L0=0, want_y=want_y)
 
 
 @pytest.mark.parametrize("want_y", [True, False])
 def test_prefill_odd_channel_groups(want_y):
     """d not a multiple of the 64-channel scan group, 4 short taps, outer taps = 1."""
-    cfg = synth.scaled(synth.CONFIGS["c2"], d=96, heads=1, taps_short=4, taps_outer=1, poles=16, kv_lens=(0,))
+    cfg = synth.scaled(synth.CONFIGS["mid8k"], d=96, heads=1, taps_short=4, taps_outer=1, poles=16, kv_lens=(0,))
     _check(cfg, 3001, L0=5, want_y=want_y)
 
 
 @pytest.mark.parametrize("want_y", [True, False])
 def test_prefill_long_prompt_262k_channel_sample(want_y):
-    cfg = synth.scaled(synth.CONFIGS["c3"], kv_lens=(0,))
+    cfg = synth.scaled(synth.CONFIGS["long262k"], kv_lens=(0,))
     chans = np.array([0, 1, 63, 64, 777, 2048, 4095])
     _check(cfg, 262144, L0=0, chans=chans, want_y=want_y)
 
 
 @pytest.mark.parametrize("want_y", [True, False])
 def test_prefill_chunks_compose_on_gpu(want_y):
-    cfg = synth.scaled(synth.CONFIGS["c2"], d=256, heads=2, kv_lens=(0,))
+    cfg = synth.scaled(synth.CONFIGS["mid8k"], d=256, heads=2, kv_lens=(0,))
     T1, T2 = 1000, 3000
     kv_cap = 4096
     _, _, lay, st_a, _ = _layer_state(cfg, 0, kv_cap)
@@ -139,7 +139,7 @@ def test_prefill_chunks_compose_on_gpu(want_y):
 
 def test_prefill_then_verify_round():
     """verify, accept and slice run from the state prefill leaves, against the oracle from its prefill."""
-    cfg = synth.scaled(synth.CONFIGS["c2"], d=512, heads=4, kv_lens=(0,), mode="greedy")
+    cfg = synth.scaled(synth.CONFIGS["mid8k"], d=512, heads=4, kv_lens=(0,), mode="greedy")
     T = 2000
     params, small, lay, st, _ = _layer_state(cfg, 0, 2048 + 64)
     pr = synth.prompt(cfg, T, 5, device="cuda")

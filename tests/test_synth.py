@@ -7,7 +7,7 @@ from hybrid_conv_iir_amd import synth
 
 
 def test_seeded_and_deterministic():
-    cfg = synth.CONFIGS["c1"]
+    cfg = synth.CONFIGS["tiny"]
     a, b = synth.make_layer(cfg), synth.make_layer(cfg)
     for key in a:
         np.testing.assert_array_equal(a[key], b[key])
@@ -15,7 +15,7 @@ def test_seeded_and_deterministic():
 
 
 def test_layer_distributions():
-    cfg = synth.CONFIGS["c2"]
+    cfg = synth.CONFIGS["mid8k"]
     p = synth.make_layer(cfg)
     assert p["w_outer"].shape == (128, 4096) and p["lam"].shape == (4096, 16)
     assert 0.5 <= p["lam"].min() and p["lam"].max() <= 0.99
@@ -31,7 +31,7 @@ def test_bf16_rounding_is_nearest_even():
 
 
 def test_geometric_agreement_planted_length_is_the_greedy_k():
-    cfg = synth.CONFIGS["c3"]
+    cfg = synth.CONFIGS["long262k"]
     lens = []
     for rnd in range(40):
         drafts, zt, ln = synth.geometric_agreement(cfg, rnd)
@@ -42,7 +42,7 @@ def test_geometric_agreement_planted_length_is_the_greedy_k():
 
 
 def test_gumbel_drafts_follow_draft_distribution():
-    cfg = synth.scaled(synth.CONFIGS["c1"], vocab=4)
+    cfg = synth.scaled(synth.CONFIGS["tiny"], vocab=4)
     z = np.array([[[[0.0, 1.0, -1.0, 0.5]]]], dtype=np.float32)
     counts = np.zeros(4)
     for rnd in range(4000):
@@ -53,7 +53,7 @@ def test_gumbel_drafts_follow_draft_distribution():
 
 
 def test_kv_prefix_cpu_shape_and_moments():
-    cfg = synth.scaled(synth.CONFIGS["c2"], kv_lens=(1000,), heads=2)
+    cfg = synth.scaled(synth.CONFIGS["mid8k"], kv_lens=(1000,), heads=2)
     k = synth.kv_prefix(cfg, 0, "k")
     assert tuple(k.shape) == (2, 1000, 128)
     kk = k.float().numpy()
