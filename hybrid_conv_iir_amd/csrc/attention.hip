@@ -139,14 +139,40 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
     }
 }
 
-__global__ void k_ticket_reset(unsigned* ticket) {
-    if (threadIdx.x == 0) ticket[0] = 0u;
+// Set-up of one verify (a kernel, so that graph capture records no memset): zero the job
+// queue's counter and write the work-list table.  Thread p < kPhaseMax owns phase p: it counts
+// the phase's items of every sequence (the per-phase totals meet in LDS), then writes each
+// sequence's base and count.
+__global__ __launch_bounds__(64) void k_verify_setup(unsigned* ticket, int32_t* table, const int32_t* kv_len,
+                                                     int nb, int H, int lim, int resident)
+{
+    __shared__ long long cnt[kPhaseMax];
+    const int p = threadIdx.x;
+    if (p == 0) ticket[0] = 0u;
+    const WorkList w = make_worklist(kv_len, nb, H, lim, resident);
+    if (p < kPhaseMax) {
+        long long c = 0;
+        if (p < w.np)
+            for (int b = 0; b < nb; ++b) c += (long long)phase_items(w, prefix_tiles(kv_len, b, lim), p) * H;
+        cnt[p] = c;
+    }
+    __syncthreads();
+    if (p < kPhaseMax) {
+        long long base = 0;
+        for (int q = 0; q < p; ++q) base += cnt[q];
+        for (int b = 0; b < nb; ++b) {
+            const int n = p < w.np ? phase_items(w, prefix_tiles(kv_len, b, lim), p) : 0;
+            table[((size_t)p * nb + b) * 2] = (int32_t)base;
+            table[((size_t)p * nb + b) * 2 + 1] = n;
+            base += (long long)n * H;
+        }
+    }
 }
 
 // -------------------------------------------------------------------- host
 
-// Workspace: the queue's ticket counter (256 bytes), then the partials
-// part_o [items][nq][Dh] and part_ml [items][nq][2].
+// Workspace: the header (the queue's ticket counter; from byte kWsTableOff the work-list
+// table), then the partials part_o [items][nq][Dh] and part_ml [items][nq][2].
 AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_kv_len, int num_cus)
 {
     AttnPlan p{};
@@ -167,8 +193,8 @@ AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_k
     p.part_o_elems = (size_t)cap * p.nq * L->head_dim;
     p.part_ml_elems = (size_t)cap * p.nq * 2;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    p.ticket_bytes = 256;
-    p.bytes = p.ticket_bytes + up(p.part_o_elems * 4) + up(p.part_ml_elems * 4);
+    p.header_bytes = kWsTableOff + up(worklist_table_bytes(nb));
+    p.bytes = p.header_bytes + up(p.part_o_elems * 4) + up(p.part_ml_elems * 4);
     return p;
 }
 
@@ -189,13 +215,17 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
     const int H = L->heads, DH = L->head_dim, nq = plan.nq;
     const float scale_log2 = kLog2e / sqrtf((float)DH);
     unsigned* ticket = (unsigned*)ws;
-    float* part_o = (float*)((char*)ws + plan.ticket_bytes);
+    int32_t* table = (int32_t*)((char*)ws + kWsTableOff);
+    float* part_o = (float*)((char*)ws + plan.header_bytes);
     float* part_ml = (float*)((char*)part_o + (plan.part_o_elems * 4 + 255) / 256 * 256);
     auto mark = [&](int i) { return (ev && ev[i]) ? hipEventRecord(ev[i], st) : hipSuccess; };
     hipError_t e = mark(0);
     if (e != hipSuccess) return e;
 
     if (plan.items_cap > 0) {
+        hipLaunchKernelGGL(k_verify_setup, dim3(1), dim3(64), 0, st, ticket, table, S->kv_len, nb, H, plan.kv_lim,
+                           plan.resident);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
         if (L->act_dtype == HCI_BF16) {
             StreamArgs A{};
             A.kc = (const uint16_t*)S->k_cache; A.vc = (const uint16_t*)S->v_cache; A.q = (const uint16_t*)blk->q;
@@ -203,8 +233,6 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
             A.H = H; A.kv_cap = S->kv_cap; A.kv_lim = plan.kv_lim; A.nq = nq; A.nb = nb; A.resident = plan.resident;
             A.scale_log2 = scale_log2;
             const int nqt = (nq + 15) / 16;
-            hipLaunchKernelGGL(k_ticket_reset, dim3(1), dim3(64), 0, st, ticket);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
             const int blocks = plan.items_cap < plan.resident ? plan.items_cap : plan.resident;
             e = launch_stream_one(A, DH, nqt, blocks, st);
             if (e != hipSuccess) return e;
@@ -224,7 +252,7 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
     F.f_out = blk->f; F.s_out = blk->s; F.y_out = blk->y;
     F.d = L->d; F.Ts = L->taps_short; F.To = L->taps_outer; F.N = L->poles; F.nc = nc;
     F.n_conv = conv ? ((L->d + kCG - 1) / kCG) * nb : 0;
-    F.kv_len = S->kv_len; F.part_o = part_o; F.part_ml = part_ml;
+    F.kv_len = S->kv_len; F.part_o = part_o; F.part_ml = part_ml; F.table = table;
     F.q = blk->q; F.kb = blk->k; F.vb = blk->v; F.o = blk->o;
     F.nb = nb; F.H = H; F.DH = DH; F.nq = nq; F.P = P; F.kv_lim = plan.kv_lim; F.resident = plan.resident;
     F.scale_log2 = scale_log2;

@@ -13,13 +13,18 @@
 //           IIR state stay in registers
 //  phase 1  thread (row slot, channel) computes f_r (short FIR) for rows
 //           r = slot, slot + 16, ...
-//  phase 2  the same threads compute g_r = sum_j w_outer[j] * fbar[i - j]
-//           from LDS, one fixed-order fma chain per output
+//  phase 2  outer FIR as kFirChunks fixed tap chunks: a task (channel,
+//           candidate, chunk, block of 16 positions) sums its chunk's taps in
+//           ascending order for 16 outputs at once over a 31-value register
+//           window (16 taps x 16 outputs per step, two LDS reads per eight
+//           multiply-adds); the chunk sums land in LDS and are added in chunk
+//           order where phase 3 reads g
 //  phase 3  thread (channel, candidate, group of four poles) runs the IIR
 //           recurrence in fp32 registers over the P positions and writes
 //           s_i (16 bytes per thread, a contiguous kilobyte per channel group);
 //           the readout y_i adds the group's terms, then the groups by a
-//           fixed-order butterfly over ceil(N/4) lanes.
+//           fixed-order butterfly over ceil(N/4) lanes (quad permutations on
+//           the vector ALU); the next position's input is read ahead.
 // All per-output arithmetic happens in a fixed order that does not depend
 // on P or on the candidate count, so a block forward and P single-position
 // forwards give identical bits for f, s and y.
@@ -31,10 +36,28 @@ namespace hci {
 
 constexpr int kCG = 16;        // channels per workgroup
 constexpr int kConvT = 256;    // threads per workgroup
+constexpr int kFirChunks = 4;  // tap chunks of the outer FIR (their sums are added in order)
 
-// LDS floats: short window + x rows, outer window + f rows, g rows, outer taps, short taps
+// LDS floats: short window + x rows, outer window + f rows, chunk sums of g, outer taps,
+// short taps
 __host__ __device__ inline size_t conv_iir_lds_floats(int Ts, int To, int R) {
-    return (size_t)((Ts - 1 + R) + (To - 1 + R) + R + To + Ts) * kCG;
+    return (size_t)((Ts - 1 + R) + (To - 1 + R) + kFirChunks * R + To + Ts) * kCG;
+}
+
+// Sum over the G lanes of an aligned group (G = 1, 2, 4, 8 or 16), the same bits on every
+// lane of the group: lane offsets G/2, ..., 2, 1 in turn.  Offsets 2 and 1 are quad
+// permutations on the vector ALU (no LDS round trip); wider groups use the LDS crossbar.
+__device__ __forceinline__ float group_sum(float v, int G) {
+    for (int off = G >> 1; off >= 4; off >>= 1) v += __shfl_xor(v, off, G);
+    if (G >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+    if (G >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+    return v;
+}
+
+// v if keep, else +0.0, by masking the bits: the load behind v stays unconditional (a
+// select on a loaded value can turn into a branch around the load)
+__device__ __forceinline__ float keep_if(float v, bool keep) {
+    return __int_as_float(__float_as_int(v) & (keep ? -1 : 0));
 }
 
 // one workgroup: channel group cgi (16 channels) of sequence b, all nc candidate blocks
@@ -51,8 +74,8 @@ __device__ __forceinline__ void conv_iir_block(
     const int W = To - 1, Ws = Ts - 1, R = nc * P;
     float* xs = lds;                            // [Ws + R][kCG]: short window rows, then x rows
     float* fb = xs + (size_t)(Ws + R) * kCG;    // [W + R][kCG]: outer window rows, then f rows
-    float* gl = fb + (size_t)(W + R) * kCG;     // [R][kCG]
-    float* wl = gl + (size_t)R * kCG;           // [To][kCG]
+    float* gl = fb + (size_t)(W + R) * kCG;     // [kFirChunks][R][kCG]: chunk sums of g
+    float* wl = gl + (size_t)kFirChunks * R * kCG;   // [To][kCG]
     float* ws = wl + (size_t)To * kCG;          // [Ts][kCG]
 
     const int ch0 = cgi * kCG;
@@ -137,18 +160,67 @@ __device__ __forceinline__ void conv_iir_block(
     }
     __syncthreads();
 
-    // phase 2: outer FIR, g_i = sum_{j<To} w_outer[j] * fbar[i-j], j ascending
-    for (int r = row; r < R; r += kConvT / kCG) {
-        const int c = r / P, i = r - c * P;
-        const float* fblk = fb + (W + c * P) * kCG + cl;   // candidate c's f rows
-        const float* fwin = fb + W * kCG + cl;             // fwin[-k * kCG] = outer window row W - k
-        float acc = 0.f;
-        int j = 0;
-#pragma unroll 8
-        for (; j <= i && j < To; ++j) acc = fmaf(wl[j * kCG + cl], fblk[(i - j) * kCG], acc);
-#pragma unroll 8
-        for (; j < To; ++j) acc = fmaf(wl[j * kCG + cl], fwin[(i - j) * kCG], acc);
-        gl[r * kCG + cl] = acc;
+    // phase 2: outer FIR, g_i = sum_{j<To} w_outer[j] * fbar[i-j].  Chunk k holds taps
+    // [k CS, min((k + 1) CS, To)), CS = ceil(To / kFirChunks); a task sums its chunk in
+    // ascending tap order for outputs i0 .. i0 + 15 of one candidate, 16 taps per step from a
+    // register window win[q] = fbar[i0 - js - 15 + q].  Taps past the chunk's end enter with
+    // weight 0.  Every output's order depends on To only (not on P or the candidate count).
+    {
+        // task t: channel t % 16, chunk (t / 64) % 4 (one chunk per wave, so the waves of a
+        // workgroup run the four chunks side by side and a wave's lanes share their steps'
+        // path), (candidate, position block) pair 4 (t / 256) + (t / 16) % 4
+        static_assert(kFirChunks * 64 == kConvT, "one tap chunk per wave");
+        const int CS = (To + kFirChunks - 1) / kFirChunks;
+        const int IB = (P + 15) / 16;                   // 16-position blocks per candidate
+        const int pairs = IB * nc;
+        const int tasks = kConvT * ((pairs + 3) / 4);
+        for (int t = tid; t < tasks; t += kConvT) {
+            const int tcl = t % kCG;
+            const int k = (t / 64) % kFirChunks;
+            const int cb = 4 * (t / kConvT) + (t / kCG) % 4;
+            if (cb >= pairs) continue;
+            const int ib = cb % IB, c = cb / IB;
+            const int i0 = 16 * ib, j0 = k * CS, j1 = min(j0 + CS, To);
+            const int crow = W + c * P;                 // LDS row of candidate c's f_0
+            const float* fcol = fb + tcl;
+            // fbar[m] of candidate c (LDS row W + m for m < 0, crow + m for m >= 0); 0 outside
+            // [-W, P) (only taps of weight 0 or outputs past P read there).  Branch-free: the
+            // row is clamped into range and the value selected, so the 31 reads of a step
+            // issue back to back.
+            auto fbar = [&](int m) -> float {
+                const int rw = m >= 0 ? crow + min(m, P - 1) : W + max(m, -W);
+                return keep_if(fcol[rw * kCG], m >= -W && m < P);
+            };
+            float acc[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) acc[u] = 0.f;
+            for (int js = j0; js < j1; js += 16) {
+                float wv[16], win[31];
+                if (js + 16 <= j1 && js >= i0 + 16) {
+                    // a full step whose window lies in the committed window rows (m = i0 - js - 15
+                    // + q < 0 for every q, and m >= -W since js + 15 < To): fixed offsets, no masks
+                    const float* wrow = wl + (size_t)js * kCG + tcl;
+                    const float* frow = fcol + (W + i0 - js - 15) * kCG;
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) wv[u] = wrow[u * kCG];
+#pragma unroll
+                    for (int q = 0; q < 31; ++q) win[q] = frow[q * kCG];
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) wv[u] = keep_if(wl[min(js + u, To - 1) * kCG + tcl], js + u < j1);
+#pragma unroll
+                    for (int q = 0; q < 31; ++q) win[q] = fbar(i0 - js - 15 + q);
+                }
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+#pragma unroll
+                    for (int o = 0; o < 16; ++o) acc[o] = fmaf(wv[u], win[o - u + 15], acc[o]);
+            }
+            float* gk = gl + ((size_t)k * R + c * P) * kCG + tcl;
+#pragma unroll
+            for (int o = 0; o < 16; ++o)
+                if (i0 + o < P) gk[(i0 + o) * kCG] = acc[o];
+        }
     }
     __syncthreads();
 
@@ -156,14 +228,58 @@ __device__ __forceinline__ void conv_iir_block(
     // group of 4 poles); 256 / (16 G) candidates advance together.  y_i adds the group's four
     // terms in pole order, then the G groups by a fixed-order butterfly: the order depends on N
     // only, never on P or the candidates.
-    {
+    if (N == 16) {
+        // 16 poles (G = 4): task (channel, candidate) per 4 lanes, one candidate per wave and
+        // pass; pointers advance by one position per step, the quad sum runs on the vector ALU
+        auto g_of = [&](int r) -> float {
+            float g = gl[r * kCG + tch];
+#pragma unroll
+            for (int k = 1; k < kFirChunks; ++k) g += gl[((size_t)k * R + r) * kCG + tch];
+            return g;
+        };
+        const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);      // == tc
+        const size_t sstep = (size_t)d * 16;
+        for (int c = wv; c < nc; c += kConvT / 64) {
+            const int r0c = c * P;
+            float st[4] = {s0[0], s0[1], s0[2], s0[3]};
+            float* so = s_out + (((size_t)b * R + r0c) * d + chn) * 16 + 4 * tg;
+            typename Act<ACT>::T* yo = y_out + ((size_t)b * R + r0c) * d + chn;
+            float gn = g_of(r0c);
+            for (int i = 0; i < P; ++i) {
+                const float g = scan ? gn : 0.f;
+                if (i + 1 < P) gn = g_of(r0c + i + 1);
+                float py = 0.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    st[q] = fmaf(lm[q], st[q], bt[q] * g);
+                    py = fmaf(cv[q], st[q], py);
+                }
+                if (scan) *(float4*)so = make_float4(st[0], st[1], st[2], st[3]);
+                py += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(py), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+                py += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(py), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+                if (scan && tg == 0) Act<ACT>::store(yo, 0, py);
+                so += sstep;
+                yo += d;
+            }
+        }
+    } else {
         const int per = kConvT / (G * kCG);
+        // g of row r: the chunk sums added in chunk order
+        auto g_of = [&](int r) -> float {
+            float g = gl[r * kCG + tch];
+#pragma unroll
+            for (int k = 1; k < kFirChunks; ++k) g += gl[((size_t)k * R + r) * kCG + tch];
+            return g;
+        };
         for (int c = tc; c - tc < nc; c += per) {
             const bool act = scan && c < nc;
+            const int cr = min(c, nc - 1) * P;        // in-range rows for the reads of idle tasks
             float st[4] = {s0[0], s0[1], s0[2], s0[3]};
+            float gn = g_of(cr);                       // the next position's input, read ahead
             for (int i = 0; i < P; ++i) {
                 const int r = c * P + i;
-                const float g = act ? gl[r * kCG + tch] : 0.f;
+                const float g = act ? gn : 0.f;
+                if (i + 1 < P) gn = g_of(cr + i + 1);
                 float py = 0.f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -180,7 +296,7 @@ __device__ __forceinline__ void conv_iir_block(
                             if (4 * tg + q < N) so[q] = st[q];
                     }
                 }
-                for (int off = G >> 1; off >= 1; off >>= 1) py += __shfl_xor(py, off, G);
+                py = group_sum(py, G);
                 if (act && tg == 0) Act<ACT>::store(y_out, ((size_t)b * R + r) * d + chn, py);
             }
         }

@@ -27,12 +27,12 @@ constexpr int kTile = HCI_KV_TILE;   // keys per KV tile
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN.
+// fp32 -> bf16, round to nearest even; NaN stays NaN (a select, not a branch)
 __device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t nan = (u >> 16) | 0x40u;
+    return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? nan : rne);
 }
 
 template <int ACT> struct Act;
@@ -90,7 +90,8 @@ struct AttnPlan {
     int resident;      // streaming workgroups kept resident (the work list is cut for this many)
     int items_cap;     // bound on the prefix work items; 0 when max_kv_len is 0, -1 when too many
     int kv_lim;        // prefix lengths are read clamped to [0, kv_lim] (= max_kv_len)
-    size_t ticket_bytes;                 // the job queue's counter (first section of the workspace)
+    size_t header_bytes;   // first section of the workspace: the job queue's counter (bytes 0..3)
+                           // and, from byte kWsTableOff, the work-list table (worklist.h)
     size_t part_o_elems, part_ml_elems;
     size_t bytes;      // workspace bytes (256-aligned sections)
 };

@@ -17,15 +17,21 @@ struct FinishArgs {
     int d, Ts, To, N, nc, n_conv;
     // combine
     const int32_t* kv_len; const float *part_o, *part_ml;
+    const int32_t* table;              // the work-list table written by the set-up kernel
     const void *q, *kb, *vb; void* o;
     int nb, H, DH, nq, P, kv_lim, resident, rg_count;
     float scale_log2;
 };
 
+// LDS row stride (bytes) of the combine role's block K and V rows: Dh activations and 16
+// bytes of padding
+__host__ __device__ inline int combine_row_bytes(int DH, int act_bytes) { return DH * act_bytes + 16; }
+
 // dynamic LDS floats of the combine role: the candidate's block K and V rows (raw
-// activations), then per row and state (four waves + the block part) O [Dh] and (m, l)
+// activations, padded rows), then per row and state (four waves + the block part) O [Dh] and
+// (m, l), then 64 block weights per wave
 __host__ __device__ inline size_t combine_lds_floats(int P, int DH, int act_bytes, int RG) {
-    return ((size_t)2 * P * DH * act_bytes + 3) / 4 + (size_t)(kCombW + 1) * RG * (DH + 2);
+    return (size_t)2 * P * combine_row_bytes(DH, act_bytes) / 4 + (size_t)(kCombW + 1) * RG * (DH + 2) + 64 * kCombW;
 }
 
 // rows per combine workgroup for these sizes (1, 2, 4, 8 or 16)

@@ -111,4 +111,17 @@ __device__ __forceinline__ bool work_item(const int32_t* kv_len, const WorkList&
     return false;
 }
 
+// ------------------------------------------------------- work-list table
+//
+// Written once per verify by the set-up kernel, before the prefix stream, and read by the
+// finish kernel: for phase p < kPhaseMax and sequence b, entry (p * nb + b) holds
+//   base  the item index of (p, b, head 0): the items of (p, b, h) are base + h n .. + n - 1
+//   n     items per head of sequence b in phase p (0 for phases past np)
+// so a reader locates every item of (b, h) with 2 kPhaseMax scalar loads and no division.
+constexpr size_t kWsTableOff = 256;                  // byte offset of the table in the workspace
+
+__host__ __device__ inline size_t worklist_table_bytes(int nb) {
+    return (size_t)kPhaseMax * (size_t)nb * 2 * sizeof(int32_t);
+}
+
 }  // namespace hci
