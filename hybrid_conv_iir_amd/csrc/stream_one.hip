@@ -1,8 +1,10 @@
 // Prefix streaming: one persistent workgroup per CU takes prefix items from
-// the job queue; its four waves split an item into contiguous runs of 32-key
-// tiles, each streamed with non-temporal 16-byte loads and the next two tiles
-// in flight, and merge their softmax states in LDS before one partial per
-// query is written.  Every wave applies all NQT 16-query tiles of the sequence
+// the job queue; its four waves share an item's 32-key tiles round-robin
+// (wave w takes tiles t0 + w, t0 + w + 4, ..., so at any moment the
+// workgroup reads four adjacent tiles, a contiguous 32 KB of keys and of
+// values), each streamed with non-temporal 16-byte loads and the next two
+// tiles in flight, and merge their softmax states in LDS before one partial
+// per query is written.  Every wave applies all NQT 16-query tiles of the sequence
 // (nc * P <= 16 NQT queries, NQT <= 4) to each KV tile it streams, so a KV
 // tile is read from HBM once, by one wave, and no barrier sits in the
 // streaming loop.  With one or two query tiles the tiles in flight sit in
@@ -31,8 +33,10 @@ __host__ __device__ constexpr size_t stream_pool_uint4() {
 }
 
 // One prefix item: tiles [t0, t1) of head h of sequence b, all nq <= 16 NQT
-// queries, written to partial `slot`.  The four waves take contiguous runs of
-// the item; each streams its run with the next two tiles' loads in flight
+// queries, written to partial `slot`.  The four waves take the item's tiles
+// round-robin (measured against contiguous runs: adjacent tiles at the same
+// time read 0.2% faster on a 262144-token prefix and 1.4% with four query
+// tiles); each streams its share with the next two tiles' loads in flight
 // while the current tile is consumed.  The waves' states merge in LDS in a
 // fixed order (wave 0, 1, 2, 3).  Every wave returns (no early exit): the
 // caller's barriers stay matched.
@@ -48,8 +52,11 @@ __device__ __forceinline__ void prefix_item(const StreamArgs& A, int b, int h, i
     // them stay scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-    const int per = (t1 - t0 + kPrefixWaves - 1) / kPrefixWaves;
-    const int w0 = min(t0 + wave * per, t1), w1 = min(w0 + per, t1);
+    // wave w takes the tiles TT(k) = t0 + w + 4k, k in [w0, w1) = [0, nk); the loops below run
+    // over k
+    const int nk = t1 - t0 > wave ? (t1 - t0 - wave + kPrefixWaves - 1) / kPrefixWaves : 0;
+    const int w0 = 0, w1 = nk;
+    auto TT = [&](int k) { return t0 + wave + kPrefixWaves * k; };
 
     PrefixAcc<DH, NQT> a;
     auto load_q = [&]() {
@@ -97,8 +104,8 @@ __device__ __forceinline__ void prefix_item(const StreamArgs& A, int b, int h, i
         // compiler then knows its own loads are complete and never waits for a direct load.
         load_q();
         compiler_fence();
-        if (w0 < w1) issue(0, w0);
-        if (w0 + 1 < w1) issue(1, w0 + 1);
+        if (w0 < w1) issue(0, TT(w0));
+        if (w0 + 1 < w1) issue(1, TT(w0 + 1));
         compiler_fence();
         HCI_WAIT_VM(0);
         compiler_fence();
@@ -118,8 +125,8 @@ __device__ __forceinline__ void prefix_item(const StreamArgs& A, int b, int h, i
             compiler_fence();
             HCI_WAIT_LGKM0();                          // the slot is read: refill it
             compiler_fence();
-            if (T + 2 < w1) issue(slot, T + 2);
-            consume_tile<DH, NQT>(a, cur, T, L, g, A.scale_log2);
+            if (T + 2 < w1) issue(slot, TT(T + 2));
+            consume_tile<DH, NQT>(a, cur, TT(T), L, g, A.scale_log2);
             slot ^= 1;
         }
         // every wave is done with its ring before the merge states overwrite the pool
@@ -129,24 +136,24 @@ __device__ __forceinline__ void prefix_item(const StreamArgs& A, int b, int h, i
         // inside the loop are unconditional, so the compiler's waits are exact
         KvTile<DH> ta, tb, tc;
         int T = w0;
-        load_tile<DH>(ta, kp, vp, T, lane);
-        if (T + 1 < w1) load_tile<DH>(tb, kp, vp, T + 1, lane);
+        load_tile<DH>(ta, kp, vp, TT(T), lane);
+        if (T + 1 < w1) load_tile<DH>(tb, kp, vp, TT(T + 1), lane);
         for (; T + 4 < w1; T += 3) {
-            load_tile<DH>(tc, kp, vp, T + 2, lane);
-            consume_tile<DH, NQT>(a, ta, T, L, g, A.scale_log2);
-            load_tile<DH>(ta, kp, vp, T + 3, lane);
-            consume_tile<DH, NQT>(a, tb, T + 1, L, g, A.scale_log2);
-            load_tile<DH>(tb, kp, vp, T + 4, lane);
-            consume_tile<DH, NQT>(a, tc, T + 2, L, g, A.scale_log2);
+            load_tile<DH>(tc, kp, vp, TT(T + 2), lane);
+            consume_tile<DH, NQT>(a, ta, TT(T), L, g, A.scale_log2);
+            load_tile<DH>(ta, kp, vp, TT(T + 3), lane);
+            consume_tile<DH, NQT>(a, tb, TT(T + 1), L, g, A.scale_log2);
+            load_tile<DH>(tb, kp, vp, TT(T + 4), lane);
+            consume_tile<DH, NQT>(a, tc, TT(T + 2), L, g, A.scale_log2);
         }
         // 1..4 tiles left: T (in ta) and T+1 (in tb) are already loaded where they exist
         const int left = w1 - T;
-        if (left >= 3) load_tile<DH>(tc, kp, vp, T + 2, lane);
-        consume_tile<DH, NQT>(a, ta, T, L, g, A.scale_log2);
-        if (left >= 4) load_tile<DH>(ta, kp, vp, T + 3, lane);
-        if (left >= 2) consume_tile<DH, NQT>(a, tb, T + 1, L, g, A.scale_log2);
-        if (left >= 3) consume_tile<DH, NQT>(a, tc, T + 2, L, g, A.scale_log2);
-        if (left >= 4) consume_tile<DH, NQT>(a, ta, T + 3, L, g, A.scale_log2);
+        if (left >= 3) load_tile<DH>(tc, kp, vp, TT(T + 2), lane);
+        consume_tile<DH, NQT>(a, ta, TT(T), L, g, A.scale_log2);
+        if (left >= 4) load_tile<DH>(ta, kp, vp, TT(T + 3), lane);
+        if (left >= 2) consume_tile<DH, NQT>(a, tb, TT(T + 1), L, g, A.scale_log2);
+        if (left >= 3) consume_tile<DH, NQT>(a, tc, TT(T + 2), L, g, A.scale_log2);
+        if (left >= 4) consume_tile<DH, NQT>(a, ta, TT(T + 3), L, g, A.scale_log2);
     }
 
     // the next ticket is taken once this item's loads are done: taken earlier, it would
