@@ -55,7 +55,7 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
     __shared__ float alpha_s[kF32Nq];
 
     const long long item = blockIdx.x;
-    const WorkList w = make_worklist(kv_len, nb, H, kv_lim, resident);
+    const WorkList w = make_worklist(kv_len, nb, H, kv_lim, resident, nq);
     int b, h, t0, t1;
     if (!work_item(kv_len, w, item, b, h, t0, t1)) return;
     const int L = prefix_len(kv_len, b, kv_lim);
@@ -144,12 +144,12 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
 // the phase's items of every sequence (the per-phase totals meet in LDS), then writes each
 // sequence's base and count.
 __global__ __launch_bounds__(64) void k_verify_setup(unsigned* ticket, int32_t* table, const int32_t* kv_len,
-                                                     int nb, int H, int lim, int resident)
+                                                     int nb, int H, int lim, int resident, int nq)
 {
     __shared__ long long cnt[kPhaseMax];
     const int p = threadIdx.x;
     if (p == 0) ticket[0] = 0u;
-    const WorkList w = make_worklist(kv_len, nb, H, lim, resident);
+    const WorkList w = make_worklist(kv_len, nb, H, lim, resident, nq);
     if (p < kPhaseMax) {
         long long c = 0;
         if (p < w.np)
@@ -182,7 +182,7 @@ AttnPlan plan_attention(const hci_layer* L, int nb, int nc, int gamma, int max_k
     p.kv_lim = max_kv_len;    // callers check max_kv_len + P <= kv_cap before any launch
     const long long tiles = (max_kv_len + kTile - 1) / kTile;
     const long long nbh = (long long)nb * L->heads;
-    const int np = worklist_np(worklist_c0(tiles * nbh, p.resident));
+    const int np = worklist_np(worklist_c0(tiles * nbh, p.resident, p.nq));
     // every phase holds at most 2R + 2 nb H items, the last at most 4R + nb H
     const long long cap = tiles > 0 ? (long long)np * (4LL * p.resident + 2 * nbh) : 0;
     if (cap > (1LL << 30)) {               // beyond any launch: the caller reports it unsupported
@@ -224,7 +224,7 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
 
     if (plan.items_cap > 0) {
         hipLaunchKernelGGL(k_verify_setup, dim3(1), dim3(64), 0, st, ticket, table, S->kv_len, nb, H, plan.kv_lim,
-                           plan.resident);
+                           plan.resident, nq);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (L->act_dtype == HCI_BF16) {
             StreamArgs A{};

@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kRoleT, kStreamSlots) void k_verify_stream(StreamAr
 {
     __shared__ uint4 lds_pool[stream_pool_uint4<DH, NQT>()];
     __shared__ unsigned s_ticket;
-    const WorkList w = make_worklist(A.kv_len, A.nb, A.H, A.kv_lim, A.resident);
+    const WorkList w = make_worklist(A.kv_len, A.nb, A.H, A.kv_lim, A.resident, A.nq);
     const long long total = work_count(A.kv_len, w);
     if (threadIdx.x == 0) s_ticket = atomicAdd(A.ticket, 1u);
     __syncthreads();

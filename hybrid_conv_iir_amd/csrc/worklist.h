@@ -28,7 +28,8 @@ __device__ __forceinline__ int prefix_tiles(const int32_t* kv_len, int b, int li
 //
 // Derived on the device from kv_len, identically by the streaming kernels
 // and the combine.  With W = H * sum_b tiles_b and R resident slots,
-// c0 = max(kChunkMin, ceil(W / 2R)) and np = the number of phases whose chunk
+// c0 = max(kChunkMin, ceil(W / sR)) (s = 2, or 1 above 32 queries per
+// sequence: worklist_split) and np = the number of phases whose chunk
 // c0 >> p stays >= kChunkMin (at most kPhaseMax).  Phase p of a prefix of T
 // tiles covers [T - (T >> p), T - (T >> (p+1))) (the last phase runs to T)
 // in chunks of c0 >> p tiles.  Items are numbered phase-major, then by
@@ -45,8 +46,15 @@ struct WorkList {
     int nb, H, lim, c0, np;
 };
 
-__host__ __device__ inline long long worklist_c0(long long total_tiles, int resident) {
-    const long long half = 2LL * (resident > 0 ? resident : 1);
+// First-phase chunks: half of a slot's fair share, or the whole share when a sequence has more
+// than 32 queries (the streaming kernel then runs its LDS-ring form, whose items end with a
+// drained pipeline and a full merge, so fewer, larger items pay: measured on 4 sequences x 4
+// candidates, 0.462 -> 0.451 ms; with 32 queries or fewer the larger items lose, 0.626 ->
+// 0.655 ms on a 262144-token prefix)
+__host__ __device__ inline int worklist_split(int nq) { return nq > 32 ? 1 : 2; }
+
+__host__ __device__ inline long long worklist_c0(long long total_tiles, int resident, int nq) {
+    const long long half = (long long)worklist_split(nq) * (resident > 0 ? resident : 1);
     long long c0 = (total_tiles + half - 1) / half;
     if (c0 < kChunkMin) c0 = kChunkMin;
     if (c0 > (1LL << 28)) c0 = 1LL << 28;
@@ -59,10 +67,11 @@ __host__ __device__ inline int worklist_np(long long c0) {
     return np;
 }
 
-__device__ __forceinline__ WorkList make_worklist(const int32_t* kv_len, int nb, int H, int lim, int resident) {
+__device__ __forceinline__ WorkList make_worklist(const int32_t* kv_len, int nb, int H, int lim, int resident,
+                                                  int nq) {
     long long tot = 0;
     for (int b = 0; b < nb; ++b) tot += prefix_tiles(kv_len, b, lim);
-    const long long c0 = worklist_c0(tot * H, resident);
+    const long long c0 = worklist_c0(tot * H, resident, nq);
     return WorkList{nb, H, lim, (int)c0, worklist_np(c0)};
 }
 

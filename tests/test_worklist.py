@@ -4,7 +4,8 @@ The prefix-streaming kernels take items from a queue and write one partial
 per item; the workspace holds a partial slot for every item the host's bound
 allows.  This test transcribes the device's work list (phase p covers the
 next half of every prefix in chunks of c0 >> p tiles, c0 = max(32,
-ceil(W / 2R)), at most 8 phases) and checks, over many ragged batches, that
+ceil(W / sR)) with s = 2, or 1 above 32 queries per sequence, at most 8
+phases) and checks, over many ragged batches, that
 the items tile every (sequence, head) prefix exactly once and that their
 count never exceeds what hci_verify_workspace_bytes provides.
 """
@@ -17,8 +18,8 @@ import pytest
 KTILE, CHUNK_MIN, PHASE_MAX = 32, 32, 8
 
 
-def _c0(total_tiles, resident):
-    half = 2 * max(resident, 1)
+def _c0(total_tiles, resident, nq):
+    half = (1 if nq > 32 else 2) * max(resident, 1)
     return min(max((total_tiles + half - 1) // half, CHUNK_MIN), 1 << 28)
 
 
@@ -29,9 +30,9 @@ def _np(c0):
     return n
 
 
-def work_items(lens, heads, lim, resident):
+def work_items(lens, heads, lim, resident, nq=13):
     tiles = [(min(max(L, 0), lim) + KTILE - 1) // KTILE for L in lens]
-    c0 = _c0(sum(tiles) * heads, resident)
+    c0 = _c0(sum(tiles) * heads, resident, nq)
     nph = _np(c0)
     items = []
     for p in range(nph):
@@ -48,11 +49,14 @@ def work_items(lens, heads, lim, resident):
 
 
 def _workspace_items(lib, layer, nb, nc, gamma, max_len):
-    """Partial slots in the workspace the host plans for (256 bytes of queue counter first)."""
+    """Partial slots in the workspace the host plans for (after the header: 256 bytes for the
+    queue counter, then the work-list table of 8 phases x nb (base, count) int32 pairs, rounded
+    up to 256 bytes)."""
     nbytes = lib.hci_verify_workspace_bytes(ctypes.byref(layer), nb, nc, gamma, max_len)
     nq = nc * (gamma + 1)
     per_item = nq * layer.head_dim * 4 + nq * 2 * 4
-    return (nbytes - 256) // per_item
+    header = 256 + (8 * nb * 2 * 4 + 255) // 256 * 256
+    return (nbytes - header) // per_item
 
 
 @pytest.fixture(scope="module")
@@ -67,10 +71,11 @@ def _layer(hci, heads, head_dim=128):
                      act_dtype=hci.BF16, w_short=p, w_outer=p, lambda_=p, beta=p, c=p)
 
 
-@pytest.mark.parametrize("name,lens,heads", [("long-context", [262144], 32), ("wide", [131072], 64),
-                                             ("4 ragged", [16384, 32768, 51200, 65536], 32), ("mid", [8192], 32)])
-def test_workloads_tile_their_prefixes(hci, name, lens, heads):
-    tiles, items = work_items(lens, heads, max(lens), 256)
+@pytest.mark.parametrize("name,lens,heads,nq", [("long-context", [262144], 32, 13), ("wide", [131072], 64, 13),
+                                                ("4 ragged", [16384, 32768, 51200, 65536], 32, 52),
+                                                ("mid", [8192], 32, 13)])
+def test_workloads_tile_their_prefixes(hci, name, lens, heads, nq):
+    tiles, items = work_items(lens, heads, max(lens), 256, nq)
     cover = {}
     for b, h, t0, t1 in items:
         assert t1 > t0
@@ -96,9 +101,9 @@ def test_item_count_never_exceeds_the_workspace(hci):
             continue
         layer = _layer(hci, heads)
         cap = _workspace_items(lib, layer, nb, nc, gamma, max_len)
-        # the device plans for its own CU count; without a GPU the host assumes 256 CUs
-        resident = 256 * (2 if nc * (gamma + 1) > 16 else 1)
-        _, items = work_items(lens, heads, max_len, resident)
+        # the device plans for its own CU count; without a GPU the host assumes 256 CUs, one
+        # streaming workgroup each
+        _, items = work_items(lens, heads, max_len, 256, nc * (gamma + 1))
         assert len(items) <= cap, (nb, heads, nc, gamma, max_len, lens, len(items), cap)
         checked += 1
     assert checked > 300
