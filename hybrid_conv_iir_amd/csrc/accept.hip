@@ -34,6 +34,7 @@ struct AccScratch {
     double gap[kAccRows];          // greedy: top-1 gap per target row
     double pm[kAccRows], ps[kAccRows];   // sampling: target row max / sum
     double qm[kAccRows], qs[kAccRows];   // sampling: draft row max / sum
+    float ztok[kAccRows], dtok[kAccRows]; // sampling: target / draft logit of row m's draft token
     double st[4];                  // recursive: (p max, p sum, q max, q sum) of the current depth
     double cm[kAccRows];           // recursive: per-candidate margin
     int na[kAccRows];              // recursive: per-candidate accepted count
@@ -125,8 +126,32 @@ __device__ void wave_row_argmax(const float* z, int V, int lane, int& arg, doubl
     gap = (b2 == -INFINITY) ? INFINITY : (double)b1 - (double)b2;
 }
 
-// softmax(z / T) statistics of one row by ONE wave: (max of z/T, sum of exp(z/T - max)) in fp64
-__device__ void wave_row_stats(const float* z, int V, double T, int lane, double& mx, double& sum) {
+// softmax(z / T) statistics of one row by ONE wave: (max of z/T, sum of exp(z/T - max)) in fp64.
+// A row of at most 64 kLaneBatch entries is loaded once (the same values in the same order as
+// the two-pass form); the lane holding entry tok (if 0 <= tok < V) stores it to *ztok.
+__device__ void wave_row_stats(const float* z, int V, double T, int lane, double& mx, double& sum,
+                               int tok = -1, float* ztok = nullptr) {
+    if (V <= 64 * kLaneBatch) {
+        float v[kLaneBatch];
+#pragma unroll
+        for (int e = 0; e < kLaneBatch; ++e) {
+            const int j = e * 64 + lane;
+            v[e] = j < V ? z[j] : -INFINITY;
+            if (ztok && j == tok) *ztok = v[e];
+        }
+        double m = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < kLaneBatch; ++e) m = fmax(m, (double)v[e] / T);
+        for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+        double s = 0.0;
+#pragma unroll
+        for (int e = 0; e < kLaneBatch; ++e)
+            if (e * 64 + lane < V) s += exp((double)v[e] / T - m);
+        for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+        mx = m;
+        sum = s;
+        return;
+    }
     double m = -INFINITY;
     for (int j0 = 0; j0 < V; j0 += 64 * kLaneBatch) {
         float v[kLaneBatch];
@@ -136,7 +161,10 @@ __device__ void wave_row_stats(const float* z, int V, double T, int lane, double
             v[e] = j < V ? z[j] : -INFINITY;
         }
 #pragma unroll
-        for (int e = 0; e < kLaneBatch; ++e) m = fmax(m, (double)v[e] / T);
+        for (int e = 0; e < kLaneBatch; ++e) {
+            m = fmax(m, (double)v[e] / T);
+            if (ztok && j0 + e * 64 + lane == tok) *ztok = v[e];
+        }
     }
     for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
     double s = 0.0;
@@ -206,6 +234,61 @@ __device__ void draw_token(F weight, int V, double r, AccScratch& sh, int& token
     margin = dmin / total;
 }
 
+
+// draw_token with the weights of the thread's run of ids [j0, j1) (j1 - j0 <= kDrawCache,
+// j0 = threadIdx.x * ceil(V / kAccT)) already in registers: the same sums in the same order
+// as draw_token, without evaluating (and loading) every weight three times.
+constexpr int kDrawCache = 4;
+__device__ void draw_token_cached(const double (&wc)[kDrawCache], int V, double r, AccScratch& sh, int& token,
+                                  double& margin)
+{
+    const int per = (V + kAccT - 1) / kAccT;
+    const int j0 = min((int)threadIdx.x * per, V), j1 = min(j0 + per, V);
+    double loc = 0.0;
+#pragma unroll
+    for (int u = 0; u < kDrawCache; ++u)
+        if (j0 + u < j1) loc += wc[u];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    double incl = loc;
+    for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    __syncthreads();
+    if (lane == 63) sh.d[wv] = incl;
+    __syncthreads();
+    double excl = 0.0;
+    for (int w = 0; w < wv; ++w) excl += sh.d[w];
+    excl += incl - loc;
+    double run = excl;
+#pragma unroll
+    for (int u = 0; u < kDrawCache; ++u)
+        if (j0 + u < j1) run += wc[u];
+    __syncthreads();
+    if (j0 < j1 && j1 == V) sh.bcast[0] = run;
+    __syncthreads();
+    const double total = sh.bcast[0];
+    const double target = r * total;
+    int first = INT_MAX, lastpos = -1;
+    double dmin = INFINITY;
+    run = excl;
+#pragma unroll
+    for (int u = 0; u < kDrawCache; ++u) {
+        const int j = j0 + u;
+        if (j < j1) {
+            const double w = wc[u];
+            run += w;
+            if (run > target && first == INT_MAX) first = j;
+            if (w > 0.0) lastpos = j;
+            dmin = fmin(dmin, fabs(run - target));
+        }
+    }
+    first = block_imin(first, sh);
+    lastpos = block_imax(lastpos, sh);
+    dmin = block_min(dmin, sh);
+    token = first != INT_MAX ? first : lastpos;
+    margin = dmin / total;
+}
 
 // Residual weight of one token after r rejections at the current depth: w^(0) = p,
 // w^(i+1) = max(0, w^(i) - z^(i) q) when rejection i changed the residual (z^(0) = 1,
@@ -378,11 +461,12 @@ __global__ __launch_bounds__(kAccT) void k_accept(
                 const int m = m0 + (wv & 1);
                 if (m <= gamma) {
                     double mx, sum;
+                    const int tok = dr[m - 1];
                     if (wv < 2) {
-                        wave_row_stats(zt_c + (size_t)(m - 1) * V, V, T, lane, mx, sum);
+                        wave_row_stats(zt_c + (size_t)(m - 1) * V, V, T, lane, mx, sum, tok, &sh.ztok[m - 1]);
                         if (lane == 0) { sh.pm[m - 1] = mx; sh.ps[m - 1] = sum; }
                     } else {
-                        wave_row_stats(zd_c + (size_t)(m - 1) * V, V, T, lane, mx, sum);
+                        wave_row_stats(zd_c + (size_t)(m - 1) * V, V, T, lane, mx, sum, tok, &sh.dtok[m - 1]);
                         if (lane == 0) { sh.qm[m - 1] = mx; sh.qs[m - 1] = sum; }
                     }
                 }
@@ -390,8 +474,8 @@ __global__ __launch_bounds__(kAccT) void k_accept(
                 for (int mm = m0; mm < m0 + kAccW / 2 && mm <= gamma; ++mm) {
                     const int t = dr[mm - 1];
                     if (t < 0 || t >= V) { k = mm - 1; done = true; break; }
-                    const double p_t = exp((double)zt_c[(size_t)(mm - 1) * V + t] / T - sh.pm[mm - 1]) / sh.ps[mm - 1];
-                    const double q_t = exp((double)zd_c[(size_t)(mm - 1) * V + t] / T - sh.qm[mm - 1]) / sh.qs[mm - 1];
+                    const double p_t = exp((double)sh.ztok[mm - 1] / T - sh.pm[mm - 1]) / sh.ps[mm - 1];
+                    const double q_t = exp((double)sh.dtok[mm - 1] / T - sh.qm[mm - 1]) / sh.qs[mm - 1];
                     const double lhs = u[mm - 1] * q_t;
                     margin = fmin(margin, fabs(lhs - p_t) / fmax(p_t, 1e-300));
                     if (!(lhs < p_t)) { k = mm - 1; done = true; break; }
@@ -415,16 +499,35 @@ __global__ __launch_bounds__(kAccT) void k_accept(
                 const double p = exp((double)prow[j] / T - pm) / ps;
                 return resid ? fmax(0.0, p - exp((double)qrow[j] / T - qm) / qs) : p;
             };
-            if (resid) {               // cannot be empty after a rejection; guard only
-                const int per = (V + kAccT - 1) / kAccT;
-                const int j0 = min((int)threadIdx.x * per, V), j1 = min(j0 + per, V);
-                double loc = 0.0;
-                for (int j = j0; j < j1; ++j) loc += weight(j);
-                if (!(block_sum(loc, sh) > 0.0)) resid = false;
-            }
+            const int per = (V + kAccT - 1) / kAccT;
+            const int j0 = min((int)threadIdx.x * per, V), j1 = min(j0 + per, V);
             int tok;
             double m2;
-            draw_token(weight, V, u[gamma], sh, tok, m2);
+            if (per <= kDrawCache) {
+                // every weight of the thread's run evaluated once (its logits loaded once)
+                double wc[kDrawCache];
+#pragma unroll
+                for (int uu = 0; uu < kDrawCache; ++uu) wc[uu] = j0 + uu < j1 ? weight(j0 + uu) : 0.0;
+                if (resid) {           // cannot be empty after a rejection; guard only
+                    double loc = 0.0;
+#pragma unroll
+                    for (int uu = 0; uu < kDrawCache; ++uu)
+                        if (j0 + uu < j1) loc += wc[uu];
+                    if (!(block_sum(loc, sh) > 0.0)) {
+                        resid = false;
+#pragma unroll
+                        for (int uu = 0; uu < kDrawCache; ++uu) wc[uu] = j0 + uu < j1 ? weight(j0 + uu) : 0.0;
+                    }
+                }
+                draw_token_cached(wc, V, u[gamma], sh, tok, m2);
+            } else {
+                if (resid) {           // cannot be empty after a rejection; guard only
+                    double loc = 0.0;
+                    for (int j = j0; j < j1; ++j) loc += weight(j);
+                    if (!(block_sum(loc, sh) > 0.0)) resid = false;
+                }
+                draw_token(weight, V, u[gamma], sh, tok, m2);
+            }
             nxt = tok;
             margin = fmin(margin, m2);
         }
