@@ -535,11 +535,11 @@ def main():
         else:
             hci.verify_block_timed(lay.c, st.c, blk.c, blk.nb, blk.nc, blk.gamma, bound, blk.ws, evs)
         dv.accept(acc, mode, cfg.temperature)
-        if evs is not None and evs[3]:
-            hip.hipEventRecord(evs[3], sp)
-        dv.slice_state(lay, st, blk, acc, bound)
         if evs is not None and evs[4]:
             hip.hipEventRecord(evs[4], sp)
+        dv.slice_state(lay, st, blk, acc, bound)
+        if evs is not None and evs[5]:
+            hip.hipEventRecord(evs[5], sp)
         bound += P
 
     for _ in range(W):
@@ -554,8 +554,8 @@ def main():
     # second, untimed pass below.
     stream_evs = []
     for _ in range(K):
-        e = _events(hip, 5)
-        e[2] = e[3] = e[4] = None
+        e = _events(hip, 6)
+        e[0] = e[3] = e[4] = e[5] = None
         stream_evs.append(e)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -565,18 +565,18 @@ def main():
     t1 = time.perf_counter()
     len_after = dv.to_host(st.kv_len).astype(np.int64)
     ms_step = (t1 - t0) * 1e3 / K
-    stream_ms = [_ms(hip, e[0], e[1]) for e in stream_evs]
+    stream_ms = [_ms(hip, e[1], e[2]) for e in stream_evs]
 
     # ---------------------------------------------------------------- breakdown pass (not timed)
-    evsets = [_events(hip, 5) for _ in range(K)]
+    evsets = [_events(hip, 6) for _ in range(K)]
     for i in range(K):
         step(evsets[i])
     torch.cuda.synchronize()
-    combine_ms = [_ms(hip, e[1], e[2]) for e in evsets]
-    verify_ms = [_ms(hip, e[0], e[2]) for e in evsets]
-    accept_ms = [_ms(hip, e[2], e[3]) for e in evsets]
-    slice_ms = [_ms(hip, e[3], e[4]) for e in evsets]
-    step_dev_ms = [_ms(hip, e[0], e[4]) for e in evsets]
+    combine_ms = [_ms(hip, e[2], e[3]) for e in evsets]
+    verify_ms = [_ms(hip, e[0], e[3]) for e in evsets]
+    accept_ms = [_ms(hip, e[3], e[4]) for e in evsets]
+    slice_ms = [_ms(hip, e[4], e[5]) for e in evsets]
+    step_dev_ms = [_ms(hip, e[0], e[5]) for e in evsets]
 
     # mean committed length over the timed steps (the prefix grows by k+1 per step)
     mean_lens = [int(a) + (int(b) - int(a)) * (K - 1) / (2.0 * K) for a, b in zip(len_before, len_after)]
@@ -607,7 +607,7 @@ def main():
         "verify_hbm_GBs": round(alg_verify / (float(np.median(verify_ms)) * 1e-3) / 1e9, 1),
         "verify_pct_of_8TBs": round(100.0 * alg_verify / (float(np.median(verify_ms)) * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "verify_positions_per_s": round(positions / (float(np.median(verify_ms)) * 1e-3), 1),
-        "breakdown_ms_median": {"verify_stream": round(float(np.median([_ms(hip, e[0], e[1]) for e in evsets])), 4),
+        "breakdown_ms_median": {"verify_stream": round(float(np.median([_ms(hip, e[1], e[2]) for e in evsets])), 4),
                                 "verify_finish": round(float(np.median(combine_ms)), 4),
                                 "accept": round(float(np.median(accept_ms)), 4),
                                 "slice": round(float(np.median(slice_ms)), 4),

@@ -226,6 +226,7 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
         hipLaunchKernelGGL(k_verify_setup, dim3(1), dim3(64), 0, st, ticket, table, S->kv_len, nb, H, plan.kv_lim,
                            plan.resident, nq);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = mark(1)) != hipSuccess) return e;
         if (L->act_dtype == HCI_BF16) {
             StreamArgs A{};
             A.kc = (const uint16_t*)S->k_cache; A.vc = (const uint16_t*)S->v_cache; A.q = (const uint16_t*)blk->q;
@@ -244,7 +245,7 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
-    if ((e = mark(1)) != hipSuccess) return e;
+    if ((e = mark(2)) != hipSuccess) return e;
 
     FinishArgs F{};
     F.w_short = L->w_short; F.w_outer = L->w_outer; F.lam = L->lambda; F.beta = L->beta; F.cc = L->c;
@@ -266,7 +267,7 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
     const size_t lds = (conv_lds > comb_lds ? conv_lds : comb_lds) * sizeof(float);
     e = launch_finish(F, L->act_dtype, rg, (int)blocks, lds, st);
     if (e != hipSuccess) return e;
-    return mark(2);
+    return mark(3);
 }
 
 }  // namespace hci

@@ -103,7 +103,8 @@ size_t stream_lds_bytes(const hci_layer* L, int nc, int P);
 constexpr size_t kMaxLds = 160 * 1024;
 
 // the whole verify: the prefix stream then the finish kernel; ev (may be null)
-// = 3 events recorded before, after the streaming part, and at the end
+// = 4 events recorded before the set-up kernel, before and after the streaming kernel, and at
+// the end
 hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block* blk,
                          int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st, hipEvent_t* ev,
                          bool conv = true);

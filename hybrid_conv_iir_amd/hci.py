@@ -207,7 +207,8 @@ def verify_block(layer: Layer, state: State, block: Block, nb: int, nc: int, gam
 
 def verify_block_timed(layer: Layer, state: State, block: Block, nb: int, nc: int, gamma: int, max_kv_len: int,
                        ws: Optional[torch.Tensor], events, stream=None) -> None:
-    """events: a ctypes array of 3 hipEvent_t handles created by the caller."""
+    """events: a ctypes array of 4 hipEvent_t handles created by the caller (before the set-up
+    kernel, before and after the streaming kernel, after the finish kernel)."""
     wsp = _ptr(ws, None, "ws") if ws is not None else None
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(_lib.hci_verify_block_timed(ctypes.byref(layer), ctypes.byref(state), ctypes.byref(block), nb, nc, gamma,

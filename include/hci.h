@@ -162,12 +162,13 @@ int hci_verify_block(const hci_layer* L, const hci_state* S, const hci_block* bl
                      int nb, int nc, int gamma, int max_kv_len,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* hci_verify_block that also records events[0..2] on `stream`: before the
- * first kernel, after the streaming part (the queue reset and the kernel that
- * reads the KV prefix), and after the finish kernel (conv/IIR scan, causal
- * block part, merge of the partials), so the caller can time the parts with
- * hipEventElapsedTime.  events must point at 3 events created
- * by the caller (entries may be NULL to skip one).  Errors as
+/* hci_verify_block that also records events[0..3] on `stream`: before the
+ * first kernel (the set-up kernel: queue counter, work-list table), right
+ * before the kernel that streams the KV prefix, right after it, and after the
+ * finish kernel (conv/IIR scan, causal block part, merge of the partials), so
+ * the caller can time the parts with hipEventElapsedTime -- events[1] to
+ * events[2] spans the streaming kernel alone.  events must point at 4 events
+ * created by the caller (entries may be NULL to skip one).  Errors as
  * hci_verify_block. */
 int hci_verify_block_timed(const hci_layer* L, const hci_state* S, const hci_block* blk,
                            int nb, int nc, int gamma, int max_kv_len,
