@@ -154,6 +154,23 @@ def test_multi4x4_needles():
     _check_round(Case(cfg, needle="self"))
 
 
+@pytest.mark.parametrize("nc,gamma", [(2, 15), (3, 10)])
+def test_query_count_at_the_ring_boundary(nc, gamma):
+    """32 queries per sequence (two 16-query tiles in registers) and 33 (the LDS-ring stream with
+    its larger work items); needles make the prefix and block parts visible."""
+    cfg = synth.scaled(synth.CONFIGS["multi4x4"], nc=nc, gamma=gamma, kv_lens=(5000, 1234), heads=2, d=128)
+    assert nc * (gamma + 1) in (32, 33)
+    _check_round(Case(cfg, needle="self"))
+
+
+def test_many_sequences_ragged():
+    """Twelve sequences with ragged and empty prefixes: the work-list table holds every
+    sequence's per-phase items, and the finish kernel locates them all."""
+    lens = (0, 1, 31, 32, 33, 700, 2048, 4099, 9000, 12345, 64, 5)
+    cfg = synth.scaled(synth.CONFIGS["mid8k"], kv_lens=lens, heads=2, d=128, cfg_id=77)
+    _check_round(Case(cfg, needle="self"))
+
+
 def test_verify_is_deterministic_and_leaves_state_untouched():
     case = Case(synth.scaled(synth.CONFIGS["mid8k"], kv_lens=(4321,)))
     say("determinism: verify twice")
