@@ -235,6 +235,20 @@ def bench_prefill(args, cfg, hip):
             one(with_y, evsets[i])
         torch.cuda.synchronize()
         res[with_y] = float(np.median([_ms(hip, e[0], e[1]) for e in evsets]))
+    # the practical copy ceiling beside the 8 TB/s read peak: a 1 GiB device-to-device copy by
+    # hci_probe_copy (read + write bytes / its best time), the pattern the KV append follows
+    csrc = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    cdst = torch.empty_like(csrc)
+    pe = _events(hip, 2)
+    copy_ms = []
+    for _ in range(4):
+        hip.hipEventRecord(pe[0], sp)
+        hci.probe_copy(cdst, csrc)
+        hip.hipEventRecord(pe[1], sp)
+        hip.hipEventSynchronize(pe[1])
+        copy_ms.append(_ms(hip, pe[0], pe[1]))
+    copy_gbs = 2.0 * csrc.numel() * 4 / (min(copy_ms[1:]) * 1e-3) / 1e9
+    del csrc, cdst
     t_state = res[False] * 1e-3
     flops = prefill_alg_flops(cfg, T)
     achieved = flops / t_state / 1e12
@@ -255,6 +269,7 @@ def bench_prefill(args, cfg, hip):
         "ms_with_outputs_y": round(res[True], 4),
         "hbm_GBs_with_outputs_y": round(prefill_alg_bytes(cfg, T, True) / (res[True] * 1e-3) / 1e9, 1),
         "fir_iir_TFLOPs_equivalent": round(achieved, 2),
+        "hbm_probe_copy_GBs": round(copy_gbs, 1),
         "roofline": {"kernel": "hci_prefill, all launches (scan, state, KV append)", "bound": "hbm",
                      "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(gbs / 8000.0, 4),
