@@ -196,15 +196,26 @@ __device__ __forceinline__ void conv_iir_block(
             for (int u = 0; u < 16; ++u) acc[u] = 0.f;
             for (int js = j0; js < j1; js += 16) {
                 float wv[16], win[31];
-                if (js + 16 <= j1 && js >= i0 + 16) {
-                    // a full step whose window lies in the committed window rows (m = i0 - js - 15
-                    // + q < 0 for every q, and m >= -W since js + 15 < To): fixed offsets, no masks
+                const bool full = js + 16 <= j1;
+                if (full && (js >= i0 + 16 || js == i0)) {
+                    // full steps at fixed LDS offsets, no masks: the window m = i0 - js - 15 + q
+                    // lies in the committed window rows (js >= i0 + 16; m >= -W since js + 15 < To)
+                    // or straddles them and candidate c's rows at q = 15 (js == i0).  Rows at
+                    // m >= P only reach outputs past P, which are not stored; they stay inside the
+                    // LDS allocation (at most row W + R + 14).
                     const float* wrow = wl + (size_t)js * kCG + tcl;
-                    const float* frow = fcol + (W + i0 - js - 15) * kCG;
 #pragma unroll
                     for (int u = 0; u < 16; ++u) wv[u] = wrow[u * kCG];
+                    if (js >= i0 + 16) {
+                        const float* frow = fcol + (W + i0 - js - 15) * kCG;
 #pragma unroll
-                    for (int q = 0; q < 31; ++q) win[q] = frow[q * kCG];
+                        for (int q = 0; q < 31; ++q) win[q] = frow[q * kCG];
+                    } else {
+                        const float* wrow0 = fcol + (W - 15) * kCG;      // q < 15: window row W + q - 15
+                        const float* brow0 = fcol + (crow - 15) * kCG;   // q >= 15: block row q - 15
+#pragma unroll
+                        for (int q = 0; q < 31; ++q) win[q] = q < 15 ? wrow0[q * kCG] : brow0[q * kCG];
+                    }
                 } else {
 #pragma unroll
                     for (int u = 0; u < 16; ++u) wv[u] = keep_if(wl[min(js + u, To - 1) * kCG + tcl], js + u < j1);

@@ -139,16 +139,17 @@ __device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, 
     const __attribute__((address_space(4))) int32_t* tab = (const __attribute__((address_space(4))) int32_t*)A.table;
     // adj[p] = adj[0] + sum of dadj[1..p]; an entry adds the steps of the phases it has passed
     // (a sum of selects, which the compiler keeps in registers)
-    long long adj0 = 0, dadj[kPhaseMax];
+    // (item indices stay below 2^30, so the bookkeeping is 32-bit)
+    int adj0 = 0, dadj[kPhaseMax];
     int cum[kPhaseMax];                                // entries before phase p
     int total = 0;
     {
-        long long prev = 0;
+        int prev = 0;
 #pragma unroll
         for (int p = 0; p < kPhaseMax; ++p) {
             const size_t e = ((size_t)p * A.nb + b) * 2;
             const int n = tab[e + 1];
-            const long long adj = (long long)tab[e] + (long long)h * n - total;
+            const int adj = tab[e] + h * n - total;
             if (p == 0) adj0 = adj;
             dadj[p] = adj - prev;
             prev = adj;
@@ -157,10 +158,10 @@ __device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, 
         }
     }
     auto item_of = [&](int f) -> long long {
-        long long a = adj0;
+        int a = adj0;
 #pragma unroll
-        for (int p = 1; p < kPhaseMax; ++p) a += f >= cum[p] ? dadj[p] : 0LL;
-        return f + a;
+        for (int p = 1; p < kPhaseMax; ++p) a += f >= cum[p] ? dadj[p] : 0;
+        return (long long)(f + a);
     };
     float M[RG], l[RG], a0[RG], a1[RG];
 #pragma unroll
@@ -300,7 +301,7 @@ __device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, 
 }
 
 template <int ACT, int RG>
-__global__ __launch_bounds__(kCombT) void k_verify_finish(FinishArgs A)
+__global__ __launch_bounds__(kCombT, 4) void k_verify_finish(FinishArgs A)
 {
     extern __shared__ float lds[];
     typedef typename Act<ACT>::T T;
