@@ -40,7 +40,14 @@ struct AccScratch {
     int na[kAccRows];              // recursive: per-candidate accepted count
     double zh[kAccRows + 1];       // recursive: residual totals z^(0..r)
     int zapp[kAccRows];            // recursive: whether rejection i changed the residual
+    int badrow[kAccRows];          // greedy: row i holds NaN / +Inf or no finite entry
 };
+
+// A row's softmax statistics are usable when its sum is >= 1 (the maximal entry contributes
+// exactly 1; a NaN or +Inf entry, or a row with no finite entry, makes the sum NaN).
+__device__ __forceinline__ bool row_finite(double sum) { return sum >= 1.0; }
+
+__device__ __forceinline__ double qnan() { return __longlong_as_double(0x7ff8000000000000LL); }
 
 __device__ __forceinline__ double block_sum(double v, AccScratch& sh) {
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -94,10 +101,12 @@ __device__ __forceinline__ int block_imax(int v, AccScratch& sh) {
 
 constexpr int kLaneBatch = 8;   // row entries each lane loads before using any of them
 
-// argmax / runner-up of one fp32 row by ONE wave (lanes stride the row, fixed butterfly)
-__device__ void wave_row_argmax(const float* z, int V, int lane, int& arg, double& gap) {
+// argmax / runner-up of one fp32 row by ONE wave (lanes stride the row, fixed butterfly);
+// bad = the row holds a NaN or +Inf entry or no entry above -Inf
+__device__ void wave_row_argmax(const float* z, int V, int lane, int& arg, double& gap, bool& bad) {
     float b1 = -INFINITY, b2 = -INFINITY;
     int i1 = INT_MAX;
+    bool nonfin = false;
     for (int j0 = 0; j0 < V; j0 += 64 * kLaneBatch) {
         float v[kLaneBatch];
 #pragma unroll
@@ -109,6 +118,7 @@ __device__ void wave_row_argmax(const float* z, int V, int lane, int& arg, doubl
         for (int e = 0; e < kLaneBatch; ++e) {     // ascending ids per lane
             const int j = j0 + e * 64 + lane;
             if (j < V) {
+                nonfin |= (v[e] != v[e]) | (v[e] == INFINITY);
                 if (v[e] > b1) { b2 = b1; b1 = v[e]; i1 = j; }
                 else if (v[e] > b2) b2 = v[e];
             }
@@ -124,6 +134,7 @@ __device__ void wave_row_argmax(const float* z, int V, int lane, int& arg, doubl
     }
     arg = i1;
     gap = (b2 == -INFINITY) ? INFINITY : (double)b1 - (double)b2;
+    bad = __builtin_amdgcn_ballot_w64(nonfin) != 0ull || b1 == -INFINITY;
 }
 
 // softmax(z / T) statistics of one row by ONE wave: (max of z/T, sum of exp(z/T - max)) in fp64.
@@ -310,7 +321,8 @@ __device__ void accept_recursive(int b, int nc, int gamma, int V, double T,
                                  const float* __restrict__ zt, const float* __restrict__ zd,
                                  const int32_t* __restrict__ drafts, const double* __restrict__ uni,
                                  int32_t* __restrict__ n_acc, int32_t* __restrict__ next,
-                                 int32_t* __restrict__ best, double* __restrict__ margin_out, AccScratch& sh)
+                                 int32_t* __restrict__ best, double* __restrict__ margin_out,
+                                 uint32_t* __restrict__ status, AccScratch& sh)
 {
     const int P = gamma + 1;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -320,6 +332,8 @@ __device__ void accept_recursive(int b, int nc, int gamma, int V, double T,
         sh.na[threadIdx.x] = 0;
     }
     int k = 0, nrej = 0, rep = 0;
+    bool bad = false;
+    uint32_t flags = 0u;
     const float* prow = nullptr;
     const float* qrow = nullptr;
     for (;;) {
@@ -339,12 +353,17 @@ __device__ void accept_recursive(int b, int nc, int gamma, int V, double T,
         }
         if (threadIdx.x == 0) sh.zh[0] = 1.0;
         __syncthreads();
+        if (!row_finite(sh.st[1]) || (k < gamma && !row_finite(sh.st[3]))) {   // uniform: read from LDS
+            bad = true;
+            break;
+        }
         if (k == gamma) break;                       // the alive path kept every draft: bonus from p_gamma
         const double pm = sh.st[0], ps = sh.st[1], qm = sh.st[2], qs = sh.st[3];
         int kept = -1;
         for (int c = 0; c < nc && kept < 0; ++c) {
             if (!((alive >> c) & 1ull)) continue;
             const int t = drafts[((size_t)b * nc + c) * gamma + k];
+            if (t < 0 || t >= V) flags |= HCI_DS_DRAFT_ID;
             if (t >= 0 && t < V) {
                 const double p_t = exp((double)prow[t] / T - pm) / ps;
                 const double q_t = exp((double)qrow[t] / T - qm) / qs;
@@ -383,6 +402,20 @@ __device__ void accept_recursive(int b, int nc, int gamma, int V, double T,
         }
         ++k;
     }
+    if (bad) {                                       // nothing is committed for this sequence
+        for (int c = threadIdx.x; c < nc; c += kAccT) {
+            const size_t o = (size_t)b * nc + c;
+            n_acc[o] = -1;
+            next[o] = -1;
+            if (margin_out) margin_out[o] = qnan();
+        }
+        if (threadIdx.x == 0) {
+            if (best) best[b] = -1;
+            report(status, b, flags | HCI_DS_NONFINITE);
+        }
+        return;
+    }
+    if (threadIdx.x == 0) report(status, b, flags);
     const double pm = sh.st[0], ps = sh.st[1], qm = sh.st[2], qs = sh.st[3];
     const int r = nrej;
     auto weight = [&](int j) {
@@ -409,10 +442,10 @@ __global__ __launch_bounds__(kAccT) void k_accept_recursive(
     int nc, int gamma, int V, double T,
     const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ drafts,
     const double* __restrict__ uni, int32_t* __restrict__ n_acc, int32_t* __restrict__ next,
-    int32_t* __restrict__ best, double* __restrict__ margin_out)
+    int32_t* __restrict__ best, double* __restrict__ margin_out, uint32_t* __restrict__ status)
 {
     __shared__ AccScratch sh;
-    accept_recursive(blockIdx.x, nc, gamma, V, T, zt, zd, drafts, uni, n_acc, next, best, margin_out, sh);
+    accept_recursive(blockIdx.x, nc, gamma, V, T, zt, zd, drafts, uni, n_acc, next, best, margin_out, status, sh);
 }
 
 // Greedy and one-candidate sampling: one workgroup per (sequence, candidate) block, blockIdx.x =
@@ -422,7 +455,7 @@ __global__ __launch_bounds__(kAccT) void k_accept(
     int mode, int nc, int gamma, int V, double T,
     const float* __restrict__ zt, const float* __restrict__ zd, const int32_t* __restrict__ drafts,
     const double* __restrict__ uni, int32_t* __restrict__ n_acc, int32_t* __restrict__ next,
-    int32_t* __restrict__ best, double* __restrict__ margin_out)
+    int32_t* __restrict__ best, double* __restrict__ margin_out, uint32_t* __restrict__ status)
 {
     __shared__ AccScratch sh;
     const int P = gamma + 1;
@@ -433,6 +466,8 @@ __global__ __launch_bounds__(kAccT) void k_accept(
         const int32_t* dr = drafts + blk * gamma;
         int k = gamma, nxt = 0;
         double margin = INFINITY;
+        bool bad = false;                  // a row the decision used is not finite
+        uint32_t flags = 0u;
 
         const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
         if (mode == HCI_GREEDY) {
@@ -441,16 +476,20 @@ __global__ __launch_bounds__(kAccT) void k_accept(
             for (int i0 = 0; i0 <= gamma && k < 0; i0 += kAccW) {
                 const int i = i0 + wv;
                 if (i <= gamma) {
-                    int g; double gap;
-                    wave_row_argmax(zt_c + (size_t)i * V, V, lane, g, gap);
-                    if (lane == 0) { sh.arg[i] = g; sh.gap[i] = gap; }
+                    int g; double gap; bool rb;
+                    wave_row_argmax(zt_c + (size_t)i * V, V, lane, g, gap, rb);
+                    if (lane == 0) { sh.arg[i] = g; sh.gap[i] = gap; sh.badrow[i] = rb ? 1 : 0; }
                 }
                 __syncthreads();
                 for (int r = i0; r < i0 + kAccW && r <= gamma; ++r)
                     if (r == gamma || dr[r] != sh.arg[r]) { k = r; break; }
             }
             nxt = sh.arg[k];
-            for (int i = 0; i <= k; ++i) margin = fmin(margin, sh.gap[i]);
+            for (int i = 0; i <= k; ++i) {
+                margin = fmin(margin, sh.gap[i]);
+                bad |= sh.badrow[i] != 0;
+            }
+            if (k < gamma && (dr[k] < 0 || dr[k] >= V)) flags |= HCI_DS_DRAFT_ID;
         } else {
             const float* zd_c = zd + blk * gamma * V;
             const double* u = uni + blk * P;
@@ -473,7 +512,7 @@ __global__ __launch_bounds__(kAccT) void k_accept(
                 __syncthreads();
                 for (int mm = m0; mm < m0 + kAccW / 2 && mm <= gamma; ++mm) {
                     const int t = dr[mm - 1];
-                    if (t < 0 || t >= V) { k = mm - 1; done = true; break; }
+                    if (t < 0 || t >= V) { k = mm - 1; done = true; flags |= HCI_DS_DRAFT_ID; break; }
                     const double p_t = exp((double)sh.ztok[mm - 1] / T - sh.pm[mm - 1]) / sh.ps[mm - 1];
                     const double q_t = exp((double)sh.dtok[mm - 1] / T - sh.qm[mm - 1]) / sh.qs[mm - 1];
                     const double lhs = u[mm - 1] * q_t;
@@ -489,6 +528,8 @@ __global__ __launch_bounds__(kAccT) void k_accept(
                 }
                 __syncthreads();
             }
+            // the rows the decision used: target rows 0..k, draft rows 0..min(k, gamma - 1)
+            for (int i = 0; i <= k; ++i) bad |= !row_finite(sh.ps[i]) || (i < gamma && !row_finite(sh.qs[i]));
             // weights of the final draw: residual after a rejection, else p_gamma
             const double pm = sh.pm[k], ps = sh.ps[k];
             bool resid = k < gamma;
@@ -532,15 +573,17 @@ __global__ __launch_bounds__(kAccT) void k_accept(
             margin = fmin(margin, m2);
         }
         if (threadIdx.x == 0) {
-            n_acc[blk] = k;
-            next[blk] = nxt;
-            if (margin_out) margin_out[blk] = margin;
-            if (nc == 1 && best) best[b] = 0;
+            n_acc[blk] = bad ? -1 : k;
+            next[blk] = bad ? -1 : nxt;
+            if (margin_out) margin_out[blk] = bad ? qnan() : margin;
+            if (nc == 1 && best) best[b] = bad ? -1 : 0;
+            report(status, b, flags | (bad ? HCI_DS_NONFINITE : 0u));
         }
     }
 }
 
-// best candidate of each sequence: the largest n_accepted, lowest index on ties
+// best candidate of each sequence: the largest n_accepted, lowest index on ties; a candidate
+// marked invalid (n_accepted -1) never wins, and -1 when none is valid
 __global__ __launch_bounds__(256) void k_accept_best(int nb, int nc, const int32_t* __restrict__ n_acc,
                                                      int32_t* __restrict__ best)
 {
@@ -551,7 +594,7 @@ __global__ __launch_bounds__(256) void k_accept_best(int nb, int nc, const int32
         const int k = n_acc[b * nc + c];
         if (k > bk) { bk = k; bc = c; }
     }
-    best[b] = bc;
+    best[b] = bk < 0 ? -1 : bc;
 }
 
 // Serial drafting with the previous-token bias (EvSpark digest, Figure 1(b)): draft m draws from
@@ -657,15 +700,16 @@ hipError_t launch_draft_sample(int nb, int gamma, int V, float temperature, cons
 
 hipError_t launch_accept(int mode, int nb, int nc, int gamma, int V, float temperature,
                          const float* zt, const float* zd, const int32_t* drafts, const double* u,
-                         int32_t* n_acc, int32_t* next, int32_t* best, double* margin, hipStream_t st)
+                         int32_t* n_acc, int32_t* next, int32_t* best, double* margin, uint32_t* status,
+                         hipStream_t st)
 {
     if (mode == HCI_SAMPLE_RECURSIVE) {
         hipLaunchKernelGGL(k_accept_recursive, dim3(nb), dim3(kAccT), 0, st, nc, gamma, V, (double)temperature,
-                           zt, zd, drafts, u, n_acc, next, best, margin);
+                           zt, zd, drafts, u, n_acc, next, best, margin, status);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(k_accept, dim3((unsigned)((long long)nb * nc)), dim3(kAccT), 0, st, mode, nc, gamma, V,
-                       (double)temperature, zt, zd, drafts, u, n_acc, next, best, margin);
+                       (double)temperature, zt, zd, drafts, u, n_acc, next, best, margin, status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nc == 1 || !best) return e;
     hipLaunchKernelGGL(k_accept_best, dim3((nb + 255) / 256), dim3(256), 0, st, nb, nc, n_acc, best);

@@ -4,6 +4,8 @@
 #include "hci_internal.h"
 
 #include <atomic>
+#include <stdio.h>
+#include <string.h>
 
 namespace hci {
 
@@ -61,7 +63,7 @@ using namespace hci;
 
 extern "C" {
 
-const char* hci_status_string(int status) {
+static const char* status_name(int status) {
     switch (status) {
         case HCI_OK: return "HCI_OK";
         case HCI_EINVAL: return "HCI_EINVAL: invalid argument";
@@ -73,7 +75,42 @@ const char* hci_status_string(int status) {
     }
 }
 
-int hci_version(void) { return 100; }
+// copies text into buf the way snprintf does (truncated, NUL-terminated when n > 0) and
+// returns the full length
+static int put_text(const char* text, char* buf, size_t n) {
+    const size_t len = strlen(text);
+    if (n > 0) {
+        const size_t m = len < n - 1 ? len : n - 1;
+        memcpy(buf, text, m);
+        buf[m] = '\0';
+    }
+    return (int)len;
+}
+
+int hci_status_string(int status, char* buf, size_t n) {
+    if (!buf && n > 0) return HCI_EINVAL;
+    return put_text(status_name(status), buf, n);
+}
+
+int hci_device_status_string(uint32_t bits, char* buf, size_t n) {
+    if (!buf && n > 0) return HCI_EINVAL;
+    static const struct { uint32_t bit; const char* name; } names[] = {
+        {HCI_DS_NONFINITE, "HCI_DS_NONFINITE"}, {HCI_DS_K_RANGE, "HCI_DS_K_RANGE"},
+        {HCI_DS_CAND_RANGE, "HCI_DS_CAND_RANGE"}, {HCI_DS_KV_LEN, "HCI_DS_KV_LEN"},
+        {HCI_DS_DRAFT_ID, "HCI_DS_DRAFT_ID"}};
+    char text[160];
+    size_t used = 0;
+    text[0] = '\0';
+    for (const auto& e : names) {
+        if (!(bits & e.bit)) continue;
+        used += (size_t)snprintf(text + used, sizeof(text) - used, "%s%s", used ? "|" : "", e.name);
+        bits &= ~e.bit;
+    }
+    if (bits) used += (size_t)snprintf(text + used, sizeof(text) - used, "%sunknown 0x%x", used ? "|" : "", bits);
+    return put_text(used ? text : "none", buf, n);
+}
+
+int hci_version(void) { return 200; }
 
 size_t hci_verify_workspace_bytes(const hci_layer* L, int nb, int nc, int gamma, int max_kv_len) {
     if (check_layer(L) != HCI_OK || nb < 1 || nc < 1 || gamma < 0 || max_kv_len < 0) return 0;
@@ -119,7 +156,7 @@ int hci_accept(int mode, int nb, int nc, int gamma, int vocab, float temperature
                const float* target_logits, const float* draft_logits,
                const int32_t* draft_tokens, const double* uniforms,
                int32_t* n_accepted, int32_t* next_token, int32_t* best_cand,
-               double* margin, hipStream_t stream) {
+               double* margin, uint32_t* status, hipStream_t stream) {
     if (mode != HCI_GREEDY && mode != HCI_SAMPLE && mode != HCI_SAMPLE_RECURSIVE) return HCI_EINVAL;
     if (nb < 1 || nb > 2147483647 || nc < 1 || nc > 64 || gamma < 0 || vocab < 1) return HCI_EINVAL;
     if (vocab > 65536 || (long long)nb * nc > 2147483647LL) return HCI_EUNSUPPORTED;
@@ -130,7 +167,7 @@ int hci_accept(int mode, int nb, int nc, int gamma, int vocab, float temperature
         if (!uniforms || (gamma > 0 && !draft_logits)) return HCI_EINVAL;
     }
     if (launch_accept(mode, nb, nc, gamma, vocab, temperature, target_logits, draft_logits, draft_tokens,
-                      uniforms, n_accepted, next_token, best_cand, margin, stream) != hipSuccess)
+                      uniforms, n_accepted, next_token, best_cand, margin, status, stream) != hipSuccess)
         return HCI_EDEVICE;
     return HCI_OK;
 }
@@ -146,7 +183,7 @@ int hci_slice_state(const hci_layer* L, const hci_state* S, const hci_block* blk
     rc = check_state(L, S, nb, (long long)max_kv_len + gamma + 1);
     if (rc) return rc;
     if (!blk || !blk->x || !blk->k || !blk->v || !blk->f || !blk->s) return HCI_EINVAL;
-    if (launch_slice(L, S, blk, nb, nc, gamma + 1, n_accepted, best_cand, stream) != hipSuccess)
+    if (launch_slice(L, S, blk, nb, nc, gamma + 1, max_kv_len, n_accepted, best_cand, stream) != hipSuccess)
         return HCI_EDEVICE;
     return HCI_OK;
 }
@@ -171,7 +208,7 @@ int hci_prefill(const hci_layer* L, const hci_state* S, int nb, int T, int max_k
         return HCI_EUNSUPPORTED;
     if (plan.nchunks > 65535) return HCI_EUNSUPPORTED;
     if (!ws || ws_bytes < plan.bytes || !aligned(ws, 256)) return HCI_EWORKSPACE;
-    if (launch_prefill(L, S, nb, T, x, k, v, y, plan, ws, stream) != hipSuccess) return HCI_EDEVICE;
+    if (launch_prefill(L, S, nb, T, max_kv_len, x, k, v, y, plan, ws, stream) != hipSuccess) return HCI_EDEVICE;
     return HCI_OK;
 }
 

@@ -46,18 +46,18 @@ constexpr int kF32Nq = 64;
 __global__ __launch_bounds__(64) void k_attn_prefix_f32(
     const float* __restrict__ kc, const float* __restrict__ vc,
     const int32_t* __restrict__ kv_len, const float* __restrict__ q,
-    float* __restrict__ part_o, float* __restrict__ part_ml,
-    int nb, int H, int DH, int kv_cap, int kv_lim, int nq, int resident, float scale_log2)
+    float* __restrict__ part_o, float* __restrict__ part_ml, const int32_t* __restrict__ ws,
+    int nb, int H, int DH, int kv_cap, int kv_lim, int nq, float scale_log2)
 {
     __shared__ float ks[kTile][kF32Dh + 1];
     __shared__ float vs[kTile][kF32Dh + 1];
     __shared__ float ps[kF32Nq][kTile + 1];
     __shared__ float alpha_s[kF32Nq];
 
-    const long long item = blockIdx.x;
-    const WorkList w = make_worklist(kv_len, nb, H, kv_lim, resident, nq);
+    const int item = blockIdx.x;
+    const WorkTable wt = read_worktable(ws, nb, H, kv_lim);
     int b, h, t0, t1;
-    if (!work_item(kv_len, w, item, b, h, t0, t1)) return;
+    if (!table_item(kv_len, wt, item, b, h, t0, t1)) return;
     const int L = prefix_len(kv_len, b, kv_lim);
     const int tid = threadIdx.x;
 
@@ -140,15 +140,17 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
 }
 
 // Set-up of one verify (a kernel, so that graph capture records no memset): zero the job
-// queue's counter and write the work-list table.  Thread p < kPhaseMax owns phase p: it counts
-// the phase's items of every sequence (the per-phase totals meet in LDS), then writes each
-// sequence's base and count.
-__global__ __launch_bounds__(64) void k_verify_setup(unsigned* ticket, int32_t* table, const int32_t* kv_len,
+// queue's counter, write the work-list header (item count, c0, np) and table, and report every
+// sequence whose kv_len lies outside [0, lim] (it is read clamped).  Thread p < kPhaseMax owns
+// phase p: it counts the phase's items of every sequence (the per-phase totals meet in LDS),
+// then writes each sequence's base and count.  Runs for every verify, also when no sequence
+// has a prefix (the finish kernel then reads an empty list, never a previous call's).
+__global__ __launch_bounds__(64) void k_verify_setup(int32_t* ws, const int32_t* kv_len, uint32_t* status,
                                                      int nb, int H, int lim, int resident, int nq)
 {
     __shared__ long long cnt[kPhaseMax];
+    int32_t* table = (int32_t*)((char*)ws + kWsTableOff);
     const int p = threadIdx.x;
-    if (p == 0) ticket[0] = 0u;
     const WorkList w = make_worklist(kv_len, nb, H, lim, resident, nq);
     if (p < kPhaseMax) {
         long long c = 0;
@@ -166,6 +168,18 @@ __global__ __launch_bounds__(64) void k_verify_setup(unsigned* ticket, int32_t* 
             table[((size_t)p * nb + b) * 2 + 1] = n;
             base += (long long)n * H;
         }
+    }
+    if (p == 0) {
+        long long total = 0;
+        for (int q = 0; q < kPhaseMax; ++q) total += cnt[q];
+        ws[kWsTicket] = 0;
+        ws[kWsTotal] = (int32_t)total;
+        ws[kWsC0] = w.c0;
+        ws[kWsNp] = w.np;
+    }
+    for (int b = p; b < nb; b += blockDim.x) {
+        const int L = kv_len[b];
+        if (L < 0 || L > lim) report(status, b, HCI_DS_KV_LEN);
     }
 }
 
@@ -222,15 +236,16 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
     hipError_t e = mark(0);
     if (e != hipSuccess) return e;
 
+    hipLaunchKernelGGL(k_verify_setup, dim3(1), dim3(64), 0, st, (int32_t*)ws, S->kv_len, S->status, nb, H,
+                       plan.kv_lim, plan.resident, nq);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = mark(1)) != hipSuccess) return e;
     if (plan.items_cap > 0) {
-        hipLaunchKernelGGL(k_verify_setup, dim3(1), dim3(64), 0, st, ticket, table, S->kv_len, nb, H, plan.kv_lim,
-                           plan.resident, nq);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = mark(1)) != hipSuccess) return e;
         if (L->act_dtype == HCI_BF16) {
             StreamArgs A{};
             A.kc = (const uint16_t*)S->k_cache; A.vc = (const uint16_t*)S->v_cache; A.q = (const uint16_t*)blk->q;
-            A.kv_len = S->kv_len; A.part_o = part_o; A.part_ml = part_ml; A.ticket = ticket;
+            A.kv_len = S->kv_len; A.part_o = part_o; A.part_ml = part_ml; A.ws = (const int32_t*)ws;
+            A.ticket = ticket;
             A.H = H; A.kv_cap = S->kv_cap; A.kv_lim = plan.kv_lim; A.nq = nq; A.nb = nb; A.resident = plan.resident;
             A.scale_log2 = scale_log2;
             const int nqt = (nq + 15) / 16;
@@ -240,8 +255,8 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
         } else {
             hipLaunchKernelGGL(k_attn_prefix_f32, dim3(plan.items_cap), dim3(64), 0, st,
                                (const float*)S->k_cache, (const float*)S->v_cache, S->kv_len,
-                               (const float*)blk->q, part_o, part_ml, nb, H, DH, S->kv_cap, plan.kv_lim, nq,
-                               plan.resident, scale_log2);
+                               (const float*)blk->q, part_o, part_ml, (const int32_t*)ws, nb, H, DH, S->kv_cap,
+                               plan.kv_lim, nq, scale_log2);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }

@@ -23,6 +23,12 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
 
 constexpr int kTile = HCI_KV_TILE;   // keys per KV tile
 
+// ORs HCI_DS_* bits into sequence b's status word; no-op when the caller passed no status
+// array.  A vector atomic from the calling lane.
+__device__ __forceinline__ void report(uint32_t* status, size_t b, uint32_t bits) {
+    if (status != nullptr && bits != 0u) atomicOr(status + b, bits);
+}
+
 // ------------------------------------------------------------------ bf16
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
@@ -110,15 +116,19 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
                          bool conv = true);
 hipError_t launch_accept(int mode, int nb, int nc, int gamma, int V, float temperature,
                          const float* zt, const float* zd, const int32_t* drafts, const double* u,
-                         int32_t* n_acc, int32_t* next, int32_t* best, double* margin, hipStream_t st);
+                         int32_t* n_acc, int32_t* next, int32_t* best, double* margin, uint32_t* status,
+                         hipStream_t st);
+// lim: the host's bound on kv_len (max_kv_len); a sequence outside [0, lim] is left unchanged
 hipError_t launch_slice(const hci_layer* L, const hci_state* S, const hci_block* blk,
-                        int nb, int nc, int P, const int32_t* n_acc, const int32_t* best, hipStream_t st);
+                        int nb, int nc, int P, int lim, const int32_t* n_acc, const int32_t* best, hipStream_t st);
 hipError_t launch_kv_copy(const hci_layer* L, const hci_state* S, int b, int row0, int nrows,
                           const void* k_rows, const void* v_rows, void* k_out, void* v_out,
                           bool write, hipStream_t st);
+// row0 < 0: append at kv_len[b] (read on the device), skipped when kv_len[b] is outside [0, lim]
 hipError_t launch_kv_pack(const hci_layer* L, const hci_state* S, int b, int row0, int nrows, const void* k_rows,
-                          const void* v_rows, size_t row_stride, size_t head_stride, hipStream_t st);
-hipError_t launch_len_add(const hci_state* S, int nb, int add, hipStream_t st);
+                          const void* v_rows, size_t row_stride, size_t head_stride, hipStream_t st, int lim = 0);
+// kv_len += add for every sequence whose kv_len is inside [0, lim]; the others are reported
+hipError_t launch_len_add(const hci_state* S, int nb, int add, int lim, hipStream_t st);
 
 // prefill of a prompt into the committed state
 struct PrefillPlan {
@@ -132,8 +142,8 @@ PrefillPlan plan_prefill(const hci_layer* L, int nb, int T, bool want_y);
 size_t prefill_lds_bytes(int To);
 bool prefill_state_path(const hci_layer* L, int T, bool want_y);
 size_t prefill_state_lds_bytes(const hci_layer* L);
-hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T, const void* x, const void* k,
-                          const void* v, void* y, const PrefillPlan& plan, void* ws, hipStream_t st);
+hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T, int lim, const void* x,
+                          const void* k, const void* v, void* y, const PrefillPlan& plan, void* ws, hipStream_t st);
 
 // dense projections
 struct LinearPlan {

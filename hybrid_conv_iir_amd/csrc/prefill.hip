@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kPfT) void k_prefill_local(
 
 __global__ __launch_bounds__(256) void k_prefill_carry(
     const float* __restrict__ lam, float* __restrict__ iir, float* __restrict__ s_loc,
-    int d, int N, int T, int nchunks, int nb)
+    const int32_t* __restrict__ kv_len, int d, int N, int T, int nchunks, int nb, int lim)
 {
     const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, ch, n), n fastest
     if (e >= (size_t)nb * d * kPfN) return;
@@ -267,7 +267,10 @@ __global__ __launch_bounds__(256) void k_prefill_carry(
         const int len = min(kPfC, T - k * kPfC);
         S = fmaf(len < kPfC ? powi(l, len) : pc, S, end);
     }
-    iir[((size_t)b * d + ch) * N + n] = S;                   // committed IIR state after the prompt
+    // committed IIR state after the prompt, unless the sequence's kv_len is out of contract (it
+    // then keeps its state; the chunk start states above still serve its outputs y)
+    const int L = kv_len[b];
+    if (L >= 0 && L <= lim) iir[((size_t)b * d + ch) * N + n] = S;
 }
 
 template <int ACT>
@@ -306,11 +309,13 @@ __global__ __launch_bounds__(kPfT) void k_prefill_fixup(
 template <int ACT>
 __global__ __launch_bounds__(256) void k_prefill_commit(
     typename Act<ACT>::T* __restrict__ short_win, float* __restrict__ outer_win,
-    const typename Act<ACT>::T* __restrict__ x, const float* __restrict__ f_tail, int d, int Ts, int To, int T)
+    const typename Act<ACT>::T* __restrict__ x, const float* __restrict__ f_tail, const int32_t* __restrict__ kv_len,
+    int d, int Ts, int To, int T, int lim)
 {
     const int b = blockIdx.y;
     const int ch = blockIdx.x * blockDim.x + threadIdx.x;
-    if (ch >= d) return;
+    const int L = kv_len[b];
+    if (ch >= d || L < 0 || L > lim) return;       // out-of-contract kv_len: the windows are kept
     // every thread owns one channel column, rows ascending: new row r reads row T + r > r of the
     // concatenation, which this thread has not written yet
     const int Ws = Ts - 1;
@@ -464,10 +469,15 @@ __global__ __launch_bounds__(256) void k_prefill_state(
     const float* __restrict__ w_short, const float* __restrict__ w_outer, const float* __restrict__ lam,
     const float* __restrict__ beta, typename Act<ACT>::T* __restrict__ short_win, float* __restrict__ outer_win,
     float* __restrict__ iir, const typename Act<ACT>::T* __restrict__ x, const float* __restrict__ e_in,
-    int d, int Ts, int To, int N, int T, int M, int chunk_len, int nchunks)
+    const int32_t* __restrict__ kv_len, int d, int Ts, int To, int N, int T, int M, int chunk_len, int nchunks,
+    int lim)
 {
     typedef typename Act<ACT>::T AT;
     extern __shared__ float lds[];
+    {
+        const int L = kv_len[blockIdx.y];
+        if (L < 0 || L > lim) return;              // out-of-contract kv_len: the state is kept (reported later)
+    }
     const int W = To - 1, Ws = Ts - 1;
     float* ft = lds;                       // [W][16]  f at positions T-W .. T-1
     float* ow = ft + (size_t)W * kPfCG;    // [W][16]  committed outer window, oldest first
@@ -549,22 +559,22 @@ __global__ __launch_bounds__(256) void k_prefill_state(
 }
 
 // K/V rows at kv_len .. kv_len+T-1 of every sequence, then the lengths
-static hipError_t append_kv(const hci_layer* L, const hci_state* S, int nb, int T, const void* k, const void* v,
-                            hipStream_t st)
+static hipError_t append_kv(const hci_layer* L, const hci_state* S, int nb, int T, int lim, const void* k,
+                            const void* v, hipStream_t st)
 {
     const size_t row_stride = (size_t)L->heads * L->head_dim;
     const size_t esz = L->act_dtype == HCI_BF16 ? 2 : 4;
     for (int b = 0; b < nb; ++b) {
         const hipError_t e = launch_kv_pack(L, S, b, -1, T, (const char*)k + (size_t)b * T * row_stride * esz,
                                             (const char*)v + (size_t)b * T * row_stride * esz, row_stride,
-                                            (size_t)L->head_dim, st);
+                                            (size_t)L->head_dim, st, lim);
         if (e != hipSuccess) return e;
     }
-    return launch_len_add(S, nb, T, st);
+    return launch_len_add(S, nb, T, lim, st);
 }
 
 template <int ACT>
-static hipError_t launch_state_path(const hci_layer* L, const hci_state* S, int nb, int T,
+static hipError_t launch_state_path(const hci_layer* L, const hci_state* S, int nb, int T, int lim,
                                     const typename Act<ACT>::T* x, const PrefillPlan& plan, void* ws, hipStream_t st)
 {
     typedef typename Act<ACT>::T AT;
@@ -577,13 +587,13 @@ static hipError_t launch_state_path(const hci_layer* L, const hci_state* S, int 
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k_prefill_state<ACT>, dim3((d + kPfCG - 1) / kPfCG, nb), dim3(256),
                        prefill_state_lds_bytes(L), st, L->w_short, L->w_outer, L->lambda, L->beta, (AT*)S->short_win,
-                       S->outer_win, S->iir, x, (const float*)e, d, L->taps_short, L->taps_outer, L->poles, T, M,
-                       plan.chunk_len, plan.nchunks);
+                       S->outer_win, S->iir, x, (const float*)e, S->kv_len, d, L->taps_short, L->taps_outer, L->poles,
+                       T, M, plan.chunk_len, plan.nchunks, lim);
     return hipGetLastError();
 }
 
-hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T, const void* x, const void* k,
-                          const void* v, void* y, const PrefillPlan& plan, void* ws, hipStream_t st)
+hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T, int lim, const void* x,
+                          const void* k, const void* v, void* y, const PrefillPlan& plan, void* ws, hipStream_t st)
 {
     float* s_loc = (float*)ws;
     float* f_tail = (float*)((char*)ws + (plan.s_elems * 4 + 255) / 256 * 256);
@@ -592,10 +602,10 @@ hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T,
     hipError_t e;
     if (plan.state_only) {
         e = L->act_dtype == HCI_BF16
-                ? launch_state_path<HCI_BF16>(L, S, nb, T, (const uint16_t*)x, plan, ws, st)
-                : launch_state_path<HCI_F32>(L, S, nb, T, (const float*)x, plan, ws, st);
+                ? launch_state_path<HCI_BF16>(L, S, nb, T, lim, (const uint16_t*)x, plan, ws, st)
+                : launch_state_path<HCI_F32>(L, S, nb, T, lim, (const float*)x, plan, ws, st);
         if (e != hipSuccess) return e;
-        return append_kv(L, S, nb, T, k, v, st);
+        return append_kv(L, S, nb, T, lim, k, v, st);
     }
     const size_t lds = prefill_lds_bytes(L->taps_outer);
     dim3 grid((d + kPfCG - 1) / kPfCG, plan.nchunks, nb);
@@ -617,7 +627,7 @@ hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T,
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t ncarry = (size_t)nb * d * kPfN;
     hipLaunchKernelGGL(k_prefill_carry, dim3((unsigned)((ncarry + 255) / 256)), dim3(256), 0, st, L->lambda, S->iir,
-                       s_loc, d, L->poles, T, plan.nchunks, nb);
+                       s_loc, S->kv_len, d, L->poles, T, plan.nchunks, nb, lim);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (y) {
         if (L->act_dtype == HCI_BF16)
@@ -631,12 +641,12 @@ hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T,
     dim3 cgrid((d + 255) / 256, nb);
     if (L->act_dtype == HCI_BF16)
         hipLaunchKernelGGL(k_prefill_commit<HCI_BF16>, cgrid, dim3(256), 0, st, (uint16_t*)S->short_win, S->outer_win,
-                           (const uint16_t*)x, f_tail, d, L->taps_short, L->taps_outer, T);
+                           (const uint16_t*)x, f_tail, S->kv_len, d, L->taps_short, L->taps_outer, T, lim);
     else
         hipLaunchKernelGGL(k_prefill_commit<HCI_F32>, cgrid, dim3(256), 0, st, (float*)S->short_win, S->outer_win,
-                           (const float*)x, f_tail, d, L->taps_short, L->taps_outer, T);
+                           (const float*)x, f_tail, S->kv_len, d, L->taps_short, L->taps_outer, T, lim);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return append_kv(L, S, nb, T, k, v, st);
+    return append_kv(L, S, nb, T, lim, k, v, st);
 }
 
 }  // namespace hci

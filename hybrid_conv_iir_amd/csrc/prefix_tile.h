@@ -32,7 +32,8 @@ __device__ __forceinline__ bf16x8 ones_bf16x8() {
 struct StreamArgs {
     const uint16_t *kc, *vc, *q; const int32_t* kv_len;
     float *part_o, *part_ml;
-    unsigned* ticket;                  // the job queue's counter (zeroed before the launch)
+    const int32_t* ws;                 // the workspace header and work-list table (set-up kernel)
+    unsigned* ticket;                  // the job queue's counter (zeroed by the set-up kernel)
     int H, kv_cap, kv_lim, nq, nb, resident;
     float scale_log2;
 };

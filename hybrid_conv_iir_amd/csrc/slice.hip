@@ -19,14 +19,21 @@ constexpr int kSliceCG = 16;         // channels per window workgroup
 constexpr int kSliceRows = 256 / kSliceCG;   // window rows handled per pass of the 256 threads
 constexpr int kSliceWinMax = 128;    // window rows staged in LDS per pass
 
-__device__ __forceinline__ void winner(const int32_t* n_acc, const int32_t* best, int b, int nc,
-                                       int gamma, int& cstar, int& k) {
-    int c = (best != nullptr && nc > 1) ? best[b] : 0;
-    c = c < 0 ? 0 : (c >= nc ? nc - 1 : c);
-    int kk = n_acc[(size_t)b * nc + c];
-    kk = kk < 0 ? 0 : (kk > gamma ? gamma : kk);
-    cstar = c;
-    k = kk;
+// The winning candidate c*, its accepted index k and the committed length L of sequence b,
+// and the HCI_DS_* bits that stop the commit (0 when it may proceed): c* outside [0, nc), k
+// outside [0, gamma], or kv_len outside [0, lim].  Nothing is clamped into range: a sequence
+// with any of these is left exactly as it was.
+__device__ __forceinline__ uint32_t slice_target(const int32_t* n_acc, const int32_t* best, const int32_t* kv_len,
+                                                 int b, int nc, int gamma, int lim, int& cstar, int& k, int& L) {
+    uint32_t bad = 0u;
+    cstar = (best != nullptr && nc > 1) ? best[b] : 0;
+    k = -1;
+    if (cstar < 0 || cstar >= nc) bad |= HCI_DS_CAND_RANGE;
+    else k = n_acc[(size_t)b * nc + cstar];
+    if (bad == 0u && (k < 0 || k > gamma)) bad |= HCI_DS_K_RANGE;
+    L = kv_len[b];
+    if (L < 0 || L > lim) bad |= HCI_DS_KV_LEN;
+    return bad;
 }
 
 template <int ACT>
@@ -62,13 +69,13 @@ __global__ __launch_bounds__(256) void k_slice(
     const float* __restrict__ f, const float* __restrict__ s,
     const typename Act<ACT>::T* __restrict__ kb, const typename Act<ACT>::T* __restrict__ vb,
     const int32_t* __restrict__ n_acc, const int32_t* __restrict__ best,
-    int d, int Ts, int To, int N, int H, int DH, int kv_cap, int nc, int gamma)
+    int d, int Ts, int To, int N, int H, int DH, int kv_cap, int nc, int gamma, int lim)
 {
     __shared__ float stage[kSliceWinMax][kSliceCG];
     const int b = blockIdx.z, role = blockIdx.y;
     const int P = gamma + 1;
-    int cstar, k;
-    winner(n_acc, best, b, nc, gamma, cstar, k);
+    int cstar, k, L;
+    if (slice_target(n_acc, best, kv_len, b, nc, gamma, lim, cstar, k, L) != 0u) return;   // reported by k_slice_len
     const size_t blk = (size_t)b * nc + cstar;
 
     if (role == 0) {
@@ -85,8 +92,6 @@ __global__ __launch_bounds__(256) void k_slice(
         for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
             dst[e] = src[e];
     } else {
-        int L = kv_len[b];
-        L = L < 0 ? 0 : L;
         const size_t per_row = (size_t)H * DH;
         const size_t n = (size_t)(k + 1) * per_row;
         const size_t slab = (size_t)kv_cap * DH;
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(256) void k_slice(
             const int i = (int)(e / per_row);
             const int h = (int)((e / DH) % H);
             const int dd = (int)(e % DH);
-            const int row = L + i;
+            const int row = L + i;               // < lim + gamma + 1 <= kv_cap (host check)
             if (row >= kv_cap) continue;
             const size_t src = ((blk * P + i) * H + h) * DH + dd;
             const size_t base = ((size_t)b * H + h) * slab;
@@ -105,18 +110,22 @@ __global__ __launch_bounds__(256) void k_slice(
 }
 
 __global__ void k_slice_len(int32_t* __restrict__ kv_len, const int32_t* __restrict__ n_acc,
-                            const int32_t* __restrict__ best, int nb, int nc, int gamma, int kv_cap)
+                            const int32_t* __restrict__ best, uint32_t* __restrict__ status, int nb, int nc,
+                            int gamma, int lim)
 {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= nb) return;
-    int cstar, k;
-    winner(n_acc, best, b, nc, gamma, cstar, k);
-    int L = kv_len[b] + k + 1;
-    kv_len[b] = L > kv_cap ? kv_cap : L;
+    int cstar, k, L;
+    const uint32_t bad = slice_target(n_acc, best, kv_len, b, nc, gamma, lim, cstar, k, L);
+    if (bad != 0u) {
+        report(status, b, bad);
+        return;
+    }
+    kv_len[b] = L + k + 1;
 }
 
 hipError_t launch_slice(const hci_layer* L, const hci_state* S, const hci_block* blk,
-                        int nb, int nc, int P, const int32_t* n_acc, const int32_t* best, hipStream_t st)
+                        int nb, int nc, int P, int lim, const int32_t* n_acc, const int32_t* best, hipStream_t st)
 {
     const int gamma = P - 1;
     const int win_blocks = (L->d + kSliceCG - 1) / kSliceCG;
@@ -126,18 +135,18 @@ hipError_t launch_slice(const hci_layer* L, const hci_state* S, const hci_block*
             (uint16_t*)S->short_win, S->outer_win, S->iir, (uint16_t*)S->k_cache, (uint16_t*)S->v_cache,
             S->kv_len, (const uint16_t*)blk->x, blk->f, blk->s, (const uint16_t*)blk->k,
             (const uint16_t*)blk->v, n_acc, best, L->d, L->taps_short, L->taps_outer, L->poles,
-            L->heads, L->head_dim, S->kv_cap, nc, gamma);
+            L->heads, L->head_dim, S->kv_cap, nc, gamma, lim);
     } else {
         hipLaunchKernelGGL(k_slice<HCI_F32>, grid, block, 0, st,
             (float*)S->short_win, S->outer_win, S->iir, (float*)S->k_cache, (float*)S->v_cache,
             S->kv_len, (const float*)blk->x, blk->f, blk->s, (const float*)blk->k,
             (const float*)blk->v, n_acc, best, L->d, L->taps_short, L->taps_outer, L->poles,
-            L->heads, L->head_dim, S->kv_cap, nc, gamma);
+            L->heads, L->head_dim, S->kv_cap, nc, gamma, lim);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_slice_len, dim3((nb + 63) / 64), dim3(64), 0, st,
-                       S->kv_len, n_acc, best, nb, nc, gamma, S->kv_cap);
+                       S->kv_len, n_acc, best, S->status, nb, nc, gamma, lim);
     return hipGetLastError();
 }
 
@@ -180,12 +189,14 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_kv_pack(T* __restrict__ kc, T* __restrict__ vc, const T* __restrict__ ks,
                                                  const T* __restrict__ vs, const int32_t* __restrict__ kv_len,
                                                  int b, int row0, int nrows, int H, int DH, int kv_cap,
-                                                 size_t row_stride, size_t head_stride)
+                                                 size_t row_stride, size_t head_stride, int lim)
 {
     constexpr int kMaxDh = 128, kPad = 8;
     __shared__ __align__(16) T vt[kTile * (kMaxDh + kPad)];
     const int L0 = row0 >= 0 ? row0 : kv_len[b];
-    if (L0 < 0 || L0 + nrows > kv_cap || DH > kMaxDh) return;     // host checks make this unreachable
+    // an appended length outside the host's bound leaves the cache alone (k_len_add reports it);
+    // the other conditions the host checks make unreachable
+    if (L0 < 0 || (row0 < 0 && L0 > lim) || L0 + nrows > kv_cap || DH > kMaxDh) return;
     const int tile = L0 / kTile + (int)blockIdx.x;
     const int r0 = tile * kTile;
     if (r0 >= L0 + nrows) return;                                  // the grid covers an upper bound of tiles
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(256) void k_kv_pack(T* __restrict__ kc, T* __restri
 }
 
 hipError_t launch_kv_pack(const hci_layer* L, const hci_state* S, int b, int row0, int nrows, const void* k_rows,
-                          const void* v_rows, size_t row_stride, size_t head_stride, hipStream_t st)
+                          const void* v_rows, size_t row_stride, size_t head_stride, hipStream_t st, int lim)
 {
     if (nrows <= 0) return hipSuccess;
     if (L->head_dim > 128 || L->head_dim % 32 || row_stride % 8 || head_stride % 8) return hipErrorInvalidValue;
@@ -247,25 +258,29 @@ hipError_t launch_kv_pack(const hci_layer* L, const hci_state* S, int b, int row
     if (L->act_dtype == HCI_BF16)
         hipLaunchKernelGGL(k_kv_pack<uint16_t>, grid, dim3(256), 0, st, (uint16_t*)S->k_cache,
                            (uint16_t*)S->v_cache, (const uint16_t*)k_rows, (const uint16_t*)v_rows, S->kv_len, b, row0,
-                           nrows, L->heads, L->head_dim, S->kv_cap, row_stride, head_stride);
+                           nrows, L->heads, L->head_dim, S->kv_cap, row_stride, head_stride, lim);
     else
         hipLaunchKernelGGL(k_kv_pack<float>, grid, dim3(256), 0, st, (float*)S->k_cache,
                            (float*)S->v_cache, (const float*)k_rows, (const float*)v_rows, S->kv_len, b, row0, nrows,
-                           L->heads, L->head_dim, S->kv_cap, row_stride, head_stride);
+                           L->heads, L->head_dim, S->kv_cap, row_stride, head_stride, lim);
     return hipGetLastError();
 }
 
-__global__ void k_len_add(int32_t* __restrict__ kv_len, int nb, int add, int kv_cap)
+__global__ void k_len_add(int32_t* __restrict__ kv_len, uint32_t* __restrict__ status, int nb, int add, int lim)
 {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= nb) return;
-    const int L = kv_len[b] + add;
-    kv_len[b] = L > kv_cap ? kv_cap : L;
+    const int L = kv_len[b];
+    if (L < 0 || L > lim) {
+        report(status, b, HCI_DS_KV_LEN);
+        return;
+    }
+    kv_len[b] = L + add;                 // <= lim + add <= kv_cap (host check)
 }
 
-hipError_t launch_len_add(const hci_state* S, int nb, int add, hipStream_t st)
+hipError_t launch_len_add(const hci_state* S, int nb, int add, int lim, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_len_add, dim3((nb + 63) / 64), dim3(64), 0, st, S->kv_len, nb, add, S->kv_cap);
+    hipLaunchKernelGGL(k_len_add, dim3((nb + 63) / 64), dim3(64), 0, st, S->kv_len, S->status, nb, add, lim);
     return hipGetLastError();
 }
 

@@ -218,17 +218,17 @@ __global__ __launch_bounds__(kRoleT, kStreamSlots) void k_verify_stream(StreamAr
 {
     __shared__ uint4 lds_pool[stream_pool_uint4<DH, NQT>()];
     __shared__ unsigned s_ticket;
-    const WorkList w = make_worklist(A.kv_len, A.nb, A.H, A.kv_lim, A.resident, A.nq);
-    const long long total = work_count(A.kv_len, w);
+    const WorkTable wt = read_worktable(A.ws, A.nb, A.H, A.kv_lim);
     if (threadIdx.x == 0) s_ticket = atomicAdd(A.ticket, 1u);
     __syncthreads();
     for (;;) {
-        const long long t = s_ticket;
+        const unsigned t = s_ticket;
         __syncthreads();                               // every wave has read the ticket
-        if (t >= total) break;
+        if (t >= (unsigned)wt.total) break;
         unsigned next = 0xffffffffu;                   // past the end unless the item takes a ticket
         int b = 0, h = 0, t0 = 0, t1 = 0;
-        if (work_item(A.kv_len, w, t, b, h, t0, t1)) prefix_item<DH, NQT>(A, b, h, t0, t1, t, lds_pool, next);
+        if (table_item(A.kv_len, wt, (int)t, b, h, t0, t1))
+            prefix_item<DH, NQT>(A, b, h, t0, t1, t, lds_pool, next);
         if (threadIdx.x == 0) s_ticket = next;
         __syncthreads();
     }

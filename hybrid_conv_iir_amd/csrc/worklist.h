@@ -1,7 +1,9 @@
 // The split of the committed KV prefixes into work items, derived on the
-// device from kv_len -- identically by the prefix-streaming kernels, which
-// take the items from a queue, and by the finish kernel, which merges their
-// partials.  Host code sizes the workspace with the bound stated below.
+// device from kv_len once per verify by the set-up kernel, which records it in
+// the workspace (header and table below); the prefix-streaming kernels take
+// the items from a queue and locate them through the table, and the finish
+// kernel merges their partials through the same table.  Host code sizes the
+// workspace with the bound stated below.
 #pragma once
 
 #include "hci_internal.h"
@@ -26,8 +28,7 @@ __device__ __forceinline__ int prefix_tiles(const int32_t* kv_len, int b, int li
 
 // ------------------------------------------------------------- work list
 //
-// Derived on the device from kv_len, identically by the streaming kernels
-// and the combine.  With W = H * sum_b tiles_b and R resident slots,
+// With W = H * sum_b tiles_b and R resident slots,
 // c0 = max(kChunkMin, ceil(W / sR)) (s = 2, or 1 above 32 queries per
 // sequence: worklist_split) and np = the number of phases whose chunk
 // c0 >> p stays >= kChunkMin (at most kPhaseMax).  Phase p of a prefix of T
@@ -89,48 +90,66 @@ __device__ __forceinline__ int phase_items(const WorkList& w, int T, int p) {
     return (e - s + c - 1) / c;
 }
 
-__device__ __forceinline__ long long work_count(const int32_t* kv_len, const WorkList& w) {
-    long long n = 0;
-    for (int p = 0; p < w.np; ++p)
-        for (int b = 0; b < w.nb; ++b) n += (long long)phase_items(w, prefix_tiles(kv_len, b, w.lim), p) * w.H;
-    return n;
-}
-
-// Locate item `item`: sequence b, head h, tiles [t0, t1); false past the last item.
-__device__ __forceinline__ bool work_item(const int32_t* kv_len, const WorkList& w, long long item,
-                                          int& b, int& h, int& t0, int& t1) {
-    for (int p = 0; p < w.np; ++p) {
-        for (int bb = 0; bb < w.nb; ++bb) {
-            const int T = prefix_tiles(kv_len, bb, w.lim);
-            const int n = phase_items(w, T, p);
-            const long long cnt = (long long)n * w.H;
-            if (item < cnt) {
-                b = bb;
-                h = (int)(item / n);
-                const int j = (int)(item - (long long)h * n);
-                int s, e;
-                phase_range(w, T, p, s, e);
-                t0 = s + j * phase_chunk(w, p);
-                t1 = min(t0 + phase_chunk(w, p), e);
-                return true;
-            }
-            item -= cnt;
-        }
-    }
-    return false;
-}
-
 // ------------------------------------------------------- work-list table
 //
 // Written once per verify by the set-up kernel, before the prefix stream, and read by the
-// finish kernel: for phase p < kPhaseMax and sequence b, entry (p * nb + b) holds
+// streaming kernels and the finish kernel.  The workspace starts with a header of int32 words
+// (the job queue's ticket counter, the item count and the work list's c0 and np), and from
+// byte kWsTableOff, for phase p < kPhaseMax and sequence b, entry (p * nb + b) holds
 //   base  the item index of (p, b, head 0): the items of (p, b, h) are base + h n .. + n - 1
-//   n     items per head of sequence b in phase p (0 for phases past np)
-// so a reader locates every item of (b, h) with 2 kPhaseMax scalar loads and no division.
+//   n     items per head of sequence b in phase p (0 for phases past np; base is then the
+//         running total)
+// so a reader locates every item of (b, h) with 2 kPhaseMax scalar loads and no division,
+// and the streaming kernels find the (p, b) entry of an item by a binary search over the
+// bases, which never decrease.
 constexpr size_t kWsTableOff = 256;                  // byte offset of the table in the workspace
+constexpr int kWsTicket = 0, kWsTotal = 1, kWsC0 = 2, kWsNp = 3;   // header words
 
 __host__ __device__ inline size_t worklist_table_bytes(int nb) {
     return (size_t)kPhaseMax * (size_t)nb * 2 * sizeof(int32_t);
+}
+
+typedef const __attribute__((address_space(4))) int32_t* const_i32;
+
+// The work list as the set-up kernel recorded it; read with scalar loads (the header and the
+// table do not change while the kernels that read them run).
+struct WorkTable {
+    const_i32 tab;       // the table (2 words per entry)
+    WorkList w;
+    int total;           // items
+};
+
+__device__ __forceinline__ WorkTable read_worktable(const void* ws, int nb, int H, int lim) {
+    const const_i32 hdr = (const_i32)ws;
+    WorkTable t;
+    t.tab = (const_i32)((const char*)ws + kWsTableOff);
+    t.w = WorkList{nb, H, lim, hdr[kWsC0], hdr[kWsNp]};
+    t.total = hdr[kWsTotal];
+    return t;
+}
+
+// Locate item `item` through the table: sequence b, head h, tiles [t0, t1); false past the last
+// item.  The entry holding it is the last one whose base is <= item (entries with no items
+// share their base with the next entry, so the search skips them).
+__device__ __forceinline__ bool table_item(const int32_t* kv_len, const WorkTable& t, int item,
+                                           int& b, int& h, int& t0, int& t1) {
+    if (item < 0 || item >= t.total) return false;
+    int lo = 0, hi = kPhaseMax * t.w.nb - 1;           // tab base of entry 0 is 0 <= item
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (t.tab[2 * mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int p = lo / t.w.nb;
+    b = lo - p * t.w.nb;
+    const int n = t.tab[2 * lo + 1];
+    const int rel = item - t.tab[2 * lo];
+    h = rel / n;
+    const int j = rel - h * n;
+    int s, e;
+    phase_range(t.w, prefix_tiles(kv_len, b, t.w.lim), p, s, e);
+    t0 = s + j * phase_chunk(t.w, p);
+    t1 = min(t0 + phase_chunk(t.w, p), e);
+    return true;
 }
 
 }  // namespace hci

@@ -60,8 +60,9 @@ class DeviceState:
         self.k_cache = torch.empty(n, dtype=at, device=device)
         self.v_cache = torch.empty(n, dtype=at, device=device)
         self.kv_len = torch.zeros(nb, dtype=torch.int32, device=device)
+        self.status = torch.zeros(nb, dtype=torch.int32, device=device)     # HCI_DS_* bits per sequence
         self.c = hci.make_state(layer.act, kv_cap, self.short_win, self.outer_win, self.iir,
-                                self.k_cache, self.v_cache, self.kv_len)
+                                self.k_cache, self.v_cache, self.kv_len, self.status)
 
     def load_small(self, st: Dict[str, np.ndarray]) -> None:
         cfg = self.layer.cfg
@@ -153,11 +154,12 @@ def verify(layer: DeviceLayer, state: DeviceState, blk: DeviceBlock, max_kv_len:
     hci.verify_block(layer.c, state.c, blk.c, blk.nb, blk.nc, blk.gamma, max_kv_len, ws, stream)
 
 
-def accept(acc: DeviceAccept, mode: int, temperature: float = 1.0, stream=None) -> None:
+def accept(acc: DeviceAccept, mode: int, temperature: float = 1.0, stream=None, status=None) -> None:
+    """status: the [nb] status words to report into (e.g. DeviceState.status), or None."""
     sample = mode != hci.GREEDY
     hci.accept(mode, acc.nb, acc.nc, acc.gamma, acc.vocab, temperature, acc.zt,
                acc.zd if sample else None, acc.drafts, acc.u if sample else None,
-               acc.n_acc, acc.next, acc.best, acc.margin, stream)
+               acc.n_acc, acc.next, acc.best, acc.margin, stream, status)
 
 
 def slice_state(layer: DeviceLayer, state: DeviceState, blk: DeviceBlock, acc: DeviceAccept, max_kv_len: int,

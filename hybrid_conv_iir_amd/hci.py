@@ -17,6 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhci.so")
 
 OK, EINVAL, ECAPACITY, EUNSUPPORTED, EDEVICE, EWORKSPACE = 0, -1, -2, -3, -4, -5
+# device status bits (include/hci.h, HCI_DS_*)
+DS_NONFINITE, DS_K_RANGE, DS_CAND_RANGE, DS_KV_LEN, DS_DRAFT_ID = 0x1, 0x2, 0x4, 0x8, 0x10
 F32, BF16 = 0, 1
 GREEDY, SAMPLE, SAMPLE_RECURSIVE = 0, 1, 2
 KV_TILE = 32
@@ -24,7 +26,7 @@ KV_TILE = 32
 
 class HciError(RuntimeError):
     def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: {_lib.hci_status_string(status).decode()} ({status})")
+        super().__init__(f"{where}: {status_string(status)} ({status})")
         self.status = status
 
 
@@ -49,7 +51,7 @@ class Layer(ctypes.Structure):
 
 class State(ctypes.Structure):
     _fields_ = [("kv_cap", _i), ("short_win", _p), ("outer_win", _p), ("iir", _p), ("k_cache", _p),
-                ("v_cache", _p), ("kv_len", _p)]
+                ("v_cache", _p), ("kv_len", _p), ("status", _p)]
 
 
 class Block(ctypes.Structure):
@@ -96,14 +98,15 @@ class Drafter(ctypes.Structure):
 
 
 EXPORTS = {
-    "hci_status_string": (ctypes.c_char_p, [_i]),
+    "hci_status_string": (_i, [_i, ctypes.c_char_p, _sz]),
+    "hci_device_status_string": (_i, [ctypes.c_uint32, ctypes.c_char_p, _sz]),
     "hci_version": (_i, []),
     "hci_verify_workspace_bytes": (_sz, [ctypes.POINTER(Layer), _i, _i, _i, _i]),
     "hci_verify_block": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), ctypes.POINTER(Block),
                               _i, _i, _i, _i, _p, _sz, _p]),
     "hci_verify_block_timed": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), ctypes.POINTER(Block),
                                     _i, _i, _i, _i, _p, _sz, _p, _p]),
-    "hci_accept": (_i, [_i, _i, _i, _i, _i, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "hci_accept": (_i, [_i, _i, _i, _i, _i, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "hci_slice_state": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), ctypes.POINTER(Block),
                              _i, _i, _i, _i, _p, _p, _p]),
     "hci_prefill_workspace_bytes": (_sz, [ctypes.POINTER(Layer), _i, _i, _i]),
@@ -170,11 +173,12 @@ def make_layer(d, taps_short, taps_outer, poles, heads, head_dim, act, w_short, 
                  _ptr(beta, f32, "beta"), _ptr(c, f32, "c"))
 
 
-def make_state(act, kv_cap, short_win, outer_win, iir, k_cache, v_cache, kv_len) -> State:
+def make_state(act, kv_cap, short_win, outer_win, iir, k_cache, v_cache, kv_len, status=None) -> State:
+    """status: optional [nb] int32 device tensor that receives the HCI_DS_* bits (uint32 words)."""
     at = act_torch_dtype(act)
     return State(kv_cap, _ptr(short_win, at, "short_win"), _ptr(outer_win, torch.float32, "outer_win"),
                  _ptr(iir, torch.float32, "iir"), _ptr(k_cache, at, "k_cache"), _ptr(v_cache, at, "v_cache"),
-                 _ptr(kv_len, torch.int32, "kv_len"))
+                 _ptr(kv_len, torch.int32, "kv_len"), _ptr(status, torch.int32, "status"))
 
 
 def make_block(act, x, q, k, v, f, s, y, o) -> Block:
@@ -189,8 +193,20 @@ def version() -> int:
     return _lib.hci_version()
 
 
+def _text(fn, value) -> str:
+    n = fn(value, None, 0)
+    buf = ctypes.create_string_buffer(n + 1)
+    fn(value, buf, n + 1)
+    return buf.value.decode()
+
+
 def status_string(status: int) -> str:
-    return _lib.hci_status_string(status).decode()
+    return _text(_lib.hci_status_string, status)
+
+
+def device_status_string(bits: int) -> str:
+    """Names of the HCI_DS_* bits set in a status word copied to the host."""
+    return _text(_lib.hci_device_status_string, int(bits) & 0xFFFFFFFF)
 
 
 def verify_workspace_bytes(layer: Layer, nb: int, nc: int, gamma: int, max_kv_len: int) -> int:
@@ -218,7 +234,8 @@ def verify_block_timed(layer: Layer, state: State, block: Block, nb: int, nc: in
 
 def accept(mode: int, nb: int, nc: int, gamma: int, vocab: int, temperature: float,
            target_logits, draft_logits, draft_tokens, uniforms,
-           n_accepted, next_token, best_cand=None, margin=None, stream=None) -> None:
+           n_accepted, next_token, best_cand=None, margin=None, stream=None, status=None) -> None:
+    """status: optional [nb] int32 device tensor receiving HCI_DS_* bits."""
     _check(_lib.hci_accept(mode, nb, nc, gamma, vocab, float(temperature),
                            _ptr(target_logits, torch.float32, "target_logits"),
                            _ptr(draft_logits, torch.float32, "draft_logits"),
@@ -226,7 +243,7 @@ def accept(mode: int, nb: int, nc: int, gamma: int, vocab: int, temperature: flo
                            _ptr(uniforms, torch.float64, "uniforms"),
                            _ptr(n_accepted, torch.int32, "n_accepted"), _ptr(next_token, torch.int32, "next_token"),
                            _ptr(best_cand, torch.int32, "best_cand"), _ptr(margin, torch.float64, "margin"),
-                           _stream(stream)), "hci_accept")
+                           _ptr(status, torch.int32, "status"), _stream(stream)), "hci_accept")
 
 
 def slice_state(layer: Layer, state: State, block: Block, nb: int, nc: int, gamma: int, max_kv_len: int,

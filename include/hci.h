@@ -57,11 +57,44 @@ extern "C" {
 /* Rows of the KV cache are grouped in tiles of this many keys. */
 #define HCI_KV_TILE 32
 
-/* Human-readable name of a status code (static storage, never NULL). */
-const char* hci_status_string(int status);
+/* Writes the human-readable name of a status code into buf (at most n bytes,
+ * always NUL-terminated when n > 0; truncated if it does not fit) and returns
+ * the length of the full name without the NUL, as snprintf does, so a call with
+ * n = 0 (buf may then be NULL) sizes the buffer.  HCI_EINVAL if buf is NULL
+ * and n > 0.  Never touches the device. */
+int hci_status_string(int status, char* buf, size_t n);
 
 /* Library ABI version (major * 100 + minor). */
 int hci_version(void);
+
+/* ------------------------------------------------------ device status word
+ *
+ * Host checks cannot see values that live on the device (kv_len, the k and
+ * c* that acceptance hands to slicing, the logits).  Kernels that find such a
+ * value out of contract OR one of these bits into the caller's status word of
+ * that sequence (uint32 per sequence, hci_state.status and the status argument
+ * of hci_accept; a NULL pointer disables the reporting but not the guard), so
+ * the caller sees it after its next synchronisation.  The bits accumulate until
+ * the caller clears them (they are never cleared by the library).  Every kernel
+ * still runs to completion; what the guard does instead is stated per bit. */
+#define HCI_DS_NONFINITE     0x1u  /* accept: a logit it read is NaN or +Inf, or a row it read has no
+                                      finite entry.  The block's n_accepted and next_token are set
+                                      to -1 (and best_cand to -1 when no candidate of the sequence
+                                      is valid), so slicing then commits nothing for it. */
+#define HCI_DS_K_RANGE       0x2u  /* slice: n_accepted of the winning candidate outside [0, gamma];
+                                      the sequence's state is left unchanged. */
+#define HCI_DS_CAND_RANGE    0x4u  /* slice: best_cand outside [0, nc); state left unchanged. */
+#define HCI_DS_KV_LEN        0x8u  /* verify / slice / prefill: kv_len[b] outside [0, max_kv_len].
+                                      Verify attends to the clamped length; slice and prefill leave
+                                      the sequence's state (windows, IIR state, cache, kv_len)
+                                      unchanged. */
+#define HCI_DS_DRAFT_ID      0x10u /* accept: a draft token id outside [0, V) (it counted as a
+                                      mismatch / rejection, as documented; reported only). */
+
+/* Writes the names of the bits set in `bits` (a status word copied to the
+ * host), separated by '|', into buf with the conventions of hci_status_string;
+ * "none" when no bit is set. */
+int hci_device_status_string(uint32_t bits, char* buf, size_t n);
 
 /* -------------------------------------------------------------- structures */
 
@@ -96,7 +129,9 @@ typedef struct hci_layer {
  *                                 Read and write logical rows only through
  *                                 hci_kv_write / hci_kv_read.
  *   kv_len    [nb] int32          readable prefix length of each sequence
- *   kv_cap                        rows per (sequence, head); multiple of 32. */
+ *   kv_cap                        rows per (sequence, head); multiple of 32
+ *   status    [nb] uint32         device status words (HCI_DS_* bits), may be
+ *                                 NULL; the kernels only OR bits in. */
 typedef struct hci_state {
     int kv_cap;
     void* short_win;
@@ -105,6 +140,7 @@ typedef struct hci_state {
     void* k_cache;
     void* v_cache;
     int32_t* kv_len;
+    uint32_t* status;              /* [nb] device status words (HCI_DS_*), or NULL */
 } hci_state;
 
 /* One verify round's block: inputs, retained intermediates, outputs.
@@ -150,7 +186,9 @@ size_t hci_verify_workspace_bytes(const hci_layer* L, int nb, int nc, int gamma,
  * Committed state is only read: a round abandoned after verify can be
  * verified again from the same state.
  *   max_kv_len  host-side upper bound on every kv_len[b] (sizes the grid);
- *               must satisfy max_kv_len + gamma + 1 <= kv_cap.
+ *               must satisfy max_kv_len + gamma + 1 <= kv_cap.  A kv_len[b]
+ *               outside [0, max_kv_len] is read clamped into that range and
+ *               reported as HCI_DS_KV_LEN in S->status.
  *   ws, ws_bytes  device workspace of at least
  *               hci_verify_workspace_bytes(...) bytes, 256-byte aligned; two
  *               calls in flight at once must not share a workspace.
@@ -218,12 +256,18 @@ int hci_verify_block_timed(const hci_layer* L, const hci_state* S, const hci_blo
  *     end (n_accepted[b][best] = k); margin [nb][nc] fp64 = smallest relative distance of any
  *     decision from its threshold (greedy: smallest top-1 logit gap of the
  *     rows read); may be NULL.
+ *   status [nb] uint32 (may be NULL): HCI_DS_NONFINITE when a logit read is
+ *     NaN or +Inf or a row read has no finite entry (-Inf entries are valid,
+ *     probability 0); the block's n_accepted and next_token are then -1 and it
+ *     cannot win best_cand (best_cand = -1 if no candidate of the sequence is
+ *     valid; in the recursive mode every candidate of the sequence is marked).
+ *     HCI_DS_DRAFT_ID when a draft id read is outside [0, V).
  * Limits: 1 <= V <= 65536; temperature > 0 in the sampling modes; nc <= 64. */
 int hci_accept(int mode, int nb, int nc, int gamma, int vocab, float temperature,
                const float* target_logits, const float* draft_logits,
                const int32_t* draft_tokens, const double* uniforms,
                int32_t* n_accepted, int32_t* next_token, int32_t* best_cand,
-               double* margin, hipStream_t stream);
+               double* margin, uint32_t* status, hipStream_t stream);
 
 /* ------------------------------------------------------------------- slice */
 
@@ -236,7 +280,9 @@ int hci_accept(int mode, int nb, int nc, int gamma, int vocab, float temperature
  *   iir       <- s_k
  * k and c* are read on the device (no host synchronisation).  best_cand may
  * be NULL when nc == 1.  max_kv_len is the same host bound as for verify.
- * Rows that would land at or beyond kv_cap are never written. */
+ * A sequence whose c* is outside [0, nc), whose k is outside [0, gamma] or
+ * whose kv_len is outside [0, max_kv_len] is left unchanged, and the matching
+ * HCI_DS_* bit is set in S->status (nothing is clamped into range). */
 int hci_slice_state(const hci_layer* L, const hci_state* S, const hci_block* blk,
                     int nb, int nc, int gamma, int max_kv_len,
                     const int32_t* n_accepted, const int32_t* best_cand,
@@ -261,6 +307,9 @@ size_t hci_prefill_workspace_bytes(const hci_layer* L, int nb, int T, int want_y
  *   all four 16-byte aligned (HCI_EINVAL otherwise).
  *   max_kv_len  host bound on every kv_len[b]; max_kv_len + T <= kv_cap.
  *   ws, ws_bytes  workspace of hci_prefill_workspace_bytes(...), 256-aligned.
+ * A sequence whose kv_len is outside [0, max_kv_len] keeps its committed state
+ * (windows, IIR state, cache rows, kv_len) and gets HCI_DS_KV_LEN in S->status;
+ * its outputs y are still written.
  * Limits: N <= 16 poles; T <= 16776960.  The IIR runs as a chunked parallel
  * scan, so its results equal the sequential recurrence up to fp32 rounding. */
 int hci_prefill(const hci_layer* L, const hci_state* S, int nb, int T, int max_kv_len,

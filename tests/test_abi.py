@@ -43,9 +43,26 @@ def test_binding_covers_every_symbol():
 
 def test_status_strings(lib):
     from hybrid_conv_iir_amd import hci
-    assert hci.version() == 100
+    assert hci.version() == 200
     for code in (0, -1, -2, -3, -4, -5):
         assert hci.status_string(code).startswith("HCI")
+    f = hci._lib.hci_status_string
+    full = hci.status_string(hci.EINVAL)
+    assert f(hci.EINVAL, None, 0) == len(full)                 # sizing call
+    buf = ctypes.create_string_buffer(b"\xff" * 8)
+    assert f(hci.EINVAL, buf, 5) == len(full)                  # truncated, NUL-terminated
+    assert buf.raw[:5] == full[:4].encode() + b"\0" and buf.raw[5:8] == b"\xff" * 3
+    assert f(hci.EINVAL, None, 5) == hci.EINVAL
+
+
+def test_device_status_strings():
+    from hybrid_conv_iir_amd import hci
+    assert hci.device_status_string(0) == "none"
+    assert hci.device_status_string(hci.DS_NONFINITE | hci.DS_KV_LEN) == "HCI_DS_NONFINITE|HCI_DS_KV_LEN"
+    assert hci.device_status_string(hci.DS_K_RANGE) == "HCI_DS_K_RANGE"
+    assert hci.device_status_string(hci.DS_CAND_RANGE | hci.DS_DRAFT_ID) == "HCI_DS_CAND_RANGE|HCI_DS_DRAFT_ID"
+    assert hci.device_status_string(0x100) == "unknown 0x100"
+    assert hci._lib.hci_device_status_string(1, None, 3) == hci.EINVAL
 
 
 def _layer(hci, **kw):
@@ -88,16 +105,16 @@ def test_accept_and_slice_validation():
     from hybrid_conv_iir_amd import hci
     lib = hci._lib
     p = 4096
-    assert lib.hci_accept(3, 1, 1, 6, 512, 1.0, p, p, p, p, p, p, p, p, None) == hci.EINVAL
-    assert lib.hci_accept(-1, 1, 1, 6, 512, 1.0, p, p, p, p, p, p, p, p, None) == hci.EINVAL
-    assert lib.hci_accept(hci.SAMPLE_RECURSIVE, 1, 2, 6, 512, -1.0, p, p, p, p, p, p, p, p, None) == hci.EINVAL
-    assert lib.hci_accept(hci.SAMPLE_RECURSIVE, 1, 2, 6, 512, 1.0, p, p, p, None, p, p, p, p, None) == hci.EINVAL
-    assert lib.hci_accept(hci.SAMPLE_RECURSIVE, 1, 65, 6, 512, 1.0, p, p, p, p, p, p, p, p, None) == hci.EINVAL
-    assert lib.hci_accept(hci.SAMPLE, 1, 1, 6, 512, 0.0, p, p, p, p, p, p, p, p, None) == hci.EINVAL
-    assert lib.hci_accept(hci.SAMPLE, 1, 1, 6, 512, 1.0, p, None, p, p, p, p, p, p, None) == hci.EINVAL
-    assert lib.hci_accept(hci.GREEDY, 1, 1, 6, 0, 1.0, p, None, p, None, p, p, p, p, None) == hci.EINVAL
-    assert lib.hci_accept(hci.GREEDY, 1, 1, 6, 1 << 20, 1.0, p, None, p, None, p, p, p, p, None) == hci.EUNSUPPORTED
-    assert lib.hci_accept(hci.GREEDY, 1, 1, 6, 512, 1.0, None, None, p, None, p, p, p, p, None) == hci.EINVAL
+    assert lib.hci_accept(3, 1, 1, 6, 512, 1.0, p, p, p, p, p, p, p, p, None, None) == hci.EINVAL
+    assert lib.hci_accept(-1, 1, 1, 6, 512, 1.0, p, p, p, p, p, p, p, p, None, None) == hci.EINVAL
+    assert lib.hci_accept(hci.SAMPLE_RECURSIVE, 1, 2, 6, 512, -1.0, p, p, p, p, p, p, p, p, None, None) == hci.EINVAL
+    assert lib.hci_accept(hci.SAMPLE_RECURSIVE, 1, 2, 6, 512, 1.0, p, p, p, None, p, p, p, p, None, None) == hci.EINVAL
+    assert lib.hci_accept(hci.SAMPLE_RECURSIVE, 1, 65, 6, 512, 1.0, p, p, p, p, p, p, p, p, None, None) == hci.EINVAL
+    assert lib.hci_accept(hci.SAMPLE, 1, 1, 6, 512, 0.0, p, p, p, p, p, p, p, p, None, None) == hci.EINVAL
+    assert lib.hci_accept(hci.SAMPLE, 1, 1, 6, 512, 1.0, p, None, p, p, p, p, p, p, None, None) == hci.EINVAL
+    assert lib.hci_accept(hci.GREEDY, 1, 1, 6, 0, 1.0, p, None, p, None, p, p, p, p, None, None) == hci.EINVAL
+    assert lib.hci_accept(hci.GREEDY, 1, 1, 6, 1 << 20, 1.0, p, None, p, None, p, p, p, p, None, None) == hci.EUNSUPPORTED
+    assert lib.hci_accept(hci.GREEDY, 1, 1, 6, 512, 1.0, None, None, p, None, p, p, p, p, None, None) == hci.EINVAL
     lay = _layer(hci)
     st = hci.State(kv_cap=512, short_win=16, outer_win=16, iir=16, k_cache=16, v_cache=16, kv_len=16)
     blk = hci.Block(x=16, q=16, k=16, v=16, f=16, s=16, y=16, o=16)
