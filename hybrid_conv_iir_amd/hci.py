@@ -106,6 +106,8 @@ EXPORTS = {
                               _i, _i, _i, _i, _p, _sz, _p]),
     "hci_verify_block_timed": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), ctypes.POINTER(Block),
                                     _i, _i, _i, _i, _p, _sz, _p, _p]),
+    "hci_verify_block_noalloc": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), ctypes.POINTER(Block),
+                                      _i, _i, _i, _i, _p]),
     "hci_accept": (_i, [_i, _i, _i, _i, _i, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "hci_slice_state": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), ctypes.POINTER(Block),
                              _i, _i, _i, _i, _p, _p, _p]),
@@ -219,6 +221,16 @@ def verify_block(layer: Layer, state: State, block: Block, nb: int, nc: int, gam
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(_lib.hci_verify_block(ctypes.byref(layer), ctypes.byref(state), ctypes.byref(block), nb, nc, gamma,
                                  max_kv_len, wsp, nbytes, _stream(stream)), "hci_verify_block")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def verify_block_noalloc(layer: Layer, state: State, block: Block, nb: int, nc: int, gamma: int, max_kv_len: int,
+                         stream=None) -> None:
+    """hci_verify_block with the library's own scratch array as workspace (no allocation)."""
+    _check(_lib.hci_verify_block_noalloc(ctypes.byref(layer), ctypes.byref(state), ctypes.byref(block), nb, nc,
+                                         gamma, max_kv_len, _stream(stream)), "hci_verify_block_noalloc")
 
 
 def verify_block_timed(layer: Layer, state: State, block: Block, nb: int, nc: int, gamma: int, max_kv_len: int,

@@ -212,6 +212,25 @@ int hci_verify_block_timed(const hci_layer* L, const hci_state* S, const hci_blo
                            int nb, int nc, int gamma, int max_kv_len,
                            void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
 
+/* hci_verify_block for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, results and errors as hci_verify_block, but the workspace is
+ * a library-owned device array of HCI_NOALLOC_SCRATCH_BYTES bytes (one per
+ * GPU, held until the process ends; its address is looked up once per device).
+ * Nothing is allocated or freed by the call.
+ *  - HCI_EWORKSPACE (nothing enqueued) when hci_verify_workspace_bytes for
+ *    these sizes exceeds HCI_NOALLOC_SCRATCH_BYTES (e.g. one sequence of up to
+ *    262144 prefix tokens at 32 or 64 heads of 128 and gamma <= 12 fits; four
+ *    sequences of four candidate blocks at 64k tokens do not).
+ *  - Every call on a GPU shares that GPU's array: calls whose work overlaps
+ *    on one GPU (two streams, or two threads) race and must be ordered by the
+ *    caller.  Each call re-initialises the parts it reads first (the queue
+ *    counter and the work list), whatever an earlier call left there.
+ *  - HCI_EDEVICE if the device's array cannot be located. */
+#define HCI_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int hci_verify_block_noalloc(const hci_layer* L, const hci_state* S, const hci_block* blk,
+                             int nb, int nc, int gamma, int max_kv_len, hipStream_t stream);
+
 /* ------------------------------------------------------------------ accept */
 
 /* Lossless acceptance for every candidate block, and the best candidate.
