@@ -45,6 +45,15 @@ Pinning (see tests/test_oracle_*.py):
     exact first-token distribution = target over every draft combination
     (decision boundaries found by bisection); Monte-Carlo joint law of the
     first two emitted tokens under a toy prefix-keyed target and drafter.
+  * token trees: every node's forward equals the chain forward over its
+    root-to-node path (chains, stars, random trees, trees deeper than the
+    outer window); the tree mask; greedy and sampling acceptance reduce to the
+    one-block rules on a chain, greedy matches a brute-force search on random
+    trees, the first emitted token is exactly target-distributed over every
+    combination of children tokens (each child with its own draft
+    distribution), a Monte-Carlo joint law of two emitted tokens on depth-2
+    trees; tree forward + slice along the accepted path equals sequential
+    steps over the path.
 """
 from .layer import (depthwise_fir, modal_iir, block_attention, verify_block,
                     as_f64, Layer, SeqState)
@@ -54,6 +63,7 @@ from .prefill import depthwise_fir_long, iir_scan, prefill_state
 from .linear import linear, rmsnorm
 from . import model
 from . import drafter
+from . import tree
 
 __all__ = [
     "depthwise_fir", "modal_iir", "block_attention", "verify_block", "as_f64",
