@@ -582,6 +582,203 @@ __global__ __launch_bounds__(kAccT) void k_accept(
     }
 }
 
+// ------------------------------------------------------------------ token trees
+//
+// Acceptance over a token tree of n <= 64 nodes per sequence (node 0 the anchor, parent p(m) < m;
+// several candidate blocks that share prefixes: EvSpark digest, Interpretation; tree verification:
+// ReaDy summary, section 5).  One workgroup per sequence walks from the anchor:
+//   greedy: at node m the target row's argmax is compared with m's children in index order and
+//     the first child holding it becomes the current node; otherwise the argmax is emitted.
+//   sampling: m's children are tried in index order against the running residual w / z of the
+//     target row p (w = p, z = 1): child c, token t, drawn from q_c = softmax(draft row c / T), is
+//     kept iff r_c q_c(t) z < w(t); a rejection sets w <- max(0, w - z q_c), z <- sum w.  A kept
+//     child becomes the current node; if all are rejected the next token is drawn from w, and at
+//     a node without children from p, with r* = u[b][0] (multi-step speculative sampling with one
+//     draft distribution per child).
+// Outputs per sequence: n_accepted = depth of the accepted node, path[0..k] = its nodes from the
+// anchor (entries past k are -1), next_token, margin.
+
+constexpr int kTreeNodes = 64;
+
+struct TreeAccScratch {
+    AccScratch a;
+    int par[kTreeNodes], first[kTreeNodes], sib[kTreeNodes], path[kTreeNodes];
+    int rnode[kTreeNodes];               // rejected children at the current node, in order
+    double rqm[kTreeNodes], rqs[kTreeNodes];
+    double zh[kTreeNodes + 1];
+    int zapp[kTreeNodes];
+    double pst[2], qst[2];
+    int flag;
+};
+
+__global__ __launch_bounds__(kAccT) void k_accept_tree(
+    int mode, int n, int V, double T, const int32_t* __restrict__ parent, const int32_t* __restrict__ tokens,
+    const float* __restrict__ zt, const float* __restrict__ zd, const double* __restrict__ uni,
+    int32_t* __restrict__ n_acc, int32_t* __restrict__ path_out, int32_t* __restrict__ next,
+    double* __restrict__ margin_out, uint32_t* __restrict__ status)
+{
+    __shared__ TreeAccScratch sh;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int32_t* tok = tokens + (size_t)b * n;
+    // the tree in LDS: parents (validated), then first child / next sibling lists in index order
+    if (tid == 0) sh.flag = 1;
+    __syncthreads();
+    if (tid < n) {
+        const int p = parent[(size_t)b * n + tid];
+        const bool ok = tid == 0 ? p == -1 : (p >= 0 && p < tid);
+        if (!ok) sh.flag = 0;
+        sh.par[tid] = ok ? p : -1;
+        sh.first[tid] = -1;
+        sh.sib[tid] = -1;
+        sh.path[tid] = -1;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int c = n - 1; c >= 1; --c) {            // prepend in descending order: lists ascend
+            const int p = sh.par[c];
+            if (p >= 0) {
+                sh.sib[c] = sh.first[p];
+                sh.first[p] = c;
+            }
+        }
+        sh.path[0] = 0;
+    }
+    __syncthreads();
+    bool bad = sh.flag == 0;
+    uint32_t flags = bad ? HCI_DS_TREE : 0u;
+    int m = 0, k = 0, nxt = -1;
+    double margin = INFINITY;
+    const float* ztb = zt + (size_t)b * n * V;
+    const float* zdb = zd ? zd + (size_t)b * n * V : nullptr;
+    while (!bad) {
+        const float* prow = ztb + (size_t)m * V;
+        if (mode == HCI_GREEDY) {
+            if (wv == 0) {
+                int g; double gap; bool rb;
+                wave_row_argmax(prow, V, lane, g, gap, rb);
+                if (lane == 0) { sh.a.arg[0] = g; sh.a.gap[0] = gap; sh.a.badrow[0] = rb ? 1 : 0; }
+            }
+            __syncthreads();
+            const int g = sh.a.arg[0];
+            margin = fmin(margin, sh.a.gap[0]);
+            if (sh.a.badrow[0]) { bad = true; break; }
+            int found = -1;
+            for (int c = sh.first[m]; c >= 0; c = sh.sib[c]) {
+                const int t = tok[c];
+                if (t < 0 || t >= V) flags |= HCI_DS_DRAFT_ID;
+                if (t == g) { found = c; break; }
+            }
+            __syncthreads();                          // arg / gap are rewritten at the next node
+            if (found < 0) { nxt = g; break; }
+            m = found;
+            sh.path[++k] = m;                         // every thread stores the same value
+            continue;
+        }
+        // sampling: the target row's statistics, then the children in order
+        if (wv == 0) {
+            double mx, sum;
+            wave_row_stats(prow, V, T, lane, mx, sum);
+            if (lane == 0) { sh.pst[0] = mx; sh.pst[1] = sum; sh.zh[0] = 1.0; }
+        }
+        __syncthreads();
+        const double pm = sh.pst[0], ps = sh.pst[1];
+        if (!row_finite(ps)) { bad = true; break; }
+        int nrej = 0, kept = -1;
+        for (int c = sh.first[m]; c >= 0 && !bad; c = sh.sib[c]) {
+            const float* qrow = zdb + (size_t)c * V;
+            if (wv == 0) {
+                double mx, sum;
+                wave_row_stats(qrow, V, T, lane, mx, sum);
+                if (lane == 0) { sh.qst[0] = mx; sh.qst[1] = sum; }
+            }
+            __syncthreads();
+            const double qm = sh.qst[0], qs = sh.qst[1];
+            if (!row_finite(qs)) { bad = true; break; }
+            // residual weight of token j after the rejections so far at this node
+            auto resid = [&](int j, double p) {
+                double w = p;
+                for (int i = 0; i < nrej; ++i)
+                    if (sh.zapp[i])
+                        w = fmax(0.0, w - __dmul_rn(sh.zh[i], exp((double)zdb[(size_t)sh.rnode[i] * V + j] / T -
+                                                                  sh.rqm[i]) / sh.rqs[i]));
+                return w;
+            };
+            const int t = tok[c];
+            if (t >= 0 && t < V) {
+                const double p_t = exp((double)prow[t] / T - pm) / ps;
+                const double q_t = exp((double)qrow[t] / T - qm) / qs;
+                const double lhs = uni[(size_t)b * n + c] * q_t * sh.zh[nrej];
+                const double rhs = resid(t, p_t);
+                margin = fmin(margin, fabs(lhs - rhs) / fmax(rhs, 1e-300));
+                if (lhs < rhs) { kept = c; break; }
+            } else {
+                flags |= HCI_DS_DRAFT_ID;
+            }
+            // rejection: total of max(0, w - z q_c) over the vocabulary
+            const double z = sh.zh[nrej];
+            double loc = 0.0;
+            for (int j = tid; j < V; j += kAccT) {
+                const double q = exp((double)qrow[j] / T - qm) / qs;
+                loc += fmax(0.0, resid(j, exp((double)prow[j] / T - pm) / ps) - __dmul_rn(z, q));
+            }
+            const double tot = block_sum(loc, sh.a);
+            __syncthreads();
+            if (tid == 0) {
+                const bool ok = tot > 0.0;            // cannot fail after a rejection; guard only
+                sh.zapp[nrej] = ok ? 1 : 0;
+                sh.zh[nrej + 1] = ok ? tot : z;
+                sh.rnode[nrej] = c;
+                sh.rqm[nrej] = qm;
+                sh.rqs[nrej] = qs;
+            }
+            __syncthreads();
+            ++nrej;
+        }
+        if (bad) break;
+        if (kept >= 0) {
+            m = kept;
+            if (tid == 0) sh.path[k + 1] = m;
+            ++k;
+            __syncthreads();
+            continue;
+        }
+        const int r = nrej;
+        auto weight = [&](int j) {
+            const double p = exp((double)prow[j] / T - pm) / ps;
+            if (r == 0) return p;
+            double w = p;
+            for (int i = 0; i < r; ++i)
+                if (sh.zapp[i])
+                    w = fmax(0.0, w - __dmul_rn(sh.zh[i], exp((double)zdb[(size_t)sh.rnode[i] * V + j] / T -
+                                                              sh.rqm[i]) / sh.rqs[i]));
+            return w;
+        };
+        int tk;
+        double m2;
+        draw_token(weight, V, uni[(size_t)b * n], sh.a, tk, m2);
+        nxt = tk;
+        margin = fmin(margin, m2);
+        break;
+    }
+    __syncthreads();
+    if (tid < n) path_out[(size_t)b * n + tid] = (!bad && tid <= k) ? sh.path[tid] : -1;
+    if (tid == 0) {
+        n_acc[b] = bad ? -1 : k;
+        next[b] = bad ? -1 : nxt;
+        if (margin_out) margin_out[b] = bad ? qnan() : margin;
+        report(status, b, flags | (bad && !(flags & HCI_DS_TREE) ? HCI_DS_NONFINITE : 0u));
+    }
+}
+
+hipError_t launch_accept_tree(int mode, int nb, int n, int V, float temperature, const int32_t* parent,
+                              const int32_t* tokens, const float* zt, const float* zd, const double* u, int32_t* n_acc,
+                              int32_t* path, int32_t* next, double* margin, uint32_t* status, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_accept_tree, dim3(nb), dim3(kAccT), 0, st, mode, n, V, (double)temperature, parent, tokens,
+                       zt, zd, u, n_acc, path, next, margin, status);
+    return hipGetLastError();
+}
+
 // best candidate of each sequence: the largest n_accepted, lowest index on ties; a candidate
 // marked invalid (n_accepted -1) never wins, and -1 when none is valid
 __global__ __launch_bounds__(256) void k_accept_best(int nb, int nc, const int32_t* __restrict__ n_acc,

@@ -97,7 +97,7 @@ int hci_device_status_string(uint32_t bits, char* buf, size_t n) {
     static const struct { uint32_t bit; const char* name; } names[] = {
         {HCI_DS_NONFINITE, "HCI_DS_NONFINITE"}, {HCI_DS_K_RANGE, "HCI_DS_K_RANGE"},
         {HCI_DS_CAND_RANGE, "HCI_DS_CAND_RANGE"}, {HCI_DS_KV_LEN, "HCI_DS_KV_LEN"},
-        {HCI_DS_DRAFT_ID, "HCI_DS_DRAFT_ID"}};
+        {HCI_DS_DRAFT_ID, "HCI_DS_DRAFT_ID"}, {HCI_DS_TREE, "HCI_DS_TREE"}};
     char text[160];
     size_t used = 0;
     text[0] = '\0';
@@ -184,6 +184,67 @@ int hci_slice_state(const hci_layer* L, const hci_state* S, const hci_block* blk
     if (rc) return rc;
     if (!blk || !blk->x || !blk->k || !blk->v || !blk->f || !blk->s) return HCI_EINVAL;
     if (launch_slice(L, S, blk, nb, nc, gamma + 1, max_kv_len, n_accepted, best_cand, stream) != hipSuccess)
+        return HCI_EDEVICE;
+    return HCI_OK;
+}
+
+static hci_block tree_block(const hci_tree* t) {
+    hci_block blk{};
+    blk.x = t->x; blk.q = t->q; blk.k = t->k; blk.v = t->v;
+    blk.f = t->f; blk.s = t->s; blk.y = t->y; blk.o = t->o;
+    return blk;
+}
+
+int hci_verify_tree(const hci_layer* L, const hci_state* S, const hci_tree* tree,
+                    int nb, int n, int max_kv_len, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_layer(L);
+    if (rc) return rc;
+    if (!tree || !tree->parent || n < 1 || max_kv_len < 0) return HCI_EINVAL;
+    if (n > 64 || L->poles > 16) return HCI_EUNSUPPORTED;
+    rc = check_state(L, S, nb, (long long)max_kv_len + n);
+    if (rc) return rc;
+    const hci_block blk = tree_block(tree);
+    rc = check_block(&blk);
+    if (rc) return rc;
+    if (tree_finish_lds_bytes(L, n) > kMaxLds) return HCI_EUNSUPPORTED;
+    const AttnPlan plan = plan_attention(L, nb, 1, n - 1, max_kv_len, device_cu_count());
+    if (plan.items_cap < 0) return HCI_EUNSUPPORTED;
+    if (!ws || ws_bytes < plan.bytes || !aligned(ws, 256)) return HCI_EWORKSPACE;
+    if (launch_verify(L, S, &blk, nb, 1, n, plan, ws, stream, nullptr, true, tree->parent) != hipSuccess)
+        return HCI_EDEVICE;
+    return HCI_OK;
+}
+
+int hci_accept_tree(int mode, int nb, int n, int vocab, float temperature, const int32_t* parent,
+                    const int32_t* tokens, const float* target_logits, const float* draft_logits,
+                    const double* uniforms, int32_t* n_accepted, int32_t* path, int32_t* next_token,
+                    double* margin, uint32_t* status, hipStream_t stream) {
+    if (mode != HCI_GREEDY && mode != HCI_SAMPLE) return HCI_EINVAL;
+    if (nb < 1 || nb > 2147483647 || n < 1 || vocab < 1) return HCI_EINVAL;
+    if (n > 64 || vocab > 65536) return HCI_EUNSUPPORTED;
+    if (!parent || !tokens || !target_logits || !n_accepted || !path || !next_token) return HCI_EINVAL;
+    if (mode == HCI_SAMPLE) {
+        if (!(temperature > 0.f) || temperature == INFINITY) return HCI_EINVAL;
+        if (!uniforms || !draft_logits) return HCI_EINVAL;
+    }
+    if (launch_accept_tree(mode, nb, n, vocab, temperature, parent, tokens, target_logits,
+                           mode == HCI_SAMPLE ? draft_logits : nullptr, uniforms, n_accepted, path, next_token, margin,
+                           status, stream) != hipSuccess)
+        return HCI_EDEVICE;
+    return HCI_OK;
+}
+
+int hci_slice_tree(const hci_layer* L, const hci_state* S, const hci_tree* tree, int nb, int n, int max_kv_len,
+                   const int32_t* n_accepted, const int32_t* path, hipStream_t stream) {
+    int rc = check_layer(L);
+    if (rc) return rc;
+    if (!tree || !tree->parent || !tree->x || !tree->k || !tree->v || !tree->f || !tree->s) return HCI_EINVAL;
+    if (n < 1 || max_kv_len < 0 || !n_accepted || !path) return HCI_EINVAL;
+    if (n > 64) return HCI_EUNSUPPORTED;
+    rc = check_state(L, S, nb, (long long)max_kv_len + n);
+    if (rc) return rc;
+    const hci_block blk = tree_block(tree);
+    if (launch_slice(L, S, &blk, nb, 1, n, max_kv_len, n_accepted, nullptr, stream, path, tree->parent) != hipSuccess)
         return HCI_EDEVICE;
     return HCI_OK;
 }

@@ -26,6 +26,7 @@
 // kernel with one item per workgroup.
 #include "conv_iir_body.h"
 #include "prefix_tile.h"
+#include "tree.h"
 #include "verify_parts.h"
 
 #include <math.h>
@@ -222,9 +223,16 @@ size_t stream_lds_bytes(const hci_layer* L, int nc, int P) {
 
 // One verify: reset the queue, stream the prefix (bf16: persistent queue kernel; fp32: one
 // workgroup per item), then the finish kernel (conv/IIR scan, causal block part, combine).
+size_t tree_finish_lds_bytes(const hci_layer* L, int n) {
+    const int act_bytes = L->act_dtype == HCI_BF16 ? 2 : 4;
+    const size_t conv = tree_conv_lds_bytes(L->taps_short, L->taps_outer, n);
+    const size_t comb = combine_lds_floats(n, L->head_dim, act_bytes, 16) * sizeof(float);
+    return conv > comb ? conv : comb;
+}
+
 hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block* blk,
                          int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st, hipEvent_t* ev,
-                         bool conv)
+                         bool conv, const int32_t* parent)
 {
     const int H = L->heads, DH = L->head_dim, nq = plan.nq;
     const float scale_log2 = kLog2e / sqrtf((float)DH);
@@ -272,14 +280,18 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
     F.q = blk->q; F.kb = blk->k; F.vb = blk->v; F.o = blk->o;
     F.nb = nb; F.H = H; F.DH = DH; F.nq = nq; F.P = P; F.kv_lim = plan.kv_lim; F.resident = plan.resident;
     F.scale_log2 = scale_log2;
+    F.parent = parent;
+    F.status = S->status;
     const int rg = combine_rows(nb, nc, H, P, plan.resident / kStreamSlots);
     F.rg_count = (P + rg - 1) / rg;
     const long long blocks = (long long)F.n_conv + (long long)F.rg_count * nc * H * nb;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     const int act_bytes = L->act_dtype == HCI_BF16 ? 2 : 4;
-    const size_t conv_lds = conv ? conv_iir_lds_floats(L->taps_short, L->taps_outer, nc * P) : 0;
-    const size_t comb_lds = combine_lds_floats(P, DH, act_bytes, rg);
-    const size_t lds = (conv_lds > comb_lds ? conv_lds : comb_lds) * sizeof(float);
+    const size_t conv_lds = !conv ? 0
+                            : parent ? tree_conv_lds_bytes(L->taps_short, L->taps_outer, P)
+                                     : conv_iir_lds_floats(L->taps_short, L->taps_outer, nc * P) * sizeof(float);
+    const size_t comb_lds = combine_lds_floats(P, DH, act_bytes, rg) * sizeof(float);
+    const size_t lds = conv_lds > comb_lds ? conv_lds : comb_lds;
     e = launch_finish(F, L->act_dtype, rg, (int)blocks, lds, st);
     if (e != hipSuccess) return e;
     return mark(3);

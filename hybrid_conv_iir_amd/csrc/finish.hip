@@ -1,6 +1,7 @@
 // The kernel that ends a verify: the conv/IIR scan and the merge of the
 // prefix partials with the causal block part.
 #include "conv_iir_body.h"
+#include "tree.h"
 #include "verify_parts.h"
 #include "worklist.h"
 
@@ -103,6 +104,9 @@ __device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, 
     float* st_o = lds + (size_t)2 * P * RS / 4;                    // [state][row][DH]
     float* st_ml = st_o + (size_t)(kCombW + 1) * RG * DH;           // [state][row][2]
     float* pwt = st_ml + (size_t)(kCombW + 1) * RG * 2 + 64 * wave; // [wave][64] block weights
+    // token trees: ancestor masks [64] (8-byte aligned) and pointer-doubling jumps [64]
+    uint64_t* tmask = (uint64_t*)(((uintptr_t)(st_ml + (size_t)(kCombW + 1) * RG * 2 + 64 * kCombW) + 7) & ~(uintptr_t)7);
+    uint8_t* tjump = (uint8_t*)(tmask + 64);
     auto krow = [&](int j) { return (const T*)(ks + (size_t)j * RS); };
     auto vrow = [&](int j) { return (const T*)(vs + (size_t)j * RS); };
 
@@ -209,6 +213,8 @@ __device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, 
         if (e < 2 * half) *dst(e) = sv[k];
     }
     for (int e = tid + SB * kCombT; e < 2 * half; e += kCombT) *dst(e) = *src(e);
+    const bool tree = A.parent != nullptr;
+    if (tree) tree_masks(A.parent + (size_t)b * P, P, tmask, tjump);     // uniform branch; has a barrier
 #pragma unroll
     for (int k = 0; k < RG; ++k) {
         float* so = st_o + ((size_t)wave * RG + k) * DH;
@@ -228,6 +234,9 @@ __device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, 
     const int jj = lane & 15, sl = lane >> 4, DS = DH / 4;
     for (int k = wave; k < nr; k += kCombW) {
         const int i = i0 + k;
+        // block keys query i sees: 0..i (a chain of candidate positions) or its ancestors and
+        // itself (a token tree; every ancestor has a lower index)
+        const uint64_t vis = tree ? tmask[i] : ~0ull;
         const T* qrow = q + (((size_t)b * nq + r0 + k) * H + h) * DH + sl * DS;
         float qv[kF32Dh / 4];
 #pragma unroll
@@ -236,8 +245,9 @@ __device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, 
         float mb = -INFINITY;
         for (int j0 = 0; j0 <= i; j0 += 16) {
             const int j = j0 + jj;
+            const bool see = j <= i && ((vis >> (j & 63)) & 1ull);
             float part = 0.f;
-            if (j <= i) {
+            if (see) {
                 const T* kr = krow(j) + sl * DS;
 #pragma unroll
                 for (int e0 = 0; e0 < kF32Dh / 4; e0 += 8) {
@@ -250,7 +260,7 @@ __device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, 
                 }
             }
             part = sum_over_rows(part);
-            const float sj = j <= i ? part * A.scale_log2 : -INFINITY;
+            const float sj = see ? part * A.scale_log2 : -INFINITY;
             if (sl == 0) pwt[j] = sj;
             mb = fmaxf(mb, sj);
         }
@@ -260,7 +270,7 @@ __device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, 
         for (int j0 = 0; j0 <= i; j0 += 16) {
             const int j = j0 + jj;
             float pj = 0.f;
-            if (j <= i) pj = __builtin_amdgcn_exp2f(pwt[j] - mb);
+            if (j <= i) pj = __builtin_amdgcn_exp2f(pwt[j] - mb);      // 0 for keys it does not see
             lsum += pj;
             if (sl == 0 && j <= i) pwt[j] = pj;
         }
@@ -308,6 +318,14 @@ __global__ __launch_bounds__(kCombT, 4) void k_verify_finish(FinishArgs A)
     const int id = blockIdx.x;
     if (id < A.n_conv) {
         const int groups = (A.d + kCG - 1) / kCG;
+        if (A.parent) {
+            const int cgi = id % groups, b = id / groups;
+            const uint32_t bad = tree_conv_block<ACT>(A.w_short, A.w_outer, A.lam, A.beta, A.cc, (const T*)A.short_win,
+                                                      A.outer_win, A.iir, (const T*)A.x, A.parent, A.f_out, A.s_out,
+                                                      (T*)A.y_out, A.d, A.Ts, A.To, A.N, A.P, cgi, b, lds);
+            if (bad && cgi == 0 && threadIdx.x == 0) report(A.status, b, bad);
+            return;
+        }
         conv_iir_block<ACT>(A.w_short, A.w_outer, A.lam, A.beta, A.cc, (const T*)A.short_win, A.outer_win, A.iir,
                             (const T*)A.x, A.f_out, A.s_out, (T*)A.y_out, A.d, A.Ts, A.To, A.N, A.nc, A.P,
                             id % groups, id / groups, lds);

@@ -111,16 +111,24 @@ constexpr size_t kMaxLds = 160 * 1024;
 // the whole verify: the prefix stream then the finish kernel; ev (may be null)
 // = 4 events recorded before the set-up kernel, before and after the streaming kernel, and at
 // the end
+// parent: a token tree per sequence ([nb][P] parents, nc = 1) instead of chains of candidate positions
 hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block* blk,
                          int nb, int nc, int P, const AttnPlan& plan, void* ws, hipStream_t st, hipEvent_t* ev,
-                         bool conv = true);
+                         bool conv = true, const int32_t* parent = nullptr);
+// dynamic LDS bytes of the finish kernel of a tree verify (tree conv role and combine role)
+size_t tree_finish_lds_bytes(const hci_layer* L, int n);
 hipError_t launch_accept(int mode, int nb, int nc, int gamma, int V, float temperature,
                          const float* zt, const float* zd, const int32_t* drafts, const double* u,
                          int32_t* n_acc, int32_t* next, int32_t* best, double* margin, uint32_t* status,
                          hipStream_t st);
 // lim: the host's bound on kv_len (max_kv_len); a sequence outside [0, lim] is left unchanged
+// path / parent (token trees, nc = 1, P = nodes): commit the accepted path's nodes as rows 0..k
 hipError_t launch_slice(const hci_layer* L, const hci_state* S, const hci_block* blk,
-                        int nb, int nc, int P, int lim, const int32_t* n_acc, const int32_t* best, hipStream_t st);
+                        int nb, int nc, int P, int lim, const int32_t* n_acc, const int32_t* best, hipStream_t st,
+                        const int32_t* path = nullptr, const int32_t* parent = nullptr);
+hipError_t launch_accept_tree(int mode, int nb, int n, int V, float temperature, const int32_t* parent,
+                              const int32_t* tokens, const float* zt, const float* zd, const double* u, int32_t* n_acc,
+                              int32_t* path, int32_t* next, double* margin, uint32_t* status, hipStream_t st);
 hipError_t launch_kv_copy(const hci_layer* L, const hci_state* S, int b, int row0, int nrows,
                           const void* k_rows, const void* v_rows, void* k_out, void* v_out,
                           bool write, hipStream_t st);

@@ -36,9 +36,31 @@ __device__ __forceinline__ uint32_t slice_target(const int32_t* n_acc, const int
     return bad;
 }
 
+// Token trees: whether the accepted path of sequence b (path [nb][n], entries 0..k) starts at
+// the anchor and follows the tree (path[i] is a child of path[i-1], so the indices ascend).
+// Threads i <= k check one step each; the answer is the same on every thread of the workgroup.
+__device__ __forceinline__ bool tree_path_ok(const int32_t* __restrict__ path, const int32_t* __restrict__ parent,
+                                             int n, int b, int k) {
+    bool ok = true;
+    for (int i = threadIdx.x; i <= k; i += blockDim.x) {
+        const int v = path[(size_t)b * n + i];
+        if (i == 0) {
+            ok = ok && v == 0;
+        } else {
+            const int prev = path[(size_t)b * n + i - 1];
+            ok = ok && v > prev && v < n && parent[(size_t)b * n + v] == prev;
+        }
+    }
+    return __syncthreads_or(!ok) == 0;
+}
+
+// block row r of the committed rows: r itself (a chain of candidate positions) or the r-th node
+// of the accepted path (a token tree)
+__device__ __forceinline__ int row_of(const int32_t* rmap, int r) { return rmap ? rmap[r] : r; }
+
 template <int ACT>
 __device__ void window_update(typename Act<ACT>::T* win, const typename Act<ACT>::T* blk_rows,
-                              int W, int d, int k, int ch0, float (*stage)[kSliceCG])
+                              int W, int d, int k, int ch0, float (*stage)[kSliceCG], const int32_t* rmap)
 {
     // new[r] = concat(old[0..W), rows[0..k])[k+1+r] for r < W.  Rows are
     // processed in ascending chunks; chunk [r0, r0+128) reads old rows at or
@@ -51,7 +73,7 @@ __device__ void window_update(typename Act<ACT>::T* win, const typename Act<ACT>
             const int m = k + 1 + r;
             float v = 0.f;
             if (ch < d) v = (m < W) ? Act<ACT>::load(win, (size_t)m * d + ch)
-                                    : Act<ACT>::load(blk_rows, (size_t)(m - W) * d + ch);
+                                    : Act<ACT>::load(blk_rows, (size_t)row_of(rmap, m - W) * d + ch);
             stage[r - r0][cl] = v;
         }
         __syncthreads();
@@ -69,25 +91,31 @@ __global__ __launch_bounds__(256) void k_slice(
     const float* __restrict__ f, const float* __restrict__ s,
     const typename Act<ACT>::T* __restrict__ kb, const typename Act<ACT>::T* __restrict__ vb,
     const int32_t* __restrict__ n_acc, const int32_t* __restrict__ best,
+    const int32_t* __restrict__ path, const int32_t* __restrict__ parent,
     int d, int Ts, int To, int N, int H, int DH, int kv_cap, int nc, int gamma, int lim)
 {
     __shared__ float stage[kSliceWinMax][kSliceCG];
     const int b = blockIdx.z, role = blockIdx.y;
     const int P = gamma + 1;
     int cstar, k, L;
-    if (slice_target(n_acc, best, kv_len, b, nc, gamma, lim, cstar, k, L) != 0u) return;   // reported by k_slice_len
+    // reported by the length kernel; the path check is workgroup-wide (every thread takes part)
+    const bool bad = slice_target(n_acc, best, kv_len, b, nc, gamma, lim, cstar, k, L) != 0u;
+    if (path != nullptr && !tree_path_ok(path, parent, P, b, bad ? -1 : k)) return;
+    if (bad) return;
     const size_t blk = (size_t)b * nc + cstar;
+    const int32_t* rmap = path ? path + (size_t)b * P : nullptr;     // a tree: nc = 1, P = its nodes
 
     if (role == 0) {
         const int ch0 = blockIdx.x * kSliceCG;
         if (ch0 >= d) return;
         if (Ts > 1)
-            window_update<ACT>(short_win + (size_t)b * (Ts - 1) * d, x + blk * P * d, Ts - 1, d, k, ch0, stage);
+            window_update<ACT>(short_win + (size_t)b * (Ts - 1) * d, x + blk * P * d, Ts - 1, d, k, ch0, stage, rmap);
         if (To > 1)
-            window_update<HCI_F32>(outer_win + (size_t)b * (To - 1) * d, f + blk * P * d, To - 1, d, k, ch0, stage);
+            window_update<HCI_F32>(outer_win + (size_t)b * (To - 1) * d, f + blk * P * d, To - 1, d, k, ch0, stage,
+                                   rmap);
     } else if (role == 1) {
         const size_t n = (size_t)d * N;
-        const float* src = s + (blk * P + k) * n;
+        const float* src = s + (blk * P + row_of(rmap, k)) * n;
         float* dst = iir + (size_t)b * n;
         for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
             dst[e] = src[e];
@@ -101,7 +129,7 @@ __global__ __launch_bounds__(256) void k_slice(
             const int dd = (int)(e % DH);
             const int row = L + i;               // < lim + gamma + 1 <= kv_cap (host check)
             if (row >= kv_cap) continue;
-            const size_t src = ((blk * P + i) * H + h) * DH + dd;
+            const size_t src = ((blk * P + row_of(rmap, i)) * H + h) * DH + dd;
             const size_t base = ((size_t)b * H + h) * slab;
             kc[base + k_elem(row, dd, DH)] = kb[src];
             vc[base + v_elem(row, dd, DH)] = vb[src];
@@ -124,8 +152,27 @@ __global__ void k_slice_len(int32_t* __restrict__ kv_len, const int32_t* __restr
     kv_len[b] = L + k + 1;
 }
 
+// kv_len += k + 1 for a token tree, after the path check (one 64-thread workgroup per sequence)
+__global__ __launch_bounds__(64) void k_slice_len_tree(int32_t* __restrict__ kv_len, const int32_t* __restrict__ n_acc,
+                                                       const int32_t* __restrict__ path,
+                                                       const int32_t* __restrict__ parent, uint32_t* __restrict__ status,
+                                                       int n, int lim)
+{
+    const int b = blockIdx.x;
+    int cstar, k, L;
+    uint32_t bad = slice_target(n_acc, nullptr, kv_len, b, 1, n - 1, lim, cstar, k, L);
+    if (!tree_path_ok(path, parent, n, b, bad ? -1 : k)) bad |= HCI_DS_TREE;
+    if (threadIdx.x != 0) return;
+    if (bad != 0u) {
+        report(status, b, bad);
+        return;
+    }
+    kv_len[b] = L + k + 1;
+}
+
 hipError_t launch_slice(const hci_layer* L, const hci_state* S, const hci_block* blk,
-                        int nb, int nc, int P, int lim, const int32_t* n_acc, const int32_t* best, hipStream_t st)
+                        int nb, int nc, int P, int lim, const int32_t* n_acc, const int32_t* best, hipStream_t st,
+                        const int32_t* path, const int32_t* parent)
 {
     const int gamma = P - 1;
     const int win_blocks = (L->d + kSliceCG - 1) / kSliceCG;
@@ -134,19 +181,23 @@ hipError_t launch_slice(const hci_layer* L, const hci_state* S, const hci_block*
         hipLaunchKernelGGL(k_slice<HCI_BF16>, grid, block, 0, st,
             (uint16_t*)S->short_win, S->outer_win, S->iir, (uint16_t*)S->k_cache, (uint16_t*)S->v_cache,
             S->kv_len, (const uint16_t*)blk->x, blk->f, blk->s, (const uint16_t*)blk->k,
-            (const uint16_t*)blk->v, n_acc, best, L->d, L->taps_short, L->taps_outer, L->poles,
+            (const uint16_t*)blk->v, n_acc, best, path, parent, L->d, L->taps_short, L->taps_outer, L->poles,
             L->heads, L->head_dim, S->kv_cap, nc, gamma, lim);
     } else {
         hipLaunchKernelGGL(k_slice<HCI_F32>, grid, block, 0, st,
             (float*)S->short_win, S->outer_win, S->iir, (float*)S->k_cache, (float*)S->v_cache,
             S->kv_len, (const float*)blk->x, blk->f, blk->s, (const float*)blk->k,
-            (const float*)blk->v, n_acc, best, L->d, L->taps_short, L->taps_outer, L->poles,
+            (const float*)blk->v, n_acc, best, path, parent, L->d, L->taps_short, L->taps_outer, L->poles,
             L->heads, L->head_dim, S->kv_cap, nc, gamma, lim);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_slice_len, dim3((nb + 63) / 64), dim3(64), 0, st,
-                       S->kv_len, n_acc, best, S->status, nb, nc, gamma, lim);
+    if (path)
+        hipLaunchKernelGGL(k_slice_len_tree, dim3(nb), dim3(64), 0, st, S->kv_len, n_acc, path, parent, S->status, P,
+                           lim);
+    else
+        hipLaunchKernelGGL(k_slice_len, dim3((nb + 63) / 64), dim3(64), 0, st,
+                           S->kv_len, n_acc, best, S->status, nb, nc, gamma, lim);
     return hipGetLastError();
 }
 

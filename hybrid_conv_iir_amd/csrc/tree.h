@@ -1,0 +1,247 @@
+// Token trees: the ancestor table shared by the tree kernels, and the
+// conv/recurrent half of a tree block forward (every node's short FIR, outer
+// FIR and modal IIR over its own root-to-node history).
+//
+// A tree of n <= 64 nodes per sequence: node 0 is the anchor, node m > 0 has a
+// parent p(m) < m.  Node m stands for the positions along the path root -> m
+// (EvSpark digest, Interpretation: several candidate blocks per step; ReaDy
+// summary, section 5: tree verification with recovery of recurrent state), so
+// its FIR windows read its ancestors, newest first, and then the committed
+// window, and its IIR state starts from its parent's state.
+//
+// One workgroup = 16 channels of one sequence (the chain kernel's channel
+// groups).  Every per-output sum is taken in the order the chain kernel
+// (conv_iir_body.h) uses -- short FIR taps ascending; the outer FIR as
+// kFirChunks tap chunks summed in ascending tap order and added in chunk
+// order; s = fma(lambda, s_parent, beta * g); y per four-pole group, then the
+// same lane butterfly -- so a node's f, s and y carry the same bits as the
+// chain forward over its path.
+#pragma once
+
+#include "conv_iir_body.h"
+
+namespace hci {
+
+constexpr int kTreeMax = 64;       // nodes per tree (the attention path's query limit)
+constexpr int kTreePoles = 16;     // poles per channel on the tree path
+
+// LDS of the ancestor table: parents [64] bytes, depths [64] bytes, ancestors [64][64] bytes
+constexpr size_t kTreeAncBytes = 2 * kTreeMax + (size_t)kTreeMax * kTreeMax;
+
+struct TreeAnc {
+    uint8_t* par;     // [n] parent (node 0: 0)
+    uint8_t* depth;   // [n]
+    uint8_t* anc;     // [n][64]: anc[m][j] = the node j steps above m, j <= depth[m]
+};
+
+__device__ __forceinline__ TreeAnc tree_anc_lds(void* base) {
+    uint8_t* p = (uint8_t*)base;
+    return TreeAnc{p, p + kTreeMax, p + 2 * kTreeMax};
+}
+
+// Whether parent entry m is valid: parent[0] == -1, 0 <= parent[m] < m for m > 0.
+__device__ __forceinline__ bool tree_parent_ok(int m, int p) { return m == 0 ? p == -1 : (p >= 0 && p < m); }
+
+// Builds the ancestor table of one tree (threads 0..n-1 each walk their own node; every parent
+// precedes its child, so a walk ends at node 0 within m steps).  An invalid parent entry is read
+// as m - 1 (the tree's outputs are then those of that reading; callers report HCI_DS_TREE).
+// Returns whether every entry was valid (the same on every thread).  Ends with a barrier.
+__device__ __forceinline__ bool tree_build(const int32_t* __restrict__ parent, int n, const TreeAnc& t,
+                                           int* flag) {
+    const int tid = threadIdx.x;
+    if (tid == 0) *flag = 1;
+    __syncthreads();
+    if (tid < n) {
+        const int p = parent[tid];
+        const bool ok = tree_parent_ok(tid, p);
+        if (!ok) *flag = 0;                          // every writer stores the same value
+        t.par[tid] = (uint8_t)(tid == 0 ? 0 : (ok ? p : tid - 1));
+    }
+    __syncthreads();
+    if (tid < n) {
+        uint8_t* row = t.anc + tid * kTreeMax;
+        int cur = tid, j = 0;
+        row[0] = (uint8_t)tid;
+        while (cur != 0) {
+            cur = t.par[cur];
+            row[++j] = (uint8_t)cur;
+        }
+        t.depth[tid] = (uint8_t)j;
+    }
+    __syncthreads();
+    return *flag != 0;
+}
+
+// LDS floats of the tree conv role (after the ancestor table, 16-byte aligned): short window +
+// x rows, outer window + f rows, chunk sums of g, outer taps, short taps, IIR states of every
+// node.
+__host__ __device__ inline size_t tree_conv_lds_bytes(int Ts, int To, int n) {
+    const size_t floats = (size_t)((Ts - 1 + n) + (To - 1 + n) + kFirChunks * n + To + Ts) * kCG +
+                          (size_t)n * kCG * kTreePoles;
+    return (kTreeAncBytes + 16 + 15) / 16 * 16 + floats * sizeof(float);
+}
+
+// One workgroup: channel group cgi (16 channels) of sequence b; the tree's n nodes are the rows
+// of x / f / s / y.  Returns the HCI_DS_* bits it found (HCI_DS_TREE), the same on every thread.
+template <int ACT>
+__device__ __forceinline__ uint32_t tree_conv_block(
+    const float* __restrict__ w_short, const float* __restrict__ w_outer,
+    const float* __restrict__ lam, const float* __restrict__ beta, const float* __restrict__ cc,
+    const typename Act<ACT>::T* __restrict__ short_win, const float* __restrict__ outer_win,
+    const float* __restrict__ iir, const typename Act<ACT>::T* __restrict__ x, const int32_t* __restrict__ parent,
+    float* __restrict__ f_out, float* __restrict__ s_out, typename Act<ACT>::T* __restrict__ y_out,
+    int d, int Ts, int To, int N, int n, int cgi, int b, void* lds_raw)
+{
+    const int W = To - 1, Ws = Ts - 1;
+    const TreeAnc t = tree_anc_lds(lds_raw);
+    int* flag = (int*)((char*)lds_raw + kTreeAncBytes);
+    float* xs = (float*)((char*)lds_raw + (kTreeAncBytes + 16 + 15) / 16 * 16);   // [Ws + n][kCG]
+    float* fb = xs + (size_t)(Ws + n) * kCG;          // [W + n][kCG]: outer window rows, then f rows
+    float* gl = fb + (size_t)(W + n) * kCG;           // [kFirChunks][n][kCG]
+    float* wl = gl + (size_t)kFirChunks * n * kCG;    // [To][kCG]
+    float* ws = wl + (size_t)To * kCG;                // [Ts][kCG]
+    float* sl = ws + (size_t)Ts * kCG;                // [n][kCG][kTreePoles]
+
+    const int ch0 = cgi * kCG;
+    const int tid = threadIdx.x;
+    const int cl = tid & (kCG - 1), row = tid >> 4;
+    const int ch = ch0 + cl;
+    const bool live = ch < d;
+    const typename Act<ACT>::T* sw = short_win + (size_t)b * Ws * d;
+    const float* ow = outer_win + (size_t)b * W * d;
+    const typename Act<ACT>::T* xb = x + (size_t)b * n * d;
+
+    const bool valid = tree_build(parent + (size_t)b * n, n, t, flag);
+
+    for (int r = row; r < W; r += kConvT / kCG) fb[r * kCG + cl] = live ? ow[(size_t)r * d + ch] : 0.f;
+    for (int r = row; r < To; r += kConvT / kCG) wl[r * kCG + cl] = live ? w_outer[(size_t)r * d + ch] : 0.f;
+    for (int r = row; r < n; r += kConvT / kCG) xs[(Ws + r) * kCG + cl] = live ? Act<ACT>::load(xb, (size_t)r * d + ch) : 0.f;
+    for (int r = row; r < Ws; r += kConvT / kCG) xs[r * kCG + cl] = live ? Act<ACT>::load(sw, (size_t)r * d + ch) : 0.f;
+    for (int r = row; r < Ts; r += kConvT / kCG) ws[r * kCG + cl] = live ? w_short[(size_t)r * d + ch] : 0.f;
+    __syncthreads();
+
+    // short FIR: f_m = sum_{j<Ts} w_short[j] * (input j positions before m on its path)
+    for (int m = row; m < n; m += kConvT / kCG) {
+        const int D = t.depth[m];
+        const uint8_t* am = t.anc + m * kTreeMax;
+        float acc = 0.f;
+        for (int j = 0; j < Ts; ++j) {
+            const int rw = j <= D ? Ws + am[j] : Ws - (j - D);
+            acc = fmaf(ws[j * kCG + cl], xs[rw * kCG + cl], acc);
+        }
+        if (live) f_out[((size_t)b * n + m) * d + ch] = acc;
+        fb[(W + m) * kCG + cl] = acc;
+    }
+    __syncthreads();
+
+    // outer FIR: chunk k of taps [k CS, min((k + 1) CS, To)) summed in ascending tap order
+    {
+        const int CS = (To + kFirChunks - 1) / kFirChunks;
+        for (int task = tid; task < n * kFirChunks * kCG; task += kConvT) {
+            const int tcl = task % kCG, k = (task / kCG) % kFirChunks, m = task / (kCG * kFirChunks);
+            const int D = t.depth[m];
+            const uint8_t* am = t.anc + m * kTreeMax;
+            const int j0 = k * CS, j1 = min(j0 + CS, To);
+            float acc = 0.f;
+            for (int j = j0; j < j1; ++j) {
+                const int rw = j <= D ? W + am[j] : W - (j - D);
+                acc = fmaf(wl[j * kCG + tcl], fb[rw * kCG + tcl], acc);
+            }
+            gl[((size_t)k * n + m) * kCG + tcl] = acc;
+        }
+    }
+    __syncthreads();
+
+    // IIR along the tree: task (channel tch, pole group tg) on G lanes; nodes in index order, so a
+    // node's parent state is already in LDS.  Waves past the first have no task (the scan over the
+    // nodes is sequential).
+    const int G = N <= 4 ? 1 : N <= 8 ? 2 : 4;
+    if (tid < kCG * G) {
+        const int tg = tid % G, tch = tid / G;
+        const int chn = ch0 + tch;
+        const bool scan = chn < d;
+        float lm[4], bt[4], cv[4], s0[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int pn = 4 * tg + q;
+            const bool ok = scan && pn < N;
+            const size_t o = (size_t)chn * N + pn;
+            lm[q] = ok ? lam[o] : 0.f;
+            bt[q] = ok ? beta[o] : 0.f;
+            cv[q] = ok ? cc[o] : 0.f;
+            s0[q] = ok ? iir[(size_t)b * d * N + o] : 0.f;
+        }
+        float* mys = sl + (size_t)tch * kTreePoles + 4 * tg;          // + m * kCG * kTreePoles
+        for (int m = 0; m < n; ++m) {
+            float g = gl[(size_t)m * kCG + tch];
+#pragma unroll
+            for (int k = 1; k < kFirChunks; ++k) g += gl[((size_t)k * n + m) * kCG + tch];
+            g = scan ? g : 0.f;
+            float st[4];
+            if (m == 0) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) st[q] = s0[q];
+            } else {
+                const float4 sp = *(const float4*)(mys + (size_t)t.par[m] * kCG * kTreePoles);
+                st[0] = sp.x; st[1] = sp.y; st[2] = sp.z; st[3] = sp.w;
+            }
+            float py = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                st[q] = fmaf(lm[q], st[q], bt[q] * g);
+                py = fmaf(cv[q], st[q], py);
+            }
+            *(float4*)(mys + (size_t)m * kCG * kTreePoles) = make_float4(st[0], st[1], st[2], st[3]);
+            if (scan) {
+                float* so = s_out + (((size_t)b * n + m) * d + chn) * N + 4 * tg;
+                if ((N & 3) == 0) {
+                    *(float4*)so = make_float4(st[0], st[1], st[2], st[3]);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (4 * tg + q < N) so[q] = st[q];
+                }
+            }
+            py = group_sum(py, G);
+            if (scan && tg == 0) Act<ACT>::store(y_out, ((size_t)b * n + m) * d + chn, py);
+        }
+    }
+    return valid ? 0u : HCI_DS_TREE;
+}
+
+// Ancestor sets of every node as bit masks (bit j of mask[m]: node j is m or one of its
+// ancestors), by pointer doubling on one wave: lane m starts from {m, p(m)} and jumps to its
+// ancestor 2^r steps up in round r.  Invalid parent entries are read as m - 1.  Called by
+// every wave of the workgroup (the first does the work); ends with a barrier.
+__device__ __forceinline__ void tree_masks(const int32_t* __restrict__ parent, int n, uint64_t* mask,
+                                           uint8_t* jump) {
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+        const int m = tid;
+        int p = 0;
+        if (m < n) {
+            const int v = parent[m];
+            p = m == 0 ? 0 : (tree_parent_ok(m, v) ? v : m - 1);
+        }
+        uint64_t mk = m < n ? ((1ull << m) | (1ull << p)) : 0ull;
+        mask[m] = mk;
+        jump[m] = (uint8_t)p;
+        for (int r = 0; r < 6; ++r) {                 // 2^6 = 64 >= any depth
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int jp = jump[m];
+            const uint64_t add = mask[jp];
+            const int jj = jump[jp];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            mk |= add;
+            mask[m] = mk;
+            jump[m] = (uint8_t)jj;
+        }
+    }
+    __syncthreads();
+}
+
+}  // namespace hci

@@ -21,6 +21,9 @@ struct FinishArgs {
     const void *q, *kb, *vb; void* o;
     int nb, H, DH, nq, P, kv_lim, resident, rg_count;
     float scale_log2;
+    // token trees (nc = 1, P = nodes): parent [nb][P], or nullptr for chains of candidate blocks
+    const int32_t* parent;
+    uint32_t* status;                  // HCI_DS_* per sequence (may be nullptr)
 };
 
 // LDS row stride (bytes) of the combine role's block K and V rows: Dh activations and 16
@@ -29,9 +32,12 @@ __host__ __device__ inline int combine_row_bytes(int DH, int act_bytes) { return
 
 // dynamic LDS floats of the combine role: the candidate's block K and V rows (raw
 // activations, padded rows), then per row and state (four waves + the block part) O [Dh] and
-// (m, l), then 64 block weights per wave
+// (m, l), then 64 block weights per wave, then (token trees) 64 ancestor masks and 64 jump
+// entries
+constexpr int kCombTreeFloats = 64 * 2 + 32;      // 64 masks (8-byte aligned) + 64 jump bytes
 __host__ __device__ inline size_t combine_lds_floats(int P, int DH, int act_bytes, int RG) {
-    return (size_t)2 * P * combine_row_bytes(DH, act_bytes) / 4 + (size_t)(kCombW + 1) * RG * (DH + 2) + 64 * kCombW;
+    return (size_t)2 * P * combine_row_bytes(DH, act_bytes) / 4 + (size_t)(kCombW + 1) * RG * (DH + 2) + 64 * kCombW +
+           kCombTreeFloats;
 }
 
 // rows per combine workgroup for these sizes (1, 2, 4, 8 or 16)

@@ -124,6 +124,70 @@ class DeviceBlock:
         return self.ws
 
 
+class DeviceTree:
+    """A token tree of n nodes per sequence: parents, per-node inputs, retained intermediates and
+    outputs, plus the acceptance buffers of its walk."""
+
+    def __init__(self, layer: DeviceLayer, nb: int, n: int, vocab: int = 1, device: str = DEV):
+        cfg = layer.cfg
+        self.layer, self.nb, self.n, self.vocab = layer, nb, n, vocab
+        at = hci.act_torch_dtype(layer.act)
+        H, Dh, d = cfg.heads, cfg.head_dim, cfg.d
+        self.parent = torch.full((nb, n), -1, dtype=torch.int32, device=device)
+        self.x = torch.zeros((nb, n, d), dtype=at, device=device)
+        self.q = torch.zeros((nb, n, H, Dh), dtype=at, device=device)
+        self.k = torch.zeros_like(self.q)
+        self.v = torch.zeros_like(self.q)
+        self.f = torch.zeros((nb, n, d), dtype=torch.float32, device=device)
+        self.s = torch.zeros((nb, n, d, cfg.poles), dtype=torch.float32, device=device)
+        self.y = torch.zeros((nb, n, d), dtype=at, device=device)
+        self.o = torch.zeros((nb, n, H, Dh), dtype=at, device=device)
+        self.tokens = torch.zeros((nb, n), dtype=torch.int32, device=device)
+        self.zt = torch.zeros((nb, n, vocab), dtype=torch.float32, device=device)
+        self.zd = torch.zeros((nb, n, vocab), dtype=torch.float32, device=device)
+        self.u = torch.zeros((nb, n), dtype=torch.float64, device=device)
+        self.n_acc = torch.zeros(nb, dtype=torch.int32, device=device)
+        self.path = torch.zeros((nb, n), dtype=torch.int32, device=device)
+        self.next = torch.zeros(nb, dtype=torch.int32, device=device)
+        self.margin = torch.zeros(nb, dtype=torch.float64, device=device)
+        self.c = hci.make_tree(layer.act, self.parent, self.x, self.q, self.k, self.v, self.f, self.s, self.y, self.o)
+        self.ws = None
+
+    def set_inputs(self, parent, x, q, k, v) -> None:
+        for dst, src in ((self.parent, parent), (self.x, x), (self.q, q), (self.k, k), (self.v, v)):
+            dst.copy_(src if isinstance(src, torch.Tensor) else to_dev(np.ascontiguousarray(src)))
+
+    def set_accept_inputs(self, tokens, zt, zd=None, u=None) -> None:
+        self.tokens.copy_(to_dev(np.asarray(tokens, np.int32)))
+        self.zt.copy_(to_dev(np.asarray(zt, np.float32)))
+        if zd is not None:
+            self.zd.copy_(to_dev(np.asarray(zd, np.float32)))
+        if u is not None:
+            self.u.copy_(to_dev(np.asarray(u, np.float64)))
+
+    def ensure_workspace(self, max_kv_len: int) -> torch.Tensor:
+        need = hci.verify_workspace_bytes(self.layer.c, self.nb, 1, self.n - 1, max_kv_len)
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.x.device)
+        return self.ws
+
+
+def verify_tree(layer: DeviceLayer, state: "DeviceState", tree: DeviceTree, max_kv_len: int, stream=None) -> None:
+    ws = tree.ensure_workspace(max_kv_len)
+    hci.verify_tree(layer.c, state.c, tree.c, tree.nb, tree.n, max_kv_len, ws, stream)
+
+
+def accept_tree(tree: DeviceTree, mode: int, temperature: float = 1.0, stream=None, status=None) -> None:
+    sample = mode != hci.GREEDY
+    hci.accept_tree(mode, tree.nb, tree.n, tree.vocab, temperature, tree.parent, tree.tokens, tree.zt,
+                    tree.zd if sample else None, tree.u if sample else None, tree.n_acc, tree.path, tree.next,
+                    tree.margin, status, stream)
+
+
+def slice_tree(layer: DeviceLayer, state: "DeviceState", tree: DeviceTree, max_kv_len: int, stream=None) -> None:
+    hci.slice_tree(layer.c, state.c, tree.c, tree.nb, tree.n, max_kv_len, tree.n_acc, tree.path, stream)
+
+
 class DeviceAccept:
     """Acceptance inputs and outputs for nb x nc blocks."""
 

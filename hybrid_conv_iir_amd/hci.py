@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libhci.so")
 
 OK, EINVAL, ECAPACITY, EUNSUPPORTED, EDEVICE, EWORKSPACE = 0, -1, -2, -3, -4, -5
 # device status bits (include/hci.h, HCI_DS_*)
-DS_NONFINITE, DS_K_RANGE, DS_CAND_RANGE, DS_KV_LEN, DS_DRAFT_ID = 0x1, 0x2, 0x4, 0x8, 0x10
+DS_NONFINITE, DS_K_RANGE, DS_CAND_RANGE, DS_KV_LEN, DS_DRAFT_ID, DS_TREE = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
 F32, BF16 = 0, 1
 GREEDY, SAMPLE, SAMPLE_RECURSIVE = 0, 1, 2
 KV_TILE = 32
@@ -56,6 +56,11 @@ class State(ctypes.Structure):
 
 class Block(ctypes.Structure):
     _fields_ = [("x", _p), ("q", _p), ("k", _p), ("v", _p), ("f", _p), ("s", _p), ("y", _p), ("o", _p)]
+
+
+class Tree(ctypes.Structure):
+    _fields_ = [("parent", _p), ("x", _p), ("q", _p), ("k", _p), ("v", _p), ("f", _p), ("s", _p), ("y", _p),
+                ("o", _p)]
 
 
 MIX_FIR, MIX_IIR, MIX_ATTN = 0, 1, 2
@@ -111,6 +116,11 @@ EXPORTS = {
     "hci_accept": (_i, [_i, _i, _i, _i, _i, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "hci_slice_state": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), ctypes.POINTER(Block),
                              _i, _i, _i, _i, _p, _p, _p]),
+    "hci_verify_tree": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), ctypes.POINTER(Tree), _i, _i, _i, _p, _sz,
+                             _p]),
+    "hci_accept_tree": (_i, [_i, _i, _i, _i, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "hci_slice_tree": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), ctypes.POINTER(Tree), _i, _i, _i, _p, _p,
+                            _p]),
     "hci_prefill_workspace_bytes": (_sz, [ctypes.POINTER(Layer), _i, _i, _i]),
     "hci_prefill": (_i, [ctypes.POINTER(Layer), ctypes.POINTER(State), _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p]),
     "hci_linear_packed_elems": (_sz, [_i, _i]),
@@ -263,6 +273,38 @@ def slice_state(layer: Layer, state: State, block: Block, nb: int, nc: int, gamm
     _check(_lib.hci_slice_state(ctypes.byref(layer), ctypes.byref(state), ctypes.byref(block), nb, nc, gamma,
                                 max_kv_len, _ptr(n_accepted, torch.int32, "n_accepted"),
                                 _ptr(best_cand, torch.int32, "best_cand"), _stream(stream)), "hci_slice_state")
+
+
+def make_tree(act, parent, x, q, k, v, f, s, y, o) -> Tree:
+    at = act_torch_dtype(act)
+    return Tree(_ptr(parent, torch.int32, "parent"), _ptr(x, at, "x"), _ptr(q, at, "q"), _ptr(k, at, "k"),
+                _ptr(v, at, "v"), _ptr(f, torch.float32, "f"), _ptr(s, torch.float32, "s"), _ptr(y, at, "y"),
+                _ptr(o, at, "o"))
+
+
+def verify_tree(layer: Layer, state: State, tree: Tree, nb: int, n: int, max_kv_len: int, ws, stream=None) -> None:
+    _check(_lib.hci_verify_tree(ctypes.byref(layer), ctypes.byref(state), ctypes.byref(tree), nb, n, max_kv_len,
+                                _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
+           "hci_verify_tree")
+
+
+def accept_tree(mode: int, nb: int, n: int, vocab: int, temperature: float, parent, tokens, target_logits,
+                draft_logits, uniforms, n_accepted, path, next_token, margin=None, status=None, stream=None) -> None:
+    _check(_lib.hci_accept_tree(mode, nb, n, vocab, float(temperature), _ptr(parent, torch.int32, "parent"),
+                                _ptr(tokens, torch.int32, "tokens"),
+                                _ptr(target_logits, torch.float32, "target_logits"),
+                                _ptr(draft_logits, torch.float32, "draft_logits"),
+                                _ptr(uniforms, torch.float64, "uniforms"),
+                                _ptr(n_accepted, torch.int32, "n_accepted"), _ptr(path, torch.int32, "path"),
+                                _ptr(next_token, torch.int32, "next_token"), _ptr(margin, torch.float64, "margin"),
+                                _ptr(status, torch.int32, "status"), _stream(stream)), "hci_accept_tree")
+
+
+def slice_tree(layer: Layer, state: State, tree: Tree, nb: int, n: int, max_kv_len: int, n_accepted, path,
+               stream=None) -> None:
+    _check(_lib.hci_slice_tree(ctypes.byref(layer), ctypes.byref(state), ctypes.byref(tree), nb, n, max_kv_len,
+                               _ptr(n_accepted, torch.int32, "n_accepted"), _ptr(path, torch.int32, "path"),
+                               _stream(stream)), "hci_slice_tree")
 
 
 def prefill_workspace_bytes(layer: Layer, nb: int, T: int, want_y: bool) -> int:

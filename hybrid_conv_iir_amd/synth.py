@@ -261,6 +261,13 @@ def gumbel_drafts(cfg: Config, draft_logits: np.ndarray, rnd: int = 0, seed: int
     return np.argmax(draft_logits.astype(np.float64) / cfg.temperature + gum, axis=-1).astype(np.int32)
 
 
+def prefix_row(cfg: Config, rnd: int, seed: int, kind: int, b: int, prefix, scale: float = math.sqrt(2.0)):
+    """A seeded N(0, scale^2) logit row keyed by (kind, sequence, drafted prefix): kind 0 = the target's
+    row after the prefix, kind 1 = the drafter's."""
+    g = np.random.default_rng([cfg.cfg_id, seed, rnd, kind, b, len(prefix)] + [int(t) for t in prefix])
+    return (g.standard_normal(cfg.vocab) * scale).astype(np.float32)
+
+
 def prefix_keyed_round(cfg: Config, rnd: int = 0, seed: int = 0, scale: float = math.sqrt(2.0)):
     """Sampling inputs whose logit rows are a seeded function of (sequence, prefix).
 
@@ -274,8 +281,7 @@ def prefix_keyed_round(cfg: Config, rnd: int = 0, seed: int = 0, scale: float = 
     nb, nc, gam, V = cfg.nb, cfg.nc, cfg.gamma, cfg.vocab
 
     def row(kind, b, prefix):
-        g = np.random.default_rng([cfg.cfg_id, seed, rnd, kind, b, len(prefix)] + [int(t) for t in prefix])
-        return (g.standard_normal(V) * scale).astype(np.float32)
+        return prefix_row(cfg, rnd, seed, kind, b, prefix, scale)
 
     noise = np.random.default_rng([cfg.cfg_id, seed, rnd, 7]).random((nb, nc, max(gam, 1), V))
     noise = np.clip(noise, 1e-300, 1.0 - 1e-16)
@@ -353,6 +359,85 @@ def round_inputs(cfg: Config, anchor: np.ndarray, rnd: int = 0, seed: int = 0,
         lens = None
     return {"drafts": drafts, "target_logits": zt, "draft_logits": zd, "uniforms": u,
             "tokens": block_tokens(anchor, drafts), "planted_len": lens}
+
+
+# ---------------------------------------------------------------- token trees
+
+def trie_of(tokens: np.ndarray):
+    """The token tree of several candidate blocks that share the anchor: one node per distinct
+    prefix.  tokens [nc][P] (position 0 = the anchor).  Nodes are numbered in order of first
+    appearance (candidate-major, position-minor), so every parent precedes its children.
+    Returns (parent [n] int32, node_token [n] int32, node_of [nc][P] int32)."""
+    nc, P = tokens.shape
+    index = {(): 0}
+    parent, node_tok = [-1], [int(tokens[0, 0])]
+    node_of = np.zeros((nc, P), np.int32)
+    for c in range(nc):
+        pre = ()
+        for i in range(1, P):
+            pre = pre + (int(tokens[c, i]),)
+            if pre not in index:
+                index[pre] = len(parent)
+                parent.append(index[pre[:-1]])
+                node_tok.append(int(tokens[c, i]))
+            node_of[c, i] = index[pre]
+    return np.array(parent, np.int32), np.array(node_tok, np.int32), node_of
+
+
+def tree_round(cfg: Config, n: Optional[int] = None, rnd: int = 0, seed: int = 0, scale: float = math.sqrt(2.0)):
+    """One round of token trees, one per sequence: the trie of cfg.nc candidate blocks whose drafts are
+    Gumbel-max draws from prefix-keyed draft rows (``prefix_row``), padded to ``n`` nodes (default: the
+    largest trie) with extra leaves whose tokens are drawn from their parent's draft row.
+
+    Returns a dict: parent [nb][n], tokens [nb][n] (node 0 = the anchor), target_logits [nb][n][V]
+    (row m: the target's row after node m's prefix), draft_logits [nb][n][V] (row m: the row node m's
+    token was drawn from; row 0 zero), uniforms [nb][n] (entry 0 = r*), n, and the tries' sizes."""
+    cand_zt, cand_zd, drafts, _ = prefix_keyed_round(cfg, rnd, seed, scale)
+    anchor = anchors(cfg, rnd, seed)
+    toks = block_tokens(anchor, drafts)
+    tries = [trie_of(toks[b]) for b in range(cfg.nb)]
+    sizes = [len(t[0]) for t in tries]
+    n = max(sizes) if n is None else n
+    assert n >= max(sizes)
+    g = np.random.default_rng([cfg.cfg_id, seed, rnd, 91])
+    parent = np.zeros((cfg.nb, n), np.int32)
+    tokens = np.zeros((cfg.nb, n), np.int32)
+    for b in range(cfg.nb):
+        par, tok, _ = tries[b]
+        par, tok = list(par), list(tok)
+        while len(par) < n:                                   # padding leaves under random nodes
+            par.append(int(g.integers(0, len(par))))
+            tok.append(-1)
+        parent[b], tokens[b] = par, tok
+    zt = np.zeros((cfg.nb, n, cfg.vocab), np.float32)
+    zd = np.zeros((cfg.nb, n, cfg.vocab), np.float32)
+    for b in range(cfg.nb):
+        pre = {0: ()}
+        for m in range(1, n):
+            p = int(parent[b, m])
+            zd[b, m] = prefix_row(cfg, rnd, seed, 1, b, pre[p], scale)
+            if tokens[b, m] < 0:                              # a padding leaf's token: a draw from its row
+                gum = -np.log(-np.log(np.clip(g.random(cfg.vocab), 1e-300, 1.0 - 1e-16)))
+                tokens[b, m] = int(np.argmax(zd[b, m].astype(np.float64) / cfg.temperature + gum))
+            pre[m] = pre[p] + (int(tokens[b, m]),)
+        for m in range(n):
+            zt[b, m] = prefix_row(cfg, rnd, seed, 0, b, pre[m], scale)
+    u = np.random.default_rng([cfg.cfg_id, seed, rnd, 92]).random((cfg.nb, n))
+    return {"parent": parent, "tokens": tokens, "target_logits": zt, "draft_logits": zd, "uniforms": u, "n": n,
+            "trie_sizes": sizes, "candidate_rows": (cand_zt, cand_zd)}
+
+
+def random_tree(n: int, kind: str, rng: np.random.Generator) -> np.ndarray:
+    """Parent array of a tree of n nodes: "chain", "star", "random" (each parent uniform over the
+    earlier nodes) or "broom" (a chain of n // 2 nodes, the rest leaves of its last node)."""
+    if kind == "chain":
+        return np.array([-1] + list(range(n - 1)), np.int32)
+    if kind == "star":
+        return np.array([-1] + [0] * (n - 1), np.int32)
+    if kind == "broom":
+        h = max(1, n // 2)
+        return np.array([-1] + list(range(h - 1)) + [h - 1] * (n - h), np.int32)
+    return np.array([-1] + [int(rng.integers(0, m)) for m in range(1, n)], np.int32)
 
 
 # ---------------------------------------------------------------- full layer stacks

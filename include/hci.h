@@ -90,6 +90,11 @@ int hci_version(void);
                                       unchanged. */
 #define HCI_DS_DRAFT_ID      0x10u /* accept: a draft token id outside [0, V) (it counted as a
                                       mismatch / rejection, as documented; reported only). */
+#define HCI_DS_TREE          0x20u /* token trees: a parent entry breaks 0 <= parent[m] < m
+                                      (parent[0] = -1), or the path handed to slicing does not
+                                      follow the tree.  Verify reads such an entry as m - 1;
+                                      acceptance marks the sequence (n_accepted -1); slicing
+                                      leaves it unchanged. */
 
 /* Writes the names of the bits set in `bits` (a status word copied to the
  * host), separated by '|', into buf with the conventions of hci_status_string;
@@ -306,6 +311,85 @@ int hci_slice_state(const hci_layer* L, const hci_state* S, const hci_block* blk
                     int nb, int nc, int gamma, int max_kv_len,
                     const int32_t* n_accepted, const int32_t* best_cand,
                     hipStream_t stream);
+
+/* ------------------------------------------------------------- token trees */
+
+/* Several candidate blocks that share prefixes, verified as one token tree
+ * (EvSpark digest, Interpretation: C = 1/2/4 candidate blocks per step; ReaDy
+ * summary, section 5: tree verification with recovery of recurrent state).
+ * Per sequence a tree of n nodes: node 0 is the anchor, node m > 0 holds a
+ * drafted token and has a parent parent[b][m] < m (parent[b][0] = -1).  Node m
+ * stands for the positions along the path root -> m, so shared prefixes are
+ * computed once.  Arrays are per node, nodes in index order:
+ *   parent [nb][n] int32
+ *   x [nb][n][d] act; q, k, v [nb][n][H][Dh] act (16-byte aligned q)
+ *   f [nb][n][d] fp32, s [nb][n][d][N] fp32, y [nb][n][d] act, o [nb][n][H][Dh] act: OUT of verify
+ * parent, x, k, v, f and s must stay unchanged between hci_verify_tree and
+ * hci_slice_tree. */
+typedef struct hci_tree {
+    const int32_t* parent;
+    const void* x;
+    const void* q;
+    const void* k;
+    const void* v;
+    float* f;
+    float* s;
+    void* y;
+    void* o;
+} hci_tree;
+
+/* One block forward over every node of every tree from the committed state
+ * (only read).  Each output at node m equals the chain block forward
+ * (hci_verify_block) over the path root -> m at its last position: the FIR
+ * windows read m's ancestors, newest first, then the committed window; the IIR
+ * state starts from the parent's state; the query attends to the committed
+ * prefix and to the block keys of m's ancestors and m itself.  f, s and y are
+ * computed with the chain kernel's summation orders, so they carry the same
+ * bits as the chain forward over the path.
+ *   ws, ws_bytes  hci_verify_workspace_bytes(L, nb, 1, n - 1, max_kv_len) bytes.
+ * Limits: 1 <= n <= 64; N <= 16 poles.  Errors as hci_verify_block; an invalid
+ * parent entry is reported (HCI_DS_TREE in S->status) and read as m - 1. */
+int hci_verify_tree(const hci_layer* L, const hci_state* S, const hci_tree* tree,
+                    int nb, int n, int max_kv_len, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Acceptance over each sequence's tree, walking from the anchor:
+ *   HCI_GREEDY: at node m the argmax of target row m (ties -> lowest id) is
+ *     compared with m's children in index order; the first child holding it
+ *     becomes the current node, otherwise the argmax is the next token.
+ *   HCI_SAMPLE: m's children are tried in index order against the running
+ *     residual w / z of p = softmax(target row m / T) (w = p, z = 1): child c
+ *     with token t, drawn from q_c = softmax(draft row c / T), is kept iff
+ *     r_c * q_c(t) * z < w(t); a rejection sets w <- max(0, w - z q_c),
+ *     z <- sum(w).  A kept child becomes the current node; if all are
+ *     rejected the next token is drawn from w, at a node without children from
+ *     p (inverse CDF with r*, as hci_accept).  Lossless when every child's
+ *     token is an independent draw from its q_c (multi-step speculative
+ *     sampling with one draft distribution per child).
+ *   Inputs: parent [nb][n]; tokens [nb][n] int32 (entry 0 unused);
+ *     target_logits [nb][n][V] fp32 (row m: the token after node m);
+ *     draft_logits [nb][n][V] fp32 (row c: the distribution node c's token was
+ *     drawn from; row 0 unused; NULL in greedy mode); uniforms [nb][n] fp64:
+ *     r_c of node c, entry 0 = r* (NULL in greedy mode).
+ *   Outputs: n_accepted [nb] = depth k of the accepted node; path [nb][n] =
+ *     its nodes from the anchor (path[b][0] = 0, entries past k = -1);
+ *     next_token [nb]; margin [nb] fp64 or NULL (as hci_accept); status [nb]
+ *     or NULL (HCI_DS_NONFINITE and HCI_DS_TREE mark the sequence with
+ *     n_accepted = next_token = -1; HCI_DS_DRAFT_ID is reported only).
+ * Limits: 1 <= n <= 64, 1 <= V <= 65536, temperature > 0 when sampling. */
+int hci_accept_tree(int mode, int nb, int n, int vocab, float temperature, const int32_t* parent,
+                    const int32_t* tokens, const float* target_logits, const float* draft_logits,
+                    const double* uniforms, int32_t* n_accepted, int32_t* path, int32_t* next_token,
+                    double* margin, uint32_t* status, hipStream_t stream);
+
+/* Commit the accepted path of each sequence's tree: its nodes path[b][0..k]
+ * (k = n_accepted[b]) play the role of block rows 0..k in hci_slice_state
+ * (KV rows appended, windows <- their last rows, IIR <- s of the accepted
+ * node, kv_len += k + 1).  A sequence whose k is outside [0, n - 1], whose
+ * kv_len is outside [0, max_kv_len] or whose path does not start at node 0 and
+ * follow the tree is left unchanged (HCI_DS_K_RANGE / HCI_DS_KV_LEN /
+ * HCI_DS_TREE in S->status). */
+int hci_slice_tree(const hci_layer* L, const hci_state* S, const hci_tree* tree, int nb, int n, int max_kv_len,
+                   const int32_t* n_accepted, const int32_t* path, hipStream_t stream);
 
 /* ----------------------------------------------------------------- prefill */
 

@@ -58,3 +58,35 @@ def test_kv_prefix_cpu_shape_and_moments():
     assert tuple(k.shape) == (2, 1000, 128)
     kk = k.float().numpy()
     assert abs(kk.mean()) < 0.02 and abs(kk.std() - 1) < 0.02
+
+
+def test_trie_of_candidates():
+    """The trie of candidate blocks: one node per distinct prefix, parents before children, and every
+    candidate position maps to the node whose path spells that candidate's prefix."""
+    rng = np.random.default_rng(4)
+    for _ in range(50):
+        nc, P, V = int(rng.integers(1, 5)), int(rng.integers(1, 9)), int(rng.integers(1, 4))
+        toks = rng.integers(0, V, (nc, P)).astype(np.int32)
+        toks[:, 0] = toks[0, 0]                                    # the shared anchor
+        parent, node_tok, node_of = synth.trie_of(toks)
+        assert parent[0] == -1 and all(0 <= parent[m] < m for m in range(1, len(parent)))
+        prefixes = {tuple(toks[c, 1:i + 1]) for c in range(nc) for i in range(P)}
+        assert len(parent) == len(prefixes)
+        for c in range(nc):
+            for i in range(P):
+                m, spelled = int(node_of[c, i]), []
+                while m != 0:
+                    spelled.append(int(node_tok[m]))
+                    m = int(parent[m])
+                assert spelled[::-1] == list(toks[c, 1:i + 1])
+
+
+def test_tree_round_shapes_and_rows():
+    cfg = synth.scaled(synth.CONFIGS["multi4x4"], vocab=4)
+    tr = synth.tree_round(cfg)
+    n = tr["n"]
+    assert tr["parent"].shape == (cfg.nb, n) and tr["target_logits"].shape == (cfg.nb, n, cfg.vocab)
+    assert max(tr["trie_sizes"]) == n and min(tr["trie_sizes"]) < cfg.nc * cfg.gamma + 1
+    for b in range(cfg.nb):
+        assert tr["parent"][b, 0] == -1 and all(0 <= tr["parent"][b, m] < m for m in range(1, n))
+        assert ((tr["tokens"][b, 1:] >= 0) & (tr["tokens"][b, 1:] < cfg.vocab)).all()
