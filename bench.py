@@ -134,11 +134,12 @@ def cpu_baseline(cfg, case_np, heads, reps):
     """
     import numpy as np
     import oracle
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        cores = 1
+        blas_threads = 1
     layer = oracle.Layer.from_dict(case_np["params"])
     small, bn, ri = case_np["small"], case_np["blk"], case_np["ri"]
     b, c = 0, 0
@@ -174,6 +175,9 @@ def cpu_baseline(cfg, case_np, heads, reps):
         "value": round(cfg.nb * cfg.nc * cfg.P / est, 3),
         "unit": "verified block-positions/s",
         "cores": int(cores),
+        "blas_threads": int(blas_threads),
+        "threads_note": ("cores = host cores available to the process; the oracle's FIR, IIR, softmax and "
+                         "acceptance loops run on one thread, only its matrix products use the BLAS threads"),
         "kind": "oracle",
         "sample": (f"fp64 numpy oracle, verify->accept->slice of one block with attention over {len(heads)} of "
                    f"{cfg.heads} heads, {reps} repetitions (timed {measured:.1f} s"
@@ -463,6 +467,9 @@ def main():
     ap.add_argument("--linear-shape", default="13,4096,12288", help="M,K,N for --mode linear")
     ap.add_argument("--model", default="m4_long", help="layer stack for --mode model")
     ap.add_argument("--prompt", type=int, default=262144, help="prompt length for --mode prefill")
+    ap.add_argument("--replay-reps", type=int, default=3, help="repetitions of the replay-equivalent timing")
+    ap.add_argument("--accept-rounds", type=int, default=64,
+                    help="seeded rounds of hci_accept for the k histogram / survival curve (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run the known-size copy kernel once on this many MiB (byte-counter calibration)")
     args = ap.parse_args()
@@ -495,9 +502,64 @@ def main():
         return bench_model(args, hip)
     if args.mode == "draft":
         return bench_draft(args, hip)
+    return bench_verify(args, cfg, hip)
+
+
+MALL_BYTES = 256 << 20          # MI355X Infinity Cache; a prefix below this could be served from it
+
+
+def kv_sets_for(cfg) -> int:
+    """KV sets the timed steps rotate over: one when the workload's KV prefix is far larger than the
+    256 MB MALL, otherwise enough copies (at least 3) that together they exceed 1 GiB, so that no step
+    finds its prefix left in the MALL by the previous one."""
+    act = 2 if cfg.act == "bf16" else 4
+    kv = sum(2 * cfg.heads * L * cfg.head_dim * act for L in cfg.kv_lens)
+    if kv >= 4 * MALL_BYTES:
+        return 1
+    return int(min(16, max(3, -(-(1 << 30) // max(kv, 1)))))
+
+
+def acceptance_stats(cfg, rounds, hip):
+    """k histogram, survival curve and smallest decision margin of hci_accept over `rounds` seeded
+    rounds of this workload's synthetic logits and drafts (fresh inputs per round)."""
+    import numpy as np
+    import torch
+    from hybrid_conv_iir_amd import device as dv
+    from hybrid_conv_iir_amd import hci, synth
+    mode = hci.GREEDY if cfg.mode == "greedy" else hci.SAMPLE
+    acc = dv.DeviceAccept(cfg.nb, cfg.nc, cfg.gamma, cfg.vocab)
+    ks, margins = [], []
+    for r in range(1, rounds + 1):
+        ri = synth.round_inputs(cfg, synth.anchors(cfg, r), r)
+        acc.set_inputs(ri["target_logits"], ri["drafts"], ri["draft_logits"], ri["uniforms"])
+        dv.accept(acc, mode, cfg.temperature)
+        n_acc, best, marg = (dv.to_host(t) for t in (acc.n_acc, acc.best, acc.margin))
+        for b in range(cfg.nb):
+            ks.append(int(n_acc[b, int(best[b])]))
+        margins.append(float(np.min(marg)))
+    hist = np.bincount(np.asarray(ks), minlength=cfg.gamma + 1)[: cfg.gamma + 1]
+    n = len(ks)
+    return {"rounds": rounds, "blocks": n,
+            "k_histogram": [int(v) for v in hist],
+            "survival": [round(float(np.sum(np.asarray(ks) >= j)) / n, 4) for j in range(1, cfg.gamma + 1)],
+            "mean_accepted_drafts": round(float(np.mean(ks)), 3),
+            "min_decision_margin": float(np.min(margins)),
+            "margin_note": ("greedy: smallest top-1 logit gap of the rows read" if cfg.mode == "greedy" else
+                            "sampling: smallest relative distance of a ratio test or inverse-CDF draw from its "
+                            "threshold")}
+
+
+def bench_verify(args, cfg, hip):
+    """verify -> accept -> slice steps on inputs resident in HBM (the metric's workload)."""
+    import numpy as np
+    import torch
+    from hybrid_conv_iir_amd import device as dv
+    from hybrid_conv_iir_amd import hci, synth
     W, K = args.warmup, args.steps
     P = cfg.P
-    kv_cap = (cfg.max_kv_len + (W + 2 * K + 2) * P + 31) // 32 * 32
+    n_sets = kv_sets_for(cfg)
+    per_set = (W + 2 * K) // n_sets + 2
+    kv_cap = (cfg.max_kv_len + (per_set + 2) * P + 31) // 32 * 32
 
     # ---------------------------------------------------------------- inputs (resident before timing)
     params = synth.make_layer(cfg)
@@ -507,60 +569,69 @@ def main():
     ri = synth.round_inputs(cfg, anchor)
     bn = synth.gather_block(cfg, tables, ri["tokens"])
     lay = dv.DeviceLayer(cfg, params)
-    st = dv.DeviceState(lay, cfg.nb, kv_cap)
-    st.load_small(small)
     heads = list(range(cfg.heads if args.cpu_heads <= 0 else min(args.cpu_heads, cfg.heads)))
     kpre_host = vpre_host = None
-    for b in range(cfg.nb):
-        kp = synth.kv_prefix(cfg, b, "k", device="cuda")
-        vp = synth.kv_prefix(cfg, b, "v", device="cuda")
-        st.write_prefix(b, kp, vp)
-        if b == 0 and not args.no_cpu_baseline:
-            kpre_host, vpre_host = dv.to_host(kp[heads]), dv.to_host(vp[heads])
-        del kp, vp
-    st.kv_len.copy_(torch.tensor(cfg.kv_lens, dtype=torch.int32))
+    sets = []
+    for si in range(n_sets):
+        st = dv.DeviceState(lay, cfg.nb, kv_cap)
+        st.load_small(small)
+        for b in range(cfg.nb):
+            kp = synth.kv_prefix(cfg, b, "k", device="cuda")
+            vp = synth.kv_prefix(cfg, b, "v", device="cuda")
+            st.write_prefix(b, kp, vp)
+            if si == 0 and b == 0 and not args.no_cpu_baseline:
+                kpre_host, vpre_host = dv.to_host(kp[heads]), dv.to_host(vp[heads])
+            del kp, vp
+        st.kv_len.copy_(torch.tensor(cfg.kv_lens, dtype=torch.int32))
+        sets.append(st)
     blk = dv.DeviceBlock(lay, cfg.nb, cfg.nc, cfg.gamma)
     blk.set_inputs(bn["x"], bn["q"], bn["k"], bn["v"])
     acc = dv.DeviceAccept(cfg.nb, cfg.nc, cfg.gamma, cfg.vocab)
     acc.set_inputs(ri["target_logits"], ri["drafts"], ri["draft_logits"], ri["uniforms"])
     mode = hci.GREEDY if cfg.mode == "greedy" else hci.SAMPLE
-    bound = cfg.max_kv_len
-    blk.ensure_workspace(bound + (W + 2 * K + 1) * P)
+    bounds = [cfg.max_kv_len] * n_sets
+    blk.ensure_workspace(kv_cap - P)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
     # ---------------------------------------------------------------- HBM read ceiling (probe)
     sink = torch.empty(hci.probe_sink_words(), dtype=torch.float32, device="cuda")
     pe = _events(hip, 2)
-    hci.probe_read(st.k_cache, sink)
+    hci.probe_read(sets[0].k_cache, sink)
     probe_ms = []
     for _ in range(5):
         hip.hipEventRecord(pe[0], sp)
-        hci.probe_read(st.k_cache, sink)
+        hci.probe_read(sets[0].k_cache, sink)
         hip.hipEventRecord(pe[1], sp)
         hip.hipEventSynchronize(pe[1])
         probe_ms.append(_ms(hip, pe[0], pe[1]))
-    probe_gbs = st.k_cache.numel() * 2 / (min(probe_ms) * 1e-3) / 1e9
+    probe_gbs = sets[0].k_cache.numel() * 2 / (min(probe_ms) * 1e-3) / 1e9
 
     # ---------------------------------------------------------------- warm-up
+    launch_lens = []                     # committed lengths each timed launch streamed (host bookkeeping)
+    counter = [0]
+
     def step(evs=None):
-        nonlocal bound
+        si = counter[0] % n_sets
+        counter[0] += 1
+        st, bound = sets[si], bounds[si]
         if evs is None:
             dv.verify(lay, st, blk, bound)
         else:
             hci.verify_block_timed(lay.c, st.c, blk.c, blk.nb, blk.nc, blk.gamma, bound, blk.ws, evs)
-        dv.accept(acc, mode, cfg.temperature)
+        dv.accept(acc, mode, cfg.temperature, status=st.status)
         if evs is not None and evs[4]:
             hip.hipEventRecord(evs[4], sp)
         dv.slice_state(lay, st, blk, acc, bound)
         if evs is not None and evs[5]:
             hip.hipEventRecord(evs[5], sp)
-        bound += P
+        bounds[si] = bound + P
+        return si
 
     for _ in range(W):
         step()
     torch.cuda.synchronize()
-    len_before = dv.to_host(st.kv_len).astype(np.int64)
+    lens_before = [dv.to_host(st.kv_len).astype(np.int64) for st in sets]
 
     # ---------------------------------------------------------------- timed region
     # Only the two events around the streaming kernel are recorded here (its
@@ -572,15 +643,24 @@ def main():
         e = _events(hip, 6)
         e[0] = e[3] = e[4] = e[5] = None
         stream_evs.append(e)
+    used = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(stream_evs[i])
+        used.append(step(stream_evs[i]))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    len_after = dv.to_host(st.kv_len).astype(np.int64)
+    lens_after = [dv.to_host(st.kv_len).astype(np.int64) for st in sets]
     ms_step = (t1 - t0) * 1e3 / K
     stream_ms = [_ms(hip, e[1], e[2]) for e in stream_evs]
+    # every step commits the same k + 1 rows to the set it used: the lengths each launch read
+    n_on = [used.count(si) for si in range(n_sets)]
+    adv = [(lens_after[si] - lens_before[si]) // max(n_on[si], 1) for si in range(n_sets)]
+    seen = [0] * n_sets
+    for si in used:
+        launch_lens.append(lens_before[si] + adv[si] * seen[si])
+        seen[si] += 1
+    mean_lens = [float(np.mean([ll[b] for ll in launch_lens])) for b in range(cfg.nb)]
 
     # ---------------------------------------------------------------- breakdown pass (not timed)
     evsets = [_events(hip, 6) for _ in range(K)]
@@ -592,15 +672,19 @@ def main():
     accept_ms = [_ms(hip, e[3], e[4]) for e in evsets]
     slice_ms = [_ms(hip, e[4], e[5]) for e in evsets]
     step_dev_ms = [_ms(hip, e[0], e[5]) for e in evsets]
+    status = [int(v) for st in sets for v in dv.to_host(st.status)]
+    assert not any(status), f"device status bits set: {[hci.device_status_string(v) for v in status]}"
 
-    # mean committed length over the timed steps (the prefix grows by k+1 per step)
-    mean_lens = [int(a) + (int(b) - int(a)) * (K - 1) / (2.0 * K) for a, b in zip(len_before, len_after)]
+    # ---------------------------------------------------------------- replay-equivalent (not timed)
+    replay = replay_equivalent(cfg, lay, sets[0], bn, acc, bounds[0], hip, sp, args.replay_reps)
+
     alg_verify = verify_alg_bytes(cfg, mean_lens)
     alg_stream = stream_alg_bytes(cfg, mean_lens)
     avg_stream_s = float(np.mean(stream_ms)) * 1e-3
     achieved = alg_stream / avg_stream_s / 1e9
     positions = cfg.nb * cfg.nc * P
     value = positions / (ms_step * 1e-3)
+    slice_med = float(np.median(slice_ms))
 
     out = {
         "metric": "verified block-positions/sec per layer",
@@ -618,6 +702,7 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[args.config], "config_id": cfg.name, "nb": cfg.nb, "nc": cfg.nc,
                    "gamma": cfg.gamma, "kv_len": list(cfg.kv_lens), "d": cfg.d, "heads": cfg.heads,
                    "head_dim": cfg.head_dim, "parallelism": "single GPU"},
+        "kv_sets_rotated": n_sets,
         "verify_ms": round(float(np.median(verify_ms)), 4),
         "verify_hbm_GBs": round(alg_verify / (float(np.median(verify_ms)) * 1e-3) / 1e9, 1),
         "verify_pct_of_8TBs": round(100.0 * alg_verify / (float(np.median(verify_ms)) * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
@@ -625,9 +710,12 @@ def main():
         "breakdown_ms_median": {"verify_stream": round(float(np.median([_ms(hip, e[1], e[2]) for e in evsets])), 4),
                                 "verify_finish": round(float(np.median(combine_ms)), 4),
                                 "accept": round(float(np.median(accept_ms)), 4),
-                                "slice": round(float(np.median(slice_ms)), 4),
+                                "slice": round(slice_med, 4),
                                 "step_device": round(float(np.median(step_dev_ms)), 4)},
-        "slice_ms": round(float(np.median(slice_ms)), 4),
+        "slice_ms": round(slice_med, 4),
+        "replay_equiv_ms": replay["replay_equiv_ms"],
+        "replay_equiv_over_slice": round(replay["replay_equiv_ms"] / slice_med, 1),
+        "replay": replay,
         "hbm_probe_read_GBs": round(probe_gbs, 1),
         "roofline": {"kernel": stream_kernel_name(cfg),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -635,12 +723,84 @@ def main():
                      "traffic": _traffic(args.config, traffic_file(args.config)),
                      "alg_bytes_per_launch": int(alg_stream),
                      "avg_launch_ms": round(avg_stream_s * 1e3, 4)},
-        "accepted_per_step": [int(x) for x in ((len_after - len_before) // K)],
+        "accepted_per_step": [int(x) for x in adv[0]],
     }
+    if args.accept_rounds > 0:
+        out["acceptance"] = acceptance_stats(cfg, args.accept_rounds, hip)
     if not args.no_cpu_baseline:
         case_np = {"params": params, "small": small, "blk": bn, "ri": ri, "kpre": kpre_host, "vpre": vpre_host}
         out["cpu_baseline"] = cpu_baseline(cfg, case_np, heads, max(1, args.cpu_reps))
     print(json.dumps(out), flush=True)
+
+
+def replay_equivalent(cfg, lay, st, bn, acc, bound, hip, sp, reps):
+    """What slicing replaces: the accepted tokens run again through the target from the committed state.
+
+    replay_equiv_ms: the k + 1 accepted positions (k of the last accept, the winning candidate's rows)
+    as k + 1 sequential single-position steps -- verify with gamma = 0, then slice at 0 -- each reading
+    the whole KV prefix; for several sequences max_b k_b + 1 batched steps.  replay_block_forward_ms:
+    the same positions as one block forward (gamma = k) plus a slice at k.  Both run on a copy of the
+    committed state (windows, IIR state and lengths are restored between repetitions; cache rows past
+    kv_len are not state); medians of `reps` repetitions, HIP events on the stream.
+    """
+    import numpy as np
+    import torch
+    from hybrid_conv_iir_amd import device as dv
+    from hybrid_conv_iir_amd import hci
+    torch.cuda.synchronize()
+    n_acc, best = dv.to_host(acc.n_acc), dv.to_host(acc.best)
+    cstar = [int(best[b]) if cfg.nc > 1 else 0 for b in range(cfg.nb)]
+    ks = [int(n_acc[b, cstar[b]]) for b in range(cfg.nb)]
+    n = max(ks) + 1
+    saved = {name: getattr(st, name).clone() for name in ("short_win", "outer_win", "iir", "kv_len")}
+
+    def restore():
+        for name, t in saved.items():
+            getattr(st, name).copy_(t)
+
+    def rows(i0, i1):
+        pick = lambda a: np.stack([a[b, cstar[b], i0:i1] for b in range(cfg.nb)])[:, None]
+        return pick(bn["x"]), pick(bn["q"]), pick(bn["k"]), pick(bn["v"])
+
+    one = []
+    for i in range(n):
+        blk = dv.DeviceBlock(lay, cfg.nb, 1, 0)
+        blk.set_inputs(*rows(i, i + 1))
+        if i == 0:
+            blk.ensure_workspace(bound + n)
+        else:
+            blk.ws = one[0].ws                                # one workspace serves the sequential steps
+        one.append(blk)
+    acc0 = dv.DeviceAccept(cfg.nb, 1, 0, cfg.vocab)           # n_accepted = 0: commit the one position
+    whole = dv.DeviceBlock(lay, cfg.nb, 1, n - 1)
+    whole.set_inputs(*rows(0, n))
+    whole.ensure_workspace(bound)
+    accn = dv.DeviceAccept(cfg.nb, 1, n - 1, cfg.vocab)
+    accn.n_acc.fill_(n - 1)
+    ev = _events(hip, 2)
+    seq_ms, blk_ms = [], []
+    for r in range(reps + 1):                                 # the first repetition warms up
+        restore()
+        hip.hipEventRecord(ev[0], sp)
+        for i in range(n):
+            dv.verify(lay, st, one[i], bound + i)
+            dv.slice_state(lay, st, one[i], acc0, bound + i)
+        hip.hipEventRecord(ev[1], sp)
+        hip.hipEventSynchronize(ev[1])
+        if r:
+            seq_ms.append(_ms(hip, ev[0], ev[1]))
+        restore()
+        hip.hipEventRecord(ev[0], sp)
+        dv.verify(lay, st, whole, bound)
+        dv.slice_state(lay, st, whole, accn, bound)
+        hip.hipEventRecord(ev[1], sp)
+        hip.hipEventSynchronize(ev[1])
+        if r:
+            blk_ms.append(_ms(hip, ev[0], ev[1]))
+    restore()
+    torch.cuda.synchronize()
+    return {"replay_equiv_ms": round(float(np.median(seq_ms)), 4), "steps": n, "accepted_k": ks,
+            "replay_block_forward_ms": round(float(np.median(blk_ms)), 4), "reps": reps}
 
 
 if __name__ == "__main__":
