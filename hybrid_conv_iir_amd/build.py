@@ -26,6 +26,10 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # compiler-formed packed fp32 ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in vector registers where they fit: otherwise the attention
+    # kernels' score accumulators land in accumulation registers and are copied out for the
+    # softmax on every tile (several hundred extra moves per KV tile with four query tiles)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I" + os.path.join(ROOT, "include"),
 ]
 
