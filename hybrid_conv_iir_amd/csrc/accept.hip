@@ -13,6 +13,7 @@
 // fixed-order butterflies and a fixed-order LDS pass, so the result does
 // not depend on scheduling.
 #include "hci_internal.h"
+#include "wave_ops.h"
 
 #include <math.h>
 #include <float.h>
@@ -27,6 +28,7 @@ constexpr int kAccRows = 64;     // P <= 64
 struct AccScratch {
     double d[kAccW];
     int i[kAccW];
+    int i2[kAccW];
     double d2[kAccW];
     double bcast[4];
     int ibcast[2];
@@ -50,7 +52,7 @@ __device__ __forceinline__ bool row_finite(double sum) { return sum >= 1.0; }
 __device__ __forceinline__ double qnan() { return __longlong_as_double(0x7ff8000000000000LL); }
 
 __device__ __forceinline__ double block_sum(double v, AccScratch& sh) {
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    v = wave_sum_f64(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh.d[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -60,7 +62,7 @@ __device__ __forceinline__ double block_sum(double v, AccScratch& sh) {
 }
 
 __device__ __forceinline__ double block_max(double v, AccScratch& sh) {
-    for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+    v = wave_max_f64(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh.d[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -70,7 +72,7 @@ __device__ __forceinline__ double block_max(double v, AccScratch& sh) {
 }
 
 __device__ __forceinline__ double block_min(double v, AccScratch& sh) {
-    for (int off = 32; off >= 1; off >>= 1) v = fmin(v, __shfl_xor(v, off));
+    v = wave_min_f64(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh.d[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -80,7 +82,7 @@ __device__ __forceinline__ double block_min(double v, AccScratch& sh) {
 }
 
 __device__ __forceinline__ int block_imin(int v, AccScratch& sh) {
-    for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+    v = wave_min_i32(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh.i[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -90,7 +92,7 @@ __device__ __forceinline__ int block_imin(int v, AccScratch& sh) {
 }
 
 __device__ __forceinline__ int block_imax(int v, AccScratch& sh) {
-    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
+    v = wave_max_i32(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) sh.i[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -124,13 +126,31 @@ __device__ void wave_row_argmax(const float* z, int V, int lane, int& arg, doubl
             }
         }
     }
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float o1 = __shfl_xor(b1, off), o2 = __shfl_xor(b2, off);
-        const int oi = __shfl_xor(i1, off);
+    // merge with a partner lane's (best, index, runner-up): the same result on both lanes
+    auto merge = [&](float o1, float o2, int oi) {
         float n1, n2; int ni;
         if (o1 > b1 || (o1 == b1 && oi < i1)) { n1 = o1; ni = oi; n2 = fmaxf(b1, o2); }
         else { n1 = b1; ni = i1; n2 = fmaxf(b2, o1); }
         b1 = n1; b2 = n2; i1 = ni;
+    };
+    merge(dpp_f32<kQuadSwap1>(b1), dpp_f32<kQuadSwap1>(b2), (int)dpp_u32<kQuadSwap1>((uint32_t)i1));
+    merge(dpp_f32<kQuadSwap2>(b1), dpp_f32<kQuadSwap2>(b2), (int)dpp_u32<kQuadSwap2>((uint32_t)i1));
+    merge(dpp_f32<kHalfMirror>(b1), dpp_f32<kHalfMirror>(b2), (int)dpp_u32<kHalfMirror>((uint32_t)i1));
+    merge(dpp_f32<kRowMirror>(b1), dpp_f32<kRowMirror>(b2), (int)dpp_u32<kRowMirror>((uint32_t)i1));
+    {
+        // the row swaps return (own, partner) in even rows (halves) and (partner, own) in odd ones
+        uint32_t a1, c1, a2, c2, ai, ci;
+        swap_pair<false>(__float_as_uint(b1), a1, c1);
+        swap_pair<false>(__float_as_uint(b2), a2, c2);
+        swap_pair<false>((uint32_t)i1, ai, ci);
+        const bool first_own = (threadIdx.x & 16) == 0;
+        merge(__uint_as_float(first_own ? c1 : a1), __uint_as_float(first_own ? c2 : a2), (int)(first_own ? ci : ai));
+        swap_pair<true>(__float_as_uint(b1), a1, c1);
+        swap_pair<true>(__float_as_uint(b2), a2, c2);
+        swap_pair<true>((uint32_t)i1, ai, ci);
+        const bool first_own32 = (threadIdx.x & 32) == 0;
+        merge(__uint_as_float(first_own32 ? c1 : a1), __uint_as_float(first_own32 ? c2 : a2),
+              (int)(first_own32 ? ci : ai));
     }
     arg = i1;
     gap = (b2 == -INFINITY) ? INFINITY : (double)b1 - (double)b2;
@@ -150,17 +170,20 @@ __device__ void wave_row_stats(const float* z, int V, double T, int lane, double
             v[e] = j < V ? z[j] : -INFINITY;
             if (ztok && j == tok) *ztok = v[e];
         }
+        double xs[kLaneBatch];
         double m = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < kLaneBatch; ++e) m = fmax(m, (double)v[e] / T);
-        for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+        for (int e = 0; e < kLaneBatch; ++e) {
+            xs[e] = over_T((double)v[e], T);
+            m = fmax(m, xs[e]);
+        }
+        m = wave_max_f64(m);
         double s = 0.0;
 #pragma unroll
         for (int e = 0; e < kLaneBatch; ++e)
-            if (e * 64 + lane < V) s += exp((double)v[e] / T - m);
-        for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+            if (e * 64 + lane < V) s += exp(xs[e] - m);
         mx = m;
-        sum = s;
+        sum = wave_sum_f64(s);
         return;
     }
     double m = -INFINITY;
@@ -173,11 +196,11 @@ __device__ void wave_row_stats(const float* z, int V, double T, int lane, double
         }
 #pragma unroll
         for (int e = 0; e < kLaneBatch; ++e) {
-            m = fmax(m, (double)v[e] / T);
+            m = fmax(m, over_T((double)v[e], T));
             if (ztok && j0 + e * 64 + lane == tok) *ztok = v[e];
         }
     }
-    for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+    m = wave_max_f64(m);
     double s = 0.0;
     for (int j0 = 0; j0 < V; j0 += 64 * kLaneBatch) {
         float v[kLaneBatch];
@@ -188,42 +211,70 @@ __device__ void wave_row_stats(const float* z, int V, double T, int lane, double
         }
 #pragma unroll
         for (int e = 0; e < kLaneBatch; ++e)
-            if (j0 + e * 64 + lane < V) s += exp((double)v[e] / T - m);
+            if (j0 + e * 64 + lane < V) s += exp(over_T((double)v[e], T) - m);
     }
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
     mx = m;
-    sum = s;
+    sum = wave_sum_f64(s);
 }
 
 
 // Inverse-CDF draw over token ids with weights weight(j) >= 0: the smallest j whose running sum
 // exceeds r x total (total = the running sum at the last token, formed exactly as the search
 // forms it), else the last token with positive weight.  Every thread owns a contiguous run of
-// ids; the run totals are scanned in a fixed order.  Returns the token and the distance of the
-// nearest running sum from the threshold, relative to the total.
+// ids; the run totals are scanned in a fixed order (a scan inside each wave, then the waves'
+// totals in wave order).  Returns the token, the distance of the nearest running sum from the
+// threshold relative to the total, and the total (0 when every weight is 0: no token is drawn
+// then, token = -1).
+
+// exclusive prefix of the thread's run total loc over the workgroup, in a fixed order
+__device__ __forceinline__ double block_excl_scan(double loc, AccScratch& sh) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const double incl = wave_incl_scan_f64(loc, lane);
+    __syncthreads();                                   // earlier readers of sh.d are done
+    if (lane == 63) sh.d[wv] = incl;
+    __syncthreads();
+    double excl = 0.0;
+    for (int w = 0; w < wv; ++w) excl += sh.d[w];
+    return excl + (incl - loc);
+}
+
+// the draw's workgroup-wide result from every thread's (first crossing, last positive id,
+// nearest distance): one exchange through LDS
+__device__ __forceinline__ void draw_result(int first, int lastpos, double dmin, double total, AccScratch& sh,
+                                            int& token, double& margin) {
+    first = wave_min_i32(first);
+    lastpos = wave_max_i32(lastpos);
+    dmin = wave_min_f64(dmin);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (lane == 0) {
+        sh.i[wv] = first;
+        sh.i2[wv] = lastpos;
+        sh.d2[wv] = dmin;
+    }
+    __syncthreads();
+    first = sh.i[0];
+    lastpos = sh.i2[0];
+    dmin = sh.d2[0];
+    for (int w = 1; w < kAccW; ++w) {
+        first = min(first, sh.i[w]);
+        lastpos = max(lastpos, sh.i2[w]);
+        dmin = fmin(dmin, sh.d2[w]);
+    }
+    token = first != INT_MAX ? first : lastpos;
+    margin = dmin / total;
+}
+
 template <typename F>
-__device__ void draw_token(F weight, int V, double r, AccScratch& sh, int& token, double& margin)
+__device__ void draw_token(F weight, int V, double r, AccScratch& sh, int& token, double& margin,
+                           double* total_out = nullptr)
 {
     const int per = (V + kAccT - 1) / kAccT;
     const int j0 = min((int)threadIdx.x * per, V), j1 = min(j0 + per, V);
     double loc = 0.0;
     for (int j = j0; j < j1; ++j) loc += weight(j);
-    // exclusive scan of the per-thread totals: Hillis-Steele inside a wave, waves in order
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    double incl = loc;
-    for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
-    __syncthreads();
-    if (lane == 63) sh.d[wv] = incl;
-    __syncthreads();
-    double excl = 0.0;
-    for (int w = 0; w < wv; ++w) excl += sh.d[w];
-    excl += incl - loc;
+    const double excl = block_excl_scan(loc, sh);
     double run = excl;
     for (int j = j0; j < j1; ++j) run += weight(j);
-    __syncthreads();
     if (j0 < j1 && j1 == V) sh.bcast[0] = run;
     __syncthreads();
     const double total = sh.bcast[0];
@@ -238,11 +289,8 @@ __device__ void draw_token(F weight, int V, double r, AccScratch& sh, int& token
         if (w > 0.0) lastpos = j;
         dmin = fmin(dmin, fabs(run - target));
     }
-    first = block_imin(first, sh);
-    lastpos = block_imax(lastpos, sh);
-    dmin = block_min(dmin, sh);
-    token = first != INT_MAX ? first : lastpos;
-    margin = dmin / total;
+    draw_result(first, lastpos, dmin, total, sh, token, margin);
+    if (total_out) *total_out = total;
 }
 
 
@@ -251,7 +299,7 @@ __device__ void draw_token(F weight, int V, double r, AccScratch& sh, int& token
 // as draw_token, without evaluating (and loading) every weight three times.
 constexpr int kDrawCache = 4;
 __device__ void draw_token_cached(const double (&wc)[kDrawCache], int V, double r, AccScratch& sh, int& token,
-                                  double& margin)
+                                  double& margin, double* total_out = nullptr)
 {
     const int per = (V + kAccT - 1) / kAccT;
     const int j0 = min((int)threadIdx.x * per, V), j1 = min(j0 + per, V);
@@ -259,23 +307,11 @@ __device__ void draw_token_cached(const double (&wc)[kDrawCache], int V, double 
 #pragma unroll
     for (int u = 0; u < kDrawCache; ++u)
         if (j0 + u < j1) loc += wc[u];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    double incl = loc;
-    for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
-    __syncthreads();
-    if (lane == 63) sh.d[wv] = incl;
-    __syncthreads();
-    double excl = 0.0;
-    for (int w = 0; w < wv; ++w) excl += sh.d[w];
-    excl += incl - loc;
+    const double excl = block_excl_scan(loc, sh);
     double run = excl;
 #pragma unroll
     for (int u = 0; u < kDrawCache; ++u)
         if (j0 + u < j1) run += wc[u];
-    __syncthreads();
     if (j0 < j1 && j1 == V) sh.bcast[0] = run;
     __syncthreads();
     const double total = sh.bcast[0];
@@ -294,11 +330,8 @@ __device__ void draw_token_cached(const double (&wc)[kDrawCache], int V, double 
             dmin = fmin(dmin, fabs(run - target));
         }
     }
-    first = block_imin(first, sh);
-    lastpos = block_imax(lastpos, sh);
-    dmin = block_min(dmin, sh);
-    token = first != INT_MAX ? first : lastpos;
-    margin = dmin / total;
+    draw_result(first, lastpos, dmin, total, sh, token, margin);
+    if (total_out) *total_out = total;
 }
 
 // Residual weight of one token after r rejections at the current depth: w^(0) = p,
@@ -365,8 +398,8 @@ __device__ void accept_recursive(int b, int nc, int gamma, int V, double T,
             const int t = drafts[((size_t)b * nc + c) * gamma + k];
             if (t < 0 || t >= V) flags |= HCI_DS_DRAFT_ID;
             if (t >= 0 && t < V) {
-                const double p_t = exp((double)prow[t] / T - pm) / ps;
-                const double q_t = exp((double)qrow[t] / T - qm) / qs;
+                const double p_t = exp(over_T((double)prow[t], T) - pm) / ps;
+                const double q_t = exp(over_T((double)qrow[t], T) - qm) / qs;
                 const double lhs = uni[((size_t)b * nc + c) * P + k] * q_t * sh.zh[nrej];
                 const double rhs = residual_weight(p_t, q_t, nrej, sh);
                 if (threadIdx.x == 0) sh.cm[c] = fmin(sh.cm[c], fabs(lhs - rhs) / fmax(rhs, 1e-300));
@@ -379,8 +412,8 @@ __device__ void accept_recursive(int b, int nc, int gamma, int V, double T,
             const double z = sh.zh[nrej];
             double loc = 0.0;
             for (int j = threadIdx.x; j < V; j += kAccT) {
-                const double q = exp((double)qrow[j] / T - qm) / qs;
-                const double w = residual_weight(exp((double)prow[j] / T - pm) / ps, q, nrej, sh);
+                const double q = exp(over_T((double)qrow[j], T) - qm) / qs;
+                const double w = residual_weight(exp(over_T((double)prow[j], T) - pm) / ps, q, nrej, sh);
                 loc += fmax(0.0, w - __dmul_rn(z, q));
             }
             const double tot = block_sum(loc, sh);
@@ -419,8 +452,8 @@ __device__ void accept_recursive(int b, int nc, int gamma, int V, double T,
     const double pm = sh.st[0], ps = sh.st[1], qm = sh.st[2], qs = sh.st[3];
     const int r = nrej;
     auto weight = [&](int j) {
-        const double p = exp((double)prow[j] / T - pm) / ps;
-        return r == 0 ? p : residual_weight(p, exp((double)qrow[j] / T - qm) / qs, r, sh);
+        const double p = exp(over_T((double)prow[j], T) - pm) / ps;
+        return r == 0 ? p : residual_weight(p, exp(over_T((double)qrow[j], T) - qm) / qs, r, sh);
     };
     int tok;
     double m2;
@@ -513,8 +546,8 @@ __global__ __launch_bounds__(kAccT) void k_accept(
                 for (int mm = m0; mm < m0 + kAccW / 2 && mm <= gamma; ++mm) {
                     const int t = dr[mm - 1];
                     if (t < 0 || t >= V) { k = mm - 1; done = true; flags |= HCI_DS_DRAFT_ID; break; }
-                    const double p_t = exp((double)sh.ztok[mm - 1] / T - sh.pm[mm - 1]) / sh.ps[mm - 1];
-                    const double q_t = exp((double)sh.dtok[mm - 1] / T - sh.qm[mm - 1]) / sh.qs[mm - 1];
+                    const double p_t = exp(over_T((double)sh.ztok[mm - 1], T) - sh.pm[mm - 1]) / sh.ps[mm - 1];
+                    const double q_t = exp(over_T((double)sh.dtok[mm - 1], T) - sh.qm[mm - 1]) / sh.qs[mm - 1];
                     const double lhs = u[mm - 1] * q_t;
                     margin = fmin(margin, fabs(lhs - p_t) / fmax(p_t, 1e-300));
                     if (!(lhs < p_t)) { k = mm - 1; done = true; break; }
@@ -537,37 +570,33 @@ __global__ __launch_bounds__(kAccT) void k_accept(
             const float* prow = zt_c + (size_t)k * V;
             const float* qrow = zd_c + (size_t)k * V;
             auto weight = [&](int j) {
-                const double p = exp((double)prow[j] / T - pm) / ps;
-                return resid ? fmax(0.0, p - exp((double)qrow[j] / T - qm) / qs) : p;
+                const double p = exp(over_T((double)prow[j], T) - pm) / ps;
+                return resid ? fmax(0.0, p - exp(over_T((double)qrow[j], T) - qm) / qs) : p;
             };
             const int per = (V + kAccT - 1) / kAccT;
             const int j0 = min((int)threadIdx.x * per, V), j1 = min(j0 + per, V);
             int tok;
-            double m2;
+            double m2, tot;
+            // an empty residual cannot follow a rejection (guard only): the draw then falls back
+            // to p_k itself
             if (per <= kDrawCache) {
                 // every weight of the thread's run evaluated once (its logits loaded once)
                 double wc[kDrawCache];
 #pragma unroll
                 for (int uu = 0; uu < kDrawCache; ++uu) wc[uu] = j0 + uu < j1 ? weight(j0 + uu) : 0.0;
-                if (resid) {           // cannot be empty after a rejection; guard only
-                    double loc = 0.0;
+                draw_token_cached(wc, V, u[gamma], sh, tok, m2, &tot);
+                if (resid && !(tot > 0.0)) {
+                    resid = false;
 #pragma unroll
-                    for (int uu = 0; uu < kDrawCache; ++uu)
-                        if (j0 + uu < j1) loc += wc[uu];
-                    if (!(block_sum(loc, sh) > 0.0)) {
-                        resid = false;
-#pragma unroll
-                        for (int uu = 0; uu < kDrawCache; ++uu) wc[uu] = j0 + uu < j1 ? weight(j0 + uu) : 0.0;
-                    }
+                    for (int uu = 0; uu < kDrawCache; ++uu) wc[uu] = j0 + uu < j1 ? weight(j0 + uu) : 0.0;
+                    draw_token_cached(wc, V, u[gamma], sh, tok, m2);
                 }
-                draw_token_cached(wc, V, u[gamma], sh, tok, m2);
             } else {
-                if (resid) {           // cannot be empty after a rejection; guard only
-                    double loc = 0.0;
-                    for (int j = j0; j < j1; ++j) loc += weight(j);
-                    if (!(block_sum(loc, sh) > 0.0)) resid = false;
+                draw_token(weight, V, u[gamma], sh, tok, m2, &tot);
+                if (resid && !(tot > 0.0)) {
+                    resid = false;
+                    draw_token(weight, V, u[gamma], sh, tok, m2);
                 }
-                draw_token(weight, V, u[gamma], sh, tok, m2);
             }
             nxt = tok;
             margin = fmin(margin, m2);
@@ -699,14 +728,14 @@ __global__ __launch_bounds__(kAccT) void k_accept_tree(
                 double w = p;
                 for (int i = 0; i < nrej; ++i)
                     if (sh.zapp[i])
-                        w = fmax(0.0, w - __dmul_rn(sh.zh[i], exp((double)zdb[(size_t)sh.rnode[i] * V + j] / T -
+                        w = fmax(0.0, w - __dmul_rn(sh.zh[i], exp(over_T((double)zdb[(size_t)sh.rnode[i] * V + j], T) -
                                                                   sh.rqm[i]) / sh.rqs[i]));
                 return w;
             };
             const int t = tok[c];
             if (t >= 0 && t < V) {
-                const double p_t = exp((double)prow[t] / T - pm) / ps;
-                const double q_t = exp((double)qrow[t] / T - qm) / qs;
+                const double p_t = exp(over_T((double)prow[t], T) - pm) / ps;
+                const double q_t = exp(over_T((double)qrow[t], T) - qm) / qs;
                 const double lhs = uni[(size_t)b * n + c] * q_t * sh.zh[nrej];
                 const double rhs = resid(t, p_t);
                 margin = fmin(margin, fabs(lhs - rhs) / fmax(rhs, 1e-300));
@@ -718,8 +747,8 @@ __global__ __launch_bounds__(kAccT) void k_accept_tree(
             const double z = sh.zh[nrej];
             double loc = 0.0;
             for (int j = tid; j < V; j += kAccT) {
-                const double q = exp((double)qrow[j] / T - qm) / qs;
-                loc += fmax(0.0, resid(j, exp((double)prow[j] / T - pm) / ps) - __dmul_rn(z, q));
+                const double q = exp(over_T((double)qrow[j], T) - qm) / qs;
+                loc += fmax(0.0, resid(j, exp(over_T((double)prow[j], T) - pm) / ps) - __dmul_rn(z, q));
             }
             const double tot = block_sum(loc, sh.a);
             __syncthreads();
@@ -744,12 +773,12 @@ __global__ __launch_bounds__(kAccT) void k_accept_tree(
         }
         const int r = nrej;
         auto weight = [&](int j) {
-            const double p = exp((double)prow[j] / T - pm) / ps;
+            const double p = exp(over_T((double)prow[j], T) - pm) / ps;
             if (r == 0) return p;
             double w = p;
             for (int i = 0; i < r; ++i)
                 if (sh.zapp[i])
-                    w = fmax(0.0, w - __dmul_rn(sh.zh[i], exp((double)zdb[(size_t)sh.rnode[i] * V + j] / T -
+                    w = fmax(0.0, w - __dmul_rn(sh.zh[i], exp(over_T((double)zdb[(size_t)sh.rnode[i] * V + j], T) -
                                                               sh.rqm[i]) / sh.rqs[i]));
             return w;
         };
@@ -797,8 +826,8 @@ __global__ __launch_bounds__(256) void k_accept_best(int nb, int nc, const int32
 // Serial drafting with the previous-token bias (EvSpark digest, Figure 1(b)): draft m draws from
 // softmax(l / T), l = z[m] + B[prev] in fp32, by the same inverse-CDF rule as the acceptance
 // draws.  One wave per sequence and no barrier: each lane holds a contiguous run of ceil(V/64)
-// token ids in registers, the row maximum, the sum and the exclusive scan of the run totals are
-// butterflies / shuffles, and the lane whose run crosses u x total walks it.
+// token ids in registers, the row maximum, the sum and the scan of the run totals are wave
+// collectives on the vector ALU, and the lane whose run crosses u x total walks it.
 constexpr int kDsMaxPer = 64;              // V <= 4096 on this path
 
 template <int PER>                         // ids per lane, a power of two >= ceil(V / 64)
@@ -823,19 +852,18 @@ __global__ __launch_bounds__(64) void k_draft_sample(int gamma, int V, double T,
             l[t] = t < n ? z[r + j] + markov[(size_t)prev * V + j] : -INFINITY;
             if (t < n) {
                 dl[r + j] = l[t];
-                mx = fmax(mx, (double)l[t] / T);
+                mx = fmax(mx, over_T((double)l[t], T));
             }
         }
-        for (int off = 32; off >= 1; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
+        mx = wave_max_f64(mx);
         double e[PER];
         double loc = 0.0;
 #pragma unroll
         for (int t = 0; t < PER; ++t) {
-            e[t] = t < n ? exp((double)l[t] / T - mx) : 0.0;
+            e[t] = t < n ? exp(over_T((double)l[t], T) - mx) : 0.0;
             loc += e[t];
         }
-        double sum = loc;
-        for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+        const double sum = wave_sum_f64(loc);
         // probabilities p_j = exp(l_j / T - mx) / sum; running sums over ascending ids
         double ploc = 0.0;
 #pragma unroll
@@ -843,12 +871,8 @@ __global__ __launch_bounds__(64) void k_draft_sample(int gamma, int V, double T,
             e[t] = e[t] / sum;
             ploc += e[t];
         }
-        double incl = ploc;
-        for (int off = 1; off < 64; off <<= 1) {
-            const double o = __shfl_up(incl, off);
-            if (lane >= off) incl += o;
-        }
-        const double total = __shfl(incl, 63);
+        double total;
+        const double incl = wave_incl_scan_f64(ploc, lane, &total);
         const double excl = incl - ploc;
         const double target = uni[(size_t)b * gamma + m] * total;
         int first = INT_MAX, lastpos = -1;
@@ -863,11 +887,9 @@ __global__ __launch_bounds__(64) void k_draft_sample(int gamma, int V, double T,
                 dmin = fmin(dmin, fabs(run - target));
             }
         }
-        for (int off = 32; off >= 1; off >>= 1) {
-            first = min(first, __shfl_xor(first, off));
-            lastpos = max(lastpos, __shfl_xor(lastpos, off));
-            dmin = fmin(dmin, __shfl_xor(dmin, off));
-        }
+        first = wave_min_i32(first);
+        lastpos = wave_max_i32(lastpos);
+        dmin = wave_min_f64(dmin);
         const int tok = first != INT_MAX ? first : lastpos;
         if (lane == 0) {
             drafts[(size_t)b * gamma + m] = tok;
