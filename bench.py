@@ -461,9 +461,12 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU-oracle sample (0 = all)")
     ap.add_argument("--cpu-reps", type=int, default=3, help="repetitions of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="verify", choices=["verify", "prefill", "linear", "model", "draft"],
+    ap.add_argument("--mode", default="verify", choices=["verify", "prefill", "linear", "model", "draft", "tree"],
                     help="verify: the verify->accept->slice step (default); prefill: prompt -> committed state; "
-                         "linear: one dense projection of the verified block")
+                         "linear: one dense projection of the verified block; tree: the candidate blocks of "
+                         "--config merged into token trees (tree verify -> accept -> slice), beside the chain step")
+    ap.add_argument("--tree-vocab", type=int, default=4,
+                    help="alphabet of the drafted tokens in --mode tree (4: nucleotides)")
     ap.add_argument("--linear-shape", default="13,4096,12288", help="M,K,N for --mode linear")
     ap.add_argument("--model", default="m4_long", help="layer stack for --mode model")
     ap.add_argument("--prompt", type=int, default=262144, help="prompt length for --mode prefill")
@@ -504,6 +507,8 @@ def main():
         return bench_model(args, hip)
     if args.mode == "draft":
         return bench_draft(args, hip)
+    if args.mode == "tree":
+        return bench_tree(args, cfg, hip)
     return bench_verify(args, cfg, hip)
 
 
@@ -739,6 +744,134 @@ def bench_verify(args, cfg, hip):
     if not args.no_cpu_baseline:
         case_np = {"params": params, "small": small, "blk": bn, "ri": ri, "kpre": kpre_host, "vpre": vpre_host}
         out["cpu_baseline"] = cpu_baseline(cfg, case_np, heads, max(1, args.cpu_reps))
+    print(json.dumps(out), flush=True)
+
+
+def bench_tree(args, cfg, hip):
+    """Token-tree verification against the chain form of the same candidates.
+
+    The nc candidate blocks of each sequence (gamma drafts each, over a small alphabet, drawn from
+    prefix-keyed draft rows) share prefixes; merged into a trie they are n <= nc * (gamma + 1)
+    nodes, each computed once (EvSpark digest, Interpretation: several candidates per round;
+    ReaDy summary, section 5: tree verification with state recovery).  One tree step =
+    hci_verify_tree -> hci_accept_tree (sampling) -> hci_slice_tree; the chain step verifies the
+    same candidates as nc blocks (hci_verify_block -> hci_accept -> hci_slice_state) on a
+    second state with the same prefixes.
+    """
+    import numpy as np
+    import torch
+    from hybrid_conv_iir_amd import device as dv
+    from hybrid_conv_iir_amd import hci, synth
+    W, K = args.warmup, args.steps
+    cfg = synth.scaled(cfg, vocab=args.tree_vocab, mode="sample")
+    tr = synth.tree_round(cfg)
+    n = int(tr["n"])
+    P = cfg.P
+    n_ev = max(3, K // 4)                                  # steps of the per-part breakdown
+    kv_cap = (cfg.max_kv_len + (W + K + n_ev + 2) * max(n, P) + 31) // 32 * 32
+
+    params = synth.make_layer(cfg)
+    small = synth.make_state_small(cfg)
+    tables = synth.make_tables(cfg)
+    lay = dv.DeviceLayer(cfg, params)
+
+    def new_state():
+        st = dv.DeviceState(lay, cfg.nb, kv_cap)
+        st.load_small(small)
+        for b in range(cfg.nb):
+            st.write_prefix(b, synth.kv_prefix(cfg, b, "k", device="cuda"), synth.kv_prefix(cfg, b, "v", device="cuda"))
+        st.kv_len.copy_(torch.tensor(cfg.kv_lens, dtype=torch.int32))
+        return st
+
+    st_t, st_c = new_state(), new_state()
+    tok = tr["tokens"]
+    tree = dv.DeviceTree(lay, cfg.nb, n, cfg.vocab)
+    tree.set_inputs(tr["parent"], tables["E_x"][tok], tables["E_q"][tok], tables["E_k"][tok], tables["E_v"][tok])
+    tree.set_accept_inputs(tok, tr["target_logits"], tr["draft_logits"], tr["uniforms"])
+    # the chain form: the same candidate blocks (the tries were built from them)
+    cand_zt, cand_zd, drafts, cand_u = synth.prefix_keyed_round(cfg)
+    bn = synth.gather_block(cfg, tables, synth.block_tokens(synth.anchors(cfg), drafts))
+    blk = dv.DeviceBlock(lay, cfg.nb, cfg.nc, cfg.gamma)
+    blk.set_inputs(bn["x"], bn["q"], bn["k"], bn["v"])
+    acc = dv.DeviceAccept(cfg.nb, cfg.nc, cfg.gamma, cfg.vocab)
+    acc.set_inputs(cand_zt, drafts, cand_zd, cand_u)
+    bound_t = [cfg.max_kv_len]
+    bound_c = [cfg.max_kv_len]
+    tree.ensure_workspace(kv_cap - n)
+    blk.ensure_workspace(kv_cap - P)
+    sp = torch.cuda.current_stream().cuda_stream
+
+    def tree_step(evs=None):
+        if evs is not None:
+            hip.hipEventRecord(evs[0], sp)
+        dv.verify_tree(lay, st_t, tree, bound_t[0])
+        if evs is not None:
+            hip.hipEventRecord(evs[1], sp)
+        dv.accept_tree(tree, hci.SAMPLE, cfg.temperature, status=st_t.status)
+        if evs is not None:
+            hip.hipEventRecord(evs[2], sp)
+        dv.slice_tree(lay, st_t, tree, bound_t[0])
+        if evs is not None:
+            hip.hipEventRecord(evs[3], sp)
+        bound_t[0] += n
+
+    def chain_step():
+        dv.verify(lay, st_c, blk, bound_c[0])
+        dv.accept(acc, hci.SAMPLE, cfg.temperature, status=st_c.status)
+        dv.slice_state(lay, st_c, blk, acc, bound_c[0])
+        bound_c[0] += P
+
+    def timed(fn, steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    for _ in range(W):
+        tree_step()
+        chain_step()
+    half = max(1, K // 2)
+    tree_ms = timed(tree_step, half)
+    chain_ms = timed(chain_step, half)
+    tree_ms = min(tree_ms, timed(tree_step, K - half) if K > half else tree_ms)
+    chain_ms = min(chain_ms, timed(chain_step, K - half) if K > half else chain_ms)
+    evs = [_events(hip, 4) for _ in range(n_ev)]
+    for e in evs:
+        tree_step(e)
+    torch.cuda.synchronize()
+    parts = {"verify_tree": float(np.median([_ms(hip, e[0], e[1]) for e in evs])),
+             "accept_tree": float(np.median([_ms(hip, e[1], e[2]) for e in evs])),
+             "slice_tree": float(np.median([_ms(hip, e[2], e[3]) for e in evs]))}
+    status = [int(v) for st in (st_t, st_c) for v in dv.to_host(st.status)]
+    assert not any(status), f"device status bits set: {[hci.device_status_string(v) for v in status]}"
+    n_acc = [int(v) for v in dv.to_host(tree.n_acc)]
+    positions = cfg.nb * cfg.nc * P
+    out = {
+        "metric": "verified tree nodes/sec per layer",
+        "value": round(cfg.nb * n / (tree_ms * 1e-3), 1),
+        "unit": "nodes/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(tree_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.act == "bf16" else "f32",
+        "data": f"synthetic (seeded N(0,1) activations and KV; drafts over a {cfg.vocab}-letter alphabet "
+                f"from prefix-keyed draft rows; no trained weights)",
+        "config": {"workload": f"token-tree verify: {cfg.nb} sequences x {cfg.nc} candidate blocks (gamma="
+                               f"{cfg.gamma}) merged into tries of {n} nodes, KV prefixes "
+                               + "/".join(str(L) for L in cfg.kv_lens),
+                   "config_id": cfg.name, "nb": cfg.nb, "nc": cfg.nc, "gamma": cfg.gamma, "nodes": n,
+                   "trie_sizes": [int(v) for v in tr["trie_sizes"]], "vocab": cfg.vocab,
+                   "kv_len": list(cfg.kv_lens), "d": cfg.d, "heads": cfg.heads, "head_dim": cfg.head_dim,
+                   "parallelism": "single GPU"},
+        "candidate_positions_per_s": round(positions / (tree_ms * 1e-3), 1),
+        "chain_ms_per_step": round(chain_ms, 4),
+        "chain_candidate_positions_per_s": round(positions / (chain_ms * 1e-3), 1),
+        "tree_over_chain_speedup": round(chain_ms / tree_ms, 3),
+        "query_rows": {"tree": cfg.nb * n, "chain": positions},
+        "breakdown_ms_median": {k: round(v, 4) for k, v in parts.items()},
+        "accepted_depths_last_step": n_acc,
+    }
     print(json.dumps(out), flush=True)
 
 

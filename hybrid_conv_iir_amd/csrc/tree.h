@@ -72,13 +72,16 @@ __device__ __forceinline__ bool tree_build(const int32_t* __restrict__ parent, i
     return *flag != 0;
 }
 
-// LDS floats of the tree conv role (after the ancestor table, 16-byte aligned): short window +
-// x rows, outer window + f rows, chunk sums of g, outer taps, short taps, IIR states of every
-// node.
+// LDS of the tree conv role: the ancestor table, a flag word, the leaf bookkeeping (leaf flags,
+// the leaves in index order, each node's owning leaf: 64 bytes each), then (16-byte aligned)
+// floats: short window + x rows, outer window + f rows, chunk sums of g, outer taps, short taps.
+constexpr size_t kTreeLeafBytes = 3 * kTreeMax;
+__host__ __device__ inline size_t tree_conv_head_bytes() {
+    return (kTreeAncBytes + 16 + kTreeLeafBytes + 15) / 16 * 16;
+}
 __host__ __device__ inline size_t tree_conv_lds_bytes(int Ts, int To, int n) {
-    const size_t floats = (size_t)((Ts - 1 + n) + (To - 1 + n) + kFirChunks * n + To + Ts) * kCG +
-                          (size_t)n * kCG * kTreePoles;
-    return (kTreeAncBytes + 16 + 15) / 16 * 16 + floats * sizeof(float);
+    const size_t floats = (size_t)((Ts - 1 + n) + (To - 1 + n) + kFirChunks * n + To + Ts) * kCG;
+    return tree_conv_head_bytes() + floats * sizeof(float);
 }
 
 // One workgroup: channel group cgi (16 channels) of sequence b; the tree's n nodes are the rows
@@ -95,12 +98,14 @@ __device__ __forceinline__ uint32_t tree_conv_block(
     const int W = To - 1, Ws = Ts - 1;
     const TreeAnc t = tree_anc_lds(lds_raw);
     int* flag = (int*)((char*)lds_raw + kTreeAncBytes);
-    float* xs = (float*)((char*)lds_raw + (kTreeAncBytes + 16 + 15) / 16 * 16);   // [Ws + n][kCG]
+    uint8_t* is_leaf = (uint8_t*)lds_raw + kTreeAncBytes + 16;     // [64]
+    uint8_t* leaves = is_leaf + kTreeMax;                           // [64] the leaves in index order
+    uint8_t* owner = leaves + kTreeMax;                             // [64] the leaf whose scan stores node m
+    float* xs = (float*)((char*)lds_raw + tree_conv_head_bytes());  // [Ws + n][kCG]
     float* fb = xs + (size_t)(Ws + n) * kCG;          // [W + n][kCG]: outer window rows, then f rows
     float* gl = fb + (size_t)(W + n) * kCG;           // [kFirChunks][n][kCG]
     float* wl = gl + (size_t)kFirChunks * n * kCG;    // [To][kCG]
     float* ws = wl + (size_t)To * kCG;                // [Ts][kCG]
-    float* sl = ws + (size_t)Ts * kCG;                // [n][kCG][kTreePoles]
 
     const int ch0 = cgi * kCG;
     const int tid = threadIdx.x;
@@ -152,12 +157,39 @@ __device__ __forceinline__ uint32_t tree_conv_block(
     }
     __syncthreads();
 
-    // IIR along the tree: task (channel tch, pole group tg) on G lanes; nodes in index order, so a
-    // node's parent state is already in LDS.  Waves past the first have no task (the scan over the
-    // nodes is sequential).
+    // IIR along the tree, one root-to-leaf path per wave and pass: the path's nodes in order from
+    // the root, each state s = fma(lambda, s_parent, beta * g) kept in registers, so no node's state
+    // is stored in LDS.  A node on several paths is computed by each of them with the same
+    // arithmetic (the same bits) and stored by one: the first leaf below it in index order.
+    if (tid < n) {
+        bool leaf = true;
+        for (int c = tid + 1; c < n; ++c) leaf = leaf && t.par[c] != tid;
+        is_leaf[tid] = leaf ? 1 : 0;
+    }
+    __syncthreads();
+    int nl = 0;
+    for (int m = 0; m < n; ++m) nl += is_leaf[m];
+    if (tid < n) {
+        if (is_leaf[tid]) {
+            int rank = 0;
+            for (int m = 0; m < tid; ++m) rank += is_leaf[m];
+            leaves[rank] = (uint8_t)tid;
+        }
+        const int dm = t.depth[tid];
+        int own = tid;
+        for (int L = 0; L < n; ++L) {
+            const int dl = t.depth[L];
+            if (is_leaf[L] && dl >= dm && t.anc[L * kTreeMax + (dl - dm)] == tid) { own = L; break; }
+        }
+        owner[tid] = (uint8_t)own;
+    }
+    __syncthreads();
+
     const int G = N <= 4 ? 1 : N <= 8 ? 2 : 4;
-    if (tid < kCG * G) {
-        const int tg = tid % G, tch = tid / G;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (lane < kCG * G) {
+        const int tg = lane % G, tch = lane / G;
         const int chn = ch0 + tch;
         const bool scan = chn < d;
         float lm[4], bt[4], cv[4], s0[4];
@@ -171,39 +203,37 @@ __device__ __forceinline__ uint32_t tree_conv_block(
             cv[q] = ok ? cc[o] : 0.f;
             s0[q] = ok ? iir[(size_t)b * d * N + o] : 0.f;
         }
-        float* mys = sl + (size_t)tch * kTreePoles + 4 * tg;          // + m * kCG * kTreePoles
-        for (int m = 0; m < n; ++m) {
-            float g = gl[(size_t)m * kCG + tch];
+        for (int li = wv; li < nl; li += kConvT / 64) {
+            const int L = leaves[li];
+            const int D = t.depth[L];
+            const uint8_t* aL = t.anc + L * kTreeMax;
+            float st[4] = {s0[0], s0[1], s0[2], s0[3]};
+            for (int j = D; j >= 0; --j) {               // node aL[j]: j steps above the leaf
+                const int m = aL[j];
+                float g = gl[(size_t)m * kCG + tch];
 #pragma unroll
-            for (int k = 1; k < kFirChunks; ++k) g += gl[((size_t)k * n + m) * kCG + tch];
-            g = scan ? g : 0.f;
-            float st[4];
-            if (m == 0) {
+                for (int k = 1; k < kFirChunks; ++k) g += gl[((size_t)k * n + m) * kCG + tch];
+                g = scan ? g : 0.f;
+                float py = 0.f;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) st[q] = s0[q];
-            } else {
-                const float4 sp = *(const float4*)(mys + (size_t)t.par[m] * kCG * kTreePoles);
-                st[0] = sp.x; st[1] = sp.y; st[2] = sp.z; st[3] = sp.w;
-            }
-            float py = 0.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                st[q] = fmaf(lm[q], st[q], bt[q] * g);
-                py = fmaf(cv[q], st[q], py);
-            }
-            *(float4*)(mys + (size_t)m * kCG * kTreePoles) = make_float4(st[0], st[1], st[2], st[3]);
-            if (scan) {
-                float* so = s_out + (((size_t)b * n + m) * d + chn) * N + 4 * tg;
-                if ((N & 3) == 0) {
-                    *(float4*)so = make_float4(st[0], st[1], st[2], st[3]);
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (4 * tg + q < N) so[q] = st[q];
+                for (int q = 0; q < 4; ++q) {
+                    st[q] = fmaf(lm[q], st[q], bt[q] * g);
+                    py = fmaf(cv[q], st[q], py);
                 }
+                const bool store = scan && owner[m] == L;
+                if (store) {
+                    float* so = s_out + (((size_t)b * n + m) * d + chn) * N + 4 * tg;
+                    if ((N & 3) == 0) {
+                        *(float4*)so = make_float4(st[0], st[1], st[2], st[3]);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (4 * tg + q < N) so[q] = st[q];
+                    }
+                }
+                py = group_sum(py, G);
+                if (store && tg == 0) Act<ACT>::store(y_out, ((size_t)b * n + m) * d + chn, py);
             }
-            py = group_sum(py, G);
-            if (scan && tg == 0) Act<ACT>::store(y_out, ((size_t)b * n + m) * d + chn, py);
         }
     }
     return valid ? 0u : HCI_DS_TREE;
