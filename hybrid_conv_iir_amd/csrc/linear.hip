@@ -7,16 +7,18 @@
 // 16 (N), the tiles of one 16-column strip stored consecutively, and inside
 // a tile element [g<4][n<16][e<8] holding W[32 kt + 8 g + e][16 nt + n], so
 // the B operand of v_mfma_f32_16x16x32_bf16 is one contiguous 16-byte load
-// per lane (a contiguous kilobyte per wave).  A workgroup owns one column
-// strip and up to 64 rows; its waves split K into contiguous ranges
-// and stream their part of the strip with non-temporal loads, the rows
-// (A operands) come from L2; the wave partials are summed in a fixed order
-// through LDS, so results do not depend on scheduling.
+// per lane (a contiguous kilobyte per wave).  A workgroup owns CT column
+// strips and up to 64 rows; its waves split K into contiguous ranges and
+// stream their part of the strips with non-temporal loads, one batch of K
+// steps in flight behind the one computed; the rows (A operands) come from
+// L2; the wave partials are summed in a fixed order through LDS, so results
+// do not depend on scheduling.
 #include "hci_internal.h"
 
 namespace hci {
 
 constexpr int kLinMT = 4;              // 16-row tiles per workgroup (64 rows)
+constexpr int kLinT = 512;             // threads per workgroup: 8 waves split K
 
 __device__ __forceinline__ bf16x8 as_bf16x8_u(u32x4 v) {
     bf16x8 r;
@@ -24,16 +26,26 @@ __device__ __forceinline__ bf16x8 as_bf16x8_u(u32x4 v) {
     return r;
 }
 
-// One workgroup: CT column strips (16 columns each) x up to 16 * MT rows; its KW waves
-// split K.  Per K step a wave loads CT weight fragments and one row fragment per 16-row tile,
-// so each row fragment read from L2 feeds CT matrix-core products.
+// K steps per register batch of one wave: BK steps of CT weight fragments and MT row fragments,
+// about 64 registers per batch (two batches are held: the one computed and the one in flight)
+__host__ __device__ constexpr int linear_batch(int CT, int MT) { return 16 / (CT + MT) > 0 ? 16 / (CT + MT) : 1; }
+
+// One workgroup: CT column strips (16 columns each) x up to 16 * MT rows; its KW waves split
+// K into contiguous ranges.  A wave streams its range in batches of BK K steps: the weight
+// fragments (non-temporal, a contiguous kilobyte per wave and strip) and the row fragments (from
+// L2) of batch i + 1 are requested before batch i's matrix-core products run, so a batch's loads
+// are always in flight behind the arithmetic and the wave never waits for a load issued after
+// the ones it needs.  Each row fragment feeds CT products.
 template <int CT, int MT, bool OUT_F32>
-__global__ __launch_bounds__(1024) void k_linear(const uint16_t* __restrict__ x, const u32x4* __restrict__ wp,
-                                                 const uint16_t* __restrict__ res, void* __restrict__ y,
-                                                 int M, int K, int N, int kspw, int parts, int act)
+__global__ __launch_bounds__(kLinT) void k_linear(const uint16_t* __restrict__ x, const u32x4* __restrict__ wp,
+                                                const uint16_t* __restrict__ res, void* __restrict__ y,
+                                                int M, int K, int N, int kspw, int parts, int act)
 {
+    constexpr int BK = linear_batch(CT, MT);
+    constexpr int EPI = (CT * MT * 256 + kLinT - 1) / kLinT;   // epilogue elements per thread
     extern __shared__ float red[];                 // [KW][CT][mts][64][4]
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, KW = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    constexpr int KW = kLinT / 64;
     const int nt0 = blockIdx.x * CT, row0 = blockIdx.y * 16 * MT;
     const int NT = N >> 4, KT = K >> 5;
     const int kt0 = wv * kspw, kt1 = min(KT, kt0 + kspw);
@@ -57,49 +69,67 @@ __global__ __launch_bounds__(1024) void k_linear(const uint16_t* __restrict__ x,
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int row = row0 + 16 * mt + rl;
-        ok[mt] = row < M;
+        ok[mt] = row < M && mt < mts;
         xr[mt] = x + (size_t)(ok[mt] ? row : 0) * K + ko;
     }
-    constexpr int U = CT >= 4 ? 2 : 4;
-    int kt = kt0;
-    for (; kt + U <= kt1; kt += U) {
-        u32x4 b[U][CT];
+    const int Np = N / parts;
+    // the residual of every output this thread writes, requested before the weight stream so it
+    // has long arrived when the epilogue needs it
+    float rv[EPI];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int c = 0; c < CT; ++c)
-                b[u][c] = cok[c] ? __builtin_nontemporal_load(wcol[c] + (size_t)(kt + u) * 64) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            if (mt < mts) {
-                u32x4 a[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    a[u] = ok[mt] ? *(const u32x4*)(xr[mt] + 32 * (kt + u)) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int c = 0; c < CT; ++c)
-                        acc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_u(a[u]), as_bf16x8_u(b[u][c]),
-                                                                             acc[c][mt], 0, 0, 0);
+    for (int j = 0; j < EPI; ++j) {
+        rv[j] = 0.f;
+        const int e = threadIdx.x + kLinT * j;
+        if (res && e < CT * MT * 256) {
+            const int n = e & 15, g = (e >> 4) & 3, r = (e >> 6) & 3, mt = (e >> 8) % MT, c = e / (256 * MT);
+            const int row = row0 + 16 * mt + 4 * g + r;
+            if (mt < mts && row < M && nt0 + c < NT) {
+                const int col = 16 * (nt0 + c) + n;
+                const int p = col / Np;
+                rv[j] = bf2f(res[((size_t)p * M + row) * Np + (col - p * Np)]);
             }
         }
     }
-    for (; kt < kt1; ++kt) {
-        u32x4 b[CT];
+    struct Batch {
+        u32x4 b[BK][CT];
+        u32x4 a[BK][MT];
+    };
+    // K steps past the wave's range load nothing and contribute zero products
+    auto load = [&](Batch& t, int kb) {
 #pragma unroll
-        for (int c = 0; c < CT; ++c)
-            b[c] = cok[c] ? __builtin_nontemporal_load(wcol[c] + (size_t)kt * 64) : u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < BK; ++u) {
+            const bool in = kb + u < kt1;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            if (mt < mts) {
-                const u32x4 a = ok[mt] ? *(const u32x4*)(xr[mt] + 32 * kt) : u32x4{0u, 0u, 0u, 0u};
+            for (int c = 0; c < CT; ++c)
+                t.b[u][c] = in && cok[c] ? __builtin_nontemporal_load(wcol[c] + (size_t)(kb + u) * 64)
+                                         : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int c = 0; c < CT; ++c)
-                    acc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_u(a), as_bf16x8_u(b[c]),
-                                                                         acc[c][mt], 0, 0, 0);
-            }
+            for (int mt = 0; mt < MT; ++mt)
+                t.a[u][mt] = in && ok[mt] ? *(const u32x4*)(xr[mt] + 32 * (kb + u)) : u32x4{0u, 0u, 0u, 0u};
         }
+    };
+    auto compute = [&](const Batch& t, int kb) {
+#pragma unroll
+        for (int u = 0; u < BK; ++u) {
+            if (kb + u >= kt1) break;               // past the wave's range: zero fragments
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                if (mt < mts) {
+#pragma unroll
+                    for (int c = 0; c < CT; ++c)
+                        acc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_u(t.a[u][mt]),
+                                                                             as_bf16x8_u(t.b[u][c]), acc[c][mt], 0, 0, 0);
+                }
+        }
+    };
+    Batch p, q;
+    if (kt0 < kt1) load(p, kt0);
+    for (int kb = kt0; kb < kt1; kb += 2 * BK) {
+        if (kb + BK < kt1) load(q, kb + BK);
+        compute(p, kb);
+        if (kb + BK >= kt1) break;
+        if (kb + 2 * BK < kt1) load(p, kb + 2 * BK);
+        compute(q, kb + BK);
     }
 #pragma unroll
     for (int c = 0; c < CT; ++c)
@@ -109,8 +139,10 @@ __global__ __launch_bounds__(1024) void k_linear(const uint16_t* __restrict__ x,
                 *(f32x4*)(red + ((((size_t)wv * CT + c) * mts + mt) * 64 + lane) * 4) = acc[c][mt];
     __syncthreads();
     // element e -> (c, mt, r, g, n): row 16 mt + 4 g + r, column 16 (nt0 + c) + n (columns fastest)
-    const int Np = N / parts;
-    for (int e = threadIdx.x; e < CT * MT * 256; e += blockDim.x) {
+#pragma unroll
+    for (int j = 0; j < EPI; ++j) {
+        const int e = threadIdx.x + kLinT * j;
+        if (e >= CT * MT * 256) break;
         const int n = e & 15, g = (e >> 4) & 3, r = (e >> 6) & 3, mt = (e >> 8) % MT, c = e / (256 * MT);
         const int row = row0 + 16 * mt + 4 * g + r;
         if (mt >= mts || row >= M || nt0 + c >= NT) continue;
@@ -120,7 +152,7 @@ __global__ __launch_bounds__(1024) void k_linear(const uint16_t* __restrict__ x,
         const int col = 16 * (nt0 + c) + n;
         const int p = col / Np;
         const size_t o = ((size_t)p * M + row) * Np + (col - p * Np);     // [parts][M][N / parts]
-        if (res) v += bf2f(res[o]);
+        if (res) v += rv[j];
         if (act == 1) v = v / (1.0f + __expf(-v));                   // SiLU
         if (OUT_F32) ((float*)y)[o] = v;
         else ((uint16_t*)y)[o] = f2bf(v);
@@ -191,46 +223,37 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(const uint16_t* __restrict__ x
     }
 }
 
-// Launch shape: CT column strips per workgroup and KW waves splitting K, sized so that the
-// grid holds about 4096 waves and the per-wave partials fit in 64 KB of LDS.
+// Launch shape: CT column strips per workgroup (the largest of 4, 3, 2, 1 that still gives every
+// CU a workgroup), up to 64 rows, and eight waves splitting K.
 LinearPlan plan_linear(int M, int K, int N) {
     LinearPlan p{};
     const int mts = (M + 15) / 16 < kLinMT ? (M + 15) / 16 : kLinMT;
     p.mt = mts <= 1 ? 1 : (mts <= 2 ? 2 : 4);
     const int NT = N / 16, KT = K / 32;
-    p.ct = NT >= 768 ? 4 : (NT >= 512 ? 2 : 1);     // keep >= 192 workgroups
-    if (p.mt == 4 && p.ct == 4) p.ct = 2;          // 4 x 4 accumulator tiles would not fit the register budget
-    const long long wgs = (long long)((NT + p.ct - 1) / p.ct) * ((M + 16 * p.mt - 1) / (16 * p.mt));
-    long long kw = (4096 + wgs - 1) / wgs;
-    const int lds_cap = 64 / (p.ct * mts);          // KB of partials per wave: ct * mts
-    if (kw > 16) kw = 16;
-    if (kw > lds_cap) kw = lds_cap;
-    if (kw > KT) kw = KT;
-    if (kw < 1) kw = 1;
-    p.kw = (int)kw;
+    const int cus = device_cu_count();
+    const int gy = (M + 16 * p.mt - 1) / (16 * p.mt);
+    p.ct = 1;
+    for (int ct = p.mt == 4 ? 2 : 4; ct > 1; --ct)
+        if ((long long)((NT + ct - 1) / ct) * gy >= cus) { p.ct = ct; break; }
+    p.kw = kLinT / 64;                             // waves past K's end stream nothing
     p.kspw = (KT + p.kw - 1) / p.kw;
     p.lds = (size_t)p.kw * p.ct * mts * 64 * 4 * sizeof(float);
     p.grid_x = (NT + p.ct - 1) / p.ct;
-    p.grid_y = (M + 16 * p.mt - 1) / (16 * p.mt);
+    p.grid_y = gy;
     return p;
 }
 
-template <int CT, int MT>
-static hipError_t launch_ct(const LinearPlan& p, int M, int K, int N, int parts, const void* x, const void* wp,
-                            const void* res, void* y, bool out_f32, int act, hipStream_t st)
+template <int CT, int MT, bool OUT_F32>
+static hipError_t launch_t(const LinearPlan& p, int M, int K, int N, int parts, const void* x, const void* wp,
+                           const void* res, void* y, int act, hipStream_t st)
 {
-    const void* fn = out_f32 ? (const void*)k_linear<CT, MT, true> : (const void*)k_linear<CT, MT, false>;
+    const void* fn = (const void*)k_linear<CT, MT, OUT_F32>;
     if (p.lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
         if (e != hipSuccess) return e;
     }
-    const dim3 grid(p.grid_x, p.grid_y), block(64 * p.kw);
-    if (out_f32)
-        hipLaunchKernelGGL((k_linear<CT, MT, true>), grid, block, p.lds, st, (const uint16_t*)x, (const u32x4*)wp,
-                           (const uint16_t*)res, y, M, K, N, p.kspw, parts, act);
-    else
-        hipLaunchKernelGGL((k_linear<CT, MT, false>), grid, block, p.lds, st, (const uint16_t*)x, (const u32x4*)wp,
-                           (const uint16_t*)res, y, M, K, N, p.kspw, parts, act);
+    hipLaunchKernelGGL((k_linear<CT, MT, OUT_F32>), dim3(p.grid_x, p.grid_y), dim3(kLinT), p.lds, st,
+                       (const uint16_t*)x, (const u32x4*)wp, (const uint16_t*)res, y, M, K, N, p.kspw, parts, act);
     return hipGetLastError();
 }
 
@@ -238,9 +261,12 @@ hipError_t launch_linear(int M, int K, int N, int parts, const void* x, const vo
                          bool out_f32, hipStream_t st, int act)
 {
     const LinearPlan p = plan_linear(M, K, N);
-#define HCI_LIN_CASE(CT_, MT_) \
-    if (p.ct == CT_ && p.mt == MT_) return launch_ct<CT_, MT_>(p, M, K, N, parts, x, wp, res, y, out_f32, act, st);
+#define HCI_LIN_CASE(CT_, MT_)                                                                                    \
+    if (p.ct == CT_ && p.mt == MT_)                                                                               \
+        return out_f32 ? launch_t<CT_, MT_, true>(p, M, K, N, parts, x, wp, res, y, act, st)                      \
+                       : launch_t<CT_, MT_, false>(p, M, K, N, parts, x, wp, res, y, act, st);
     HCI_LIN_CASE(4, 1) HCI_LIN_CASE(4, 2)
+    HCI_LIN_CASE(3, 1) HCI_LIN_CASE(3, 2)
     HCI_LIN_CASE(2, 1) HCI_LIN_CASE(2, 2) HCI_LIN_CASE(2, 4)
     HCI_LIN_CASE(1, 1) HCI_LIN_CASE(1, 2) HCI_LIN_CASE(1, 4)
 #undef HCI_LIN_CASE
