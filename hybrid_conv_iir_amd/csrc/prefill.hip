@@ -65,9 +65,15 @@ __device__ __forceinline__ float powi(float x, int e) {      // x^e, e >= 0, by 
 }
 
 
+// LDS row pitches of the chunk kernel: f rows and sub-chunk states padded by one float, so that
+// the four sub-chunks a wave serves (rows 16 apart) and the 16 channels of a state row fall in
+// different banks
+constexpr int kFbP = kPfCG + 1;
+constexpr int kSeP = kPfN + 1;
+
 size_t prefill_lds_bytes(int To) {
     const int Wp = pf_taps_padded(To) - 1;
-    return ((size_t)(Wp + kPfC) * kPfCG + (size_t)pf_taps_padded(To) * kPfCG + (size_t)kPfSub * kPfCG * kPfN) * 4;
+    return ((size_t)(Wp + kPfC) * kFbP + (size_t)pf_taps_padded(To) * kPfCG + (size_t)kPfSub * kPfCG * kSeP) * 4;
 }
 
 constexpr int kScCh = 64;                  // channels per scan workgroup (32 lanes x 2 channels)
@@ -123,9 +129,9 @@ __global__ __launch_bounds__(kPfT) void k_prefill_local(
     extern __shared__ float lds[];
     const int TP = pf_taps_padded(To);
     const int W = To - 1, Wp = TP - 1;
-    float* fb = lds;                               // [Wp + C][16]: row r holds fbar[t0 - Wp + r]
-    float* wl = fb + (size_t)(Wp + kPfC) * kPfCG;  // [TP][16], zero past To
-    float* se = wl + (size_t)TP * kPfCG;           // [sub][16 ch][16 poles]
+    float* fb = lds;                               // [Wp + C][kFbP]: row r holds fbar[t0 - Wp + r]
+    float* wl = fb + (size_t)(Wp + kPfC) * kFbP;   // [TP][16], zero past To
+    float* se = wl + (size_t)TP * kPfCG;           // [sub][16 ch][kSeP]: sub-chunk states
 
     const int cg = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
     const int ch0 = cg * kPfCG;
@@ -135,25 +141,56 @@ __global__ __launch_bounds__(kPfT) void k_prefill_local(
     const typename Act<ACT>::T* sw = short_win + (size_t)b * (Ts - 1) * d;
     const float* ow = outer_win + (size_t)b * W * d;
 
-    // short FIR over the chunk and its halo: fbar[t] for t in [t0 - Wp, t0 + C)
-    for (int e = tid; e < (Wp + kPfC) * kPfCG; e += kPfT) {
-        const int r = e / kPfCG, c = e % kPfCG, ch = ch0 + c;
-        const int t = t0 - Wp + r;
-        float v = 0.f;
-        if (ch < d) {
-            if (t < 0) {
-                v = (t >= -W) ? ow[(size_t)(W + t) * d + ch] : 0.f;     // committed outer-FIR inputs
-            } else if (t < T) {
-                for (int j = 0; j < Ts; ++j) {
-                    const int m = t - j;
-                    const float xv = (m >= 0) ? Act<ACT>::load(xb, (size_t)m * d + ch)
-                                              : Act<ACT>::load(sw, (size_t)(Ts - 1 + m) * d + ch);
-                    v = fmaf(w_short[(size_t)j * d + ch], xv, v);
+    // short FIR over the chunk and its halo: fbar[t] for t in [t0 - Wp, t0 + C).  Thread (c, q)
+    // takes the contiguous rows [q R, q R + R) in order, its previous Ts - 1 inputs in registers,
+    // so x is loaded once per row (up to kScTs short taps; longer filters load every tap).
+    {
+        const int rows = Wp + kPfC, R = (rows + kPfSub - 1) / kPfSub;
+        const int c = tid % kPfCG, q = tid / kPfCG, ch = ch0 + c;
+        const bool live = ch < d;
+        const int r0 = q * R, r1 = min(r0 + R, rows);
+        // xbar(m): the short-FIR input at position m (the committed short window before the prompt)
+        auto xbar = [&](int m) -> float {
+            if (!live || m >= T || m < -(Ts - 1)) return 0.f;
+            return m >= 0 ? Act<ACT>::load(xb, (size_t)m * d + ch) : Act<ACT>::load(sw, (size_t)(Ts - 1 + m) * d + ch);
+        };
+        auto emit = [&](int r, int t, float v) {
+            if (live && r >= Wp && t >= T - W && t < T) f_tail[((size_t)b * W + (t - (T - W))) * d + ch] = v;
+            fb[r * kFbP + c] = v;
+        };
+        if (Ts <= kScTs) {
+            float ws_[kScTs], xw[kScTs];               // xw[j] = xbar(t - j) for the running t
+#pragma unroll
+            for (int j = 0; j < kScTs; ++j) ws_[j] = live && j < Ts ? w_short[(size_t)j * d + ch] : 0.f;
+#pragma unroll
+            for (int j = 1; j < kScTs; ++j) xw[j] = j < Ts ? xbar(t0 - Wp + r0 - j) : 0.f;
+            for (int r = r0; r < r1; ++r) {
+                const int t = t0 - Wp + r;
+                xw[0] = xbar(t);
+                float v = 0.f;
+                if (t < 0) {
+                    v = live && t >= -W ? ow[(size_t)(W + t) * d + ch] : 0.f;     // committed outer-FIR inputs
+                } else if (t < T) {
+#pragma unroll
+                    for (int j = 0; j < kScTs; ++j)
+                        if (j < Ts) v = fmaf(ws_[j], xw[j], v);
                 }
-                if (r >= Wp && t >= T - W) f_tail[((size_t)b * W + (t - (T - W))) * d + ch] = v;
+                emit(r, t, v);
+#pragma unroll
+                for (int j = kScTs - 1; j > 0; --j) xw[j] = xw[j - 1];
+            }
+        } else {
+            for (int r = r0; r < r1; ++r) {
+                const int t = t0 - Wp + r;
+                float v = 0.f;
+                if (t < 0) {
+                    v = live && t >= -W ? ow[(size_t)(W + t) * d + ch] : 0.f;
+                } else if (t < T && live) {
+                    for (int j = 0; j < Ts; ++j) v = fmaf(w_short[(size_t)j * d + ch], xbar(t - j), v);
+                }
+                emit(r, t, v);
             }
         }
-        fb[e] = v;
     }
     for (int e = tid; e < TP * kPfCG; e += kPfT) {
         const int j = e / kPfCG, c = e % kPfCG, ch = ch0 + c;
@@ -173,7 +210,7 @@ __global__ __launch_bounds__(kPfT) void k_prefill_local(
         float R[31];
         const int base = Wp + tau0 - jb - 15;      // fb row of R[0]
 #pragma unroll
-        for (int m = 0; m < 31; ++m) R[m] = fb[(base + m) * kPfCG + c];
+        for (int m = 0; m < 31; ++m) R[m] = fb[(base + m) * kFbP + c];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
             const float w = wl[(jb + u) * kPfCG + c];
@@ -208,7 +245,7 @@ __global__ __launch_bounds__(kPfT) void k_prefill_local(
         y[i] = acc;
     }
 #pragma unroll
-    for (int n = 0; n < kPfN; ++n) se[((size_t)sub * kPfCG + c) * kPfN + n] = s[n];
+    for (int n = 0; n < kPfN; ++n) se[((size_t)sub * kPfCG + c) * kSeP + n] = s[n];
     __syncthreads();
 
     // in-chunk carry: thread (channel c2, pole n2) turns the 16 sub-chunk end states into start states
@@ -218,8 +255,8 @@ __global__ __launch_bounds__(kPfT) void k_prefill_local(
         float S = 0.f;
         for (int sb = 0; sb < kPfSub; ++sb) {
             const int len = max(0, min(kPfS, T - (t0 + sb * kPfS)));
-            const float e = se[((size_t)sb * kPfCG + c2) * kPfN + n2];
-            se[((size_t)sb * kPfCG + c2) * kPfN + n2] = S;                 // start state of sub-chunk sb
+            const float e = se[((size_t)sb * kPfCG + c2) * kSeP + n2];
+            se[((size_t)sb * kPfCG + c2) * kSeP + n2] = S;                 // start state of sub-chunk sb
             S = fmaf(powi(l2, len), S, e);
         }
         if (ch2 < d) s_loc[(((size_t)b * nchunks + chunk) * d + ch2) * kPfN + n2] = S;   // chunk end (local)
@@ -230,7 +267,7 @@ __global__ __launch_bounds__(kPfT) void k_prefill_local(
     if (y_loc != nullptr && ch < d) {
         float p[kPfN];
 #pragma unroll
-        for (int n = 0; n < kPfN; ++n) p[n] = se[((size_t)sub * kPfCG + c) * kPfN + n];
+        for (int n = 0; n < kPfN; ++n) p[n] = se[((size_t)sub * kPfCG + c) * kSeP + n];
 #pragma unroll
         for (int i = 0; i < kPfS; ++i) {
             if (i < valid) {
