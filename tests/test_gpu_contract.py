@@ -97,7 +97,9 @@ def test_abandoned_round_can_be_verified_again():
 
 SUSTAINED_ROUNDS = int(os.environ.get("HCI_SUSTAINED_ROUNDS", "256"))
 ATTN_ROUNDS = {0, 1, 63, 127, 255}
-ATTN_HEADS = [0, 17, 42, 63]
+# the first and last eight heads (the first and last items of every phase of the prefix work list,
+# and every residue of the workgroup -> XCD round robin at both ends) and two in between
+ATTN_HEADS = list(range(8)) + [17, 42] + list(range(56, 64))
 
 
 def test_wide131k_sustained_loop_state_equality():

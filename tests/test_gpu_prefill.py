@@ -105,8 +105,12 @@ def test_prefill_odd_channel_groups(want_y):
 
 @pytest.mark.parametrize("want_y", [True, False])
 def test_prefill_long_prompt_262k_channel_sample(want_y):
+    """A channel sample that covers every XCD at both ends of the channel range: workgroups go to
+    the eight XCDs round robin, channel group fastest (16-channel groups on the output path, 64 on
+    the state path), so the first and last eight groups of either size land on every XCD."""
     cfg = synth.scaled(synth.CONFIGS["long262k"], kv_lens=(0,))
-    chans = np.array([0, 1, 63, 64, 777, 2048, 4095])
+    ends = [16 * k for k in range(8)] + [64 * k + 63 for k in range(8)]
+    chans = np.unique(np.array([0, 1, 63, 64, 777, 2048] + ends + [cfg.d - 1 - c for c in ends]))
     _check(cfg, 262144, L0=0, chans=chans, want_y=want_y)
 
 
