@@ -165,3 +165,31 @@ def test_prefill_then_verify_round():
     assert_f32_close(dv.to_host(blk.s)[0, 0], ref["s"], "s after prefill")
     assert_out_close(cfg, dv.to_host(blk.y)[0, 0], ref["y"], "y after prefill")
     assert_out_close(cfg, dv.to_host(blk.o)[0, 0], ref["o"], "o after prefill")
+
+
+def test_full_width_prefill_then_verify_round():
+    """The 8192-token workload's layer (d = 4096, 32 x 128 heads) started from the state a prefill
+    of an 8192-token prompt leaves instead of a drawn one: verify against the oracle's prefill."""
+    cfg = synth.scaled(synth.CONFIGS["mid8k"], kv_lens=(0,), mode="greedy")
+    T = 8192
+    params, small, lay, st, _ = _layer_state(cfg, 0, T + 64)
+    pr = synth.prompt(cfg, T, 6, device="cuda")
+    say("full-width prefill then verify")
+    _run_prefill(lay, st, cfg, T, 0, pr, want_y=False)
+    tables = synth.make_tables(cfg)
+    ri = synth.round_inputs(cfg, synth.anchors(cfg))
+    bn = synth.gather_block(cfg, tables, ri["tokens"])
+    blk = dv.DeviceBlock(lay, 1, 1, cfg.gamma)
+    blk.set_inputs(bn["x"], bn["q"], bn["k"], bn["v"])
+    dv.verify(lay, st, blk, T)
+    torch.cuda.synchronize()
+    st_o = oracle.SeqState(small["short_win"][0], small["outer_win"][0], small["iir"][0],
+                           [np.zeros((cfg.heads, 0, cfg.head_dim))], [np.zeros((cfg.heads, 0, cfg.head_dim))])
+    lay_o = oracle.Layer.from_dict(params)
+    new, _ = oracle.prefill_state(lay_o, st_o, dv.to_host(pr["x"][0]), dv.to_host(pr["k"][0]), dv.to_host(pr["v"][0]),
+                                  long=True)
+    ref = oracle.verify_block(lay_o, new, bn["x"][0, 0], bn["q"][0, 0], bn["k"][0, 0], bn["v"][0, 0])
+    assert_f32_close(dv.to_host(blk.f)[0, 0], ref["f"], "f after prefill")
+    assert_f32_close(dv.to_host(blk.s)[0, 0], ref["s"], "s after prefill")
+    assert_out_close(cfg, dv.to_host(blk.y)[0, 0], ref["y"], "y after prefill")
+    assert_out_close(cfg, dv.to_host(blk.o)[0, 0], ref["o"], "o after prefill")
