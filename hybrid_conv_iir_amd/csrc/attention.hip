@@ -146,8 +146,10 @@ __global__ __launch_bounds__(64) void k_attn_prefix_f32(
 // phase p: it counts the phase's items of every sequence (the per-phase totals meet in LDS),
 // then writes each sequence's base and count.  Runs for every verify, also when no sequence
 // has a prefix (the finish kernel then reads an empty list, never a previous call's).
+// first_ticket: the number of streaming workgroups (workgroup i runs item i first, so the queue
+// hands out items from there on)
 __global__ __launch_bounds__(64) void k_verify_setup(int32_t* ws, const int32_t* kv_len, uint32_t* status,
-                                                     int nb, int H, int lim, int resident, int nq)
+                                                     int nb, int H, int lim, int resident, int nq, int first_ticket)
 {
     __shared__ long long cnt[kPhaseMax];
     int32_t* table = (int32_t*)((char*)ws + kWsTableOff);
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(64) void k_verify_setup(int32_t* ws, const int32_t*
     if (p == 0) {
         long long total = 0;
         for (int q = 0; q < kPhaseMax; ++q) total += cnt[q];
-        ws[kWsTicket] = 0;
+        ws[kWsTicket] = first_ticket;
         ws[kWsTotal] = (int32_t)total;
         ws[kWsC0] = w.c0;
         ws[kWsNp] = w.np;
@@ -244,8 +246,10 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
     hipError_t e = mark(0);
     if (e != hipSuccess) return e;
 
+    const int stream_blocks = plan.items_cap <= 0 || L->act_dtype != HCI_BF16 ? 0
+                              : (plan.items_cap < plan.resident ? plan.items_cap : plan.resident);
     hipLaunchKernelGGL(k_verify_setup, dim3(1), dim3(64), 0, st, (int32_t*)ws, S->kv_len, S->status, nb, H,
-                       plan.kv_lim, plan.resident, nq);
+                       plan.kv_lim, plan.resident, nq, stream_blocks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(1)) != hipSuccess) return e;
     if (plan.items_cap > 0) {
@@ -257,8 +261,7 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
             A.H = H; A.kv_cap = S->kv_cap; A.kv_lim = plan.kv_lim; A.nq = nq; A.nb = nb; A.resident = plan.resident;
             A.scale_log2 = scale_log2;
             const int nqt = (nq + 15) / 16;
-            const int blocks = plan.items_cap < plan.resident ? plan.items_cap : plan.resident;
-            e = launch_stream_one(A, DH, nqt, blocks, st);
+            e = launch_stream_one(A, DH, nqt, stream_blocks, st);
             if (e != hipSuccess) return e;
         } else {
             hipLaunchKernelGGL(k_attn_prefix_f32, dim3(plan.items_cap), dim3(64), 0, st,

@@ -1,5 +1,6 @@
-// Prefix streaming: one persistent workgroup per CU takes prefix items from
-// the job queue; its four waves share an item's 32-key tiles round-robin
+// Prefix streaming: one persistent workgroup per CU runs prefix item
+// blockIdx.x and then takes items from the job queue; its four waves share
+// an item's 32-key tiles round-robin
 // (wave w takes tiles t0 + w, t0 + w + 4, ..., so at any moment the
 // workgroup reads four adjacent tiles, a contiguous 32 KB of keys and of
 // values), each streamed with non-temporal 16-byte loads and the next two
@@ -212,14 +213,15 @@ __device__ __forceinline__ void prefix_item(const StreamArgs& A, int b, int h, i
     }
 }
 
-// Persistent workgroup: prefix items from the queue.
+// Persistent workgroup: its own index is its first item (no queue round trip before the first
+// loads; the set-up kernel starts the queue past the grid), then items from the queue.
 template <int DH, int NQT>
 __global__ __launch_bounds__(kRoleT, kStreamSlots) void k_verify_stream(StreamArgs A)
 {
     __shared__ uint4 lds_pool[stream_pool_uint4<DH, NQT>()];
     __shared__ unsigned s_ticket;
     const WorkTable wt = read_worktable(A.ws, A.nb, A.H, A.kv_lim);
-    if (threadIdx.x == 0) s_ticket = atomicAdd(A.ticket, 1u);
+    if (threadIdx.x == 0) s_ticket = blockIdx.x;
     __syncthreads();
     for (;;) {
         const unsigned t = s_ticket;
