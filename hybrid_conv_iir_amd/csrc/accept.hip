@@ -43,6 +43,7 @@ struct AccScratch {
     double zh[kAccRows + 1];       // recursive: residual totals z^(0..r)
     int zapp[kAccRows];            // recursive: whether rejection i changed the residual
     int badrow[kAccRows];          // greedy: row i holds NaN / +Inf or no finite entry
+    double uu[kAccRows];           // sampling: the block's uniforms, staged at the start
 };
 
 // A row's softmax statistics are usable when its sum is >= 1 (the maximal entry contributes
@@ -160,8 +161,10 @@ __device__ void wave_row_argmax(const float* z, int V, int lane, int& arg, doubl
 // softmax(z / T) statistics of one row by ONE wave: (max of z/T, sum of exp(z/T - max)) in fp64.
 // A row of at most 64 kLaneBatch entries is loaded once (the same values in the same order as
 // the two-pass form); the lane holding entry tok (if 0 <= tok < V) stores it to *ztok.
+// ecache (rows of at most 64 kLaneBatch entries only; may be null): receives exp(z_j / T - max)
+// for every entry j < V, the values the sum adds, for a later draw from the same row.
 __device__ void wave_row_stats(const float* z, int V, double T, int lane, double& mx, double& sum,
-                               int tok = -1, float* ztok = nullptr) {
+                               int tok = -1, float* ztok = nullptr, double* ecache = nullptr) {
     if (V <= 64 * kLaneBatch) {
         float v[kLaneBatch];
 #pragma unroll
@@ -181,7 +184,11 @@ __device__ void wave_row_stats(const float* z, int V, double T, int lane, double
         double s = 0.0;
 #pragma unroll
         for (int e = 0; e < kLaneBatch; ++e)
-            if (e * 64 + lane < V) s += exp(xs[e] - m);
+            if (e * 64 + lane < V) {
+                const double ex = exp(xs[e] - m);
+                s += ex;
+                if (ecache) ecache[e * 64 + lane] = ex;
+            }
         mx = m;
         sum = wave_sum_f64(s);
         return;
@@ -491,6 +498,9 @@ __global__ __launch_bounds__(kAccT) void k_accept(
     int32_t* __restrict__ best, double* __restrict__ margin_out, uint32_t* __restrict__ status)
 {
     __shared__ AccScratch sh;
+    // rows of at most 64 kLaneBatch tokens: the exp terms of the four rows a ratio step reads
+    // (target rows m0 - 1, m0; draft rows m0 - 1, m0), kept for the final draw
+    __shared__ double ecache[kAccW][64 * kLaneBatch];
     const int P = gamma + 1;
     {
         const size_t blk = blockIdx.x;
@@ -527,18 +537,26 @@ __global__ __launch_bounds__(kAccT) void k_accept(
             const float* zd_c = zd + blk * gamma * V;
             const double* u = uni + blk * P;
             // ratio tests two drafts at a time: waves 0,1 take target rows m-1, waves 2,3 draft rows m-1
+            const bool cached = V <= 64 * kLaneBatch;
+            // the uniforms are staged before the first row statistics (whose barrier publishes
+            // them), so neither the ratio tests nor the draw waits on a global load
+            if ((int)threadIdx.x < P) sh.uu[threadIdx.x] = u[threadIdx.x];
             k = gamma;
             bool done = false;
+            int m_last = 1;                    // m0 of the last ratio step (its rows are in ecache)
             for (int m0 = 1; m0 <= gamma && !done; m0 += kAccW / 2) {
                 const int m = m0 + (wv & 1);
+                m_last = m0;
                 if (m <= gamma) {
                     double mx, sum;
                     const int tok = dr[m - 1];
                     if (wv < 2) {
-                        wave_row_stats(zt_c + (size_t)(m - 1) * V, V, T, lane, mx, sum, tok, &sh.ztok[m - 1]);
+                        wave_row_stats(zt_c + (size_t)(m - 1) * V, V, T, lane, mx, sum, tok, &sh.ztok[m - 1],
+                                       cached ? ecache[wv] : nullptr);
                         if (lane == 0) { sh.pm[m - 1] = mx; sh.ps[m - 1] = sum; }
                     } else {
-                        wave_row_stats(zd_c + (size_t)(m - 1) * V, V, T, lane, mx, sum, tok, &sh.dtok[m - 1]);
+                        wave_row_stats(zd_c + (size_t)(m - 1) * V, V, T, lane, mx, sum, tok, &sh.dtok[m - 1],
+                                       cached ? ecache[wv] : nullptr);
                         if (lane == 0) { sh.qm[m - 1] = mx; sh.qs[m - 1] = sum; }
                     }
                 }
@@ -548,7 +566,7 @@ __global__ __launch_bounds__(kAccT) void k_accept(
                     if (t < 0 || t >= V) { k = mm - 1; done = true; flags |= HCI_DS_DRAFT_ID; break; }
                     const double p_t = exp(over_T((double)sh.ztok[mm - 1], T) - sh.pm[mm - 1]) / sh.ps[mm - 1];
                     const double q_t = exp(over_T((double)sh.dtok[mm - 1], T) - sh.qm[mm - 1]) / sh.qs[mm - 1];
-                    const double lhs = u[mm - 1] * q_t;
+                    const double lhs = sh.uu[mm - 1] * q_t;
                     margin = fmin(margin, fabs(lhs - p_t) / fmax(p_t, 1e-300));
                     if (!(lhs < p_t)) { k = mm - 1; done = true; break; }
                 }
@@ -556,11 +574,16 @@ __global__ __launch_bounds__(kAccT) void k_accept(
             if (k == gamma) {          // every draft kept: the bonus row p_gamma is still needed
                 if (wv == 0) {
                     double mx, sum;
-                    wave_row_stats(zt_c + (size_t)gamma * V, V, T, lane, mx, sum);
+                    wave_row_stats(zt_c + (size_t)gamma * V, V, T, lane, mx, sum, -1, nullptr,
+                                   cached ? ecache[0] : nullptr);
                     if (lane == 0) { sh.pm[gamma] = mx; sh.ps[gamma] = sum; }
                 }
                 __syncthreads();
             }
+            // the cached exp terms of row k: target row k in slot k - (m_last - 1), draft row k two
+            // slots further (the bonus row p_gamma in slot 0)
+            const double* ct = cached ? ecache[k == gamma ? 0 : k - (m_last - 1)] : nullptr;
+            const double* cq = cached && k < gamma ? ecache[2 + k - (m_last - 1)] : nullptr;
             // the rows the decision used: target rows 0..k, draft rows 0..min(k, gamma - 1)
             for (int i = 0; i <= k; ++i) bad |= !row_finite(sh.ps[i]) || (i < gamma && !row_finite(sh.qs[i]));
             // weights of the final draw: residual after a rejection, else p_gamma
@@ -570,8 +593,8 @@ __global__ __launch_bounds__(kAccT) void k_accept(
             const float* prow = zt_c + (size_t)k * V;
             const float* qrow = zd_c + (size_t)k * V;
             auto weight = [&](int j) {
-                const double p = exp(over_T((double)prow[j], T) - pm) / ps;
-                return resid ? fmax(0.0, p - exp(over_T((double)qrow[j], T) - qm) / qs) : p;
+                const double p = (ct ? ct[j] : exp(over_T((double)prow[j], T) - pm)) / ps;
+                return resid ? fmax(0.0, p - (cq ? cq[j] : exp(over_T((double)qrow[j], T) - qm)) / qs) : p;
             };
             const int per = (V + kAccT - 1) / kAccT;
             const int j0 = min((int)threadIdx.x * per, V), j1 = min(j0 + per, V);
@@ -584,18 +607,18 @@ __global__ __launch_bounds__(kAccT) void k_accept(
                 double wc[kDrawCache];
 #pragma unroll
                 for (int uu = 0; uu < kDrawCache; ++uu) wc[uu] = j0 + uu < j1 ? weight(j0 + uu) : 0.0;
-                draw_token_cached(wc, V, u[gamma], sh, tok, m2, &tot);
+                draw_token_cached(wc, V, sh.uu[gamma], sh, tok, m2, &tot);
                 if (resid && !(tot > 0.0)) {
                     resid = false;
 #pragma unroll
                     for (int uu = 0; uu < kDrawCache; ++uu) wc[uu] = j0 + uu < j1 ? weight(j0 + uu) : 0.0;
-                    draw_token_cached(wc, V, u[gamma], sh, tok, m2);
+                    draw_token_cached(wc, V, sh.uu[gamma], sh, tok, m2);
                 }
             } else {
-                draw_token(weight, V, u[gamma], sh, tok, m2, &tot);
+                draw_token(weight, V, sh.uu[gamma], sh, tok, m2, &tot);
                 if (resid && !(tot > 0.0)) {
                     resid = false;
-                    draw_token(weight, V, u[gamma], sh, tok, m2);
+                    draw_token(weight, V, sh.uu[gamma], sh, tok, m2);
                 }
             }
             nxt = tok;
