@@ -267,6 +267,7 @@ int hci_prefill(const hci_layer* L, const hci_state* S, int nb, int T, int max_k
     const PrefillPlan plan = plan_prefill(L, nb, T, y != nullptr);
     if (plan.state_only ? prefill_state_lds_bytes(L) > 65536 : prefill_lds_bytes(L->taps_outer) > kMaxLds)
         return HCI_EUNSUPPORTED;
+    if (plan.y_mfma && prefill_y_lds_bytes(L->taps_outer) > kMaxLds) return HCI_EUNSUPPORTED;
     if (plan.nchunks > 65535) return HCI_EUNSUPPORTED;
     if (!ws || ws_bytes < plan.bytes || !aligned(ws, 256)) return HCI_EWORKSPACE;
     if (launch_prefill(L, S, nb, T, max_kv_len, x, k, v, y, plan, ws, stream) != hipSuccess) return HCI_EDEVICE;

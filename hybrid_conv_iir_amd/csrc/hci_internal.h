@@ -140,7 +140,8 @@ hipError_t launch_len_add(const hci_state* S, int nb, int add, int lim, hipStrea
 
 // prefill of a prompt into the committed state
 struct PrefillPlan {
-    bool state_only;             // folded FIR/IIR path (no outputs y; T >= To)
+    bool state_only;             // folded FIR/IIR path for the state (T >= To)
+    bool y_mfma;                 // outputs y by the matrix-core pass (bf16), next to the state path
     int sub_len, chunk_len;      // state path: positions per scan thread and per chunk
     int nchunks;                 // chunks (256 positions on the output path, chunk_len on the state path)
     size_t s_elems, ftail_elems, yloc_elems;
@@ -150,6 +151,7 @@ PrefillPlan plan_prefill(const hci_layer* L, int nb, int T, bool want_y);
 size_t prefill_lds_bytes(int To);
 bool prefill_state_path(const hci_layer* L, int T, bool want_y);
 size_t prefill_state_lds_bytes(const hci_layer* L);
+size_t prefill_y_lds_bytes(int To);
 hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T, int lim, const void* x,
                           const void* k, const void* v, void* y, const PrefillPlan& plan, void* ws, hipStream_t st);
 

@@ -24,6 +24,11 @@
 //   k_kv_pack        K/V rows appended in the tiled cache layout, then
 //   k_len_add        kv_len += T.
 //
+// With bf16 activations the outputs y take a third route, k_prefill_y (one
+// pass over the prompt per 16 channels on the matrix cores, described with the
+// kernel), and the state the folded path below; the chunked kernels above
+// serve fp32 layers and the shapes k_prefill_y does not cover.
+//
 // When only the state is wanted (no per-position outputs y) the outer FIR
 // is folded into the IIR instead.  Both are linear and time-invariant per
 // channel, so the state after the prompt is a fixed linear functional of
@@ -42,6 +47,7 @@
 //   k_prefill_state  per (16 channels): chunk carries -> V, one pass over the
 //                    taps for H, B and A, the new IIR state and both windows
 #include "hci_internal.h"
+#include "wave_ops.h"
 
 namespace hci {
 
@@ -82,8 +88,12 @@ constexpr int kScTs = 4;                   // short taps held in registers on th
 constexpr int kScU = 8;                    // positions loaded ahead per step
 constexpr int kScPad = kPfN + 1;           // LDS row pitch of the sub-chunk states
 
+bool prefill_y_mfma(const hci_layer* L, int T);
+
+// the folded state path: the state only, or the state next to the outputs y on the matrix cores
 bool prefill_state_path(const hci_layer* L, int T, bool want_y) {
-    return !want_y && T >= L->taps_outer && L->taps_short <= kScTs && L->d % 2 == 0 && L->poles <= kPfN;
+    return (!want_y || prefill_y_mfma(L, T)) && T >= L->taps_outer && L->taps_short <= kScTs && L->d % 2 == 0 &&
+           L->poles <= kPfN;
 }
 
 size_t prefill_state_lds_bytes(const hci_layer* L) {
@@ -96,6 +106,7 @@ PrefillPlan plan_prefill(const hci_layer* L, int nb, int T, bool want_y) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     if (prefill_state_path(L, T, want_y)) {
         p.state_only = true;
+        p.y_mfma = want_y;
         const int M = T - L->taps_outer + 1;
         const long long ncg = (L->d + kScCh - 1) / kScCh;
         long long want = (4096 + ncg * nb - 1) / (ncg * nb);
@@ -595,6 +606,360 @@ __global__ __launch_bounds__(256) void k_prefill_state(
     }
 }
 
+// ------------------------------------------------------------ outputs y on the matrix cores
+//
+// With bf16 activations the prompt's outputs y come from one pass per 16
+// channels over the whole prompt, in tiles of 256 positions (16 blocks of 16),
+// the IIR state carried from tile to tile in registers; the committed state
+// itself is left to the folded state path, which runs afterwards.  Per channel
+// and tile (block n, position i inside a block, pole p):
+//   g[16n+i] = sum_k Wt[i][k] F[k][n],  F[k][n] = f[t0+16n-Wh+k],  Wt[i][k] = w[i+Wh-k]
+//              (the outer FIR as a Toeplitz product over a window of Wh+16 inputs)
+//   E[p][n]  = sum_m beta_p lam_p^(15-m) g[16n+m]      block n's inputs, at its end
+//   sig_n    = lam^(16n) sig_0 + sum_{k<n} lam^(16(n-1-k)) E[.][k]   state before block n
+//   y[16n+i] = sum_{m<=i} h[i-m] g[16n+m] + sum_p c_p lam_p^(i+1) sig_n[p],
+//              h[k] = sum_p c_p beta_p lam_p^k
+// The products run on v_mfma (16x16x32 bf16 for the FIR, 16x16x16 bf16 for the
+// others) with every fp32 operand split into two bf16 terms (hi + lo) and the
+// lo x lo term dropped, so each sum carries a relative error of about 2^-14 of
+// the magnitudes of its terms before y is rounded to bf16.  In the accumulator
+// layout lane (q, n) holds rows 4q..4q+3 of column n, which is also the B-operand
+// layout of the 16x16x16 products: g and the states feed the next product in
+// place, and the scan over the 16 blocks runs across the 16 lanes of a row.
+
+constexpr int kYC = 16;                    // channels per workgroup
+constexpr int kYW = 8;                     // waves; wave w owns channels 2w and 2w + 1
+constexpr int kYT = 64 * kYW;
+constexpr int kYTile = 256;                // positions per tile
+constexpr int kYH = kScTs - 1;             // x rows kept before the tile (short FIR history)
+constexpr int kYKs = 5;                    // FIR window steps of 32 inputs at most (To <= 144)
+constexpr int kYysP = kYTile + 4;          // LDS pitch of the staged outputs (floats)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__host__ __device__ inline int y_halo(int To) { return (To - 1 + 7) / 8 * 8; }     // Wh: >= To - 1, multiple of 8
+__host__ __device__ inline int y_ksteps(int To) { return (y_halo(To) + 16 + 31) / 32; }
+__host__ __device__ inline int y_ring(int To) { return y_halo(To) + kYTile; }       // f ring length (positions)
+// ring row pitch: 16 bytes past the length, so that the 16 channel rows start in different banks
+__host__ __device__ inline int y_ring_pitch(int To) { return y_ring(To) + 8; }
+
+size_t prefill_y_lds_bytes(int To) {
+    return (size_t)(kYH + kYTile) * kYC * 2 + (size_t)2 * kYC * y_ring_pitch(To) * 2 + (size_t)kYC * kYysP * 4;
+}
+
+bool prefill_y_mfma(const hci_layer* L, int T) {
+    return L->act_dtype == HCI_BF16 && L->d % 8 == 0 && y_ksteps(L->taps_outer) <= kYKs && T >= L->taps_outer &&
+           L->taps_short <= kScTs && L->poles <= kPfN;
+}
+
+__device__ __forceinline__ double powi_d(double x, int e) {
+    double r = 1.0;
+    while (e > 0) {
+        if (e & 1) r *= x;
+        x *= x;
+        e >>= 1;
+    }
+    return r;
+}
+
+// v = hi + lo in bf16 (round to nearest even twice)
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+    hi = f2bf(v);
+    lo = f2bf(v - bf2f(hi));
+}
+__device__ __forceinline__ void split_bf16_d(double v, uint16_t& hi, uint16_t& lo) {
+    hi = f2bf((float)v);
+    lo = f2bf((float)(v - (double)bf2f(hi)));
+}
+
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int KS>
+__global__ __launch_bounds__(kYT) void k_prefill_y(
+    const float* __restrict__ w_short, const float* __restrict__ w_outer, const float* __restrict__ lam,
+    const float* __restrict__ beta, const float* __restrict__ cc, const uint16_t* __restrict__ short_win,
+    const float* __restrict__ outer_win, const float* __restrict__ iir, const uint16_t* __restrict__ x,
+    uint16_t* __restrict__ y, int d, int Ts, int To, int N, int T, int ncg, int nb)
+{
+    extern __shared__ __align__(16) unsigned char ylds[];
+    const int Wh = y_halo(To), RL = y_ring(To), RP = y_ring_pitch(To), W = To - 1;
+    uint16_t* xs = (uint16_t*)ylds;                        // [kYH + 256][16]: x at t0 - kYH ..
+    uint16_t* fh = xs + (kYH + kYTile) * kYC;              // [16][RP]: f, bf16 hi terms, ring
+    uint16_t* fl = fh + kYC * RP;                          // [16][RP]: lo terms
+    float* ys = (float*)(fl + kYC * RP);                   // [16][kYysP]: outputs of the tile
+
+    // neighbouring channel groups on one XCD (workgroups are dealt to the 8 XCDs in turn), so
+    // that the 32-byte row pieces of x and y of adjacent groups meet in one L2
+    const int total = ncg * nb;
+    int wg = blockIdx.x;
+    if (total % 8 == 0) wg = (wg % 8) * (total / 8) + wg / 8;
+    const int cg = wg % ncg, b = wg / ncg, ch0 = cg * kYC;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int li = lane & 15, lq = lane >> 4;
+    const uint16_t* xb = x + (size_t)b * T * d;
+    uint16_t* yb = y + (size_t)b * T * d;
+
+    // ---- per-channel operands of the wave's two channels
+    bf16x8 Ah[2][KS], Al[2][KS];                   // Toeplitz FIR operand: lane (i, q) holds Wt[i][32s + 8q + e]
+    s16x4 Bh[2], Bl[2], Hh[2], Hl[2], Chh[2], Cl[2];
+    f32x4 L1[2], Ln[2], sig[2];                    // lane (q, n): poles 4q + r
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int ch = ch0 + 2 * wv + u;
+        const bool live = ch < d;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            uint16_t h8[8], l8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = li + Wh - (32 * s + 8 * lq + e);
+                const float w = (live && j >= 0 && j < To) ? w_outer[(size_t)j * d + ch] : 0.f;
+                split_bf16(w, h8[e], l8[e]);
+            }
+            uint4 ph, pl;
+            ph.x = h8[0] | ((uint32_t)h8[1] << 16); ph.y = h8[2] | ((uint32_t)h8[3] << 16);
+            ph.z = h8[4] | ((uint32_t)h8[5] << 16); ph.w = h8[6] | ((uint32_t)h8[7] << 16);
+            pl.x = l8[0] | ((uint32_t)l8[1] << 16); pl.y = l8[2] | ((uint32_t)l8[3] << 16);
+            pl.z = l8[4] | ((uint32_t)l8[5] << 16); pl.w = l8[6] | ((uint32_t)l8[7] << 16);
+            Ah[u][s] = __builtin_bit_cast(bf16x8, ph);
+            Al[u][s] = __builtin_bit_cast(bf16x8, pl);
+        }
+        const float* lp = lam + (size_t)ch * N;
+        const float* bp = beta + (size_t)ch * N;
+        const float* cp = cc + (size_t)ch * N;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = 4 * lq + e;              // operand column
+            double bl = 0.0, hv = 0.0, cv = 0.0;
+            if (live && li < N) bl = (double)bp[li] * powi_d(lp[li], 15 - m);           // [p = li][m]
+            if (live && m <= li)                                                         // [i = li][m]
+                for (int p = 0; p < N; ++p) hv += (double)cp[p] * bp[p] * powi_d(lp[p], li - m);
+            if (live && m < N) cv = (double)cp[m] * powi_d(lp[m], li + 1);             // [i = li][p = m]
+            uint16_t h, l;
+            split_bf16_d(bl, h, l); Bh[u][e] = (short)h; Bl[u][e] = (short)l;
+            split_bf16_d(hv, h, l); Hh[u][e] = (short)h; Hl[u][e] = (short)l;
+            split_bf16_d(cv, h, l); Chh[u][e] = (short)h; Cl[u][e] = (short)l;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int p = 4 * lq + r;
+            const bool ok = live && p < N;
+            const double l = ok ? (double)lp[p] : 0.0;
+            L1[u][r] = (float)powi_d(l, 16);
+            Ln[u][r] = (float)powi_d(l, 16 * li);
+            sig[u][r] = ok ? iir[((size_t)b * d + ch) * N + p] : 0.f;
+        }
+    }
+
+    // ---- LDS: x history (the committed short window before the prompt), f ring (the committed
+    // outer window at positions -W .. -1, zeros elsewhere); ring slot of position t: (t + Wh) mod RL
+    for (int e = tid; e < kYH * kYC; e += kYT) {
+        const int t = e / kYC - kYH, ch = ch0 + e % kYC;
+        xs[e] = (ch < d && t >= -(Ts - 1)) ? short_win[((size_t)b * (Ts - 1) + (Ts - 1 + t)) * d + ch] : (uint16_t)0;
+    }
+    for (int e = tid; e < kYC * RP; e += kYT) {
+        const int t = e % RP - Wh, ch = ch0 + e / RP;
+        const float v = (ch < d && t < 0 && t >= -W) ? outer_win[((size_t)b * W + (W + t)) * d + ch] : 0.f;
+        uint16_t h, l;
+        split_bf16(v, h, l);
+        fh[e] = h;
+        fl[e] = l;
+    }
+
+    // x rows of a tile: thread (row, half) loads channels 8 half .. 8 half + 7 of one row.  Loads
+    // and output stores run unconditionally, so that the compiler can count them in flight: a
+    // row past the prompt reads row T - 1 (x there only reaches outputs past the prompt: both
+    // filters are causal) and writes row T - 1's outputs, a half past d takes half 0 (same data,
+    // same values written twice; d % 8 == 0, so a half lies wholly inside or outside)
+    const int xrow = tid >> 1, xhalf = (ch0 + 8 * (tid & 1) < d) ? (tid & 1) : 0;
+    auto load_x = [&](int t0) -> uint4 {
+        const int t = min(t0 + xrow, T - 1);
+        return load_nt((const uint4*)(xb + (size_t)t * d + ch0 + 8 * xhalf));
+    };
+    *(uint4*)(xs + (kYH + xrow) * kYC + 8 * xhalf) = load_x(0);
+    // tiles t + 1 and t + 2 in flight in two register sets with fixed roles (a copy from one
+    // set to the other would wait for the load)
+    uint4 xq1 = load_x(kYTile), xq2 = load_x(2 * kYTile);
+
+    // short FIR: thread (ac, ablk) makes positions 8 ablk .. 8 ablk + 7 of channel ac
+    const int ac = tid & 15, ablk = tid >> 4;
+    float wsr[kScTs];
+#pragma unroll
+    for (int j = 0; j < kScTs; ++j) wsr[j] = (ch0 + ac < d && j < Ts) ? w_short[(size_t)j * d + ch0 + ac] : 0.f;
+
+    const int ntiles = (T + kYTile - 1) / kYTile;
+    int base = 0;                                  // t0 mod RL
+    // ring slot of window row 8 lq of block li in the current tile, reduced mod RL
+    int rs = 16 * li + 8 * lq;
+    if (rs >= RL) rs -= RL;                        // RL >= 256, rs < 264
+    // body of one tile; xn holds the next tile's x rows and is refilled with the rows 3 tiles ahead
+    auto tile_step = [&](int tile, uint4& xn) {
+        const int t0 = tile * kYTile;
+        // A: f of the tile into the ring, split into bf16 terms
+        {
+            float xv[8 + kYH];
+#pragma unroll
+            for (int k = 0; k < 8 + kYH; ++k) xv[k] = bf2f(xs[(8 * ablk + k) * kYC + ac]);
+            uint16_t h8[8], l8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float f = 0.f;
+#pragma unroll
+                for (int j = 0; j < kScTs; ++j) f = fmaf(wsr[j], xv[kYH + e - j], f);
+                split_bf16(f, h8[e], l8[e]);
+            }
+            int sl = base + Wh + 8 * ablk;
+            if (sl >= RL) sl -= RL;
+            uint4 ph, pl;
+            ph.x = h8[0] | ((uint32_t)h8[1] << 16); ph.y = h8[2] | ((uint32_t)h8[3] << 16);
+            ph.z = h8[4] | ((uint32_t)h8[5] << 16); ph.w = h8[6] | ((uint32_t)h8[7] << 16);
+            pl.x = l8[0] | ((uint32_t)l8[1] << 16); pl.y = l8[2] | ((uint32_t)l8[3] << 16);
+            pl.z = l8[4] | ((uint32_t)l8[5] << 16); pl.w = l8[6] | ((uint32_t)l8[7] << 16);
+            *(uint4*)(fh + ac * RP + sl) = ph;
+            *(uint4*)(fl + ac * RP + sl) = pl;
+        }
+        __syncthreads();
+
+        // B: the wave's two channels through the four products
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int c = 2 * wv + u;
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
+            // window rows past Wh + 15 meet only zero taps; they read ring slots of other positions,
+            // finite unless an earlier input was not (and then every later output is not either)
+            int sl = rs;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const uint4 vh = *(const uint4*)(fh + c * RP + sl);
+                const uint4 vl = *(const uint4*)(fl + c * RP + sl);
+                sl += 32;
+                if (sl >= RL) sl -= RL;
+                const bf16x8 bh = __builtin_bit_cast(bf16x8, vh), bl = __builtin_bit_cast(bf16x8, vl);
+                a1 = mfma32(Ah[u][s], bl, a1);
+                a2 = mfma32(Al[u][s], bh, a2);
+                a0 = mfma32(Ah[u][s], bh, a0);
+            }
+            s16x4 gh, gl;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint16_t h, l;
+                split_bf16(a0[r] + (a1[r] + a2[r]), h, l);
+                gh[r] = (short)h;
+                gl[r] = (short)l;
+            }
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            f32x4 E = mfma16(Bh[u], gl, z);
+            E = mfma16(Bl[u], gh, E);
+            E = mfma16(Bh[u], gh, E);
+            // inclusive scan over the blocks: I_n = sum_{k<=n} lam^(16(n-k)) E_k
+            f32x4 I = E, Lp = L1[u];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) I[r] = fmaf(Lp[r], dpp_f32<kRowShr1>(I[r]), I[r]);
+            Lp *= Lp;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) I[r] = fmaf(Lp[r], dpp_f32<kRowShr2>(I[r]), I[r]);
+            Lp *= Lp;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) I[r] = fmaf(Lp[r], dpp_f32<kRowShr4>(I[r]), I[r]);
+            Lp *= Lp;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) I[r] = fmaf(Lp[r], dpp_f32<kRowShr8>(I[r]), I[r]);
+            Lp *= Lp;                              // lam^256
+            s16x4 sh_, sl_;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float sg = fmaf(Ln[u][r], sig[u][r], dpp_f32<kRowShr1>(I[r]));    // state before block n
+                uint16_t h, l;
+                split_bf16(sg, h, l);
+                sh_[r] = (short)h;
+                sl_[r] = (short)l;
+                const float i15 = __int_as_float(__builtin_amdgcn_ds_bpermute((lq * 16 + 15) * 4, __float_as_int(I[r])));
+                sig[u][r] = fmaf(Lp[r], sig[u][r], i15);                                // state after the tile
+            }
+            f32x4 Y = mfma16(Hh[u], gl, z);
+            Y = mfma16(Hl[u], gh, Y);
+            Y = mfma16(Chh[u], sl_, Y);
+            Y = mfma16(Cl[u], sh_, Y);
+            Y = mfma16(Hh[u], gh, Y);
+            Y = mfma16(Chh[u], sh_, Y);
+            *(f32x4*)(ys + c * kYysP + 16 * li + 4 * lq) = Y;
+        }
+        __syncthreads();
+
+        // C: outputs of the tile (rows of 8 channels, bf16), the x history for the next tile
+        {
+            const int t = min(t0 + xrow, T - 1);
+            uint16_t o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = f2bf(ys[(8 * xhalf + e) * kYysP + (t - t0)]);
+            uint4 pk;
+            pk.x = o[0] | ((uint32_t)o[1] << 16); pk.y = o[2] | ((uint32_t)o[3] << 16);
+            pk.z = o[4] | ((uint32_t)o[5] << 16); pk.w = o[6] | ((uint32_t)o[7] << 16);
+            *(uint4*)(yb + (size_t)t * d + ch0 + 8 * xhalf) = pk;
+        }
+        uint4 hist = make_uint4(0u, 0u, 0u, 0u);
+        if (tid < 2 * kYH) hist = *(const uint4*)(xs + (kYTile + (tid >> 1)) * kYC + 8 * (tid & 1));
+        __syncthreads();
+        if (tid < 2 * kYH) *(uint4*)(xs + (tid >> 1) * kYC + 8 * (tid & 1)) = hist;
+        *(uint4*)(xs + (kYH + xrow) * kYC + 8 * xhalf) = xn;
+        xn = load_x(t0 + 3 * kYTile);
+        base += kYTile;
+        if (base >= RL) base -= RL;
+        rs += kYTile;
+        if (rs >= RL) rs -= RL;
+        __syncthreads();
+    };
+    // every load issued so far has landed before the loop: registers loaded above and used in
+    // the loop (taps, states) then leave no wait at the loop head, which would also wait for the
+    // prefetched tiles on every pass
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();                               // the LDS set-up above is complete
+    // pairs of tiles with no branch between them (the count of loads and stores in flight is
+    // then the same on every path into a wait), an odd last tile after the loop
+    int tile = 0;
+    for (; tile + 1 < ntiles; tile += 2) {
+        tile_step(tile, xq1);
+        tile_step(tile + 1, xq2);
+    }
+    if (tile < ntiles) tile_step(tile, xq1);
+}
+
+template <int KS>
+static hipError_t launch_y_ks(const hci_layer* L, const hci_state* S, int nb, int T, const uint16_t* x, uint16_t* y,
+                              hipStream_t st)
+{
+    const int d = L->d, ncg = (d + kYC - 1) / kYC;
+    const size_t lds = prefill_y_lds_bytes(L->taps_outer);
+    hipError_t e;
+    if (lds > 65536 && (e = hipFuncSetAttribute((const void*)k_prefill_y<KS>,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_prefill_y<KS>, dim3((unsigned)(ncg * nb)), dim3(kYT), lds, st, L->w_short, L->w_outer,
+                       L->lambda, L->beta, L->c, (const uint16_t*)S->short_win, S->outer_win, S->iir, x, y, d,
+                       L->taps_short, L->taps_outer, L->poles, T, ncg, nb);
+    return hipGetLastError();
+}
+
+static hipError_t launch_y_mfma(const hci_layer* L, const hci_state* S, int nb, int T, const void* x, void* y,
+                                hipStream_t st)
+{
+    const uint16_t* xa = (const uint16_t*)x;
+    uint16_t* ya = (uint16_t*)y;
+    switch (y_ksteps(L->taps_outer)) {
+        case 1: return launch_y_ks<1>(L, S, nb, T, xa, ya, st);
+        case 2: return launch_y_ks<2>(L, S, nb, T, xa, ya, st);
+        case 3: return launch_y_ks<3>(L, S, nb, T, xa, ya, st);
+        case 4: return launch_y_ks<4>(L, S, nb, T, xa, ya, st);
+        case 5: return launch_y_ks<5>(L, S, nb, T, xa, ya, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 // K/V rows at kv_len .. kv_len+T-1 of every sequence, then the lengths
 static hipError_t append_kv(const hci_layer* L, const hci_state* S, int nb, int T, int lim, const void* k,
                             const void* v, hipStream_t st)
@@ -638,6 +1003,8 @@ hipError_t launch_prefill(const hci_layer* L, const hci_state* S, int nb, int T,
     const int d = L->d;
     hipError_t e;
     if (plan.state_only) {
+        // outputs first: they start from the committed state the state path then replaces
+        if (plan.y_mfma && (e = launch_y_mfma(L, S, nb, T, x, y, st)) != hipSuccess) return e;
         e = L->act_dtype == HCI_BF16
                 ? launch_state_path<HCI_BF16>(L, S, nb, T, lim, (const uint16_t*)x, plan, ws, st)
                 : launch_state_path<HCI_F32>(L, S, nb, T, lim, (const float*)x, plan, ws, st);

@@ -414,7 +414,11 @@ size_t hci_prefill_workspace_bytes(const hci_layer* L, int nb, int T, int want_y
  * (windows, IIR state, cache rows, kv_len) and gets HCI_DS_KV_LEN in S->status;
  * its outputs y are still written.
  * Limits: N <= 16 poles; T <= 16776960.  The IIR runs as a chunked parallel
- * scan, so its results equal the sequential recurrence up to fp32 rounding. */
+ * scan, so the state equals the sequential recurrence up to fp32 rounding.
+ * With bf16 activations (d % 8 == 0, T >= To, Ts <= 4, To <= 144) the outputs
+ * y come from matrix-core products whose fp32 operands are split into two
+ * bf16 terms: each sum carries a relative error of about 2^-14 of the
+ * magnitudes of its terms before y is rounded to bf16. */
 int hci_prefill(const hci_layer* L, const hci_state* S, int nb, int T, int max_kv_len,
                 const void* x, const void* k, const void* v, void* y,
                 void* ws, size_t ws_bytes, hipStream_t stream);
