@@ -672,6 +672,20 @@ __device__ __forceinline__ void split_bf16_d(double v, uint16_t& hi, uint16_t& l
     lo = f2bf((float)(v - (double)bf2f(hi)));
 }
 
+typedef float pf_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 pf_bf16x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 values -> two bf16 (round to nearest even, one v_cvt_pk_bf16_f32), a in the low half
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    const pf_f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, pf_bf16x2));
+}
+// the split of two values: hi = bf16(v), lo = bf16(v - hi), packed in pairs
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = pk_bf16(a, b);
+    lo = pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
 __device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
@@ -805,21 +819,21 @@ __global__ __launch_bounds__(kYT) void k_prefill_y(
             float xv[8 + kYH];
 #pragma unroll
             for (int k = 0; k < 8 + kYH; ++k) xv[k] = bf2f(xs[(8 * ablk + k) * kYC + ac]);
-            uint16_t h8[8], l8[8];
+            float fv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float f = 0.f;
 #pragma unroll
                 for (int j = 0; j < kScTs; ++j) f = fmaf(wsr[j], xv[kYH + e - j], f);
-                split_bf16(f, h8[e], l8[e]);
+                fv[e] = f;
             }
             int sl = base + Wh + 8 * ablk;
             if (sl >= RL) sl -= RL;
             uint4 ph, pl;
-            ph.x = h8[0] | ((uint32_t)h8[1] << 16); ph.y = h8[2] | ((uint32_t)h8[3] << 16);
-            ph.z = h8[4] | ((uint32_t)h8[5] << 16); ph.w = h8[6] | ((uint32_t)h8[7] << 16);
-            pl.x = l8[0] | ((uint32_t)l8[1] << 16); pl.y = l8[2] | ((uint32_t)l8[3] << 16);
-            pl.z = l8[4] | ((uint32_t)l8[5] << 16); pl.w = l8[6] | ((uint32_t)l8[7] << 16);
+            split2(fv[0], fv[1], ph.x, pl.x);
+            split2(fv[2], fv[3], ph.y, pl.y);
+            split2(fv[4], fv[5], ph.z, pl.z);
+            split2(fv[6], fv[7], ph.w, pl.w);
             *(uint4*)(fh + ac * RP + sl) = ph;
             *(uint4*)(fl + ac * RP + sl) = pl;
         }
@@ -844,14 +858,10 @@ __global__ __launch_bounds__(kYT) void k_prefill_y(
                 a2 = mfma32(Al[u][s], bh, a2);
                 a0 = mfma32(Ah[u][s], bh, a0);
             }
-            s16x4 gh, gl;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint16_t h, l;
-                split_bf16(a0[r] + (a1[r] + a2[r]), h, l);
-                gh[r] = (short)h;
-                gl[r] = (short)l;
-            }
+            uint2 gh2, gl2;
+            split2(a0[0] + (a1[0] + a2[0]), a0[1] + (a1[1] + a2[1]), gh2.x, gl2.x);
+            split2(a0[2] + (a1[2] + a2[2]), a0[3] + (a1[3] + a2[3]), gh2.y, gl2.y);
+            const s16x4 gh = __builtin_bit_cast(s16x4, gh2), gl = __builtin_bit_cast(s16x4, gl2);
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
             f32x4 E = mfma16(Bh[u], gl, z);
             E = mfma16(Bl[u], gh, E);
@@ -870,17 +880,17 @@ __global__ __launch_bounds__(kYT) void k_prefill_y(
 #pragma unroll
             for (int r = 0; r < 4; ++r) I[r] = fmaf(Lp[r], dpp_f32<kRowShr8>(I[r]), I[r]);
             Lp *= Lp;                              // lam^256
-            s16x4 sh_, sl_;
+            float sg[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float sg = fmaf(Ln[u][r], sig[u][r], dpp_f32<kRowShr1>(I[r]));    // state before block n
-                uint16_t h, l;
-                split_bf16(sg, h, l);
-                sh_[r] = (short)h;
-                sl_[r] = (short)l;
+                sg[r] = fmaf(Ln[u][r], sig[u][r], dpp_f32<kRowShr1>(I[r]));           // state before block n
                 const float i15 = __int_as_float(__builtin_amdgcn_ds_bpermute((lq * 16 + 15) * 4, __float_as_int(I[r])));
                 sig[u][r] = fmaf(Lp[r], sig[u][r], i15);                                // state after the tile
             }
+            uint2 sh2, sl2;
+            split2(sg[0], sg[1], sh2.x, sl2.x);
+            split2(sg[2], sg[3], sh2.y, sl2.y);
+            const s16x4 sh_ = __builtin_bit_cast(s16x4, sh2), sl_ = __builtin_bit_cast(s16x4, sl2);
             f32x4 Y = mfma16(Hh[u], gl, z);
             Y = mfma16(Hl[u], gh, Y);
             Y = mfma16(Chh[u], sl_, Y);
@@ -894,12 +904,14 @@ __global__ __launch_bounds__(kYT) void k_prefill_y(
         // C: outputs of the tile (rows of 8 channels, bf16), the x history for the next tile
         {
             const int t = min(t0 + xrow, T - 1);
-            uint16_t o[8];
+            float o[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = f2bf(ys[(8 * xhalf + e) * kYysP + (t - t0)]);
+            for (int e = 0; e < 8; ++e) o[e] = ys[(8 * xhalf + e) * kYysP + (t - t0)];
             uint4 pk;
-            pk.x = o[0] | ((uint32_t)o[1] << 16); pk.y = o[2] | ((uint32_t)o[3] << 16);
-            pk.z = o[4] | ((uint32_t)o[5] << 16); pk.w = o[6] | ((uint32_t)o[7] << 16);
+            pk.x = pk_bf16(o[0], o[1]);
+            pk.y = pk_bf16(o[2], o[3]);
+            pk.z = pk_bf16(o[4], o[5]);
+            pk.w = pk_bf16(o[6], o[7]);
             *(uint4*)(yb + (size_t)t * d + ch0 + 8 * xhalf) = pk;
         }
         uint4 hist = make_uint4(0u, 0u, 0u, 0u);
