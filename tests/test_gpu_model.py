@@ -236,3 +236,38 @@ def test_model_block_plus_slice_matches_sequential_steps_on_gpu():
                 continue
             for n in a.layers[l]:
                 close_f32(a.layers[l][n], f64(s.layers[l][n]), f"k={k} layer {l} {n}")
+
+
+def test_model_stack_graph_replay_equals_eager():
+    """The stack verify captured in a HIP graph replays to the eager call's bits: every layer's
+    tensors and the residual stream (no memset is recorded; the workspace is allocated before the
+    capture).  The outputs are cleared by eager work before each replay."""
+    mc = synth.model_scaled(synth.MODEL_CONFIGS["m4_small"], nc=2, gamma=5, kv_lens=(129, 40), cfg_id=215)
+    case = ModelCase(mc)
+    bound = max(mc.kv_lens)
+    outs = [case.blk.x] + [t for lb in case.blk.layers for t in lb.values() if isinstance(t, torch.Tensor)]
+    say("model graph: eager verify")
+    dm.verify(case.dmodel, case.st, case.blk, bound)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    x0 = case.blk.x[0].clone()
+    say("model graph: capture")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            dm.verify(case.dmodel, case.st, case.blk, bound, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        case.blk.x[0].copy_(x0)
+        torch.cuda.synchronize()
+        say(f"model graph: replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (t, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(t.view(torch.uint8), e.view(torch.uint8)), f"replay {rep}: output tensor {i}"
