@@ -307,6 +307,18 @@ def bench_linear(args, hip):
         hip.hipEventRecord(evs[i][1], sp)
     torch.cuda.synchronize()
     ms = float(np.median([_ms(hip, e[0], e[1]) for e in evs]))
+    # the practical floor for the same bytes: the streaming read probe over the same four weight
+    # copies in turn, one launch each, timed the same way
+    sink = torch.empty(hci.probe_sink_words(), dtype=torch.float32, device="cuda")
+    for i in range(args.warmup):
+        hci.probe_read(wps[i % 4], sink)
+    pevs = [_events(hip, 2) for _ in range(args.steps)]
+    for i in range(args.steps):
+        hip.hipEventRecord(pevs[i][0], sp)
+        hci.probe_read(wps[i % 4], sink)
+        hip.hipEventRecord(pevs[i][1], sp)
+    torch.cuda.synchronize()
+    read_ms = float(np.median([_ms(hip, e[0], e[1]) for e in pevs]))
     alg = 2.0 * (K * N + M * K + M * N)
     gbs = alg / (ms * 1e-3) / 1e9
     out = {
@@ -316,6 +328,8 @@ def bench_linear(args, hip):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) rows, N(0,1/K) weights)",
         "config": {"workload": f"y = x W with x {M}x{K}, W {K}x{N} bf16 (a block of {M} rows through a "
                                f"{K}->{N} projection)", "M": M, "K": K, "N": N},
+        "read_probe_ms_same_bytes": round(read_ms, 5),
+        "fraction_of_read_probe": round(read_ms / ms, 4),
         "roofline": {"kernel": "k_linear", "bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0,
                      "unit": "GB/s", "frac": round(gbs / 8000.0, 4), "traffic": None, "alg_bytes_per_launch": alg},
     }
