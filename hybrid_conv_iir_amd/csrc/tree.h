@@ -19,6 +19,7 @@
 #pragma once
 
 #include "conv_iir_body.h"
+#include "wave_ops.h"
 
 namespace hci {
 
@@ -72,12 +73,11 @@ __device__ __forceinline__ bool tree_build(const int32_t* __restrict__ parent, i
     return *flag != 0;
 }
 
-// LDS of the tree conv role: the ancestor table, a flag word, the leaf bookkeeping (leaf flags,
-// the leaves in index order, each node's owning leaf: 64 bytes each), then (16-byte aligned)
-// floats: short window + x rows, outer window + f rows, chunk sums of g, outer taps, short taps.
-constexpr size_t kTreeLeafBytes = 3 * kTreeMax;
+// LDS of the tree conv role: the ancestor table, a flag word, the nodes of every depth as bit
+// masks [64], then (16-byte aligned) floats: short window + x rows, outer window + f rows, chunk
+// sums of g, outer taps, short taps.
 __host__ __device__ inline size_t tree_conv_head_bytes() {
-    return (kTreeAncBytes + 16 + kTreeLeafBytes + 15) / 16 * 16;
+    return (kTreeAncBytes + 16 + kTreeMax * 8 + 15) / 16 * 16;
 }
 __host__ __device__ inline size_t tree_conv_lds_bytes(int Ts, int To, int n) {
     const size_t floats = (size_t)((Ts - 1 + n) + (To - 1 + n) + kFirChunks * n + To + Ts) * kCG;
@@ -98,17 +98,15 @@ __device__ __forceinline__ uint32_t tree_conv_block(
     const int W = To - 1, Ws = Ts - 1;
     const TreeAnc t = tree_anc_lds(lds_raw);
     int* flag = (int*)((char*)lds_raw + kTreeAncBytes);
-    uint8_t* is_leaf = (uint8_t*)lds_raw + kTreeAncBytes + 16;     // [64]
-    uint8_t* leaves = is_leaf + kTreeMax;                           // [64] the leaves in index order
-    uint8_t* owner = leaves + kTreeMax;                             // [64] the leaf whose scan stores node m
+    uint64_t* dmask = (uint64_t*)((char*)lds_raw + kTreeAncBytes + 16);   // [64]: the nodes of depth D
     float* xs = (float*)((char*)lds_raw + tree_conv_head_bytes());  // [Ws + n][kCG]
     float* fb = xs + (size_t)(Ws + n) * kCG;          // [W + n][kCG]: outer window rows, then f rows
-    float* gl = fb + (size_t)(W + n) * kCG;           // [kFirChunks][n][kCG]
+    float* gl = fb + (size_t)(W + n) * kCG;           // [kFirChunks][n][kCG]: chunk sums of g
     float* wl = gl + (size_t)kFirChunks * n * kCG;    // [To][kCG]
     float* ws = wl + (size_t)To * kCG;                // [Ts][kCG]
 
     const int ch0 = cgi * kCG;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int cl = tid & (kCG - 1), row = tid >> 4;
     const int ch = ch0 + cl;
     const bool live = ch < d;
@@ -116,13 +114,52 @@ __device__ __forceinline__ uint32_t tree_conv_block(
     const float* ow = outer_win + (size_t)b * W * d;
     const typename Act<ACT>::T* xb = x + (size_t)b * n * d;
 
-    const bool valid = tree_build(parent + (size_t)b * n, n, t, flag);
+    // every load of the workgroup in one round (values to registers first; the common sizes, up
+    // to 128 window rows and taps and 64 nodes, then the rest by plain loops), in flight while the
+    // ancestor table is built
+    constexpr int SW = 8, SX = 4;                       // rows per thread of the register batch
+    float vw[SW], vt[SW], vx[SX], vsw, vst;
+#pragma unroll
+    for (int u = 0; u < SW; ++u) {
+        const int r = row + 16 * u;
+        vw[u] = live && r < W ? ow[(size_t)r * d + ch] : 0.f;
+        vt[u] = live && r < To ? w_outer[(size_t)r * d + ch] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < SX; ++u) {
+        const int r = row + 16 * u;
+        vx[u] = live && r < n ? Act<ACT>::load(xb, (size_t)r * d + ch) : 0.f;
+    }
+    vsw = live && row < Ws ? Act<ACT>::load(sw, (size_t)row * d + ch) : 0.f;
+    vst = live && row < Ts ? w_short[(size_t)row * d + ch] : 0.f;
 
-    for (int r = row; r < W; r += kConvT / kCG) fb[r * kCG + cl] = live ? ow[(size_t)r * d + ch] : 0.f;
-    for (int r = row; r < To; r += kConvT / kCG) wl[r * kCG + cl] = live ? w_outer[(size_t)r * d + ch] : 0.f;
-    for (int r = row; r < n; r += kConvT / kCG) xs[(Ws + r) * kCG + cl] = live ? Act<ACT>::load(xb, (size_t)r * d + ch) : 0.f;
-    for (int r = row; r < Ws; r += kConvT / kCG) xs[r * kCG + cl] = live ? Act<ACT>::load(sw, (size_t)r * d + ch) : 0.f;
-    for (int r = row; r < Ts; r += kConvT / kCG) ws[r * kCG + cl] = live ? w_short[(size_t)r * d + ch] : 0.f;
+    const bool valid = tree_build(parent + (size_t)b * n, n, t, flag);
+    // the nodes of every depth (n <= 64: one lane per node), published by the barrier below
+    const int dl = lane < n ? (int)t.depth[lane] : -1;
+    const int maxD = wave_max_i32(dl);
+    for (int D = 0; D <= maxD; ++D) {
+        const uint64_t mk = __ballot(dl == D);
+        if (tid == 0) dmask[D] = mk;
+    }
+
+#pragma unroll
+    for (int u = 0; u < SW; ++u) {
+        const int r = row + 16 * u;
+        if (r < W) fb[r * kCG + cl] = vw[u];
+        if (r < To) wl[r * kCG + cl] = vt[u];
+    }
+#pragma unroll
+    for (int u = 0; u < SX; ++u) {
+        const int r = row + 16 * u;
+        if (r < n) xs[(Ws + r) * kCG + cl] = vx[u];
+    }
+    if (row < Ws) xs[row * kCG + cl] = vsw;
+    if (row < Ts) ws[row * kCG + cl] = vst;
+    for (int r = row + 16 * SW; r < W; r += kConvT / kCG) fb[r * kCG + cl] = live ? ow[(size_t)r * d + ch] : 0.f;
+    for (int r = row + 16 * SW; r < To; r += kConvT / kCG) wl[r * kCG + cl] = live ? w_outer[(size_t)r * d + ch] : 0.f;
+    for (int r = row + 16 * SX; r < n; r += kConvT / kCG) xs[(Ws + r) * kCG + cl] = live ? Act<ACT>::load(xb, (size_t)r * d + ch) : 0.f;
+    for (int r = row + 16; r < Ws; r += kConvT / kCG) xs[r * kCG + cl] = live ? Act<ACT>::load(sw, (size_t)r * d + ch) : 0.f;
+    for (int r = row + 16; r < Ts; r += kConvT / kCG) ws[r * kCG + cl] = live ? w_short[(size_t)r * d + ch] : 0.f;
     __syncthreads();
 
     // short FIR: f_m = sum_{j<Ts} w_short[j] * (input j positions before m on its path)
@@ -139,88 +176,111 @@ __device__ __forceinline__ uint32_t tree_conv_block(
     }
     __syncthreads();
 
-    // outer FIR: chunk k of taps [k CS, min((k + 1) CS, To)) summed in ascending tap order
-    {
-        const int CS = (To + kFirChunks - 1) / kFirChunks;
-        for (int task = tid; task < n * kFirChunks * kCG; task += kConvT) {
-            const int tcl = task % kCG, k = (task / kCG) % kFirChunks, m = task / (kCG * kFirChunks);
-            const int D = t.depth[m];
-            const uint8_t* am = t.anc + m * kTreeMax;
-            const int j0 = k * CS, j1 = min(j0 + CS, To);
-            float acc = 0.f;
-            for (int j = j0; j < j1; ++j) {
-                const int rw = j <= D ? W + am[j] : W - (j - D);
-                acc = fmaf(wl[j * kCG + tcl], fb[rw * kCG + tcl], acc);
-            }
-            gl[((size_t)k * n + m) * kCG + tcl] = acc;
+    // outer FIR in the chain kernel's order: chunk k sums taps [k CS, min((k + 1) CS, To)) in
+    // ascending order from zero, and the IIR adds the chunk sums in chunk order.  Tap j of node m
+    // (depth D) reads its ancestor j steps up for j <= D and the committed-window row W - (j - D)
+    // past it, so a chunk that starts past D reads window rows only: its sum is the same for every
+    // node of depth D, taken once per depth and stored for each of them; the other chunks are
+    // summed per node.
+    const int CS = (To + kFirChunks - 1) / kFirChunks;
+    // per node: a node's chunk sum over taps [j0, j1), ancestors first, then window rows
+    auto node_chunk = [&](int m, int k, int tcl) {
+        const int D = t.depth[m];
+        const int j0 = k * CS, j1 = min(j0 + CS, To);
+        const uint8_t* am = t.anc + m * kTreeMax;
+        const int ja = min(D, j1 - 1);                  // the last ancestor tap of the chunk
+        float acc = 0.f;
+#pragma unroll 4
+        for (int j = j0; j <= ja; ++j) acc = fmaf(wl[j * kCG + tcl], fb[(W + am[j]) * kCG + tcl], acc);
+#pragma unroll 8
+        for (int j = ja + 1; j < j1; ++j) acc = fmaf(wl[j * kCG + tcl], fb[(W - (j - D)) * kCG + tcl], acc);
+        gl[((size_t)k * n + m) * kCG + tcl] = acc;
+    };
+    // chunk 0 starts at tap 0 <= D: always per node, (node, channel) tasks
+    for (int task = tid; task < n * kCG; task += kConvT) node_chunk(task / kCG, 0, task % kCG);
+    // later chunks per node only in trees deeper than a chunk
+    if (maxD >= CS)
+        for (int task = tid; task < n * (kFirChunks - 1) * kCG; task += kConvT) {
+            const int tcl = task % kCG, k = 1 + (task / kCG) % (kFirChunks - 1), m = task / (kCG * (kFirChunks - 1));
+            if (k * CS <= (int)t.depth[m]) node_chunk(m, k, tcl);
         }
+    // per depth: the chunks that start past D, stored for every node of depth D
+    for (int task = tid; task < (maxD + 1) * (kFirChunks - 1) * kCG; task += kConvT) {
+        const int tcl = task % kCG, k = 1 + (task / kCG) % (kFirChunks - 1), D = task / (kCG * (kFirChunks - 1));
+        const int j0 = k * CS, j1 = min(j0 + CS, To);
+        if (j0 <= D) continue;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int j = j0; j < j1; ++j) acc = fmaf(wl[j * kCG + tcl], fb[(W - (j - D)) * kCG + tcl], acc);
+        for (uint64_t mk = dmask[D]; mk != 0; mk &= mk - 1)
+            gl[((size_t)k * n + __builtin_ctzll(mk)) * kCG + tcl] = acc;
     }
     __syncthreads();
+
+    // leaves and owners on the lanes of every wave (no LDS round trips): lane m stands for node
+    // m.  A node is stored by the first leaf below it in index order, the smallest such leaf:
+    // children have larger indices than their parents, so one pass from the last node down
+    // hands every node's smallest leaf to its parent after all of its children.
+    const int pm = lane < n ? (int)t.par[lane] : 0;
+    uint64_t haschild = 0;
+    for (int c = 1; c < n; ++c) haschild |= 1ull << __builtin_amdgcn_readlane(pm, c);
+    const bool is_leaf = lane < n && !((haschild >> lane) & 1ull);
+    int minleaf = is_leaf ? lane : kTreeMax;
+    for (int c = n - 1; c >= 1; --c) {
+        const int v = __builtin_amdgcn_readlane(minleaf, c), p = __builtin_amdgcn_readlane(pm, c);
+        if (lane == p) minleaf = min(minleaf, v);
+    }
+    const uint64_t leafmask = __ballot(is_leaf);
+    const int nl = __popcll(leafmask);
 
     // IIR along the tree, one root-to-leaf path per wave and pass: the path's nodes in order from
-    // the root, each state s = fma(lambda, s_parent, beta * g) kept in registers, so no node's state
-    // is stored in LDS.  A node on several paths is computed by each of them with the same
-    // arithmetic (the same bits) and stored by one: the first leaf below it in index order.
-    if (tid < n) {
-        bool leaf = true;
-        for (int c = tid + 1; c < n; ++c) leaf = leaf && t.par[c] != tid;
-        is_leaf[tid] = leaf ? 1 : 0;
-    }
-    __syncthreads();
-    int nl = 0;
-    for (int m = 0; m < n; ++m) nl += is_leaf[m];
-    if (tid < n) {
-        if (is_leaf[tid]) {
-            int rank = 0;
-            for (int m = 0; m < tid; ++m) rank += is_leaf[m];
-            leaves[rank] = (uint8_t)tid;
-        }
-        const int dm = t.depth[tid];
-        int own = tid;
-        for (int L = 0; L < n; ++L) {
-            const int dl = t.depth[L];
-            if (is_leaf[L] && dl >= dm && t.anc[L * kTreeMax + (dl - dm)] == tid) { own = L; break; }
-        }
-        owner[tid] = (uint8_t)own;
-    }
-    __syncthreads();
-
+    // the root (lane j holds the node j steps above the leaf), each state s = fma(lambda, s_parent,
+    // beta * g) kept in registers, the next node's input read ahead.  A node on several paths is
+    // computed by each of them with the same arithmetic (the same bits) and stored by its owner.
     const int G = N <= 4 ? 1 : N <= 8 ? 2 : 4;
-    const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if (lane < kCG * G) {
-        const int tg = lane % G, tch = lane / G;
-        const int chn = ch0 + tch;
-        const bool scan = chn < d;
-        float lm[4], bt[4], cv[4], s0[4];
+    const int tg = lane % G, tch = (lane / G) % kCG;
+    const int chn = ch0 + tch;
+    const bool task_lane = lane < kCG * G;
+    const bool scan = task_lane && chn < d;
+    float lm[4], bt[4], cv[4], s0[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int pn = 4 * tg + q;
-            const bool ok = scan && pn < N;
-            const size_t o = (size_t)chn * N + pn;
-            lm[q] = ok ? lam[o] : 0.f;
-            bt[q] = ok ? beta[o] : 0.f;
-            cv[q] = ok ? cc[o] : 0.f;
-            s0[q] = ok ? iir[(size_t)b * d * N + o] : 0.f;
-        }
-        for (int li = wv; li < nl; li += kConvT / 64) {
-            const int L = leaves[li];
-            const int D = t.depth[L];
-            const uint8_t* aL = t.anc + L * kTreeMax;
+    for (int q = 0; q < 4; ++q) {
+        const int pn = 4 * tg + q;
+        const bool ok = scan && pn < N;
+        const size_t o = (size_t)chn * N + pn;
+        lm[q] = ok ? lam[o] : 0.f;
+        bt[q] = ok ? beta[o] : 0.f;
+        cv[q] = ok ? cc[o] : 0.f;
+        s0[q] = ok ? iir[(size_t)b * d * N + o] : 0.f;
+    }
+    // g of node m: the chunk sums in chunk order
+    auto g_of = [&](int m) -> float {
+        float g = gl[(size_t)m * kCG + tch];
+#pragma unroll
+        for (int k = 1; k < kFirChunks; ++k) g += gl[((size_t)k * n + m) * kCG + tch];
+        return g;
+    };
+    for (int li = wv; li < nl; li += kConvT / 64) {
+        uint64_t mk = leafmask;
+        for (int i = 0; i < li; ++i) mk &= mk - 1;
+        const int L = __builtin_ctzll(mk);               // the li-th leaf in index order
+        const int D = t.depth[L];
+        const int pv = t.anc[L * kTreeMax + lane];       // lane j: the node j steps above L
+        if (task_lane) {
             float st[4] = {s0[0], s0[1], s0[2], s0[3]};
-            for (int j = D; j >= 0; --j) {               // node aL[j]: j steps above the leaf
-                const int m = aL[j];
-                float g = gl[(size_t)m * kCG + tch];
-#pragma unroll
-                for (int k = 1; k < kFirChunks; ++k) g += gl[((size_t)k * n + m) * kCG + tch];
-                g = scan ? g : 0.f;
+            float gn = g_of(__builtin_amdgcn_readlane(pv, D));
+            for (int j = D; j >= 0; --j) {
+                const int m = __builtin_amdgcn_readlane(pv, j);
+                const float g = scan ? gn : 0.f;
+                if (j > 0) gn = g_of(__builtin_amdgcn_readlane(pv, j - 1));
                 float py = 0.f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     st[q] = fmaf(lm[q], st[q], bt[q] * g);
                     py = fmaf(cv[q], st[q], py);
                 }
-                const bool store = scan && owner[m] == L;
+                const bool store = scan && __builtin_amdgcn_readlane(minleaf, m) == L;
                 if (store) {
                     float* so = s_out + (((size_t)b * n + m) * d + chn) * N + 4 * tg;
                     if ((N & 3) == 0) {
