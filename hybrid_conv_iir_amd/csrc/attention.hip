@@ -285,7 +285,7 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
     F.scale_log2 = scale_log2;
     F.parent = parent;
     F.status = S->status;
-    const int rg = combine_rows(nb, nc, H, P, plan.resident / kStreamSlots);
+    const int rg = combine_rows(nb, nc, H, P, plan.resident / kStreamSlots, parent != nullptr);
     F.rg_count = (P + rg - 1) / rg;
     const long long blocks = (long long)F.n_conv + (long long)F.rg_count * nc * H * nb;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;

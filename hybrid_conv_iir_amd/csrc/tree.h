@@ -217,21 +217,23 @@ __device__ __forceinline__ uint32_t tree_conv_block(
     }
     __syncthreads();
 
-    // leaves and owners on the lanes of every wave (no LDS round trips): lane m stands for node
-    // m.  A node is stored by the first leaf below it in index order, the smallest such leaf:
-    // children have larger indices than their parents, so one pass from the last node down
-    // hands every node's smallest leaf to its parent after all of its children.
-    const int pm = lane < n ? (int)t.par[lane] : 0;
-    uint64_t haschild = 0;
-    for (int c = 1; c < n; ++c) haschild |= 1ull << __builtin_amdgcn_readlane(pm, c);
-    const bool is_leaf = lane < n && !((haschild >> lane) & 1ull);
-    int minleaf = is_leaf ? lane : kTreeMax;
-    for (int c = n - 1; c >= 1; --c) {
-        const int v = __builtin_amdgcn_readlane(minleaf, c), p = __builtin_amdgcn_readlane(pm, c);
-        if (lane == p) minleaf = min(minleaf, v);
+    // leaves and owners, lane m of every wave standing for node m: a node is a leaf when no node
+    // one level deeper has it as parent; it is stored by the first leaf below it in index order
+    bool is_leaf = false;
+    if (lane < n) {
+        is_leaf = true;
+        if (dl < maxD)
+            for (uint64_t mk = dmask[dl + 1]; mk != 0; mk &= mk - 1)
+                if (t.par[__builtin_ctzll(mk)] == lane) { is_leaf = false; break; }
     }
     const uint64_t leafmask = __ballot(is_leaf);
     const int nl = __popcll(leafmask);
+    int minleaf = kTreeMax;
+    if (lane < n)
+        for (uint64_t mk = leafmask; mk != 0; mk &= mk - 1) {
+            const int L = __builtin_ctzll(mk), dL = t.depth[L];
+            if (dL >= dl && t.anc[L * kTreeMax + (dL - dl)] == lane) { minleaf = L; break; }
+        }
 
     // IIR along the tree, one root-to-leaf path per wave and pass: the path's nodes in order from
     // the root (lane j holds the node j steps above the leaf), each state s = fma(lambda, s_parent,

@@ -41,7 +41,7 @@ __host__ __device__ inline size_t combine_lds_floats(int P, int DH, int act_byte
 }
 
 // rows per combine workgroup for these sizes (1, 2, 4, 8 or 16)
-int combine_rows(int nb, int nc, int H, int P, int num_cus);
+int combine_rows(int nb, int nc, int H, int P, int num_cus, bool tree);
 // the finish kernel: grid = F.n_conv + F.rg_count * nc * H * nb workgroups of kCombT threads
 hipError_t launch_finish(const FinishArgs& F, int act_dtype, int rg, int blocks, size_t lds, hipStream_t st);
 
