@@ -661,6 +661,12 @@ struct TreeAccScratch {
     int zapp[kTreeNodes];
     double pst[2], qst[2];
     int flag;
+    // greedy: every target row's argmax, top-1 gap and bad-row flag, taken before the walk;
+    // sampling: the row statistics (max, sum of exp) of the rows the walk visits, per node
+    int garg[kTreeNodes], gbad[kTreeNodes];
+    double ggap[kTreeNodes];
+    double pm_[kTreeNodes], ps_[kTreeNodes], qm_[kTreeNodes], qs_[kTreeNodes];
+    float zp_[kTreeNodes], zq_[kTreeNodes];  // node c's drafted token in its parent's target row / its draft row
 };
 
 __global__ __launch_bounds__(kAccT) void k_accept_tree(
@@ -695,56 +701,71 @@ __global__ __launch_bounds__(kAccT) void k_accept_tree(
         }
         sh.path[0] = 0;
     }
+    const float* ztb = zt + (size_t)b * n * V;
+    const float* zdb = zd ? zd + (size_t)b * n * V : nullptr;
+    // greedy: every target row's argmax, the four waves side by side (none depends on the walk,
+    // and without exponentials they are cheap); sampling: every drafted token's two logits
+    if (mode == HCI_GREEDY) {
+        for (int r = wv; r < n; r += kAccW) {
+            int g; double gap; bool rb;
+            wave_row_argmax(ztb + (size_t)r * V, V, lane, g, gap, rb);
+            if (lane == 0) { sh.garg[r] = g; sh.ggap[r] = gap; sh.gbad[r] = rb ? 1 : 0; }
+        }
+    } else {
+        if (tid > 0 && tid < n) {
+            const int t = tok[tid], p = sh.par[tid];
+            const bool ok = t >= 0 && t < V && p >= 0;
+            sh.zp_[tid] = ok ? ztb[(size_t)p * V + t] : 0.f;
+            sh.zq_[tid] = ok ? zdb[(size_t)tid * V + t] : 0.f;
+        }
+    }
     __syncthreads();
     bool bad = sh.flag == 0;
     uint32_t flags = bad ? HCI_DS_TREE : 0u;
     int m = 0, k = 0, nxt = -1;
     double margin = INFINITY;
-    const float* ztb = zt + (size_t)b * n * V;
-    const float* zdb = zd ? zd + (size_t)b * n * V : nullptr;
     while (!bad) {
         const float* prow = ztb + (size_t)m * V;
-        if (mode == HCI_GREEDY) {
-            if (wv == 0) {
-                int g; double gap; bool rb;
-                wave_row_argmax(prow, V, lane, g, gap, rb);
-                if (lane == 0) { sh.a.arg[0] = g; sh.a.gap[0] = gap; sh.a.badrow[0] = rb ? 1 : 0; }
-            }
-            __syncthreads();
-            const int g = sh.a.arg[0];
-            margin = fmin(margin, sh.a.gap[0]);
-            if (sh.a.badrow[0]) { bad = true; break; }
+        if (mode == HCI_GREEDY) {                     // every thread walks the same path: no barrier
+            const int g = sh.garg[m];
+            margin = fmin(margin, sh.ggap[m]);
+            if (sh.gbad[m]) { bad = true; break; }
             int found = -1;
             for (int c = sh.first[m]; c >= 0; c = sh.sib[c]) {
                 const int t = tok[c];
                 if (t < 0 || t >= V) flags |= HCI_DS_DRAFT_ID;
                 if (t == g) { found = c; break; }
             }
-            __syncthreads();                          // arg / gap are rewritten at the next node
             if (found < 0) { nxt = g; break; }
             m = found;
-            sh.path[++k] = m;                         // every thread stores the same value
+            if (tid == 0) sh.path[k + 1] = m;
+            ++k;
             continue;
         }
-        // sampling: the target row's statistics, then the children in order
-        if (wv == 0) {
-            double mx, sum;
-            wave_row_stats(prow, V, T, lane, mx, sum);
-            if (lane == 0) { sh.pst[0] = mx; sh.pst[1] = sum; sh.zh[0] = 1.0; }
+        // sampling: the statistics of the target row and of the children's draft rows in one round
+        // (wave w: entries w, w + 4, ... of [target row m, draft rows of m's children in order]),
+        // then the children in order
+        {
+            if (wv == 0) {
+                double mx, sum;
+                wave_row_stats(prow, V, T, lane, mx, sum);
+                if (lane == 0) { sh.pm_[m] = mx; sh.ps_[m] = sum; sh.zh[0] = 1.0; }
+            }
+            int i = 1;
+            for (int c = sh.first[m]; c >= 0; c = sh.sib[c], ++i)
+                if (i % kAccW == wv) {
+                    double mx, sum;
+                    wave_row_stats(zdb + (size_t)c * V, V, T, lane, mx, sum);
+                    if (lane == 0) { sh.qm_[c] = mx; sh.qs_[c] = sum; }
+                }
         }
         __syncthreads();
-        const double pm = sh.pst[0], ps = sh.pst[1];
+        const double pm = sh.pm_[m], ps = sh.ps_[m];
         if (!row_finite(ps)) { bad = true; break; }
         int nrej = 0, kept = -1;
         for (int c = sh.first[m]; c >= 0 && !bad; c = sh.sib[c]) {
             const float* qrow = zdb + (size_t)c * V;
-            if (wv == 0) {
-                double mx, sum;
-                wave_row_stats(qrow, V, T, lane, mx, sum);
-                if (lane == 0) { sh.qst[0] = mx; sh.qst[1] = sum; }
-            }
-            __syncthreads();
-            const double qm = sh.qst[0], qs = sh.qst[1];
+            const double qm = sh.qm_[c], qs = sh.qs_[c];
             if (!row_finite(qs)) { bad = true; break; }
             // residual weight of token j after the rejections so far at this node
             auto resid = [&](int j, double p) {
@@ -757,8 +778,8 @@ __global__ __launch_bounds__(kAccT) void k_accept_tree(
             };
             const int t = tok[c];
             if (t >= 0 && t < V) {
-                const double p_t = exp(over_T((double)prow[t], T) - pm) / ps;
-                const double q_t = exp(over_T((double)qrow[t], T) - qm) / qs;
+                const double p_t = exp(over_T((double)sh.zp_[c], T) - pm) / ps;
+                const double q_t = exp(over_T((double)sh.zq_[c], T) - qm) / qs;
                 const double lhs = uni[(size_t)b * n + c] * q_t * sh.zh[nrej];
                 const double rhs = resid(t, p_t);
                 margin = fmin(margin, fabs(lhs - rhs) / fmax(rhs, 1e-300));
