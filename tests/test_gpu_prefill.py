@@ -103,6 +103,24 @@ def test_prefill_odd_channel_groups(want_y):
     _check(cfg, 3001, L0=5, want_y=want_y)
 
 
+# The matrix-core outputs pass covers outer filters of up to 145 taps in 1..5 window steps of 32
+# inputs (the window is To - 1 rounded up to 8, plus 16): each step count once, ragged prompt
+# lengths, short filters of 2..4 taps, few and many poles, two sequences, a last channel group
+# of 8 channels (d = 40); 160 taps take the chunked output path.
+@pytest.mark.parametrize("To,Ts,N,T,d", [
+    (7, 2, 3, 700, 40),        # one step
+    (17, 4, 16, 513, 40),      # one step, the window exactly 32 inputs
+    (40, 3, 16, 1000, 48),     # two steps
+    (81, 4, 5, 257, 40),       # three steps
+    (100, 2, 16, 999, 40),     # four steps
+    (145, 3, 16, 2000, 48),    # five steps, the longest filter of the pass
+    (160, 3, 16, 700, 40),     # past the pass: the chunked output path
+])
+def test_prefill_outputs_every_window_length(To, Ts, N, T, d):
+    cfg = synth.scaled(synth.CONFIGS["mid8k"], d=d, heads=1, taps_short=Ts, taps_outer=To, poles=N, kv_lens=(0, 0))
+    _check(cfg, T, L0=11, want_y=True)
+
+
 @pytest.mark.parametrize("want_y", [True, False])
 def test_prefill_long_prompt_262k_channel_sample(want_y):
     """A channel sample that covers every XCD at both ends of the channel range: workgroups go to
