@@ -295,6 +295,11 @@ hipError_t launch_verify(const hci_layer* L, const hci_state* S, const hci_block
                                      : conv_iir_lds_floats(L->taps_short, L->taps_outer, nc * P) * sizeof(float);
     const size_t comb_lds = combine_lds_floats(P, DH, act_bytes, rg) * sizeof(float);
     const size_t lds = conv_lds > comb_lds ? conv_lds : comb_lds;
+    // combine workgroups first when the grid outgrows one round of resident workgroups (4 x 4
+    // candidates: finish 45 -> 41 us); conv first when all are resident at once (its chain is
+    // the longer one: long context 12.7 against 13.2 us)
+    const long long per_cu = lds > 0 && kMaxLds / lds < (size_t)kFinishPerCu ? (long long)(kMaxLds / lds) : kFinishPerCu;
+    F.comb_first = blocks > per_cu * (plan.resident / kStreamSlots) ? 1 : 0;
     e = launch_finish(F, L->act_dtype, rg, (int)blocks, lds, st);
     if (e != hipSuccess) return e;
     return mark(3);

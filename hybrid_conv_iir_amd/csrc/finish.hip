@@ -311,12 +311,17 @@ __device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, 
 }
 
 template <int ACT, int RG>
-__global__ __launch_bounds__(kCombT, 4) void k_verify_finish(FinishArgs A)
+__global__ __launch_bounds__(kCombT, kFinishPerCu) void k_verify_finish(FinishArgs A)
 {
     extern __shared__ float lds[];
     typedef typename Act<ACT>::T T;
-    const int id = blockIdx.x;
-    if (id < A.n_conv) {
+    // the grid's first indices are dispatched first: the conv workgroups (the longer chain)
+    // when the whole grid is resident at once, else the combine workgroups
+    const int n_comb = (int)gridDim.x - A.n_conv;
+    const int bid = blockIdx.x;
+    const bool is_conv = A.comb_first ? bid >= n_comb : bid < A.n_conv;
+    if (is_conv) {
+        const int id = A.comb_first ? bid - n_comb : bid;
         const int groups = (A.d + kCG - 1) / kCG;
         if (A.parent) {
             const int cgi = id % groups, b = id / groups;
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(kCombT, 4) void k_verify_finish(FinishArgs A)
                             id % groups, id / groups, lds);
         return;
     }
-    const int j = id - A.n_conv;            // (rg, c, h, b), row group fastest
+    const int j = A.comb_first ? bid : bid - A.n_conv;    // (rg, c, h, b), row group fastest
     const int rg = j % A.rg_count;
     const int t = j / A.rg_count;
     const int c = t % A.nc, h = (t / A.nc) % A.H, b = t / (A.nc * A.H);

@@ -8,6 +8,9 @@ namespace hci {
 
 constexpr int kCombT = 256;
 constexpr int kCombW = kCombT / 64;
+// finish workgroups resident per CU as far as registers go (the kernel's launch bound: four
+// waves per SIMD, one wave of each workgroup on each SIMD)
+constexpr int kFinishPerCu = 4;
 
 struct FinishArgs {
     // conv / IIR
@@ -15,6 +18,7 @@ struct FinishArgs {
     const void* short_win; const float* outer_win; const float* iir; const void* x;
     float* f_out; float* s_out; void* y_out;
     int d, Ts, To, N, nc, n_conv;
+    int comb_first;                    // 1: the combine workgroups take the grid's low indices
     // combine
     const int32_t* kv_len; const float *part_o, *part_ml;
     const int32_t* table;              // the work-list table written by the set-up kernel
