@@ -44,6 +44,21 @@ __host__ __device__ inline size_t conv_iir_lds_floats(int Ts, int To, int R) {
     return (size_t)((Ts - 1 + R) + (To - 1 + R) + kFirChunks * R + To + Ts) * kCG;
 }
 
+// Raw bits of one activation (a 16-bit load for bf16) and their value: the conversion is applied
+// where the value is used, so that a batch of loads stays in flight (a conversion right after a
+// load makes the compiler wait for that load there, and loads complete in order).
+template <int ACT> struct ActRaw;
+template <> struct ActRaw<HCI_F32> {
+    typedef float R;
+    __device__ static __forceinline__ R load(const float* p, size_t i) { return p[i]; }
+    __device__ static __forceinline__ float cvt(R r) { return r; }
+};
+template <> struct ActRaw<HCI_BF16> {
+    typedef uint32_t R;
+    __device__ static __forceinline__ R load(const uint16_t* p, size_t i) { return p[i]; }
+    __device__ static __forceinline__ float cvt(R r) { return __uint_as_float(r << 16); }
+};
+
 // Sum over the G lanes of an aligned group (G = 1, 2, 4, 8 or 16), the same bits on every
 // lane of the group: lane offsets G/2, ..., 2, 1 in turn.  Offsets 2 and 1 are quad
 // permutations on the vector ALU (no LDS round trip); wider groups use the LDS crossbar.
@@ -93,50 +108,52 @@ __device__ __forceinline__ void conv_iir_block(
     const int tg = tid % G, tch = (tid / G) % kCG, tc = tid / (G * kCG);
     const int chn = ch0 + tch;
     const bool scan = chn < d;                          // uniform across the G lanes of a task
+    // (loaded from clamped addresses, zeroed past the channels or poles before the scan)
     float lm[4], bt[4], cv[4], s0[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int n = 4 * tg + q;
-        const bool ok = scan && n < N;
-        const size_t o = (size_t)chn * N + n;
-        lm[q] = ok ? lam[o] : 0.f;
-        bt[q] = ok ? beta[o] : 0.f;
-        cv[q] = ok ? cc[o] : 0.f;
-        s0[q] = ok ? iir[(size_t)b * d * N + o] : 0.f;
+        const size_t o = (size_t)min(chn, d - 1) * N + min(4 * tg + q, N - 1);
+        lm[q] = lam[o];
+        bt[q] = beta[o];
+        cv[q] = cc[o];
+        s0[q] = iir[(size_t)b * d * N + o];
     }
 
     // phase 0: every load of the workgroup in one round: all values go to registers first
     // (the common sizes: up to 128 window rows and taps, 64 block rows, 16 short taps), then
-    // to LDS; rows beyond those sizes are staged by a plain loop afterwards
+    // to LDS; rows beyond those sizes are staged by a plain loop afterwards.  The loads are
+    // unconditional, from clamped (always valid) addresses, their values masked where they are
+    // stored: with no branch around a load the compiler counts the loads in flight exactly and
+    // waits for each one only where it is used; activations stay raw bits until then (a
+    // conversion next to a load would wait for it there).
     {
         constexpr int SW = 8, SX = 4;                   // rows per thread of the register batch
-        float vw[SW], vt[SW], vx[SX], vsw, vst;
+        const int chc = min(ch, d - 1);
+        float vw[SW], vt[SW], vst;
+        typename ActRaw<ACT>::R rx[SX], rsw;
 #pragma unroll
         for (int u = 0; u < SW; ++u) {
             const int r = row + 16 * u;
-            vw[u] = live && r < W ? ow[(size_t)r * d + ch] : 0.f;
-            vt[u] = live && r < To ? w_outer[(size_t)r * d + ch] : 0.f;
+            vw[u] = (W > 0 ? ow + (size_t)min(r, W - 1) * d : w_outer)[chc];     // no window: any valid row
+            vt[u] = w_outer[(size_t)min(r, To - 1) * d + chc];
+        }
+#pragma unroll
+        for (int u = 0; u < SX; ++u) rx[u] = ActRaw<ACT>::load(xb, (size_t)min(row + 16 * u, R - 1) * d + chc);
+        rsw = ActRaw<ACT>::load(Ws > 0 ? sw + (size_t)min(row, Ws - 1) * d : xb, chc);
+        vst = w_short[(size_t)min(row, Ts - 1) * d + chc];
+#pragma unroll
+        for (int u = 0; u < SW; ++u) {
+            const int r = row + 16 * u;
+            if (r < W) fb[r * kCG + cl] = keep_if(vw[u], live);
+            if (r < To) wl[r * kCG + cl] = keep_if(vt[u], live);
         }
 #pragma unroll
         for (int u = 0; u < SX; ++u) {
             const int r = row + 16 * u;
-            vx[u] = live && r < R ? Act<ACT>::load(xb, (size_t)r * d + ch) : 0.f;
+            if (r < R) xs[(Ws + r) * kCG + cl] = keep_if(ActRaw<ACT>::cvt(rx[u]), live);
         }
-        vsw = live && row < Ws ? Act<ACT>::load(sw, (size_t)row * d + ch) : 0.f;
-        vst = live && row < Ts ? w_short[(size_t)row * d + ch] : 0.f;
-#pragma unroll
-        for (int u = 0; u < SW; ++u) {
-            const int r = row + 16 * u;
-            if (r < W) fb[r * kCG + cl] = vw[u];
-            if (r < To) wl[r * kCG + cl] = vt[u];
-        }
-#pragma unroll
-        for (int u = 0; u < SX; ++u) {
-            const int r = row + 16 * u;
-            if (r < R) xs[(Ws + r) * kCG + cl] = vx[u];
-        }
-        if (row < Ws) xs[row * kCG + cl] = vsw;
-        if (row < Ts) ws[row * kCG + cl] = vst;
+        if (row < Ws) xs[row * kCG + cl] = keep_if(ActRaw<ACT>::cvt(rsw), live);
+        if (row < Ts) ws[row * kCG + cl] = keep_if(vst, live);
         for (int r = row + 16 * SW; r < W; r += kConvT / kCG) fb[r * kCG + cl] = live ? ow[(size_t)r * d + ch] : 0.f;
         for (int r = row + 16 * SW; r < To; r += kConvT / kCG) wl[r * kCG + cl] = live ? w_outer[(size_t)r * d + ch] : 0.f;
         for (int r = row + 16 * SX; r < R; r += kConvT / kCG) xs[(Ws + r) * kCG + cl] = live ? Act<ACT>::load(xb, (size_t)r * d + ch) : 0.f;
@@ -234,6 +251,15 @@ __device__ __forceinline__ void conv_iir_block(
         }
     }
     __syncthreads();
+
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const bool ok = scan && 4 * tg + q < N;
+        lm[q] = keep_if(lm[q], ok);
+        bt[q] = keep_if(bt[q], ok);
+        cv[q] = keep_if(cv[q], ok);
+        s0[q] = keep_if(s0[q], ok);
+    }
 
     // phase 3: IIR scan from the committed state, in registers.  A task = (channel, candidate,
     // group of 4 poles); 256 / (16 G) candidates advance together.  y_i adds the group's four

@@ -44,16 +44,15 @@ __device__ __forceinline__ TreeAnc tree_anc_lds(void* base) {
 __device__ __forceinline__ bool tree_parent_ok(int m, int p) { return m == 0 ? p == -1 : (p >= 0 && p < m); }
 
 // Builds the ancestor table of one tree (threads 0..n-1 each walk their own node; every parent
-// precedes its child, so a walk ends at node 0 within m steps).  An invalid parent entry is read
-// as m - 1 (the tree's outputs are then those of that reading; callers report HCI_DS_TREE).
-// Returns whether every entry was valid (the same on every thread).  Ends with a barrier.
-__device__ __forceinline__ bool tree_build(const int32_t* __restrict__ parent, int n, const TreeAnc& t,
-                                           int* flag) {
+// precedes its child, so a walk ends at node 0 within m steps).  p is thread tid's parent entry,
+// loaded by the caller (for tid < n).  An invalid parent entry is read as m - 1 (the tree's
+// outputs are then those of that reading; callers report HCI_DS_TREE).  Returns whether every
+// entry was valid (the same on every thread).  Ends with a barrier.
+__device__ __forceinline__ bool tree_build(int p, int n, const TreeAnc& t, int* flag) {
     const int tid = threadIdx.x;
     if (tid == 0) *flag = 1;
     __syncthreads();
     if (tid < n) {
-        const int p = parent[tid];
         const bool ok = tree_parent_ok(tid, p);
         if (!ok) *flag = 0;                          // every writer stores the same value
         t.par[tid] = (uint8_t)(tid == 0 ? 0 : (ok ? p : tid - 1));
@@ -74,10 +73,11 @@ __device__ __forceinline__ bool tree_build(const int32_t* __restrict__ parent, i
 }
 
 // LDS of the tree conv role: the ancestor table, a flag word, the nodes of every depth as bit
-// masks [64], then (16-byte aligned) floats: short window + x rows, outer window + f rows, chunk
-// sums of g, outer taps, short taps.
+// masks [64], the owner of every node [64] (u32) and whether it has a child [64] (bytes), then
+// (16-byte aligned) floats: short window + x rows, outer window + f rows, chunk sums of g, outer
+// taps, short taps.
 __host__ __device__ inline size_t tree_conv_head_bytes() {
-    return (kTreeAncBytes + 16 + kTreeMax * 8 + 15) / 16 * 16;
+    return (kTreeAncBytes + 16 + kTreeMax * 8 + kTreeMax * 4 + kTreeMax + 15) / 16 * 16;
 }
 __host__ __device__ inline size_t tree_conv_lds_bytes(int Ts, int To, int n) {
     const size_t floats = (size_t)((Ts - 1 + n) + (To - 1 + n) + kFirChunks * n + To + Ts) * kCG;
@@ -99,6 +99,8 @@ __device__ __forceinline__ uint32_t tree_conv_block(
     const TreeAnc t = tree_anc_lds(lds_raw);
     int* flag = (int*)((char*)lds_raw + kTreeAncBytes);
     uint64_t* dmask = (uint64_t*)((char*)lds_raw + kTreeAncBytes + 16);   // [64]: the nodes of depth D
+    uint32_t* owner = (uint32_t*)(dmask + kTreeMax);     // [64]: the first leaf (index order) below a node
+    uint8_t* haschild = (uint8_t*)(owner + kTreeMax);    // [64]
     float* xs = (float*)((char*)lds_raw + tree_conv_head_bytes());  // [Ws + n][kCG]
     float* fb = xs + (size_t)(Ws + n) * kCG;          // [W + n][kCG]: outer window rows, then f rows
     float* gl = fb + (size_t)(W + n) * kCG;           // [kFirChunks][n][kCG]: chunk sums of g
@@ -114,47 +116,88 @@ __device__ __forceinline__ uint32_t tree_conv_block(
     const float* ow = outer_win + (size_t)b * W * d;
     const typename Act<ACT>::T* xb = x + (size_t)b * n * d;
 
-    // every load of the workgroup in one round (values to registers first; the common sizes, up
-    // to 128 window rows and taps and 64 nodes, then the rest by plain loops), in flight while the
-    // ancestor table is built
+    // The parent entries are requested first: loads return in order, so the ancestor table, the
+    // leaves and the owners below are built while the window, tap, input and IIR parameter loads
+    // are still in flight.
+    const int pin = parent[(size_t)b * n + min(tid, n - 1)];     // used for tid < n only
+    asm volatile("" ::: "memory");                  // issued before every load below
+
+    // every other load of the workgroup in one round (values to registers first; the common
+    // sizes, up to 128 window rows and taps and 64 nodes, then the rest by plain loops)
+    // Every load is unconditional, from a clamped (always valid) address, its value masked where
+    // it is stored: with no branch around a load the compiler counts the loads in flight exactly
+    // and waits for each one only where it is used; activations stay raw bits until then (a
+    // conversion next to a load would wait for it there).
     constexpr int SW = 8, SX = 4;                       // rows per thread of the register batch
-    float vw[SW], vt[SW], vx[SX], vsw, vst;
+    const int chc = min(ch, d - 1);
+    float vw[SW], vt[SW], vst;
+    typename ActRaw<ACT>::R rx[SX], rsw;
 #pragma unroll
     for (int u = 0; u < SW; ++u) {
         const int r = row + 16 * u;
-        vw[u] = live && r < W ? ow[(size_t)r * d + ch] : 0.f;
-        vt[u] = live && r < To ? w_outer[(size_t)r * d + ch] : 0.f;
+        vw[u] = (W > 0 ? ow + (size_t)min(r, W - 1) * d : w_outer)[chc];     // no window: any valid row
+        vt[u] = w_outer[(size_t)min(r, To - 1) * d + chc];
     }
 #pragma unroll
-    for (int u = 0; u < SX; ++u) {
-        const int r = row + 16 * u;
-        vx[u] = live && r < n ? Act<ACT>::load(xb, (size_t)r * d + ch) : 0.f;
-    }
-    vsw = live && row < Ws ? Act<ACT>::load(sw, (size_t)row * d + ch) : 0.f;
-    vst = live && row < Ts ? w_short[(size_t)row * d + ch] : 0.f;
+    for (int u = 0; u < SX; ++u) rx[u] = ActRaw<ACT>::load(xb, (size_t)min(row + 16 * u, n - 1) * d + chc);
+    rsw = ActRaw<ACT>::load(Ws > 0 ? sw + (size_t)min(row, Ws - 1) * d : xb, chc);
+    vst = w_short[(size_t)min(row, Ts - 1) * d + chc];
 
-    const bool valid = tree_build(parent + (size_t)b * n, n, t, flag);
-    // the nodes of every depth (n <= 64: one lane per node), published by the barrier below
+    // IIR task of this thread (channel ch0 + tch, poles 4 tg .. 4 tg + 3 of one root-to-leaf path
+    // per wave and pass) and its parameters, used after the FIR
+    const int G = N <= 4 ? 1 : N <= 8 ? 2 : 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tg = lane % G, tch = (lane / G) % kCG;
+    const int chn = ch0 + tch;
+    const bool task_lane = lane < kCG * G;
+    const bool scan = task_lane && chn < d;
+    float lm[4], bt[4], cv[4], s0[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const size_t o = (size_t)min(chn, d - 1) * N + min(4 * tg + q, N - 1);
+        lm[q] = lam[o];
+        bt[q] = beta[o];
+        cv[q] = cc[o];
+        s0[q] = iir[(size_t)b * d * N + o];
+    }
+
+    if (tid < kTreeMax) {
+        owner[tid] = kTreeMax;
+        haschild[tid] = 0;
+    }
+    const bool valid = tree_build(pin, n, t, flag);     // its first barrier publishes the two arrays
+    // the nodes of every depth (n <= 64: one lane per node) and the leaves (no child)
     const int dl = lane < n ? (int)t.depth[lane] : -1;
     const int maxD = wave_max_i32(dl);
     for (int D = 0; D <= maxD; ++D) {
         const uint64_t mk = __ballot(dl == D);
         if (tid == 0) dmask[D] = mk;
     }
+    if (tid > 0 && tid < n) haschild[t.par[tid]] = 1;
+    __syncthreads();
+    const bool is_leaf = lane < n && haschild[lane] == 0;
+    const uint64_t leafmask = __ballot(is_leaf);
+    const int nl = __popcll(leafmask);
+    // a node is stored by the first leaf below it in index order: every leaf takes the minimum
+    // over the nodes of its root path (published by the barrier after the LDS stores below)
+    if (tid < n && is_leaf) {
+        const uint8_t* am = t.anc + tid * kTreeMax;
+        for (int j = 0; j <= dl; ++j) atomicMin(&owner[am[j]], (uint32_t)tid);
+    }
 
 #pragma unroll
     for (int u = 0; u < SW; ++u) {
         const int r = row + 16 * u;
-        if (r < W) fb[r * kCG + cl] = vw[u];
-        if (r < To) wl[r * kCG + cl] = vt[u];
+        if (r < W) fb[r * kCG + cl] = keep_if(vw[u], live);
+        if (r < To) wl[r * kCG + cl] = keep_if(vt[u], live);
     }
 #pragma unroll
     for (int u = 0; u < SX; ++u) {
         const int r = row + 16 * u;
-        if (r < n) xs[(Ws + r) * kCG + cl] = vx[u];
+        if (r < n) xs[(Ws + r) * kCG + cl] = keep_if(ActRaw<ACT>::cvt(rx[u]), live);
     }
-    if (row < Ws) xs[row * kCG + cl] = vsw;
-    if (row < Ts) ws[row * kCG + cl] = vst;
+    if (row < Ws) xs[row * kCG + cl] = keep_if(ActRaw<ACT>::cvt(rsw), live);
+    if (row < Ts) ws[row * kCG + cl] = keep_if(vst, live);
     for (int r = row + 16 * SW; r < W; r += kConvT / kCG) fb[r * kCG + cl] = live ? ow[(size_t)r * d + ch] : 0.f;
     for (int r = row + 16 * SW; r < To; r += kConvT / kCG) wl[r * kCG + cl] = live ? w_outer[(size_t)r * d + ch] : 0.f;
     for (int r = row + 16 * SX; r < n; r += kConvT / kCG) xs[(Ws + r) * kCG + cl] = live ? Act<ACT>::load(xb, (size_t)r * d + ch) : 0.f;
@@ -217,44 +260,19 @@ __device__ __forceinline__ uint32_t tree_conv_block(
     }
     __syncthreads();
 
-    // leaves and owners, lane m of every wave standing for node m: a node is a leaf when no node
-    // one level deeper has it as parent; it is stored by the first leaf below it in index order
-    bool is_leaf = false;
-    if (lane < n) {
-        is_leaf = true;
-        if (dl < maxD)
-            for (uint64_t mk = dmask[dl + 1]; mk != 0; mk &= mk - 1)
-                if (t.par[__builtin_ctzll(mk)] == lane) { is_leaf = false; break; }
-    }
-    const uint64_t leafmask = __ballot(is_leaf);
-    const int nl = __popcll(leafmask);
-    int minleaf = kTreeMax;
-    if (lane < n)
-        for (uint64_t mk = leafmask; mk != 0; mk &= mk - 1) {
-            const int L = __builtin_ctzll(mk), dL = t.depth[L];
-            if (dL >= dl && t.anc[L * kTreeMax + (dL - dl)] == lane) { minleaf = L; break; }
-        }
-
     // IIR along the tree, one root-to-leaf path per wave and pass: the path's nodes in order from
     // the root (lane j holds the node j steps above the leaf), each state s = fma(lambda, s_parent,
     // beta * g) kept in registers, the next node's input read ahead.  A node on several paths is
     // computed by each of them with the same arithmetic (the same bits) and stored by its owner.
-    const int G = N <= 4 ? 1 : N <= 8 ? 2 : 4;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tg = lane % G, tch = (lane / G) % kCG;
-    const int chn = ch0 + tch;
-    const bool task_lane = lane < kCG * G;
-    const bool scan = task_lane && chn < d;
-    float lm[4], bt[4], cv[4], s0[4];
+    const int minleaf = lane < n ? (int)owner[lane] : kTreeMax;
+    // the IIR parameters of a lane past the channels or poles are zero
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int pn = 4 * tg + q;
-        const bool ok = scan && pn < N;
-        const size_t o = (size_t)chn * N + pn;
-        lm[q] = ok ? lam[o] : 0.f;
-        bt[q] = ok ? beta[o] : 0.f;
-        cv[q] = ok ? cc[o] : 0.f;
-        s0[q] = ok ? iir[(size_t)b * d * N + o] : 0.f;
+        const bool ok = scan && 4 * tg + q < N;
+        lm[q] = keep_if(lm[q], ok);
+        bt[q] = keep_if(bt[q], ok);
+        cv[q] = keep_if(cv[q], ok);
+        s0[q] = keep_if(s0[q], ok);
     }
     // g of node m: the chunk sums in chunk order
     auto g_of = [&](int m) -> float {
