@@ -30,6 +30,7 @@
 // forwards give identical bits for f, s and y.
 #pragma once
 
+#include "act_raw.h"
 #include "hci_internal.h"
 
 namespace hci {
@@ -43,21 +44,6 @@ constexpr int kFirChunks = 4;  // tap chunks of the outer FIR (their sums are ad
 __host__ __device__ inline size_t conv_iir_lds_floats(int Ts, int To, int R) {
     return (size_t)((Ts - 1 + R) + (To - 1 + R) + kFirChunks * R + To + Ts) * kCG;
 }
-
-// Raw bits of one activation (a 16-bit load for bf16) and their value: the conversion is applied
-// where the value is used, so that a batch of loads stays in flight (a conversion right after a
-// load makes the compiler wait for that load there, and loads complete in order).
-template <int ACT> struct ActRaw;
-template <> struct ActRaw<HCI_F32> {
-    typedef float R;
-    __device__ static __forceinline__ R load(const float* p, size_t i) { return p[i]; }
-    __device__ static __forceinline__ float cvt(R r) { return r; }
-};
-template <> struct ActRaw<HCI_BF16> {
-    typedef uint32_t R;
-    __device__ static __forceinline__ R load(const uint16_t* p, size_t i) { return p[i]; }
-    __device__ static __forceinline__ float cvt(R r) { return __uint_as_float(r << 16); }
-};
 
 // Sum over the G lanes of an aligned group (G = 1, 2, 4, 8 or 16), the same bits on every
 // lane of the group: lane offsets G/2, ..., 2, 1 in turn.  Offsets 2 and 1 are quad

@@ -11,6 +11,7 @@
 //   2  KV rows kv_len .. kv_len+k <- block k/v rows 0..k of c* (tiled layout)
 // k_slice_len then advances kv_len; it runs after every role of k_slice has
 // read the old length (stream order).
+#include "act_raw.h"
 #include "hci_internal.h"
 
 namespace hci {
@@ -64,17 +65,35 @@ __device__ void window_update(typename Act<ACT>::T* win, const typename Act<ACT>
 {
     // new[r] = concat(old[0..W), rows[0..k])[k+1+r] for r < W.  Rows are
     // processed in ascending chunks; chunk [r0, r0+128) reads old rows at or
-    // above r0+k+1, which no earlier chunk has overwritten.
+    // above r0+k+1, which no earlier chunk has overwritten.  A thread's rows of
+    // a chunk are loaded in one round (unconditional loads from clamped rows and
+    // channels, raw bits until they are staged), so their latencies overlap.
+    constexpr int RPT = kSliceWinMax / kSliceRows;     // rows per thread and chunk
     const int tid = threadIdx.x, cl = tid % kSliceCG, part = tid / kSliceCG;
     const int ch = ch0 + cl;
+    const int chc = min(ch, d - 1);
     for (int r0 = 0; r0 < W; r0 += kSliceWinMax) {
         const int r1 = min(W, r0 + kSliceWinMax);
-        for (int r = r0 + part; r < r1; r += kSliceRows) {
-            const int m = k + 1 + r;
-            float v = 0.f;
-            if (ch < d) v = (m < W) ? Act<ACT>::load(win, (size_t)m * d + ch)
-                                    : Act<ACT>::load(blk_rows, (size_t)row_of(rmap, m - W) * d + ch);
-            stage[r - r0][cl] = v;
+        // block rows first through the path (a token tree), all in one round
+        int rb[RPT];
+        if (rmap) {
+#pragma unroll
+            for (int u = 0; u < RPT; ++u) rb[u] = rmap[max(k + 1 + min(r0 + part + u * kSliceRows, r1 - 1) - W, 0)];
+        } else {
+#pragma unroll
+            for (int u = 0; u < RPT; ++u) rb[u] = max(k + 1 + min(r0 + part + u * kSliceRows, r1 - 1) - W, 0);
+        }
+        typename ActRaw<ACT>::R v[RPT];
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int m = k + 1 + min(r0 + part + u * kSliceRows, r1 - 1);
+            const typename Act<ACT>::T* src = m < W ? win + (size_t)m * d : blk_rows + (size_t)rb[u] * d;
+            v[u] = ActRaw<ACT>::load(src, chc);
+        }
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int r = r0 + part + u * kSliceRows;
+            if (r < r1) stage[r - r0][cl] = ch < d ? ActRaw<ACT>::cvt(v[u]) : 0.f;
         }
         __syncthreads();
         for (int r = r0 + part; r < r1; r += kSliceRows)
