@@ -112,11 +112,13 @@ __device__ void wave_row_argmax(const float* z, int V, int lane, int& arg, doubl
     bool nonfin = false;
     for (int j0 = 0; j0 < V; j0 += 64 * kLaneBatch) {
         float v[kLaneBatch];
+        // unconditional loads from clamped ids (no branch around a load, so the batch stays in
+        // flight), masked afterwards
 #pragma unroll
-        for (int e = 0; e < kLaneBatch; ++e) {
-            const int j = j0 + e * 64 + lane;
-            v[e] = j < V ? z[j] : -INFINITY;
-        }
+        for (int e = 0; e < kLaneBatch; ++e) v[e] = z[min(j0 + e * 64 + lane, V - 1)];
+#pragma unroll
+        for (int e = 0; e < kLaneBatch; ++e)
+            if (j0 + e * 64 + lane >= V) v[e] = -INFINITY;
 #pragma unroll
         for (int e = 0; e < kLaneBatch; ++e) {     // ascending ids per lane
             const int j = j0 + e * 64 + lane;
@@ -166,11 +168,15 @@ __device__ void wave_row_argmax(const float* z, int V, int lane, int& arg, doubl
 __device__ void wave_row_stats(const float* z, int V, double T, int lane, double& mx, double& sum,
                                int tok = -1, float* ztok = nullptr, double* ecache = nullptr) {
     if (V <= 64 * kLaneBatch) {
+        // unconditional loads from clamped ids (no branch around a load and no use of a value
+        // before the last load is issued, so the batch stays in flight), masked afterwards
         float v[kLaneBatch];
+#pragma unroll
+        for (int e = 0; e < kLaneBatch; ++e) v[e] = z[min(e * 64 + lane, V - 1)];
 #pragma unroll
         for (int e = 0; e < kLaneBatch; ++e) {
             const int j = e * 64 + lane;
-            v[e] = j < V ? z[j] : -INFINITY;
+            if (j >= V) v[e] = -INFINITY;
             if (ztok && j == tok) *ztok = v[e];
         }
         double xs[kLaneBatch];
@@ -197,10 +203,10 @@ __device__ void wave_row_stats(const float* z, int V, double T, int lane, double
     for (int j0 = 0; j0 < V; j0 += 64 * kLaneBatch) {
         float v[kLaneBatch];
 #pragma unroll
-        for (int e = 0; e < kLaneBatch; ++e) {
-            const int j = j0 + e * 64 + lane;
-            v[e] = j < V ? z[j] : -INFINITY;
-        }
+        for (int e = 0; e < kLaneBatch; ++e) v[e] = z[min(j0 + e * 64 + lane, V - 1)];
+#pragma unroll
+        for (int e = 0; e < kLaneBatch; ++e)
+            if (j0 + e * 64 + lane >= V) v[e] = -INFINITY;
 #pragma unroll
         for (int e = 0; e < kLaneBatch; ++e) {
             m = fmax(m, over_T((double)v[e], T));
@@ -212,10 +218,10 @@ __device__ void wave_row_stats(const float* z, int V, double T, int lane, double
     for (int j0 = 0; j0 < V; j0 += 64 * kLaneBatch) {
         float v[kLaneBatch];
 #pragma unroll
-        for (int e = 0; e < kLaneBatch; ++e) {
-            const int j = j0 + e * 64 + lane;
-            v[e] = j < V ? z[j] : 0.f;
-        }
+        for (int e = 0; e < kLaneBatch; ++e) v[e] = z[min(j0 + e * 64 + lane, V - 1)];
+#pragma unroll
+        for (int e = 0; e < kLaneBatch; ++e)
+            if (j0 + e * 64 + lane >= V) v[e] = 0.f;
 #pragma unroll
         for (int e = 0; e < kLaneBatch; ++e)
             if (j0 + e * 64 + lane < V) s += exp(over_T((double)v[e], T) - m);
