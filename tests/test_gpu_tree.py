@@ -111,13 +111,20 @@ def test_tree_verify_parity_bf16(kind, n, lens):
     _check_verify(TreeCase(cfg, parent, tokens))
 
 
-@pytest.mark.parametrize("act", ["f32", "bf16"])
-def test_tree_conv_bits_equal_the_chain_over_each_path(act):
-    """f, s and y of every node carry the bits of the chain verify over its root-to-node path."""
+@pytest.mark.parametrize("act,shape", [("f32", "random"), ("bf16", "random"), ("f32", "trie"), ("bf16", "trie")])
+def test_tree_conv_bits_equal_the_chain_over_each_path(act, shape):
+    """f, s and y of every node carry the bits of the chain verify over its root-to-node path: a
+    random 30-node tree (many root-to-leaf paths: the per-node FIR) and a trie of four candidate
+    blocks sharing prefixes (few paths: the FIR along each path)."""
     cfg = synth.scaled(synth.CONFIGS["tiny"], vocab=64) if act == "f32" else _small_bf16((700,))
     rng = np.random.default_rng(21)
-    n = 30
-    parent = synth.random_tree(n, "random", rng)[None]
+    if shape == "random":
+        n = 30
+        parent = synth.random_tree(n, "random", rng)[None]
+    else:
+        tr = synth.tree_round(synth.scaled(cfg, nc=4, gamma=12, vocab=4, kv_lens=cfg.kv_lens[:1]))
+        parent = tr["parent"][:1]
+        n = parent.shape[1]
     tokens = rng.integers(0, cfg.vocab, (1, n))
     tc = TreeCase(cfg, parent, tokens)
     say(f"tree vs chain bits ({act})")
