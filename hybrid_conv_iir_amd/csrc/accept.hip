@@ -894,12 +894,24 @@ __global__ __launch_bounds__(64) void k_draft_sample(int gamma, int V, double T,
     prev = prev < 0 ? 0 : (prev >= V ? V - 1 : prev);
     for (int m = 0; m < gamma; ++m) {
         const size_t r = ((size_t)b * gamma + m) * V;
-        float l[PER];
+        // the run's logits and bias entries in one batch: unconditional loads from clamped ids
+        // (no branch around a load, no value used before the last load is issued), masked after
+        float zl[PER], bl[PER], l[PER];
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+            const int j = min(j0 + t, V - 1);
+            zl[t] = z[r + j];
+            bl[t] = markov[(size_t)prev * V + j];
+        }
+        // every value in hand before any is used under a condition (which would otherwise pull
+        // its load into that branch)
+#pragma unroll
+        for (int t = 0; t < PER; ++t) asm volatile("" : "+v"(zl[t]), "+v"(bl[t]));
         double mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < PER; ++t) {
             const int j = j0 + t;
-            l[t] = t < n ? z[r + j] + markov[(size_t)prev * V + j] : -INFINITY;
+            l[t] = t < n ? zl[t] + bl[t] : -INFINITY;
             if (t < n) {
                 dl[r + j] = l[t];
                 mx = fmax(mx, over_T((double)l[t], T));
