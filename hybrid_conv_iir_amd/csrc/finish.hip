@@ -105,7 +105,10 @@ __device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, 
     float* st_ml = st_o + (size_t)(kCombW + 1) * RG * DH;           // [state][row][2]
     float* pwt = st_ml + (size_t)(kCombW + 1) * RG * 2 + 64 * wave; // [wave][64] block weights
     // token trees: ancestor masks [64] (8-byte aligned) and pointer-doubling jumps [64]
-    uint64_t* tmask = (uint64_t*)(((uintptr_t)(st_ml + (size_t)(kCombW + 1) * RG * 2 + 64 * kCombW) + 7) & ~(uintptr_t)7);
+    // (an even float offset from the 16-byte aligned LDS base: 8-byte aligned; pointer arithmetic
+    // on the LDS array, not on integers, so that the accesses stay LDS instructions)
+    const size_t moff = ((size_t)(st_ml - lds) + (size_t)(kCombW + 1) * RG * 2 + 64 * kCombW + 1) & ~(size_t)1;
+    uint64_t* tmask = (uint64_t*)(lds + moff);
     uint8_t* tjump = (uint8_t*)(tmask + 64);
     auto krow = [&](int j) { return (const T*)(ks + (size_t)j * RS); };
     auto vrow = [&](int j) { return (const T*)(vs + (size_t)j * RS); };
@@ -238,10 +241,19 @@ __device__ __forceinline__ void combine_job(const FinishArgs& A, int c, int rg, 
         // itself (a token tree; every ancestor has a lower index)
         const uint64_t vis = tree ? tmask[i] : ~0ull;
         const T* qrow = q + (((size_t)b * nq + r0 + k) * H + h) * DH + sl * DS;
+        // the query slice: every 16-byte piece requested first (from clamped, always valid
+        // offsets; pieces past DS are not used), then converted, so the loads are in flight
+        // together instead of one conversion waiting for each
+        constexpr int QP = (kF32Dh / 4) * (int)sizeof(T) / 16;          // pieces of a full slice
+        uint4 qr[QP];
+#pragma unroll
+        for (int pc = 0; pc < QP; ++pc)
+            qr[pc] = *(const uint4*)(qrow + min(pc * 16 / (int)sizeof(T), DS - 16 / (int)sizeof(T)));
+#pragma unroll
+        for (int pc = 0; pc < QP; ++pc) asm volatile("" : "+v"(qr[pc].x), "+v"(qr[pc].y), "+v"(qr[pc].z), "+v"(qr[pc].w));
         float qv[kF32Dh / 4];
 #pragma unroll
-        for (int e0 = 0; e0 < kF32Dh / 4; e0 += 8)
-            if (e0 < DS) load8<ACT>(qrow + e0, qv + e0);
+        for (int e0 = 0; e0 < kF32Dh / 4; e0 += 8) load8<ACT>((const T*)qr + e0, qv + e0);
         float mb = -INFINITY;
         for (int j0 = 0; j0 <= i; j0 += 16) {
             const int j = j0 + jj;
