@@ -183,18 +183,21 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(const uint16_t* __restrict__ x
     const uint16_t* xr = x + (size_t)blockIdx.x * K;
     uint16_t* yr = y + (size_t)blockIdx.x * K;
     const int nw = blockDim.x >> 6;
-    float v[8];
+    float v[8], g[8];
     float s = 0.f;
     if (VEC) {
-        for (int i = 0; i < 8; ++i) v[i] = 0.f;
-        const int k0 = 8 * threadIdx.x;
-        if (k0 < K) {
-            const u32x4 w = *(const u32x4*)(xr + k0);
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-            for (int i = 0; i < 4; ++i) {
-                v[2 * i] = __uint_as_float(ws[i] << 16);
-                v[2 * i + 1] = __uint_as_float(ws[i] & 0xffff0000u);
-            }
+        // the row's eight values and their eight gains requested together (clamped, always valid
+        // offsets; a thread past K contributes zeros and stores nothing), so the gains are in hand
+        // when the sum of squares is
+        const int k0 = 8 * threadIdx.x, kc = min(k0, K - 8);
+        const u32x4 w = *(const u32x4*)(xr + kc);
+        const float4 g0 = *(const float4*)(gamma + kc), g1 = *(const float4*)(gamma + kc + 4);
+        g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+        g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = k0 < K ? __uint_as_float(ws[i] << 16) : 0.f;
+            v[2 * i + 1] = k0 < K ? __uint_as_float(ws[i] & 0xffff0000u) : 0.f;
         }
         for (int i = 0; i < 8; ++i) s = fmaf(v[i], v[i], s);
     } else {
@@ -214,8 +217,8 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(const uint16_t* __restrict__ x
         if (k0 < K) {
             uint32_t o[4];
             for (int i = 0; i < 4; ++i)
-                o[i] = (uint32_t)f2bf(v[2 * i] * inv * gamma[k0 + 2 * i]) |
-                       ((uint32_t)f2bf(v[2 * i + 1] * inv * gamma[k0 + 2 * i + 1]) << 16);
+                o[i] = (uint32_t)f2bf(v[2 * i] * inv * g[2 * i]) |
+                       ((uint32_t)f2bf(v[2 * i + 1] * inv * g[2 * i + 1]) << 16);
             *(u32x4*)(yr + k0) = u32x4{o[0], o[1], o[2], o[3]};
         }
     } else {
@@ -285,7 +288,8 @@ hipError_t launch_linear_pack(int K, int N, const void* w, void* wp, hipStream_t
 
 hipError_t launch_rmsnorm(int M, int K, const void* x, const float* g, float eps, void* y, hipStream_t st)
 {
-    const bool vec = K % 8 == 0 && K <= 8 * 1024 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)y % 16) == 0;
+    const bool vec = K % 8 == 0 && K <= 8 * 1024 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)y % 16) == 0 &&
+                     ((uintptr_t)g % 16) == 0;
     if (vec) {
         const int threads = ((K / 8 + 63) / 64) * 64;
         hipLaunchKernelGGL(k_rmsnorm<true>, dim3(M), dim3(threads), 0, st, (const uint16_t*)x, g, eps, (uint16_t*)y,

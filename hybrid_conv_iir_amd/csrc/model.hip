@@ -50,8 +50,71 @@ __global__ __launch_bounds__(256) void k_hyena_mixer(
     float* hl = ub + (size_t)(KIND == HCI_MIX_FIR ? Wl + P : P) * kMxCG;   // FIR: [Tl][16]
     const int tid = threadIdx.x;
 
-    // short FIR of the three streams over [window ; block rows]
-    for (int e = tid; e < 3 * P * kMxCG; e += blockDim.x) {
+    // Every load of the workgroup in one round, to registers first: the short FIR's inputs and
+    // taps of the thread's elements (three streams over [window ; block rows]), the long window
+    // and taps (FIR kind), the IIR parameters and state (IIR kind).  The loads are unconditional,
+    // from clamped (always valid) addresses, and the values are masked where they are used, so
+    // they are in flight together (a load under a condition, or a value used right after its
+    // load, makes the compiler wait for it there); the batches cover the common sizes, plain
+    // loops the rest.
+    constexpr int EZ = 3, JT = 4, EL = 8;               // short-FIR elements, short taps, long rows per thread
+    const int nz = 3 * P * kMxCG;
+    float zv[EZ][JT], zw[EZ][JT];
+#pragma unroll
+    for (int u = 0; u < EZ; ++u) {
+        const int e = min(tid + u * (int)blockDim.x, nz - 1);
+        const int c = e % kMxCG, i = (e / kMxCG) % P, sidx = e / (kMxCG * P);
+        const int chc = min(ch0 + c, d - 1), col = sidx * d + chc;
+#pragma unroll
+        for (int j = 0; j < JT; ++j) {
+            const int jj = min(j, Ts - 1), m = i - jj;
+            const float* src = m >= 0 ? z + ((size_t)sidx * rows + row0 + m) * d + chc
+                                      : short_win + ((size_t)b * Ws + (Ws + m)) * 3 * d + col;
+            zv[u][j] = *src;
+            zw[u][j] = w_short[(size_t)jj * 3 * d + col];
+        }
+    }
+    float lw[EL], lt[EL];
+    if (KIND == HCI_MIX_FIR) {
+        const int chc = min(ch0 + tid % kMxCG, d - 1);
+#pragma unroll
+        for (int u = 0; u < EL; ++u) {
+            const int r = (tid + u * (int)blockDim.x) / kMxCG;
+            lw[u] = Wl > 0 ? long_win[((size_t)b * Wl + min(r, Wl - 1)) * d + chc] : 0.f;
+            lt[u] = w_long[(size_t)min(r, Tl - 1) * d + chc];
+        }
+    }
+    // IIR kind: 16 channels x 16 pole lanes
+    const int ic = tid >> 4, in = tid & 15, ich = ch0 + ic;
+    float il = 0.f, ibt = 0.f, icv = 0.f, is0 = 0.f;
+    if (KIND != HCI_MIX_FIR) {
+        const size_t o = (size_t)min(ich, d - 1) * N + min(in, N - 1);
+        il = lam[o];
+        ibt = beta[o];
+        icv = cc[o];
+        is0 = iir[(size_t)b * d * N + o];
+    }
+#pragma unroll
+    for (int u = 0; u < EZ; ++u) {
+        const int e = tid + u * (int)blockDim.x;
+        if (e >= nz) break;
+        const int c = e % kMxCG, i = (e / kMxCG) % P, sidx = e / (kMxCG * P);
+        const int ch = ch0 + c, col = sidx * d + ch;
+        float acc = 0.f;
+        if (ch < d) {
+#pragma unroll
+            for (int j = 0; j < JT; ++j)
+                if (j < Ts) acc = fmaf(zw[u][j], zv[u][j], acc);
+            for (int j = JT; j < Ts; ++j) {
+                const int m = i - j;
+                const float v = m >= 0 ? z[((size_t)sidx * rows + row0 + m) * d + ch]
+                                       : short_win[((size_t)b * Ws + (Ws + m)) * 3 * d + col];
+                acc = fmaf(w_short[(size_t)j * 3 * d + col], v, acc);
+            }
+        }
+        zh[e] = acc;
+    }
+    for (int e = tid + EZ * (int)blockDim.x; e < nz; e += blockDim.x) {
         const int c = e % kMxCG, i = (e / kMxCG) % P, sidx = e / (kMxCG * P);
         const int ch = ch0 + c;
         float acc = 0.f;
@@ -67,11 +130,18 @@ __global__ __launch_bounds__(256) void k_hyena_mixer(
         zh[e] = acc;
     }
     if (KIND == HCI_MIX_FIR) {
-        for (int e = tid; e < Wl * kMxCG; e += blockDim.x) {
+        const bool live = ch0 + tid % kMxCG < d;
+#pragma unroll
+        for (int u = 0; u < EL; ++u) {
+            const int e = tid + u * (int)blockDim.x;
+            if (e < Wl * kMxCG) ub[e] = live ? lw[u] : 0.f;
+            if (e < Tl * kMxCG) hl[e] = live ? lt[u] : 0.f;
+        }
+        for (int e = tid + EL * (int)blockDim.x; e < Wl * kMxCG; e += blockDim.x) {
             const int ch = ch0 + e % kMxCG, r = e / kMxCG;
             ub[e] = ch < d ? long_win[((size_t)b * Wl + r) * d + ch] : 0.f;
         }
-        for (int e = tid; e < Tl * kMxCG; e += blockDim.x) {
+        for (int e = tid + EL * (int)blockDim.x; e < Tl * kMxCG; e += blockDim.x) {
             const int ch = ch0 + e % kMxCG, j = e / kMxCG;
             hl[e] = ch < d ? w_long[(size_t)j * d + ch] : 0.f;
         }
@@ -94,20 +164,22 @@ __global__ __launch_bounds__(256) void k_hyena_mixer(
             y[(row0 + i) * d + ch] = f2bf(zh[(size_t)i * kMxCG + c] * h);
         }
     } else {
-        // 16 channels x 16 pole lanes; the readout sums the pole lanes by butterfly
-        const int c = tid >> 4, n = tid & 15, ch = ch0 + c;
+        // 16 channels x 16 pole lanes (parameters loaded above); the readout sums the pole lanes
+        // by butterfly
+        const int c = ic, n = in, ch = ich;
         const bool ok = ch < d && n < N;
-        const size_t o = (size_t)ch * N + n;
-        const float l = ok ? lam[o] : 0.f, bt = ok ? beta[o] : 0.f, cv = ok ? cc[o] : 0.f;
-        float s = ok ? iir[(size_t)b * d * N + o] : 0.f;
+        const float l = ok ? il : 0.f, bt = ok ? ibt : 0.f, cv = ok ? icv : 0.f;
+        float s = ok ? is0 : 0.f;
         for (int i = 0; i < P; ++i) {
             s = fmaf(l, s, bt * ub[i * kMxCG + c]);
             if (ok) s_out[((row0 + i) * d + ch) * N + n] = s;
+            // the 16 pole lanes of a channel are one row of the wave: their sum by row rotations
+            // on the vector ALU (lane 0 of the row holds a fixed-order result)
             float part = cv * s;
-            part += __shfl_xor(part, 8);
-            part += __shfl_xor(part, 4);
-            part += __shfl_xor(part, 2);
-            part += __shfl_xor(part, 1);
+            part += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(part), 0x128, 0xF, 0xF, false));  // row_ror:8
+            part += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(part), 0x124, 0xF, 0xF, false));  // row_ror:4
+            part += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(part), 0x122, 0xF, 0xF, false));  // row_ror:2
+            part += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(part), 0x121, 0xF, 0xF, false));  // row_ror:1
             if (n == 0 && ch < d) y[(row0 + i) * d + ch] = f2bf(zh[(size_t)i * kMxCG + c] * part);
         }
     }
