@@ -43,11 +43,31 @@ __global__ __launch_bounds__(64) void k_draft_attn(const uint16_t* __restrict__ 
     const int d = H * DH, nk = W + i + 1;                  // the window and block keys 0..i
     const size_t rows = (size_t)nb * (W + gamma);
     const uint16_t* qrow = qkv + ((size_t)nb * W + (size_t)b * gamma + i) * d + h * DH;
+    // The query and the lane's two key rows are requested in one round (keys past nk from a
+    // clamped, always valid row, their scores masked), every piece in hand before any is
+    // converted: a conversion right after a load makes the compiler wait for that load there.
+    u32x4 qr[16], kr[2][16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) qr[c] = *(const u32x4*)(qrow + 8 * c);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int j = min(lane + 64 * u, nk - 1);
+        const size_t row = j < W ? (size_t)b * W + j : (size_t)nb * W + (size_t)b * gamma + (j - W);
+        const uint16_t* krow = qkv + (rows + row) * d + h * DH;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) kr[u][c] = *(const u32x4*)(krow + 8 * c);
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) asm volatile("" : "+v"(qr[c].x), "+v"(qr[c].y), "+v"(qr[c].z), "+v"(qr[c].w));
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            asm volatile("" : "+v"(kr[u][c].x), "+v"(kr[u][c].y), "+v"(kr[u][c].z), "+v"(kr[u][c].w));
     float q[128];
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-        const u32x4 v = *(const u32x4*)(qrow + 8 * c);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t w[4] = {qr[c].x, qr[c].y, qr[c].z, qr[c].w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             q[8 * c + 2 * t] = __uint_as_float(w[t] << 16);
@@ -59,24 +79,18 @@ __global__ __launch_bounds__(64) void k_draft_attn(const uint16_t* __restrict__ 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int j = lane + 64 * u;
-        sc[u] = -INFINITY;
-        if (j < nk) {
-            const size_t row = j < W ? (size_t)b * W + j : (size_t)nb * W + (size_t)b * gamma + (j - W);
-            const uint16_t* krow = qkv + (rows + row) * d + h * DH;
-            float s = 0.f;
+        float s = 0.f;
 #pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const u32x4 v = *(const u32x4*)(krow + 8 * c);
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int c = 0; c < 16; ++c) {
+            const uint32_t w[4] = {kr[u][c].x, kr[u][c].y, kr[u][c].z, kr[u][c].w};
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    s = fmaf(q[8 * c + 2 * t], __uint_as_float(w[t] << 16), s);
-                    s = fmaf(q[8 * c + 2 * t + 1], __uint_as_float(w[t] & 0xffff0000u), s);
-                }
+            for (int t = 0; t < 4; ++t) {
+                s = fmaf(q[8 * c + 2 * t], __uint_as_float(w[t] << 16), s);
+                s = fmaf(q[8 * c + 2 * t + 1], __uint_as_float(w[t] & 0xffff0000u), s);
             }
-            sc[u] = s * scale;
-            mloc = fmaxf(mloc, sc[u]);
         }
+        sc[u] = j < nk ? s * scale : -INFINITY;
+        if (j < nk) mloc = fmaxf(mloc, sc[u]);
     }
     for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
     float sum = 0.f;
@@ -93,13 +107,28 @@ __global__ __launch_bounds__(64) void k_draft_attn(const uint16_t* __restrict__ 
     for (int u = 0; u < 2; ++u)
         if (lane + 64 * u < nk) pr[lane + 64 * u] = sc[u] * inv;
     __syncthreads();
+    // the value rows 32 at a time, each batch requested in one round (rows past nk from a
+    // clamped row, not used), then summed in key order
+    constexpr int VB = 32;
     float a0 = 0.f, a1 = 0.f;
-    for (int j = 0; j < nk; ++j) {
-        const size_t row = j < W ? (size_t)b * W + j : (size_t)nb * W + (size_t)b * gamma + (j - W);
-        const uint32_t v2 = *(const uint32_t*)(qkv + (2 * rows + row) * d + h * DH + 2 * lane);
-        const float p = pr[j];
-        a0 = fmaf(p, __uint_as_float(v2 << 16), a0);
-        a1 = fmaf(p, __uint_as_float(v2 & 0xffff0000u), a1);
+    for (int j0 = 0; j0 < nk; j0 += VB) {
+        uint32_t vv[VB];
+#pragma unroll
+        for (int t = 0; t < VB; ++t) {
+            const int j = min(j0 + t, nk - 1);
+            const size_t row = j < W ? (size_t)b * W + j : (size_t)nb * W + (size_t)b * gamma + (j - W);
+            vv[t] = *(const uint32_t*)(qkv + (2 * rows + row) * d + h * DH + 2 * lane);
+        }
+#pragma unroll
+        for (int t = 0; t < VB; ++t) asm volatile("" : "+v"(vv[t]));
+#pragma unroll
+        for (int t = 0; t < VB; ++t) {
+            if (j0 + t < nk) {
+                const float p = pr[j0 + t];
+                a0 = fmaf(p, __uint_as_float(vv[t] << 16), a0);
+                a1 = fmaf(p, __uint_as_float(vv[t] & 0xffff0000u), a1);
+            }
+        }
     }
     const uint32_t packed = (uint32_t)f2bf(a0) | ((uint32_t)f2bf(a1) << 16);
     *(uint32_t*)(o + ((size_t)b * gamma + i) * d + h * DH + 2 * lane) = packed;
