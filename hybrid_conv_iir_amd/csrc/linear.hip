@@ -227,20 +227,33 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(const uint16_t* __restrict__ x
 }
 
 // Launch shape: CT column strips per workgroup (the largest of 4, 3, 2, 1 that still gives every
-// CU a workgroup), up to 64 rows, and eight waves splitting K.
+// CU a workgroup), up to 64 rows, and eight waves splitting K.  Rows are split over fewer
+// 16-row tiles per workgroup while one strip per workgroup would leave CUs idle (a 64-row window
+// through a 1024-column weight: 64 workgroups with four row tiles each, or 256 with one): the
+// row groups of a strip then read its weight again, from L2 (their workgroups are a multiple of
+// eight apart in the grid, so they share an XCD when the strip count is a multiple of eight), and
+// every sum keeps its order (the waves' K split does not depend on the rows).
 LinearPlan plan_linear(int M, int K, int N) {
     LinearPlan p{};
     const int mts = (M + 15) / 16 < kLinMT ? (M + 15) / 16 : kLinMT;
     p.mt = mts <= 1 ? 1 : (mts <= 2 ? 2 : 4);
     const int NT = N / 16, KT = K / 32;
     const int cus = device_cu_count();
+    while (p.mt > 1 && (long long)NT * ((M + 16 * p.mt - 1) / (16 * p.mt)) < cus) p.mt /= 2;
     const int gy = (M + 16 * p.mt - 1) / (16 * p.mt);
     p.ct = 1;
-    for (int ct = p.mt == 4 ? 2 : 4; ct > 1; --ct)
+    const int ct_max = p.mt == 4 ? 2 : 4;
+    for (int ct = ct_max; ct > 1; --ct)
         if ((long long)((NT + ct - 1) / ct) * gy >= cus) { p.ct = ct; break; }
+    // a grid a little over one workgroup per CU runs in two rounds (one workgroup of this kernel
+    // fits a CU): more strips per workgroup bring it back to one when that is enough
+    // (a 76-row block through a 3072-column weight: 384 -> 192 workgroups)
+    if ((long long)((NT + p.ct - 1) / p.ct) * gy > cus)
+        for (int ct = p.ct + 1; ct <= ct_max; ++ct)
+            if ((long long)((NT + ct - 1) / ct) * gy <= cus) { p.ct = ct; break; }
     p.kw = kLinT / 64;                             // waves past K's end stream nothing
     p.kspw = (KT + p.kw - 1) / p.kw;
-    p.lds = (size_t)p.kw * p.ct * mts * 64 * 4 * sizeof(float);
+    p.lds = (size_t)p.kw * p.ct * (mts < p.mt ? mts : p.mt) * 64 * 4 * sizeof(float);
     p.grid_x = (NT + p.ct - 1) / p.ct;
     p.grid_y = gy;
     return p;
