@@ -976,7 +976,6 @@ hipError_t launch_draft_sample(int nb, int gamma, int V, float temperature, cons
     HCI_DS(1) HCI_DS(2) HCI_DS(4) HCI_DS(8) HCI_DS(16) HCI_DS(32) HCI_DS(64)
 #undef HCI_DS
     return hipErrorInvalidValue;
-    return hipGetLastError();
 }
 
 hipError_t launch_accept(int mode, int nb, int nc, int gamma, int V, float temperature,
