@@ -875,21 +875,30 @@ __global__ __launch_bounds__(256) void k_accept_best(int nb, int nc, const int32
 
 // Serial drafting with the previous-token bias (EvSpark digest, Figure 1(b)): draft m draws from
 // softmax(l / T), l = z[m] + B[prev] in fp32, by the same inverse-CDF rule as the acceptance
-// draws.  One wave per sequence and no barrier: each lane holds a contiguous run of ceil(V/64)
-// token ids in registers, the row maximum, the sum and the scan of the run totals are wave
-// collectives on the vector ALU, and the lane whose run crosses u x total walks it.
-constexpr int kDsMaxPer = 64;              // V <= 4096 on this path
+// draws.  One workgroup of four waves per sequence: each thread holds a contiguous run of
+// ceil(V/256) token ids in registers; the row maximum, the sum and the scan of the run totals
+// are wave collectives on the vector ALU whose four wave results meet in LDS (one barrier per
+// exchange, each exchange with slots of its own, combined in wave order), and the thread whose
+// run crosses u x total walks it.  A draw is bound by its fp64 exp and division work, which four
+// waves split four ways.
+constexpr int kDsW = 4;                    // waves per sequence
+constexpr int kDsT = 64 * kDsW;
+constexpr int kDsMaxPer = 16;              // V <= 4096 on this path
 
-template <int PER>                         // ids per lane, a power of two >= ceil(V / 64)
-__global__ __launch_bounds__(64) void k_draft_sample(int gamma, int V, double T, const float* __restrict__ z,
-                                                     const float* __restrict__ markov,
-                                                     const int32_t* __restrict__ anchor,
-                                                     const double* __restrict__ uni, int32_t* __restrict__ drafts,
-                                                     float* __restrict__ dl, double* __restrict__ margin_out)
+template <int PER>                         // ids per thread, a power of two >= ceil(V / 256)
+__global__ __launch_bounds__(kDsT) void k_draft_sample(int gamma, int V, double T, const float* __restrict__ z,
+                                                       const float* __restrict__ markov,
+                                                       const int32_t* __restrict__ anchor,
+                                                       const double* __restrict__ uni, int32_t* __restrict__ drafts,
+                                                       float* __restrict__ dl, double* __restrict__ margin_out)
 {
-    const int b = blockIdx.x, lane = threadIdx.x;
-    const int per = (V + 63) / 64;
-    const int j0 = min(lane * per, V), j1 = min(j0 + per, V), n = j1 - j0;
+    // the four exchanges of a draw: maximum, sum, scan totals, and the crossing (first id,
+    // last id with weight, smallest distance to the target)
+    __shared__ double x_max[kDsW], x_sum[kDsW], x_tot[kDsW], x_dmin[kDsW];
+    __shared__ int x_first[kDsW], x_last[kDsW];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int per = (V + kDsT - 1) / kDsT;
+    const int j0 = min(tid * per, V), j1 = min(j0 + per, V), n = j1 - j0;
     int prev = anchor[b];
     prev = prev < 0 ? 0 : (prev >= V ? V - 1 : prev);
     for (int m = 0; m < gamma; ++m) {
@@ -918,6 +927,11 @@ __global__ __launch_bounds__(64) void k_draft_sample(int gamma, int V, double T,
             }
         }
         mx = wave_max_f64(mx);
+        if (lane == 0) x_max[wave] = mx;
+        __syncthreads();
+        mx = x_max[0];
+#pragma unroll
+        for (int w = 1; w < kDsW; ++w) mx = fmax(mx, x_max[w]);
         double e[PER];
         double loc = 0.0;
 #pragma unroll
@@ -925,7 +939,12 @@ __global__ __launch_bounds__(64) void k_draft_sample(int gamma, int V, double T,
             e[t] = t < n ? exp(over_T((double)l[t], T) - mx) : 0.0;
             loc += e[t];
         }
-        const double sum = wave_sum_f64(loc);
+        loc = wave_sum_f64(loc);
+        if (lane == 0) x_sum[wave] = loc;
+        __syncthreads();
+        double sum = x_sum[0];
+#pragma unroll
+        for (int w = 1; w < kDsW; ++w) sum += x_sum[w];
         // probabilities p_j = exp(l_j / T - mx) / sum; running sums over ascending ids
         double ploc = 0.0;
 #pragma unroll
@@ -933,8 +952,17 @@ __global__ __launch_bounds__(64) void k_draft_sample(int gamma, int V, double T,
             e[t] = e[t] / sum;
             ploc += e[t];
         }
-        double total;
-        const double incl = wave_incl_scan_f64(ploc, lane, &total);
+        double wtot;
+        double incl = wave_incl_scan_f64(ploc, lane, &wtot);
+        if (lane == 0) x_tot[wave] = wtot;
+        __syncthreads();
+        double off = 0.0, total = x_tot[0];
+#pragma unroll
+        for (int w = 1; w < kDsW; ++w) {
+            if (w == wave) off = total;
+            total += x_tot[w];
+        }
+        incl += off;
         const double excl = incl - ploc;
         const double target = uni[(size_t)b * gamma + m] * total;
         int first = INT_MAX, lastpos = -1;
@@ -952,8 +980,23 @@ __global__ __launch_bounds__(64) void k_draft_sample(int gamma, int V, double T,
         first = wave_min_i32(first);
         lastpos = wave_max_i32(lastpos);
         dmin = wave_min_f64(dmin);
-        const int tok = first != INT_MAX ? first : lastpos;
         if (lane == 0) {
+            x_first[wave] = first;
+            x_last[wave] = lastpos;
+            x_dmin[wave] = dmin;
+        }
+        __syncthreads();
+        first = x_first[0];
+        lastpos = x_last[0];
+        dmin = x_dmin[0];
+#pragma unroll
+        for (int w = 1; w < kDsW; ++w) {
+            first = min(first, x_first[w]);
+            lastpos = max(lastpos, x_last[w]);
+            dmin = fmin(dmin, x_dmin[w]);
+        }
+        const int tok = first != INT_MAX ? first : lastpos;
+        if (tid == 0) {
             drafts[(size_t)b * gamma + m] = tok;
             if (margin_out) margin_out[(size_t)b * gamma + m] = dmin / total;
         }
@@ -965,15 +1008,15 @@ hipError_t launch_draft_sample(int nb, int gamma, int V, float temperature, cons
                                const int32_t* anchor, const double* u, int32_t* drafts, float* dl, double* margin,
                                hipStream_t st)
 {
-    if (V > 64 * kDsMaxPer) return hipErrorInvalidValue;
-    const int per = (V + 63) / 64;
+    if (V > kDsT * kDsMaxPer) return hipErrorInvalidValue;
+    const int per = (V + kDsT - 1) / kDsT;
 #define HCI_DS(PER_)                                                                                            \
     if (per <= PER_) {                                                                                           \
-        hipLaunchKernelGGL(k_draft_sample<PER_>, dim3(nb), dim3(64), 0, st, gamma, V, (double)temperature, z,  \
+        hipLaunchKernelGGL(k_draft_sample<PER_>, dim3(nb), dim3(kDsT), 0, st, gamma, V, (double)temperature, z,  \
                            markov, anchor, u, drafts, dl, margin);                                               \
         return hipGetLastError();                                                                                \
     }
-    HCI_DS(1) HCI_DS(2) HCI_DS(4) HCI_DS(8) HCI_DS(16) HCI_DS(32) HCI_DS(64)
+    HCI_DS(1) HCI_DS(2) HCI_DS(4) HCI_DS(8) HCI_DS(16)
 #undef HCI_DS
     return hipErrorInvalidValue;
 }
