@@ -28,8 +28,11 @@ def _f64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
+# launch plans covered: three strips of one row tile (13 x 12288), one strip of four row tiles
+# (52 x 4096), rows split to one tile per workgroup to fill the CUs (64 x 1024), two strips of four
+# row tiles to fit one round of workgroups (76 x 3072), ragged rows and strips
 @pytest.mark.parametrize("M,K,N", [(1, 32, 16), (13, 4096, 12288), (52, 4096, 4096), (64, 1024, 1024),
-                                   (65, 64, 48), (200, 512, 256), (3, 96, 4112)])
+                                   (76, 1024, 3072), (65, 64, 48), (200, 512, 256), (3, 96, 4112)])
 @pytest.mark.parametrize("out_f32,with_res", [(False, False), (True, False), (False, True)])
 def test_linear_matches_oracle(M, K, N, out_f32, with_res):
     say(f"linear M={M} K={K} N={N} out_f32={out_f32} residual={with_res}")
