@@ -28,11 +28,14 @@ def _f64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-# launch plans covered: three strips of one row tile (13 x 12288), one strip of four row tiles
-# (52 x 4096), rows split to one tile per workgroup to fill the CUs (64 x 1024), two strips of four
-# row tiles to fit one round of workgroups (76 x 3072), ragged rows and strips
+# every launch plan (strips x 16-row tiles per workgroup): 1 x 1 (64 x 1024: rows split to one
+# tile per workgroup to fill the CUs), 2 x 1 (3 x 4112: two strips to fit one round of workgroups),
+# 3 x 1 (13 x 12288), 4 x 1, 1 x 2, 2 x 2, 3 x 2, 4 x 2 (the short-K shapes), 1 x 4 (52 x 4096),
+# 2 x 4 (76 x 3072), with ragged rows and strips
 @pytest.mark.parametrize("M,K,N", [(1, 32, 16), (13, 4096, 12288), (52, 4096, 4096), (64, 1024, 1024),
-                                   (76, 1024, 3072), (65, 64, 48), (200, 512, 256), (3, 96, 4112)])
+                                   (76, 1024, 3072), (65, 64, 48), (200, 512, 256), (3, 96, 4112),
+                                   (8, 64, 16384), (20, 64, 4096), (20, 64, 8192), (20, 64, 12288),
+                                   (20, 64, 16384)])
 @pytest.mark.parametrize("out_f32,with_res", [(False, False), (True, False), (False, True)])
 def test_linear_matches_oracle(M, K, N, out_f32, with_res):
     say(f"linear M={M} K={K} N={N} out_f32={out_f32} residual={with_res}")
