@@ -23,7 +23,9 @@ def f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("V,gamma,T", [(16, 1, 1.0), (512, 12, 1.0), (512, 32, 0.5), (4096, 6, 2.0), (33, 7, 1.0)])
+# every run length of the four-wave sampler (ids per thread 1, 2, 4, 8, 16), ragged last runs
+@pytest.mark.parametrize("V,gamma,T", [(16, 1, 1.0), (512, 12, 1.0), (512, 32, 0.5), (4096, 6, 2.0), (33, 7, 1.0),
+                                       (1000, 5, 1.0), (1537, 4, 0.75)])
 def test_draft_sample_matches_oracle(V, gamma, T):
     nb = 3
     g = torch.Generator().manual_seed(V * 100 + gamma)
