@@ -3,12 +3,13 @@
 // the block forward already produced -- no target computation is replayed.
 //
 // k_slice reads k and the winning candidate c* on the device, so no host
-// synchronisation sits between acceptance and slicing.  Workgroup roles
-// (blockIdx.y):
-//   0  FIR windows: 64 channels per workgroup; the new window rows are first
+// synchronisation sits between acceptance and slicing.  Workgroup roles, by
+// range of blockIdx.x (blockIdx.z = sequence):
+//   0  FIR windows: 16 channels per workgroup; the new window rows are first
 //      gathered into LDS, then written back (the update is in place)
-//   1  IIR state <- s_k of c*
-//   2  KV rows kv_len .. kv_len+k <- block k/v rows 0..k of c* (tiled layout)
+//   1  IIR state <- s_k of c* (kSliceAux workgroups, 16-byte copies)
+//   2  KV rows kv_len .. kv_len+k <- block k/v rows 0..k of c* (tiled layout;
+//      kSliceAux workgroups)
 // k_slice_len then advances kv_len; it runs after every role of k_slice has
 // read the old length (stream order).
 #include "act_raw.h"
@@ -19,6 +20,10 @@ namespace hci {
 constexpr int kSliceCG = 16;         // channels per window workgroup
 constexpr int kSliceRows = 256 / kSliceCG;   // window rows handled per pass of the 256 threads
 constexpr int kSliceWinMax = 128;    // window rows staged in LDS per pass
+// workgroups of each copy role per sequence: the IIR state (d N floats) and the accepted K/V rows
+// are tens of kilobytes, so a few workgroups copy them, and a 4-sequence slice fits one round of
+// resident workgroups
+constexpr int kSliceAux = 64;
 
 // The winning candidate c*, its accepted index k and the committed length L of sequence b,
 // and the HCI_DS_* bits that stop the commit (0 when it may proceed): c* outside [0, nc), k
@@ -114,7 +119,10 @@ __global__ __launch_bounds__(256) void k_slice(
     int d, int Ts, int To, int N, int H, int DH, int kv_cap, int nc, int gamma, int lim)
 {
     __shared__ float stage[kSliceWinMax][kSliceCG];
-    const int b = blockIdx.z, role = blockIdx.y;
+    const int b = blockIdx.z;
+    const int win_blocks = (int)gridDim.x - 2 * kSliceAux;
+    const int role = (int)blockIdx.x < win_blocks ? 0 : ((int)blockIdx.x < win_blocks + kSliceAux ? 1 : 2);
+    const int wg = role == 0 ? (int)blockIdx.x : (int)blockIdx.x - win_blocks - (role - 1) * kSliceAux;
     const int P = gamma + 1;
     int cstar, k, L;
     // reported by the length kernel; the path check is workgroup-wide (every thread takes part)
@@ -125,7 +133,7 @@ __global__ __launch_bounds__(256) void k_slice(
     const int32_t* rmap = path ? path + (size_t)b * P : nullptr;     // a tree: nc = 1, P = its nodes
 
     if (role == 0) {
-        const int ch0 = blockIdx.x * kSliceCG;
+        const int ch0 = wg * kSliceCG;
         if (ch0 >= d) return;
         if (Ts > 1)
             window_update<ACT>(short_win + (size_t)b * (Ts - 1) * d, x + blk * P * d, Ts - 1, d, k, ch0, stage, rmap);
@@ -136,13 +144,19 @@ __global__ __launch_bounds__(256) void k_slice(
         const size_t n = (size_t)d * N;
         const float* src = s + (blk * P + row_of(rmap, k)) * n;
         float* dst = iir + (size_t)b * n;
-        for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
-            dst[e] = src[e];
+        const size_t t0 = (size_t)wg * blockDim.x + threadIdx.x, stride = (size_t)kSliceAux * blockDim.x;
+        if (((uintptr_t)src % 16) == 0 && ((uintptr_t)dst % 16) == 0) {
+            const size_t n4 = n / 4;
+            for (size_t e = t0; e < n4; e += stride) ((float4*)dst)[e] = ((const float4*)src)[e];
+            for (size_t e = 4 * n4 + t0; e < n; e += stride) dst[e] = src[e];
+        } else {
+            for (size_t e = t0; e < n; e += stride) dst[e] = src[e];
+        }
     } else {
         const size_t per_row = (size_t)H * DH;
         const size_t n = (size_t)(k + 1) * per_row;
         const size_t slab = (size_t)kv_cap * DH;
-        for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+        for (size_t e = (size_t)wg * blockDim.x + threadIdx.x; e < n; e += (size_t)kSliceAux * blockDim.x) {
             const int i = (int)(e / per_row);
             const int h = (int)((e / DH) % H);
             const int dd = (int)(e % DH);
@@ -195,7 +209,7 @@ hipError_t launch_slice(const hci_layer* L, const hci_state* S, const hci_block*
 {
     const int gamma = P - 1;
     const int win_blocks = (L->d + kSliceCG - 1) / kSliceCG;
-    dim3 grid(win_blocks < 256 ? 256 : win_blocks, 3, nb), block(256);
+    dim3 grid(win_blocks + 2 * kSliceAux, 1, nb), block(256);
     if (L->act_dtype == HCI_BF16) {
         hipLaunchKernelGGL(k_slice<HCI_BF16>, grid, block, 0, st,
             (uint16_t*)S->short_win, S->outer_win, S->iir, (uint16_t*)S->k_cache, (uint16_t*)S->v_cache,
